@@ -1,0 +1,265 @@
+"""Benchmark of the chunked SSD scan on one MI355X.
+
+One step = ssd_fwd followed by ssd_bwd (y and all five gradients) on the
+headline workload g2h8_d128: B=4, G=2, H=8, T=8192, dk=dv=128, float32,
+seeded synthetic inputs resident in HBM.  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+
+Throughput (`value`) is the nominal fwd+bwd FLOP count of the step divided
+by the measured step time.  Nominal FLOPs per (token, head), with chunk
+length C = 64 and causal tiles counted as half:
+    forward  C(dk+dv) + 4 dk dv
+    backward C(3dk+2dv) + 10 dk dv   (includes recomputing the chunk states)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "SSD fwd & fwd_bwd ms + TFLOP/s (% roofline), g2h8_d128 B=4 T=8192 fp32"
+PEAK_FP32_MFMA = 157.3e12   # MI355X dense fp32 matrix, FLOP/s
+PEAK_HBM = 8.0e12           # MI355X HBM3E, B/s
+C_NOM = 64
+# The benchmark pages' JAX "chunked" fwd_bwd at this workload on an RTX 3090
+# (kernel_ssd_gpu.json, record chunked·fwd_bwd·g2h8_d128·T8192, median_ms).
+PAGE_FWD_BWD_MS = 11.883384999237023
+
+
+def nominal_flops(s):
+    N = s.B * s.H * s.T
+    f = N * (C_NOM * (s.dk + s.dv) + 4 * s.dk * s.dv)
+    b = N * (C_NOM * (3 * s.dk + 2 * s.dv) + 10 * s.dk * s.dv)
+    return f, b
+
+
+def io_bytes(s):
+    inp = 4 * (2 * s.B * s.G * s.T * s.dk + s.B * s.H * s.T * s.dv + s.B * s.H * s.T + s.B * s.H * s.dk * s.dv)
+    y = 4 * s.B * s.H * s.T * s.dv
+    return inp + y, 3 * inp + 2 * y
+
+
+def kernel_work(s):
+    """Algorithmic work per launch of each kernel: (bound, amount, unit)."""
+    N = s.B * s.H * s.T
+    NC = (s.T + 63) // 64
+    E = s.dk * s.dv
+    states = 4 * s.B * s.H * NC * E
+    return {
+        "chunk_cumsum": ("hbm", 4 * N + 4 * s.B * s.H * NC * 64 + 4 * s.B * s.H * NC, "B"),
+        "chunk_state": ("mfma", N * 2 * E, "FLOP"),
+        "state_pass": ("hbm", 2 * states + 4 * s.B * s.H * E, "B"),
+        "chunk_output": ("mfma", N * (C_NOM * (s.dk + s.dv) + 2 * E), "FLOP"),
+        "chunk_dstate": ("mfma", N * 2 * E, "FLOP"),
+        "state_pass_rev": ("hbm", 2 * states + 4 * s.B * s.H * E, "B"),
+        "bwd_grads": ("mfma", N * (C_NOM * (3 * s.dk + 2 * s.dv) + 6 * E), "FLOP"),
+    }
+
+
+def source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "chunked_ssd_scan_fwd_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary,
+    or None if absent or taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        d = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    ent = d.get(kernel)
+    if not ent or ent.get("workload") != workload or ent.get("source_hash") != source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_info():
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return model
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="g2h8_d128_T8192")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
+              "this build has no multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import chunked_ssd_scan_fwd_amd as ssd
+    from ssd_workload import workload, make_inputs, rel_err
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP device", file=sys.stderr)
+        sys.exit(1)
+    w = workload(args.workload)
+    s = w.shape
+    x = make_inputs(s, w.seed, mu=w.mu)
+    d = {k: torch.from_numpy(v).to("cuda") for k, v in x.items()}
+    sa = ssd.ShapeArg(s.B, s.G, s.H, s.T, s.dk, s.dv)
+    ws = torch.empty(ssd.workspace_size(sa, True), dtype=torch.uint8, device="cuda")
+    y = torch.empty((s.B, s.H, s.T, s.dv), device="cuda")
+    grads = (torch.empty((s.B, s.G, s.T, s.dk), device="cuda"), torch.empty((s.B, s.G, s.T, s.dk), device="cuda"),
+             torch.empty((s.B, s.H, s.T, s.dv), device="cuda"), torch.empty((s.B, s.H, s.T), device="cuda"),
+             torch.empty((s.B, s.H, s.dk, s.dv), device="cuda"))
+
+    def fwd():
+        ssd.fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["h0"], out=y, workspace=ws)
+
+    def bwd():
+        ssd.bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["h0"], d["dy"], out=grads, workspace=ws)
+
+    def step():
+        fwd()
+        bwd()
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    step()
+    torch.cuda.synchronize()
+    first_call_ms = (time.perf_counter() - t0) * 1e3
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    def timed(fn, K, with_kernels=False):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        if with_kernels:
+            kt = ssd.kernel_timing().__enter__()
+        evs[0].record()
+        for i in range(K):
+            fn()
+            evs[i + 1].record()
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - wall0) * 1e3
+        if with_kernels:
+            kt.__exit__(None, None, None)
+        per = [evs[i].elapsed_time(evs[i + 1]) for i in range(K)]
+        total = evs[0].elapsed_time(evs[K])
+        return total / K, per, wall / K, (kt.results if with_kernels else None)
+
+    K = args.steps
+    # Timed region: exactly K steps, with per-kernel HIP events on the launch stream.
+    step_ms, per_step, wall_ms, kern = timed(step, K, with_kernels=True)
+    fwd_ms, fwd_per, _, _ = timed(fwd, K)
+    bwd_ms, bwd_per, _, _ = timed(bwd, K)
+
+    f_fwd, f_bwd = nominal_flops(s)
+    b_fwd, b_fwd_bwd = io_bytes(s)
+    value = (f_fwd + f_bwd) / (step_ms * 1e-3) / 1e12
+    t_roof_fb = max((f_fwd + f_bwd) / PEAK_FP32_MFMA, b_fwd_bwd / PEAK_HBM)
+    t_roof_f = max(f_fwd / PEAK_FP32_MFMA, b_fwd / PEAK_HBM)
+
+    work = kernel_work(s)
+    kernels = {}
+    for name, (tot, cnt) in kern.items():
+        if cnt:
+            kernels[name] = {"avg_us": 1e3 * tot / cnt, "launches": cnt, "share": tot / (step_ms * K)}
+    dom = max(kernels, key=lambda n: kernels[n]["avg_us"] * kernels[n]["launches"])
+    bound, amount, unit = work[dom]
+    avg_s = kernels[dom]["avg_us"] * 1e-6
+    if bound == "mfma":
+        roof = {"bound": "mfma", "achieved": amount / avg_s / 1e12, "peak": PEAK_FP32_MFMA / 1e12,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": amount / avg_s / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["kernel"] = dom
+    roof["work_per_launch"] = amount
+    roof["traffic"] = traffic_from_profiles(dom, w.name)
+    for name in kernels:
+        bnd, amt, _ = work[name]
+        a = amt / (kernels[name]["avg_us"] * 1e-6)
+        kernels[name]["achieved"] = a / 1e12 if bnd == "mfma" else a / 1e9
+        kernels[name]["unit"] = "TFLOP/s" if bnd == "mfma" else "GB/s"
+        kernels[name]["frac"] = a / (PEAK_FP32_MFMA if bnd == "mfma" else PEAK_HBM)
+
+    cpu = None
+    parity = None
+    if not args.no_cpu:
+        # CPU baseline: the fp64 oracle on the whole workload, on the host cores.
+        import oracle
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ref_y = oracle.fwd(x["q"], x["k"], x["v"], x["log_alpha"], x["h0"])
+        ref = oracle.bwd(x["q"], x["k"], x["v"], x["log_alpha"], x["h0"], x["dy"])
+        cpu_s = time.perf_counter() - t0
+        cpu = {"value": (f_fwd + f_bwd) / cpu_s / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+               "kind": "oracle", "seconds": cpu_s, "cpu_model": cpu_info(),
+               "sample": f"whole {w.name} workload, one fwd + bwd in fp64 (nominal FLOPs / wall time)"}
+        # parity of the last timed GPU step against the oracle (whole tensors)
+        fwd()
+        bwd()
+        torch.cuda.synchronize()
+        parity = {"y": rel_err(y.cpu().numpy(), ref_y)}
+        for name, t in zip(("dq", "dk", "dv", "dlog_alpha", "dh0"), grads):
+            parity[name] = rel_err(t.cpu().numpy(), ref[name])
+
+    def q(vals):
+        a = np.asarray(vals)
+        return {"median_ms": float(np.median(a)), "q1_ms": float(np.percentile(a, 25)),
+                "q3_ms": float(np.percentile(a, 75))}
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": (PAGE_FWD_BWD_MS / step_ms) if w.name == "g2h8_d128_T8192" else None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: B={s.B} G={s.G} H={s.H} T={s.T} dk={s.dk} dv={s.dv}, "
+                               "step = ssd_fwd + ssd_bwd", "chunk": 64, "seed": w.seed},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "fwd_bwd": {**q(per_step), "tflops": value, "roofline_frac": t_roof_fb / (step_ms * 1e-3),
+                    "gbps_io": b_fwd_bwd / (step_ms * 1e-3) / 1e9, "wall_ms": wall_ms},
+        "fwd": {**q(fwd_per), "ms": fwd_ms, "tflops": f_fwd / (fwd_ms * 1e-3) / 1e12,
+                "roofline_frac": t_roof_f / (fwd_ms * 1e-3), "gbps_io": b_fwd / (fwd_ms * 1e-3) / 1e9},
+        "bwd": {**q(bwd_per), "ms": bwd_ms, "tflops": f_bwd / (bwd_ms * 1e-3) / 1e12},
+        "kernels": kernels,
+        "parity_rel_err": parity,
+        "first_call_ms": first_call_ms,
+        "device": torch.cuda.get_device_name(0),
+        "source_hash": source_hash(),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,34 @@
+// Internal host-side declarations shared by the validation unit and the HIP
+// launch unit.  Not part of the public ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "ssd.h"
+
+namespace ssd {
+
+constexpr int kChunk = SSD_CHUNK;   // steps per chunk = wavefront width
+constexpr int64_t kMaxDim = 128;    // largest supported dk / dv
+
+struct Layout {
+    int64_t NC = 0;      // chunks per sequence, ceil(T / 64)
+    int64_t NCp = 0;     // NC rounded up to a multiple of 64
+    int64_t E = 0;       // dk * dv
+    int64_t Epad = 0;    // E rounded up to a multiple of 64 (slab stride, floats)
+    size_t off[5] = {0, 0, 0, 0, 0};   // bcum, bl, states, dstates, total bytes
+};
+
+// SSD_OK, SSD_ERR_NULL (shape == NULL), SSD_ERR_SHAPE or SSD_ERR_UNSUPPORTED.
+int check_shape(const ssd_shape *s);
+
+// Workspace layout for a valid shape.  Empty shapes give total == 0.
+Layout make_layout(const ssd_shape *s, bool backward);
+
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Padded MFMA tile width (32, 64 or 128) for a supported dk / dv.
+inline int pad_dim(int64_t d) { return d <= 32 ? 32 : (d <= 64 ? 64 : 128); }
+
+}  // namespace ssd

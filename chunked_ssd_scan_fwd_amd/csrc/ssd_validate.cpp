@@ -1,0 +1,96 @@
+// Host-only argument checks and workspace layout for the SSD scan C ABI.
+// This unit makes no HIP call.
+#include "ssd_internal.h"
+
+namespace ssd {
+
+int check_shape(const ssd_shape *s)
+{
+    if (!s) return SSD_ERR_NULL;
+    if (s->B < 0 || s->T < 0 || s->G < 1 || s->H < 1 || s->dk < 1 || s->dv < 1) return SSD_ERR_SHAPE;
+    if (s->H % s->G != 0) return SSD_ERR_SHAPE;
+    // Keep every element index comfortably inside 64-bit arithmetic and the
+    // per-(b,h) sequence offsets inside 32-bit chunk counts.
+    const int64_t lim = int64_t(1) << 40;
+    if (s->B > lim || s->H > lim || s->T > lim) return SSD_ERR_SHAPE;
+    const int64_t dmax = s->dk > s->dv ? s->dk : s->dv;
+    if (dmax > kMaxDim) return SSD_ERR_UNSUPPORTED;
+    if (s->B > lim / s->H) return SSD_ERR_SHAPE;           // B*H <= 2^40, no overflow below
+    if (s->B * s->H > lim / (s->T + 1)) return SSD_ERR_SHAPE;
+    if (s->B * s->H * (s->T + 1) > lim / dmax) return SSD_ERR_SHAPE;
+    if ((s->T + kChunk - 1) / kChunk > (int64_t(1) << 30)) return SSD_ERR_SHAPE;
+    // Every launch grid is one-dimensional: blocks must fit in 2^31 - 1.
+    const int64_t nc = (s->T + kChunk - 1) / kChunk;
+    const int64_t grid_lim = (int64_t(1) << 31) - 1;
+    if (s->B * s->H > grid_lim / 16) return SSD_ERR_UNSUPPORTED;
+    if (nc > 0 && s->B * s->H > grid_lim / nc) return SSD_ERR_UNSUPPORTED;
+    return SSD_OK;
+}
+
+static size_t round_up(size_t x, size_t m) { return (x + m - 1) / m * m; }
+
+Layout make_layout(const ssd_shape *s, bool backward)
+{
+    Layout L;
+    L.NC = (s->T + kChunk - 1) / kChunk;
+    L.NCp = (L.NC + 63) / 64 * 64;
+    L.E = s->dk * s->dv;
+    L.Epad = (L.E + 63) / 64 * 64;
+    const size_t BH = size_t(s->B) * size_t(s->H);
+    if (BH == 0 || s->T == 0) return L;   // nothing to store
+    size_t o = 0;
+    L.off[0] = o;
+    o = round_up(o + BH * size_t(L.NC) * kChunk * sizeof(float), 256);
+    L.off[1] = o;
+    o = round_up(o + BH * size_t(L.NCp) * sizeof(float), 256);
+    L.off[2] = o;
+    o = round_up(o + BH * size_t(L.NC) * size_t(L.Epad) * sizeof(float), 256);
+    L.off[3] = o;
+    if (backward) o = round_up(o + BH * size_t(L.NC) * size_t(L.Epad) * sizeof(float), 256);
+    L.off[4] = o;
+    return L;
+}
+
+}  // namespace ssd
+
+extern "C" {
+
+size_t ssd_fwd_workspace_size(const ssd_shape *shape)
+{
+    if (ssd::check_shape(shape) != SSD_OK) return (size_t)-1;
+    return ssd::make_layout(shape, false).off[4];
+}
+
+size_t ssd_bwd_workspace_size(const ssd_shape *shape)
+{
+    if (ssd::check_shape(shape) != SSD_OK) return (size_t)-1;
+    return ssd::make_layout(shape, true).off[4];
+}
+
+int ssd_workspace_layout(const ssd_shape *shape, int backward, size_t offsets[5])
+{
+    if (!offsets) return SSD_ERR_NULL;
+    const int rc = ssd::check_shape(shape);
+    if (rc != SSD_OK) return rc;
+    const ssd::Layout L = ssd::make_layout(shape, backward != 0);
+    for (int i = 0; i < 5; ++i) offsets[i] = L.off[i];
+    return SSD_OK;
+}
+
+const char *ssd_strerror(int status)
+{
+    switch (status) {
+    case SSD_OK: return "success";
+    case SSD_ERR_NULL: return "a required pointer is NULL";
+    case SSD_ERR_SHAPE: return "invalid shape (negative size, G < 1, H not a multiple of G, or too large)";
+    case SSD_ERR_UNSUPPORTED: return "unsupported shape (dk and dv must be in 1..128)";
+    case SSD_ERR_WORKSPACE: return "workspace smaller than the size query requires";
+    case SSD_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case SSD_ERR_DEVICE: return "HIP launch or runtime error";
+    default: return "unknown status";
+    }
+}
+
+int ssd_chunk_size(void) { return SSD_CHUNK; }
+
+}  // extern "C"

@@ -1,0 +1,126 @@
+"""CPU checks of the C ABI: the library loads, exports every declared symbol,
+and rejects bad arguments on the host before any GPU work."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import chunked_ssd_scan_fwd_amd as ssd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssd.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssd_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ssd.library()
+    names = declared_functions()
+    assert "ssd_fwd" in names and "ssd_bwd" in names
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in ssd.h but not exported"
+
+
+def _call_fwd(shape, ptr=1, ws_bytes=0):
+    lib = ssd.library()
+    p = ctypes.c_void_p(ptr) if ptr else None
+    return lib.ssd_fwd(ctypes.byref(shape), p, p, p, p, p, p, p, ws_bytes, None)
+
+
+def _call_bwd(shape, ptr=1, ws_bytes=0):
+    lib = ssd.library()
+    p = ctypes.c_void_p(ptr) if ptr else None
+    return lib.ssd_bwd(ctypes.byref(shape), *([p] * 11), p, ws_bytes, None)
+
+
+@pytest.mark.parametrize("shape,code", [
+    (ssd.ShapeArg(1, 3, 4, 10, 8, 8), 2),      # H % G != 0
+    (ssd.ShapeArg(1, 0, 4, 10, 8, 8), 2),      # G < 1
+    (ssd.ShapeArg(-1, 1, 1, 10, 8, 8), 2),     # negative B
+    (ssd.ShapeArg(1, 1, 1, -5, 8, 8), 2),      # negative T
+    (ssd.ShapeArg(1, 1, 1, 10, 0, 8), 2),      # dk = 0
+    (ssd.ShapeArg(1, 1, 1, 10, 129, 8), 3),    # dk above the supported range
+    (ssd.ShapeArg(1, 1, 1, 10, 8, 200), 3),    # dv above the supported range
+    (ssd.ShapeArg(1 << 40, 1 << 40, 1 << 40, 10, 8, 8), 2),   # overflow guard
+])
+def test_bad_shapes_rejected(shape, code):
+    assert _call_fwd(shape) == code
+    assert _call_bwd(shape) == code
+
+
+def test_null_shape_and_pointers():
+    lib = ssd.library()
+    assert lib.ssd_fwd(None, *([None] * 7), 0, None) == 1
+    s = ssd.ShapeArg(1, 1, 1, 10, 8, 8)
+    assert _call_fwd(s, ptr=0) == 1
+    assert _call_bwd(s, ptr=0) == 1
+
+
+def test_misaligned_pointer_rejected():
+    s = ssd.ShapeArg(1, 1, 1, 10, 8, 8)
+    assert _call_fwd(s, ptr=0x1004) == 5
+    assert _call_bwd(s, ptr=0x1004) == 5
+
+
+def test_workspace_too_small_rejected():
+    s = ssd.ShapeArg(1, 1, 1, 10, 8, 8)
+    need = ssd.workspace_size(s, False)
+    assert need > 0
+    assert _call_fwd(s, ptr=0x1000, ws_bytes=need - 1) == 4
+    assert _call_bwd(s, ptr=0x1000, ws_bytes=ssd.workspace_size(s, True) - 1) == 4
+
+
+def test_empty_problems_need_no_workspace():
+    assert ssd.workspace_size(ssd.ShapeArg(0, 1, 1, 10, 8, 8), True) == 0
+    assert ssd.workspace_size(ssd.ShapeArg(2, 1, 1, 0, 8, 8), False) == 0
+    # empty forward needs no pointers at all
+    assert _call_fwd(ssd.ShapeArg(0, 1, 1, 10, 8, 8), ptr=0) == 0
+
+
+@pytest.mark.parametrize("B,G,H,T,dk,dv", [(4, 2, 8, 8192, 128, 128), (2, 1, 24, 8192, 128, 64),
+                                           (4, 2, 4, 2048, 48, 40), (1, 1, 1, 1, 1, 1)])
+def test_workspace_layout_formula(B, G, H, T, dk, dv):
+    s = ssd.ShapeArg(B, G, H, T, dk, dv)
+    off = ssd.workspace_layout(s, True)
+    NC = (T + 63) // 64
+    NCp = (NC + 63) // 64 * 64
+    Epad = (dk * dv + 63) // 64 * 64
+    BH = B * H
+
+    def up(x):
+        return (x + 255) // 256 * 256
+
+    assert off[0] == 0
+    assert off[1] == up(BH * NC * 64 * 4)
+    assert off[2] == up(off[1] + BH * NCp * 4)
+    assert off[3] == up(off[2] + BH * NC * Epad * 4)
+    assert off[4] == up(off[3] + BH * NC * Epad * 4)
+    assert ssd.workspace_size(s, True) == off[4]
+    assert ssd.workspace_size(s, False) == off[3]
+
+
+def test_status_strings_and_constants():
+    lib = ssd.library()
+    for code in range(7):
+        assert lib.ssd_strerror(code)
+    assert lib.ssd_strerror(99) == b"unknown status"
+    assert lib.ssd_chunk_size() == ssd.CHUNK == 64
+    names = [lib.ssd_kernel_name(i).decode() for i in range(lib.ssd_kernel_count())]
+    assert "bwd_grads" in names and "state_pass" in names
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 1, 4, 8)
+    with pytest.raises(ValueError):
+        ssd.fwd(x, x, x, torch.zeros(1, 1, 4), torch.zeros(1, 1, 8, 8))
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(ImportError):
+        ssd.library(str(tmp_path / "missing.so"))

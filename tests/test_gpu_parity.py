@@ -1,0 +1,263 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Bar (rel_err = max|out - ref| / max|ref| over the whole tensor):
+y <= 2e-5, each of dq, dk, dv, dlog_alpha, dh0 <= 5e-5.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from ssd_workload import Shape, make_inputs, rel_err, WORKLOADS, workload
+from gpu_util import need_gpu, say, to_dev, hip_fwd, hip_bwd, host
+
+pytestmark = pytest.mark.gpu
+
+TOL_Y = 2e-5
+TOL_G = 5e-5
+GRADS = ("dq", "dk", "dv", "dlog_alpha", "dh0")
+
+ZOO = [
+    Shape(1, 1, 1, 1, 1, 1),
+    Shape(2, 1, 1, 2, 3, 5),
+    Shape(1, 2, 4, 17, 48, 40),
+    Shape(2, 2, 4, 63, 128, 128),
+    Shape(1, 1, 3, 65, 128, 64),
+    Shape(2, 3, 6, 100, 64, 32),
+    Shape(1, 1, 1, 200, 128, 1),
+    Shape(1, 2, 2, 130, 1, 128),
+    Shape(2, 2, 8, 256, 128, 128),
+    Shape(1, 1, 24, 300, 128, 64),
+    Shape(3, 1, 2, 129, 33, 97),
+]
+
+
+def _id(s):
+    return f"B{s.B}G{s.G}H{s.H}T{s.T}dk{s.dk}dv{s.dv}"
+
+
+def check_fwd(x, tol=TOL_Y):
+    d = to_dev(x)
+    y = host(hip_fwd(d))
+    ref = oracle.fwd(x["q"], x["k"], x["v"], x["log_alpha"], x["h0"])
+    e = rel_err(y, ref)
+    assert e <= tol, f"y rel_err {e:.3e}"
+    return e
+
+
+def check_bwd(x, tol=TOL_G):
+    d = to_dev(x)
+    g = {k: host(v) for k, v in hip_bwd(d).items()}
+    ref = oracle.bwd(x["q"], x["k"], x["v"], x["log_alpha"], x["h0"], x["dy"])
+    errs = {k: rel_err(g[k], ref[k]) for k in GRADS}
+    bad = {k: e for k, e in errs.items() if not e <= tol}
+    assert not bad, f"gradient rel_err over bar: {bad}"
+    return errs
+
+
+@pytest.mark.parametrize("shape", ZOO, ids=_id)
+def test_forward_shape_zoo(shape):
+    need_gpu()
+    say(f"fwd {_id(shape)}")
+    check_fwd(make_inputs(shape, seed=shape.T * 7 + shape.dk))
+
+
+@pytest.mark.parametrize("shape", ZOO, ids=_id)
+def test_backward_shape_zoo(shape):
+    need_gpu()
+    say(f"bwd {_id(shape)}")
+    check_bwd(make_inputs(shape, seed=shape.T * 11 + shape.dv))
+
+
+def test_chunk_states_match_oracle():
+    """Step-level check: the state entering every chunk, as left in the
+    workspace by ssd_fwd, against the oracle's state at the chunk boundary."""
+    need_gpu()
+    import torch
+    import chunked_ssd_scan_fwd_amd as ssd
+    shape = Shape(2, 2, 4, 300, 48, 40)
+    x = make_inputs(shape, seed=5)
+    d = to_dev(x)
+    sa = ssd.ShapeArg(shape.B, shape.G, shape.H, shape.T, shape.dk, shape.dv)
+    ws = torch.empty(ssd.workspace_size(sa, False), dtype=torch.uint8, device="cuda")
+    say("chunk states B2G2H4T300")
+    ssd.fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["h0"], workspace=ws)
+    off = ssd.workspace_layout(sa, False)
+    NC = (shape.T + 63) // 64
+    E = shape.dk * shape.dv
+    Epad = (E + 63) // 64 * 64
+    st = host(ws[off[2]:off[2] + shape.B * shape.H * NC * Epad * 4].view(torch.float32))
+    st = st.reshape(shape.B, shape.H, NC, Epad)[..., :E].reshape(shape.B, shape.H, NC, shape.dk, shape.dv)
+    _, ref = oracle.fwd(x["q"], x["k"], x["v"], x["log_alpha"], x["h0"], chunk=64)
+    assert rel_err(st, ref) <= TOL_Y
+    # within-chunk cumulative log-decay and chunk totals
+    bc = host(ws[off[0]:off[0] + shape.B * shape.H * NC * 64 * 4].view(torch.float32))
+    bc = bc.reshape(shape.B, shape.H, NC * 64)
+    la = np.zeros((shape.B, shape.H, NC * 64))
+    la[..., :shape.T] = x["log_alpha"]
+    ref_b = np.cumsum(la.reshape(shape.B, shape.H, NC, 64), axis=-1).reshape(shape.B, shape.H, -1)
+    assert rel_err(bc, ref_b) <= 1e-6
+
+
+@pytest.mark.parametrize("idx", [0, 1, 2])
+def test_workload_full_size(idx):
+    """Full-size parity on the three smaller workloads (whole tensors)."""
+    need_gpu()
+    w = WORKLOADS[idx]
+    say(f"workload {w.name}")
+    x = make_inputs(w.shape, w.seed, mu=w.mu)
+    check_fwd(x)
+    check_bwd(x)
+
+
+@pytest.mark.parametrize("name,b,g", [("g1h24_dk128_dv64_T8192", 1, 0), ("g2h8_d128_T8192", 3, 1),
+                                      ("g2h8_d128_T8192", 0, 0)])
+def test_workload_large_sampled(name, b, g):
+    """Large workloads: the HIP path runs the whole problem; the oracle
+    recomputes one (batch, group) slice, which depends on nothing else."""
+    need_gpu()
+    w = workload(name)
+    s = w.shape
+    hpg = s.hpg
+    say(f"workload {name} slice b={b} g={g}")
+    x = make_inputs(s, w.seed, mu=w.mu)
+    d = to_dev(x)
+    y = host(hip_fwd(d))
+    gr = {k: host(v) for k, v in hip_bwd(d).items()}
+    hs = slice(g * hpg, (g + 1) * hpg)
+    xs = {"q": x["q"][b:b + 1, g:g + 1], "k": x["k"][b:b + 1, g:g + 1], "v": x["v"][b:b + 1, hs],
+          "log_alpha": x["log_alpha"][b:b + 1, hs], "h0": x["h0"][b:b + 1, hs], "dy": x["dy"][b:b + 1, hs]}
+    ref_y = oracle.fwd(xs["q"], xs["k"], xs["v"], xs["log_alpha"], xs["h0"])
+    assert rel_err(y[b:b + 1, hs], ref_y) <= TOL_Y
+    ref = oracle.bwd(xs["q"], xs["k"], xs["v"], xs["log_alpha"], xs["h0"], xs["dy"])
+    got = {"dq": gr["dq"][b:b + 1, g:g + 1], "dk": gr["dk"][b:b + 1, g:g + 1], "dv": gr["dv"][b:b + 1, hs],
+           "dlog_alpha": gr["dlog_alpha"][b:b + 1, hs], "dh0": gr["dh0"][b:b + 1, hs]}
+    errs = {k: rel_err(got[k], ref[k]) for k in GRADS}
+    assert all(e <= TOL_G for e in errs.values()), errs
+
+
+def test_headline_identities_full_size():
+    """Properties that hold at any size, checked on the whole headline problem:
+    <q,dq> = L, <k,dk> = <v,dv> = L - <h0,dh0>, dlog_alpha[:,:,0] = <h0,dh0> per head."""
+    need_gpu()
+    w = workload("g2h8_d128_T8192")
+    say("headline identities")
+    x = make_inputs(w.shape, w.seed, mu=w.mu)
+    d = to_dev(x)
+    y = host(hip_fwd(d)).astype(np.float64)
+    g = {k: host(v).astype(np.float64) for k, v in hip_bwd(d).items()}
+    L = float(np.sum(x["dy"].astype(np.float64) * y))
+    h0t = float(np.sum(x["h0"].astype(np.float64) * g["dh0"]))
+    scale = float(np.sum(np.abs(x["dy"].astype(np.float64) * y)))
+    assert abs(np.sum(x["q"] * g["dq"]) - L) <= 1e-5 * scale
+    assert abs(np.sum(x["k"] * g["dk"]) - (L - h0t)) <= 1e-5 * scale
+    assert abs(np.sum(x["v"] * g["dv"]) - (L - h0t)) <= 1e-5 * scale
+    per_head = np.sum(x["h0"] * g["dh0"], axis=(2, 3))
+    assert rel_err(g["dlog_alpha"][:, :, 0], per_head) <= 1e-4
+
+
+def test_zero_decay_no_h0():
+    need_gpu()
+    s = Shape(2, 2, 4, 150, 64, 64)
+    x = make_inputs(s, 3)
+    x["log_alpha"][:] = 0.0
+    x["h0"][:] = 0.0
+    say("zero decay")
+    check_fwd(x)
+    check_bwd(x)
+
+
+def test_strong_decay():
+    need_gpu()
+    s = Shape(1, 1, 2, 130, 32, 32)
+    x = make_inputs(s, 4)
+    x["log_alpha"][:] = -80.0
+    say("strong decay")
+    check_fwd(x)
+    check_bwd(x)
+
+
+def test_group_replication_matches():
+    """Replicating q, k to one group per head gives the grouped result."""
+    need_gpu()
+    s = Shape(2, 2, 8, 140, 128, 128)
+    x = make_inputs(s, 8)
+    idx = np.arange(s.H) // s.hpg
+    xr = dict(x)
+    xr["q"] = np.ascontiguousarray(x["q"][:, idx])
+    xr["k"] = np.ascontiguousarray(x["k"][:, idx])
+    say("group replication")
+    d, dr = to_dev(x), to_dev(xr)
+    y, yr = host(hip_fwd(d)), host(hip_fwd(dr))
+    assert rel_err(yr, y) <= TOL_Y
+    g, gr = hip_bwd(d), hip_bwd(dr)
+    dq = host(g["dq"])
+    dqr = host(gr["dq"]).reshape(s.B, s.G, s.hpg, s.T, s.dk).sum(axis=2)
+    assert rel_err(dqr, dq) <= TOL_G
+
+
+def test_deterministic():
+    need_gpu()
+    s = Shape(2, 2, 8, 257, 128, 128)
+    x = make_inputs(s, 9)
+    d = to_dev(x)
+    say("determinism")
+    y1, y2 = host(hip_fwd(d)), host(hip_fwd(d))
+    np.testing.assert_array_equal(y1, y2)
+    g1 = {k: host(v) for k, v in hip_bwd(d).items()}
+    g2 = {k: host(v) for k, v in hip_bwd(d).items()}
+    for k in GRADS:
+        np.testing.assert_array_equal(g1[k], g2[k])
+
+
+def test_guard_bands_poisoned_workspace_and_side_stream():
+    """Outputs inside NaN guard bands, a NaN-filled workspace, a non-default
+    stream, and unmodified inputs."""
+    need_gpu()
+    import torch
+    import chunked_ssd_scan_fwd_amd as ssd
+    s = Shape(2, 2, 4, 190, 48, 40)
+    x = make_inputs(s, 10)
+    d = to_dev(x)
+    before = {k: v.clone() for k, v in d.items()}
+    guard = 256
+
+    def guarded(shape):
+        n = int(np.prod(shape))
+        buf = torch.full((n + 2 * guard,), float("nan"), device="cuda")
+        return buf, buf[guard:guard + n].view(shape)
+
+    sa = ssd.ShapeArg(s.B, s.G, s.H, s.T, s.dk, s.dv)
+    ws = torch.full((ssd.workspace_size(sa, True) // 4 + 1,), float("nan"), device="cuda")
+    bufs = [guarded(sh) for sh in [(s.B, s.H, s.T, s.dv), (s.B, s.G, s.T, s.dk), (s.B, s.G, s.T, s.dk),
+                                   (s.B, s.H, s.T, s.dv), (s.B, s.H, s.T), (s.B, s.H, s.dk, s.dv)]]
+    say("guard bands / side stream")
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        ssd.fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["h0"], out=bufs[0][1], workspace=ws)
+        ssd.bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["h0"], d["dy"],
+                out=tuple(b[1] for b in bufs[1:]), workspace=ws)
+    side.synchronize()
+    for buf, view in bufs:
+        b = buf.cpu().numpy()
+        assert np.all(np.isnan(b[:guard])) and np.all(np.isnan(b[-guard:]))
+        assert np.all(np.isfinite(view.cpu().numpy()))
+    ref_y = oracle.fwd(x["q"], x["k"], x["v"], x["log_alpha"], x["h0"])
+    assert rel_err(bufs[0][1].cpu().numpy(), ref_y) <= TOL_Y
+    ref = oracle.bwd(x["q"], x["k"], x["v"], x["log_alpha"], x["h0"], x["dy"])
+    for (buf, view), name in zip(bufs[1:], GRADS):
+        assert rel_err(view.cpu().numpy(), ref[name]) <= TOL_G, name
+    for k in d:
+        assert torch.equal(d[k], before[k])
+
+
+def test_empty_shapes():
+    need_gpu()
+    import torch
+    import chunked_ssd_scan_fwd_amd as ssd
+    say("empty shapes")
+    x = to_dev(make_inputs(Shape(2, 1, 2, 0, 8, 8), 1))
+    y = ssd.fwd(x["q"], x["k"], x["v"], x["log_alpha"], x["h0"])
+    assert y.shape == (2, 2, 0, 8)
+    dq, dk, dv, dla, dh0 = ssd.bwd(x["q"], x["k"], x["v"], x["log_alpha"], x["h0"], x["dy"])
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dh0).item() == 0

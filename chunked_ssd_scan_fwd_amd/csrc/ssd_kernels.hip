@@ -19,11 +19,18 @@
 //   dQ = dP K + diag(e^b) dY S_in^T
 //   dK = dP^T Q + diag(e^{b_L - b}) V dS_out^T
 //   dV = (Q K^T o D)^T dY + diag(e^{b_L - b}) K dS_out
-//   dlog_alpha_r = sum_{t >= r, t in chunk} (q_t.dq_t - k_t.dk_t)  (per head)
-//                  + <dS_out(c), S_in(c+1)>_F
+//   dlog_alpha_r = sum_{i >= r, j < r} M_ij                    (intra)
+//                + sum_{i >= r} e^{b_i} q_i . (dY S_in^T)_i        (output via S_in)
+//                + sum_{j < r} e^{b_L - b_j} k_j . (V dS_out^T)_j  (outgoing state)
+//                + e^{b_L} <dS_out, S_in>_F
+//   with M = (Q K^T) o D o (dY V^T).
 //
-// (the last line: L depends on b_t only through e^{b_t} q_t, e^{-b_t} k_t
-// and, at the chunk's end, through the factor e^{b_L} of the outgoing state).
+// The last formula differentiates each decay factor directly: D_ij depends
+// on log_alpha_r exactly when j < r <= i, e^{b_i} when r <= i, e^{b_L - b_j}
+// when r > j, and e^{b_L} always.  It equals the suffix sum of
+// q_t.dq_t - k_t.dk_t plus the boundary term, but it has no cancelling O(1)
+// terms (the diagonal of M and the last position's state term cancel
+// exactly in that form), so its error scales with dlog_alpha itself.
 //
 // All contractions run on v_mfma_f32_32x32x2f32 (fp32 in, fp32 accumulate).
 // For that instruction, lane l supplies A[l%32][l/32] and B[l/32][l%32] of a
@@ -416,6 +423,7 @@ __global__ __launch_bounds__(NTH) void k_bwd_grads(
     __shared__ float bs[CH], eb[CH], el[CH];
     __shared__ float redQ[NCBK][CH], redK[NCBK][CH];
     __shared__ float redB[NTH / 64];
+    __shared__ float redR[NTH / 64][CH];
 
     const int64_t c = blockIdx.x % NC;
     const int64_t bg = blockIdx.x / NC;
@@ -462,8 +470,9 @@ __global__ __launch_bounds__(NTH) void k_bwd_grads(
         stage_rows<DVP, LDY, false>(dYs, dy + (bh * T + c * CH) * dv_, rows, dv_, vecV != 0, nullptr);
         __syncthreads();
 
-        // dP = (dY V^T) o D into LDS; P = (Q K^T) o D kept in registers.
-        f32x16 pP = zero16();
+        // dP = (dY V^T) o D into LDS; P = (Q K^T) o D and M = P o (dY V^T)
+        // kept in registers.
+        f32x16 pP = zero16(), pM = zero16();
         if (wave < 3) {
             f32x16 a = zero16();
 #pragma unroll 8
@@ -475,6 +484,7 @@ __global__ __launch_bounds__(NTH) void k_bwd_grads(
                 const float D = (j <= i) ? expf(bs[i] - bs[j]) : 0.f;
                 dPs[i * LDP + j] = a[r] * D;
                 pP[r] = accA[r] * D;
+                pM[r] = pP[r] * a[r];
             }
         }
         __syncthreads();
@@ -494,16 +504,16 @@ __global__ __launch_bounds__(NTH) void k_bwd_grads(
                     a = mfma32(dYs[(rb * 32 + cl) * LDY + nn], sv, a);
                 }
 #pragma unroll
-                for (int r = 0; r < 16; ++r) a[r] *= eb[rb * 32 + acc_row(r, lane)];
-                const int kend = (rb + 1) * 32;
-                for (int jj = 0; jj < kend; jj += 2)
-                    a = mfma32(dPs[(rb * 32 + cl) * LDP + jj + kh], Ks[(jj + kh) * LDK + col], a);
-#pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int row = rb * 32 + acc_row(r, lane);
+                    a[r] *= eb[row];
+                    // e^{b_i} q_i . (dY S_in^T)_i, partial over this column block
                     const float s = sum32(a[r] * Qs[row * LDK + col]);
                     if (cl == 0) redQ[cb][row] = s;
                 }
+                const int kend = (rb + 1) * 32;
+                for (int jj = 0; jj < kend; jj += 2)
+                    a = mfma32(dPs[(rb * 32 + cl) * LDP + jj + kh], Ks[(jj + kh) * LDK + col], a);
                 dQacc[jw] += a;
             }
         }
@@ -523,26 +533,31 @@ __global__ __launch_bounds__(NTH) void k_bwd_grads(
                     a = mfma32(VPs[(rb * 32 + cl) * LDV + nn], sv, a);
                 }
 #pragma unroll
-                for (int r = 0; r < 16; ++r) a[r] *= el[rb * 32 + acc_row(r, lane)];
-                for (int jj = rb * 32; jj < CH; jj += 2)
-                    a = mfma32(dPs[(jj + kh) * LDP + rb * 32 + cl], Qs[(jj + kh) * LDK + col], a);
-#pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int row = rb * 32 + acc_row(r, lane);
+                    a[r] *= el[row];
+                    // e^{b_L - b_j} k_j . (V dS_out^T)_j, partial over this column block
                     const float s = sum32(a[r] * Ks[row * LDK + col]);
                     if (cl == 0) redK[cb][row] = s;
                 }
+                for (int jj = rb * 32; jj < CH; jj += 2)
+                    a = mfma32(dPs[(jj + kh) * LDP + rb * 32 + cl], Qs[(jj + kh) * LDK + col], a);
                 dKacc[jw] += a;
             }
         }
-        __syncthreads();   // V and dP are dead; P goes where V was
+        __syncthreads();   // V and dP are dead; P goes where V was, M where dP was
 
         if (wave < 3) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int i = ib * 32 + acc_row(r, lane), j = jb * 32 + cl;
                 VPs[i * LDV + j] = pP[r];
+                dPs[i * LDP + j] = pM[r];
             }
+        } else {
+            // upper-right tile of M is zero (j > i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dPs[acc_row(r, lane) * LDP + 32 + cl] = 0.f;
         }
         __syncthreads();
 
@@ -574,18 +589,39 @@ __global__ __launch_bounds__(NTH) void k_bwd_grads(
             }
         }
 
-        // Boundary term <dS_out(c), S_in(c+1)> (zero for the last chunk).
+        // Rectangle sums R_r = sum_{i >= r} sum_{j < r} M_ij: exclusive prefix
+        // over j of every row (in place), then a suffix over i per column.
+        for (int i = wave * 16; i < wave * 16 + 16; ++i) {
+            float x = dPs[i * LDP + lane];
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float yv = __shfl_up(x, off);
+                if (lane >= off) x += yv;
+            }
+            // shift, not subtract: the diagonal term must not enter the prefix
+            float xe = __shfl_up(x, 1);
+            if (lane == 0) xe = 0.f;
+            dPs[i * LDP + lane] = xe;
+        }
+        __syncthreads();
+        {
+            float racc = 0.f;
+            for (int i = wave * 16; i < wave * 16 + 16; ++i)
+                if (i >= lane) racc += dPs[i * LDP + lane];
+            redR[wave][lane] = racc;
+        }
+
+        // <dS_out(c), S_in(c)>_F (dS_out is zero for the last chunk).
         float part = 0.f;
         if (c + 1 < NC) {
-            const float *Sn = states + (bh * NC + c + 1) * Epad;
             if ((E & 3) == 0) {
                 for (int64_t e = (int64_t)threadIdx.x * 4; e < E; e += NTH * 4) {
                     const float4 x = *reinterpret_cast<const float4 *>(dSo + e);
-                    const float4 z = *reinterpret_cast<const float4 *>(Sn + e);
+                    const float4 z = *reinterpret_cast<const float4 *>(Sin + e);
                     part += x.x * z.x + x.y * z.y + x.z * z.z + x.w * z.w;
                 }
             } else {
-                for (int64_t e = threadIdx.x; e < E; e += NTH) part += dSo[e] * Sn[e];
+                for (int64_t e = threadIdx.x; e < E; e += NTH) part += dSo[e] * Sin[e];
             }
         }
         part = sum64(part);
@@ -593,21 +629,27 @@ __global__ __launch_bounds__(NTH) void k_bwd_grads(
         __syncthreads();
 
         if (wave == 0) {
-            const float beta = (redB[0] + redB[1]) + (redB[2] + redB[3]);
-            float sq = 0.f, sk = 0.f;
+            const float fro = (redB[0] + redB[1]) + (redB[2] + redB[3]);
+            const float ebl = expf(bl[bh * NCp + c]);
+            float iq = 0.f, ik = 0.f;
 #pragma unroll
             for (int cb = 0; cb < NCBK; ++cb) {
-                sq += redQ[cb][lane];
-                sk += redK[cb][lane];
+                iq += redQ[cb][lane];
+                ik += redK[cb][lane];
             }
-            float x = sq - sk;
-            // inclusive suffix sum over the chunk's positions
+            const float rint = (redR[0][lane] + redR[1][lane]) + (redR[2][lane] + redR[3][lane]);
+            // inclusive suffix sum of iq, exclusive prefix sum of ik
+            float sq = iq, pk = ik;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
-                const float yv = __shfl_down(x, off);
-                if (lane + off < 64) x += yv;
+                const float a1 = __shfl_down(sq, off);
+                const float a2 = __shfl_up(pk, off);
+                if (lane + off < 64) sq += a1;
+                if (lane >= off) pk += a2;
             }
-            if (lane < rows) dla[bh * T + c * CH + lane] = x + beta;
+            float pke = __shfl_up(pk, 1);
+            if (lane == 0) pke = 0.f;
+            if (lane < rows) dla[bh * T + c * CH + lane] = rint + sq + pke + ebl * fro;
         }
         __syncthreads();
     }

@@ -54,11 +54,9 @@ def kernel_work(s):
     states = 4 * s.B * s.H * NC * E
     return {
         "chunk_cumsum": ("hbm", 4 * N + 4 * s.B * s.H * NC * 64 + 4 * s.B * s.H * NC, "B"),
-        "chunk_state": ("mfma", N * 2 * E, "FLOP"),
-        "state_pass": ("hbm", 2 * states + 4 * s.B * s.H * E, "B"),
+        "state_scan": ("mfma", N * 2 * E, "FLOP"),
         "chunk_output": ("mfma", N * (C_NOM * (s.dk + s.dv) + 2 * E), "FLOP"),
-        "chunk_dstate": ("mfma", N * 2 * E, "FLOP"),
-        "state_pass_rev": ("hbm", 2 * states + 4 * s.B * s.H * E, "B"),
+        "state_scan_bidir": ("mfma", 2 * N * 2 * E, "FLOP"),
         "bwd_grads": ("mfma", N * (C_NOM * (3 * s.dk + 2 * s.dv) + 6 * E), "FLOP"),
     }
 

@@ -95,13 +95,13 @@ __device__ __forceinline__ float readlane_f(float x, int l)
 // Copy rows [0, rows) x cols [0, d) of a row-major global tile with row
 // stride d into LDS dst[CH][LD]; columns d..DP-1 and rows >= rows become 0.
 // Each row is optionally scaled by w[row] (LDS).
-template <int DP, int LD, bool SCALE>
+template <int DP, int LD, bool SCALE, int NT = NTH>
 __device__ __forceinline__ void stage_rows(float *dst, const float *__restrict__ src, int rows, int d,
                                            bool vec, const float *w)
 {
     if (vec) {
         constexpr int Q4 = DP / 4;
-        for (int idx = threadIdx.x; idx < CH * Q4; idx += NTH) {
+        for (int idx = threadIdx.x; idx < CH * Q4; idx += NT) {
             const int t = idx / Q4, c4 = (idx - t * Q4) * 4;
             float4 val = make_float4(0.f, 0.f, 0.f, 0.f);
             if (t < rows && c4 < d) val = *reinterpret_cast<const float4 *>(src + (size_t)t * d + c4);
@@ -119,7 +119,7 @@ __device__ __forceinline__ void stage_rows(float *dst, const float *__restrict__
             p[3] = val.w;
         }
     } else {
-        for (int idx = threadIdx.x; idx < CH * DP; idx += NTH) {
+        for (int idx = threadIdx.x; idx < CH * DP; idx += NT) {
             const int t = idx / DP, cc = idx - t * DP;
             float val = (t < rows && cc < d) ? src[(size_t)t * d + cc] : 0.f;
             if (SCALE) val *= w[t];
@@ -153,164 +153,310 @@ __global__ __launch_bounds__(NTH) void k_chunk_cumsum(const float *__restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// K3 (MODE 0): X_c = K^T diag(e^{b_L - b}) V  (dk x dv), the chunk's own
-//              contribution to the outgoing state.
-// B1 (MODE 1): Z_c = Q^T diag(e^{b}) dY      (dk x dv), the chunk's own
-//              contribution to the gradient of the incoming state.
-// One block per (b,h,chunk); the 32x32 output tiles are spread over the four
-// waves; the contraction over the 64 chunk positions reads both operands
-// from LDS.
-template <int DKP, int DVP, int MODE>
-__global__ __launch_bounds__(NTH) void k_chunk_state(const float *__restrict__ Ag, const float *__restrict__ Bg,
-                                                     const float *__restrict__ bcum, const float *__restrict__ bl,
-                                                     float *__restrict__ states, int G, int H, int64_t T, int dk,
-                                                     int dv, int64_t NC, int64_t NCp, int64_t Epad, int vecA,
-                                                     int vecB)
+// Helpers for the 8-wave kernels.
+
+constexpr int NTW = 512;   // 8 waves per block
+
+__device__ __forceinline__ float4 zero4() { return make_float4(0.f, 0.f, 0.f, 0.f); }
+
+// p[c4 .. c4+3] of a row with `lim` valid entries (the rest read as 0).
+// vec: one aligned 16-byte load (requires lim % 4 == 0 and an aligned row).
+__device__ __forceinline__ float4 load4(const float *__restrict__ p, int c4, int lim, bool vec)
 {
-    constexpr int LDA = DKP, LDB = DVP;
-    __shared__ float As[CH * LDA];
-    __shared__ float Bs[CH * LDB];
-    __shared__ float w[CH];
+    if (vec) return (c4 < lim) ? *reinterpret_cast<const float4 *>(p + c4) : zero4();
+    float4 r;
+    r.x = (c4 + 0 < lim) ? p[c4 + 0] : 0.f;
+    r.y = (c4 + 1 < lim) ? p[c4 + 1] : 0.f;
+    r.z = (c4 + 2 < lim) ? p[c4 + 2] : 0.f;
+    r.w = (c4 + 3 < lim) ? p[c4 + 3] : 0.f;
+    return r;
+}
 
-    const int64_t c = blockIdx.x % NC;
-    const int64_t bh = blockIdx.x / NC;
-    const int h = (int)(bh % H);
-    const int64_t b = bh / H;
-    const int g = h / (H / G);
-    const int rows = (int)((T - c * CH) < CH ? (T - c * CH) : CH);
-    const float *a_src = Ag + ((b * G + g) * T + c * CH) * dk;
-    const float *b_src = Bg + (bh * T + c * CH) * dv;
-
-    if (threadIdx.x < CH) {
-        const int t = threadIdx.x;
-        const float bt = bcum[bh * NC * CH + c * CH + t];
-        const float wt = (MODE == 0) ? expf(bl[bh * NCp + c] - bt) : expf(bt);
-        w[t] = (t < rows) ? wt : 0.f;
+// Load a ROWS x DP tile (row-major, row stride d, `nrows` valid rows, d valid
+// columns) into registers, PER float4 per thread, zero padded.
+template <int ROWS, int DP, int NT, int PER>
+__device__ __forceinline__ void tile_to_regs(float4 (&buf)[PER], const float *__restrict__ src, int nrows, int d,
+                                             bool vec)
+{
+    constexpr int Q4 = DP / 4;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+        const int idx = threadIdx.x + u * NT;
+        const int r = idx / Q4, c4 = (idx - r * Q4) * 4;
+        buf[u] = (idx < ROWS * Q4 && r < nrows) ? load4(src + (size_t)r * d, c4, d, vec) : zero4();
     }
-    stage_rows<DKP, LDA, false>(As, a_src, rows, dk, vecA != 0, nullptr);
-    __syncthreads();
-    stage_rows<DVP, LDB, true>(Bs, b_src, rows, dv, vecB != 0, w);
-    __syncthreads();
+}
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int cl = lane & 31, kh = lane >> 5;
-    constexpr int NIB = DKP / 32, NJB = DVP / 32, NBLK = NIB * NJB, NBW = (NBLK + 3) / 4;
-    f32x16 acc[NBW];
+// Store a register tile (see tile_to_regs) into LDS dst[ROWS][LD].
+template <int ROWS, int DP, int NT, int PER, int LD>
+__device__ __forceinline__ void regs_to_lds(const float4 (&buf)[PER], float *dst)
+{
+    constexpr int Q4 = DP / 4;
 #pragma unroll
-    for (int j = 0; j < NBW; ++j) acc[j] = zero16();
-
-#pragma unroll 4
-    for (int k = 0; k < CH; k += 2) {
-        const int kr = k + kh;
-#pragma unroll
-        for (int j = 0; j < NBW; ++j) {
-            const int blk = wave + 4 * j;
-            if (blk < NBLK) {
-                const int ib = blk / NJB, jb = blk % NJB;
-                acc[j] = mfma32(As[kr * LDA + ib * 32 + cl], Bs[kr * LDB + jb * 32 + cl], acc[j]);
-            }
-        }
-    }
-
-    float *dst = states + (bh * NC + c) * Epad;
-#pragma unroll
-    for (int j = 0; j < NBW; ++j) {
-        const int blk = wave + 4 * j;
-        if (blk < NBLK) {
-            const int ib = blk / NJB, jb = blk % NJB;
-            const int n = jb * 32 + cl;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int i = ib * 32 + acc_row(r, lane);
-                if (i < dk && n < dv) dst[i * dv + n] = acc[j][r];
+    for (int u = 0; u < PER; ++u) {
+        const int idx = threadIdx.x + u * NT;
+        if (idx < ROWS * Q4) {
+            const int r = idx / Q4, c4 = (idx - r * Q4) * 4;
+            if (LD % 4 == 0) {
+                *reinterpret_cast<float4 *>(dst + r * LD + c4) = buf[u];
+            } else {
+                float *pp = dst + r * LD + c4;
+                pp[0] = buf[u].x;
+                pp[1] = buf[u].y;
+                pp[2] = buf[u].z;
+                pp[3] = buf[u].w;
             }
         }
     }
 }
 
-// ---------------------------------------------------------------------------
-// K4 / B2: sequential pass over chunks, in place over the per-chunk slabs.
-// Forward (REV = false):  S = h0;  for c = 0..NC-1:  x = slab[c]; slab[c] = S;
-//                         S = e^{b_L(c)} S + x.       (slab[c] becomes S_in(c))
-// Reverse (REV = true):   S = 0;   for c = NC-1..0:  z = slab[c]; slab[c] = S;
-//                         S = e^{b_L(c)} S + z;  fin = S at the end.
-//                         (slab[c] becomes dS_out(c), fin = dh0)
-// Each thread carries 4 consecutive state elements through every chunk; the
-// per-chunk decays are loaded 64 at a time (one per lane) and broadcast with
-// readlane.  Loads of 16 chunks are issued before their stores.
-template <bool REV>
-__global__ __launch_bounds__(NTH) void k_state_pass(float *__restrict__ states, const float *__restrict__ bl,
-                                                    const float *__restrict__ init, float *__restrict__ fin,
-                                                    int64_t NC, int64_t NCp, int64_t E, int64_t Epad,
-                                                    int64_t blocks_per_bh)
+// acc += A * B over k in [0, KP), with A(i, k) = As[(rbase + i) * LDA + k]
+// (LDS) and B(k, j) = S[j][k] read from global memory, S row-major with row
+// stride `ld`, rows j >= limj and columns k >= limk reading as 0.  Lane
+// (j, h) loads S[j][k0 + 4h .. k0 + 4h + 3] as one float4 and feeds it to
+// four MFMAs; A is read at the matching permuted k.
+template <int KP, int LDA>
+__device__ __forceinline__ void mma_bt_global(f32x16 &acc, const float *As, int rbase, const float *__restrict__ S,
+                                              int j, int limj, int limk, int ld, bool vec, int lane)
 {
-    constexpr int BATCH = 16;
-    const int64_t bh = blockIdx.x / blocks_per_bh;
-    const int64_t e0 = ((blockIdx.x - bh * blocks_per_bh) * NTH + threadIdx.x) * 4;
-    const bool active = e0 < Epad;
-    const int lane = threadIdx.x & 63;
-    float *base = states + bh * NC * Epad + e0;
+    const int cl = lane & 31, kh = lane >> 5;
+    const float *srow = S + (size_t)j * ld;
+    const bool ok = j < limj;
+    const float *arow = As + (rbase + cl) * LDA + 4 * kh;
+#pragma unroll 2
+    for (int k0 = 0; k0 < KP; k0 += 8) {
+        const float4 f = ok ? load4(srow, k0 + 4 * kh, limk, vec) : zero4();
+        acc = mfma32(arow[k0 + 0], f.x, acc);
+        acc = mfma32(arow[k0 + 1], f.y, acc);
+        acc = mfma32(arow[k0 + 2], f.z, acc);
+        acc = mfma32(arow[k0 + 3], f.w, acc);
+    }
+}
 
-    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-    if (!REV && init && active) {
-        const float *ip = init + bh * E + e0;
-        if (e0 + 0 < E) s0 = ip[0];
-        if (e0 + 1 < E) s1 = ip[1];
-        if (e0 + 2 < E) s2 = ip[2];
-        if (e0 + 3 < E) s3 = ip[3];
+// acc += A * B over k in [0, KP), with A(i, k) = As[(rbase + i) * LDA + k]
+// (LDS) and B(k, j) = S[k][j] read from global memory (row stride ld, rows
+// k >= limk and columns j >= limj reading as 0).  Lanes read consecutive j.
+template <int KP, int LDA>
+__device__ __forceinline__ void mma_b_global(f32x16 &acc, const float *As, int rbase, const float *__restrict__ S,
+                                             int j, int limj, int limk, int ld, int lane)
+{
+    const int cl = lane & 31, kh = lane >> 5;
+    const bool ok = j < limj;
+    const float *arow = As + (rbase + cl) * LDA + kh;
+#pragma unroll 8
+    for (int k0 = 0; k0 < KP; k0 += 2) {
+        const int kk = k0 + kh;
+        const float sv = (ok && kk < limk) ? S[(size_t)kk * ld + j] : 0.f;
+        acc = mfma32(arow[k0], sv, acc);
+    }
+}
+
+// Q K^T tiles of a chunk (causal 32x32 tiles (0,0), (1,0), (1,1)), the dk
+// contraction split over six waves: waves 0-2 end up holding the full tile
+// (w % 3), the partial sums of waves 3-5 pass through `scratch` (3 x 1024).
+template <int DKP, int LDQ, int LDK>
+__device__ __forceinline__ f32x16 qk_tiles(const float *Qs, const float *Ks, float *scratch, int wave, int lane)
+{
+    const int cl = lane & 31, kh = lane >> 5;
+    const int tile = wave % 3, half = wave / 3;
+    const int ib = (tile == 0) ? 0 : 1, jb = (tile == 2) ? 1 : 0;
+    f32x16 acc = zero16();
+    if (wave < 6) {
+        const int k0 = half * (DKP / 2);
+#pragma unroll 8
+        for (int kk = k0; kk < k0 + DKP / 2; kk += 2)
+            acc = mfma32(Qs[(ib * 32 + cl) * LDQ + kk + kh], Ks[(jb * 32 + cl) * LDK + kk + kh], acc);
+        if (wave >= 3) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) scratch[tile * 1024 + r * 64 + lane] = acc[r];
+        }
+    }
+    __syncthreads();
+    if (wave < 3) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] += scratch[tile * 1024 + r * 64 + lane];
+    }
+    __syncthreads();
+    return acc;
+}
+
+// ---------------------------------------------------------------------------
+// K3 + K4 fused: sequential scan over chunks with the state held in MFMA
+// accumulators (v_mfma_f32_16x16x4f32: lane l supplies A[l%16][l/16] and
+// B[l/16][l%16]; accumulator r of lane l is row 4*(l/16) + r, column l%16).
+//
+//   forward (dir 0):  S = h0;  for c = 0 .. NC-1:
+//                       slab[c] = S;  S = e^{b_L(c)} S + K_c^T diag(e^{b_L - b}) V_c
+//   reverse (dir 1):  S = 0;   for c = NC-1 .. 0:
+//                       slab[c] = S;  S = e^{b_L(c)} S + Q_c^T diag(e^{b}) dY_c
+//                     dh0 = S
+//
+// so the forward slabs hold S_in(c), the state entering chunk c, and the
+// reverse slabs hold dS_out(c), the gradient of the state leaving chunk c.
+// The chunk's own contribution is formed on the fly and never stored.
+// One block of 4 waves owns a 32 x TJ tile of one head's dk x dv state; the
+// next chunk's operand tiles are prefetched into registers while the current
+// chunk's MFMAs run, then written to the other half of a double-buffered LDS
+// tile.  Blocks of one (b, g) are placed on one XCD so that the group's q/k
+// and each head's v/dy tiles are shared through that XCD's L2.
+constexpr int TI = 32;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma16(float a, float b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+template <int DKP, int DVP>
+__global__ __launch_bounds__(NTH) void k_state_scan(
+    const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
+    const float *__restrict__ dy, const float *__restrict__ h0, const float *__restrict__ bcum,
+    const float *__restrict__ bl, float *__restrict__ states, float *__restrict__ dstates,
+    float *__restrict__ dh0, int G, int H, int64_t T, int dk, int dv, int64_t NC, int64_t NCp, int64_t Epad,
+    int64_t per_dir, int vecK, int vecV)
+{
+    constexpr int TJ = DVP < 64 ? DVP : 64;
+    constexpr int NTJ = DVP / TJ;
+    constexpr int NTILE = (DKP / TI) * NTJ;
+    constexpr int LDA = TI + 16, LDB = TJ + 16;
+    constexpr int A4 = CH * TI / 4, B4 = CH * TJ / 4;
+    constexpr int APER = (A4 + NTH - 1) / NTH, BPER = (B4 + NTH - 1) / NTH;
+    constexpr int NB16 = (2 * (TJ / 16)) / 4;   // 16x16 accumulator tiles per wave
+    __shared__ __attribute__((aligned(16))) float As[2][CH * LDA];
+    __shared__ __attribute__((aligned(16))) float Bs[2][CH * LDB];
+
+    // XCD-aware order: consecutive logical blocks share blockIdx % 8.
+    const int64_t nblk = gridDim.x;
+    int64_t L = blockIdx.x;
+    if ((nblk & 7) == 0) L = (int64_t)(blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
+    const int dir = (int)(L / per_dir);
+    const int64_t rem = L - dir * per_dir;
+    const int64_t bh = rem / NTILE;
+    const int tile = (int)(rem - bh * NTILE);
+    const int i0 = (tile / NTJ) * TI, j0 = (tile % NTJ) * TJ;
+    const int h = (int)(bh % H);
+    const int64_t b = bh / H;
+    const int g = h / (H / G);
+    const float *Asrc = (dir == 0 ? k : q) + (b * G + g) * T * dk + i0;
+    const float *Bsrc = (dir == 0 ? v : dy) + bh * T * dv + j0;
+    float *slab = (dir == 0 ? states : dstates) + bh * NC * Epad;
+    const float *bcb = bcum + bh * NC * CH;
+    const int lima = dk - i0, limb = dv - j0;
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int l16 = lane & 15, q4 = lane >> 4;
+    const int rblk = wave & 1;                 // 16-row block of the tile
+    const int cblk0 = (wave >> 1) * NB16;      // first 16-column block
+
+    // operand prefetch for one chunk
+    float4 abuf[APER], bbuf[BPER];
+    float bt[BPER], blc = 0.f;
+    auto prefetch = [&](int64_t c) {
+        const int rows = (int)((T - c * CH) < CH ? (T - c * CH) : CH);
+#pragma unroll
+        for (int u = 0; u < APER; ++u) {
+            const int idx = threadIdx.x + u * NTH;
+            const int r = idx / (TI / 4), c4 = (idx - r * (TI / 4)) * 4;
+            abuf[u] = (idx < A4 && r < rows) ? load4(Asrc + (c * CH + r) * dk, c4, lima, vecK != 0) : zero4();
+        }
+#pragma unroll
+        for (int u = 0; u < BPER; ++u) {
+            const int idx = threadIdx.x + u * NTH;
+            const int r = idx / (TJ / 4), c4 = (idx - r * (TJ / 4)) * 4;
+            bbuf[u] = (idx < B4 && r < rows) ? load4(Bsrc + (c * CH + r) * dv, c4, limb, vecV != 0) : zero4();
+            bt[u] = (idx < B4) ? bcb[c * CH + r] : 0.f;
+        }
+        blc = bl[bh * NCp + c];
+    };
+
+    f32x4 acc[NB16];
+#pragma unroll
+    for (int u = 0; u < NB16; ++u) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = i0 + rblk * 16 + 4 * q4 + r, col = j0 + (cblk0 + u) * 16 + l16;
+            acc[u][r] = (dir == 0 && row < dk && col < dv) ? h0[bh * (int64_t)dk * dv + (int64_t)row * dv + col] : 0.f;
+        }
     }
 
-    for (int64_t g0 = 0; g0 < NC; g0 += 64) {
-        const int cnt = (int)((NC - g0) < 64 ? (NC - g0) : 64);
-        float dl = 0.f;
-        if (lane < cnt) {
-            const int64_t cc = REV ? NC - 1 - (g0 + lane) : g0 + lane;
-            dl = expf(bl[bh * NCp + cc]);
+    prefetch(dir == 0 ? 0 : NC - 1);
+    for (int64_t s = 0; s < NC; ++s) {
+        const int64_t c = (dir == 0) ? s : NC - 1 - s;
+        const int buf = (int)(s & 1);
+        // stage this chunk's operands; scale B rows by the decay weights
+#pragma unroll
+        for (int u = 0; u < APER; ++u) {
+            const int idx = threadIdx.x + u * NTH;
+            if (idx < A4) {
+                const int r = idx / (TI / 4), c4 = (idx - r * (TI / 4)) * 4;
+                *reinterpret_cast<float4 *>(&As[buf][r * LDA + c4]) = abuf[u];
+            }
         }
-        for (int j0 = 0; j0 < cnt; j0 += BATCH) {
-            float4 x[BATCH];
 #pragma unroll
-            for (int u = 0; u < BATCH; ++u) {
-                const int j = j0 + u;
-                if (j < cnt && active) {
-                    const int64_t cc = REV ? NC - 1 - (g0 + j) : g0 + j;
-                    x[u] = *reinterpret_cast<const float4 *>(base + cc * Epad);
-                }
+        for (int u = 0; u < BPER; ++u) {
+            const int idx = threadIdx.x + u * NTH;
+            if (idx < B4) {
+                const int r = idx / (TJ / 4), c4 = (idx - r * (TJ / 4)) * 4;
+                const float w = (dir == 0) ? expf(blc - bt[u]) : expf(bt[u]);
+                float4 x = bbuf[u];
+                x.x *= w;
+                x.y *= w;
+                x.z *= w;
+                x.w *= w;
+                *reinterpret_cast<float4 *>(&Bs[buf][r * LDB + c4]) = x;
             }
+        }
+        const float decay = expf(blc);
+        if (s + 1 < NC) prefetch(dir == 0 ? c + 1 : c - 1);
+        __syncthreads();
+
+        // slab[c] = S (state entering the chunk in this direction)
+        float *dst = slab + c * Epad;
 #pragma unroll
-            for (int u = 0; u < BATCH; ++u) {
-                const int j = j0 + u;
-                if (j < cnt) {
-                    const float d = readlane_f(dl, j);
-                    if (active) {
-                        const int64_t cc = REV ? NC - 1 - (g0 + j) : g0 + j;
-                        *reinterpret_cast<float4 *>(base + cc * Epad) = make_float4(s0, s1, s2, s3);
-                        s0 = d * s0 + x[u].x;
-                        s1 = d * s1 + x[u].y;
-                        s2 = d * s2 + x[u].z;
-                        s3 = d * s3 + x[u].w;
-                    }
-                }
+        for (int u = 0; u < NB16; ++u) {
+            const int col = j0 + (cblk0 + u) * 16 + l16;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = i0 + rblk * 16 + 4 * q4 + r;
+                if (row < dk && col < dv) dst[row * dv + col] = acc[u][r];
+                acc[u][r] *= decay;
             }
+        }
+        // S += A^T B over the chunk's 64 positions
+        const float *Ab = &As[buf][q4 * LDA + rblk * 16 + l16];
+        const float *Bb = &Bs[buf][q4 * LDB + cblk0 * 16 + l16];
+#pragma unroll 4
+        for (int kk = 0; kk < CH; kk += 4) {
+            const float a = Ab[kk * LDA];
+#pragma unroll
+            for (int u = 0; u < NB16; ++u) acc[u] = mfma16(a, Bb[kk * LDB + u * 16], acc[u]);
         }
     }
-    if (REV && fin && active) {
-        float *fp = fin + bh * E + e0;
-        if (e0 + 0 < E) fp[0] = s0;
-        if (e0 + 1 < E) fp[1] = s1;
-        if (e0 + 2 < E) fp[2] = s2;
-        if (e0 + 3 < E) fp[3] = s3;
+    if (dir == 1) {
+#pragma unroll
+        for (int u = 0; u < NB16; ++u) {
+            const int col = j0 + (cblk0 + u) * 16 + l16;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = i0 + rblk * 16 + 4 * q4 + r;
+                if (row < dk && col < dv) dh0[bh * (int64_t)dk * dv + (int64_t)row * dv + col] = acc[u][r];
+            }
+        }
     }
 }
 
 // ---------------------------------------------------------------------------
 // K2 + K5: output of one chunk for every head of one group.
-// One block per (b,g,chunk).  Q K^T (causal 32x32 tiles only) is formed once
-// and kept in registers; per head it is masked and decayed into P (LDS),
-// then Y = P V + diag(e^b) (Q S_in) with V staged in LDS and S_in read from
-// the state slabs.
+// One block of 8 waves per (b,g,chunk).  Q K^T (causal 32x32 tiles) is
+// formed once and kept in registers.  Per head: the next head's V tile and
+// incoming state S_in are prefetched into registers while this head runs;
+// P = (Q K^T) o D goes to LDS; then each wave computes one 32x32 tile of
+// Y = P V + diag(e^b) (Q S_in) with every operand read from LDS.  For dv < 128
+// the Q S_in contraction is split over the spare waves and summed in a fixed
+// order.
 template <int DKP, int DVP>
-__global__ __launch_bounds__(NTH) void k_chunk_output(const float *__restrict__ q, const float *__restrict__ k,
+__global__ __launch_bounds__(NTW) void k_chunk_output(const float *__restrict__ q, const float *__restrict__ k,
                                                       const float *__restrict__ v, const float *__restrict__ bcum,
                                                       const float *__restrict__ states, float *__restrict__ y,
                                                       int G, int H, int64_t T, int dk, int dv, int64_t NC,
@@ -319,9 +465,14 @@ __global__ __launch_bounds__(NTH) void k_chunk_output(const float *__restrict__ 
     constexpr int LDQ = DKP + 1;
     constexpr int LDKV = (DKP > DVP ? DKP : DVP) + 1;
     constexpr int LDP = CH + 1;
+    constexpr int NCB = DVP / 32, NOB = 2 * NCB, KS = 8 / NOB;
+    constexpr int VPER = (CH * DVP / 4 + NTW - 1) / NTW;
+    constexpr int SPER = (DKP * DVP / 4 + NTW - 1) / NTW;
     __shared__ float Qs[CH * LDQ];
     __shared__ float KVs[CH * LDKV];
+    __shared__ __attribute__((aligned(16))) float Ss[DKP * DVP];
     __shared__ float Ps[CH * LDP];
+    __shared__ float Red[KS > 1 ? (KS - 1) * NOB * 1024 : 1];
     __shared__ float bs[CH], eb[CH];
 
     const int64_t c = blockIdx.x % NC;
@@ -329,34 +480,39 @@ __global__ __launch_bounds__(NTH) void k_chunk_output(const float *__restrict__ 
     const int g = (int)(bg % G);
     const int64_t b = bg / G;
     const int hpg = H / G;
+    const int64_t bh0 = b * H + (int64_t)g * hpg;
     const int rows = (int)((T - c * CH) < CH ? (T - c * CH) : CH);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int cl = lane & 31, kh = lane >> 5;
 
-    stage_rows<DKP, LDQ, false>(Qs, q + (bg * T + c * CH) * dk, rows, dk, vecK != 0, nullptr);
-    stage_rows<DKP, LDKV, false>(KVs, k + (bg * T + c * CH) * dk, rows, dk, vecK != 0, nullptr);
+    float4 vbuf[VPER], sbuf[SPER];
+    float bpre = 0.f;
+    auto prefetch = [&](int hh) {
+        const int64_t bh = bh0 + hh;
+        tile_to_regs<CH, DVP, NTW, VPER>(vbuf, v + (bh * T + c * CH) * dv, rows, dv, vecV != 0);
+        tile_to_regs<DKP, DVP, NTW, SPER>(sbuf, states + (bh * NC + c) * Epad, dk, dv, vecV != 0);
+        if (threadIdx.x < CH) bpre = bcum[bh * NC * CH + c * CH + threadIdx.x];
+    };
+    prefetch(0);
+
+    stage_rows<DKP, LDQ, false, NTW>(Qs, q + (bg * T + c * CH) * dk, rows, dk, vecK != 0, nullptr);
+    stage_rows<DKP, LDKV, false, NTW>(KVs, k + (bg * T + c * CH) * dk, rows, dk, vecK != 0, nullptr);
     __syncthreads();
+    const f32x16 accA = qk_tiles<DKP, LDQ, LDKV>(Qs, KVs, Ps, wave, lane);
+    const int ib = (wave == 0) ? 0 : 1, jb = (wave == 2) ? 1 : 0;
 
-    // Causal tiles of Q K^T: wave 0 -> (0,0), wave 1 -> (1,0), wave 2 -> (1,1).
-    const int ib = (wave == 0) ? 0 : 1;
-    const int jb = (wave == 2) ? 1 : 0;
-    f32x16 accA = zero16();
-    if (wave < 3) {
-#pragma unroll 8
-        for (int kk = 0; kk < DKP; kk += 2)
-            accA = mfma32(Qs[(ib * 32 + cl) * LDQ + kk + kh], KVs[(jb * 32 + cl) * LDKV + kk + kh], accA);
-    }
-    __syncthreads();   // K no longer needed; its LDS holds V from here on
-
-    constexpr int NCB = DVP / 32, NOB = 2 * NCB, NBW = (NOB + 3) / 4;
+    const int ob = wave % NOB, ks = wave / NOB;
+    const int rb = ob / NCB, cb = ob % NCB;
+    const int n = cb * 32 + cl;
     for (int hh = 0; hh < hpg; ++hh) {
-        const int64_t bh = b * H + (int64_t)g * hpg + hh;
+        const int64_t bh = bh0 + hh;
+        regs_to_lds<CH, DVP, NTW, VPER, LDKV>(vbuf, KVs);
+        regs_to_lds<DKP, DVP, NTW, SPER, DVP>(sbuf, Ss);
         if (threadIdx.x < CH) {
-            const float bt = bcum[bh * NC * CH + c * CH + threadIdx.x];
-            bs[threadIdx.x] = bt;
-            eb[threadIdx.x] = expf(bt);
+            bs[threadIdx.x] = bpre;
+            eb[threadIdx.x] = expf(bpre);
         }
-        stage_rows<DVP, LDKV, false>(KVs, v + (bh * T + c * CH) * dv, rows, dv, vecV != 0, nullptr);
+        if (hh + 1 < hpg) prefetch(hh + 1);
         __syncthreads();
         if (wave < 3) {
 #pragma unroll
@@ -367,30 +523,37 @@ __global__ __launch_bounds__(NTH) void k_chunk_output(const float *__restrict__ 
         }
         __syncthreads();
 
-        const float *st = states + (bh * NC + c) * Epad;
-#pragma unroll
-        for (int jw = 0; jw < NBW; ++jw) {
-            const int ob = wave + 4 * jw;
-            if (ob < NOB) {
-                const int rb = ob / NCB, cb = ob % NCB;
-                const int n = cb * 32 + cl;
-                f32x16 ay = zero16(), ai = zero16();
-                const int kend = (rb + 1) * 32;
-                for (int kk = 0; kk < kend; kk += 2)
-                    ay = mfma32(Ps[(rb * 32 + cl) * LDP + kk + kh], KVs[(kk + kh) * LDKV + n], ay);
+        f32x16 ay = zero16(), ai = zero16();
+        if (ks == 0) {
+            const int kend = (rb + 1) * 32;
+            for (int kk = 0; kk < kend; kk += 2)
+                ay = mfma32(Ps[(rb * 32 + cl) * LDP + kk + kh], KVs[(kk + kh) * LDKV + n], ay);
+        }
+        {
+            constexpr int KL = DKP / KS;
+            const int i0 = ks * KL;
 #pragma unroll 8
-                for (int i = 0; i < DKP; i += 2) {
-                    const int ii = i + kh;
-                    const float sv = (ii < dk && n < dv) ? st[ii * dv + n] : 0.f;
-                    ai = mfma32(Qs[(rb * 32 + cl) * LDQ + ii], sv, ai);
-                }
-                if (n < dv) {
+            for (int i = i0; i < i0 + KL; i += 2)
+                ai = mfma32(Qs[(rb * 32 + cl) * LDQ + i + kh], Ss[(i + kh) * DVP + n], ai);
+        }
+        if (KS > 1) {
+            if (ks > 0) {
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int row = rb * 32 + acc_row(r, lane);
-                        if (row < rows) y[(bh * T + c * CH + row) * dv + n] = ay[r] + eb[row] * ai[r];
-                    }
+                for (int r = 0; r < 16; ++r) Red[((ks - 1) * NOB + ob) * 1024 + r * 64 + lane] = ai[r];
+            }
+            __syncthreads();
+            if (ks == 0) {
+                for (int kk2 = 1; kk2 < KS; ++kk2) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) ai[r] += Red[((kk2 - 1) * NOB + ob) * 1024 + r * 64 + lane];
                 }
+            }
+        }
+        if (ks == 0 && n < dv) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = rb * 32 + acc_row(r, lane);
+                if (row < rows) y[(bh * T + c * CH + row) * dv + n] = ay[r] + eb[row] * ai[r];
             }
         }
         __syncthreads();
@@ -399,10 +562,13 @@ __global__ __launch_bounds__(NTH) void k_chunk_output(const float *__restrict__ 
 
 // ---------------------------------------------------------------------------
 // B3 + B4: gradients of one chunk for every head of one group.
-// One block per (b,g,chunk).  dq and dk are summed over the group's heads in
-// registers (ascending head order); dv and dlog_alpha are written per head.
+// One block of 8 waves per (b,g,chunk).  dq and dk are summed over the
+// group's heads in registers (ascending head order); dv and dlog_alpha are
+// written per head.  The next head's V and dY tiles are prefetched into
+// registers while this head runs; the incoming state S_in and the outgoing
+// state gradient dS_out are read from the workspace slabs as MFMA operands.
 template <int DKP, int DVP>
-__global__ __launch_bounds__(NTH) void k_bwd_grads(
+__global__ __launch_bounds__(NTW) void k_bwd_grads(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
     const float *__restrict__ dy, const float *__restrict__ bcum, const float *__restrict__ bl,
     const float *__restrict__ states, const float *__restrict__ dstates, float *__restrict__ dq,
@@ -413,8 +579,9 @@ __global__ __launch_bounds__(NTH) void k_bwd_grads(
     constexpr int LDY = DVP + 1;
     constexpr int LDV = (DVP > CH ? DVP : CH) + 1;   // holds V, later P (C x C)
     constexpr int LDP = CH + 1;
-    constexpr int NCBK = DKP / 32, NOBK = 2 * NCBK, NBWK = (NOBK + 3) / 4;
-    constexpr int NCBV = DVP / 32, NOBV = 2 * NCBV, NBWV = (NOBV + 3) / 4;
+    constexpr int NCBK = DKP / 32, NOBK = 2 * NCBK;
+    constexpr int NCBV = DVP / 32, NOBV = 2 * NCBV;
+    constexpr int VPER = (CH * DVP / 4 + NTW - 1) / NTW;
     __shared__ float Qs[CH * LDK];
     __shared__ float Ks[CH * LDK];
     __shared__ float dYs[CH * LDY];
@@ -422,130 +589,121 @@ __global__ __launch_bounds__(NTH) void k_bwd_grads(
     __shared__ float dPs[CH * LDP];
     __shared__ float bs[CH], eb[CH], el[CH];
     __shared__ float redQ[NCBK][CH], redK[NCBK][CH];
-    __shared__ float redB[NTH / 64];
-    __shared__ float redR[NTH / 64][CH];
+    __shared__ float redR[NTW / 64][CH];
+    __shared__ float redB[NTW / 64];
 
     const int64_t c = blockIdx.x % NC;
     const int64_t bg = blockIdx.x / NC;
     const int g = (int)(bg % G);
     const int64_t b = bg / G;
     const int hpg = H / G;
+    const int64_t bh0 = b * H + (int64_t)g * hpg;
     const int rows = (int)((T - c * CH) < CH ? (T - c * CH) : CH);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int cl = lane & 31, kh = lane >> 5;
     const int64_t E = (int64_t)dk_ * dv_;
 
-    stage_rows<DKP, LDK, false>(Qs, q + (bg * T + c * CH) * dk_, rows, dk_, vecK != 0, nullptr);
-    stage_rows<DKP, LDK, false>(Ks, k + (bg * T + c * CH) * dk_, rows, dk_, vecK != 0, nullptr);
+    float4 vbuf[VPER], ybuf[VPER];
+    float bpre = 0.f, blpre = 0.f;
+    auto prefetch = [&](int hh) {
+        const int64_t bh = bh0 + hh;
+        tile_to_regs<CH, DVP, NTW, VPER>(vbuf, v + (bh * T + c * CH) * dv_, rows, dv_, vecV != 0);
+        tile_to_regs<CH, DVP, NTW, VPER>(ybuf, dy + (bh * T + c * CH) * dv_, rows, dv_, vecV != 0);
+        if (threadIdx.x < CH) {
+            bpre = bcum[bh * NC * CH + c * CH + threadIdx.x];
+            blpre = bl[bh * NCp + c];
+        }
+    };
+    prefetch(0);
+
+    stage_rows<DKP, LDK, false, NTW>(Qs, q + (bg * T + c * CH) * dk_, rows, dk_, vecK != 0, nullptr);
+    stage_rows<DKP, LDK, false, NTW>(Ks, k + (bg * T + c * CH) * dk_, rows, dk_, vecK != 0, nullptr);
     __syncthreads();
+    const f32x16 accA = qk_tiles<DKP, LDK, LDK>(Qs, Ks, dPs, wave, lane);
+    const int tile = wave % 3, half = wave / 3;
+    const int ib = (tile == 0) ? 0 : 1, jb = (tile == 2) ? 1 : 0;
 
-    const int ib = (wave == 0) ? 0 : 1;
-    const int jb = (wave == 2) ? 1 : 0;
-    f32x16 accA = zero16();
-    if (wave < 3) {
-#pragma unroll 8
-        for (int kk = 0; kk < DKP; kk += 2)
-            accA = mfma32(Qs[(ib * 32 + cl) * LDK + kk + kh], Ks[(jb * 32 + cl) * LDK + kk + kh], accA);
-    }
-
-    f32x16 dQacc[NBWK], dKacc[NBWK];
-#pragma unroll
-    for (int j = 0; j < NBWK; ++j) {
-        dQacc[j] = zero16();
-        dKacc[j] = zero16();
-    }
+    // output tile of this wave for dq/dk (C x dk) and dv (C x dv)
+    const int rbk = wave / NCBK, cbk = wave % NCBK, colk = cbk * 32 + cl;
+    const int rbv = wave / NCBV, cbv = wave % NCBV, colv = cbv * 32 + cl;
+    const bool hasK = wave < NOBK, hasV = wave < NOBV;
+    f32x16 dQacc = zero16(), dKacc = zero16();
 
     for (int hh = 0; hh < hpg; ++hh) {
-        const int64_t bh = b * H + (int64_t)g * hpg + hh;
+        const int64_t bh = bh0 + hh;
         const float *Sin = states + (bh * NC + c) * Epad;
         const float *dSo = dstates + (bh * NC + c) * Epad;
+        regs_to_lds<CH, DVP, NTW, VPER, LDV>(vbuf, VPs);
+        regs_to_lds<CH, DVP, NTW, VPER, LDY>(ybuf, dYs);
+        const float blh = blpre;   // chunk total of this head (threads < 64)
         if (threadIdx.x < CH) {
             const int t = threadIdx.x;
-            const float bt = bcum[bh * NC * CH + c * CH + t];
-            bs[t] = bt;
-            eb[t] = expf(bt);
-            el[t] = (t < rows) ? expf(bl[bh * NCp + c] - bt) : 0.f;
+            bs[t] = bpre;
+            eb[t] = expf(bpre);
+            el[t] = (t < rows) ? expf(blh - bpre) : 0.f;
         }
-        stage_rows<DVP, LDV, false>(VPs, v + (bh * T + c * CH) * dv_, rows, dv_, vecV != 0, nullptr);
-        stage_rows<DVP, LDY, false>(dYs, dy + (bh * T + c * CH) * dv_, rows, dv_, vecV != 0, nullptr);
+        if (hh + 1 < hpg) prefetch(hh + 1);
         __syncthreads();
 
-        // dP = (dY V^T) o D into LDS; P = (Q K^T) o D and M = P o (dY V^T)
-        // kept in registers.
+        // (1) state terms (operands from the workspace slabs) and, on six
+        //     waves, half-contractions of dY V^T.
+        f32x16 aQ = zero16(), aK = zero16(), aD = zero16();
+        if (wave < 6) {
+            const int n0 = half * (DVP / 2);
+#pragma unroll 4
+            for (int nn = n0; nn < n0 + DVP / 2; nn += 2)
+                aD = mfma32(dYs[(ib * 32 + cl) * LDY + nn + kh], VPs[(jb * 32 + cl) * LDV + nn + kh], aD);
+        }
+        if (hasK) {
+            // dY S_in^T : B(n, i) = S_in[i][n]
+            mma_bt_global<DVP, LDY>(aQ, dYs, rbk * 32, Sin, colk, dk_, dv_, dv_, vecV != 0, lane);
+            // V dS_out^T : B(n, i) = dS_out[i][n]
+            mma_bt_global<DVP, LDV>(aK, VPs, rbk * 32, dSo, colk, dk_, dv_, dv_, vecV != 0, lane);
+        }
+        __syncthreads();   // all reads of V done
+        if (wave >= 3 && wave < 6) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) VPs[tile * 1024 + r * 64 + lane] = aD[r];
+        }
+        __syncthreads();
         f32x16 pP = zero16(), pM = zero16();
         if (wave < 3) {
-            f32x16 a = zero16();
-#pragma unroll 8
-            for (int n = 0; n < DVP; n += 2)
-                a = mfma32(dYs[(ib * 32 + cl) * LDY + n + kh], VPs[(jb * 32 + cl) * LDV + n + kh], a);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
+                const float a = aD[r] + VPs[tile * 1024 + r * 64 + lane];
                 const int i = ib * 32 + acc_row(r, lane), j = jb * 32 + cl;
                 const float D = (j <= i) ? expf(bs[i] - bs[j]) : 0.f;
-                dPs[i * LDP + j] = a[r] * D;
+                dPs[i * LDP + j] = a * D;
                 pP[r] = accA[r] * D;
-                pM[r] = pP[r] * a[r];
+                pM[r] = pP[r] * a;
             }
         }
         __syncthreads();
 
-        // dQ_h = diag(e^b) dY S_in^T + dP K ; row sums of dQ_h o Q -> redQ.
+        // (2) dQ_h and dK_h; per-row state terms of dlog_alpha.
+        if (hasK) {
 #pragma unroll
-        for (int jw = 0; jw < NBWK; ++jw) {
-            const int ob = wave + 4 * jw;
-            if (ob < NOBK) {
-                const int rb = ob / NCBK, cb = ob % NCBK;
-                const int col = cb * 32 + cl;
-                f32x16 a = zero16();
-#pragma unroll 8
-                for (int n = 0; n < DVP; n += 2) {
-                    const int nn = n + kh;
-                    const float sv = (col < dk_ && nn < dv_) ? Sin[col * dv_ + nn] : 0.f;
-                    a = mfma32(dYs[(rb * 32 + cl) * LDY + nn], sv, a);
+            for (int r = 0; r < 16; ++r) {
+                const int row = rbk * 32 + acc_row(r, lane);
+                aQ[r] *= eb[row];
+                aK[r] *= el[row];
+                // e^{b_i} q_i.(dY S_in^T)_i and e^{b_L-b_j} k_j.(V dS_out^T)_j, partial over this column tile
+                const float sq = sum32(aQ[r] * Qs[row * LDK + colk]);
+                const float sk = sum32(aK[r] * Ks[row * LDK + colk]);
+                if (cl == 0) {
+                    redQ[cbk][row] = sq;
+                    redK[cbk][row] = sk;
                 }
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = rb * 32 + acc_row(r, lane);
-                    a[r] *= eb[row];
-                    // e^{b_i} q_i . (dY S_in^T)_i, partial over this column block
-                    const float s = sum32(a[r] * Qs[row * LDK + col]);
-                    if (cl == 0) redQ[cb][row] = s;
-                }
-                const int kend = (rb + 1) * 32;
-                for (int jj = 0; jj < kend; jj += 2)
-                    a = mfma32(dPs[(rb * 32 + cl) * LDP + jj + kh], Ks[(jj + kh) * LDK + col], a);
-                dQacc[jw] += a;
             }
+            const int kend = (rbk + 1) * 32;
+            for (int jj = 0; jj < kend; jj += 2)
+                aQ = mfma32(dPs[(rbk * 32 + cl) * LDP + jj + kh], Ks[(jj + kh) * LDK + colk], aQ);
+            for (int jj = rbk * 32; jj < CH; jj += 2)
+                aK = mfma32(dPs[(jj + kh) * LDP + rbk * 32 + cl], Qs[(jj + kh) * LDK + colk], aK);
+            dQacc += aQ;
+            dKacc += aK;
         }
-
-        // dK_h = diag(e^{bL-b}) V dS_out^T + dP^T Q ; row sums of dK_h o K -> redK.
-#pragma unroll
-        for (int jw = 0; jw < NBWK; ++jw) {
-            const int ob = wave + 4 * jw;
-            if (ob < NOBK) {
-                const int rb = ob / NCBK, cb = ob % NCBK;
-                const int col = cb * 32 + cl;
-                f32x16 a = zero16();
-#pragma unroll 8
-                for (int n = 0; n < DVP; n += 2) {
-                    const int nn = n + kh;
-                    const float sv = (col < dk_ && nn < dv_) ? dSo[col * dv_ + nn] : 0.f;
-                    a = mfma32(VPs[(rb * 32 + cl) * LDV + nn], sv, a);
-                }
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = rb * 32 + acc_row(r, lane);
-                    a[r] *= el[row];
-                    // e^{b_L - b_j} k_j . (V dS_out^T)_j, partial over this column block
-                    const float s = sum32(a[r] * Ks[row * LDK + col]);
-                    if (cl == 0) redK[cb][row] = s;
-                }
-                for (int jj = rb * 32; jj < CH; jj += 2)
-                    a = mfma32(dPs[(jj + kh) * LDP + rb * 32 + cl], Qs[(jj + kh) * LDK + col], a);
-                dKacc[jw] += a;
-            }
-        }
-        __syncthreads();   // V and dP are dead; P goes where V was, M where dP was
+        __syncthreads();   // dP is dead; P goes where V was, M where dP was
 
         if (wave < 3) {
 #pragma unroll
@@ -554,44 +712,34 @@ __global__ __launch_bounds__(NTH) void k_bwd_grads(
                 VPs[i * LDV + j] = pP[r];
                 dPs[i * LDP + j] = pM[r];
             }
-        } else {
+        } else if (wave == 3) {
             // upper-right tile of M is zero (j > i)
 #pragma unroll
             for (int r = 0; r < 16; ++r) dPs[acc_row(r, lane) * LDP + 32 + cl] = 0.f;
         }
         __syncthreads();
 
-        // dV_h = diag(e^{bL-b}) K dS_out + P^T dY.
+        // (3) dV_h = diag(e^{bL-b}) K dS_out + P^T dY.
+        if (hasV) {
+            f32x16 aV = zero16();
+            // K dS_out : B(i, n) = dS_out[i][n]
+            mma_b_global<DKP, LDK>(aV, Ks, rbv * 32, dSo, colv, dv_, dk_, dv_, lane);
 #pragma unroll
-        for (int jw = 0; jw < NBWV; ++jw) {
-            const int ob = wave + 4 * jw;
-            if (ob < NOBV) {
-                const int rb = ob / NCBV, cb = ob % NCBV;
-                const int col = cb * 32 + cl;
-                f32x16 a = zero16();
-#pragma unroll 8
-                for (int i = 0; i < DKP; i += 2) {
-                    const int ii = i + kh;
-                    const float sv = (ii < dk_ && col < dv_) ? dSo[ii * dv_ + col] : 0.f;
-                    a = mfma32(Ks[(rb * 32 + cl) * LDK + ii], sv, a);
-                }
+            for (int r = 0; r < 16; ++r) aV[r] *= el[rbv * 32 + acc_row(r, lane)];
+            for (int jj = rbv * 32; jj < CH; jj += 2)
+                aV = mfma32(VPs[(jj + kh) * LDV + rbv * 32 + cl], dYs[(jj + kh) * LDY + colv], aV);
+            if (colv < dv_) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) a[r] *= el[rb * 32 + acc_row(r, lane)];
-                for (int jj = rb * 32; jj < CH; jj += 2)
-                    a = mfma32(VPs[(jj + kh) * LDV + rb * 32 + cl], dYs[(jj + kh) * LDY + col], a);
-                if (col < dv_) {
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int row = rb * 32 + acc_row(r, lane);
-                        if (row < rows) dv[(bh * T + c * CH + row) * dv_ + col] = a[r];
-                    }
+                for (int r = 0; r < 16; ++r) {
+                    const int row = rbv * 32 + acc_row(r, lane);
+                    if (row < rows) dv[(bh * T + c * CH + row) * dv_ + colv] = aV[r];
                 }
             }
         }
 
-        // Rectangle sums R_r = sum_{i >= r} sum_{j < r} M_ij: exclusive prefix
-        // over j of every row (in place), then a suffix over i per column.
-        for (int i = wave * 16; i < wave * 16 + 16; ++i) {
+        // (4) Rectangle sums R_r = sum_{i >= r} sum_{j < r} M_ij: exclusive
+        //     prefix over j of every row (in place), then a suffix over i.
+        for (int i = wave * 8; i < wave * 8 + 8; ++i) {
             float x = dPs[i * LDP + lane];
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
@@ -606,7 +754,7 @@ __global__ __launch_bounds__(NTH) void k_bwd_grads(
         __syncthreads();
         {
             float racc = 0.f;
-            for (int i = wave * 16; i < wave * 16 + 16; ++i)
+            for (int i = wave * 8; i < wave * 8 + 8; ++i)
                 if (i >= lane) racc += dPs[i * LDP + lane];
             redR[wave][lane] = racc;
         }
@@ -615,13 +763,13 @@ __global__ __launch_bounds__(NTH) void k_bwd_grads(
         float part = 0.f;
         if (c + 1 < NC) {
             if ((E & 3) == 0) {
-                for (int64_t e = (int64_t)threadIdx.x * 4; e < E; e += NTH * 4) {
+                for (int64_t e = (int64_t)threadIdx.x * 4; e < E; e += NTW * 4) {
                     const float4 x = *reinterpret_cast<const float4 *>(dSo + e);
                     const float4 z = *reinterpret_cast<const float4 *>(Sin + e);
                     part += x.x * z.x + x.y * z.y + x.z * z.z + x.w * z.w;
                 }
             } else {
-                for (int64_t e = threadIdx.x; e < E; e += NTH) part += dSo[e] * Sin[e];
+                for (int64_t e = threadIdx.x; e < E; e += NTW) part += dSo[e] * Sin[e];
             }
         }
         part = sum64(part);
@@ -629,15 +777,19 @@ __global__ __launch_bounds__(NTH) void k_bwd_grads(
         __syncthreads();
 
         if (wave == 0) {
-            const float fro = (redB[0] + redB[1]) + (redB[2] + redB[3]);
-            const float ebl = expf(bl[bh * NCp + c]);
+            float fro = 0.f, rint = 0.f;
+#pragma unroll
+            for (int w = 0; w < NTW / 64; ++w) {
+                fro += redB[w];
+                rint += redR[w][lane];
+            }
+            const float ebl = expf(blh);
             float iq = 0.f, ik = 0.f;
 #pragma unroll
             for (int cb = 0; cb < NCBK; ++cb) {
                 iq += redQ[cb][lane];
                 ik += redK[cb][lane];
             }
-            const float rint = (redR[0][lane] + redR[1][lane]) + (redR[2][lane] + redR[3][lane]);
             // inclusive suffix sum of iq, exclusive prefix sum of ik
             float sq = iq, pk = ik;
 #pragma unroll
@@ -654,22 +806,14 @@ __global__ __launch_bounds__(NTH) void k_bwd_grads(
         __syncthreads();
     }
 
+    if (hasK && colk < dk_) {
 #pragma unroll
-    for (int jw = 0; jw < NBWK; ++jw) {
-        const int ob = wave + 4 * jw;
-        if (ob < NOBK) {
-            const int rb = ob / NCBK, cb = ob % NCBK;
-            const int col = cb * 32 + cl;
-            if (col < dk_) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = rb * 32 + acc_row(r, lane);
-                    if (row < rows) {
-                        const int64_t o = (bg * T + c * CH + row) * dk_ + col;
-                        dq[o] = dQacc[jw][r];
-                        dk[o] = dKacc[jw][r];
-                    }
-                }
+        for (int r = 0; r < 16; ++r) {
+            const int row = rbk * 32 + acc_row(r, lane);
+            if (row < rows) {
+                const int64_t o = (bg * T + c * CH + row) * dk_ + colk;
+                dq[o] = dQacc[r];
+                dk[o] = dKacc[r];
             }
         }
     }
@@ -685,9 +829,9 @@ __global__ __launch_bounds__(NTH) void k_zero(float *__restrict__ p, int64_t n)
 // ---------------------------------------------------------------------------
 // Kernel timing (optional, process-global).
 
-enum KernelId { KID_CUMSUM = 0, KID_STATE, KID_PASS, KID_OUTPUT, KID_DSTATE, KID_PASS_REV, KID_GRADS, KID_COUNT };
-static const char *kKernelNames[KID_COUNT] = {"chunk_cumsum", "chunk_state", "state_pass", "chunk_output",
-                                              "chunk_dstate", "state_pass_rev", "bwd_grads"};
+enum KernelId { KID_CUMSUM = 0, KID_SCAN, KID_OUTPUT, KID_SCAN2, KID_GRADS, KID_COUNT };
+static const char *kKernelNames[KID_COUNT] = {"chunk_cumsum", "state_scan", "chunk_output", "state_scan_bidir",
+                                              "bwd_grads"};
 
 struct Timing {
     bool on = false;
@@ -781,8 +925,11 @@ static int launch_status()
     return hipGetLastError() == hipSuccess ? SSD_OK : SSD_ERR_DEVICE;
 }
 
-static int run_prefix(const Problem &P, const float *q, const float *k, const float *v, const float *la,
-                      const float *h0, hipStream_t st)
+// Chunk cumsum, then the fused state scan: the forward direction only
+// (ndir = 1, fills `states` with S_in) or both directions in one launch
+// (ndir = 2, also fills `dstates` with dS_out and writes dh0).
+static int run_scan(const Problem &P, int ndir, const float *q, const float *k, const float *v, const float *dy,
+                    const float *la, const float *h0, float *dh0, hipStream_t st)
 {
     const ssd_shape &s = P.s;
     const int64_t BH = s.B * s.H;
@@ -794,17 +941,14 @@ static int run_prefix(const Problem &P, const float *q, const float *k, const fl
     }
     if (launch_status() != SSD_OK) return SSD_ERR_DEVICE;
     {
-        TimedLaunch tl(KID_STATE, st);
-        SSD_DISPATCH_DIMS(P.DKP, P.DVP, (k_chunk_state<KP, VP, 0><<<dim3((unsigned)(BH * P.L.NC)), dim3(NTH), 0, st>>>(
-                                             k, v, P.bcum, P.bl, P.states, (int)s.G, (int)s.H, s.T, (int)s.dk,
-                                             (int)s.dv, P.L.NC, P.L.NCp, P.L.Epad, P.vecK, P.vecV)));
-    }
-    if (launch_status() != SSD_OK) return SSD_ERR_DEVICE;
-    {
-        TimedLaunch tl(KID_PASS, st);
-        const int64_t bpb = (P.L.Epad / 4 + NTH - 1) / NTH;
-        k_state_pass<false><<<dim3((unsigned)(BH * bpb)), dim3(NTH), 0, st>>>(P.states, P.bl, h0, nullptr, P.L.NC,
-                                                                             P.L.NCp, P.L.E, P.L.Epad, bpb);
+        TimedLaunch tl(ndir == 1 ? KID_SCAN : KID_SCAN2, st);
+        SSD_DISPATCH_DIMS(P.DKP, P.DVP, ({
+            constexpr int TJ = VP < 64 ? VP : 64;
+            const int64_t per_dir = BH * (KP / TI) * (VP / TJ);
+            k_state_scan<KP, VP><<<dim3((unsigned)(ndir * per_dir)), dim3(NTH), 0, st>>>(
+                q, k, v, dy, h0, P.bcum, P.bl, P.states, P.dstates, dh0, (int)s.G, (int)s.H, s.T, (int)s.dk,
+                (int)s.dv, P.L.NC, P.L.NCp, P.L.Epad, per_dir, P.vecK, P.vecV);
+        }));
     }
     return launch_status();
 }
@@ -853,12 +997,12 @@ int ssd_fwd(const ssd_shape *shape, const float *q, const float *k, const float 
     if (rc != SSD_OK) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
 
-    rc = run_prefix(P, q, k, v, log_alpha, h0, st);
+    rc = run_scan(P, 1, q, k, v, nullptr, log_alpha, h0, nullptr, st);
     if (rc != SSD_OK) return rc;
     {
         TimedLaunch tl(KID_OUTPUT, st);
         SSD_DISPATCH_DIMS(P.DKP, P.DVP,
-                          (k_chunk_output<KP, VP><<<dim3((unsigned)(s.B * s.G * P.L.NC)), dim3(NTH), 0, st>>>(
+                          (k_chunk_output<KP, VP><<<dim3((unsigned)(s.B * s.G * P.L.NC)), dim3(NTW), 0, st>>>(
                               q, k, v, P.bcum, P.states, y, (int)s.G, (int)s.H, s.T, (int)s.dk, (int)s.dv, P.L.NC,
                               P.L.Epad, P.vecK, P.vecV)));
     }
@@ -891,28 +1035,13 @@ int ssd_bwd(const ssd_shape *shape, const float *q, const float *k, const float 
     rc = prepare(shape, true, workspace, workspace_bytes, &P);
     if (rc != SSD_OK) return rc;
 
-    // Recompute the incoming state of every chunk.
-    rc = run_prefix(P, q, k, v, log_alpha, h0, st);
+    // S_in (forward) and dS_out (reverse) of every chunk, and dh0.
+    rc = run_scan(P, 2, q, k, v, dy, log_alpha, h0, dh0, st);
     if (rc != SSD_OK) return rc;
-    const int64_t BH = s.B * s.H;
-    {
-        TimedLaunch tl(KID_DSTATE, st);
-        SSD_DISPATCH_DIMS(P.DKP, P.DVP, (k_chunk_state<KP, VP, 1><<<dim3((unsigned)(BH * P.L.NC)), dim3(NTH), 0, st>>>(
-                                             q, dy, P.bcum, P.bl, P.dstates, (int)s.G, (int)s.H, s.T, (int)s.dk,
-                                             (int)s.dv, P.L.NC, P.L.NCp, P.L.Epad, P.vecK, P.vecV)));
-    }
-    if (launch_status() != SSD_OK) return SSD_ERR_DEVICE;
-    {
-        TimedLaunch tl(KID_PASS_REV, st);
-        const int64_t bpb = (P.L.Epad / 4 + NTH - 1) / NTH;
-        k_state_pass<true><<<dim3((unsigned)(BH * bpb)), dim3(NTH), 0, st>>>(P.dstates, P.bl, nullptr, dh0, P.L.NC,
-                                                                            P.L.NCp, P.L.E, P.L.Epad, bpb);
-    }
-    if (launch_status() != SSD_OK) return SSD_ERR_DEVICE;
     {
         TimedLaunch tl(KID_GRADS, st);
         SSD_DISPATCH_DIMS(P.DKP, P.DVP,
-                          (k_bwd_grads<KP, VP><<<dim3((unsigned)(s.B * s.G * P.L.NC)), dim3(NTH), 0, st>>>(
+                          (k_bwd_grads<KP, VP><<<dim3((unsigned)(s.B * s.G * P.L.NC)), dim3(NTW), 0, st>>>(
                               q, k, v, dy, P.bcum, P.bl, P.states, P.dstates, dq, dk, dv, dlog_alpha, (int)s.G,
                               (int)s.H, s.T, (int)s.dk, (int)s.dv, P.L.NC, P.L.NCp, P.L.Epad, P.vecK, P.vecV)));
     }

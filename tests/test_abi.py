@@ -111,7 +111,7 @@ def test_status_strings_and_constants():
     assert lib.ssd_strerror(99) == b"unknown status"
     assert lib.ssd_chunk_size() == ssd.CHUNK == 64
     names = [lib.ssd_kernel_name(i).decode() for i in range(lib.ssd_kernel_count())]
-    assert "bwd_grads" in names and "state_pass" in names
+    assert "bwd_grads" in names and "state_scan" in names
 
 
 def test_binding_rejects_cpu_tensors():

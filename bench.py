@@ -5,6 +5,8 @@ headline workload g2h8_d128: B=4, G=2, H=8, T=8192, dk=dv=128, float32,
 seeded synthetic inputs resident in HBM.  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+    python bench.py --copy-mib N      # plain device copy of N MiB, 5 times: the
+                                      # reference kernel for scaling HBM counters
 
 Throughput (`value`) is the nominal fwd+bwd FLOP count of the step divided
 by the measured step time.  Nominal FLOPs per (token, head), with chunk
@@ -104,6 +106,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="g2h8_d128_T8192")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB (5 launches) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -118,6 +122,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a HIP device", file=sys.stderr)
         sys.exit(1)
+    if args.copy_mib > 0:
+        n = args.copy_mib * (1 << 20) // 4
+        src = torch.ones(n, device="cuda")
+        dst = torch.empty(n, device="cuda")
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": 4 * n, "launches": 5}), flush=True)
+        return
     w = workload(args.workload)
     s = w.shape
     x = make_inputs(s, w.seed, mu=w.mu)

@@ -159,42 +159,45 @@ constexpr int NTW = 512;   // 8 waves per block
 
 __device__ __forceinline__ float4 zero4() { return make_float4(0.f, 0.f, 0.f, 0.f); }
 
-// p[c4 .. c4+3] of a row with `lim` valid entries (the rest read as 0).
+// row[c4 .. c4+3] of the row starting at base + rowoff, which has `lim`
+// valid entries (the rest read as 0).  `base` is uniform across the wave and
+// the per-lane offset is 32-bit, so the load addresses from a scalar base.
 // vec: one aligned 16-byte load (requires lim % 4 == 0 and an aligned row).
-__device__ __forceinline__ float4 load4(const float *__restrict__ p, int c4, int lim, bool vec)
+__device__ __forceinline__ float4 load4(const float *__restrict__ base, uint32_t rowoff, int c4, int lim, bool vec)
 {
-    if (vec) return (c4 < lim) ? *reinterpret_cast<const float4 *>(p + c4) : zero4();
+    const float *p = base + (rowoff + (uint32_t)c4);
+    if (vec) return (c4 < lim) ? *reinterpret_cast<const float4 *>(p) : zero4();
     float4 r;
-    r.x = (c4 + 0 < lim) ? p[c4 + 0] : 0.f;
-    r.y = (c4 + 1 < lim) ? p[c4 + 1] : 0.f;
-    r.z = (c4 + 2 < lim) ? p[c4 + 2] : 0.f;
-    r.w = (c4 + 3 < lim) ? p[c4 + 3] : 0.f;
+    r.x = (c4 + 0 < lim) ? p[0] : 0.f;
+    r.y = (c4 + 1 < lim) ? p[1] : 0.f;
+    r.z = (c4 + 2 < lim) ? p[2] : 0.f;
+    r.w = (c4 + 3 < lim) ? p[3] : 0.f;
     return r;
 }
 
 // Load a ROWS x DP tile (row-major, row stride d, `nrows` valid rows, d valid
 // columns) into registers, PER float4 per thread, zero padded.
 template <int ROWS, int DP, int NT, int PER>
-__device__ __forceinline__ void tile_to_regs(float4 (&buf)[PER], const float *__restrict__ src, int nrows, int d,
-                                             bool vec)
+__device__ __forceinline__ void tile_to_regs(int tid, float4 (&buf)[PER], const float *__restrict__ src, int nrows,
+                                             int d, bool vec)
 {
     constexpr int Q4 = DP / 4;
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
-        const int idx = threadIdx.x + u * NT;
+        const int idx = tid + u * NT;
         const int r = idx / Q4, c4 = (idx - r * Q4) * 4;
-        buf[u] = (idx < ROWS * Q4 && r < nrows) ? load4(src + (size_t)r * d, c4, d, vec) : zero4();
+        buf[u] = (idx < ROWS * Q4 && r < nrows) ? load4(src, (uint32_t)(r * d), c4, d, vec) : zero4();
     }
 }
 
 // Store a register tile (see tile_to_regs) into LDS dst[ROWS][LD].
 template <int ROWS, int DP, int NT, int PER, int LD>
-__device__ __forceinline__ void regs_to_lds(const float4 (&buf)[PER], float *dst)
+__device__ __forceinline__ void regs_to_lds(int tid, const float4 (&buf)[PER], float *dst)
 {
     constexpr int Q4 = DP / 4;
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
-        const int idx = threadIdx.x + u * NT;
+        const int idx = tid + u * NT;
         if (idx < ROWS * Q4) {
             const int r = idx / Q4, c4 = (idx - r * Q4) * 4;
             if (LD % 4 == 0) {
@@ -207,47 +210,6 @@ __device__ __forceinline__ void regs_to_lds(const float4 (&buf)[PER], float *dst
                 pp[3] = buf[u].w;
             }
         }
-    }
-}
-
-// acc += A * B over k in [0, KP), with A(i, k) = As[(rbase + i) * LDA + k]
-// (LDS) and B(k, j) = S[j][k] read from global memory, S row-major with row
-// stride `ld`, rows j >= limj and columns k >= limk reading as 0.  Lane
-// (j, h) loads S[j][k0 + 4h .. k0 + 4h + 3] as one float4 and feeds it to
-// four MFMAs; A is read at the matching permuted k.
-template <int KP, int LDA>
-__device__ __forceinline__ void mma_bt_global(f32x16 &acc, const float *As, int rbase, const float *__restrict__ S,
-                                              int j, int limj, int limk, int ld, bool vec, int lane)
-{
-    const int cl = lane & 31, kh = lane >> 5;
-    const float *srow = S + (size_t)j * ld;
-    const bool ok = j < limj;
-    const float *arow = As + (rbase + cl) * LDA + 4 * kh;
-#pragma unroll 2
-    for (int k0 = 0; k0 < KP; k0 += 8) {
-        const float4 f = ok ? load4(srow, k0 + 4 * kh, limk, vec) : zero4();
-        acc = mfma32(arow[k0 + 0], f.x, acc);
-        acc = mfma32(arow[k0 + 1], f.y, acc);
-        acc = mfma32(arow[k0 + 2], f.z, acc);
-        acc = mfma32(arow[k0 + 3], f.w, acc);
-    }
-}
-
-// acc += A * B over k in [0, KP), with A(i, k) = As[(rbase + i) * LDA + k]
-// (LDS) and B(k, j) = S[k][j] read from global memory (row stride ld, rows
-// k >= limk and columns j >= limj reading as 0).  Lanes read consecutive j.
-template <int KP, int LDA>
-__device__ __forceinline__ void mma_b_global(f32x16 &acc, const float *As, int rbase, const float *__restrict__ S,
-                                             int j, int limj, int limk, int ld, int lane)
-{
-    const int cl = lane & 31, kh = lane >> 5;
-    const bool ok = j < limj;
-    const float *arow = As + (rbase + cl) * LDA + kh;
-#pragma unroll 8
-    for (int k0 = 0; k0 < KP; k0 += 2) {
-        const int kk = k0 + kh;
-        const float sv = (ok && kk < limk) ? S[(size_t)kk * ld + j] : 0.f;
-        acc = mfma32(arow[k0], sv, acc);
     }
 }
 
@@ -358,13 +320,13 @@ __global__ __launch_bounds__(NTH) void k_state_scan(
         for (int u = 0; u < APER; ++u) {
             const int idx = threadIdx.x + u * NTH;
             const int r = idx / (TI / 4), c4 = (idx - r * (TI / 4)) * 4;
-            abuf[u] = (idx < A4 && r < rows) ? load4(Asrc + (c * CH + r) * dk, c4, lima, vecK != 0) : zero4();
+            abuf[u] = (idx < A4 && r < rows) ? load4(Asrc + c * CH * dk, (uint32_t)(r * dk), c4, lima, vecK != 0) : zero4();
         }
 #pragma unroll
         for (int u = 0; u < BPER; ++u) {
             const int idx = threadIdx.x + u * NTH;
             const int r = idx / (TJ / 4), c4 = (idx - r * (TJ / 4)) * 4;
-            bbuf[u] = (idx < B4 && r < rows) ? load4(Bsrc + (c * CH + r) * dv, c4, limb, vecV != 0) : zero4();
+            bbuf[u] = (idx < B4 && r < rows) ? load4(Bsrc + c * CH * dv, (uint32_t)(r * dv), c4, limb, vecV != 0) : zero4();
             bt[u] = (idx < B4) ? bcb[c * CH + r] : 0.f;
         }
         blc = bl[bh * NCp + c];
@@ -489,8 +451,8 @@ __global__ __launch_bounds__(NTW) void k_chunk_output(const float *__restrict__ 
     float bpre = 0.f;
     auto prefetch = [&](int hh) {
         const int64_t bh = bh0 + hh;
-        tile_to_regs<CH, DVP, NTW, VPER>(vbuf, v + (bh * T + c * CH) * dv, rows, dv, vecV != 0);
-        tile_to_regs<DKP, DVP, NTW, SPER>(sbuf, states + (bh * NC + c) * Epad, dk, dv, vecV != 0);
+        tile_to_regs<CH, DVP, NTW, VPER>(threadIdx.x, vbuf, v + (bh * T + c * CH) * dv, rows, dv, vecV != 0);
+        tile_to_regs<DKP, DVP, NTW, SPER>(threadIdx.x, sbuf, states + (bh * NC + c) * Epad, dk, dv, vecV != 0);
         if (threadIdx.x < CH) bpre = bcum[bh * NC * CH + c * CH + threadIdx.x];
     };
     prefetch(0);
@@ -506,8 +468,8 @@ __global__ __launch_bounds__(NTW) void k_chunk_output(const float *__restrict__ 
     const int n = cb * 32 + cl;
     for (int hh = 0; hh < hpg; ++hh) {
         const int64_t bh = bh0 + hh;
-        regs_to_lds<CH, DVP, NTW, VPER, LDKV>(vbuf, KVs);
-        regs_to_lds<DKP, DVP, NTW, SPER, DVP>(sbuf, Ss);
+        regs_to_lds<CH, DVP, NTW, VPER, LDKV>(threadIdx.x, vbuf, KVs);
+        regs_to_lds<DKP, DVP, NTW, SPER, DVP>(threadIdx.x, sbuf, Ss);
         if (threadIdx.x < CH) {
             bs[threadIdx.x] = bpre;
             eb[threadIdx.x] = expf(bpre);
@@ -562,11 +524,70 @@ __global__ __launch_bounds__(NTW) void k_chunk_output(const float *__restrict__ 
 
 // ---------------------------------------------------------------------------
 // B3 + B4: gradients of one chunk for every head of one group.
-// One block of 8 waves per (b,g,chunk).  dq and dk are summed over the
-// group's heads in registers (ascending head order); dv and dlog_alpha are
-// written per head.  The next head's V and dY tiles are prefetched into
-// registers while this head runs; the incoming state S_in and the outgoing
-// state gradient dS_out are read from the workspace slabs as MFMA operands.
+//
+// One block of 8 waves per (b, g, chunk).  The group's heads are taken in
+// ascending order; dq and dk are summed over them in registers.  Per head:
+//
+//   state phase  S_in and dS_out are streamed through LDS in slabs of 32
+//                state columns (all dk rows of both).  With the slab's 32
+//                columns n of dY and V:
+//                    Gq += dY[:, n] S_in[:, n]^T      (C x dk, 32x32 tiles)
+//                    Gk += V[:, n] dS_out[:, n]^T     (C x dk, 32x32 tiles)
+//                    Gv[:, n] = K dS_out[:, n]        (C x 32, 16x16 tiles)
+//                and every thread adds the products of the state elements
+//                it staged to <dS_out, S_in>.
+//   intra phase  dP = (dY V^T) o D and P = (Q K^T) o D, then
+//                    dQ += diag(e^b) Gq + dP K
+//                    dK += diag(e^{b_L - b}) Gk + dP^T Q
+//                    dV  = diag(e^{b_L - b}) Gv + P^T dY
+//                and dlog_alpha for the chunk's positions.
+//
+// Every MFMA operand is read from LDS.  The LDS regions are Q / slabs (the
+// two share memory in time; Q is staged again for every head), K, dY,
+// V / ((dY V^T) partial sums + P) and dP / M.  The next head's V, dY and
+// first slab, and each next slab, are loaded into registers while the
+// current ones are in use.  Row strides keep the 16-byte row reads and the
+// column reads free of LDS bank conflicts.
+template <int DKP, int DVP>
+struct BwdCfg {
+    static constexpr int LDK = DKP + 4;   // Q, K
+    static constexpr int LDV = DVP + 4;   // dY, V
+    static constexpr int LDP = CH + 4;    // dP, M, P
+    static constexpr int LSL = 36;        // slab rows: 32 state columns + 4
+    static constexpr int NKB = DKP / 32;  // 32-column blocks of dk
+    static constexpr int NTK = 2 * NKB;   // 32x32 tiles of a C x dk result
+    static constexpr int NSL = DVP / 32;  // slabs per state
+    static constexpr int SCR = 3 * 1024;  // (dY V^T) partial sums, start of the V region
+    static constexpr int QN = (CH * LDK > 2 * DKP * LSL) ? CH * LDK : 2 * DKP * LSL;
+    static constexpr int VN = (CH * LDV > SCR + CH * LDP) ? CH * LDV : SCR + CH * LDP;
+    static constexpr int PN = (CH * LDP > SCR) ? CH * LDP : SCR;
+    static constexpr int TPER = (CH * DVP / 4 + NTW - 1) / NTW;   // float4 / thread, C x dv tile
+    static constexpr int QPER = (CH * DKP / 4 + NTW - 1) / NTW;   // float4 / thread, C x dk tile
+    static constexpr int SPER = (DKP * 8 + NTW - 1) / NTW;        // float4 / thread, one state slab
+};
+
+// acc += A B^T over k in [k0, k1) (a multiple of 8 long): A and B are the
+// 32-row blocks starting at A and B (row-major in LDS, row strides LDA and
+// LDB).  Lane (kh, r) reads k0 + 4kh .. k0 + 4kh + 3 of its rows with one
+// 16-byte load and feeds them to four MFMAs; MFMA s contracts over the k
+// pair (k0 + s, k0 + 4 + s).
+template <int LDA, int LDB>
+__device__ __forceinline__ void mma_abt(f32x16 &acc, const float *A, const float *B, int k0, int k1, int lane)
+{
+    const int cl = lane & 31, kh = lane >> 5;
+    const float *a = A + cl * LDA + 4 * kh;
+    const float *b = B + cl * LDB + 4 * kh;
+#pragma unroll 2
+    for (int kk = k0; kk < k1; kk += 8) {
+        const float4 x = *reinterpret_cast<const float4 *>(a + kk);
+        const float4 y = *reinterpret_cast<const float4 *>(b + kk);
+        acc = mfma32(x.x, y.x, acc);
+        acc = mfma32(x.y, y.y, acc);
+        acc = mfma32(x.z, y.z, acc);
+        acc = mfma32(x.w, y.w, acc);
+    }
+}
+
 template <int DKP, int DVP>
 __global__ __launch_bounds__(NTW) void k_bwd_grads(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
@@ -575,22 +596,22 @@ __global__ __launch_bounds__(NTW) void k_bwd_grads(
     float *__restrict__ dk, float *__restrict__ dv, float *__restrict__ dla, int G, int H, int64_t T, int dk_,
     int dv_, int64_t NC, int64_t NCp, int64_t Epad, int vecK, int vecV)
 {
-    constexpr int LDK = DKP + 1;
-    constexpr int LDY = DVP + 1;
-    constexpr int LDV = (DVP > CH ? DVP : CH) + 1;   // holds V, later P (C x C)
-    constexpr int LDP = CH + 1;
-    constexpr int NCBK = DKP / 32, NOBK = 2 * NCBK;
-    constexpr int NCBV = DVP / 32, NOBV = 2 * NCBV;
-    constexpr int VPER = (CH * DVP / 4 + NTW - 1) / NTW;
-    __shared__ float Qs[CH * LDK];
-    __shared__ float Ks[CH * LDK];
-    __shared__ float dYs[CH * LDY];
-    __shared__ float VPs[CH * LDV];
-    __shared__ float dPs[CH * LDP];
+    using Cfg = BwdCfg<DKP, DVP>;
+    constexpr int LDK = Cfg::LDK, LDV = Cfg::LDV, LDP = Cfg::LDP, LSL = Cfg::LSL;
+    constexpr int NKB = Cfg::NKB, NTK = Cfg::NTK, NSL = Cfg::NSL, SCR = Cfg::SCR;
+    constexpr int TPER = Cfg::TPER, QPER = Cfg::QPER, SPER = Cfg::SPER;
+    __shared__ __attribute__((aligned(16))) float RQ[Cfg::QN];
+    __shared__ __attribute__((aligned(16))) float RK[CH * LDK];
+    __shared__ __attribute__((aligned(16))) float RY[CH * LDV];
+    __shared__ __attribute__((aligned(16))) float RV[Cfg::VN];
+    __shared__ __attribute__((aligned(16))) float RP[Cfg::PN];
     __shared__ float bs[CH], eb[CH], el[CH];
-    __shared__ float redQ[NCBK][CH], redK[NCBK][CH];
+    __shared__ float redQ[NKB][CH], redK[NKB][CH];
     __shared__ float redR[NTW / 64][CH];
     __shared__ float redB[NTW / 64];
+    float *const slS = RQ;               // S_in slab   [DKP][LSL]
+    float *const slD = RQ + DKP * LSL;   // dS_out slab [DKP][LSL]
+    float *const Pm = RV + SCR;          // P           [CH][LDP]
 
     const int64_t c = blockIdx.x % NC;
     const int64_t bg = blockIdx.x / NC;
@@ -599,148 +620,262 @@ __global__ __launch_bounds__(NTW) void k_bwd_grads(
     const int hpg = H / G;
     const int64_t bh0 = b * H + (int64_t)g * hpg;
     const int rows = (int)((T - c * CH) < CH ? (T - c * CH) : CH);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int cl = lane & 31, kh = lane >> 5;
-    const int64_t E = (int64_t)dk_ * dv_;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int cl = lane & 31;
+    const int l16 = lane & 15, lq = lane >> 4;
+    const bool vk = vecK != 0, vv = vecV != 0;
+    const float *qsrc = q + (bg * T + c * CH) * dk_;
 
-    float4 vbuf[VPER], ybuf[VPER];
-    float bpre = 0.f, blpre = 0.f;
-    auto prefetch = [&](int hh) {
+    float4 vbuf[TPER], ybuf[TPER];   // a head's V and dY
+    float4 sbuf[SPER], dbuf[SPER];   // a slab of S_in and of dS_out
+    float4 qbuf[QPER];               // Q
+    float bpre = 0.f, blpre = 0.f;   // a head's b (thread t < 64: position t) and b_L
+
+    auto load_vy = [&](int hh, int tid) {
         const int64_t bh = bh0 + hh;
-        tile_to_regs<CH, DVP, NTW, VPER>(vbuf, v + (bh * T + c * CH) * dv_, rows, dv_, vecV != 0);
-        tile_to_regs<CH, DVP, NTW, VPER>(ybuf, dy + (bh * T + c * CH) * dv_, rows, dv_, vecV != 0);
-        if (threadIdx.x < CH) {
-            bpre = bcum[bh * NC * CH + c * CH + threadIdx.x];
+        tile_to_regs<CH, DVP, NTW, TPER>(tid, vbuf, v + (bh * T + c * CH) * dv_, rows, dv_, vv);
+        tile_to_regs<CH, DVP, NTW, TPER>(tid, ybuf, dy + (bh * T + c * CH) * dv_, rows, dv_, vv);
+        if (tid < CH) {
+            bpre = bcum[bh * NC * CH + c * CH + tid];
             blpre = bl[bh * NCp + c];
         }
     };
-    prefetch(0);
+    auto load_slab = [&](int hh, int m, int tid) {
+        const int64_t off = ((bh0 + hh) * NC + c) * Epad + 32 * m;
+        const int lim = dv_ - 32 * m;
+#pragma unroll
+        for (int u = 0; u < SPER; ++u) {
+            const int idx = tid + u * NTW;
+            const int r = idx >> 3, c4 = (idx & 7) * 4;
+            const bool ok = idx < DKP * 8 && r < dk_;
+            sbuf[u] = ok ? load4(states + off, (uint32_t)(r * dv_), c4, lim, vv) : zero4();
+            dbuf[u] = ok ? load4(dstates + off, (uint32_t)(r * dv_), c4, lim, vv) : zero4();
+        }
+    };
+    // Write the staged slab to LDS; returns this thread's part of <dS_out, S_in>.
+    auto store_slab = [&](int tid) -> float {
+        float f = 0.f;
+#pragma unroll
+        for (int u = 0; u < SPER; ++u) {
+            const int idx = tid + u * NTW;
+            if (idx < DKP * 8) {
+                const int r = idx >> 3, c4 = (idx & 7) * 4;
+                *reinterpret_cast<float4 *>(slS + r * LSL + c4) = sbuf[u];
+                *reinterpret_cast<float4 *>(slD + r * LSL + c4) = dbuf[u];
+                f += sbuf[u].x * dbuf[u].x + sbuf[u].y * dbuf[u].y + sbuf[u].z * dbuf[u].z +
+                     sbuf[u].w * dbuf[u].w;
+            }
+        }
+        return f;
+    };
 
-    stage_rows<DKP, LDK, false, NTW>(Qs, q + (bg * T + c * CH) * dk_, rows, dk_, vecK != 0, nullptr);
-    stage_rows<DKP, LDK, false, NTW>(Ks, k + (bg * T + c * CH) * dk_, rows, dk_, vecK != 0, nullptr);
+    // ---- block set-up: K, Q, A = Q K^T, the first head's V, dY and slab.
+    load_vy(0, tid);
+    tile_to_regs<CH, DKP, NTW, QPER>(tid, qbuf, qsrc, rows, dk_, vk);
+    regs_to_lds<CH, DKP, NTW, QPER, LDK>(tid, qbuf, RQ);
+    tile_to_regs<CH, DKP, NTW, QPER>(tid, qbuf, k + (bg * T + c * CH) * dk_, rows, dk_, vk);
+    regs_to_lds<CH, DKP, NTW, QPER, LDK>(tid, qbuf, RK);
+    load_slab(0, 0, tid);
     __syncthreads();
-    const f32x16 accA = qk_tiles<DKP, LDK, LDK>(Qs, Ks, dPs, wave, lane);
-    const int tile = wave % 3, half = wave / 3;
-    const int ib = (tile == 0) ? 0 : 1, jb = (tile == 2) ? 1 : 0;
+    // causal 32x32 tiles (0,0), (1,0), (1,1) of Q K^T; waves w and w + 3 split dk
+    const int at = wave % 3, ah = wave / 3;
+    const int aib = (at == 0) ? 0 : 1, ajb = (at == 2) ? 1 : 0;
+    f32x16 accA = zero16();
+    if (wave < 6)
+        mma_abt<LDK, LDK>(accA, RQ + aib * 32 * LDK, RK + ajb * 32 * LDK, ah * (DKP / 2), (ah + 1) * (DKP / 2),
+                          lane);
+    if (wave >= 3 && wave < 6) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) RP[at * 1024 + r * 64 + lane] = accA[r];
+    }
+    __syncthreads();
+    if (wave < 3) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) accA[r] += RP[at * 1024 + r * 64 + lane];
+    }
+    regs_to_lds<CH, DVP, NTW, TPER, LDV>(tid, vbuf, RV);
+    regs_to_lds<CH, DVP, NTW, TPER, LDV>(tid, ybuf, RY);
+    float fro_next = store_slab(tid);
+    __syncthreads();
 
-    // output tile of this wave for dq/dk (C x dk) and dv (C x dv)
-    const int rbk = wave / NCBK, cbk = wave % NCBK, colk = cbk * 32 + cl;
-    const int rbv = wave / NCBV, cbv = wave % NCBV, colv = cbv * 32 + cl;
-    const bool hasK = wave < NOBK, hasV = wave < NOBV;
+    const int rbk = wave / NKB, cbk = wave % NKB;   // this wave's dq / dk tile (waves < NTK)
+    const bool hasK = wave < NTK;
     f32x16 dQacc = zero16(), dKacc = zero16();
 
     for (int hh = 0; hh < hpg; ++hh) {
+        // Per-lane index arithmetic is redone inside the loop (the asm hides
+        // that tid is loop-invariant): hoisting it would exceed the register
+        // budget.
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        const int lane = tid & 63, cl = lane & 31, l16 = lane & 15, lq = lane >> 4;
         const int64_t bh = bh0 + hh;
-        const float *Sin = states + (bh * NC + c) * Epad;
-        const float *dSo = dstates + (bh * NC + c) * Epad;
-        regs_to_lds<CH, DVP, NTW, VPER, LDV>(vbuf, VPs);
-        regs_to_lds<CH, DVP, NTW, VPER, LDY>(ybuf, dYs);
-        const float blh = blpre;   // chunk total of this head (threads < 64)
-        if (threadIdx.x < CH) {
-            const int t = threadIdx.x;
-            bs[t] = bpre;
-            eb[t] = expf(bpre);
-            el[t] = (t < rows) ? expf(blh - bpre) : 0.f;
-        }
-        if (hh + 1 < hpg) prefetch(hh + 1);
-        __syncthreads();
+        const float bcur = bpre, blh = blpre;
+        float fro = fro_next;
 
-        // (1) state terms (operands from the workspace slabs) and, on six
-        //     waves, half-contractions of dY V^T.
-        f32x16 aQ = zero16(), aK = zero16(), aD = zero16();
-        if (wave < 6) {
-            const int n0 = half * (DVP / 2);
-#pragma unroll 4
-            for (int nn = n0; nn < n0 + DVP / 2; nn += 2)
-                aD = mfma32(dYs[(ib * 32 + cl) * LDY + nn + kh], VPs[(jb * 32 + cl) * LDV + nn + kh], aD);
-        }
-        if (hasK) {
-            // dY S_in^T : B(n, i) = S_in[i][n]
-            mma_bt_global<DVP, LDY>(aQ, dYs, rbk * 32, Sin, colk, dk_, dv_, dv_, vecV != 0, lane);
-            // V dS_out^T : B(n, i) = dS_out[i][n]
-            mma_bt_global<DVP, LDV>(aK, VPs, rbk * 32, dSo, colk, dk_, dv_, dv_, vecV != 0, lane);
-        }
-        __syncthreads();   // all reads of V done
-        if (wave >= 3 && wave < 6) {
+        // ---- state phase
+        f32x16 gq = zero16(), gk = zero16();
+        f32x4 gv[NSL];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) VPs[tile * 1024 + r * 64 + lane] = aD[r];
-        }
-        __syncthreads();
-        f32x16 pP = zero16(), pM = zero16();
-        if (wave < 3) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float a = aD[r] + VPs[tile * 1024 + r * 64 + lane];
-                const int i = ib * 32 + acc_row(r, lane), j = jb * 32 + cl;
-                const float D = (j <= i) ? expf(bs[i] - bs[j]) : 0.f;
-                dPs[i * LDP + j] = a * D;
-                pP[r] = accA[r] * D;
-                pM[r] = pP[r] * a;
+        for (int m = 0; m < NSL; ++m) {
+            if (m > 0) {
+                __syncthreads();   // slab m - 1 fully read
+                fro += store_slab(tid);
             }
+            if (m + 1 < NSL)
+                load_slab(hh, m + 1, tid);
+            else
+                tile_to_regs<CH, DKP, NTW, QPER>(tid, qbuf, qsrc, rows, dk_, vk);
+            if (m > 0) __syncthreads();
+            if (hasK) {
+                mma_abt<LDV, LSL>(gq, RY + rbk * 32 * LDV + 32 * m, slS + cbk * 32 * LSL, 0, 32, lane);
+                mma_abt<LDV, LSL>(gk, RV + rbk * 32 * LDV + 32 * m, slD + cbk * 32 * LSL, 0, 32, lane);
+            }
+            // Gv tile: positions 16 rt .. 16 rt + 15, state columns 32 m + 16 ct .. + 15
+            const int rt = ((wave >> 1) + m) & 3, ct = wave & 1;
+            const float *ak = RK + (16 * rt + l16) * LDK + 4 * lq;
+            const float *bd = slD + 4 * lq * LSL + 16 * ct + l16;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+            for (int i0 = 0; i0 < DKP; i0 += 16) {
+                const float4 a = *reinterpret_cast<const float4 *>(ak + i0);
+                acc = mfma16(a.x, bd[(i0 + 0) * LSL], acc);
+                acc = mfma16(a.y, bd[(i0 + 1) * LSL], acc);
+                acc = mfma16(a.z, bd[(i0 + 2) * LSL], acc);
+                acc = mfma16(a.w, bd[(i0 + 3) * LSL], acc);
+            }
+            gv[m] = acc;
+        }
+
+        // ---- intra phase
+        __syncthreads();   // slab reads done
+        regs_to_lds<CH, DKP, NTW, QPER, LDK>(tid, qbuf, RQ);
+        if (tid < CH) {
+            bs[tid] = bcur;
+            eb[tid] = expf(bcur);
+            el[tid] = (tid < rows) ? expf(blh - bcur) : 0.f;
+        }
+        if (hh + 1 < hpg) {
+            load_vy(hh + 1, tid);
+            load_slab(hh + 1, 0, tid);
         }
         __syncthreads();
 
-        // (2) dQ_h and dK_h; per-row state terms of dlog_alpha.
+        // state parts of dQ and dK, and their rows' dlog_alpha terms
         if (hasK) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int row = rbk * 32 + acc_row(r, lane);
-                aQ[r] *= eb[row];
-                aK[r] *= el[row];
-                // e^{b_i} q_i.(dY S_in^T)_i and e^{b_L-b_j} k_j.(V dS_out^T)_j, partial over this column tile
-                const float sq = sum32(aQ[r] * Qs[row * LDK + colk]);
-                const float sk = sum32(aK[r] * Ks[row * LDK + colk]);
+                gq[r] *= eb[row];
+                gk[r] *= el[row];
+                const float sq = sum32(gq[r] * RQ[row * LDK + cbk * 32 + cl]);
+                const float sk = sum32(gk[r] * RK[row * LDK + cbk * 32 + cl]);
                 if (cl == 0) {
                     redQ[cbk][row] = sq;
                     redK[cbk][row] = sk;
                 }
             }
-            const int kend = (rbk + 1) * 32;
-            for (int jj = 0; jj < kend; jj += 2)
-                aQ = mfma32(dPs[(rbk * 32 + cl) * LDP + jj + kh], Ks[(jj + kh) * LDK + colk], aQ);
-            for (int jj = rbk * 32; jj < CH; jj += 2)
-                aK = mfma32(dPs[(jj + kh) * LDP + rbk * 32 + cl], Qs[(jj + kh) * LDK + colk], aK);
-            dQacc += aQ;
-            dKacc += aK;
+            dQacc += gq;
+            dKacc += gk;
         }
-        __syncthreads();   // dP is dead; P goes where V was, M where dP was
-
+#pragma unroll
+        for (int m = 0; m < NSL; ++m) {
+            const int rt = ((wave >> 1) + m) & 3;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) gv[m][r] *= el[16 * rt + 4 * lq + r];
+        }
+        // dY V^T, causal tiles; waves w and w + 3 split dv
+        f32x16 aD = zero16();
+        if (wave < 6)
+            mma_abt<LDV, LDV>(aD, RY + aib * 32 * LDV, RV + ajb * 32 * LDV, ah * (DVP / 2), (ah + 1) * (DVP / 2),
+                              lane);
+        __syncthreads();   // V reads done
+        if (wave >= 3 && wave < 6) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) RV[at * 1024 + r * 64 + lane] = aD[r];
+        }
+        __syncthreads();
+        f32x16 pM = zero16();
         if (wave < 3) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int i = ib * 32 + acc_row(r, lane), j = jb * 32 + cl;
-                VPs[i * LDV + j] = pP[r];
-                dPs[i * LDP + j] = pM[r];
+                const int i = aib * 32 + acc_row(r, lane), j = ajb * 32 + cl;
+                const float a = aD[r] + RV[at * 1024 + r * 64 + lane];
+                const float D = (j <= i) ? expf(bs[i] - bs[j]) : 0.f;
+                const float p = accA[r] * D;
+                RP[i * LDP + j] = a * D;   // dP
+                Pm[i * LDP + j] = p;       // P
+                pM[r] = p * a;             // M
             }
-        } else if (wave == 3) {
-            // upper-right tile of M is zero (j > i)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) dPs[acc_row(r, lane) * LDP + 32 + cl] = 0.f;
         }
         __syncthreads();
 
-        // (3) dV_h = diag(e^{bL-b}) K dS_out + P^T dY.
-        if (hasV) {
-            f32x16 aV = zero16();
-            // K dS_out : B(i, n) = dS_out[i][n]
-            mma_b_global<DKP, LDK>(aV, Ks, rbv * 32, dSo, colv, dv_, dk_, dv_, lane);
+        if (hasK) {
+            // dQ += dP K over j <= i
+            {
+                const float *a = RP + (rbk * 32 + cl) * LDP + 4 * (lane >> 5);
+                const float *bk = RK + 4 * (lane >> 5) * LDK + cbk * 32 + cl;
+                const int jend = (rbk + 1) * 32;
+                for (int j0 = 0; j0 < jend; j0 += 8) {
+                    const float4 x = *reinterpret_cast<const float4 *>(a + j0);
+                    dQacc = mfma32(x.x, bk[(j0 + 0) * LDK], dQacc);
+                    dQacc = mfma32(x.y, bk[(j0 + 1) * LDK], dQacc);
+                    dQacc = mfma32(x.z, bk[(j0 + 2) * LDK], dQacc);
+                    dQacc = mfma32(x.w, bk[(j0 + 3) * LDK], dQacc);
+                }
+            }
+            // dK += dP^T Q over j >= i
+            {
+                const float *a = RP + 4 * (lane >> 5) * LDP + rbk * 32 + cl;
+                const float *bq = RQ + 4 * (lane >> 5) * LDK + cbk * 32 + cl;
+                for (int j0 = rbk * 32; j0 < CH; j0 += 8) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) aV[r] *= el[rbv * 32 + acc_row(r, lane)];
-            for (int jj = rbv * 32; jj < CH; jj += 2)
-                aV = mfma32(VPs[(jj + kh) * LDV + rbv * 32 + cl], dYs[(jj + kh) * LDY + colv], aV);
-            if (colv < dv_) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = rbv * 32 + acc_row(r, lane);
-                    if (row < rows) dv[(bh * T + c * CH + row) * dv_ + colv] = aV[r];
+                    for (int s = 0; s < 4; ++s) dKacc = mfma32(a[(j0 + s) * LDP], bq[(j0 + s) * LDK], dKacc);
                 }
             }
         }
+        // dV = Gv + P^T dY over j >= t, written per 16x16 tile
+        float *dvb = dv + (bh * T + c * CH) * dv_;
+#pragma unroll
+        for (int m = 0; m < NSL; ++m) {
+            const int rt = ((wave >> 1) + m) & 3, ct = wave & 1;
+            f32x4 acc = gv[m];
+            const float *a = Pm + 4 * lq * LDP + 16 * rt + l16;
+            const float *by = RY + 4 * lq * LDV + 32 * m + 16 * ct + l16;
+            for (int j0 = 16 * rt; j0 < CH; j0 += 16) {
+#pragma unroll
+                for (int s = 0; s < 4; ++s) acc = mfma16(a[(j0 + s) * LDP], by[(j0 + s) * LDV], acc);
+            }
+            const int n = 32 * m + 16 * ct + l16;
+            if (n < dv_) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 16 * rt + 4 * lq + r;
+                    if (t < rows) dvb[(uint32_t)(t * dv_ + n)] = acc[r];
+                }
+            }
+        }
+        __syncthreads();   // dP, P, Q and dY reads done
 
-        // (4) Rectangle sums R_r = sum_{i >= r} sum_{j < r} M_ij: exclusive
-        //     prefix over j of every row (in place), then a suffix over i.
+        // M to LDS (its upper-right tile is zero); the next head's V, dY, first slab
+        if (wave < 3) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) RP[(aib * 32 + acc_row(r, lane)) * LDP + ajb * 32 + cl] = pM[r];
+        } else if (wave == 3) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) RP[acc_row(r, lane) * LDP + 32 + cl] = 0.f;
+        }
+        if (hh + 1 < hpg) {
+            regs_to_lds<CH, DVP, NTW, TPER, LDV>(tid, vbuf, RV);
+            regs_to_lds<CH, DVP, NTW, TPER, LDV>(tid, ybuf, RY);
+            fro_next = store_slab(tid);
+        }
+        __syncthreads();
+
+        // Rectangle sums R_r = sum_{i >= r} sum_{j < r} M_ij: exclusive prefix
+        // over j of every row (in place), then a suffix over i.
         for (int i = wave * 8; i < wave * 8 + 8; ++i) {
-            float x = dPs[i * LDP + lane];
+            float x = RP[i * LDP + lane];
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
                 const float yv = __shfl_up(x, off);
@@ -749,44 +884,29 @@ __global__ __launch_bounds__(NTW) void k_bwd_grads(
             // shift, not subtract: the diagonal term must not enter the prefix
             float xe = __shfl_up(x, 1);
             if (lane == 0) xe = 0.f;
-            dPs[i * LDP + lane] = xe;
+            RP[i * LDP + lane] = xe;
         }
         __syncthreads();
         {
             float racc = 0.f;
             for (int i = wave * 8; i < wave * 8 + 8; ++i)
-                if (i >= lane) racc += dPs[i * LDP + lane];
+                if (i >= lane) racc += RP[i * LDP + lane];
             redR[wave][lane] = racc;
         }
-
-        // <dS_out(c), S_in(c)>_F (dS_out is zero for the last chunk).
-        float part = 0.f;
-        if (c + 1 < NC) {
-            if ((E & 3) == 0) {
-                for (int64_t e = (int64_t)threadIdx.x * 4; e < E; e += NTW * 4) {
-                    const float4 x = *reinterpret_cast<const float4 *>(dSo + e);
-                    const float4 z = *reinterpret_cast<const float4 *>(Sin + e);
-                    part += x.x * z.x + x.y * z.y + x.z * z.z + x.w * z.w;
-                }
-            } else {
-                for (int64_t e = threadIdx.x; e < E; e += NTW) part += dSo[e] * Sin[e];
-            }
-        }
-        part = sum64(part);
-        if (lane == 0) redB[wave] = part;
+        fro = sum64(fro);
+        if (lane == 0) redB[wave] = fro;
         __syncthreads();
 
         if (wave == 0) {
-            float fro = 0.f, rint = 0.f;
+            float frob = 0.f, rint = 0.f;
 #pragma unroll
             for (int w = 0; w < NTW / 64; ++w) {
-                fro += redB[w];
+                frob += redB[w];
                 rint += redR[w][lane];
             }
-            const float ebl = expf(blh);
             float iq = 0.f, ik = 0.f;
 #pragma unroll
-            for (int cb = 0; cb < NCBK; ++cb) {
+            for (int cb = 0; cb < NKB; ++cb) {
                 iq += redQ[cb][lane];
                 ik += redK[cb][lane];
             }
@@ -801,19 +921,21 @@ __global__ __launch_bounds__(NTW) void k_bwd_grads(
             }
             float pke = __shfl_up(pk, 1);
             if (lane == 0) pke = 0.f;
-            if (lane < rows) dla[bh * T + c * CH + lane] = rint + sq + pke + ebl * fro;
+            if (lane < rows) dla[bh * T + c * CH + lane] = rint + sq + pke + expf(blh) * frob;
         }
-        __syncthreads();
     }
 
-    if (hasK && colk < dk_) {
+    if (hasK) {
+        const int colk = cbk * 32 + cl;
+        if (colk < dk_) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int row = rbk * 32 + acc_row(r, lane);
-            if (row < rows) {
-                const int64_t o = (bg * T + c * CH + row) * dk_ + colk;
-                dq[o] = dQacc[r];
-                dk[o] = dKacc[r];
+            for (int r = 0; r < 16; ++r) {
+                const int row = rbk * 32 + acc_row(r, lane);
+                if (row < rows) {
+                    const int64_t o = (bg * T + c * CH + row) * dk_ + colk;
+                    dq[o] = dQacc[r];
+                    dk[o] = dKacc[r];
+                }
             }
         }
     }

@@ -56,6 +56,15 @@ __device__ __forceinline__ f32x16 mfma32(float a, float b, f32x16 c)
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
+// v_mfma_f32_16x16x4f32: lane l supplies A[l%16][l/16] and B[l/16][l%16];
+// accumulator register r of lane l holds row 4*(l/16) + r, column l%16.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma16(float a, float b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
 // Row (within the 32x32 tile) of accumulator register r in lane `lane`.
 __device__ __forceinline__ int acc_row(int r, int lane)
 {
@@ -70,62 +79,54 @@ __device__ __forceinline__ f32x16 zero16()
     return z;
 }
 
-// Sum over the 32 lanes that share lane/32 (fixed butterfly order).
-__device__ __forceinline__ float sum32(float x)
+// Cross-lane sums and scans with DPP (VALU data-parallel primitives, no LDS
+// traffic).  dpp_add<C, R>(x) adds the value of the lane that DPP control C
+// selects, or 0 where it selects none or the row (16 lanes) is not in mask R.
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ float dpp_add(float x)
 {
-    x += __shfl_xor(x, 16);
-    x += __shfl_xor(x, 8);
-    x += __shfl_xor(x, 4);
-    x += __shfl_xor(x, 2);
-    x += __shfl_xor(x, 1);
-    return x;
+    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROWS, 0xf, true));
+}
+constexpr int kRowShr = 0x110, kRowRor = 0x120, kRowBcast15 = 0x142, kRowBcast31 = 0x143, kWaveShr1 = 0x138;
+
+// Sum of each 32-lane half: the result is in lanes 31 (lanes 0-31) and 63
+// (lanes 32-63).
+__device__ __forceinline__ float sum32_hi(float x)
+{
+    x = dpp_add<kRowRor + 8>(x);
+    x = dpp_add<kRowRor + 4>(x);
+    x = dpp_add<kRowRor + 2>(x);
+    x = dpp_add<kRowRor + 1>(x);          // every lane: the sum of its row
+    return dpp_add<kRowBcast15, 0xa>(x);  // rows 1 and 3 add rows 0 and 2
 }
 
-__device__ __forceinline__ float sum64(float x)
+// Sum of all 64 lanes, in lane 63.
+__device__ __forceinline__ float sum64_hi(float x)
 {
-    x += __shfl_xor(x, 32);
-    return sum32(x);
+    x = sum32_hi(x);
+    return dpp_add<kRowBcast31, 0xc>(x);  // rows 2 and 3 add lane 31
+}
+
+// Inclusive prefix sum over the 64 lanes (lane l: x_0 + ... + x_l).
+__device__ __forceinline__ float scan64(float x)
+{
+    x = dpp_add<kRowShr + 1>(x);
+    x = dpp_add<kRowShr + 2>(x);
+    x = dpp_add<kRowShr + 4>(x);
+    x = dpp_add<kRowShr + 8>(x);          // prefix within each row
+    x = dpp_add<kRowBcast15, 0xa>(x);
+    return dpp_add<kRowBcast31, 0xc>(x);
+}
+
+// The value of lane l - 1 (0 in lane 0).
+__device__ __forceinline__ float shift_up1(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kWaveShr1, 0xf, 0xf, true));
 }
 
 __device__ __forceinline__ float readlane_f(float x, int l)
 {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
-}
-
-// Copy rows [0, rows) x cols [0, d) of a row-major global tile with row
-// stride d into LDS dst[CH][LD]; columns d..DP-1 and rows >= rows become 0.
-// Each row is optionally scaled by w[row] (LDS).
-template <int DP, int LD, bool SCALE, int NT = NTH>
-__device__ __forceinline__ void stage_rows(float *dst, const float *__restrict__ src, int rows, int d,
-                                           bool vec, const float *w)
-{
-    if (vec) {
-        constexpr int Q4 = DP / 4;
-        for (int idx = threadIdx.x; idx < CH * Q4; idx += NT) {
-            const int t = idx / Q4, c4 = (idx - t * Q4) * 4;
-            float4 val = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (t < rows && c4 < d) val = *reinterpret_cast<const float4 *>(src + (size_t)t * d + c4);
-            if (SCALE) {
-                const float s = w[t];
-                val.x *= s;
-                val.y *= s;
-                val.z *= s;
-                val.w *= s;
-            }
-            float *p = dst + t * LD + c4;
-            p[0] = val.x;
-            p[1] = val.y;
-            p[2] = val.z;
-            p[3] = val.w;
-        }
-    } else {
-        for (int idx = threadIdx.x; idx < CH * DP; idx += NT) {
-            const int t = idx / DP, cc = idx - t * DP;
-            float val = (t < rows && cc < d) ? src[(size_t)t * d + cc] : 0.f;
-            if (SCALE) val *= w[t];
-            dst[t * LD + cc] = val;
-        }
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -159,34 +160,62 @@ constexpr int NTW = 512;   // 8 waves per block
 
 __device__ __forceinline__ float4 zero4() { return make_float4(0.f, 0.f, 0.f, 0.f); }
 
-// row[c4 .. c4+3] of the row starting at base + rowoff, which has `lim`
-// valid entries (the rest read as 0).  `base` is uniform across the wave and
-// the per-lane offset is 32-bit, so the load addresses from a scalar base.
-// vec: one aligned 16-byte load (requires lim % 4 == 0 and an aligned row).
-__device__ __forceinline__ float4 load4(const float *__restrict__ base, uint32_t rowoff, int c4, int lim, bool vec)
+// Global memory goes through buffer resources: a resource covers `bytes`
+// bytes from a base address, and a lane whose byte offset is at or past the
+// end (kOOB is always past it) reads 0 and has its store dropped by the
+// hardware.  Tile edges are masked that way, without branches, so the loads
+// of a tile issue back to back and the compiler's count of memory operations
+// in flight stays exact.  Every resource covers one tile, slab or row, far
+// below 2 GiB.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOOB = 0x80000000u;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, int64_t bytes)
 {
-    const float *p = base + (rowoff + (uint32_t)c4);
-    if (vec) return (c4 < lim) ? *reinterpret_cast<const float4 *>(p) : zero4();
-    float4 r;
-    r.x = (c4 + 0 < lim) ? p[0] : 0.f;
-    r.y = (c4 + 1 < lim) ? p[1] : 0.f;
-    r.z = (c4 + 2 < lim) ? p[2] : 0.f;
-    r.w = (c4 + 3 < lim) ? p[3] : 0.f;
-    return r;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// Load a ROWS x DP tile (row-major, row stride d, `nrows` valid rows, d valid
-// columns) into registers, PER float4 per thread, zero padded.
+__device__ __forceinline__ float4 gload4(rsrc_t r, uint32_t off)
+{
+    const auto x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return make_float4(__int_as_float(x[0]), __int_as_float(x[1]), __int_as_float(x[2]), __int_as_float(x[3]));
+}
+
+__device__ __forceinline__ float gload1(rsrc_t r, uint32_t off)
+{
+    return __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
+__device__ __forceinline__ void gstore1(rsrc_t r, uint32_t off, float x)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(x), r, off, 0, 0);
+}
+
+// Elements c4 .. c4+3 of the row that starts at element `rowoff` of resource
+// r; the row has `lim` elements (the rest read as 0), and nothing is read
+// when `ok` is false.  vec: one 16-byte load (lim % 4 == 0, rows 16-byte
+// aligned).
+__device__ __forceinline__ float4 load4(rsrc_t r, uint32_t rowoff, int c4, int lim, bool ok, bool vec)
+{
+    if (vec) return gload4(r, (ok && c4 < lim) ? (rowoff + (uint32_t)c4) * 4u : kOOB);
+    float e[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) e[i] = gload1(r, (ok && c4 + i < lim) ? (rowoff + (uint32_t)(c4 + i)) * 4u : kOOB);
+    return make_float4(e[0], e[1], e[2], e[3]);
+}
+
+// Load a ROWS x DP tile into registers, PER float4 per thread, zero padded:
+// row-major with row stride d and d valid columns, from resource r, which
+// covers exactly the valid rows (rows past them read as 0).
 template <int ROWS, int DP, int NT, int PER>
-__device__ __forceinline__ void tile_to_regs(int tid, float4 (&buf)[PER], const float *__restrict__ src, int nrows,
-                                             int d, bool vec)
+__device__ __forceinline__ void tile_to_regs(int tid, float4 (&buf)[PER], rsrc_t r, int d, bool vec)
 {
     constexpr int Q4 = DP / 4;
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
         const int idx = tid + u * NT;
-        const int r = idx / Q4, c4 = (idx - r * Q4) * 4;
-        buf[u] = (idx < ROWS * Q4 && r < nrows) ? load4(src, (uint32_t)(r * d), c4, d, vec) : zero4();
+        const int row = idx / Q4, c4 = (idx - row * Q4) * 4;
+        buf[u] = load4(r, (uint32_t)(row * d), c4, d, idx < ROWS * Q4, vec);
     }
 }
 
@@ -213,34 +242,40 @@ __device__ __forceinline__ void regs_to_lds(int tid, const float4 (&buf)[PER], f
     }
 }
 
-// Q K^T tiles of a chunk (causal 32x32 tiles (0,0), (1,0), (1,1)), the dk
-// contraction split over six waves: waves 0-2 end up holding the full tile
-// (w % 3), the partial sums of waves 3-5 pass through `scratch` (3 x 1024).
-template <int DKP, int LDQ, int LDK>
-__device__ __forceinline__ f32x16 qk_tiles(const float *Qs, const float *Ks, float *scratch, int wave, int lane)
+// acc += A B^T over k in [k0, k1) (a multiple of 8 long): A and B are the
+// 32-row blocks starting at A and B (row-major in LDS, row strides LDA and
+// LDB).  Lane (kh, r) reads k0 + 4kh .. k0 + 4kh + 3 of its rows with one
+// 16-byte load and feeds them to four MFMAs; MFMA s contracts over the k
+// pair (k0 + s, k0 + 4 + s).
+template <int LDA, int LDB>
+__device__ __forceinline__ void mma_abt(f32x16 &acc, const float *A, const float *B, int k0, int k1, int lane)
 {
     const int cl = lane & 31, kh = lane >> 5;
-    const int tile = wave % 3, half = wave / 3;
-    const int ib = (tile == 0) ? 0 : 1, jb = (tile == 2) ? 1 : 0;
-    f32x16 acc = zero16();
-    if (wave < 6) {
-        const int k0 = half * (DKP / 2);
-#pragma unroll 8
-        for (int kk = k0; kk < k0 + DKP / 2; kk += 2)
-            acc = mfma32(Qs[(ib * 32 + cl) * LDQ + kk + kh], Ks[(jb * 32 + cl) * LDK + kk + kh], acc);
-        if (wave >= 3) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) scratch[tile * 1024 + r * 64 + lane] = acc[r];
-        }
+    const float *a = A + cl * LDA + 4 * kh;
+    const float *b = B + cl * LDB + 4 * kh;
+#pragma unroll 2
+    for (int kk = k0; kk < k1; kk += 8) {
+        const float4 x = *reinterpret_cast<const float4 *>(a + kk);
+        const float4 y = *reinterpret_cast<const float4 *>(b + kk);
+        acc = mfma32(x.x, y.x, acc);
+        acc = mfma32(x.y, y.y, acc);
+        acc = mfma32(x.z, y.z, acc);
+        acc = mfma32(x.w, y.w, acc);
     }
-    __syncthreads();
-    if (wave < 3) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] += scratch[tile * 1024 + r * 64 + lane];
-    }
-    __syncthreads();
-    return acc;
 }
+
+// acc += A B^T for the 16-row blocks starting at A and B (row-major in LDS,
+// row strides LDA and LDB) over k in [k0, k1) (a multiple of 16 long), on
+// v_mfma_f32_16x16x4f32.  Lane (q, r) reads k0 + 4q .. k0 + 4q + 3 of its
+// rows with one 16-byte load; MFMA s contracts over k0 + s + {0, 4, 8, 12}.
+template <int LDA, int LDB>
+__device__ __forceinline__ void mma16_abt(f32x4 &acc, const float *A, const float *B, int k0, int k1, int lane);
+
+// The C x C tiles of Q K^T, dY V^T, P and dP are handled as a 4 x 4 grid of
+// 16x16 tiles, two per wave (tiles w and 15 - w of wave w, row-major), so
+// every wave forms the same number of elements and no partial sums cross
+// waves.  Tiles above the diagonal are zero.
+__device__ __forceinline__ int cc_tile(int wave, int u) { return u == 0 ? wave : 15 - wave; }
 
 // ---------------------------------------------------------------------------
 // K3 + K4 fused: sequential scan over chunks with the state held in MFMA
@@ -256,37 +291,66 @@ __device__ __forceinline__ f32x16 qk_tiles(const float *Qs, const float *Ks, flo
 // so the forward slabs hold S_in(c), the state entering chunk c, and the
 // reverse slabs hold dS_out(c), the gradient of the state leaving chunk c.
 // The chunk's own contribution is formed on the fly and never stored.
-// One block of 4 waves owns a 32 x TJ tile of one head's dk x dv state; the
-// next chunk's operand tiles are prefetched into registers while the current
-// chunk's MFMAs run, then written to the other half of a double-buffered LDS
-// tile.  Blocks of one (b, g) are placed on one XCD so that the group's q/k
-// and each head's v/dy tiles are shared through that XCD's L2.
+//
+// One block owns a 32 x TJ tile of one head's dk x dv state and has two
+// kinds of waves, one of each per SIMD:
+//   * four compute waves hold the state (each a 16 x TJ/2 slice) and per
+//     chunk read their operands from LDS, store the state and run the MFMAs;
+//   * four loader waves keep the operand tiles of the next PD chunks in
+//     flight in registers and per chunk write the next one, its rows scaled
+//     by the decay weights, into the other half of the double-buffered LDS
+//     tiles.
+// A loader wave's memory and exp work thus runs on its SIMD while the
+// compute wave's MFMAs do, and no compute wave ever waits on a global load.
+// The number of steps is rounded up to a multiple of PD with no-op steps
+// (zero operands, decay 1, stores dropped), so no load or store is
+// conditional and the compiler's count of loads in flight is exact.
+// A compute wave owns two 16x16 accumulator tiles whose columns interleave
+// (tile u holds the wave's columns 2j + u), so one 8-byte LDS read gives a
+// lane both B operands.  Blocks of one (b, g) are placed on one XCD so that
+// the group's q/k and each head's v/dy tiles are shared through its L2.
 constexpr int TI = 32;
+constexpr int NTS = 512;   // 4 compute + 4 loader waves
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ f32x4 mfma16(float a, float b, f32x4 c)
+template <int LDA, int LDB>
+__device__ __forceinline__ void mma16_abt(f32x4 &acc, const float *A, const float *B, int k0, int k1, int lane)
 {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    const int l16 = lane & 15, lq = lane >> 4;
+    const float *a = A + l16 * LDA + 4 * lq;
+    const float *b = B + l16 * LDB + 4 * lq;
+#pragma unroll 2
+    for (int kk = k0; kk < k1; kk += 16) {
+        const float4 x = *reinterpret_cast<const float4 *>(a + kk);
+        const float4 y = *reinterpret_cast<const float4 *>(b + kk);
+        acc = mfma16(x.x, y.x, acc);
+        acc = mfma16(x.y, y.y, acc);
+        acc = mfma16(x.z, y.z, acc);
+        acc = mfma16(x.w, y.w, acc);
+    }
 }
 
-template <int DKP, int DVP>
-__global__ __launch_bounds__(NTH) void k_state_scan(
+template <int DKP, int DVP, bool VEC>
+__global__ __launch_bounds__(NTS, 2) void k_state_scan(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
     const float *__restrict__ dy, const float *__restrict__ h0, const float *__restrict__ bcum,
     const float *__restrict__ bl, float *__restrict__ states, float *__restrict__ dstates,
     float *__restrict__ dh0, int G, int H, int64_t T, int dk, int dv, int64_t NC, int64_t NCp, int64_t Epad,
-    int64_t per_dir, int vecK, int vecV)
+    int64_t per_dir)
 {
     constexpr int TJ = DVP < 64 ? DVP : 64;
     constexpr int NTJ = DVP / TJ;
     constexpr int NTILE = (DKP / TI) * NTJ;
-    constexpr int LDA = TI + 16, LDB = TJ + 16;
+    constexpr int NU = TJ / 32;                       // accumulator tiles per compute wave (1 or 2)
+    constexpr int WC = TJ / 2;                        // columns per compute wave
+    constexpr int LDA = TI + 16;                      // A reads: rows 16 banks apart
+    constexpr int LDB = (NU == 2) ? TJ + 32 : TJ + 16;   // B reads: rows 32 (b64) / 16 (b32) banks apart
+    constexpr int NLT = 256;                          // loader threads
     constexpr int A4 = CH * TI / 4, B4 = CH * TJ / 4;
-    constexpr int APER = (A4 + NTH - 1) / NTH, BPER = (B4 + NTH - 1) / NTH;
-    constexpr int NB16 = (2 * (TJ / 16)) / 4;   // 16x16 accumulator tiles per wave
+    constexpr int APER = (A4 + NLT - 1) / NLT, BPER = (B4 + NLT - 1) / NLT;
+    constexpr int PD = 3;                             // chunks loaded ahead
     __shared__ __attribute__((aligned(16))) float As[2][CH * LDA];
     __shared__ __attribute__((aligned(16))) float Bs[2][CH * LDB];
+    __shared__ float decs[2];                         // e^{b_L} of the chunk in each half
 
     // XCD-aware order: consecutive logical blocks share blockIdx % 8.
     const int64_t nblk = gridDim.x;
@@ -300,141 +364,205 @@ __global__ __launch_bounds__(NTH) void k_state_scan(
     const int h = (int)(bh % H);
     const int64_t b = bh / H;
     const int g = h / (H / G);
-    const float *Asrc = (dir == 0 ? k : q) + (b * G + g) * T * dk + i0;
-    const float *Bsrc = (dir == 0 ? v : dy) + bh * T * dv + j0;
-    float *slab = (dir == 0 ? states : dstates) + bh * NC * Epad;
-    const float *bcb = bcum + bh * NC * CH;
-    const int lima = dk - i0, limb = dv - j0;
+    const int64_t E = (int64_t)dk * dv;
+    const int64_t NS = (NC + PD - 1) / PD * PD;       // steps, NC rounded up
+    const int wave = threadIdx.x >> 6;
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int l16 = lane & 15, q4 = lane >> 4;
-    const int rblk = wave & 1;                 // 16-row block of the tile
-    const int cblk0 = (wave >> 1) * NB16;      // first 16-column block
-
-    // operand prefetch for one chunk
-    float4 abuf[APER], bbuf[BPER];
-    float bt[BPER], blc = 0.f;
-    auto prefetch = [&](int64_t c) {
-        const int rows = (int)((T - c * CH) < CH ? (T - c * CH) : CH);
+    if (wave >= 4) {
+        // ---------------- loader waves
+        const int lt = threadIdx.x - 256;
+        const float *Asrc = (dir == 0 ? k : q) + (b * G + g) * T * dk;   // row 0, column 0
+        const float *Bsrc = (dir == 0 ? v : dy) + bh * T * dv;
+        const float *bcb = bcum + bh * NC * CH;
+        const int lima = dk - i0, limb = dv - j0;
+        struct Stage {
+            float4 a[APER], b[BPER];
+            float bt[BPER], blc;
+        };
+        Stage stg[PD];
+        // operands of step s (chunk c(s)); steps past the end load zeros
+        auto prefetch = [&](Stage &S, int64_t s) {
+            const bool live = s < NC;
+            const int64_t c = live ? (dir == 0 ? s : NC - 1 - s) : 0;
+            const int rows = (int)((T - c * CH) < CH ? (T - c * CH) : CH);
+            const rsrc_t ab = make_rsrc(Asrc + c * CH * dk, live ? (int64_t)rows * dk * 4 : 0);
+            const rsrc_t bb = make_rsrc(Bsrc + c * CH * dv, live ? (int64_t)rows * dv * 4 : 0);
+            const rsrc_t br = make_rsrc(bcb + c * CH, live ? CH * 4 : 0);
 #pragma unroll
-        for (int u = 0; u < APER; ++u) {
-            const int idx = threadIdx.x + u * NTH;
-            const int r = idx / (TI / 4), c4 = (idx - r * (TI / 4)) * 4;
-            abuf[u] = (idx < A4 && r < rows) ? load4(Asrc + c * CH * dk, (uint32_t)(r * dk), c4, lima, vecK != 0) : zero4();
+            for (int u = 0; u < APER; ++u) {
+                const int idx = lt + u * NLT;
+                const int r = idx / (TI / 4), c4 = (idx - r * (TI / 4)) * 4;
+                S.a[u] = load4(ab, (uint32_t)(r * dk + i0), c4, lima, idx < A4, VEC);
+            }
+#pragma unroll
+            for (int u = 0; u < BPER; ++u) {
+                const int idx = lt + u * NLT;
+                const int r = idx / (TJ / 4), c4 = (idx - r * (TJ / 4)) * 4;
+                S.b[u] = load4(bb, (uint32_t)(r * dv + j0), c4, limb, idx < B4, VEC);
+                S.bt[u] = gload1(br, idx < B4 ? (uint32_t)r * 4u : kOOB);
+            }
+            const float blc = bl[bh * NCp + c];
+            S.blc = live ? blc : 0.f;
+        };
+        // stage S into LDS half `buf`, B rows scaled by the decay weights
+        auto stage = [&](const Stage &S, int buf) {
+#pragma unroll
+            for (int u = 0; u < APER; ++u) {
+                const int idx = lt + u * NLT;
+                if (A4 % NLT == 0 || idx < A4) {
+                    const int r = idx / (TI / 4), c4 = (idx - r * (TI / 4)) * 4;
+                    *reinterpret_cast<float4 *>(&As[buf][r * LDA + c4]) = S.a[u];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < BPER; ++u) {
+                const int idx = lt + u * NLT;
+                if (B4 % NLT == 0 || idx < B4) {
+                    const int r = idx / (TJ / 4), c4 = (idx - r * (TJ / 4)) * 4;
+                    const float w = (dir == 0) ? expf(S.blc - S.bt[u]) : expf(S.bt[u]);
+                    float4 x = S.b[u];
+                    x.x *= w;
+                    x.y *= w;
+                    x.z *= w;
+                    x.w *= w;
+                    *reinterpret_cast<float4 *>(&Bs[buf][r * LDB + c4]) = x;
+                }
+            }
+            if (lt == 0) decs[buf] = expf(S.blc);
+        };
+        // step s: chunk s is published by the barrier; stage chunk s + 1
+        // into the other half and refill its registers with chunk s + 1 + PD
+        auto step = [&](int64_t s, int u) {
+            __syncthreads();
+            const int un = (u + 1) % PD;
+            stage(stg[un], (int)((s + 1) & 1));
+            prefetch(stg[un], s + 1 + PD);
+        };
+#pragma unroll
+        for (int u = 0; u < PD; ++u) prefetch(stg[u], u);
+        stage(stg[0], 0);
+        prefetch(stg[0], PD);
+        // the first PD steps are peeled so that the loop is entered with the
+        // loads in flight that it repeats with
+#pragma unroll
+        for (int u = 0; u < PD; ++u) step(u, u);
+        for (int64_t s0 = PD; s0 < NS; s0 += PD) {
+#pragma unroll
+            for (int u = 0; u < PD; ++u) step(s0 + u, u);
         }
-#pragma unroll
-        for (int u = 0; u < BPER; ++u) {
-            const int idx = threadIdx.x + u * NTH;
-            const int r = idx / (TJ / 4), c4 = (idx - r * (TJ / 4)) * 4;
-            bbuf[u] = (idx < B4 && r < rows) ? load4(Bsrc + c * CH * dv, (uint32_t)(r * dv), c4, limb, vecV != 0) : zero4();
-            bt[u] = (idx < B4) ? bcb[c * CH + r] : 0.f;
-        }
-        blc = bl[bh * NCp + c];
-    };
-
-    f32x4 acc[NB16];
-#pragma unroll
-    for (int u = 0; u < NB16; ++u) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = i0 + rblk * 16 + 4 * q4 + r, col = j0 + (cblk0 + u) * 16 + l16;
-            acc[u][r] = (dir == 0 && row < dk && col < dv) ? h0[bh * (int64_t)dk * dv + (int64_t)row * dv + col] : 0.f;
-        }
+        return;
     }
 
-    prefetch(dir == 0 ? 0 : NC - 1);
-    for (int64_t s = 0; s < NC; ++s) {
-        const int64_t c = (dir == 0) ? s : NC - 1 - s;
-        const int buf = (int)(s & 1);
-        // stage this chunk's operands; scale B rows by the decay weights
-#pragma unroll
-        for (int u = 0; u < APER; ++u) {
-            const int idx = threadIdx.x + u * NTH;
-            if (idx < A4) {
-                const int r = idx / (TI / 4), c4 = (idx - r * (TI / 4)) * 4;
-                *reinterpret_cast<float4 *>(&As[buf][r * LDA + c4]) = abuf[u];
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < BPER; ++u) {
-            const int idx = threadIdx.x + u * NTH;
-            if (idx < B4) {
-                const int r = idx / (TJ / 4), c4 = (idx - r * (TJ / 4)) * 4;
-                const float w = (dir == 0) ? expf(blc - bt[u]) : expf(bt[u]);
-                float4 x = bbuf[u];
-                x.x *= w;
-                x.y *= w;
-                x.z *= w;
-                x.w *= w;
-                *reinterpret_cast<float4 *>(&Bs[buf][r * LDB + c4]) = x;
-            }
-        }
-        const float decay = expf(blc);
-        if (s + 1 < NC) prefetch(dir == 0 ? c + 1 : c - 1);
-        __syncthreads();
+    // ---------------- compute waves
+    const int lane = threadIdx.x & 63;
+    const int l16 = lane & 15, q4 = lane >> 4;
+    const int rblk = wave & 1;              // 16-row block of the tile
+    const int wc0 = (wave >> 1) * WC;       // first column of this wave within the tile
+    float *slab = (dir == 0 ? states : dstates) + bh * NC * Epad;
 
-        // slab[c] = S (state entering the chunk in this direction)
-        float *dst = slab + c * Epad;
+    // byte offset of accumulator (u, r) in a dk x dv state, kOOB outside it
+    auto soff = [&](int u, int r) -> uint32_t {
+        const int row = i0 + rblk * 16 + 4 * q4 + r, col = j0 + wc0 + NU * l16 + u;
+        return (row < dk && col < dv) ? (uint32_t)(row * dv + col) * 4u : kOOB;
+    };
+    f32x4 acc[NU];
+    {
+        const rsrc_t hr = make_rsrc(h0 + bh * E, dir == 0 ? E * 4 : 0);   // the reverse pass starts at 0
 #pragma unroll
-        for (int u = 0; u < NB16; ++u) {
-            const int col = j0 + (cblk0 + u) * 16 + l16;
+        for (int u = 0; u < NU; ++u) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[u][r] = gload1(hr, soff(u, r));
+        }
+    }
+    const float *Ab0 = &As[0][q4 * LDA + rblk * 16 + l16];
+    const float *Bb0 = &Bs[0][q4 * LDB + wc0 + NU * l16];
+    for (int64_t s = 0; s < NS; ++s) {
+        const int buf = (int)(s & 1);
+        __syncthreads();   // chunk s staged in half `buf`
+        float av[CH / 4];
+        float bv[CH / 4][NU];
+        const float *Ab = Ab0 + buf * (CH * LDA);
+        const float *Bb = Bb0 + buf * (CH * LDB);
+#pragma unroll
+        for (int kk = 0; kk < CH / 4; ++kk) {
+            av[kk] = Ab[4 * kk * LDA];
+            if (NU == 2) {
+                const float2 t2 = *reinterpret_cast<const float2 *>(Bb + 4 * kk * LDB);
+                bv[kk][0] = t2.x;
+                bv[kk][NU - 1] = t2.y;
+            } else {
+                bv[kk][0] = Bb[4 * kk * LDB];
+            }
+        }
+        const float decay = decs[buf];
+        // slab[c] = S (state entering the chunk in this direction); no-op steps store nothing
+        const bool live = s < NC;
+        const rsrc_t dst = make_rsrc(slab + (live ? (dir == 0 ? s : NC - 1 - s) : 0) * Epad, live ? E * 4 : 0);
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int row = i0 + rblk * 16 + 4 * q4 + r;
-                if (row < dk && col < dv) dst[row * dv + col] = acc[u][r];
+                gstore1(dst, soff(u, r), acc[u][r]);
                 acc[u][r] *= decay;
             }
         }
         // S += A^T B over the chunk's 64 positions
-        const float *Ab = &As[buf][q4 * LDA + rblk * 16 + l16];
-        const float *Bb = &Bs[buf][q4 * LDB + cblk0 * 16 + l16];
-#pragma unroll 4
-        for (int kk = 0; kk < CH; kk += 4) {
-            const float a = Ab[kk * LDA];
 #pragma unroll
-            for (int u = 0; u < NB16; ++u) acc[u] = mfma16(a, Bb[kk * LDB + u * 16], acc[u]);
+        for (int kk = 0; kk < CH / 4; ++kk) {
+#pragma unroll
+            for (int u = 0; u < NU; ++u) acc[u] = mfma16(av[kk], bv[kk][u], acc[u]);
         }
     }
     if (dir == 1) {
+        const rsrc_t hr = make_rsrc(dh0 + bh * E, E * 4);
 #pragma unroll
-        for (int u = 0; u < NB16; ++u) {
-            const int col = j0 + (cblk0 + u) * 16 + l16;
+        for (int u = 0; u < NU; ++u) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = i0 + rblk * 16 + 4 * q4 + r;
-                if (row < dk && col < dv) dh0[bh * (int64_t)dk * dv + (int64_t)row * dv + col] = acc[u][r];
-            }
+            for (int r = 0; r < 4; ++r) gstore1(hr, soff(u, r), acc[u][r]);
         }
     }
 }
 
 // ---------------------------------------------------------------------------
 // K2 + K5: output of one chunk for every head of one group.
-// One block of 8 waves per (b,g,chunk).  Q K^T (causal 32x32 tiles) is
-// formed once and kept in registers.  Per head: the next head's V tile and
-// incoming state S_in are prefetched into registers while this head runs;
-// P = (Q K^T) o D goes to LDS; then each wave computes one 32x32 tile of
-// Y = P V + diag(e^b) (Q S_in) with every operand read from LDS.  For dv < 128
-// the Q S_in contraction is split over the spare waves and summed in a fixed
-// order.
+//
+// One block of 8 waves per (b, g, chunk).  Q K^T (causal 32x32 tiles) is
+// formed once and kept in the registers of waves 0-2.  Per head, P = (Q K^T) o D
+// goes to LDS next to the head's V, and S_in is streamed through LDS in
+// slabs of 32 state columns (double-buffered, the next slab loaded into
+// registers while the current one is in use).  For slab columns n every
+// wave computes one 16x16 tile of
+//     Y[:, n] = diag(e^b) Q S_in[:, n] + P V[:, n]
+// with its row block rotating over the slabs, so the causal P V work is the
+// same for every wave.  Every MFMA operand comes from LDS.
 template <int DKP, int DVP>
+struct OutCfg {
+    static constexpr int LDK = DKP + 4;   // Q, K
+    static constexpr int LDV = DVP + 4;   // V
+    static constexpr int LDP = CH + 4;    // P
+    static constexpr int LSL = 36;        // slab rows: 32 state columns + 4
+    static constexpr int NSL = DVP / 32;
+    static constexpr int KVN = (LDK > LDV ? LDK : LDV) * CH;
+    static constexpr int PN = CH * LDP;
+    static constexpr int TPER = (CH * DVP / 4 + NTW - 1) / NTW;
+    static constexpr int QPER = (CH * DKP / 4 + NTW - 1) / NTW;
+    static constexpr int SPER = (DKP * 8 + NTW - 1) / NTW;
+};
+
+template <int DKP, int DVP, bool VEC>
 __global__ __launch_bounds__(NTW) void k_chunk_output(const float *__restrict__ q, const float *__restrict__ k,
                                                       const float *__restrict__ v, const float *__restrict__ bcum,
                                                       const float *__restrict__ states, float *__restrict__ y,
                                                       int G, int H, int64_t T, int dk, int dv, int64_t NC,
-                                                      int64_t Epad, int vecK, int vecV)
+                                                      int64_t Epad)
 {
-    constexpr int LDQ = DKP + 1;
-    constexpr int LDKV = (DKP > DVP ? DKP : DVP) + 1;
-    constexpr int LDP = CH + 1;
-    constexpr int NCB = DVP / 32, NOB = 2 * NCB, KS = 8 / NOB;
-    constexpr int VPER = (CH * DVP / 4 + NTW - 1) / NTW;
-    constexpr int SPER = (DKP * DVP / 4 + NTW - 1) / NTW;
-    __shared__ float Qs[CH * LDQ];
-    __shared__ float KVs[CH * LDKV];
-    __shared__ __attribute__((aligned(16))) float Ss[DKP * DVP];
-    __shared__ float Ps[CH * LDP];
-    __shared__ float Red[KS > 1 ? (KS - 1) * NOB * 1024 : 1];
+    using Cfg = OutCfg<DKP, DVP>;
+    constexpr int LDK = Cfg::LDK, LDV = Cfg::LDV, LDP = Cfg::LDP, LSL = Cfg::LSL, NSL = Cfg::NSL;
+    constexpr int TPER = Cfg::TPER, QPER = Cfg::QPER, SPER = Cfg::SPER;
+    __shared__ __attribute__((aligned(16))) float RQ[CH * LDK];
+    __shared__ __attribute__((aligned(16))) float RKV[Cfg::KVN];   // K, then each head's V
+    __shared__ __attribute__((aligned(16))) float RP[Cfg::PN];     // Q K^T partial sums, then P
+    __shared__ __attribute__((aligned(16))) float SL[2][DKP * LSL];
     __shared__ float bs[CH], eb[CH];
 
     const int64_t c = blockIdx.x % NC;
@@ -444,81 +572,148 @@ __global__ __launch_bounds__(NTW) void k_chunk_output(const float *__restrict__ 
     const int hpg = H / G;
     const int64_t bh0 = b * H + (int64_t)g * hpg;
     const int rows = (int)((T - c * CH) < CH ? (T - c * CH) : CH);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int cl = lane & 31, kh = lane >> 5;
+    const int tid0 = threadIdx.x, wave = tid0 >> 6;
+    constexpr bool vk = VEC, vv = VEC;   // 16-byte loads (dk and dv multiples of 4)
 
-    float4 vbuf[VPER], sbuf[SPER];
-    float bpre = 0.f;
-    auto prefetch = [&](int hh) {
-        const int64_t bh = bh0 + hh;
-        tile_to_regs<CH, DVP, NTW, VPER>(threadIdx.x, vbuf, v + (bh * T + c * CH) * dv, rows, dv, vecV != 0);
-        tile_to_regs<DKP, DVP, NTW, SPER>(threadIdx.x, sbuf, states + (bh * NC + c) * Epad, dk, dv, vecV != 0);
-        if (threadIdx.x < CH) bpre = bcum[bh * NC * CH + c * CH + threadIdx.x];
+    const int64_t E = (int64_t)dk * dv;
+    float4 vbuf[TPER], sbuf[SPER];
+    float bpre = 0.f;   // b at position tid & 63 of the head being loaded
+    // Loads of head hh; hh == hpg (one past the last head) loads zeros, so the
+    // prefetches need no condition and the compiler's count of loads in
+    // flight stays exact.
+    auto load_v = [&](int hh, int tid) {
+        const bool live = hh < hpg;
+        const int64_t bh = bh0 + (live ? hh : 0);
+        tile_to_regs<CH, DVP, NTW, TPER>(
+            tid, vbuf, make_rsrc(v + (bh * T + c * CH) * dv, live ? (int64_t)rows * dv * 4 : 0), dv, vv);
+        bpre = gload1(make_rsrc(bcum + bh * NC * CH + c * CH, live ? CH * 4 : 0), (uint32_t)(tid & 63) * 4u);
     };
-    prefetch(0);
+    auto load_slab = [&](int hh, int m, int tid) {
+        const bool live = hh < hpg;
+        const rsrc_t src = make_rsrc(states + ((bh0 + (live ? hh : 0)) * NC + c) * Epad, live ? E * 4 : 0);
+        const int lim = dv - 32 * m;
+#pragma unroll
+        for (int u = 0; u < SPER; ++u) {
+            const int idx = tid + u * NTW;
+            const int r = idx >> 3, c4 = (idx & 7) * 4;
+            sbuf[u] = load4(src, (uint32_t)(r * dv + 32 * m), c4, lim, idx < DKP * 8 && r < dk, vv);
+        }
+    };
+    auto store_slab = [&](float *dst, int tid) {
+#pragma unroll
+        for (int u = 0; u < SPER; ++u) {
+            const int idx = tid + u * NTW;
+            if (idx < DKP * 8) {
+                const int r = idx >> 3, c4 = (idx & 7) * 4;
+                *reinterpret_cast<float4 *>(dst + r * LSL + c4) = sbuf[u];
+            }
+        }
+    };
 
-    stage_rows<DKP, LDQ, false, NTW>(Qs, q + (bg * T + c * CH) * dk, rows, dk, vecK != 0, nullptr);
-    stage_rows<DKP, LDKV, false, NTW>(KVs, k + (bg * T + c * CH) * dk, rows, dk, vecK != 0, nullptr);
+    // ---- block set-up: Q, K, A = Q K^T; the first head's V and slab in flight.
+    {
+        float4 qb[QPER];
+        tile_to_regs<CH, DKP, NTW, QPER>(tid0, qb, make_rsrc(q + (bg * T + c * CH) * dk, (int64_t)rows * dk * 4), dk,
+                                         vk);
+        regs_to_lds<CH, DKP, NTW, QPER, LDK>(tid0, qb, RQ);
+        tile_to_regs<CH, DKP, NTW, QPER>(tid0, qb, make_rsrc(k + (bg * T + c * CH) * dk, (int64_t)rows * dk * 4), dk,
+                                         vk);
+        regs_to_lds<CH, DKP, NTW, QPER, LDK>(tid0, qb, RKV);
+    }
+    load_v(0, tid0);
+    load_slab(0, 0, tid0);
     __syncthreads();
-    const f32x16 accA = qk_tiles<DKP, LDQ, LDKV>(Qs, KVs, Ps, wave, lane);
-    const int ib = (wave == 0) ? 0 : 1, jb = (wave == 2) ? 1 : 0;
+    // this wave's two 16x16 tiles of Q K^T
+    f32x4 accA[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int t = cc_tile(wave, u), ti = t >> 2, tj = t & 3;
+        accA[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (tj <= ti) mma16_abt<LDK, LDK>(accA[u], RQ + 16 * ti * LDK, RKV + 16 * tj * LDK, 0, DKP, tid0 & 63);
+    }
+    __syncthreads();   // K is dead
 
-    const int ob = wave % NOB, ks = wave / NOB;
-    const int rb = ob / NCB, cb = ob % NCB;
-    const int n = cb * 32 + cl;
     for (int hh = 0; hh < hpg; ++hh) {
+        // per-lane index arithmetic stays inside the loop (see k_bwd_grads)
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        const int lane = tid & 63, cl = lane & 31, l16 = lane & 15, lq = lane >> 4;
         const int64_t bh = bh0 + hh;
-        regs_to_lds<CH, DVP, NTW, VPER, LDKV>(threadIdx.x, vbuf, KVs);
-        regs_to_lds<DKP, DVP, NTW, SPER, DVP>(threadIdx.x, sbuf, Ss);
-        if (threadIdx.x < CH) {
-            bs[threadIdx.x] = bpre;
-            eb[threadIdx.x] = expf(bpre);
+        const rsrc_t yb = make_rsrc(y + (bh * T + c * CH) * dv, (int64_t)rows * dv * 4);
+
+        regs_to_lds<CH, DVP, NTW, TPER, LDV>(tid, vbuf, RKV);
+        if (tid < CH) {
+            bs[tid] = bpre;
+            eb[tid] = expf(bpre);
         }
-        if (hh + 1 < hpg) prefetch(hh + 1);
+        store_slab(SL[0], tid);
+        if (NSL > 1) {
+            load_slab(hh, 1, tid);
+        } else {
+            load_v(hh + 1, tid);
+            load_slab(hh + 1, 0, tid);
+        }
         __syncthreads();
-        if (wave < 3) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int i = ib * 32 + acc_row(r, lane), j = jb * 32 + cl;
-                Ps[i * LDP + j] = (j <= i) ? accA[r] * expf(bs[i] - bs[j]) : 0.f;
+        for (int u = 0; u < 2; ++u) {
+            const int t = cc_tile(wave, u), ti = t >> 2, tj = t & 3;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * ti + 4 * lq + r, j = 16 * tj + l16;
+                RP[i * LDP + j] = (j <= i) ? accA[u][r] * expf(bs[i] - bs[j]) : 0.f;
             }
         }
         __syncthreads();
 
-        f32x16 ay = zero16(), ai = zero16();
-        if (ks == 0) {
-            const int kend = (rb + 1) * 32;
-            for (int kk = 0; kk < kend; kk += 2)
-                ay = mfma32(Ps[(rb * 32 + cl) * LDP + kk + kh], KVs[(kk + kh) * LDKV + n], ay);
-        }
-        {
-            constexpr int KL = DKP / KS;
-            const int i0 = ks * KL;
-#pragma unroll 8
-            for (int i = i0; i < i0 + KL; i += 2)
-                ai = mfma32(Qs[(rb * 32 + cl) * LDQ + i + kh], Ss[(i + kh) * DVP + n], ai);
-        }
-        if (KS > 1) {
-            if (ks > 0) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) Red[((ks - 1) * NOB + ob) * 1024 + r * 64 + lane] = ai[r];
+        for (int m = 0; m < NSL; ++m) {
+            if (m > 0) {
+                store_slab(SL[m & 1], tid);
+                if (m + 1 < NSL) {
+                    load_slab(hh, m + 1, tid);
+                } else {
+                    load_v(hh + 1, tid);
+                    load_slab(hh + 1, 0, tid);
+                }
+                __syncthreads();
             }
-            __syncthreads();
-            if (ks == 0) {
-                for (int kk2 = 1; kk2 < KS; ++kk2) {
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) ai[r] += Red[((kk2 - 1) * NOB + ob) * 1024 + r * 64 + lane];
+            // tile: positions 16 rt .. 16 rt + 15, columns 32 m + 16 ct .. + 15
+            const int rt = ((wave >> 1) + m) & 3, ct = wave & 1;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            {
+                const float *aq = RQ + (16 * rt + l16) * LDK + 4 * lq;
+                const float *bsl = SL[m & 1] + 4 * lq * LSL + 16 * ct + l16;
+#pragma unroll 4
+                for (int i0 = 0; i0 < DKP; i0 += 16) {
+                    const float4 a = *reinterpret_cast<const float4 *>(aq + i0);
+                    acc = mfma16(a.x, bsl[(i0 + 0) * LSL], acc);
+                    acc = mfma16(a.y, bsl[(i0 + 1) * LSL], acc);
+                    acc = mfma16(a.z, bsl[(i0 + 2) * LSL], acc);
+                    acc = mfma16(a.w, bsl[(i0 + 3) * LSL], acc);
                 }
             }
-        }
-        if (ks == 0 && n < dv) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = rb * 32 + acc_row(r, lane);
-                if (row < rows) y[(bh * T + c * CH + row) * dv + n] = ay[r] + eb[row] * ai[r];
+            for (int r = 0; r < 4; ++r) acc[r] *= eb[16 * rt + 4 * lq + r];
+            {
+                const float *ap = RP + (16 * rt + l16) * LDP + 4 * lq;
+                const float *bv = RKV + 4 * lq * LDV + 32 * m + 16 * ct + l16;
+                const int jend = 16 * (rt + 1);
+                for (int j0 = 0; j0 < jend; j0 += 16) {
+                    const float4 a = *reinterpret_cast<const float4 *>(ap + j0);
+                    acc = mfma16(a.x, bv[(j0 + 0) * LDV], acc);
+                    acc = mfma16(a.y, bv[(j0 + 1) * LDV], acc);
+                    acc = mfma16(a.z, bv[(j0 + 2) * LDV], acc);
+                    acc = mfma16(a.w, bv[(j0 + 3) * LDV], acc);
+                }
+            }
+            const int n = 32 * m + 16 * ct + l16;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * rt + 4 * lq + r;   // rows past the sequence end fall outside yb
+                gstore1(yb, n < dv ? (uint32_t)(t * dv + n) * 4u : kOOB, acc[r]);
             }
         }
-        __syncthreads();
+        __syncthreads();   // V, P and slab reads done before the next head's writes
     }
 }
 
@@ -557,48 +752,25 @@ struct BwdCfg {
     static constexpr int NKB = DKP / 32;  // 32-column blocks of dk
     static constexpr int NTK = 2 * NKB;   // 32x32 tiles of a C x dk result
     static constexpr int NSL = DVP / 32;  // slabs per state
-    static constexpr int SCR = 3 * 1024;  // (dY V^T) partial sums, start of the V region
     static constexpr int QN = (CH * LDK > 2 * DKP * LSL) ? CH * LDK : 2 * DKP * LSL;
-    static constexpr int VN = (CH * LDV > SCR + CH * LDP) ? CH * LDV : SCR + CH * LDP;
-    static constexpr int PN = (CH * LDP > SCR) ? CH * LDP : SCR;
+    static constexpr int VN = (CH * LDV > CH * LDP) ? CH * LDV : CH * LDP;
+    static constexpr int PN = CH * LDP;
     static constexpr int TPER = (CH * DVP / 4 + NTW - 1) / NTW;   // float4 / thread, C x dv tile
     static constexpr int QPER = (CH * DKP / 4 + NTW - 1) / NTW;   // float4 / thread, C x dk tile
     static constexpr int SPER = (DKP * 8 + NTW - 1) / NTW;        // float4 / thread, one state slab
 };
 
-// acc += A B^T over k in [k0, k1) (a multiple of 8 long): A and B are the
-// 32-row blocks starting at A and B (row-major in LDS, row strides LDA and
-// LDB).  Lane (kh, r) reads k0 + 4kh .. k0 + 4kh + 3 of its rows with one
-// 16-byte load and feeds them to four MFMAs; MFMA s contracts over the k
-// pair (k0 + s, k0 + 4 + s).
-template <int LDA, int LDB>
-__device__ __forceinline__ void mma_abt(f32x16 &acc, const float *A, const float *B, int k0, int k1, int lane)
-{
-    const int cl = lane & 31, kh = lane >> 5;
-    const float *a = A + cl * LDA + 4 * kh;
-    const float *b = B + cl * LDB + 4 * kh;
-#pragma unroll 2
-    for (int kk = k0; kk < k1; kk += 8) {
-        const float4 x = *reinterpret_cast<const float4 *>(a + kk);
-        const float4 y = *reinterpret_cast<const float4 *>(b + kk);
-        acc = mfma32(x.x, y.x, acc);
-        acc = mfma32(x.y, y.y, acc);
-        acc = mfma32(x.z, y.z, acc);
-        acc = mfma32(x.w, y.w, acc);
-    }
-}
-
-template <int DKP, int DVP>
+template <int DKP, int DVP, bool VEC>
 __global__ __launch_bounds__(NTW) void k_bwd_grads(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
     const float *__restrict__ dy, const float *__restrict__ bcum, const float *__restrict__ bl,
     const float *__restrict__ states, const float *__restrict__ dstates, float *__restrict__ dq,
     float *__restrict__ dk, float *__restrict__ dv, float *__restrict__ dla, int G, int H, int64_t T, int dk_,
-    int dv_, int64_t NC, int64_t NCp, int64_t Epad, int vecK, int vecV)
+    int dv_, int64_t NC, int64_t NCp, int64_t Epad)
 {
     using Cfg = BwdCfg<DKP, DVP>;
     constexpr int LDK = Cfg::LDK, LDV = Cfg::LDV, LDP = Cfg::LDP, LSL = Cfg::LSL;
-    constexpr int NKB = Cfg::NKB, NTK = Cfg::NTK, NSL = Cfg::NSL, SCR = Cfg::SCR;
+    constexpr int NKB = Cfg::NKB, NTK = Cfg::NTK, NSL = Cfg::NSL;
     constexpr int TPER = Cfg::TPER, QPER = Cfg::QPER, SPER = Cfg::SPER;
     __shared__ __attribute__((aligned(16))) float RQ[Cfg::QN];
     __shared__ __attribute__((aligned(16))) float RK[CH * LDK];
@@ -611,7 +783,7 @@ __global__ __launch_bounds__(NTW) void k_bwd_grads(
     __shared__ float redB[NTW / 64];
     float *const slS = RQ;               // S_in slab   [DKP][LSL]
     float *const slD = RQ + DKP * LSL;   // dS_out slab [DKP][LSL]
-    float *const Pm = RV + SCR;          // P           [CH][LDP]
+    float *const Pm = RV;                // P           [CH][LDP] (after V)
 
     const int64_t c = blockIdx.x % NC;
     const int64_t bg = blockIdx.x / NC;
@@ -623,33 +795,39 @@ __global__ __launch_bounds__(NTW) void k_bwd_grads(
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int cl = lane & 31;
     const int l16 = lane & 15, lq = lane >> 4;
-    const bool vk = vecK != 0, vv = vecV != 0;
-    const float *qsrc = q + (bg * T + c * CH) * dk_;
+    constexpr bool vk = VEC, vv = VEC;   // 16-byte loads (dk and dv multiples of 4)
+    const int64_t E = (int64_t)dk_ * dv_;
+    const rsrc_t qsrc = make_rsrc(q + (bg * T + c * CH) * dk_, (int64_t)rows * dk_ * 4);
 
     float4 vbuf[TPER], ybuf[TPER];   // a head's V and dY
     float4 sbuf[SPER], dbuf[SPER];   // a slab of S_in and of dS_out
     float4 qbuf[QPER];               // Q
     float bpre = 0.f, blpre = 0.f;   // a head's b (thread t < 64: position t) and b_L
 
+    // Loads of head hh; hh == hpg (one past the last head) loads zeros, so the
+    // prefetches need no condition and the compiler's count of loads in
+    // flight stays exact.
     auto load_vy = [&](int hh, int tid) {
-        const int64_t bh = bh0 + hh;
-        tile_to_regs<CH, DVP, NTW, TPER>(tid, vbuf, v + (bh * T + c * CH) * dv_, rows, dv_, vv);
-        tile_to_regs<CH, DVP, NTW, TPER>(tid, ybuf, dy + (bh * T + c * CH) * dv_, rows, dv_, vv);
-        if (tid < CH) {
-            bpre = bcum[bh * NC * CH + c * CH + tid];
-            blpre = bl[bh * NCp + c];
-        }
+        const bool live = hh < hpg;
+        const int64_t bh = bh0 + (live ? hh : 0);
+        const int64_t tb = live ? (int64_t)rows * dv_ * 4 : 0;
+        tile_to_regs<CH, DVP, NTW, TPER>(tid, vbuf, make_rsrc(v + (bh * T + c * CH) * dv_, tb), dv_, vv);
+        tile_to_regs<CH, DVP, NTW, TPER>(tid, ybuf, make_rsrc(dy + (bh * T + c * CH) * dv_, tb), dv_, vv);
+        bpre = gload1(make_rsrc(bcum + bh * NC * CH + c * CH, live ? CH * 4 : 0), (uint32_t)(tid & 63) * 4u);
+        blpre = bl[bh * NCp + c];
     };
     auto load_slab = [&](int hh, int m, int tid) {
-        const int64_t off = ((bh0 + hh) * NC + c) * Epad + 32 * m;
+        const bool live = hh < hpg;
+        const int64_t off = ((bh0 + (live ? hh : 0)) * NC + c) * Epad;
+        const rsrc_t sr = make_rsrc(states + off, live ? E * 4 : 0), dr = make_rsrc(dstates + off, live ? E * 4 : 0);
         const int lim = dv_ - 32 * m;
 #pragma unroll
         for (int u = 0; u < SPER; ++u) {
             const int idx = tid + u * NTW;
             const int r = idx >> 3, c4 = (idx & 7) * 4;
             const bool ok = idx < DKP * 8 && r < dk_;
-            sbuf[u] = ok ? load4(states + off, (uint32_t)(r * dv_), c4, lim, vv) : zero4();
-            dbuf[u] = ok ? load4(dstates + off, (uint32_t)(r * dv_), c4, lim, vv) : zero4();
+            sbuf[u] = load4(sr, (uint32_t)(r * dv_ + 32 * m), c4, lim, ok, vv);
+            dbuf[u] = load4(dr, (uint32_t)(r * dv_ + 32 * m), c4, lim, ok, vv);
         }
     };
     // Write the staged slab to LDS; returns this thread's part of <dS_out, S_in>.
@@ -671,28 +849,22 @@ __global__ __launch_bounds__(NTW) void k_bwd_grads(
 
     // ---- block set-up: K, Q, A = Q K^T, the first head's V, dY and slab.
     load_vy(0, tid);
-    tile_to_regs<CH, DKP, NTW, QPER>(tid, qbuf, qsrc, rows, dk_, vk);
+    tile_to_regs<CH, DKP, NTW, QPER>(tid, qbuf, qsrc, dk_, vk);
     regs_to_lds<CH, DKP, NTW, QPER, LDK>(tid, qbuf, RQ);
-    tile_to_regs<CH, DKP, NTW, QPER>(tid, qbuf, k + (bg * T + c * CH) * dk_, rows, dk_, vk);
+    tile_to_regs<CH, DKP, NTW, QPER>(tid, qbuf, make_rsrc(k + (bg * T + c * CH) * dk_, (int64_t)rows * dk_ * 4), dk_,
+                                     vk);
     regs_to_lds<CH, DKP, NTW, QPER, LDK>(tid, qbuf, RK);
     load_slab(0, 0, tid);
     __syncthreads();
-    // causal 32x32 tiles (0,0), (1,0), (1,1) of Q K^T; waves w and w + 3 split dk
-    const int at = wave % 3, ah = wave / 3;
-    const int aib = (at == 0) ? 0 : 1, ajb = (at == 2) ? 1 : 0;
-    f32x16 accA = zero16();
-    if (wave < 6)
-        mma_abt<LDK, LDK>(accA, RQ + aib * 32 * LDK, RK + ajb * 32 * LDK, ah * (DKP / 2), (ah + 1) * (DKP / 2),
-                          lane);
-    if (wave >= 3 && wave < 6) {
+    // this wave's two 16x16 tiles of Q K^T
+    f32x4 accA[2];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) RP[at * 1024 + r * 64 + lane] = accA[r];
+    for (int u = 0; u < 2; ++u) {
+        const int t = cc_tile(wave, u), ti = t >> 2, tj = t & 3;
+        accA[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (tj <= ti) mma16_abt<LDK, LDK>(accA[u], RQ + 16 * ti * LDK, RK + 16 * tj * LDK, 0, DKP, lane);
     }
-    __syncthreads();
-    if (wave < 3) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) accA[r] += RP[at * 1024 + r * 64 + lane];
-    }
+    __syncthreads();   // Q reads done before the slab overwrites it
     regs_to_lds<CH, DVP, NTW, TPER, LDV>(tid, vbuf, RV);
     regs_to_lds<CH, DVP, NTW, TPER, LDV>(tid, ybuf, RY);
     float fro_next = store_slab(tid);
@@ -725,7 +897,7 @@ __global__ __launch_bounds__(NTW) void k_bwd_grads(
             if (m + 1 < NSL)
                 load_slab(hh, m + 1, tid);
             else
-                tile_to_regs<CH, DKP, NTW, QPER>(tid, qbuf, qsrc, rows, dk_, vk);
+                tile_to_regs<CH, DKP, NTW, QPER>(tid, qbuf, qsrc, dk_, vk);
             if (m > 0) __syncthreads();
             if (hasK) {
                 mma_abt<LDV, LSL>(gq, RY + rbk * 32 * LDV + 32 * m, slS + cbk * 32 * LSL, 0, 32, lane);
@@ -755,10 +927,8 @@ __global__ __launch_bounds__(NTW) void k_bwd_grads(
             eb[tid] = expf(bcur);
             el[tid] = (tid < rows) ? expf(blh - bcur) : 0.f;
         }
-        if (hh + 1 < hpg) {
-            load_vy(hh + 1, tid);
-            load_slab(hh + 1, 0, tid);
-        }
+        load_vy(hh + 1, tid);
+        load_slab(hh + 1, 0, tid);
         __syncthreads();
 
         // state parts of dQ and dK, and their rows' dlog_alpha terms
@@ -768,9 +938,9 @@ __global__ __launch_bounds__(NTW) void k_bwd_grads(
                 const int row = rbk * 32 + acc_row(r, lane);
                 gq[r] *= eb[row];
                 gk[r] *= el[row];
-                const float sq = sum32(gq[r] * RQ[row * LDK + cbk * 32 + cl]);
-                const float sk = sum32(gk[r] * RK[row * LDK + cbk * 32 + cl]);
-                if (cl == 0) {
+                const float sq = sum32_hi(gq[r] * RQ[row * LDK + cbk * 32 + cl]);
+                const float sk = sum32_hi(gk[r] * RK[row * LDK + cbk * 32 + cl]);
+                if (cl == 31) {
                     redQ[cbk][row] = sq;
                     redK[cbk][row] = sk;
                 }
@@ -784,28 +954,27 @@ __global__ __launch_bounds__(NTW) void k_bwd_grads(
 #pragma unroll
             for (int r = 0; r < 4; ++r) gv[m][r] *= el[16 * rt + 4 * lq + r];
         }
-        // dY V^T, causal tiles; waves w and w + 3 split dv
-        f32x16 aD = zero16();
-        if (wave < 6)
-            mma_abt<LDV, LDV>(aD, RY + aib * 32 * LDV, RV + ajb * 32 * LDV, ah * (DVP / 2), (ah + 1) * (DVP / 2),
-                              lane);
-        __syncthreads();   // V reads done
-        if (wave >= 3 && wave < 6) {
+        // this wave's two 16x16 tiles of dY V^T
+        f32x4 aD[2];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) RV[at * 1024 + r * 64 + lane] = aD[r];
+        for (int u = 0; u < 2; ++u) {
+            const int t = cc_tile(wave, u), ti = t >> 2, tj = t & 3;
+            aD[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (tj <= ti) mma16_abt<LDV, LDV>(aD[u], RY + 16 * ti * LDV, RV + 16 * tj * LDV, 0, DVP, lane);
         }
-        __syncthreads();
-        f32x16 pM = zero16();
-        if (wave < 3) {
+        __syncthreads();   // V reads done: P overwrites V
+        f32x4 pM[2];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int i = aib * 32 + acc_row(r, lane), j = ajb * 32 + cl;
-                const float a = aD[r] + RV[at * 1024 + r * 64 + lane];
+        for (int u = 0; u < 2; ++u) {
+            const int t = cc_tile(wave, u), ti = t >> 2, tj = t & 3;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * ti + 4 * lq + r, j = 16 * tj + l16;
                 const float D = (j <= i) ? expf(bs[i] - bs[j]) : 0.f;
-                const float p = accA[r] * D;
-                RP[i * LDP + j] = a * D;   // dP
-                Pm[i * LDP + j] = p;       // P
-                pM[r] = p * a;             // M
+                const float p = accA[u][r] * D;
+                RP[i * LDP + j] = aD[u][r] * D;   // dP
+                Pm[i * LDP + j] = p;              // P
+                pM[u][r] = p * aD[u][r];          // M
             }
         }
         __syncthreads();
@@ -835,7 +1004,7 @@ __global__ __launch_bounds__(NTW) void k_bwd_grads(
             }
         }
         // dV = Gv + P^T dY over j >= t, written per 16x16 tile
-        float *dvb = dv + (bh * T + c * CH) * dv_;
+        const rsrc_t dvb = make_rsrc(dv + (bh * T + c * CH) * dv_, (int64_t)rows * dv_ * 4);
 #pragma unroll
         for (int m = 0; m < NSL; ++m) {
             const int rt = ((wave >> 1) + m) & 3, ct = wave & 1;
@@ -847,44 +1016,32 @@ __global__ __launch_bounds__(NTW) void k_bwd_grads(
                 for (int s = 0; s < 4; ++s) acc = mfma16(a[(j0 + s) * LDP], by[(j0 + s) * LDV], acc);
             }
             const int n = 32 * m + 16 * ct + l16;
-            if (n < dv_) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = 16 * rt + 4 * lq + r;
-                    if (t < rows) dvb[(uint32_t)(t * dv_ + n)] = acc[r];
-                }
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * rt + 4 * lq + r;   // rows past the sequence end fall outside dvb
+                gstore1(dvb, n < dv_ ? (uint32_t)(t * dv_ + n) * 4u : kOOB, acc[r]);
             }
         }
         __syncthreads();   // dP, P, Q and dY reads done
 
-        // M to LDS (its upper-right tile is zero); the next head's V, dY, first slab
-        if (wave < 3) {
+        // M to LDS (zero above the diagonal); the next head's V, dY, first slab
 #pragma unroll
-            for (int r = 0; r < 16; ++r) RP[(aib * 32 + acc_row(r, lane)) * LDP + ajb * 32 + cl] = pM[r];
-        } else if (wave == 3) {
+        for (int u = 0; u < 2; ++u) {
+            const int t = cc_tile(wave, u), ti = t >> 2, tj = t & 3;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) RP[acc_row(r, lane) * LDP + 32 + cl] = 0.f;
+            for (int r = 0; r < 4; ++r) RP[(16 * ti + 4 * lq + r) * LDP + 16 * tj + l16] = pM[u][r];
         }
-        if (hh + 1 < hpg) {
-            regs_to_lds<CH, DVP, NTW, TPER, LDV>(tid, vbuf, RV);
-            regs_to_lds<CH, DVP, NTW, TPER, LDV>(tid, ybuf, RY);
-            fro_next = store_slab(tid);
-        }
+        regs_to_lds<CH, DVP, NTW, TPER, LDV>(tid, vbuf, RV);   // zeros after the last head
+        regs_to_lds<CH, DVP, NTW, TPER, LDV>(tid, ybuf, RY);
+        fro_next = store_slab(tid);
         __syncthreads();
 
         // Rectangle sums R_r = sum_{i >= r} sum_{j < r} M_ij: exclusive prefix
         // over j of every row (in place), then a suffix over i.
-        for (int i = wave * 8; i < wave * 8 + 8; ++i) {
-            float x = RP[i * LDP + lane];
 #pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float yv = __shfl_up(x, off);
-                if (lane >= off) x += yv;
-            }
+        for (int i = wave * 8; i < wave * 8 + 8; ++i) {
             // shift, not subtract: the diagonal term must not enter the prefix
-            float xe = __shfl_up(x, 1);
-            if (lane == 0) xe = 0.f;
-            RP[i * LDP + lane] = xe;
+            RP[i * LDP + lane] = shift_up1(scan64(RP[i * LDP + lane]));
         }
         __syncthreads();
         {
@@ -893,8 +1050,8 @@ __global__ __launch_bounds__(NTW) void k_bwd_grads(
                 if (i >= lane) racc += RP[i * LDP + lane];
             redR[wave][lane] = racc;
         }
-        fro = sum64(fro);
-        if (lane == 0) redB[wave] = fro;
+        fro = sum64_hi(fro);
+        if (lane == 63) redB[wave] = fro;
         __syncthreads();
 
         if (wave == 0) {
@@ -921,22 +1078,21 @@ __global__ __launch_bounds__(NTW) void k_bwd_grads(
             }
             float pke = __shfl_up(pk, 1);
             if (lane == 0) pke = 0.f;
-            if (lane < rows) dla[bh * T + c * CH + lane] = rint + sq + pke + expf(blh) * frob;
+            gstore1(make_rsrc(dla + bh * T + c * CH, (int64_t)rows * 4), (uint32_t)lane * 4u,
+                    rint + sq + pke + expf(blh) * frob);
         }
     }
 
     if (hasK) {
         const int colk = cbk * 32 + cl;
-        if (colk < dk_) {
+        const int64_t tb = (int64_t)rows * dk_ * 4;
+        const rsrc_t qr = make_rsrc(dq + (bg * T + c * CH) * dk_, tb), kr = make_rsrc(dk + (bg * T + c * CH) * dk_, tb);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = rbk * 32 + acc_row(r, lane);
-                if (row < rows) {
-                    const int64_t o = (bg * T + c * CH + row) * dk_ + colk;
-                    dq[o] = dQacc[r];
-                    dk[o] = dKacc[r];
-                }
-            }
+        for (int r = 0; r < 16; ++r) {
+            const int row = rbk * 32 + acc_row(r, lane);   // rows past the sequence end fall outside
+            const uint32_t o = colk < dk_ ? (uint32_t)(row * dk_ + colk) * 4u : kOOB;
+            gstore1(qr, o, dQacc[r]);
+            gstore1(kr, o, dKacc[r]);
         }
     }
 }
@@ -1034,11 +1190,17 @@ static void collect_timing()
         else { constexpr int KP = 128, VP = 128; BODY; }                              \
     } while (0)
 
+#define SSD_DISPATCH(P_, BODY)                                                     \
+    do {                                                                           \
+        if ((P_).vec) { constexpr bool VE = true; SSD_DISPATCH_DIMS((P_).DKP, (P_).DVP, BODY); } \
+        else { constexpr bool VE = false; SSD_DISPATCH_DIMS((P_).DKP, (P_).DVP, BODY); }      \
+    } while (0)
+
 struct Problem {
     ssd_shape s;
     Layout L;
     int DKP, DVP;
-    int vecK, vecV;
+    bool vec;   // dk and dv multiples of 4: 16-byte loads
     float *bcum, *bl, *states, *dstates;
 };
 
@@ -1064,12 +1226,12 @@ static int run_scan(const Problem &P, int ndir, const float *q, const float *k, 
     if (launch_status() != SSD_OK) return SSD_ERR_DEVICE;
     {
         TimedLaunch tl(ndir == 1 ? KID_SCAN : KID_SCAN2, st);
-        SSD_DISPATCH_DIMS(P.DKP, P.DVP, ({
+        SSD_DISPATCH(P, ({
             constexpr int TJ = VP < 64 ? VP : 64;
             const int64_t per_dir = BH * (KP / TI) * (VP / TJ);
-            k_state_scan<KP, VP><<<dim3((unsigned)(ndir * per_dir)), dim3(NTH), 0, st>>>(
+            k_state_scan<KP, VP, VE><<<dim3((unsigned)(ndir * per_dir)), dim3(NTS), 0, st>>>(
                 q, k, v, dy, h0, P.bcum, P.bl, P.states, P.dstates, dh0, (int)s.G, (int)s.H, s.T, (int)s.dk,
-                (int)s.dv, P.L.NC, P.L.NCp, P.L.Epad, per_dir, P.vecK, P.vecV);
+                (int)s.dv, P.L.NC, P.L.NCp, P.L.Epad, per_dir);
         }));
     }
     return launch_status();
@@ -1086,8 +1248,7 @@ static int prepare(const ssd_shape *shape, bool backward, void *ws, size_t ws_by
     }
     P->DKP = pad_dim(shape->dk);
     P->DVP = pad_dim(shape->dv);
-    P->vecK = (shape->dk % 4) == 0;
-    P->vecV = (shape->dv % 4) == 0;
+    P->vec = (shape->dk % 4) == 0 && (shape->dv % 4) == 0;
     char *w = static_cast<char *>(ws);
     P->bcum = reinterpret_cast<float *>(w + P->L.off[0]);
     P->bl = reinterpret_cast<float *>(w + P->L.off[1]);
@@ -1123,10 +1284,10 @@ int ssd_fwd(const ssd_shape *shape, const float *q, const float *k, const float 
     if (rc != SSD_OK) return rc;
     {
         TimedLaunch tl(KID_OUTPUT, st);
-        SSD_DISPATCH_DIMS(P.DKP, P.DVP,
-                          (k_chunk_output<KP, VP><<<dim3((unsigned)(s.B * s.G * P.L.NC)), dim3(NTW), 0, st>>>(
+        SSD_DISPATCH(P,
+                          (k_chunk_output<KP, VP, VE><<<dim3((unsigned)(s.B * s.G * P.L.NC)), dim3(NTW), 0, st>>>(
                               q, k, v, P.bcum, P.states, y, (int)s.G, (int)s.H, s.T, (int)s.dk, (int)s.dv, P.L.NC,
-                              P.L.Epad, P.vecK, P.vecV)));
+                              P.L.Epad)));
     }
     return launch_status();
 }
@@ -1162,10 +1323,10 @@ int ssd_bwd(const ssd_shape *shape, const float *q, const float *k, const float 
     if (rc != SSD_OK) return rc;
     {
         TimedLaunch tl(KID_GRADS, st);
-        SSD_DISPATCH_DIMS(P.DKP, P.DVP,
-                          (k_bwd_grads<KP, VP><<<dim3((unsigned)(s.B * s.G * P.L.NC)), dim3(NTW), 0, st>>>(
+        SSD_DISPATCH(P,
+                          (k_bwd_grads<KP, VP, VE><<<dim3((unsigned)(s.B * s.G * P.L.NC)), dim3(NTW), 0, st>>>(
                               q, k, v, dy, P.bcum, P.bl, P.states, P.dstates, dq, dk, dv, dlog_alpha, (int)s.G,
-                              (int)s.H, s.T, (int)s.dk, (int)s.dv, P.L.NC, P.L.NCp, P.L.Epad, P.vecK, P.vecV)));
+                              (int)s.H, s.T, (int)s.dk, (int)s.dv, P.L.NC, P.L.NCp, P.L.Epad)));
     }
     return launch_status();
 }

@@ -269,7 +269,21 @@ __device__ __forceinline__ void mma_abt(f32x16 &acc, const float *A, const float
 // v_mfma_f32_16x16x4f32.  Lane (q, r) reads k0 + 4q .. k0 + 4q + 3 of its
 // rows with one 16-byte load; MFMA s contracts over k0 + s + {0, 4, 8, 12}.
 template <int LDA, int LDB>
-__device__ __forceinline__ void mma16_abt(f32x4 &acc, const float *A, const float *B, int k0, int k1, int lane);
+__device__ __forceinline__ void mma16_abt(f32x4 &acc, const float *A, const float *B, int k0, int k1, int lane)
+{
+    const int l16 = lane & 15, lq = lane >> 4;
+    const float *a = A + l16 * LDA + 4 * lq;
+    const float *b = B + l16 * LDB + 4 * lq;
+#pragma unroll 2
+    for (int kk = k0; kk < k1; kk += 16) {
+        const float4 x = *reinterpret_cast<const float4 *>(a + kk);
+        const float4 y = *reinterpret_cast<const float4 *>(b + kk);
+        acc = mfma16(x.x, y.x, acc);
+        acc = mfma16(x.y, y.y, acc);
+        acc = mfma16(x.z, y.z, acc);
+        acc = mfma16(x.w, y.w, acc);
+    }
+}
 
 // The C x C tiles of Q K^T, dY V^T, P and dP are handled as a 4 x 4 grid of
 // 16x16 tiles, two per wave (tiles w and 15 - w of wave w, row-major), so
@@ -296,61 +310,49 @@ __device__ __forceinline__ int cc_tile(int wave, int u) { return u == 0 ? wave :
 // kinds of waves, one of each per SIMD:
 //   * four compute waves hold the state (each a 16 x TJ/2 slice) and per
 //     chunk read their operands from LDS, store the state and run the MFMAs;
-//   * four loader waves keep the operand tiles of the next PD chunks in
-//     flight in registers and per chunk write the next one, its rows scaled
+//   * four loader waves keep the operand tiles of the next PD steps in flight
+//     in registers and per step write the next step's tiles, their rows scaled
 //     by the decay weights, into the other half of the double-buffered LDS
 //     tiles.
-// A loader wave's memory and exp work thus runs on its SIMD while the
-// compute wave's MFMAs do, and no compute wave ever waits on a global load.
-// The number of steps is rounded up to a multiple of PD with no-op steps
-// (zero operands, decay 1, stores dropped), so no load or store is
-// conditional and the compiler's count of loads in flight is exact.
-// A compute wave owns two 16x16 accumulator tiles whose columns interleave
-// (tile u holds the wave's columns 2j + u), so one 8-byte LDS read gives a
-// lane both B operands.  Blocks of one (b, g) are placed on one XCD so that
-// the group's q/k and each head's v/dy tiles are shared through its L2.
+// A step covers CPS consecutive chunks, so the per-step synchronisation is
+// paid once per CPS chunks.  A loader wave's memory and exp work runs on its
+// SIMD while the compute wave's MFMAs do, and no compute wave waits on a
+// global load.  The number of steps is rounded up to a multiple of PD with
+// no-op chunks (zero operands, decay 1, stores dropped), so no load or store
+// is conditional and the compiler's count of loads in flight is exact.
+// A compute wave owns NU = TJ/32 16x16 accumulator tiles whose columns
+// interleave (tile u holds the wave's columns NU j + u), so one LDS read of
+// NU consecutive floats gives a lane all its B operands.  Blocks of one
+// (b, g) are placed on one XCD so that the group's q/k and each head's v/dy
+// tiles are shared through that XCD's L2.
 constexpr int TI = 32;
-constexpr int NTS = 512;   // 4 compute + 4 loader waves
+constexpr int NTS = 512;        // 4 compute + 4 loader waves
+constexpr int kNumCUs = 256;    // MI355X compute units
 
-template <int LDA, int LDB>
-__device__ __forceinline__ void mma16_abt(f32x4 &acc, const float *A, const float *B, int k0, int k1, int lane)
-{
-    const int l16 = lane & 15, lq = lane >> 4;
-    const float *a = A + l16 * LDA + 4 * lq;
-    const float *b = B + l16 * LDB + 4 * lq;
-#pragma unroll 2
-    for (int kk = k0; kk < k1; kk += 16) {
-        const float4 x = *reinterpret_cast<const float4 *>(a + kk);
-        const float4 y = *reinterpret_cast<const float4 *>(b + kk);
-        acc = mfma16(x.x, y.x, acc);
-        acc = mfma16(x.y, y.y, acc);
-        acc = mfma16(x.z, y.z, acc);
-        acc = mfma16(x.w, y.w, acc);
-    }
-}
-
-template <int DKP, int DVP, bool VEC>
-__global__ __launch_bounds__(NTS, 2) void k_state_scan(
+template <int DKP, int DVP, bool VEC, int TJ, int CPS>
+__global__ __launch_bounds__(NTS) void k_state_scan(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
     const float *__restrict__ dy, const float *__restrict__ h0, const float *__restrict__ bcum,
     const float *__restrict__ bl, float *__restrict__ states, float *__restrict__ dstates,
     float *__restrict__ dh0, int G, int H, int64_t T, int dk, int dv, int64_t NC, int64_t NCp, int64_t Epad,
     int64_t per_dir)
 {
-    constexpr int TJ = DVP < 64 ? DVP : 64;
+    static_assert(TJ <= DVP && DVP % TJ == 0 && (TJ == 32 || TJ == 64 || TJ == 128), "tile width");
     constexpr int NTJ = DVP / TJ;
     constexpr int NTILE = (DKP / TI) * NTJ;
-    constexpr int NU = TJ / 32;                       // accumulator tiles per compute wave (1 or 2)
+    constexpr int NU = TJ / 32;                       // accumulator tiles per compute wave
     constexpr int WC = TJ / 2;                        // columns per compute wave
     constexpr int LDA = TI + 16;                      // A reads: rows 16 banks apart
-    constexpr int LDB = (NU == 2) ? TJ + 32 : TJ + 16;   // B reads: rows 32 (b64) / 16 (b32) banks apart
+    // B reads of NU floats per lane: rows 16 (b32) or 32 (b64) banks apart;
+    // b128 reads cover 256 contiguous bytes per 16 lanes
+    constexpr int LDB = (NU == 1) ? TJ + 16 : (NU == 2) ? TJ + 32 : TJ + 4;
     constexpr int NLT = 256;                          // loader threads
     constexpr int A4 = CH * TI / 4, B4 = CH * TJ / 4;
     constexpr int APER = (A4 + NLT - 1) / NLT, BPER = (B4 + NLT - 1) / NLT;
-    constexpr int PD = 3;                             // chunks loaded ahead
-    __shared__ __attribute__((aligned(16))) float As[2][CH * LDA];
-    __shared__ __attribute__((aligned(16))) float Bs[2][CH * LDB];
-    __shared__ float decs[2];                         // e^{b_L} of the chunk in each half
+    constexpr int PD = (CPS == 1) ? 3 : 2;            // steps loaded ahead
+    __shared__ __attribute__((aligned(16))) float As[2][CPS][CH * LDA];
+    __shared__ __attribute__((aligned(16))) float Bs[2][CPS][CH * LDB];
+    __shared__ float decs[2][CPS];                    // e^{b_L} of each staged chunk
 
     // XCD-aware order: consecutive logical blocks share blockIdx % 8.
     const int64_t nblk = gridDim.x;
@@ -365,7 +367,8 @@ __global__ __launch_bounds__(NTS, 2) void k_state_scan(
     const int64_t b = bh / H;
     const int g = h / (H / G);
     const int64_t E = (int64_t)dk * dv;
-    const int64_t NS = (NC + PD - 1) / PD * PD;       // steps, NC rounded up
+    const int64_t NSC = (NC + CPS - 1) / CPS;        // steps holding real chunks
+    const int64_t NS = (NSC + PD - 1) / PD * PD;      // steps, rounded up
     const int wave = threadIdx.x >> 6;
 
     if (wave >= 4) {
@@ -379,11 +382,11 @@ __global__ __launch_bounds__(NTS, 2) void k_state_scan(
             float4 a[APER], b[BPER];
             float bt[BPER], blc;
         };
-        Stage stg[PD];
-        // operands of step s (chunk c(s)); steps past the end load zeros
-        auto prefetch = [&](Stage &S, int64_t s) {
-            const bool live = s < NC;
-            const int64_t c = live ? (dir == 0 ? s : NC - 1 - s) : 0;
+        Stage stg[PD][CPS];
+        // operands of chunk n of the scan order; chunks past the end load zeros
+        auto prefetch = [&](Stage &S, int64_t n) {
+            const bool live = n < NC;
+            const int64_t c = live ? (dir == 0 ? n : NC - 1 - n) : 0;
             const int rows = (int)((T - c * CH) < CH ? (T - c * CH) : CH);
             const rsrc_t ab = make_rsrc(Asrc + c * CH * dk, live ? (int64_t)rows * dk * 4 : 0);
             const rsrc_t bb = make_rsrc(Bsrc + c * CH * dv, live ? (int64_t)rows * dv * 4 : 0);
@@ -404,14 +407,14 @@ __global__ __launch_bounds__(NTS, 2) void k_state_scan(
             const float blc = bl[bh * NCp + c];
             S.blc = live ? blc : 0.f;
         };
-        // stage S into LDS half `buf`, B rows scaled by the decay weights
-        auto stage = [&](const Stage &S, int buf) {
+        // stage S into LDS half `buf`, slot cc; B rows scaled by the decay weights
+        auto stage = [&](const Stage &S, int buf, int cc) {
 #pragma unroll
             for (int u = 0; u < APER; ++u) {
                 const int idx = lt + u * NLT;
                 if (A4 % NLT == 0 || idx < A4) {
                     const int r = idx / (TI / 4), c4 = (idx - r * (TI / 4)) * 4;
-                    *reinterpret_cast<float4 *>(&As[buf][r * LDA + c4]) = S.a[u];
+                    *reinterpret_cast<float4 *>(&As[buf][cc][r * LDA + c4]) = S.a[u];
                 }
             }
 #pragma unroll
@@ -425,23 +428,32 @@ __global__ __launch_bounds__(NTS, 2) void k_state_scan(
                     x.y *= w;
                     x.z *= w;
                     x.w *= w;
-                    *reinterpret_cast<float4 *>(&Bs[buf][r * LDB + c4]) = x;
+                    *reinterpret_cast<float4 *>(&Bs[buf][cc][r * LDB + c4]) = x;
                 }
             }
-            if (lt == 0) decs[buf] = expf(S.blc);
+            if (lt == 0) decs[buf][cc] = expf(S.blc);
         };
-        // step s: chunk s is published by the barrier; stage chunk s + 1
-        // into the other half and refill its registers with chunk s + 1 + PD
+        // step s: its chunks are published by the barrier; stage step s + 1
+        // into the other half and refill its registers with step s + 1 + PD
         auto step = [&](int64_t s, int u) {
             __syncthreads();
             const int un = (u + 1) % PD;
-            stage(stg[un], (int)((s + 1) & 1));
-            prefetch(stg[un], s + 1 + PD);
+#pragma unroll
+            for (int cc = 0; cc < CPS; ++cc) {
+                stage(stg[un][cc], (int)((s + 1) & 1), cc);
+                prefetch(stg[un][cc], (s + 1 + PD) * CPS + cc);
+            }
         };
 #pragma unroll
-        for (int u = 0; u < PD; ++u) prefetch(stg[u], u);
-        stage(stg[0], 0);
-        prefetch(stg[0], PD);
+        for (int u = 0; u < PD; ++u) {
+#pragma unroll
+            for (int cc = 0; cc < CPS; ++cc) prefetch(stg[u][cc], (int64_t)u * CPS + cc);
+        }
+#pragma unroll
+        for (int cc = 0; cc < CPS; ++cc) {
+            stage(stg[0][cc], 0, cc);
+            prefetch(stg[0][cc], (int64_t)PD * CPS + cc);
+        }
         // the first PD steps are peeled so that the loop is entered with the
         // loads in flight that it repeats with
 #pragma unroll
@@ -472,45 +484,57 @@ __global__ __launch_bounds__(NTS, 2) void k_state_scan(
         for (int u = 0; u < NU; ++u) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[u][r] = gload1(hr, soff(u, r));
+            // Wait for the h0 loads here: otherwise every state store in the
+            // loop waits on the stores before it.
+            asm volatile("" : "+v"(acc[u]));
         }
     }
-    const float *Ab0 = &As[0][q4 * LDA + rblk * 16 + l16];
-    const float *Bb0 = &Bs[0][q4 * LDB + wc0 + NU * l16];
     for (int64_t s = 0; s < NS; ++s) {
         const int buf = (int)(s & 1);
-        __syncthreads();   // chunk s staged in half `buf`
-        float av[CH / 4];
-        float bv[CH / 4][NU];
-        const float *Ab = Ab0 + buf * (CH * LDA);
-        const float *Bb = Bb0 + buf * (CH * LDB);
+        __syncthreads();   // step s staged in half `buf`
 #pragma unroll
-        for (int kk = 0; kk < CH / 4; ++kk) {
-            av[kk] = Ab[4 * kk * LDA];
-            if (NU == 2) {
-                const float2 t2 = *reinterpret_cast<const float2 *>(Bb + 4 * kk * LDB);
-                bv[kk][0] = t2.x;
-                bv[kk][NU - 1] = t2.y;
-            } else {
-                bv[kk][0] = Bb[4 * kk * LDB];
+        for (int cc = 0; cc < CPS; ++cc) {
+            float av[CH / 4];
+            float bv[CH / 4][NU];
+            const float *Ab = &As[buf][cc][q4 * LDA + rblk * 16 + l16];
+            const float *Bb = &Bs[buf][cc][q4 * LDB + wc0 + NU * l16];
+#pragma unroll
+            for (int kk = 0; kk < CH / 4; ++kk) {
+                av[kk] = Ab[4 * kk * LDA];
+                if constexpr (NU == 4) {
+                    const float4 t4 = *reinterpret_cast<const float4 *>(Bb + 4 * kk * LDB);
+                    bv[kk][0] = t4.x;
+                    bv[kk][1] = t4.y;
+                    bv[kk][2] = t4.z;
+                    bv[kk][3] = t4.w;
+                } else if constexpr (NU == 2) {
+                    const float2 t2 = *reinterpret_cast<const float2 *>(Bb + 4 * kk * LDB);
+                    bv[kk][0] = t2.x;
+                    bv[kk][1] = t2.y;
+                } else {
+                    bv[kk][0] = Bb[4 * kk * LDB];
+                }
             }
-        }
-        const float decay = decs[buf];
-        // slab[c] = S (state entering the chunk in this direction); no-op steps store nothing
-        const bool live = s < NC;
-        const rsrc_t dst = make_rsrc(slab + (live ? (dir == 0 ? s : NC - 1 - s) : 0) * Epad, live ? E * 4 : 0);
+            const float decay = decs[buf][cc];
+            // slab[c] = S (state entering the chunk in this direction); no-op chunks store nothing
+            const int64_t n = s * CPS + cc;
+            const bool live = n < NC;
+            const rsrc_t dst =
+                make_rsrc(slab + (live ? (dir == 0 ? n : NC - 1 - n) : 0) * Epad, live ? E * 4 : 0);
 #pragma unroll
-        for (int u = 0; u < NU; ++u) {
+            for (int u = 0; u < NU; ++u) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                gstore1(dst, soff(u, r), acc[u][r]);
-                acc[u][r] *= decay;
+                for (int r = 0; r < 4; ++r) {
+                    gstore1(dst, soff(u, r), acc[u][r]);
+                    acc[u][r] *= decay;
+                }
             }
-        }
-        // S += A^T B over the chunk's 64 positions
+            // S += A^T B over the chunk's 64 positions
 #pragma unroll
-        for (int kk = 0; kk < CH / 4; ++kk) {
+            for (int kk = 0; kk < CH / 4; ++kk) {
 #pragma unroll
-            for (int u = 0; u < NU; ++u) acc[u] = mfma16(av[kk], bv[kk][u], acc[u]);
+                for (int u = 0; u < NU; ++u) acc[u] = mfma16(av[kk], bv[kk][u], acc[u]);
+            }
         }
     }
     if (dir == 1) {
@@ -683,7 +707,7 @@ __global__ __launch_bounds__(NTW) void k_chunk_output(const float *__restrict__ 
             {
                 const float *aq = RQ + (16 * rt + l16) * LDK + 4 * lq;
                 const float *bsl = SL[m & 1] + 4 * lq * LSL + 16 * ct + l16;
-#pragma unroll 4
+#pragma unroll 2
                 for (int i0 = 0; i0 < DKP; i0 += 16) {
                     const float4 a = *reinterpret_cast<const float4 *>(aq + i0);
                     acc = mfma16(a.x, bsl[(i0 + 0) * LSL], acc);
@@ -753,7 +777,7 @@ struct BwdCfg {
     static constexpr int NTK = 2 * NKB;   // 32x32 tiles of a C x dk result
     static constexpr int NSL = DVP / 32;  // slabs per state
     static constexpr int QN = (CH * LDK > 2 * DKP * LSL) ? CH * LDK : 2 * DKP * LSL;
-    static constexpr int VN = (CH * LDV > CH * LDP) ? CH * LDV : CH * LDP;
+    static constexpr int VN = CH * LDV;
     static constexpr int PN = CH * LDP;
     static constexpr int TPER = (CH * DVP / 4 + NTW - 1) / NTW;   // float4 / thread, C x dv tile
     static constexpr int QPER = (CH * DKP / 4 + NTW - 1) / NTW;   // float4 / thread, C x dk tile
@@ -783,7 +807,6 @@ __global__ __launch_bounds__(NTW) void k_bwd_grads(
     __shared__ float redB[NTW / 64];
     float *const slS = RQ;               // S_in slab   [DKP][LSL]
     float *const slD = RQ + DKP * LSL;   // dS_out slab [DKP][LSL]
-    float *const Pm = RV;                // P           [CH][LDP] (after V)
 
     const int64_t c = blockIdx.x % NC;
     const int64_t bg = blockIdx.x / NC;
@@ -885,9 +908,30 @@ __global__ __launch_bounds__(NTW) void k_bwd_grads(
         const float bcur = bpre, blh = blpre;
         float fro = fro_next;
 
-        // ---- state phase
+        // ---- head start: the head's decays, and P^T = ((Q K^T) o D)^T in RP
+        if (tid < CH) {
+            bs[tid] = bcur;
+            eb[tid] = expf(bcur);
+            el[tid] = (tid < rows) ? expf(blh - bcur) : 0.f;
+        }
+        __syncthreads();   // decays visible; the previous head's reads of RP done
+        f32x4 Dm[2];       // the decay mask D on this wave's two 16x16 tiles
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int t = cc_tile(wave, u), ti = t >> 2, tj = t & 3;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * ti + 4 * lq + r, j = 16 * tj + l16;
+                Dm[u][r] = (j <= i) ? expf(bs[i] - bs[j]) : 0.f;
+                RP[j * LDP + i] = accA[u][r] * Dm[u][r];
+            }
+        }
+        __syncthreads();   // P^T visible
+
+        // ---- state phase, with dY V^T and dV accumulated slab by slab
+        const rsrc_t dvb = make_rsrc(dv + (bh * T + c * CH) * dv_, (int64_t)rows * dv_ * 4);
         f32x16 gq = zero16(), gk = zero16();
-        f32x4 gv[NSL];
+        f32x4 aD[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
         for (int m = 0; m < NSL; ++m) {
             if (m > 0) {
@@ -903,33 +947,68 @@ __global__ __launch_bounds__(NTW) void k_bwd_grads(
                 mma_abt<LDV, LSL>(gq, RY + rbk * 32 * LDV + 32 * m, slS + cbk * 32 * LSL, 0, 32, lane);
                 mma_abt<LDV, LSL>(gk, RV + rbk * 32 * LDV + 32 * m, slD + cbk * 32 * LSL, 0, 32, lane);
             }
-            // Gv tile: positions 16 rt .. 16 rt + 15, state columns 32 m + 16 ct .. + 15
-            const int rt = ((wave >> 1) + m) & 3, ct = wave & 1;
-            const float *ak = RK + (16 * rt + l16) * LDK + 4 * lq;
-            const float *bd = slD + 4 * lq * LSL + 16 * ct + l16;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-            for (int i0 = 0; i0 < DKP; i0 += 16) {
-                const float4 a = *reinterpret_cast<const float4 *>(ak + i0);
-                acc = mfma16(a.x, bd[(i0 + 0) * LSL], acc);
-                acc = mfma16(a.y, bd[(i0 + 1) * LSL], acc);
-                acc = mfma16(a.z, bd[(i0 + 2) * LSL], acc);
-                acc = mfma16(a.w, bd[(i0 + 3) * LSL], acc);
+            // dY V^T over this slab's 32 columns
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int t = cc_tile(wave, u), ti = t >> 2, tj = t & 3;
+                if (tj <= ti)
+                    mma16_abt<LDV, LDV>(aD[u], RY + 16 * ti * LDV, RV + 16 * tj * LDV, 32 * m, 32 * m + 32, lane);
             }
-            gv[m] = acc;
+            // dV tile: positions 16 rt .. 16 rt + 15, columns 32 m + 16 ct .. + 15:
+            //   diag(e^{b_L - b}) K dS_out + P^T dY   (P^T[t][j] nonzero for j >= t)
+            const int rt = ((wave >> 1) + m) & 3, ct = wave & 1;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            {
+                const float *ak = RK + (16 * rt + l16) * LDK + 4 * lq;
+                const float *bd = slD + 4 * lq * LSL + 16 * ct + l16;
+#pragma unroll 2
+                for (int i0 = 0; i0 < DKP; i0 += 16) {
+                    const float4 x = *reinterpret_cast<const float4 *>(ak + i0);
+                    acc = mfma16(x.x, bd[(i0 + 0) * LSL], acc);
+                    acc = mfma16(x.y, bd[(i0 + 1) * LSL], acc);
+                    acc = mfma16(x.z, bd[(i0 + 2) * LSL], acc);
+                    acc = mfma16(x.w, bd[(i0 + 3) * LSL], acc);
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[r] *= el[16 * rt + 4 * lq + r];
+            {
+                const float *ap = RP + (16 * rt + l16) * LDP + 4 * lq;
+                const float *by = RY + 4 * lq * LDV + 32 * m + 16 * ct + l16;
+                for (int j0 = 16 * rt; j0 < CH; j0 += 16) {
+                    const float4 x = *reinterpret_cast<const float4 *>(ap + j0);
+                    acc = mfma16(x.x, by[(j0 + 0) * LDV], acc);
+                    acc = mfma16(x.y, by[(j0 + 1) * LDV], acc);
+                    acc = mfma16(x.z, by[(j0 + 2) * LDV], acc);
+                    acc = mfma16(x.w, by[(j0 + 3) * LDV], acc);
+                }
+            }
+            const int n = 32 * m + 16 * ct + l16;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * rt + 4 * lq + r;   // rows past the sequence end fall outside dvb
+                gstore1(dvb, n < dv_ ? (uint32_t)(t * dv_ + n) * 4u : kOOB, acc[r]);
+            }
         }
 
         // ---- intra phase
-        __syncthreads();   // slab reads done
+        __syncthreads();   // slab and P^T reads done
         regs_to_lds<CH, DKP, NTW, QPER, LDK>(tid, qbuf, RQ);
-        if (tid < CH) {
-            bs[tid] = bcur;
-            eb[tid] = expf(bcur);
-            el[tid] = (tid < rows) ? expf(blh - bcur) : 0.f;
-        }
         load_vy(hh + 1, tid);
         load_slab(hh + 1, 0, tid);
-        __syncthreads();
+        // dP = (dY V^T) o D into RP; M = (Q K^T) o D o (dY V^T) kept for the rectangle sums
+        f32x4 pM[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int t = cc_tile(wave, u), ti = t >> 2, tj = t & 3;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * ti + 4 * lq + r, j = 16 * tj + l16;
+                RP[i * LDP + j] = aD[u][r] * Dm[u][r];
+                pM[u][r] = accA[u][r] * Dm[u][r] * aD[u][r];
+            }
+        }
+        __syncthreads();   // Q and dP visible
 
         // state parts of dQ and dK, and their rows' dlog_alpha terms
         if (hasK) {
@@ -947,39 +1026,6 @@ __global__ __launch_bounds__(NTW) void k_bwd_grads(
             }
             dQacc += gq;
             dKacc += gk;
-        }
-#pragma unroll
-        for (int m = 0; m < NSL; ++m) {
-            const int rt = ((wave >> 1) + m) & 3;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) gv[m][r] *= el[16 * rt + 4 * lq + r];
-        }
-        // this wave's two 16x16 tiles of dY V^T
-        f32x4 aD[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int t = cc_tile(wave, u), ti = t >> 2, tj = t & 3;
-            aD[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (tj <= ti) mma16_abt<LDV, LDV>(aD[u], RY + 16 * ti * LDV, RV + 16 * tj * LDV, 0, DVP, lane);
-        }
-        __syncthreads();   // V reads done: P overwrites V
-        f32x4 pM[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int t = cc_tile(wave, u), ti = t >> 2, tj = t & 3;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = 16 * ti + 4 * lq + r, j = 16 * tj + l16;
-                const float D = (j <= i) ? expf(bs[i] - bs[j]) : 0.f;
-                const float p = accA[u][r] * D;
-                RP[i * LDP + j] = aD[u][r] * D;   // dP
-                Pm[i * LDP + j] = p;              // P
-                pM[u][r] = p * aD[u][r];          // M
-            }
-        }
-        __syncthreads();
-
-        if (hasK) {
             // dQ += dP K over j <= i
             {
                 const float *a = RP + (rbk * 32 + cl) * LDP + 4 * (lane >> 5);
@@ -1003,26 +1049,7 @@ __global__ __launch_bounds__(NTW) void k_bwd_grads(
                 }
             }
         }
-        // dV = Gv + P^T dY over j >= t, written per 16x16 tile
-        const rsrc_t dvb = make_rsrc(dv + (bh * T + c * CH) * dv_, (int64_t)rows * dv_ * 4);
-#pragma unroll
-        for (int m = 0; m < NSL; ++m) {
-            const int rt = ((wave >> 1) + m) & 3, ct = wave & 1;
-            f32x4 acc = gv[m];
-            const float *a = Pm + 4 * lq * LDP + 16 * rt + l16;
-            const float *by = RY + 4 * lq * LDV + 32 * m + 16 * ct + l16;
-            for (int j0 = 16 * rt; j0 < CH; j0 += 16) {
-#pragma unroll
-                for (int s = 0; s < 4; ++s) acc = mfma16(a[(j0 + s) * LDP], by[(j0 + s) * LDV], acc);
-            }
-            const int n = 32 * m + 16 * ct + l16;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 16 * rt + 4 * lq + r;   // rows past the sequence end fall outside dvb
-                gstore1(dvb, n < dv_ ? (uint32_t)(t * dv_ + n) * 4u : kOOB, acc[r]);
-            }
-        }
-        __syncthreads();   // dP, P, Q and dY reads done
+        __syncthreads();   // dP and Q reads done
 
         // M to LDS (zero above the diagonal); the next head's V, dY, first slab
 #pragma unroll
@@ -1226,12 +1253,25 @@ static int run_scan(const Problem &P, int ndir, const float *q, const float *k, 
     if (launch_status() != SSD_OK) return SSD_ERR_DEVICE;
     {
         TimedLaunch tl(ndir == 1 ? KID_SCAN : KID_SCAN2, st);
+        // Two chunks per step when there is at most one block per CU (the
+        // paired tiles fill most of a CU's LDS); otherwise one.  State tiles
+        // are 32 x 64 (32 x dv for dv < 64): wider tiles re-read fewer operand
+        // tiles but halve the number of independent sequential chains per CU,
+        // which measured slower.
+        const int64_t tiles_k = BH * (P.DKP / TI);
+        const bool pair = ndir * tiles_k * (P.DVP / (P.DVP < 64 ? P.DVP : 64)) <= kNumCUs;
         SSD_DISPATCH(P, ({
             constexpr int TJ = VP < 64 ? VP : 64;
-            const int64_t per_dir = BH * (KP / TI) * (VP / TJ);
-            k_state_scan<KP, VP, VE><<<dim3((unsigned)(ndir * per_dir)), dim3(NTS), 0, st>>>(
-                q, k, v, dy, h0, P.bcum, P.bl, P.states, P.dstates, dh0, (int)s.G, (int)s.H, s.T, (int)s.dk,
-                (int)s.dv, P.L.NC, P.L.NCp, P.L.Epad, per_dir);
+            const int64_t per_dir = tiles_k * (VP / TJ);
+            const dim3 grid((unsigned)(ndir * per_dir)), blk(NTS);
+            if (pair)
+                k_state_scan<KP, VP, VE, TJ, 2><<<grid, blk, 0, st>>>(
+                    q, k, v, dy, h0, P.bcum, P.bl, P.states, P.dstates, dh0, (int)s.G, (int)s.H, s.T, (int)s.dk,
+                    (int)s.dv, P.L.NC, P.L.NCp, P.L.Epad, per_dir);
+            else
+                k_state_scan<KP, VP, VE, TJ, 1><<<grid, blk, 0, st>>>(
+                    q, k, v, dy, h0, P.bcum, P.bl, P.states, P.dstates, dh0, (int)s.G, (int)s.H, s.T, (int)s.dk,
+                    (int)s.dv, P.L.NC, P.L.NCp, P.L.Epad, per_dir);
         }));
     }
     return launch_status();

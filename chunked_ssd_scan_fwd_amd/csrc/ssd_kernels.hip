@@ -550,27 +550,52 @@ __global__ __launch_bounds__(NTS) void k_state_scan(
 // ---------------------------------------------------------------------------
 // K2 + K5: output of one chunk for every head of one group.
 //
-// One block of 8 waves per (b, g, chunk).  Q K^T (causal 32x32 tiles) is
-// formed once and kept in the registers of waves 0-2.  Per head, P = (Q K^T) o D
-// goes to LDS next to the head's V, and S_in is streamed through LDS in
-// slabs of 32 state columns (double-buffered, the next slab loaded into
-// registers while the current one is in use).  For slab columns n every
-// wave computes one 16x16 tile of
-//     Y[:, n] = diag(e^b) Q S_in[:, n] + P V[:, n]
-// with its row block rotating over the slabs, so the causal P V work is the
-// same for every wave.  Every MFMA operand comes from LDS.
+// One block of 8 waves per (b, g, chunk).  Wave w owns the 32 positions
+// rt = w / 4 of the chunk and, for one head at a time, one 32-column block
+// of Y, all on v_mfma_f32_32x32x2f32.  A step covers HPS = 128 / DVP heads
+// (one for dv = 128): slot w % 4 picks head hs = slot / NCT of the step and
+// column block ct = slot % NCT.
+//
+//   Y[rows rt, cols ct] = diag(e^b) Q[rt] S_in[:, ct] + P[rt, :] V[:, ct]
+//
+// MFMA s of a contraction over d takes the index pair (8m + s, 8m + 4 + s)
+// for s < 4, so a lane (kh, i) holds the four consecutive elements
+// 8m + 4kh .. 8m + 4kh + 3 of its row in one float4.  Only the B operands of
+// the two products are read from LDS, with 4-byte reads, so the LDS traffic
+// per MFMA is a quarter of that of 16x16 tiles with both operands in LDS:
+//   * Q[rt], the A operand of Q S_in, is the same for the group's heads and
+//     stays in registers for the whole block;
+//   * P[rt, :] is the A operand of P V.  Accumulator register r of the
+//     transposed product K Q^T holds, in lane (kh, i), the element of row
+//     8 (r / 4) + 4 kh + r % 4, which is exactly the index lane (kh, i)
+//     supplies to MFMA r of a 32-deep contraction; so K Q^T is formed once
+//     per block and kept in registers, and per head only its decay factors
+//     exp(b_i - b_j) are applied.  The four waves of a row block each sum
+//     a quarter of dk and exchange the partial sums through LDS;
+//   * the step's S_in and V tiles are staged in LDS.  Their row stride
+//     DVP + 8 puts the rows 4 apart that the two lane halves read into
+//     different banks.
+// The next step's tiles are loaded into registers meanwhile, their loads
+// spread over the Q S_in MFMAs: a CU's load path moves about 16 bytes per
+// clock, so issued together they would hold up the issuing waves for
+// thousands of cycles.  LDS operands are read one MFMA group ahead.
 template <int DKP, int DVP>
 struct OutCfg {
-    static constexpr int LDK = DKP + 4;   // Q, K
-    static constexpr int LDV = DVP + 4;   // V
-    static constexpr int LDP = CH + 4;    // P
-    static constexpr int LSL = 36;        // slab rows: 32 state columns + 4
-    static constexpr int NSL = DVP / 32;
-    static constexpr int KVN = (LDK > LDV ? LDK : LDV) * CH;
-    static constexpr int PN = CH * LDP;
-    static constexpr int TPER = (CH * DVP / 4 + NTW - 1) / NTW;
-    static constexpr int QPER = (CH * DKP / 4 + NTW - 1) / NTW;
-    static constexpr int SPER = (DKP * 8 + NTW - 1) / NTW;
+    static constexpr int NCT = DVP / 32;          // 32-column blocks of Y per head
+    static constexpr int HPS = 4 / NCT;           // heads per step
+    static constexpr int LS = DVP + 8;            // S_in and V row stride
+    static constexpr int LDK = DKP + 4;           // Q and K row stride (set-up)
+    static constexpr int SN = HPS * DKP * LS;     // S_in tiles (floats)
+    static constexpr int XN = 3 * 4 * 4 * 256;    // partial sums of K Q^T
+    static constexpr int QKN = 2 * CH * LDK;      // Q and K tiles
+    static constexpr int SXN = SN > XN ? (SN > QKN ? SN : QKN) : (XN > QKN ? XN : QKN);
+    static constexpr int VN = HPS * CH * LS;
+    static constexpr int SPH = (DKP * DVP / 4 + NTW - 1) / NTW;   // float4 / thread, one S_in
+    static constexpr int VPH = CH * DVP / 4 / NTW;                // float4 / thread, one V tile
+    static constexpr int NL = HPS * (SPH + VPH) + 1;              // loads / thread / step
+    static constexpr int NQ = DKP / 8;                            // float4 of a Q row per lane
+    static constexpr int NQQ = DKP / 32;                          // the same, per quarter of dk
+    static constexpr int QPER = (CH * DKP / 4 + NTW - 1) / NTW;   // float4 / thread, one C x dk tile
 };
 
 template <int DKP, int DVP, bool VEC>
@@ -581,13 +606,13 @@ __global__ __launch_bounds__(NTW) void k_chunk_output(const float *__restrict__ 
                                                       int64_t Epad)
 {
     using Cfg = OutCfg<DKP, DVP>;
-    constexpr int LDK = Cfg::LDK, LDV = Cfg::LDV, LDP = Cfg::LDP, LSL = Cfg::LSL, NSL = Cfg::NSL;
-    constexpr int TPER = Cfg::TPER, QPER = Cfg::QPER, SPER = Cfg::SPER;
-    __shared__ __attribute__((aligned(16))) float RQ[CH * LDK];
-    __shared__ __attribute__((aligned(16))) float RKV[Cfg::KVN];   // K, then each head's V
-    __shared__ __attribute__((aligned(16))) float RP[Cfg::PN];     // Q K^T partial sums, then P
-    __shared__ __attribute__((aligned(16))) float SL[2][DKP * LSL];
-    __shared__ float bs[CH], eb[CH];
+    constexpr int NCT = Cfg::NCT, HPS = Cfg::HPS, LS = Cfg::LS, LDK = Cfg::LDK;
+    constexpr int SPH = Cfg::SPH, VPH = Cfg::VPH, NL = Cfg::NL, NQ = Cfg::NQ, NQQ = Cfg::NQQ;
+    // S_in tiles; Q, K and then the K Q^T partial sums at set-up
+    __shared__ __attribute__((aligned(16))) float SX[Cfg::SXN];
+    __shared__ __attribute__((aligned(16))) float VS[Cfg::VN];
+    __shared__ __attribute__((aligned(16))) float bs[HPS * CH];
+    __shared__ __attribute__((aligned(16))) float eb[HPS * CH];
 
     const int64_t c = blockIdx.x % NC;
     const int64_t bg = blockIdx.x / NC;
@@ -596,148 +621,238 @@ __global__ __launch_bounds__(NTW) void k_chunk_output(const float *__restrict__ 
     const int hpg = H / G;
     const int64_t bh0 = b * H + (int64_t)g * hpg;
     const int rows = (int)((T - c * CH) < CH ? (T - c * CH) : CH);
-    const int tid0 = threadIdx.x, wave = tid0 >> 6;
-    constexpr bool vk = VEC, vv = VEC;   // 16-byte loads (dk and dv multiples of 4)
-
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int rt = wave >> 2, slot = wave & 3;
+    const int hs = slot / NCT, ct = slot % NCT;
     const int64_t E = (int64_t)dk * dv;
-    float4 vbuf[TPER], sbuf[SPER];
-    float bpre = 0.f;   // b at position tid & 63 of the head being loaded
-    // Loads of head hh; hh == hpg (one past the last head) loads zeros, so the
-    // prefetches need no condition and the compiler's count of loads in
-    // flight stays exact.
-    auto load_v = [&](int hh, int tid) {
-        const bool live = hh < hpg;
-        const int64_t bh = bh0 + (live ? hh : 0);
-        tile_to_regs<CH, DVP, NTW, TPER>(
-            tid, vbuf, make_rsrc(v + (bh * T + c * CH) * dv, live ? (int64_t)rows * dv * 4 : 0), dv, vv);
-        bpre = gload1(make_rsrc(bcum + bh * NC * CH + c * CH, live ? CH * 4 : 0), (uint32_t)(tid & 63) * 4u);
-    };
-    auto load_slab = [&](int hh, int m, int tid) {
-        const bool live = hh < hpg;
-        const rsrc_t src = make_rsrc(states + ((bh0 + (live ? hh : 0)) * NC + c) * Epad, live ? E * 4 : 0);
-        const int lim = dv - 32 * m;
-#pragma unroll
-        for (int u = 0; u < SPER; ++u) {
-            const int idx = tid + u * NTW;
-            const int r = idx >> 3, c4 = (idx & 7) * 4;
-            sbuf[u] = load4(src, (uint32_t)(r * dv + 32 * m), c4, lim, idx < DKP * 8 && r < dk, vv);
+
+    // Next step's S_in and V tiles and cumulative decays, in registers.
+    // Heads past the group's last load zeros, so no load is conditional and
+    // the compiler's count of loads in flight stays exact.  issue<U>() issues
+    // load U of the NL loads of a step.
+    float4 sbuf[HPS][SPH], vbuf[HPS][VPH];
+    float bpre = 0.f;
+    auto issue = [&](int step, int tid, int u) {
+        if (u < NL - 1) {
+            const bool isv = u >= HPS * SPH;
+            const int uu = isv ? u - HPS * SPH : u;
+            const int h2 = isv ? uu / VPH : uu / SPH, e = isv ? uu % VPH : uu % SPH;
+            const int hh = step * HPS + h2;
+            const bool live = hh < hpg;
+            const int64_t bh = bh0 + (live ? hh : 0);
+            const int idx = tid + e * NTW;
+            const int r = idx / (DVP / 4), c4 = (idx % (DVP / 4)) * 4;
+            if (!isv) {
+                const rsrc_t sr = make_rsrc(states + (bh * NC + c) * Epad, live ? E * 4 : 0);
+                sbuf[h2][e] = load4(sr, (uint32_t)(r * dv), c4, dv, idx < DKP * DVP / 4, VEC);
+            } else {
+                const rsrc_t vr = make_rsrc(v + (bh * T + c * CH) * dv, live ? (int64_t)rows * dv * 4 : 0);
+                vbuf[h2][e] = load4(vr, (uint32_t)(r * dv), c4, dv, true, VEC);
+            }
+        } else {
+            // wave w < HPS loads head w's 64 cumulative decays
+            const int hh = step * HPS + (wave < HPS ? wave : 0);
+            const bool live = hh < hpg && wave < HPS;
+            bpre = gload1(make_rsrc(bcum + (bh0 + (live ? hh : 0)) * NC * CH + c * CH, live ? CH * 4 : 0),
+                          (uint32_t)(tid & 63) * 4u);
         }
     };
-    auto store_slab = [&](float *dst, int tid) {
+    auto stage = [&](int tid) {
 #pragma unroll
-        for (int u = 0; u < SPER; ++u) {
-            const int idx = tid + u * NTW;
-            if (idx < DKP * 8) {
-                const int r = idx >> 3, c4 = (idx & 7) * 4;
-                *reinterpret_cast<float4 *>(dst + r * LSL + c4) = sbuf[u];
+        for (int h2 = 0; h2 < HPS; ++h2) {
+#pragma unroll
+            for (int u = 0; u < SPH; ++u) {
+                const int idx = tid + u * NTW;
+                if (idx < DKP * DVP / 4) {
+                    const int r = idx / (DVP / 4), c4 = (idx % (DVP / 4)) * 4;
+                    *reinterpret_cast<float4 *>(SX + (h2 * DKP + r) * LS + c4) = sbuf[h2][u];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < VPH; ++u) {
+                const int idx = tid + u * NTW;
+                const int r = idx / (DVP / 4), c4 = (idx % (DVP / 4)) * 4;
+                *reinterpret_cast<float4 *>(VS + (h2 * CH + r) * LS + c4) = vbuf[h2][u];
             }
         }
+        if (wave < HPS) {
+            bs[wave * CH + (tid & 63)] = bpre;
+            eb[wave * CH + (tid & 63)] = expf(bpre);
+        }
     };
 
-    // ---- block set-up: Q, K, A = Q K^T; the first head's V and slab in flight.
+    // ---- block set-up: Q rows in registers, K Q^T, the first step staged.
+    float4 qa[NQ];   // Q[32 rt + i][8m + 4kh .. 8m + 4kh + 3] in lane (kh, i)
+    f32x16 kqt[2];   // (K Q^T)[32 jt + row(r)][32 rt + i], jt <= rt
     {
-        float4 qb[QPER];
-        tile_to_regs<CH, DKP, NTW, QPER>(tid0, qb, make_rsrc(q + (bg * T + c * CH) * dk, (int64_t)rows * dk * 4), dk,
-                                         vk);
-        regs_to_lds<CH, DKP, NTW, QPER, LDK>(tid0, qb, RQ);
-        tile_to_regs<CH, DKP, NTW, QPER>(tid0, qb, make_rsrc(k + (bg * T + c * CH) * dk, (int64_t)rows * dk * 4), dk,
-                                         vk);
-        regs_to_lds<CH, DKP, NTW, QPER, LDK>(tid0, qb, RKV);
-    }
-    load_v(0, tid0);
-    load_slab(0, 0, tid0);
-    __syncthreads();
-    // this wave's two 16x16 tiles of Q K^T
-    f32x4 accA[2];
+        const int tid = threadIdx.x, lane = tid & 63, cl = lane & 31, kh = lane >> 5;
+        {
+            float4 qb[Cfg::QPER], kb[Cfg::QPER];
+            const int64_t tb = (int64_t)rows * dk * 4;
+            tile_to_regs<CH, DKP, NTW, Cfg::QPER>(tid, qb, make_rsrc(q + (bg * T + c * CH) * dk, tb), dk, VEC);
+            tile_to_regs<CH, DKP, NTW, Cfg::QPER>(tid, kb, make_rsrc(k + (bg * T + c * CH) * dk, tb), dk, VEC);
+            regs_to_lds<CH, DKP, NTW, Cfg::QPER, LDK>(tid, qb, SX);
+            regs_to_lds<CH, DKP, NTW, Cfg::QPER, LDK>(tid, kb, SX + CH * LDK);
+        }
+        __syncthreads();
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int t = cc_tile(wave, u), ti = t >> 2, tj = t & 3;
-        accA[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (tj <= ti) mma16_abt<LDK, LDK>(accA[u], RQ + 16 * ti * LDK, RKV + 16 * tj * LDK, 0, DKP, tid0 & 63);
+        for (int u = 0; u < NL; ++u) issue(0, tid, u);
+#pragma unroll
+        for (int m = 0; m < NQ; ++m)
+            qa[m] = *reinterpret_cast<const float4 *>(SX + (32 * rt + cl) * LDK + 8 * m + 4 * kh);
+        // this wave's quarter of dk: m in [slot NQQ, slot NQQ + NQQ)
+        float4 ka[2][NQQ];
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt) {
+#pragma unroll
+            for (int mm = 0; mm < NQQ; ++mm)
+                ka[jt][mm] = *reinterpret_cast<const float4 *>(SX + (CH + 32 * jt + cl) * LDK +
+                                                               8 * (slot * NQQ + mm) + 4 * kh);
+        }
+        __syncthreads();   // Q and K read before the partial sums overwrite them
+        f32x16 part[2] = {zero16(), zero16()};
+#pragma unroll
+        for (int m = 0; m < NQ; ++m) {
+            if (m / NQQ == slot) {
+#pragma unroll
+                for (int jt = 0; jt < 2; ++jt) {
+                    if (jt <= rt) {
+                        const float4 x = ka[jt][m % NQQ], yq = qa[m];
+                        part[jt] = mfma32(x.x, yq.x, part[jt]);
+                        part[jt] = mfma32(x.y, yq.y, part[jt]);
+                        part[jt] = mfma32(x.z, yq.z, part[jt]);
+                        part[jt] = mfma32(x.w, yq.w, part[jt]);
+                    }
+                }
+            }
+        }
+        // partial sums: tile rt + jt (0: rows 0-31 x cols 0-31, 1: 32-63 x 0-31,
+        // 2: 32-63 x 32-63 of Q K^T), quarter slot, register group a
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt) {
+            if (jt <= rt) {
+#pragma unroll
+                for (int a = 0; a < 4; ++a)
+                    *reinterpret_cast<float4 *>(SX + ((((rt + jt) * 4 + slot) * 4 + a) * 64 + lane) * 4) =
+                        make_float4(part[jt][4 * a], part[jt][4 * a + 1], part[jt][4 * a + 2], part[jt][4 * a + 3]);
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt) {
+            kqt[jt] = zero16();
+            if (jt <= rt) {
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq) {
+#pragma unroll
+                    for (int a = 0; a < 4; ++a) {
+                        const float4 x =
+                            *reinterpret_cast<const float4 *>(SX + ((((rt + jt) * 4 + qq) * 4 + a) * 64 + lane) * 4);
+                        kqt[jt][4 * a] += x.x;
+                        kqt[jt][4 * a + 1] += x.y;
+                        kqt[jt][4 * a + 2] += x.z;
+                        kqt[jt][4 * a + 3] += x.w;
+                    }
+                }
+            }
+        }
+        __syncthreads();   // partial sums read before S_in overwrites them
+        stage(tid);
+        __syncthreads();
     }
-    __syncthreads();   // K is dead
 
-    for (int hh = 0; hh < hpg; ++hh) {
+    const int nstep = (hpg + HPS - 1) / HPS;
+    for (int st = 0; st < nstep; ++st) {
         // per-lane index arithmetic stays inside the loop (see k_bwd_grads)
         int tid = threadIdx.x;
         asm volatile("" : "+v"(tid));
-        const int lane = tid & 63, cl = lane & 31, l16 = lane & 15, lq = lane >> 4;
-        const int64_t bh = bh0 + hh;
-        const rsrc_t yb = make_rsrc(y + (bh * T + c * CH) * dv, (int64_t)rows * dv * 4);
+        const int lane = tid & 63, cl = lane & 31, kh = lane >> 5;
+        const int hh = st * HPS + hs;
+        const bool live = hh < hpg;
+        const int64_t bh = bh0 + (live ? hh : 0);
 
-        regs_to_lds<CH, DVP, NTW, TPER, LDV>(tid, vbuf, RKV);
-        if (tid < CH) {
-            bs[tid] = bpre;
-            eb[tid] = expf(bpre);
+        // Q S_in; MFMA group m issues the next step's loads [m NL / NQ, (m + 1) NL / NQ)
+        // two accumulators, so that one wave alone issues MFMAs back to back
+        f32x16 acc = zero16(), acc2 = zero16();
+        {
+            const float *sb = SX + (hs * DKP + 4 * kh) * LS + 32 * ct + cl;
+            float bq[2][4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) bq[0][s] = sb[s * LS];
+#pragma unroll
+            for (int m = 0; m < NQ; ++m) {
+                if (m + 1 < NQ) {
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) bq[(m + 1) & 1][s] = sb[(8 * (m + 1) + s) * LS];
+                }
+#pragma unroll
+                for (int u = m * NL / NQ; u < (m + 1) * NL / NQ; ++u) issue(st + 1, tid, u);
+                acc = mfma32(qa[m].x, bq[m & 1][0], acc);
+                acc2 = mfma32(qa[m].y, bq[m & 1][1], acc2);
+                acc = mfma32(qa[m].z, bq[m & 1][2], acc);
+                acc2 = mfma32(qa[m].w, bq[m & 1][3], acc2);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
-        store_slab(SL[0], tid);
-        if (NSL > 1) {
-            load_slab(hh, 1, tid);
-        } else {
-            load_v(hh + 1, tid);
-            load_slab(hh + 1, 0, tid);
+        const float *bsh = bs + hs * CH, *ebh = eb + hs * CH;
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            const float4 e = *reinterpret_cast<const float4 *>(ebh + 32 * rt + 8 * a + 4 * kh);
+            acc[4 * a] = (acc[4 * a] + acc2[4 * a]) * e.x;
+            acc[4 * a + 1] = (acc[4 * a + 1] + acc2[4 * a + 1]) * e.y;
+            acc[4 * a + 2] = (acc[4 * a + 2] + acc2[4 * a + 2]) * e.z;
+            acc[4 * a + 3] = (acc[4 * a + 3] + acc2[4 * a + 3]) * e.w;
         }
+        acc2 = zero16();
+        // P V: p_ij = (Q K^T)_ij exp(b_i - b_j) for j <= i, exp(-inf) = 0 above
+        // the diagonal; the row group's V operands and decays are read ahead.
+        {
+            const int i = 32 * rt + cl;
+            const float bi = bsh[i];
+            const float *vb = VS + (hs * CH + 4 * kh) * LS + 32 * ct + cl;
+#pragma unroll
+            for (int jt = 0; jt < 2; ++jt) {
+                if (jt <= rt) {
+                    float bv[16];
+                    float4 bj[4];
+#pragma unroll
+                    for (int a = 0; a < 4; ++a) {
+                        bj[a] = *reinterpret_cast<const float4 *>(bsh + 32 * jt + 8 * a + 4 * kh);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) bv[4 * a + e] = vb[(32 * jt + 8 * a + e) * LS];
+                    }
+                    __builtin_amdgcn_sched_barrier(0);   // all reads issued before the MFMAs
+                    float p[16];
+#pragma unroll
+                    for (int a = 0; a < 4; ++a) {
+                        const float bjs[4] = {bj[a].x, bj[a].y, bj[a].z, bj[a].w};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int j = 32 * jt + 8 * a + 4 * kh + e;
+                            p[4 * a + e] = kqt[jt][4 * a + e] * __expf(j <= i ? bi - bjs[e] : -INFINITY);
+                        }
+                    }
+                    __builtin_amdgcn_sched_barrier(0);   // the decay factors before the MFMAs
+#pragma unroll
+                    for (int r = 0; r < 16; r += 2) {
+                        acc = mfma32(p[r], bv[r], acc);
+                        acc2 = mfma32(p[r + 1], bv[r + 1], acc2);
+                    }
+                }
+            }
+        }
+        {
+            const rsrc_t yb = make_rsrc(y + (bh * T + c * CH) * dv, live ? (int64_t)rows * dv * 4 : 0);
+            const int n = 32 * ct + cl;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int t = 32 * rt + acc_row(r, lane);   // rows past the sequence end fall outside yb
+                gstore1(yb, n < dv ? (uint32_t)(t * dv + n) * 4u : kOOB, acc[r] + acc2[r]);
+            }
+        }
+        __syncthreads();   // S_in, V and decay reads done before the next step's writes
+        stage(tid);
         __syncthreads();
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int t = cc_tile(wave, u), ti = t >> 2, tj = t & 3;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = 16 * ti + 4 * lq + r, j = 16 * tj + l16;
-                RP[i * LDP + j] = (j <= i) ? accA[u][r] * expf(bs[i] - bs[j]) : 0.f;
-            }
-        }
-        __syncthreads();
-
-#pragma unroll
-        for (int m = 0; m < NSL; ++m) {
-            if (m > 0) {
-                store_slab(SL[m & 1], tid);
-                if (m + 1 < NSL) {
-                    load_slab(hh, m + 1, tid);
-                } else {
-                    load_v(hh + 1, tid);
-                    load_slab(hh + 1, 0, tid);
-                }
-                __syncthreads();
-            }
-            // tile: positions 16 rt .. 16 rt + 15, columns 32 m + 16 ct .. + 15
-            const int rt = ((wave >> 1) + m) & 3, ct = wave & 1;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            {
-                const float *aq = RQ + (16 * rt + l16) * LDK + 4 * lq;
-                const float *bsl = SL[m & 1] + 4 * lq * LSL + 16 * ct + l16;
-#pragma unroll 2
-                for (int i0 = 0; i0 < DKP; i0 += 16) {
-                    const float4 a = *reinterpret_cast<const float4 *>(aq + i0);
-                    acc = mfma16(a.x, bsl[(i0 + 0) * LSL], acc);
-                    acc = mfma16(a.y, bsl[(i0 + 1) * LSL], acc);
-                    acc = mfma16(a.z, bsl[(i0 + 2) * LSL], acc);
-                    acc = mfma16(a.w, bsl[(i0 + 3) * LSL], acc);
-                }
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] *= eb[16 * rt + 4 * lq + r];
-            {
-                const float *ap = RP + (16 * rt + l16) * LDP + 4 * lq;
-                const float *bv = RKV + 4 * lq * LDV + 32 * m + 16 * ct + l16;
-                const int jend = 16 * (rt + 1);
-                for (int j0 = 0; j0 < jend; j0 += 16) {
-                    const float4 a = *reinterpret_cast<const float4 *>(ap + j0);
-                    acc = mfma16(a.x, bv[(j0 + 0) * LDV], acc);
-                    acc = mfma16(a.y, bv[(j0 + 1) * LDV], acc);
-                    acc = mfma16(a.z, bv[(j0 + 2) * LDV], acc);
-                    acc = mfma16(a.w, bv[(j0 + 3) * LDV], acc);
-                }
-            }
-            const int n = 32 * m + 16 * ct + l16;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 16 * rt + 4 * lq + r;   // rows past the sequence end fall outside yb
-                gstore1(yb, n < dv ? (uint32_t)(t * dv + n) * 4u : kOOB, acc[r]);
-            }
-        }
-        __syncthreads();   // V, P and slab reads done before the next head's writes
     }
 }
 

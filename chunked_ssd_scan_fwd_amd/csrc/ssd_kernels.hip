@@ -859,44 +859,62 @@ __global__ __launch_bounds__(NTW) void k_chunk_output(const float *__restrict__ 
 // ---------------------------------------------------------------------------
 // B3 + B4: gradients of one chunk for every head of one group.
 //
-// One block of 8 waves per (b, g, chunk).  The group's heads are taken in
-// ascending order; dq and dk are summed over them in registers.  Per head:
+// One block of 8 waves per (b, g, chunk); the group's heads are taken in
+// ascending order and dq, dk are summed over them in registers.  All
+// products run on v_mfma_f32_32x32x2f32 with one operand in registers where
+// it is reused, and the other read from LDS with conflict-free strides.
+// Per head:
 //
-//   state phase  S_in and dS_out are streamed through LDS in slabs of 32
-//                state columns (all dk rows of both).  With the slab's 32
-//                columns n of dY and V:
-//                    Gq += dY[:, n] S_in[:, n]^T      (C x dk, 32x32 tiles)
-//                    Gk += V[:, n] dS_out[:, n]^T     (C x dk, 32x32 tiles)
-//                    Gv[:, n] = K dS_out[:, n]        (C x 32, 16x16 tiles)
-//                and every thread adds the products of the state elements
-//                it staged to <dS_out, S_in>.
-//   intra phase  dP = (dY V^T) o D and P = (Q K^T) o D, then
-//                    dQ += diag(e^b) Gq + dP K
-//                    dK += diag(e^{b_L - b}) Gk + dP^T Q
-//                    dV  = diag(e^{b_L - b}) Gv + P^T dY
-//                and dlog_alpha for the chunk's positions.
+//   pass 1 (state)  S_in and dS_out stream through LDS in double-buffered
+//                   slabs of 32 state rows.  For slab rows k:
+//                     waves 0-3:  Gq[rt, k] = dY[rt] S_in[k, :]^T   (their half of dv)
+//                     waves 4-7:  Gk[rt, k] = V[rt] dS_out[k, :]^T
+//                   folded at once into the cross-head sums
+//                     dQ += diag(e^b) Gq,  dK += diag(e^{b_L - b}) Gk
+//                   and into the rows' dlog_alpha dot products; and
+//                     Gv[jt, ct] += K[jt, k] dS_out[k, ct]      (one dv tile per wave)
+//                   The wave's rows of dY (or V) stay in registers across
+//                   the slabs, and each thread adds up <dS_out, S_in> over
+//                   the elements it stages.
+//   pass 2 (intra)  dY and V go to LDS.  With P = (Q K^T) o D and
+//                   dP = (dY V^T) o D:
+//                     dV = diag(e^{b_L - b}) Gv + P^T dY    (stored per head)
+//                     dQ += dP K,  dK += dP^T Q
+//                   and dlog_alpha for the chunk's positions.
 //
-// Every MFMA operand is read from LDS.  The LDS regions are Q / slabs (the
-// two share memory in time; Q is staged again for every head), K, dY,
-// V / ((dY V^T) partial sums + P) and dP / M.  The next head's V, dY and
-// first slab, and each next slab, are loaded into registers while the
-// current ones are in use.  Row strides keep the 16-byte row reads and the
-// column reads free of LDS bank conflicts.
+// Q K^T is formed once per block and kept in registers in the accumulator
+// layout of Q K^T tiles: register r of lane (kh, j) holds row
+// 8 (r / 4) + 4 kh + r % 4, column j, which is the operand layout of P^T in
+// P^T dY and matches the accumulators of the dY V^T tiles, so P, dP and
+// M = P o dP need no data movement.  dY V^T is split over pairs of waves
+// (halves of dv) and summed through LDS; dP goes to LDS once for the
+// transposed reads of dQ += dP K and dK += dP^T Q.
+//
+// The rectangle sums R_r = sum_{i >= r, j < r} M_ij of dlog_alpha use that
+// only the strictly lower triangle of M enters, and an element M_ij (j < i)
+// is counted for r in (j, i]:
+//     R_r = sum_{t < r} (c_t - w_t),  c_t = sum_{i > t} M_it,  w_t = sum_{j < t} M_tj,
+// so the chunk needs the row and column sums of M's strictly lower part and
+// one exclusive prefix sum, all from registers.
 template <int DKP, int DVP>
 struct BwdCfg {
-    static constexpr int LDK = DKP + 4;   // Q, K
-    static constexpr int LDV = DVP + 4;   // dY, V
-    static constexpr int LDP = CH + 4;    // dP, M, P
-    static constexpr int LSL = 36;        // slab rows: 32 state columns + 4
-    static constexpr int NKB = DKP / 32;  // 32-column blocks of dk
-    static constexpr int NTK = 2 * NKB;   // 32x32 tiles of a C x dk result
-    static constexpr int NSL = DVP / 32;  // slabs per state
-    static constexpr int QN = (CH * LDK > 2 * DKP * LSL) ? CH * LDK : 2 * DKP * LSL;
-    static constexpr int VN = CH * LDV;
-    static constexpr int PN = CH * LDP;
-    static constexpr int TPER = (CH * DVP / 4 + NTW - 1) / NTW;   // float4 / thread, C x dv tile
-    static constexpr int QPER = (CH * DKP / 4 + NTW - 1) / NTW;   // float4 / thread, C x dk tile
-    static constexpr int SPER = (DKP * 8 + NTW - 1) / NTW;        // float4 / thread, one state slab
+    static constexpr int cmax(int a, int b) { return a > b ? a : b; }
+    static constexpr int NKS = DKP / 32;      // 32-row slabs of the states
+    static constexpr int NCT = DVP / 32;      // 32-column blocks of dv
+    static constexpr int NH = DVP / 2;        // dv columns per half
+    static constexpr int NA = NH / 8;         // float4 of a row half per lane
+    static constexpr int LDQ = DKP + 4;       // Q rows (column reads pair rows i, i + 8)
+    static constexpr int LDK = DKP + 8;       // K rows (column reads pair rows j, j + 4)
+    static constexpr int LSL = DVP + 4;       // slab rows (column reads pair rows k, k + 8)
+    static constexpr int LDY = DVP + 8;       // dY, V rows (column reads pair rows i, i + 4)
+    static constexpr int LDP = CH + 4;        // dP rows (column reads pair rows i, i + 8)
+    static constexpr int SLN = 32 * LSL;      // one slab of one state
+    static constexpr int XN = cmax(cmax(cmax(4 * SLN, 2 * CH * LDY), 2 * CH * LDQ), cmax(12 * 1024, cmax(4 * NKS * 1024, 6 * 1024 + CH * LDP)));
+    static constexpr int SPER = (32 * DVP / 4 + NTW - 1) / NTW;   // float4 / thread, one slab of one state
+    static constexpr int QPER = (CH * DKP / 4 + NTW - 1) / NTW;   // float4 / thread, one C x dk tile
+    static constexpr int NQQ = DKP / 32;                          // float4 per lane, a quarter of dk
+    static constexpr int RD2 = (NCT == 4) ? 6 : 2;                // reducer of dY V^T tile (1, 1)
+    static constexpr int PD2 = (NCT == 4) ? 2 : 6;                // its partner
 };
 
 template <int DKP, int DVP, bool VEC>
@@ -908,20 +926,16 @@ __global__ __launch_bounds__(NTW) void k_bwd_grads(
     int dv_, int64_t NC, int64_t NCp, int64_t Epad)
 {
     using Cfg = BwdCfg<DKP, DVP>;
-    constexpr int LDK = Cfg::LDK, LDV = Cfg::LDV, LDP = Cfg::LDP, LSL = Cfg::LSL;
-    constexpr int NKB = Cfg::NKB, NTK = Cfg::NTK, NSL = Cfg::NSL;
-    constexpr int TPER = Cfg::TPER, QPER = Cfg::QPER, SPER = Cfg::SPER;
-    __shared__ __attribute__((aligned(16))) float RQ[Cfg::QN];
-    __shared__ __attribute__((aligned(16))) float RK[CH * LDK];
-    __shared__ __attribute__((aligned(16))) float RY[CH * LDV];
-    __shared__ __attribute__((aligned(16))) float RV[Cfg::VN];
-    __shared__ __attribute__((aligned(16))) float RP[Cfg::PN];
-    __shared__ float bs[CH], eb[CH], el[CH];
-    __shared__ float redQ[NKB][CH], redK[NKB][CH];
-    __shared__ float redR[NTW / 64][CH];
-    __shared__ float redB[NTW / 64];
-    float *const slS = RQ;               // S_in slab   [DKP][LSL]
-    float *const slD = RQ + DKP * LSL;   // dS_out slab [DKP][LSL]
+    constexpr int NKS = Cfg::NKS, NCT = Cfg::NCT, NH = Cfg::NH, NA = Cfg::NA;
+    constexpr int LDQ = Cfg::LDQ, LDK = Cfg::LDK, LSL = Cfg::LSL, LDY = Cfg::LDY, LDP = Cfg::LDP;
+    constexpr int SLN = Cfg::SLN, SPER = Cfg::SPER, QPER = Cfg::QPER, NQQ = Cfg::NQQ;
+    __shared__ __attribute__((aligned(16))) float QL[CH * LDQ];
+    __shared__ __attribute__((aligned(16))) float KL[CH * LDK];
+    // slabs (pass 1); dY, V and then dP (pass 2); partial sums (set-up, end)
+    __shared__ __attribute__((aligned(16))) float X[Cfg::XN];
+    __shared__ __attribute__((aligned(16))) float QKT[3 * 1024];   // Q K^T tiles, accumulator layout
+    __shared__ __attribute__((aligned(16))) float bs[CH], eb[CH], el[CH];
+    __shared__ float redq[2][CH], redk[2][CH], rsm[3][32], csm[3][2][32], redf[NTW / 64], sfx[CH];
 
     const int64_t c = blockIdx.x % NC;
     const int64_t bg = blockIdx.x / NC;
@@ -930,87 +944,151 @@ __global__ __launch_bounds__(NTW) void k_bwd_grads(
     const int hpg = H / G;
     const int64_t bh0 = b * H + (int64_t)g * hpg;
     const int rows = (int)((T - c * CH) < CH ? (T - c * CH) : CH);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int cl = lane & 31;
-    const int l16 = lane & 15, lq = lane >> 4;
-    constexpr bool vk = VEC, vv = VEC;   // 16-byte loads (dk and dv multiples of 4)
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int grp = wave >> 2, rt = (wave >> 1) & 1, half = wave & 1;
+    const bool gvw = wave < 2 * NCT;              // owns dV tile (jv, cv)
+    const int jv = wave / NCT, cv = wave % NCT;
+    // dY V^T tile td (0: rows 0-31 x cols 0-31, 1: 32-63 x 0-31, 2: 32-63 x 32-63):
+    // the reducer takes dv half 0, its partner half 1
+    const int td = (wave == 0 || wave == 4) ? 0 : (wave == 1 || wave == 5) ? 1
+                 : (wave == Cfg::RD2 || wave == Cfg::PD2) ? 2 : -1;
+    const bool red = wave == 0 || wave == 1 || wave == Cfg::RD2;
     const int64_t E = (int64_t)dk_ * dv_;
-    const rsrc_t qsrc = make_rsrc(q + (bg * T + c * CH) * dk_, (int64_t)rows * dk_ * 4);
 
-    float4 vbuf[TPER], ybuf[TPER];   // a head's V and dY
-    float4 sbuf[SPER], dbuf[SPER];   // a slab of S_in and of dS_out
-    float4 qbuf[QPER];               // Q
-    float bpre = 0.f, blpre = 0.f;   // a head's b (thread t < 64: position t) and b_L
+    struct Slab { float4 s[SPER], d[SPER]; };
+    float4 ar[NA];             // dY (waves 0-3) or V (4-7): row 32 rt + i, dv half `half`
+    // QKT[t][a][lane][e] = register 4a + e of lane `lane` of Q K^T tile t
+    auto qkt = [&](int t, int r, int lane) { return QKT[t * 1024 + ((r >> 2) * 64 + lane) * 4 + (r & 3)]; };
+    Slab p0, pn;               // next head's slab 0; the next slab to stage (pass 1), the next head's slab 1 (pass 2)
+    float bpre = 0.f, blpre = 0.f;
 
-    // Loads of head hh; hh == hpg (one past the last head) loads zeros, so the
-    // prefetches need no condition and the compiler's count of loads in
-    // flight stays exact.
-    auto load_vy = [&](int hh, int tid) {
+    auto load_a = [&](int hh, int tid) {
         const bool live = hh < hpg;
         const int64_t bh = bh0 + (live ? hh : 0);
-        const int64_t tb = live ? (int64_t)rows * dv_ * 4 : 0;
-        tile_to_regs<CH, DVP, NTW, TPER>(tid, vbuf, make_rsrc(v + (bh * T + c * CH) * dv_, tb), dv_, vv);
-        tile_to_regs<CH, DVP, NTW, TPER>(tid, ybuf, make_rsrc(dy + (bh * T + c * CH) * dv_, tb), dv_, vv);
-        bpre = gload1(make_rsrc(bcum + bh * NC * CH + c * CH, live ? CH * 4 : 0), (uint32_t)(tid & 63) * 4u);
-        blpre = bl[bh * NCp + c];
+        const float *src = (grp ? v : dy) + (bh * T + c * CH) * dv_;
+        const rsrc_t r = make_rsrc(src, live ? (int64_t)rows * dv_ * 4 : 0);
+        const int lane = tid & 63, cl = lane & 31, kh = lane >> 5;
+#pragma unroll
+        for (int m = 0; m < NA; ++m)
+            ar[m] = load4(r, (uint32_t)((32 * rt + cl) * dv_), half * NH + 8 * m + 4 * kh, dv_, true, VEC);
     };
-    auto load_slab = [&](int hh, int m, int tid) {
+    auto load_a1 = [&](int hh, int tid, int m) {   // one float4 of load_a
+        const bool live = hh < hpg;
+        const int64_t bh = bh0 + (live ? hh : 0);
+        const float *src = (grp ? v : dy) + (bh * T + c * CH) * dv_;
+        const rsrc_t r = make_rsrc(src, live ? (int64_t)rows * dv_ * 4 : 0);
+        const int lane = tid & 63, cl = lane & 31, kh = lane >> 5;
+        ar[m] = load4(r, (uint32_t)((32 * rt + cl) * dv_), half * NH + 8 * m + 4 * kh, dv_, true, VEC);
+    };
+    auto load_slab = [&](Slab &p, int hh, int ks, int tid) {
         const bool live = hh < hpg;
         const int64_t off = ((bh0 + (live ? hh : 0)) * NC + c) * Epad;
         const rsrc_t sr = make_rsrc(states + off, live ? E * 4 : 0), dr = make_rsrc(dstates + off, live ? E * 4 : 0);
-        const int lim = dv_ - 32 * m;
 #pragma unroll
         for (int u = 0; u < SPER; ++u) {
             const int idx = tid + u * NTW;
-            const int r = idx >> 3, c4 = (idx & 7) * 4;
-            const bool ok = idx < DKP * 8 && r < dk_;
-            sbuf[u] = load4(sr, (uint32_t)(r * dv_ + 32 * m), c4, lim, ok, vv);
-            dbuf[u] = load4(dr, (uint32_t)(r * dv_ + 32 * m), c4, lim, ok, vv);
+            const int r = idx / (DVP / 4), c4 = (idx % (DVP / 4)) * 4;
+            const bool ok = idx < 32 * DVP / 4;
+            p.s[u] = load4(sr, (uint32_t)((32 * ks + r) * dv_), c4, dv_, ok, VEC);
+            p.d[u] = load4(dr, (uint32_t)((32 * ks + r) * dv_), c4, dv_, ok, VEC);
         }
     };
-    // Write the staged slab to LDS; returns this thread's part of <dS_out, S_in>.
-    auto store_slab = [&](int tid) -> float {
+    // Stage a slab into buffer buf; returns this thread's part of <dS_out, S_in>.
+    auto store_slab = [&](const Slab &p, int buf, int tid) -> float {
         float f = 0.f;
+        float *ds = X + buf * 2 * SLN;
 #pragma unroll
         for (int u = 0; u < SPER; ++u) {
             const int idx = tid + u * NTW;
-            if (idx < DKP * 8) {
-                const int r = idx >> 3, c4 = (idx & 7) * 4;
-                *reinterpret_cast<float4 *>(slS + r * LSL + c4) = sbuf[u];
-                *reinterpret_cast<float4 *>(slD + r * LSL + c4) = dbuf[u];
-                f += sbuf[u].x * dbuf[u].x + sbuf[u].y * dbuf[u].y + sbuf[u].z * dbuf[u].z +
-                     sbuf[u].w * dbuf[u].w;
+            if (idx < 32 * DVP / 4) {
+                const int r = idx / (DVP / 4), c4 = (idx % (DVP / 4)) * 4;
+                *reinterpret_cast<float4 *>(ds + r * LSL + c4) = p.s[u];
+                *reinterpret_cast<float4 *>(ds + SLN + r * LSL + c4) = p.d[u];
+                f += p.s[u].x * p.d[u].x + p.s[u].y * p.d[u].y + p.s[u].z * p.d[u].z + p.s[u].w * p.d[u].w;
             }
         }
         return f;
     };
+    auto load_b = [&](int hh, int tid) {
+        const bool live = hh < hpg;
+        const int64_t bh = bh0 + (live ? hh : 0);
+        bpre = gload1(make_rsrc(bcum + bh * NC * CH + c * CH, live ? CH * 4 : 0), (uint32_t)(tid & 63) * 4u);
+        blpre = gload1(make_rsrc(bl + bh * NCp + c, live ? 4 : 0), 0u);
+    };
+    auto stage_b = [&](int tid) {
+        if (tid < CH) {
+            bs[tid] = bpre;
+            eb[tid] = expf(bpre);
+            el[tid] = (tid < rows) ? expf(blpre - bpre) : 0.f;
+        }
+    };
 
-    // ---- block set-up: K, Q, A = Q K^T, the first head's V, dY and slab.
-    load_vy(0, tid);
-    tile_to_regs<CH, DKP, NTW, QPER>(tid, qbuf, qsrc, dk_, vk);
-    regs_to_lds<CH, DKP, NTW, QPER, LDK>(tid, qbuf, RQ);
-    tile_to_regs<CH, DKP, NTW, QPER>(tid, qbuf, make_rsrc(k + (bg * T + c * CH) * dk_, (int64_t)rows * dk_ * 4), dk_,
-                                     vk);
-    regs_to_lds<CH, DKP, NTW, QPER, LDK>(tid, qbuf, RK);
-    load_slab(0, 0, tid);
-    __syncthreads();
-    // this wave's two 16x16 tiles of Q K^T
-    f32x4 accA[2];
+    // ---- block set-up: Q, K in LDS; Q K^T; the first head's operands.
+    float fro_next;
+    {
+        const int tid = threadIdx.x, lane = tid & 63, cl = lane & 31, kh = lane >> 5;
+        {
+            float4 qb[QPER], kb[QPER];
+            const int64_t tb = (int64_t)rows * dk_ * 4;
+            tile_to_regs<CH, DKP, NTW, QPER>(tid, qb, make_rsrc(q + (bg * T + c * CH) * dk_, tb), dk_, VEC);
+            tile_to_regs<CH, DKP, NTW, QPER>(tid, kb, make_rsrc(k + (bg * T + c * CH) * dk_, tb), dk_, VEC);
+            load_a(0, tid);
+            load_slab(p0, 0, 0, tid);
+            if (NKS > 1) load_slab(pn, 0, 1, tid);
+            load_b(0, tid);
+            regs_to_lds<CH, DKP, NTW, QPER, LDQ>(tid, qb, QL);
+            regs_to_lds<CH, DKP, NTW, QPER, LDK>(tid, kb, KL);
+        }
+        __syncthreads();
+        // 12 units (tile t, quarter of dk); wave w takes units w and w + 8
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int t = cc_tile(wave, u), ti = t >> 2, tj = t & 3;
-        accA[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (tj <= ti) mma16_abt<LDK, LDK>(accA[u], RQ + 16 * ti * LDK, RK + 16 * tj * LDK, 0, DKP, lane);
+        for (int uu = 0; uu < 2; ++uu) {
+            const int u = wave + 8 * uu;
+            if (u < 12) {
+                const int t = u >> 2, qt = u & 3, it = t > 0, jt = t == 2;
+                f32x16 acc = zero16();
+#pragma unroll
+                for (int mm = 0; mm < NQQ; ++mm) {
+                    const int col = 8 * (qt * NQQ + mm) + 4 * kh;
+                    const float4 x = *reinterpret_cast<const float4 *>(QL + (32 * it + cl) * LDQ + col);
+                    const float4 y = *reinterpret_cast<const float4 *>(KL + (32 * jt + cl) * LDK + col);
+                    acc = mfma32(x.x, y.x, acc);
+                    acc = mfma32(x.y, y.y, acc);
+                    acc = mfma32(x.z, y.z, acc);
+                    acc = mfma32(x.w, y.w, acc);
+                }
+#pragma unroll
+                for (int a = 0; a < 4; ++a)
+                    *reinterpret_cast<float4 *>(X + ((u * 4 + a) * 64 + lane) * 4) =
+                        make_float4(acc[4 * a], acc[4 * a + 1], acc[4 * a + 2], acc[4 * a + 3]);
+            }
+        }
+        __syncthreads();
+        // sum the four quarters of each tile
+        for (int f = tid; f < 3 * 256; f += NTW) {
+            const int t = f >> 8, o = (f & 255) * 4;
+            float4 acc4 = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int qt = 0; qt < 4; ++qt) {
+                const float4 x = *reinterpret_cast<const float4 *>(X + (t * 4 + qt) * 1024 + o);
+                acc4.x += x.x;
+                acc4.y += x.y;
+                acc4.z += x.z;
+                acc4.w += x.w;
+            }
+            *reinterpret_cast<float4 *>(QKT + t * 1024 + o) = acc4;
+        }
+        __syncthreads();   // partial sums read before the slabs overwrite them
+        fro_next = store_slab(p0, 0, tid);
+        if (NKS > 1) fro_next += store_slab(pn, 1, tid);
+        if (NKS > 2) load_slab(pn, 0, 2, tid);
+        stage_b(tid);
+        __syncthreads();
     }
-    __syncthreads();   // Q reads done before the slab overwrites it
-    regs_to_lds<CH, DVP, NTW, TPER, LDV>(tid, vbuf, RV);
-    regs_to_lds<CH, DVP, NTW, TPER, LDV>(tid, ybuf, RY);
-    float fro_next = store_slab(tid);
-    __syncthreads();
 
-    const int rbk = wave / NKB, cbk = wave % NKB;   // this wave's dq / dk tile (waves < NTK)
-    const bool hasK = wave < NTK;
-    f32x16 dQacc = zero16(), dKacc = zero16();
+    f32x16 dacc[NKS];   // dQ^T (waves 0-3) or dK^T (4-7): state rows 32 ks + row(r), positions 32 rt + i
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) dacc[ks] = zero16();
 
     for (int hh = 0; hh < hpg; ++hh) {
         // Per-lane index arithmetic is redone inside the loop (the asm hides
@@ -1018,223 +1096,385 @@ __global__ __launch_bounds__(NTW) void k_bwd_grads(
         // budget.
         int tid = threadIdx.x;
         asm volatile("" : "+v"(tid));
-        const int lane = tid & 63, cl = lane & 31, l16 = lane & 15, lq = lane >> 4;
+        const int lane = tid & 63, cl = lane & 31, kh = lane >> 5;
         const int64_t bh = bh0 + hh;
-        const float bcur = bpre, blh = blpre;
+        const float blh = blpre;
         float fro = fro_next;
+        f32x16 gv = zero16();
 
-        // ---- head start: the head's decays, and P^T = ((Q K^T) o D)^T in RP
-        if (tid < CH) {
-            bs[tid] = bcur;
-            eb[tid] = expf(bcur);
-            el[tid] = (tid < rows) ? expf(blh - bcur) : 0.f;
-        }
-        __syncthreads();   // decays visible; the previous head's reads of RP done
-        f32x4 Dm[2];       // the decay mask D on this wave's two 16x16 tiles
+        // ---- pass 1: state slabs
+        const float *W = grp ? KL : QL;
+        const int ldw = grp ? LDK : LDQ;
+        // Fold one slab's tile, held transposed (register r of lane (kh, i): state
+        // row 32 ks + row(r), position 32 rt + i): dQ^T (dK^T) += tile x the
+        // position's scale, and the lane adds the position's dot product with its
+        // Q (K) row over those state rows.
+        const float sa = (grp ? el : eb)[32 * rt + cl];   // e^b (dQ) or e^{b_L - b} (dK)
+        float rd = 0.f;
+        auto fold = [&](const f32x16 &gt, const int ks) {
+            const float *wr = W + (32 * rt + cl) * ldw + 32 * ks + 4 * kh;
+            float t = 0.f;
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int t = cc_tile(wave, u), ti = t >> 2, tj = t & 3;
+            for (int a = 0; a < 4; ++a) {
+                const float4 w4 = *reinterpret_cast<const float4 *>(wr + 8 * a);
+                const float ws[4] = {w4.x, w4.y, w4.z, w4.w};
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = 16 * ti + 4 * lq + r, j = 16 * tj + l16;
-                Dm[u][r] = (j <= i) ? expf(bs[i] - bs[j]) : 0.f;
-                RP[j * LDP + i] = accA[u][r] * Dm[u][r];
-            }
-        }
-        __syncthreads();   // P^T visible
-
-        // ---- state phase, with dY V^T and dV accumulated slab by slab
-        const rsrc_t dvb = make_rsrc(dv + (bh * T + c * CH) * dv_, (int64_t)rows * dv_ * 4);
-        f32x16 gq = zero16(), gk = zero16();
-        f32x4 aD[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-        for (int m = 0; m < NSL; ++m) {
-            if (m > 0) {
-                __syncthreads();   // slab m - 1 fully read
-                fro += store_slab(tid);
-            }
-            if (m + 1 < NSL)
-                load_slab(hh, m + 1, tid);
-            else
-                tile_to_regs<CH, DKP, NTW, QPER>(tid, qbuf, qsrc, dk_, vk);
-            if (m > 0) __syncthreads();
-            if (hasK) {
-                mma_abt<LDV, LSL>(gq, RY + rbk * 32 * LDV + 32 * m, slS + cbk * 32 * LSL, 0, 32, lane);
-                mma_abt<LDV, LSL>(gk, RV + rbk * 32 * LDV + 32 * m, slD + cbk * 32 * LSL, 0, 32, lane);
-            }
-            // dY V^T over this slab's 32 columns
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int t = cc_tile(wave, u), ti = t >> 2, tj = t & 3;
-                if (tj <= ti)
-                    mma16_abt<LDV, LDV>(aD[u], RY + 16 * ti * LDV, RV + 16 * tj * LDV, 32 * m, 32 * m + 32, lane);
-            }
-            // dV tile: positions 16 rt .. 16 rt + 15, columns 32 m + 16 ct .. + 15:
-            //   diag(e^{b_L - b}) K dS_out + P^T dY   (P^T[t][j] nonzero for j >= t)
-            const int rt = ((wave >> 1) + m) & 3, ct = wave & 1;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            {
-                const float *ak = RK + (16 * rt + l16) * LDK + 4 * lq;
-                const float *bd = slD + 4 * lq * LSL + 16 * ct + l16;
-#pragma unroll 2
-                for (int i0 = 0; i0 < DKP; i0 += 16) {
-                    const float4 x = *reinterpret_cast<const float4 *>(ak + i0);
-                    acc = mfma16(x.x, bd[(i0 + 0) * LSL], acc);
-                    acc = mfma16(x.y, bd[(i0 + 1) * LSL], acc);
-                    acc = mfma16(x.z, bd[(i0 + 2) * LSL], acc);
-                    acc = mfma16(x.w, bd[(i0 + 3) * LSL], acc);
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * a + e;
+                    dacc[ks][r] += sa * gt[r];
+                    t += gt[r] * ws[e];
                 }
             }
+            rd += sa * t;
+        };
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] *= el[16 * rt + 4 * lq + r];
+        for (int ks = 0; ks < NKS; ++ks) {
+            if (ks > 0) __syncthreads();   // slab ks visible, slab ks - 1 read
+            if (ks >= 1 && ks + 1 < NKS) {
+                fro += store_slab(pn, (ks + 1) & 1, tid);
+                if (ks + 2 < NKS) load_slab(pn, hh, ks + 2, tid);
+            }
+            const float *sS = X + (ks & 1) * 2 * SLN, *sD = sS + SLN;
             {
-                const float *ap = RP + (16 * rt + l16) * LDP + 4 * lq;
-                const float *by = RY + 4 * lq * LDV + 32 * m + 16 * ct + l16;
-                for (int j0 = 16 * rt; j0 < CH; j0 += 16) {
-                    const float4 x = *reinterpret_cast<const float4 *>(ap + j0);
-                    acc = mfma16(x.x, by[(j0 + 0) * LDV], acc);
-                    acc = mfma16(x.y, by[(j0 + 1) * LDV], acc);
-                    acc = mfma16(x.z, by[(j0 + 2) * LDV], acc);
-                    acc = mfma16(x.w, by[(j0 + 3) * LDV], acc);
+                // Gq / Gk (chain gt) and Gv (chain gv) alternate, so each wave keeps
+                // two independent MFMA chains in flight; operands are read one group
+                // ahead.  Gv MFMA s contracts slab rows (gvrow(s), + 8).
+                constexpr int GPM = 16 / NA;   // Gv MFMAs per Gq group
+                f32x16 gt = zero16();
+                const float *bp = (grp ? sD : sS) + cl * LSL + half * NH + 4 * kh;
+                float4 yb[2];
+                yb[0] = *reinterpret_cast<const float4 *>(bp);
+                if (gvw) {
+                    const float *kp = KL + (32 * jv + cl) * LDK + 32 * ks + 8 * kh;
+                    const float *bd = sD + 8 * kh * LSL + 32 * cv + cl;
+                    auto gvrow = [](int t) { return 16 * (t >> 3) + 4 * ((t >> 2) & 1) + (t & 3); };
+                    float4 xk[4];
+#pragma unroll
+                    for (int g2 = 0; g2 < 4; ++g2)
+                        xk[g2] = *reinterpret_cast<const float4 *>(kp + 16 * (g2 >> 1) + 4 * (g2 & 1));
+                    float bv[2][GPM];
+#pragma unroll
+                    for (int u = 0; u < GPM; ++u) bv[0][u] = bd[gvrow(u) * LSL];
+#pragma unroll
+                    for (int m = 0; m < NA; ++m) {
+                        if (m + 1 < NA) {
+                            yb[(m + 1) & 1] = *reinterpret_cast<const float4 *>(bp + 8 * (m + 1));
+#pragma unroll
+                            for (int u = 0; u < GPM; ++u) bv[(m + 1) & 1][u] = bd[gvrow((m + 1) * GPM + u) * LSL];
+                        }
+                        const float4 y = yb[m & 1];
+                        const float ya[4] = {y.x, y.y, y.z, y.w}, aa[4] = {ar[m].x, ar[m].y, ar[m].z, ar[m].w};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            gt = mfma32(ya[e], aa[e], gt);
+#pragma unroll
+                            for (int u = e * GPM / 4; u < (e + 1) * GPM / 4; ++u) {
+                                const int t = m * GPM + u;
+                                const float4 x = xk[t >> 2];
+                                const float xs[4] = {x.x, x.y, x.z, x.w};
+                                gv = mfma32(xs[t & 3], bv[m & 1][u], gv);
+                            }
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                } else {
+#pragma unroll
+                    for (int m = 0; m < NA; ++m) {
+                        if (m + 1 < NA) yb[(m + 1) & 1] = *reinterpret_cast<const float4 *>(bp + 8 * (m + 1));
+                        const float4 y = yb[m & 1];
+                        gt = mfma32(y.x, ar[m].x, gt);
+                        gt = mfma32(y.y, ar[m].y, gt);
+                        gt = mfma32(y.z, ar[m].z, gt);
+                        gt = mfma32(y.w, ar[m].w, gt);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
+                fold(gt, ks);
+            }
+        }
+        // the two lane halves hold the dot products over different state rows
+        rd += __shfl_xor(rd, 32);
+        if (kh == 0) (grp ? redk[half] : redq[half])[32 * rt + cl] = rd;
+        fro = sum64_hi(fro);
+        if (lane == 63) redf[wave] = fro;
+        __syncthreads();   // slabs read
+        {
+            float *dst = X + (grp ? CH * LDY : 0) + (32 * rt + cl) * LDY + half * NH + 4 * kh;
+#pragma unroll
+            for (int m = 0; m < NA; ++m) *reinterpret_cast<float4 *>(dst + 8 * m) = ar[m];
+        }
+        __syncthreads();   // dY and V in LDS
+
+        // ---- pass 2
+        const float *RY = X, *RV = X + CH * LDY;
+        if (gvw) {
+            // dV tile (rows 32 jv + row(r), columns 32 cv + i) = diag(e^{b_L - b}) Gv + P^T dY.
+            // Per row block of P the operands are read and P formed first, then 16
+            // MFMAs run on two chains.
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                const float4 e4 = *reinterpret_cast<const float4 *>(el + 32 * jv + 8 * a + 4 * kh);
+                gv[4 * a] *= e4.x;
+                gv[4 * a + 1] *= e4.y;
+                gv[4 * a + 2] *= e4.z;
+                gv[4 * a + 3] *= e4.w;
+            }
+            f32x16 gv2 = zero16();
+            const int j = 32 * jv + cl;
+            const float bj = bs[j];
+#pragma unroll
+            for (int it = 0; it < 2; ++it) {
+                if (it >= jv) {
+                    float p[16], yv[16];
+#pragma unroll
+                    for (int a = 0; a < 4; ++a) {
+                        const float4 k4 = *reinterpret_cast<const float4 *>(QKT + (it + jv) * 1024 + (a * 64 + lane) * 4);
+                        const float4 b4 = *reinterpret_cast<const float4 *>(bs + 32 * it + 8 * a + 4 * kh);
+                        const float ks4[4] = {k4.x, k4.y, k4.z, k4.w}, bis[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int i = 32 * it + 8 * a + 4 * kh + e;
+                            yv[4 * a + e] = RY[i * LDY + 32 * cv + cl];
+                            p[4 * a + e] = ks4[e] * __expf(j <= i ? bis[e] - bj : -INFINITY);
+                        }
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int r = 0; r < 16; r += 2) {
+                        gv = mfma32(p[r], yv[r], gv);
+                        gv2 = mfma32(p[r + 1], yv[r + 1], gv2);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
-            const int n = 32 * m + 16 * ct + l16;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 16 * rt + 4 * lq + r;   // rows past the sequence end fall outside dvb
-                gstore1(dvb, n < dv_ ? (uint32_t)(t * dv_ + n) * 4u : kOOB, acc[r]);
-            }
-        }
-
-        // ---- intra phase
-        __syncthreads();   // slab and P^T reads done
-        regs_to_lds<CH, DKP, NTW, QPER, LDK>(tid, qbuf, RQ);
-        load_vy(hh + 1, tid);
-        load_slab(hh + 1, 0, tid);
-        // dP = (dY V^T) o D into RP; M = (Q K^T) o D o (dY V^T) kept for the rectangle sums
-        f32x4 pM[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int t = cc_tile(wave, u), ti = t >> 2, tj = t & 3;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = 16 * ti + 4 * lq + r, j = 16 * tj + l16;
-                RP[i * LDP + j] = aD[u][r] * Dm[u][r];
-                pM[u][r] = accA[u][r] * Dm[u][r] * aD[u][r];
-            }
-        }
-        __syncthreads();   // Q and dP visible
-
-        // state parts of dQ and dK, and their rows' dlog_alpha terms
-        if (hasK) {
+            gv += gv2;
+            const rsrc_t dvb = make_rsrc(dv + (bh * T + c * CH) * dv_, (int64_t)rows * dv_ * 4);
+            const int n = 32 * cv + cl;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int row = rbk * 32 + acc_row(r, lane);
-                gq[r] *= eb[row];
-                gk[r] *= el[row];
-                const float sq = sum32_hi(gq[r] * RQ[row * LDK + cbk * 32 + cl]);
-                const float sk = sum32_hi(gk[r] * RK[row * LDK + cbk * 32 + cl]);
-                if (cl == 31) {
-                    redQ[cbk][row] = sq;
-                    redK[cbk][row] = sk;
+                const int t = 32 * jv + acc_row(r, lane);   // rows past the sequence end fall outside dvb
+                gstore1(dvb, n < dv_ ? (uint32_t)(t * dv_ + n) * 4u : kOOB, gv[r]);
+            }
+        }
+        // dY V^T: each wave of a pair over one half of dv.  The next head's A rows
+        // are loaded one per MFMA group, so the loads do not all queue at once.
+        f32x16 ad = zero16();
+        if (td >= 0) {
+            const int it = td > 0, jt = td == 2, hd = red ? 0 : 1;
+            const float *ya = RY + (32 * it + cl) * LDY + hd * NH + 4 * kh;
+            const float *vb = RV + (32 * jt + cl) * LDY + hd * NH + 4 * kh;
+#pragma unroll
+            for (int m = 0; m < NA; ++m) {
+                const float4 x = *reinterpret_cast<const float4 *>(ya + 8 * m);
+                const float4 y = *reinterpret_cast<const float4 *>(vb + 8 * m);
+                ad = mfma32(x.x, y.x, ad);
+                ad = mfma32(x.y, y.y, ad);
+                ad = mfma32(x.z, y.z, ad);
+                ad = mfma32(x.w, y.w, ad);
+                load_a1(hh + 1, tid, m);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+#pragma unroll
+            for (int m = 0; m < NA; ++m) load_a1(hh + 1, tid, m);
+        }
+        load_b(hh + 1, tid);
+        __syncthreads();   // dY and V read
+        // both waves of a pair publish their half of the tile
+        if (td >= 0) {
+            float *xo = X + (2 * td + (red ? 0 : 1)) * 1024;
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+                *reinterpret_cast<float4 *>(xo + (a * 64 + lane) * 4) =
+                    make_float4(ad[4 * a], ad[4 * a + 1], ad[4 * a + 2], ad[4 * a + 3]);
+        }
+        __syncthreads();   // the halves of dY V^T visible
+        float *const DP = X + 6 * 1024;   // dP [CH][LDP]
+
+        if (td >= 0) {
+            // dP = (dY V^T) o D to LDS, and the row and column sums of the strictly
+            // lower part of M = (Q K^T) o D o (dY V^T); the reducer takes registers
+            // 0-7 of the tile, its partner 8-15
+            const int it = td > 0, jt = td == 2, hw = red ? 0 : 1;
+            const float *xp = X + (2 * td + (red ? 1 : 0)) * 1024;
+            const int j = 32 * jt + cl;
+            const float bj = bs[j];
+            float ms[8], csum = 0.f;
+#pragma unroll
+            for (int a2 = 0; a2 < 2; ++a2) {
+                const int a = 2 * hw + a2;
+                const float4 x = *reinterpret_cast<const float4 *>(xp + (a * 64 + lane) * 4);
+                const float4 k4 = *reinterpret_cast<const float4 *>(QKT + td * 1024 + (a * 64 + lane) * 4);
+                const float4 b4 = *reinterpret_cast<const float4 *>(bs + 32 * it + 8 * a + 4 * kh);
+                const float xs[4] = {x.x, x.y, x.z, x.w}, ks4[4] = {k4.x, k4.y, k4.z, k4.w};
+                const float bis[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int i = 32 * it + 8 * a + 4 * kh + e;
+                    const float own = hw == 0 ? ad[4 * a2 + e] : ad[8 + 4 * a2 + e];
+                    const float d = __expf(j <= i ? bis[e] - bj : -INFINITY);
+                    const float dp = (own + xs[e]) * d;
+                    DP[i * LDP + j] = dp;
+                    ms[4 * a2 + e] = (j < i) ? ks4[e] * dp : 0.f;   // (Q K^T) o D o (dY V^T)
+                    csum += ms[4 * a2 + e];
                 }
             }
-            dQacc += gq;
-            dKacc += gk;
-            // dQ += dP K over j <= i
-            {
-                const float *a = RP + (rbk * 32 + cl) * LDP + 4 * (lane >> 5);
-                const float *bk = RK + 4 * (lane >> 5) * LDK + cbk * 32 + cl;
-                const int jend = (rbk + 1) * 32;
-                for (int j0 = 0; j0 < jend; j0 += 8) {
-                    const float4 x = *reinterpret_cast<const float4 *>(a + j0);
-                    dQacc = mfma32(x.x, bk[(j0 + 0) * LDK], dQacc);
-                    dQacc = mfma32(x.y, bk[(j0 + 1) * LDK], dQacc);
-                    dQacc = mfma32(x.z, bk[(j0 + 2) * LDK], dQacc);
-                    dQacc = mfma32(x.w, bk[(j0 + 3) * LDK], dQacc);
+#pragma unroll
+            for (int r = 0; r < 8; ++r) ms[r] = dpp_add<kRowRor + 8>(ms[r]);
+#pragma unroll
+            for (int r = 0; r < 8; ++r) ms[r] = dpp_add<kRowRor + 4>(ms[r]);
+#pragma unroll
+            for (int r = 0; r < 8; ++r) ms[r] = dpp_add<kRowRor + 2>(ms[r]);
+#pragma unroll
+            for (int r = 0; r < 8; ++r) ms[r] = dpp_add<kRowRor + 1>(ms[r]);
+#pragma unroll
+            for (int r = 0; r < 8; ++r) ms[r] = dpp_add<kRowBcast15, 0xa>(ms[r]);
+            if (cl == 31) {
+#pragma unroll
+                for (int r = 0; r < 8; ++r) rsm[td][acc_row(8 * hw + r, lane)] = ms[r];
+            }
+            csum += __shfl_xor(csum, 32);
+            if (kh == 0) csm[td][hw][cl] = csum;
+        }
+        __syncthreads();   // dP and the reductions visible
+        // the next head's first slabs, in flight over the intra products
+        load_slab(p0, hh + 1, 0, tid);
+
+        if (grp == 0) {
+            // dQ[rt, ct] += dP[rt, :] K[:, ct] over j < 32 (rt + 1); this wave takes ct = half (mod 2)
+            // the wave's tiles (ct = half, half + 2) run interleaved on independent chains
+            const float *ap = DP + (32 * rt + cl) * LDP + 4 * kh;
+            const float *bk = KL + 4 * kh * LDK + cl;
+#pragma unroll
+            for (int a = 0; a < 8; ++a) {
+                if (a < 4 * (rt + 1)) {
+                    const float4 x = *reinterpret_cast<const float4 *>(ap + 8 * a);
+#pragma unroll
+                    for (int ct = 0; ct < NKS; ++ct) {
+                        if ((ct & 1) == half) {
+                            dacc[ct] = mfma32(bk[(8 * a + 0) * LDK + 32 * ct], x.x, dacc[ct]);
+                            dacc[ct] = mfma32(bk[(8 * a + 1) * LDK + 32 * ct], x.y, dacc[ct]);
+                            dacc[ct] = mfma32(bk[(8 * a + 2) * LDK + 32 * ct], x.z, dacc[ct]);
+                            dacc[ct] = mfma32(bk[(8 * a + 3) * LDK + 32 * ct], x.w, dacc[ct]);
+                        }
+                    }
+                }
+                if (a == 1 && NKS > 1) load_slab(pn, hh + 1, 1, tid);
+            }
+        } else {
+            // dK[rt, ct] += dP[:, rt]^T Q[:, ct] over i >= 32 rt; MFMA s = 8 g2 + e
+            // contracts rows (i0 + 16 g2 + e, + 8)
+            // the wave's tiles (ct = half, half + 2) run interleaved on independent chains
+            const float *ap = DP + 8 * kh * LDP + 32 * rt + cl;
+            const float *bq = QL + 8 * kh * LDQ + cl;
+#pragma unroll
+            for (int it = 0; it < 2; ++it) {
+                if (it >= rt) {
+#pragma unroll
+                    for (int g2 = 0; g2 < 2; ++g2) {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const int i = 32 * it + 16 * g2 + e;
+                            const float x = ap[i * LDP];
+#pragma unroll
+                            for (int ct = 0; ct < NKS; ++ct) {
+                                if ((ct & 1) == half) dacc[ct] = mfma32(bq[i * LDQ + 32 * ct], x, dacc[ct]);
+                            }
+                        }
+                        if (it == 1 && g2 == 0 && NKS > 1) load_slab(pn, hh + 1, 1, tid);
+                    }
                 }
             }
-            // dK += dP^T Q over j >= i
-            {
-                const float *a = RP + 4 * (lane >> 5) * LDP + rbk * 32 + cl;
-                const float *bq = RQ + 4 * (lane >> 5) * LDK + cbk * 32 + cl;
-                for (int j0 = rbk * 32; j0 < CH; j0 += 8) {
-#pragma unroll
-                    for (int s = 0; s < 4; ++s) dKacc = mfma32(a[(j0 + s) * LDP], bq[(j0 + s) * LDK], dKacc);
-                }
-            }
         }
-        __syncthreads();   // dP and Q reads done
-
-        // M to LDS (zero above the diagonal); the next head's V, dY, first slab
+        if (wave == 7) {
+            // dlog_alpha_r = R_r + sum_{i >= r} iq_i + sum_{j < r} ik_j + e^{b_L} <dS_out, S_in>
+            const int t = lane;
+            const float ik = redk[0][t] + redk[1][t];
+            const float rw = t < 32 ? rsm[0][t] : rsm[1][t - 32] + rsm[2][t - 32];
+            const float cs = t < 32 ? csm[0][0][t] + csm[0][1][t] + csm[1][0][t] + csm[1][1][t]
+                                    : csm[2][0][t - 32] + csm[2][1][t - 32];
+            float frob = 0.f;
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int t = cc_tile(wave, u), ti = t >> 2, tj = t & 3;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) RP[(16 * ti + 4 * lq + r) * LDP + 16 * tj + l16] = pM[u][r];
+            for (int w = 0; w < NTW / 64; ++w) frob += redf[w];
+            // suffix sum of iq: prefix sum over the reversed rows
+            const float iqr = redq[0][63 - t] + redq[1][63 - t];
+            sfx[63 - t] = scan64(iqr);
+            const float rr = shift_up1(scan64(cs - rw)), pk = shift_up1(scan64(ik));
+            // lanes exchange through sfx: order the write before the read
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            const float sq = sfx[t];
+            gstore1(make_rsrc(dla + bh * T + c * CH, (int64_t)rows * 4), (uint32_t)t * 4u,
+                    rr + sq + pk + expf(blh) * frob);
         }
-        regs_to_lds<CH, DVP, NTW, TPER, LDV>(tid, vbuf, RV);   // zeros after the last head
-        regs_to_lds<CH, DVP, NTW, TPER, LDV>(tid, ybuf, RY);
-        fro_next = store_slab(tid);
+        __syncthreads();   // dP, dY V^T sums and reductions read; the slab buffers are free
+        fro_next = store_slab(p0, 0, tid);
+        if (NKS > 1) fro_next += store_slab(pn, 1, tid);
+        if (NKS > 2) load_slab(pn, hh + 1, 2, tid);
+        stage_b(tid);
         __syncthreads();
-
-        // Rectangle sums R_r = sum_{i >= r} sum_{j < r} M_ij: exclusive prefix
-        // over j of every row (in place), then a suffix over i.
-#pragma unroll
-        for (int i = wave * 8; i < wave * 8 + 8; ++i) {
-            // shift, not subtract: the diagonal term must not enter the prefix
-            RP[i * LDP + lane] = shift_up1(scan64(RP[i * LDP + lane]));
-        }
-        __syncthreads();
-        {
-            float racc = 0.f;
-            for (int i = wave * 8; i < wave * 8 + 8; ++i)
-                if (i >= lane) racc += RP[i * LDP + lane];
-            redR[wave][lane] = racc;
-        }
-        fro = sum64_hi(fro);
-        if (lane == 63) redB[wave] = fro;
-        __syncthreads();
-
-        if (wave == 0) {
-            float frob = 0.f, rint = 0.f;
-#pragma unroll
-            for (int w = 0; w < NTW / 64; ++w) {
-                frob += redB[w];
-                rint += redR[w][lane];
-            }
-            float iq = 0.f, ik = 0.f;
-#pragma unroll
-            for (int cb = 0; cb < NKB; ++cb) {
-                iq += redQ[cb][lane];
-                ik += redK[cb][lane];
-            }
-            // inclusive suffix sum of iq, exclusive prefix sum of ik
-            float sq = iq, pk = ik;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float a1 = __shfl_down(sq, off);
-                const float a2 = __shfl_up(pk, off);
-                if (lane + off < 64) sq += a1;
-                if (lane >= off) pk += a2;
-            }
-            float pke = __shfl_up(pk, 1);
-            if (lane == 0) pke = 0.f;
-            gstore1(make_rsrc(dla + bh * T + c * CH, (int64_t)rows * 4), (uint32_t)lane * 4u,
-                    rint + sq + pke + expf(blh) * frob);
-        }
     }
 
-    if (hasK) {
-        const int colk = cbk * 32 + cl;
-        const int64_t tb = (int64_t)rows * dk_ * 4;
-        const rsrc_t qr = make_rsrc(dq + (bg * T + c * CH) * dk_, tb), kr = make_rsrc(dk + (bg * T + c * CH) * dk_, tb);
+    // ---- dq, dk: the two dv halves of each tile summed, transposed through
+    // LDS into [position][dk] rows, stored with 16-byte writes
+    {
+        const int tid = threadIdx.x, lane = tid & 63, cl = lane & 31, kh = lane >> 5;
+        float *xs = X + ((grp * 2 + rt) * NKS) * 1024;
+        if (half == 1) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int row = rbk * 32 + acc_row(r, lane);   // rows past the sequence end fall outside
-            const uint32_t o = colk < dk_ ? (uint32_t)(row * dk_ + colk) * 4u : kOOB;
-            gstore1(qr, o, dQacc[r]);
-            gstore1(kr, o, dKacc[r]);
+            for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+                for (int a = 0; a < 4; ++a)
+                    *reinterpret_cast<float4 *>(xs + ks * 1024 + (a * 64 + lane) * 4) =
+                        make_float4(dacc[ks][4 * a], dacc[ks][4 * a + 1], dacc[ks][4 * a + 2], dacc[ks][4 * a + 3]);
+            }
+        }
+        __syncthreads();
+        if (half == 0) {
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    const float4 x = *reinterpret_cast<const float4 *>(xs + ks * 1024 + (a * 64 + lane) * 4);
+                    dacc[ks][4 * a] += x.x;
+                    dacc[ks][4 * a + 1] += x.y;
+                    dacc[ks][4 * a + 2] += x.z;
+                    dacc[ks][4 * a + 3] += x.w;
+                }
+            }
+        }
+        __syncthreads();
+        // OUT[grp][position][k], row stride LDQ
+        if (half == 0) {
+            float *o = X + grp * CH * LDQ + (32 * rt + cl) * LDQ + 4 * kh;
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+                for (int a = 0; a < 4; ++a)
+                    *reinterpret_cast<float4 *>(o + 32 * ks + 8 * a) =
+                        make_float4(dacc[ks][4 * a], dacc[ks][4 * a + 1], dacc[ks][4 * a + 2], dacc[ks][4 * a + 3]);
+            }
+        }
+        __syncthreads();
+        const int64_t tb = (int64_t)rows * dk_ * 4;
+        const rsrc_t rq = make_rsrc(dq + (bg * T + c * CH) * dk_, tb), rk = make_rsrc(dk + (bg * T + c * CH) * dk_, tb);
+        constexpr int Q4 = DKP / 4;
+        for (int idx = tid; idx < 2 * CH * Q4; idx += NTW) {
+            const int gg = idx / (CH * Q4), rem = idx - gg * CH * Q4;
+            const int row = rem / Q4, c4 = (rem - row * Q4) * 4;
+            const float4 x = *reinterpret_cast<const float4 *>(X + gg * CH * LDQ + row * LDQ + c4);
+            const rsrc_t r = gg ? rk : rq;
+            if (VEC) {
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    __builtin_bit_cast(__attribute__((ext_vector_type(4))) int, x), r,
+                    c4 < dk_ ? (uint32_t)(row * dk_ + c4) * 4u : kOOB, 0, 0);
+            } else {
+                const float xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    gstore1(r, c4 + e < dk_ ? (uint32_t)(row * dk_ + c4 + e) * 4u : kOOB, xs[e]);
+            }
         }
     }
 }

@@ -859,36 +859,35 @@ __global__ __launch_bounds__(NTW) void k_chunk_output(const float *__restrict__ 
 // ---------------------------------------------------------------------------
 // B3 + B4: gradients of one chunk for every head of one group.
 //
-// One block of 8 waves per (b, g, chunk); the group's heads are taken in
-// ascending order and dq, dk are summed over them in registers.  All
-// products run on v_mfma_f32_32x32x2f32 with one operand in registers where
-// it is reused, and the other read from LDS with conflict-free strides.
-// Per head:
+// One block of 4 waves (one per SIMD, so a wave may hold up to 512 registers,
+// the MFMA accumulators in AGPRs) per (b, g, chunk); the group's heads are
+// taken in ascending order and dq, dk are summed over them in registers.  All
+// products run on v_mfma_f32_32x32x2f32.  Wave w has side grp = w / 2 (0: dQ,
+// 1: dK) and row block rt = w % 2 (positions 32 rt .. 32 rt + 31).  Per head:
 //
 //   pass 1 (state)  S_in and dS_out stream through LDS in double-buffered
-//                   slabs of 32 state rows.  For slab rows k:
-//                     waves 0-3:  Gq[rt, k] = dY[rt] S_in[k, :]^T   (their half of dv)
-//                     waves 4-7:  Gk[rt, k] = V[rt] dS_out[k, :]^T
-//                   folded at once into the cross-head sums
-//                     dQ += diag(e^b) Gq,  dK += diag(e^{b_L - b}) Gk
-//                   and into the rows' dlog_alpha dot products; and
-//                     Gv[jt, ct] += K[jt, k] dS_out[k, ct]      (one dv tile per wave)
-//                   The wave's rows of dY (or V) stay in registers across
-//                   the slabs, and each thread adds up <dS_out, S_in> over
-//                   the elements it stages.
+//                   slabs of 32 state rows k.  Each wave keeps its 32 rows of
+//                   dY (dQ side) or V (dK side) over all of dv in registers
+//                   and accumulates, for every 32-row block of dk, the
+//                   transposed tile
+//                       dQ^T[k, rt] += e^b     x (S_in dY^T)[k, rt]
+//                       dK^T[k, rt] += e^{b_L-b} x (dS_out V^T)[k, rt]
+//                   (the scale is per position, i.e. per lane), together with
+//                   the rows' dlog_alpha dot products, summed in-lane; and
+//                       Gv[rt, cv] += K[rt, k] dS_out[k, cv]
+//                   for its dv column blocks cv.  Each thread adds up
+//                   <dS_out, S_in> over the elements it stages.
 //   pass 2 (intra)  dY and V go to LDS.  With P = (Q K^T) o D and
 //                   dP = (dY V^T) o D:
-//                     dV = diag(e^{b_L - b}) Gv + P^T dY    (stored per head)
-//                     dQ += dP K,  dK += dP^T Q
+//                       dV = diag(e^{b_L - b}) Gv + P^T dY    (stored per head)
+//                       dQ^T += K^T dP^T,  dK^T += Q^T dP
 //                   and dlog_alpha for the chunk's positions.
 //
-// Q K^T is formed once per block and kept in registers in the accumulator
-// layout of Q K^T tiles: register r of lane (kh, j) holds row
-// 8 (r / 4) + 4 kh + r % 4, column j, which is the operand layout of P^T in
-// P^T dY and matches the accumulators of the dY V^T tiles, so P, dP and
-// M = P o dP need no data movement.  dY V^T is split over pairs of waves
-// (halves of dv) and summed through LDS; dP goes to LDS once for the
-// transposed reads of dQ += dP K and dK += dP^T Q.
+// Q K^T is formed once per block and kept in LDS in the accumulator layout of
+// Q K^T tiles (register r of lane (kh, j): row 8 (r / 4) + 4 kh + r % 4,
+// column j), which is the operand layout of P^T in P^T dY and matches the
+// accumulators of the dY V^T tiles, so P, dP and M = (Q K^T) o D o (dY V^T)
+// need no data movement.  dP goes to LDS once for the two intra products.
 //
 // The rectangle sums R_r = sum_{i >= r, j < r} M_ij of dlog_alpha use that
 // only the strictly lower triangle of M enters, and an element M_ij (j < i)
@@ -896,29 +895,30 @@ __global__ __launch_bounds__(NTW) void k_chunk_output(const float *__restrict__ 
 //     R_r = sum_{t < r} (c_t - w_t),  c_t = sum_{i > t} M_it,  w_t = sum_{j < t} M_tj,
 // so the chunk needs the row and column sums of M's strictly lower part and
 // one exclusive prefix sum, all from registers.
+constexpr int NTB = 256;   // 4 waves, one per SIMD
+
 template <int DKP, int DVP>
 struct BwdCfg {
     static constexpr int cmax(int a, int b) { return a > b ? a : b; }
     static constexpr int NKS = DKP / 32;      // 32-row slabs of the states
     static constexpr int NCT = DVP / 32;      // 32-column blocks of dv
-    static constexpr int NH = DVP / 2;        // dv columns per half
-    static constexpr int NA = NH / 8;         // float4 of a row half per lane
+    static constexpr int NCW = NCT >= 2 ? NCT / 2 : 1;   // dV column blocks per wave
+    static constexpr int NA = DVP / 8;        // float4 of a dY / V row per lane
     static constexpr int LDQ = DKP + 4;       // Q rows (column reads pair rows i, i + 8)
     static constexpr int LDK = DKP + 8;       // K rows (column reads pair rows j, j + 4)
     static constexpr int LSL = DVP + 4;       // slab rows (column reads pair rows k, k + 8)
     static constexpr int LDY = DVP + 8;       // dY, V rows (column reads pair rows i, i + 4)
     static constexpr int LDP = CH + 4;        // dP rows (column reads pair rows i, i + 8)
     static constexpr int SLN = 32 * LSL;      // one slab of one state
-    static constexpr int XN = cmax(cmax(cmax(4 * SLN, 2 * CH * LDY), 2 * CH * LDQ), cmax(12 * 1024, cmax(4 * NKS * 1024, 6 * 1024 + CH * LDP)));
-    static constexpr int SPER = (32 * DVP / 4 + NTW - 1) / NTW;   // float4 / thread, one slab of one state
-    static constexpr int QPER = (CH * DKP / 4 + NTW - 1) / NTW;   // float4 / thread, one C x dk tile
+    static constexpr int XN = cmax(cmax(cmax(4 * SLN, 2 * CH * LDY), 2 * CH * LDQ),
+                                   cmax(12 * 1024, 1024 + CH * LDP));
+    static constexpr int SPER = (32 * DVP / 4 + NTB - 1) / NTB;   // float4 / thread, one slab of one state
+    static constexpr int QPER = (CH * DKP / 4 + NTB - 1) / NTB;   // float4 / thread, one C x dk tile
     static constexpr int NQQ = DKP / 32;                          // float4 per lane, a quarter of dk
-    static constexpr int RD2 = (NCT == 4) ? 6 : 2;                // reducer of dY V^T tile (1, 1)
-    static constexpr int PD2 = (NCT == 4) ? 2 : 6;                // its partner
 };
 
 template <int DKP, int DVP, bool VEC>
-__global__ __launch_bounds__(NTW) void k_bwd_grads(
+__global__ __launch_bounds__(NTB) void k_bwd_grads(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
     const float *__restrict__ dy, const float *__restrict__ bcum, const float *__restrict__ bl,
     const float *__restrict__ states, const float *__restrict__ dstates, float *__restrict__ dq,
@@ -926,7 +926,7 @@ __global__ __launch_bounds__(NTW) void k_bwd_grads(
     int dv_, int64_t NC, int64_t NCp, int64_t Epad)
 {
     using Cfg = BwdCfg<DKP, DVP>;
-    constexpr int NKS = Cfg::NKS, NCT = Cfg::NCT, NH = Cfg::NH, NA = Cfg::NA;
+    constexpr int NKS = Cfg::NKS, NCT = Cfg::NCT, NCW = Cfg::NCW, NA = Cfg::NA;
     constexpr int LDQ = Cfg::LDQ, LDK = Cfg::LDK, LSL = Cfg::LSL, LDY = Cfg::LDY, LDP = Cfg::LDP;
     constexpr int SLN = Cfg::SLN, SPER = Cfg::SPER, QPER = Cfg::QPER, NQQ = Cfg::NQQ;
     __shared__ __attribute__((aligned(16))) float QL[CH * LDQ];
@@ -935,7 +935,7 @@ __global__ __launch_bounds__(NTW) void k_bwd_grads(
     __shared__ __attribute__((aligned(16))) float X[Cfg::XN];
     __shared__ __attribute__((aligned(16))) float QKT[3 * 1024];   // Q K^T tiles, accumulator layout
     __shared__ __attribute__((aligned(16))) float bs[CH], eb[CH], el[CH];
-    __shared__ float redq[2][CH], redk[2][CH], rsm[3][32], csm[3][2][32], redf[NTW / 64], sfx[CH];
+    __shared__ float redq[CH], redk[CH], rsm[3][32], csm[3][32], redf[NTB / 64], sfx[CH];
 
     const int64_t c = blockIdx.x % NC;
     const int64_t bg = blockIdx.x / NC;
@@ -945,40 +945,27 @@ __global__ __launch_bounds__(NTW) void k_bwd_grads(
     const int64_t bh0 = b * H + (int64_t)g * hpg;
     const int rows = (int)((T - c * CH) < CH ? (T - c * CH) : CH);
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    const int grp = wave >> 2, rt = (wave >> 1) & 1, half = wave & 1;
-    const bool gvw = wave < 2 * NCT;              // owns dV tile (jv, cv)
-    const int jv = wave / NCT, cv = wave % NCT;
-    // dY V^T tile td (0: rows 0-31 x cols 0-31, 1: 32-63 x 0-31, 2: 32-63 x 32-63):
-    // the reducer takes dv half 0, its partner half 1
-    const int td = (wave == 0 || wave == 4) ? 0 : (wave == 1 || wave == 5) ? 1
-                 : (wave == Cfg::RD2 || wave == Cfg::PD2) ? 2 : -1;
-    const bool red = wave == 0 || wave == 1 || wave == Cfg::RD2;
+    const int grp = wave >> 1, rt = wave & 1;
+    const bool gvw = grp * NCW < NCT;            // owns dV tiles (rt, grp NCW + u)
     const int64_t E = (int64_t)dk_ * dv_;
 
     struct Slab { float4 s[SPER], d[SPER]; };
-    float4 ar[NA];             // dY (waves 0-3) or V (4-7): row 32 rt + i, dv half `half`
+    float4 ar[NA];             // dY (dQ side) or V (dK side): row 32 rt + i, columns 8m + 4kh .. + 3
     // QKT[t][a][lane][e] = register 4a + e of lane `lane` of Q K^T tile t
-    auto qkt = [&](int t, int r, int lane) { return QKT[t * 1024 + ((r >> 2) * 64 + lane) * 4 + (r & 3)]; };
-    Slab p0, pn;               // next head's slab 0; the next slab to stage (pass 1), the next head's slab 1 (pass 2)
+    // (t = 0: rows 0-31 x cols 0-31, 1: rows 32-63 x cols 0-31, 2: rows 32-63 x cols 32-63)
+    auto qkt4 = [&](int t, int a, int lane) {
+        return *reinterpret_cast<const float4 *>(QKT + t * 1024 + (a * 64 + lane) * 4);
+    };
+    Slab p0, pn;               // the next head's slabs 0 and 1; in pass 1, the next slab to stage
     float bpre = 0.f, blpre = 0.f;
 
-    auto load_a = [&](int hh, int tid) {
+    auto load_a1 = [&](int hh, int tid, int m) {   // float4 m of the wave's A rows of head hh
         const bool live = hh < hpg;
         const int64_t bh = bh0 + (live ? hh : 0);
         const float *src = (grp ? v : dy) + (bh * T + c * CH) * dv_;
         const rsrc_t r = make_rsrc(src, live ? (int64_t)rows * dv_ * 4 : 0);
         const int lane = tid & 63, cl = lane & 31, kh = lane >> 5;
-#pragma unroll
-        for (int m = 0; m < NA; ++m)
-            ar[m] = load4(r, (uint32_t)((32 * rt + cl) * dv_), half * NH + 8 * m + 4 * kh, dv_, true, VEC);
-    };
-    auto load_a1 = [&](int hh, int tid, int m) {   // one float4 of load_a
-        const bool live = hh < hpg;
-        const int64_t bh = bh0 + (live ? hh : 0);
-        const float *src = (grp ? v : dy) + (bh * T + c * CH) * dv_;
-        const rsrc_t r = make_rsrc(src, live ? (int64_t)rows * dv_ * 4 : 0);
-        const int lane = tid & 63, cl = lane & 31, kh = lane >> 5;
-        ar[m] = load4(r, (uint32_t)((32 * rt + cl) * dv_), half * NH + 8 * m + 4 * kh, dv_, true, VEC);
+        ar[m] = load4(r, (uint32_t)((32 * rt + cl) * dv_), 8 * m + 4 * kh, dv_, true, VEC);
     };
     auto load_slab = [&](Slab &p, int hh, int ks, int tid) {
         const bool live = hh < hpg;
@@ -986,7 +973,7 @@ __global__ __launch_bounds__(NTW) void k_bwd_grads(
         const rsrc_t sr = make_rsrc(states + off, live ? E * 4 : 0), dr = make_rsrc(dstates + off, live ? E * 4 : 0);
 #pragma unroll
         for (int u = 0; u < SPER; ++u) {
-            const int idx = tid + u * NTW;
+            const int idx = tid + u * NTB;
             const int r = idx / (DVP / 4), c4 = (idx % (DVP / 4)) * 4;
             const bool ok = idx < 32 * DVP / 4;
             p.s[u] = load4(sr, (uint32_t)((32 * ks + r) * dv_), c4, dv_, ok, VEC);
@@ -999,7 +986,7 @@ __global__ __launch_bounds__(NTW) void k_bwd_grads(
         float *ds = X + buf * 2 * SLN;
 #pragma unroll
         for (int u = 0; u < SPER; ++u) {
-            const int idx = tid + u * NTW;
+            const int idx = tid + u * NTB;
             if (idx < 32 * DVP / 4) {
                 const int r = idx / (DVP / 4), c4 = (idx % (DVP / 4)) * 4;
                 *reinterpret_cast<float4 *>(ds + r * LSL + c4) = p.s[u];
@@ -1030,42 +1017,41 @@ __global__ __launch_bounds__(NTW) void k_bwd_grads(
         {
             float4 qb[QPER], kb[QPER];
             const int64_t tb = (int64_t)rows * dk_ * 4;
-            tile_to_regs<CH, DKP, NTW, QPER>(tid, qb, make_rsrc(q + (bg * T + c * CH) * dk_, tb), dk_, VEC);
-            tile_to_regs<CH, DKP, NTW, QPER>(tid, kb, make_rsrc(k + (bg * T + c * CH) * dk_, tb), dk_, VEC);
-            load_a(0, tid);
+            tile_to_regs<CH, DKP, NTB, QPER>(tid, qb, make_rsrc(q + (bg * T + c * CH) * dk_, tb), dk_, VEC);
+            tile_to_regs<CH, DKP, NTB, QPER>(tid, kb, make_rsrc(k + (bg * T + c * CH) * dk_, tb), dk_, VEC);
+#pragma unroll
+            for (int m = 0; m < NA; ++m) load_a1(0, tid, m);
             load_slab(p0, 0, 0, tid);
             if (NKS > 1) load_slab(pn, 0, 1, tid);
             load_b(0, tid);
-            regs_to_lds<CH, DKP, NTW, QPER, LDQ>(tid, qb, QL);
-            regs_to_lds<CH, DKP, NTW, QPER, LDK>(tid, kb, KL);
+            regs_to_lds<CH, DKP, NTB, QPER, LDQ>(tid, qb, QL);
+            regs_to_lds<CH, DKP, NTB, QPER, LDK>(tid, kb, KL);
         }
         __syncthreads();
-        // 12 units (tile t, quarter of dk); wave w takes units w and w + 8
+        // 12 units (tile t, quarter of dk); wave w takes units w, w + 4, w + 8
 #pragma unroll
-        for (int uu = 0; uu < 2; ++uu) {
-            const int u = wave + 8 * uu;
-            if (u < 12) {
-                const int t = u >> 2, qt = u & 3, it = t > 0, jt = t == 2;
-                f32x16 acc = zero16();
+        for (int uu = 0; uu < 3; ++uu) {
+            const int u = wave + 4 * uu;
+            const int t = u >> 2, qt = u & 3, it = t > 0, jt = t == 2;
+            f32x16 acc = zero16();
 #pragma unroll
-                for (int mm = 0; mm < NQQ; ++mm) {
-                    const int col = 8 * (qt * NQQ + mm) + 4 * kh;
-                    const float4 x = *reinterpret_cast<const float4 *>(QL + (32 * it + cl) * LDQ + col);
-                    const float4 y = *reinterpret_cast<const float4 *>(KL + (32 * jt + cl) * LDK + col);
-                    acc = mfma32(x.x, y.x, acc);
-                    acc = mfma32(x.y, y.y, acc);
-                    acc = mfma32(x.z, y.z, acc);
-                    acc = mfma32(x.w, y.w, acc);
-                }
-#pragma unroll
-                for (int a = 0; a < 4; ++a)
-                    *reinterpret_cast<float4 *>(X + ((u * 4 + a) * 64 + lane) * 4) =
-                        make_float4(acc[4 * a], acc[4 * a + 1], acc[4 * a + 2], acc[4 * a + 3]);
+            for (int mm = 0; mm < NQQ; ++mm) {
+                const int col = 8 * (qt * NQQ + mm) + 4 * kh;
+                const float4 x = *reinterpret_cast<const float4 *>(QL + (32 * it + cl) * LDQ + col);
+                const float4 y = *reinterpret_cast<const float4 *>(KL + (32 * jt + cl) * LDK + col);
+                acc = mfma32(x.x, y.x, acc);
+                acc = mfma32(x.y, y.y, acc);
+                acc = mfma32(x.z, y.z, acc);
+                acc = mfma32(x.w, y.w, acc);
             }
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+                *reinterpret_cast<float4 *>(X + ((u * 4 + a) * 64 + lane) * 4) =
+                    make_float4(acc[4 * a], acc[4 * a + 1], acc[4 * a + 2], acc[4 * a + 3]);
         }
         __syncthreads();
         // sum the four quarters of each tile
-        for (int f = tid; f < 3 * 256; f += NTW) {
+        for (int f = tid; f < 3 * 256; f += NTB) {
             const int t = f >> 8, o = (f & 255) * 4;
             float4 acc4 = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
@@ -1086,21 +1072,20 @@ __global__ __launch_bounds__(NTW) void k_bwd_grads(
         __syncthreads();
     }
 
-    f32x16 dacc[NKS];   // dQ^T (waves 0-3) or dK^T (4-7): state rows 32 ks + row(r), positions 32 rt + i
+    f32x16 dacc[NKS];   // dQ^T (dQ side) or dK^T (dK side): state rows 32 ks + row(r), positions 32 rt + i
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) dacc[ks] = zero16();
 
     for (int hh = 0; hh < hpg; ++hh) {
-        // Per-lane index arithmetic is redone inside the loop (the asm hides
-        // that tid is loop-invariant): hoisting it would exceed the register
-        // budget.
         int tid = threadIdx.x;
         asm volatile("" : "+v"(tid));
         const int lane = tid & 63, cl = lane & 31, kh = lane >> 5;
         const int64_t bh = bh0 + hh;
         const float blh = blpre;
         float fro = fro_next;
-        f32x16 gv = zero16();
+        f32x16 gv[NCW];
+#pragma unroll
+        for (int u = 0; u < NCW; ++u) gv[u] = zero16();
 
         // ---- pass 1: state slabs
         const float *W = grp ? KL : QL;
@@ -1135,71 +1120,63 @@ __global__ __launch_bounds__(NTW) void k_bwd_grads(
                 if (ks + 2 < NKS) load_slab(pn, hh, ks + 2, tid);
             }
             const float *sS = X + (ks & 1) * 2 * SLN, *sD = sS + SLN;
+            // Gq / Gk: A = slab rows (row i of the slab in lane i), B = the wave's rows;
+            // operands read one MFMA group ahead
+            f32x16 gt = zero16();
             {
-                // Gq / Gk (chain gt) and Gv (chain gv) alternate, so each wave keeps
-                // two independent MFMA chains in flight; operands are read one group
-                // ahead.  Gv MFMA s contracts slab rows (gvrow(s), + 8).
-                constexpr int GPM = 16 / NA;   // Gv MFMAs per Gq group
-                f32x16 gt = zero16();
-                const float *bp = (grp ? sD : sS) + cl * LSL + half * NH + 4 * kh;
+                const float *bp = (grp ? sD : sS) + cl * LSL + 4 * kh;
                 float4 yb[2];
                 yb[0] = *reinterpret_cast<const float4 *>(bp);
-                if (gvw) {
-                    const float *kp = KL + (32 * jv + cl) * LDK + 32 * ks + 8 * kh;
-                    const float *bd = sD + 8 * kh * LSL + 32 * cv + cl;
-                    auto gvrow = [](int t) { return 16 * (t >> 3) + 4 * ((t >> 2) & 1) + (t & 3); };
-                    float4 xk[4];
 #pragma unroll
-                    for (int g2 = 0; g2 < 4; ++g2)
-                        xk[g2] = *reinterpret_cast<const float4 *>(kp + 16 * (g2 >> 1) + 4 * (g2 & 1));
-                    float bv[2][GPM];
-#pragma unroll
-                    for (int u = 0; u < GPM; ++u) bv[0][u] = bd[gvrow(u) * LSL];
-#pragma unroll
-                    for (int m = 0; m < NA; ++m) {
-                        if (m + 1 < NA) {
-                            yb[(m + 1) & 1] = *reinterpret_cast<const float4 *>(bp + 8 * (m + 1));
-#pragma unroll
-                            for (int u = 0; u < GPM; ++u) bv[(m + 1) & 1][u] = bd[gvrow((m + 1) * GPM + u) * LSL];
-                        }
-                        const float4 y = yb[m & 1];
-                        const float ya[4] = {y.x, y.y, y.z, y.w}, aa[4] = {ar[m].x, ar[m].y, ar[m].z, ar[m].w};
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            gt = mfma32(ya[e], aa[e], gt);
-#pragma unroll
-                            for (int u = e * GPM / 4; u < (e + 1) * GPM / 4; ++u) {
-                                const int t = m * GPM + u;
-                                const float4 x = xk[t >> 2];
-                                const float xs[4] = {x.x, x.y, x.z, x.w};
-                                gv = mfma32(xs[t & 3], bv[m & 1][u], gv);
-                            }
-                        }
-                        __builtin_amdgcn_sched_barrier(0);
-                    }
-                } else {
-#pragma unroll
-                    for (int m = 0; m < NA; ++m) {
-                        if (m + 1 < NA) yb[(m + 1) & 1] = *reinterpret_cast<const float4 *>(bp + 8 * (m + 1));
-                        const float4 y = yb[m & 1];
-                        gt = mfma32(y.x, ar[m].x, gt);
-                        gt = mfma32(y.y, ar[m].y, gt);
-                        gt = mfma32(y.z, ar[m].z, gt);
-                        gt = mfma32(y.w, ar[m].w, gt);
-                        __builtin_amdgcn_sched_barrier(0);
-                    }
+                for (int m = 0; m < NA; ++m) {
+                    if (m + 1 < NA) yb[(m + 1) & 1] = *reinterpret_cast<const float4 *>(bp + 8 * (m + 1));
+                    const float4 y = yb[m & 1];
+                    gt = mfma32(y.x, ar[m].x, gt);
+                    gt = mfma32(y.y, ar[m].y, gt);
+                    gt = mfma32(y.z, ar[m].z, gt);
+                    gt = mfma32(y.w, ar[m].w, gt);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-                fold(gt, ks);
             }
+            // Gv: MFMA group g2 contracts slab rows (16 (g2 / 2) + 4 (g2 % 2) + e, + 8)
+            if (gvw) {
+                const float *kp = KL + (32 * rt + cl) * LDK + 32 * ks + 8 * kh;
+                const float *bd = sD + 8 * kh * LSL + 32 * grp * NCW + cl;
+                float4 xk[2];
+                float bv[2][NCW][4];
+                auto ldv = [&](int g2, int buf) {
+                    const int o = 16 * (g2 >> 1) + 4 * (g2 & 1);
+                    xk[buf] = *reinterpret_cast<const float4 *>(kp + o);
+#pragma unroll
+                    for (int u = 0; u < NCW; ++u) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) bv[buf][u][e] = bd[(o + e) * LSL + 32 * u];
+                    }
+                };
+                ldv(0, 0);
+#pragma unroll
+                for (int g2 = 0; g2 < 4; ++g2) {
+                    if (g2 + 1 < 4) ldv(g2 + 1, (g2 + 1) & 1);
+                    const float4 x = xk[g2 & 1];
+                    const float xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+#pragma unroll
+                        for (int u = 0; u < NCW; ++u) gv[u] = mfma32(xs[e], bv[g2 & 1][u][e], gv[u]);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            fold(gt, ks);
         }
         // the two lane halves hold the dot products over different state rows
         rd += __shfl_xor(rd, 32);
-        if (kh == 0) (grp ? redk[half] : redq[half])[32 * rt + cl] = rd;
+        if (kh == 0) (grp ? redk : redq)[32 * rt + cl] = rd;
         fro = sum64_hi(fro);
         if (lane == 63) redf[wave] = fro;
         __syncthreads();   // slabs read
         {
-            float *dst = X + (grp ? CH * LDY : 0) + (32 * rt + cl) * LDY + half * NH + 4 * kh;
+            float *dst = X + (grp ? CH * LDY : 0) + (32 * rt + cl) * LDY + 4 * kh;
 #pragma unroll
             for (int m = 0; m < NA; ++m) *reinterpret_cast<float4 *>(dst + 8 * m) = ar[m];
         }
@@ -1207,142 +1184,158 @@ __global__ __launch_bounds__(NTW) void k_bwd_grads(
 
         // ---- pass 2
         const float *RY = X, *RV = X + CH * LDY;
+        // dV tiles (rows 32 rt + row(r), columns 32 (grp NCW + u) + i) =
+        // diag(e^{b_L - b}) Gv + P^T dY.  P is formed per row block of positions,
+        // then the MFMAs run.
         if (gvw) {
-            // dV tile (rows 32 jv + row(r), columns 32 cv + i) = diag(e^{b_L - b}) Gv + P^T dY.
-            // Per row block of P the operands are read and P formed first, then 16
-            // MFMAs run on two chains.
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
-                const float4 e4 = *reinterpret_cast<const float4 *>(el + 32 * jv + 8 * a + 4 * kh);
-                gv[4 * a] *= e4.x;
-                gv[4 * a + 1] *= e4.y;
-                gv[4 * a + 2] *= e4.z;
-                gv[4 * a + 3] *= e4.w;
+                const float4 e4 = *reinterpret_cast<const float4 *>(el + 32 * rt + 8 * a + 4 * kh);
+#pragma unroll
+                for (int u = 0; u < NCW; ++u) {
+                    gv[u][4 * a] *= e4.x;
+                    gv[u][4 * a + 1] *= e4.y;
+                    gv[u][4 * a + 2] *= e4.z;
+                    gv[u][4 * a + 3] *= e4.w;
+                }
             }
-            f32x16 gv2 = zero16();
-            const int j = 32 * jv + cl;
+            const int j = 32 * rt + cl;
             const float bj = bs[j];
 #pragma unroll
             for (int it = 0; it < 2; ++it) {
-                if (it >= jv) {
-                    float p[16], yv[16];
+                if (it >= rt) {
+                    float p[16];
 #pragma unroll
                     for (int a = 0; a < 4; ++a) {
-                        const float4 k4 = *reinterpret_cast<const float4 *>(QKT + (it + jv) * 1024 + (a * 64 + lane) * 4);
+                        const float4 k4 = qkt4(it + rt, a, lane);
                         const float4 b4 = *reinterpret_cast<const float4 *>(bs + 32 * it + 8 * a + 4 * kh);
                         const float ks4[4] = {k4.x, k4.y, k4.z, k4.w}, bis[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const int i = 32 * it + 8 * a + 4 * kh + e;
-                            yv[4 * a + e] = RY[i * LDY + 32 * cv + cl];
                             p[4 * a + e] = ks4[e] * __expf(j <= i ? bis[e] - bj : -INFINITY);
                         }
                     }
-                    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                    for (int r = 0; r < 16; r += 2) {
-                        gv = mfma32(p[r], yv[r], gv);
-                        gv2 = mfma32(p[r + 1], yv[r + 1], gv2);
+                    for (int r = 0; r < 16; ++r) {
+                        const int i = 32 * it + acc_row(r, lane);
+#pragma unroll
+                        for (int u = 0; u < NCW; ++u)
+                            gv[u] = mfma32(p[r], RY[i * LDY + 32 * (grp * NCW + u) + cl], gv[u]);
                     }
+                }
+            }
+            const rsrc_t dvb = make_rsrc(dv + (bh * T + c * CH) * dv_, (int64_t)rows * dv_ * 4);
+#pragma unroll
+            for (int u = 0; u < NCW; ++u) {
+                const int n = 32 * (grp * NCW + u) + cl;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int t = 32 * rt + acc_row(r, lane);   // rows past the sequence end fall outside dvb
+                    gstore1(dvb, n < dv_ ? (uint32_t)(t * dv_ + n) * 4u : kOOB, gv[u][r]);
+                }
+            }
+        }
+        // dY V^T tiles: tile 0 (rows 0-31 x cols 0-31) on wave 0, tile 1 (32-63 x 0-31)
+        // split over dv halves between waves 1 and 3, tile 2 (32-63 x 32-63) on wave 3.
+        // The next head's A rows are loaded one per MFMA group.
+        f32x16 ad = zero16(), ad2 = zero16();
+        auto dyvt = [&](f32x16 &acc, int it, int jt, int m0, int m1, bool lda) {
+#pragma unroll
+            for (int m = 0; m < NA; ++m) {
+                if (m >= m0 && m < m1) {
+                    const float4 x = *reinterpret_cast<const float4 *>(RY + (32 * it + cl) * LDY + 8 * m + 4 * kh);
+                    const float4 y = *reinterpret_cast<const float4 *>(RV + (32 * jt + cl) * LDY + 8 * m + 4 * kh);
+                    acc = mfma32(x.x, y.x, acc);
+                    acc = mfma32(x.y, y.y, acc);
+                    acc = mfma32(x.z, y.z, acc);
+                    acc = mfma32(x.w, y.w, acc);
+                    if (lda) load_a1(hh + 1, tid, m);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
-            gv += gv2;
-            const rsrc_t dvb = make_rsrc(dv + (bh * T + c * CH) * dv_, (int64_t)rows * dv_ * 4);
-            const int n = 32 * cv + cl;
+        };
+        if (wave == 0) {
+            dyvt(ad, 0, 0, 0, NA, true);
+        } else if (wave == 1) {
+            dyvt(ad, 1, 0, 0, NA / 2, true);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int t = 32 * jv + acc_row(r, lane);   // rows past the sequence end fall outside dvb
-                gstore1(dvb, n < dv_ ? (uint32_t)(t * dv_ + n) * 4u : kOOB, gv[r]);
-            }
-        }
-        // dY V^T: each wave of a pair over one half of dv.  The next head's A rows
-        // are loaded one per MFMA group, so the loads do not all queue at once.
-        f32x16 ad = zero16();
-        if (td >= 0) {
-            const int it = td > 0, jt = td == 2, hd = red ? 0 : 1;
-            const float *ya = RY + (32 * it + cl) * LDY + hd * NH + 4 * kh;
-            const float *vb = RV + (32 * jt + cl) * LDY + hd * NH + 4 * kh;
-#pragma unroll
-            for (int m = 0; m < NA; ++m) {
-                const float4 x = *reinterpret_cast<const float4 *>(ya + 8 * m);
-                const float4 y = *reinterpret_cast<const float4 *>(vb + 8 * m);
-                ad = mfma32(x.x, y.x, ad);
-                ad = mfma32(x.y, y.y, ad);
-                ad = mfma32(x.z, y.z, ad);
-                ad = mfma32(x.w, y.w, ad);
-                load_a1(hh + 1, tid, m);
-                __builtin_amdgcn_sched_barrier(0);
-            }
+            for (int m = NA / 2; m < NA; ++m) load_a1(hh + 1, tid, m);
+        } else if (wave == 3) {
+            dyvt(ad2, 1, 0, NA / 2, NA, false);
+            dyvt(ad, 1, 1, 0, NA, true);
         } else {
 #pragma unroll
             for (int m = 0; m < NA; ++m) load_a1(hh + 1, tid, m);
         }
         load_b(hh + 1, tid);
         __syncthreads();   // dY and V read
-        // both waves of a pair publish their half of the tile
-        if (td >= 0) {
-            float *xo = X + (2 * td + (red ? 0 : 1)) * 1024;
+        if (wave == 3) {
 #pragma unroll
             for (int a = 0; a < 4; ++a)
-                *reinterpret_cast<float4 *>(xo + (a * 64 + lane) * 4) =
-                    make_float4(ad[4 * a], ad[4 * a + 1], ad[4 * a + 2], ad[4 * a + 3]);
+                *reinterpret_cast<float4 *>(X + (a * 64 + lane) * 4) =
+                    make_float4(ad2[4 * a], ad2[4 * a + 1], ad2[4 * a + 2], ad2[4 * a + 3]);
         }
-        __syncthreads();   // the halves of dY V^T visible
-        float *const DP = X + 6 * 1024;   // dP [CH][LDP]
+        __syncthreads();   // wave 3's half of tile 1 visible
+        float *const DP = X + 1024;   // dP [CH][LDP]
 
-        if (td >= 0) {
+        if (wave != 2) {
             // dP = (dY V^T) o D to LDS, and the row and column sums of the strictly
-            // lower part of M = (Q K^T) o D o (dY V^T); the reducer takes registers
-            // 0-7 of the tile, its partner 8-15
-            const int it = td > 0, jt = td == 2, hw = red ? 0 : 1;
-            const float *xp = X + (2 * td + (red ? 1 : 0)) * 1024;
+            // lower part of M = (Q K^T) o D o (dY V^T)
+            const int td = wave == 0 ? 0 : wave == 1 ? 1 : 2;
+            const int it = td > 0, jt = td == 2;
+            if (wave == 1) {
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    const float4 x = *reinterpret_cast<const float4 *>(X + (a * 64 + lane) * 4);
+                    ad[4 * a] += x.x;
+                    ad[4 * a + 1] += x.y;
+                    ad[4 * a + 2] += x.z;
+                    ad[4 * a + 3] += x.w;
+                }
+            }
             const int j = 32 * jt + cl;
             const float bj = bs[j];
-            float ms[8], csum = 0.f;
+            float ms[16], csum = 0.f;
 #pragma unroll
-            for (int a2 = 0; a2 < 2; ++a2) {
-                const int a = 2 * hw + a2;
-                const float4 x = *reinterpret_cast<const float4 *>(xp + (a * 64 + lane) * 4);
-                const float4 k4 = *reinterpret_cast<const float4 *>(QKT + td * 1024 + (a * 64 + lane) * 4);
+            for (int a = 0; a < 4; ++a) {
+                const float4 k4 = qkt4(td, a, lane);
                 const float4 b4 = *reinterpret_cast<const float4 *>(bs + 32 * it + 8 * a + 4 * kh);
-                const float xs[4] = {x.x, x.y, x.z, x.w}, ks4[4] = {k4.x, k4.y, k4.z, k4.w};
-                const float bis[4] = {b4.x, b4.y, b4.z, b4.w};
+                const float ks4[4] = {k4.x, k4.y, k4.z, k4.w}, bis[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int i = 32 * it + 8 * a + 4 * kh + e;
-                    const float own = hw == 0 ? ad[4 * a2 + e] : ad[8 + 4 * a2 + e];
+                    const int r = 4 * a + e, i = 32 * it + 8 * a + 4 * kh + e;
                     const float d = __expf(j <= i ? bis[e] - bj : -INFINITY);
-                    const float dp = (own + xs[e]) * d;
+                    const float dp = ad[r] * d;
                     DP[i * LDP + j] = dp;
-                    ms[4 * a2 + e] = (j < i) ? ks4[e] * dp : 0.f;   // (Q K^T) o D o (dY V^T)
-                    csum += ms[4 * a2 + e];
+                    ms[r] = (j < i) ? ks4[e] * dp : 0.f;   // (Q K^T) o D o (dY V^T)
+                    csum += ms[r];
                 }
             }
 #pragma unroll
-            for (int r = 0; r < 8; ++r) ms[r] = dpp_add<kRowRor + 8>(ms[r]);
+            for (int r = 0; r < 16; ++r) ms[r] = dpp_add<kRowRor + 8>(ms[r]);
 #pragma unroll
-            for (int r = 0; r < 8; ++r) ms[r] = dpp_add<kRowRor + 4>(ms[r]);
+            for (int r = 0; r < 16; ++r) ms[r] = dpp_add<kRowRor + 4>(ms[r]);
 #pragma unroll
-            for (int r = 0; r < 8; ++r) ms[r] = dpp_add<kRowRor + 2>(ms[r]);
+            for (int r = 0; r < 16; ++r) ms[r] = dpp_add<kRowRor + 2>(ms[r]);
 #pragma unroll
-            for (int r = 0; r < 8; ++r) ms[r] = dpp_add<kRowRor + 1>(ms[r]);
+            for (int r = 0; r < 16; ++r) ms[r] = dpp_add<kRowRor + 1>(ms[r]);
 #pragma unroll
-            for (int r = 0; r < 8; ++r) ms[r] = dpp_add<kRowBcast15, 0xa>(ms[r]);
+            for (int r = 0; r < 16; ++r) ms[r] = dpp_add<kRowBcast15, 0xa>(ms[r]);
             if (cl == 31) {
 #pragma unroll
-                for (int r = 0; r < 8; ++r) rsm[td][acc_row(8 * hw + r, lane)] = ms[r];
+                for (int r = 0; r < 16; ++r) rsm[td][acc_row(r, lane)] = ms[r];
             }
             csum += __shfl_xor(csum, 32);
-            if (kh == 0) csm[td][hw][cl] = csum;
+            if (kh == 0) csm[td][cl] = csum;
         }
         __syncthreads();   // dP and the reductions visible
         // the next head's first slabs, in flight over the intra products
         load_slab(p0, hh + 1, 0, tid);
 
         if (grp == 0) {
-            // dQ[rt, ct] += dP[rt, :] K[:, ct] over j < 32 (rt + 1); this wave takes ct = half (mod 2)
-            // the wave's tiles (ct = half, half + 2) run interleaved on independent chains
+            // dQ^T[ct, rt] += K[:, ct]^T dP[rt, :]^T over j < 32 (rt + 1); all tiles
+            // interleaved on independent chains
             const float *ap = DP + (32 * rt + cl) * LDP + 4 * kh;
             const float *bk = KL + 4 * kh * LDK + cl;
 #pragma unroll
@@ -1351,20 +1344,18 @@ __global__ __launch_bounds__(NTW) void k_bwd_grads(
                     const float4 x = *reinterpret_cast<const float4 *>(ap + 8 * a);
 #pragma unroll
                     for (int ct = 0; ct < NKS; ++ct) {
-                        if ((ct & 1) == half) {
-                            dacc[ct] = mfma32(bk[(8 * a + 0) * LDK + 32 * ct], x.x, dacc[ct]);
-                            dacc[ct] = mfma32(bk[(8 * a + 1) * LDK + 32 * ct], x.y, dacc[ct]);
-                            dacc[ct] = mfma32(bk[(8 * a + 2) * LDK + 32 * ct], x.z, dacc[ct]);
-                            dacc[ct] = mfma32(bk[(8 * a + 3) * LDK + 32 * ct], x.w, dacc[ct]);
-                        }
+                        dacc[ct] = mfma32(bk[(8 * a + 0) * LDK + 32 * ct], x.x, dacc[ct]);
+                        dacc[ct] = mfma32(bk[(8 * a + 1) * LDK + 32 * ct], x.y, dacc[ct]);
+                        dacc[ct] = mfma32(bk[(8 * a + 2) * LDK + 32 * ct], x.z, dacc[ct]);
+                        dacc[ct] = mfma32(bk[(8 * a + 3) * LDK + 32 * ct], x.w, dacc[ct]);
                     }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
                 if (a == 1 && NKS > 1) load_slab(pn, hh + 1, 1, tid);
             }
         } else {
-            // dK[rt, ct] += dP[:, rt]^T Q[:, ct] over i >= 32 rt; MFMA s = 8 g2 + e
+            // dK^T[ct, rt] += Q[:, ct]^T dP[:, rt] over i >= 32 rt; MFMA s = 8 g2 + e
             // contracts rows (i0 + 16 g2 + e, + 8)
-            // the wave's tiles (ct = half, half + 2) run interleaved on independent chains
             const float *ap = DP + 8 * kh * LDP + 32 * rt + cl;
             const float *bq = QL + 8 * kh * LDQ + cl;
 #pragma unroll
@@ -1377,28 +1368,25 @@ __global__ __launch_bounds__(NTW) void k_bwd_grads(
                             const int i = 32 * it + 16 * g2 + e;
                             const float x = ap[i * LDP];
 #pragma unroll
-                            for (int ct = 0; ct < NKS; ++ct) {
-                                if ((ct & 1) == half) dacc[ct] = mfma32(bq[i * LDQ + 32 * ct], x, dacc[ct]);
-                            }
+                            for (int ct = 0; ct < NKS; ++ct) dacc[ct] = mfma32(bq[i * LDQ + 32 * ct], x, dacc[ct]);
                         }
+                        __builtin_amdgcn_sched_barrier(0);
                         if (it == 1 && g2 == 0 && NKS > 1) load_slab(pn, hh + 1, 1, tid);
                     }
                 }
             }
         }
-        if (wave == 7) {
+        if (wave == 2) {
             // dlog_alpha_r = R_r + sum_{i >= r} iq_i + sum_{j < r} ik_j + e^{b_L} <dS_out, S_in>
             const int t = lane;
-            const float ik = redk[0][t] + redk[1][t];
+            const float ik = redk[t];
             const float rw = t < 32 ? rsm[0][t] : rsm[1][t - 32] + rsm[2][t - 32];
-            const float cs = t < 32 ? csm[0][0][t] + csm[0][1][t] + csm[1][0][t] + csm[1][1][t]
-                                    : csm[2][0][t - 32] + csm[2][1][t - 32];
+            const float cs = t < 32 ? csm[0][t] + csm[1][t] : csm[2][t - 32];
             float frob = 0.f;
 #pragma unroll
-            for (int w = 0; w < NTW / 64; ++w) frob += redf[w];
+            for (int w = 0; w < NTB / 64; ++w) frob += redf[w];
             // suffix sum of iq: prefix sum over the reversed rows
-            const float iqr = redq[0][63 - t] + redq[1][63 - t];
-            sfx[63 - t] = scan64(iqr);
+            sfx[63 - t] = scan64(redq[63 - t]);
             const float rr = shift_up1(scan64(cs - rw)), pk = shift_up1(scan64(ik));
             // lanes exchange through sfx: order the write before the read
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -1416,51 +1404,23 @@ __global__ __launch_bounds__(NTW) void k_bwd_grads(
         __syncthreads();
     }
 
-    // ---- dq, dk: the two dv halves of each tile summed, transposed through
-    // LDS into [position][dk] rows, stored with 16-byte writes
+    // ---- dq, dk: transposed through LDS into [position][dk] rows, stored with
+    // 16-byte writes
     {
         const int tid = threadIdx.x, lane = tid & 63, cl = lane & 31, kh = lane >> 5;
-        float *xs = X + ((grp * 2 + rt) * NKS) * 1024;
-        if (half == 1) {
+        float *o = X + grp * CH * LDQ + (32 * rt + cl) * LDQ + 4 * kh;
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
+        for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
-                for (int a = 0; a < 4; ++a)
-                    *reinterpret_cast<float4 *>(xs + ks * 1024 + (a * 64 + lane) * 4) =
-                        make_float4(dacc[ks][4 * a], dacc[ks][4 * a + 1], dacc[ks][4 * a + 2], dacc[ks][4 * a + 3]);
-            }
-        }
-        __syncthreads();
-        if (half == 0) {
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-#pragma unroll
-                for (int a = 0; a < 4; ++a) {
-                    const float4 x = *reinterpret_cast<const float4 *>(xs + ks * 1024 + (a * 64 + lane) * 4);
-                    dacc[ks][4 * a] += x.x;
-                    dacc[ks][4 * a + 1] += x.y;
-                    dacc[ks][4 * a + 2] += x.z;
-                    dacc[ks][4 * a + 3] += x.w;
-                }
-            }
-        }
-        __syncthreads();
-        // OUT[grp][position][k], row stride LDQ
-        if (half == 0) {
-            float *o = X + grp * CH * LDQ + (32 * rt + cl) * LDQ + 4 * kh;
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-#pragma unroll
-                for (int a = 0; a < 4; ++a)
-                    *reinterpret_cast<float4 *>(o + 32 * ks + 8 * a) =
-                        make_float4(dacc[ks][4 * a], dacc[ks][4 * a + 1], dacc[ks][4 * a + 2], dacc[ks][4 * a + 3]);
-            }
+            for (int a = 0; a < 4; ++a)
+                *reinterpret_cast<float4 *>(o + 32 * ks + 8 * a) =
+                    make_float4(dacc[ks][4 * a], dacc[ks][4 * a + 1], dacc[ks][4 * a + 2], dacc[ks][4 * a + 3]);
         }
         __syncthreads();
         const int64_t tb = (int64_t)rows * dk_ * 4;
         const rsrc_t rq = make_rsrc(dq + (bg * T + c * CH) * dk_, tb), rk = make_rsrc(dk + (bg * T + c * CH) * dk_, tb);
         constexpr int Q4 = DKP / 4;
-        for (int idx = tid; idx < 2 * CH * Q4; idx += NTW) {
+        for (int idx = tid; idx < 2 * CH * Q4; idx += NTB) {
             const int gg = idx / (CH * Q4), rem = idx - gg * CH * Q4;
             const int row = rem / Q4, c4 = (rem - row * Q4) * 4;
             const float4 x = *reinterpret_cast<const float4 *>(X + gg * CH * LDQ + row * LDQ + c4);
@@ -1719,7 +1679,7 @@ int ssd_bwd(const ssd_shape *shape, const float *q, const float *k, const float 
     {
         TimedLaunch tl(KID_GRADS, st);
         SSD_DISPATCH(P,
-                          (k_bwd_grads<KP, VP, VE><<<dim3((unsigned)(s.B * s.G * P.L.NC)), dim3(NTW), 0, st>>>(
+                          (k_bwd_grads<KP, VP, VE><<<dim3((unsigned)(s.B * s.G * P.L.NC)), dim3(NTB), 0, st>>>(
                               q, k, v, dy, P.bcum, P.bl, P.states, P.dstates, dq, dk, dv, dlog_alpha, (int)s.G,
                               (int)s.H, s.T, (int)s.dk, (int)s.dv, P.L.NC, P.L.NCp, P.L.Epad)));
     }

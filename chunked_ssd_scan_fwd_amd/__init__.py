@@ -186,12 +186,23 @@ class kernel_timing:
     """Context manager: per-kernel HIP-event timing of ssd_fwd/ssd_bwd launches.
 
     ``with kernel_timing() as kt: ...`` then ``kt.results`` maps kernel name
-    to (total_ms, launches)."""
+    to (total_ms, launches).  ``kernels`` names the kernels to time (default:
+    all); each timed dispatch costs a few microseconds of stream time."""
+
+    def __init__(self, kernels=None):
+        self.kernels = kernels
 
     def __enter__(self):
         lib = library()
+        mask = -1
+        if self.kernels is not None:
+            names = [lib.ssd_kernel_name(i).decode() for i in range(lib.ssd_kernel_count())]
+            unknown = set(self.kernels) - set(names)
+            if unknown:
+                raise ValueError(f"unknown kernels {sorted(unknown)}; known: {names}")
+            mask = sum(1 << names.index(n) for n in self.kernels)
         lib.ssd_kernel_timing_reset()
-        lib.ssd_kernel_timing_enable(1)
+        lib.ssd_kernel_timing_enable(mask)
         self.results = {}
         return self
 

@@ -37,8 +37,10 @@
 // 32x2 by 2x32 product, and accumulator register r of lane l holds row
 // 8*(r/4) + 4*(l/32) + r%4, column l%32 of the 32x32 result.
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <stdint.h>
+#include <tuple>
 #include <vector>
 
 #include "ssd.h"
@@ -1454,7 +1456,7 @@ static const char *kKernelNames[KID_COUNT] = {"chunk_cumsum", "state_scan", "chu
                                               "bwd_grads"};
 
 struct Timing {
-    bool on = false;
+    unsigned mask = 0;   // bit kid: time kernel kid
     std::vector<hipEvent_t> pool;
     std::vector<hipEvent_t> pending[KID_COUNT][2];
     double total[KID_COUNT] = {};
@@ -1474,27 +1476,35 @@ static hipEvent_t get_event()
     return e;
 }
 
-struct TimedLaunch {
-    int kid;
-    hipStream_t st;
-    hipEvent_t a = nullptr, b = nullptr;
-    TimedLaunch(int kid_, hipStream_t st_) : kid(kid_), st(st_)
-    {
-        if (g_timing.on) {
-            a = get_event();
-            b = get_event();
-            if (a && b) hipEventRecord(a, st);
+// Launches f on st.  When kernel kid is timed, the start and stop events are
+// bound to the kernel's own dispatch through hipExtLaunchKernel, so they time
+// the kernel alone and put no extra packets between kernels on the stream.
+template <typename... P, typename... A>
+static void launch(int kid, void (*f)(P...), dim3 grid, dim3 blk, hipStream_t st, A... a)
+{
+    static_assert(sizeof...(P) == sizeof...(A), "argument count");
+    std::tuple<P...> args{static_cast<P>(a)...};
+    void *ptrs[sizeof...(P)];
+    std::apply([&](auto &...x) {
+        int i = 0;
+        ((ptrs[i++] = static_cast<void *>(&x)), ...);
+    }, args);
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (kid >= 0 && ((g_timing.mask >> kid) & 1u)) {
+        e0 = get_event();
+        e1 = get_event();
+        if (!e0 || !e1) {
+            if (e0) g_timing.pool.push_back(e0);
+            if (e1) g_timing.pool.push_back(e1);
+            e0 = e1 = nullptr;
         }
     }
-    ~TimedLaunch()
-    {
-        if (a && b) {
-            hipEventRecord(b, st);
-            g_timing.pending[kid][0].push_back(a);
-            g_timing.pending[kid][1].push_back(b);
-        }
+    hipExtLaunchKernel(reinterpret_cast<const void *>(f), grid, blk, ptrs, 0, st, e0, e1, 0);
+    if (e0 && e1) {
+        g_timing.pending[kid][0].push_back(e0);
+        g_timing.pending[kid][1].push_back(e1);
     }
-};
+}
 
 static void collect_timing()
 {
@@ -1560,14 +1570,13 @@ static int run_scan(const Problem &P, int ndir, const float *q, const float *k, 
     const ssd_shape &s = P.s;
     const int64_t BH = s.B * s.H;
     {
-        TimedLaunch tl(KID_CUMSUM, st);
         const int64_t nw = BH * P.L.NC;
         const int64_t grid = (nw + 3) / 4;
-        k_chunk_cumsum<<<dim3((unsigned)grid), dim3(NTH), 0, st>>>(la, P.bcum, P.bl, s.T, P.L.NC, P.L.NCp, nw);
+        launch(KID_CUMSUM, k_chunk_cumsum, dim3((unsigned)grid), dim3(NTH), st, la, P.bcum, P.bl, s.T, P.L.NC,
+               P.L.NCp, nw);
     }
     if (launch_status() != SSD_OK) return SSD_ERR_DEVICE;
     {
-        TimedLaunch tl(ndir == 1 ? KID_SCAN : KID_SCAN2, st);
         // Two chunks per step when there is at most one block per CU (the
         // paired tiles fill most of a CU's LDS); otherwise one.  State tiles
         // are 32 x 64 (32 x dv for dv < 64): wider tiles re-read fewer operand
@@ -1575,18 +1584,19 @@ static int run_scan(const Problem &P, int ndir, const float *q, const float *k, 
         // which measured slower.
         const int64_t tiles_k = BH * (P.DKP / TI);
         const bool pair = ndir * tiles_k * (P.DVP / (P.DVP < 64 ? P.DVP : 64)) <= kNumCUs;
+        const int kid = ndir == 1 ? KID_SCAN : KID_SCAN2;
         SSD_DISPATCH(P, ({
             constexpr int TJ = VP < 64 ? VP : 64;
             const int64_t per_dir = tiles_k * (VP / TJ);
             const dim3 grid((unsigned)(ndir * per_dir)), blk(NTS);
             if (pair)
-                k_state_scan<KP, VP, VE, TJ, 2><<<grid, blk, 0, st>>>(
-                    q, k, v, dy, h0, P.bcum, P.bl, P.states, P.dstates, dh0, (int)s.G, (int)s.H, s.T, (int)s.dk,
-                    (int)s.dv, P.L.NC, P.L.NCp, P.L.Epad, per_dir);
+                launch(kid, k_state_scan<KP, VP, VE, TJ, 2>, grid, blk, st, q, k, v, dy, h0, P.bcum, P.bl,
+                       P.states, P.dstates, dh0, (int)s.G, (int)s.H, s.T, (int)s.dk, (int)s.dv, P.L.NC, P.L.NCp,
+                       P.L.Epad, per_dir);
             else
-                k_state_scan<KP, VP, VE, TJ, 1><<<grid, blk, 0, st>>>(
-                    q, k, v, dy, h0, P.bcum, P.bl, P.states, P.dstates, dh0, (int)s.G, (int)s.H, s.T, (int)s.dk,
-                    (int)s.dv, P.L.NC, P.L.NCp, P.L.Epad, per_dir);
+                launch(kid, k_state_scan<KP, VP, VE, TJ, 1>, grid, blk, st, q, k, v, dy, h0, P.bcum, P.bl,
+                       P.states, P.dstates, dh0, (int)s.G, (int)s.H, s.T, (int)s.dk, (int)s.dv, P.L.NC, P.L.NCp,
+                       P.L.Epad, per_dir);
         }));
     }
     return launch_status();
@@ -1637,13 +1647,9 @@ int ssd_fwd(const ssd_shape *shape, const float *q, const float *k, const float 
 
     rc = run_scan(P, 1, q, k, v, nullptr, log_alpha, h0, nullptr, st);
     if (rc != SSD_OK) return rc;
-    {
-        TimedLaunch tl(KID_OUTPUT, st);
-        SSD_DISPATCH(P,
-                          (k_chunk_output<KP, VP, VE><<<dim3((unsigned)(s.B * s.G * P.L.NC)), dim3(NTW), 0, st>>>(
-                              q, k, v, P.bcum, P.states, y, (int)s.G, (int)s.H, s.T, (int)s.dk, (int)s.dv, P.L.NC,
-                              P.L.Epad)));
-    }
+    SSD_DISPATCH(P, launch(KID_OUTPUT, k_chunk_output<KP, VP, VE>, dim3((unsigned)(s.B * s.G * P.L.NC)),
+                           dim3(NTW), st, q, k, v, P.bcum, P.states, y, (int)s.G, (int)s.H, s.T, (int)s.dk,
+                           (int)s.dv, P.L.NC, P.L.Epad));
     return launch_status();
 }
 
@@ -1661,7 +1667,7 @@ int ssd_bwd(const ssd_shape *shape, const float *q, const float *k, const float 
         if (!dh0) return SSD_ERR_NULL;
         if (!aligned16(dh0)) return SSD_ERR_ALIGN;
         const int64_t n = s.B * s.H * s.dk * s.dv;
-        k_zero<<<dim3((unsigned)((n + NTH - 1) / NTH)), dim3(NTH), 0, st>>>(dh0, n);
+        launch(-1, k_zero, dim3((unsigned)((n + NTH - 1) / NTH)), dim3(NTH), st, dh0, n);
         return launch_status();
     }
     if (!q || !k || !v || !log_alpha || !h0 || !dy || !dq || !dk || !dv || !dlog_alpha || !dh0)
@@ -1676,19 +1682,15 @@ int ssd_bwd(const ssd_shape *shape, const float *q, const float *k, const float 
     // S_in (forward) and dS_out (reverse) of every chunk, and dh0.
     rc = run_scan(P, 2, q, k, v, dy, log_alpha, h0, dh0, st);
     if (rc != SSD_OK) return rc;
-    {
-        TimedLaunch tl(KID_GRADS, st);
-        SSD_DISPATCH(P,
-                          (k_bwd_grads<KP, VP, VE><<<dim3((unsigned)(s.B * s.G * P.L.NC)), dim3(NTB), 0, st>>>(
-                              q, k, v, dy, P.bcum, P.bl, P.states, P.dstates, dq, dk, dv, dlog_alpha, (int)s.G,
-                              (int)s.H, s.T, (int)s.dk, (int)s.dv, P.L.NC, P.L.NCp, P.L.Epad)));
-    }
+    SSD_DISPATCH(P, launch(KID_GRADS, k_bwd_grads<KP, VP, VE>, dim3((unsigned)(s.B * s.G * P.L.NC)), dim3(NTB),
+                           st, q, k, v, dy, P.bcum, P.bl, P.states, P.dstates, dq, dk, dv, dlog_alpha, (int)s.G,
+                           (int)s.H, s.T, (int)s.dk, (int)s.dv, P.L.NC, P.L.NCp, P.L.Epad));
     return launch_status();
 }
 
-int ssd_kernel_timing_enable(int enable)
+int ssd_kernel_timing_enable(int mask)
 {
-    g_timing.on = enable != 0;
+    g_timing.mask = static_cast<unsigned>(mask);
     return SSD_OK;
 }
 

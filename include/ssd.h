@@ -128,13 +128,18 @@ const char *ssd_strerror(int status);
 /* Chunk length used by the kernels (SSD_CHUNK). */
 int ssd_chunk_size(void);
 
-/* Optional per-kernel timing with HIP events, for benchmarks.  When enabled,
- * every kernel launch of ssd_fwd/ssd_bwd is bracketed by two events recorded
- * on the launch stream.  ssd_kernel_timing_read synchronizes on the recorded
- * events and returns, for kernel id `kid` (0 <= kid < ssd_kernel_count()),
- * the summed duration in milliseconds and the number of launches since the
- * last reset.  Process-global, not thread-safe, off by default. */
-int ssd_kernel_timing_enable(int enable);
+/* Optional per-kernel timing with HIP events, for benchmarks.
+ * ssd_kernel_timing_enable(mask) times the launches of the kernels whose bit
+ * (1 << kid) is set in `mask` (-1: all kernels; 0: off, the default): their
+ * start and stop events are bound to the kernel's own dispatch on the launch
+ * stream (hipExtLaunchKernel), so they cover the kernel alone.  A timed
+ * dispatch still costs a few microseconds of stream time, so a benchmark
+ * that also times whole calls should time only the kernels it needs.
+ * ssd_kernel_timing_read synchronizes on the recorded events and returns,
+ * for kernel id `kid` (0 <= kid < ssd_kernel_count()), the summed duration
+ * in milliseconds and the number of timed launches since the last reset.
+ * Process-global, not thread-safe. */
+int ssd_kernel_timing_enable(int mask);
 int ssd_kernel_timing_reset(void);
 int ssd_kernel_timing_read(int kid, double *total_ms, int64_t *count);
 int ssd_kernel_count(void);

@@ -1077,6 +1077,10 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
     f32x16 dacc[NKS];   // dQ^T (dQ side) or dK^T (dK side): state rows 32 ks + row(r), positions 32 rt + i
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) dacc[ks] = zero16();
+    // wave 0: dQ^T rows 32 (NKS - 1) .., positions 32 ..; wave 3: dK^T rows
+    // 32 (NKS - 1) .., positions 0 .. (intra parts taken over from waves 1, 2)
+    constexpr bool OFF = NKS > 1;
+    f32x16 xacc = zero16();
 
     for (int hh = 0; hh < hpg; ++hh) {
         int tid = threadIdx.x;
@@ -1238,11 +1242,12 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
                 }
             }
         }
-        // dY V^T tiles: tile 0 (rows 0-31 x cols 0-31) on wave 0, tile 1 (32-63 x 0-31)
-        // split over dv halves between waves 1 and 3, tile 2 (32-63 x 32-63) on wave 3.
-        // The next head's A rows are loaded one per MFMA group.
-        f32x16 ad = zero16(), ad2 = zero16();
-        auto dyvt = [&](f32x16 &acc, int it, int jt, int m0, int m1, bool lda) {
+        // dY V^T tiles: tile 0 (rows 0-31 x cols 0-31) split over dv halves between
+        // waves 0 and 2, tile 1 (32-63 x 0-31) on wave 1, tile 2 (32-63 x 32-63) on
+        // wave 3, so that with the dV tiles every wave runs the same number of
+        // MFMAs.  The next head's A rows are loaded LPG per MFMA group.
+        f32x16 ad = zero16();
+        auto dyvt = [&](f32x16 &acc, int it, int jt, int m0, int m1, int LPG) {
 #pragma unroll
             for (int m = 0; m < NA; ++m) {
                 if (m >= m0 && m < m1) {
@@ -1252,33 +1257,30 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
                     acc = mfma32(x.y, y.y, acc);
                     acc = mfma32(x.z, y.z, acc);
                     acc = mfma32(x.w, y.w, acc);
-                    if (lda) load_a1(hh + 1, tid, m);
+#pragma unroll
+                    for (int l = 0; l < LPG; ++l) load_a1(hh + 1, tid, (m - m0) * LPG + l);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
         };
         if (wave == 0) {
-            dyvt(ad, 0, 0, 0, NA, true);
+            dyvt(ad, 0, 0, 0, NA / 2, 2);
         } else if (wave == 1) {
-            dyvt(ad, 1, 0, 0, NA / 2, true);
-#pragma unroll
-            for (int m = NA / 2; m < NA; ++m) load_a1(hh + 1, tid, m);
-        } else if (wave == 3) {
-            dyvt(ad2, 1, 0, NA / 2, NA, false);
-            dyvt(ad, 1, 1, 0, NA, true);
+            dyvt(ad, 1, 0, 0, NA, 1);
+        } else if (wave == 2) {
+            dyvt(ad, 0, 0, NA / 2, NA, 2);
         } else {
-#pragma unroll
-            for (int m = 0; m < NA; ++m) load_a1(hh + 1, tid, m);
+            dyvt(ad, 1, 1, 0, NA, 1);
         }
         load_b(hh + 1, tid);
         __syncthreads();   // dY and V read
-        if (wave == 3) {
+        if (wave == 2) {
 #pragma unroll
             for (int a = 0; a < 4; ++a)
                 *reinterpret_cast<float4 *>(X + (a * 64 + lane) * 4) =
-                    make_float4(ad2[4 * a], ad2[4 * a + 1], ad2[4 * a + 2], ad2[4 * a + 3]);
+                    make_float4(ad[4 * a], ad[4 * a + 1], ad[4 * a + 2], ad[4 * a + 3]);
         }
-        __syncthreads();   // wave 3's half of tile 1 visible
+        __syncthreads();   // wave 2's half of tile 0 visible
         float *const DP = X + 1024;   // dP [CH][LDP]
 
         if (wave != 2) {
@@ -1286,7 +1288,7 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
             // lower part of M = (Q K^T) o D o (dY V^T)
             const int td = wave == 0 ? 0 : wave == 1 ? 1 : 2;
             const int it = td > 0, jt = td == 2;
-            if (wave == 1) {
+            if (wave == 0) {
 #pragma unroll
                 for (int a = 0; a < 4; ++a) {
                     const float4 x = *reinterpret_cast<const float4 *>(X + (a * 64 + lane) * 4);
@@ -1335,6 +1337,11 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
         // the next head's first slabs, in flight over the intra products
         load_slab(p0, hh + 1, 0, tid);
 
+        // Intra products.  The row blocks rt = 1 (dQ) and rt = 0 (dK) have twice
+        // the work of the others, so with dk > 32 their last 32 state rows are
+        // taken by the other wave of the side (wave 0 for wave 1, wave 3 for wave
+        // 2), summed over heads in xacc and added at the end.
+        const bool shed = OFF && (wave == 1 || wave == 2);
         if (grp == 0) {
             // dQ^T[ct, rt] += K[:, ct]^T dP[rt, :]^T over j < 32 (rt + 1); all tiles
             // interleaved on independent chains
@@ -1346,14 +1353,30 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
                     const float4 x = *reinterpret_cast<const float4 *>(ap + 8 * a);
 #pragma unroll
                     for (int ct = 0; ct < NKS; ++ct) {
-                        dacc[ct] = mfma32(bk[(8 * a + 0) * LDK + 32 * ct], x.x, dacc[ct]);
-                        dacc[ct] = mfma32(bk[(8 * a + 1) * LDK + 32 * ct], x.y, dacc[ct]);
-                        dacc[ct] = mfma32(bk[(8 * a + 2) * LDK + 32 * ct], x.z, dacc[ct]);
-                        dacc[ct] = mfma32(bk[(8 * a + 3) * LDK + 32 * ct], x.w, dacc[ct]);
+                        if (ct < NKS - 1 || !shed) {
+                            dacc[ct] = mfma32(bk[(8 * a + 0) * LDK + 32 * ct], x.x, dacc[ct]);
+                            dacc[ct] = mfma32(bk[(8 * a + 1) * LDK + 32 * ct], x.y, dacc[ct]);
+                            dacc[ct] = mfma32(bk[(8 * a + 2) * LDK + 32 * ct], x.z, dacc[ct]);
+                            dacc[ct] = mfma32(bk[(8 * a + 3) * LDK + 32 * ct], x.w, dacc[ct]);
+                        }
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
                 if (a == 1 && NKS > 1) load_slab(pn, hh + 1, 1, tid);
+            }
+            if (OFF && wave == 0) {
+                // dQ^T[NKS - 1, 1] for wave 1
+                const float *ap1 = DP + (32 + cl) * LDP + 4 * kh;
+                const float *bk1 = bk + 32 * (NKS - 1);
+#pragma unroll
+                for (int a = 0; a < 8; ++a) {
+                    const float4 x = *reinterpret_cast<const float4 *>(ap1 + 8 * a);
+                    xacc = mfma32(bk1[(8 * a + 0) * LDK], x.x, xacc);
+                    xacc = mfma32(bk1[(8 * a + 1) * LDK], x.y, xacc);
+                    xacc = mfma32(bk1[(8 * a + 2) * LDK], x.z, xacc);
+                    xacc = mfma32(bk1[(8 * a + 3) * LDK], x.w, xacc);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
         } else {
             // dK^T[ct, rt] += Q[:, ct]^T dP[:, rt] over i >= 32 rt; MFMA s = 8 g2 + e
@@ -1370,10 +1393,29 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
                             const int i = 32 * it + 16 * g2 + e;
                             const float x = ap[i * LDP];
 #pragma unroll
-                            for (int ct = 0; ct < NKS; ++ct) dacc[ct] = mfma32(bq[i * LDQ + 32 * ct], x, dacc[ct]);
+                            for (int ct = 0; ct < NKS; ++ct) {
+                                if (ct < NKS - 1 || !shed) dacc[ct] = mfma32(bq[i * LDQ + 32 * ct], x, dacc[ct]);
+                            }
                         }
                         __builtin_amdgcn_sched_barrier(0);
                         if (it == 1 && g2 == 0 && NKS > 1) load_slab(pn, hh + 1, 1, tid);
+                    }
+                }
+            }
+            if (OFF && wave == 3) {
+                // dK^T[NKS - 1, 0] for wave 2
+                const float *ap0 = DP + 8 * kh * LDP + cl;
+                const float *bq1 = bq + 32 * (NKS - 1);
+#pragma unroll
+                for (int it = 0; it < 2; ++it) {
+#pragma unroll
+                    for (int g2 = 0; g2 < 2; ++g2) {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const int i = 32 * it + 16 * g2 + e;
+                            xacc = mfma32(bq1[i * LDQ], ap0[i * LDP], xacc);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
                     }
                 }
             }
@@ -1417,6 +1459,20 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
             for (int a = 0; a < 4; ++a)
                 *reinterpret_cast<float4 *>(o + 32 * ks + 8 * a) =
                     make_float4(dacc[ks][4 * a], dacc[ks][4 * a + 1], dacc[ks][4 * a + 2], dacc[ks][4 * a + 3]);
+        }
+        __syncthreads();
+        if (OFF && (wave == 0 || wave == 3)) {
+            // add the tiles taken over from waves 1 (dQ, positions 32 ..) and 2 (dK, positions 0 ..)
+            float *ox = X + grp * CH * LDQ + (32 * (1 - rt) + cl) * LDQ + 4 * kh + 32 * (NKS - 1);
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                float4 y = *reinterpret_cast<const float4 *>(ox + 8 * a);
+                y.x += xacc[4 * a];
+                y.y += xacc[4 * a + 1];
+                y.z += xacc[4 * a + 2];
+                y.w += xacc[4 * a + 3];
+                *reinterpret_cast<float4 *>(ox + 8 * a) = y;
+            }
         }
         __syncthreads();
         const int64_t tb = (int64_t)rows * dk_ * 4;

@@ -1248,11 +1248,18 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
         // MFMAs.  The next head's A rows are loaded LPG per MFMA group.
         f32x16 ad = zero16();
         auto dyvt = [&](f32x16 &acc, int it, int jt, int m0, int m1, int LPG) {
+            const float *xa = RY + (32 * it + cl) * LDY + 4 * kh, *ya = RV + (32 * jt + cl) * LDY + 4 * kh;
+            float4 xb[2], yb[2];
+            xb[m0 & 1] = *reinterpret_cast<const float4 *>(xa + 8 * m0);
+            yb[m0 & 1] = *reinterpret_cast<const float4 *>(ya + 8 * m0);
 #pragma unroll
             for (int m = 0; m < NA; ++m) {
                 if (m >= m0 && m < m1) {
-                    const float4 x = *reinterpret_cast<const float4 *>(RY + (32 * it + cl) * LDY + 8 * m + 4 * kh);
-                    const float4 y = *reinterpret_cast<const float4 *>(RV + (32 * jt + cl) * LDY + 8 * m + 4 * kh);
+                    if (m + 1 < m1) {
+                        xb[(m + 1) & 1] = *reinterpret_cast<const float4 *>(xa + 8 * (m + 1));
+                        yb[(m + 1) & 1] = *reinterpret_cast<const float4 *>(ya + 8 * (m + 1));
+                    }
+                    const float4 x = xb[m & 1], y = yb[m & 1];
                     acc = mfma32(x.x, y.x, acc);
                     acc = mfma32(x.y, y.y, acc);
                     acc = mfma32(x.z, y.z, acc);
@@ -1347,20 +1354,34 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
             // interleaved on independent chains
             const float *ap = DP + (32 * rt + cl) * LDP + 4 * kh;
             const float *bk = KL + 4 * kh * LDK + cl;
+            // operands of step (a, e) are read one step ahead: x for the next a,
+            // the K column values for the next e
+            const int na = 4 * (rt + 1);
+            float4 xq[2];
+            float kq[2][NKS];
+            auto ldk = [&](int a, int e, int buf) {
+#pragma unroll
+                for (int ct = 0; ct < NKS; ++ct) kq[buf][ct] = bk[(8 * a + e) * LDK + 32 * ct];
+            };
+            xq[0] = *reinterpret_cast<const float4 *>(ap);
+            ldk(0, 0, 0);
 #pragma unroll
             for (int a = 0; a < 8; ++a) {
-                if (a < 4 * (rt + 1)) {
-                    const float4 x = *reinterpret_cast<const float4 *>(ap + 8 * a);
+                if (a < na) {
+                    if (a + 1 < na) xq[(a + 1) & 1] = *reinterpret_cast<const float4 *>(ap + 8 * (a + 1));
+                    const float4 x = xq[a & 1];
+                    const float xs[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
-                    for (int ct = 0; ct < NKS; ++ct) {
-                        if (ct < NKS - 1 || !shed) {
-                            dacc[ct] = mfma32(bk[(8 * a + 0) * LDK + 32 * ct], x.x, dacc[ct]);
-                            dacc[ct] = mfma32(bk[(8 * a + 1) * LDK + 32 * ct], x.y, dacc[ct]);
-                            dacc[ct] = mfma32(bk[(8 * a + 2) * LDK + 32 * ct], x.z, dacc[ct]);
-                            dacc[ct] = mfma32(bk[(8 * a + 3) * LDK + 32 * ct], x.w, dacc[ct]);
+                    for (int e = 0; e < 4; ++e) {
+                        const int f = 4 * a + e;
+                        if (e < 3) ldk(a, e + 1, (f + 1) & 1);
+                        else if (a + 1 < na) ldk(a + 1, 0, (f + 1) & 1);
+#pragma unroll
+                        for (int ct = 0; ct < NKS; ++ct) {
+                            if (ct < NKS - 1 || !shed) dacc[ct] = mfma32(kq[f & 1][ct], xs[e], dacc[ct]);
                         }
+                        __builtin_amdgcn_sched_barrier(0);
                     }
-                    __builtin_amdgcn_sched_barrier(0);
                 }
                 if (a == 1 && NKS > 1) load_slab(pn, hh + 1, 1, tid);
             }
@@ -1383,23 +1404,26 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
             // contracts rows (i0 + 16 g2 + e, + 8)
             const float *ap = DP + 8 * kh * LDP + 32 * rt + cl;
             const float *bq = QL + 8 * kh * LDQ + cl;
+            // step f = 16 it + 8 g2 + e contracts rows (32 it + 16 g2 + e, + 8); its
+            // operands are read one step ahead
+            float xd[2], qv[2][NKS];
+            auto ldq = [&](int f, int buf) {
+                const int i = 32 * (f >> 4) + 16 * ((f >> 3) & 1) + (f & 7);
+                xd[buf] = ap[i * LDP];
 #pragma unroll
-            for (int it = 0; it < 2; ++it) {
-                if (it >= rt) {
+                for (int ct = 0; ct < NKS; ++ct) qv[buf][ct] = bq[i * LDQ + 32 * ct];
+            };
+            ldq(16 * rt, 0);
 #pragma unroll
-                    for (int g2 = 0; g2 < 2; ++g2) {
+            for (int f = 0; f < 32; ++f) {
+                if (f >= 16 * rt) {
+                    if (f + 1 < 32) ldq(f + 1, (f + 1) & 1);
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            const int i = 32 * it + 16 * g2 + e;
-                            const float x = ap[i * LDP];
-#pragma unroll
-                            for (int ct = 0; ct < NKS; ++ct) {
-                                if (ct < NKS - 1 || !shed) dacc[ct] = mfma32(bq[i * LDQ + 32 * ct], x, dacc[ct]);
-                            }
-                        }
-                        __builtin_amdgcn_sched_barrier(0);
-                        if (it == 1 && g2 == 0 && NKS > 1) load_slab(pn, hh + 1, 1, tid);
+                    for (int ct = 0; ct < NKS; ++ct) {
+                        if (ct < NKS - 1 || !shed) dacc[ct] = mfma32(qv[f & 1][ct], xd[f & 1], dacc[ct]);
                     }
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (f == 23 && NKS > 1) load_slab(pn, hh + 1, 1, tid);
                 }
             }
             if (OFF && wave == 3) {

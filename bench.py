@@ -103,7 +103,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=20,
+                    help="untimed steps first; the GPU needs some 20 ms of work to reach its working clocks")
     ap.add_argument("--workload", default="g2h8_d128_T8192")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-mib", type=int, default=0,

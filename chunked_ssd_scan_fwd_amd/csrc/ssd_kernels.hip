@@ -969,18 +969,31 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
         const int lane = tid & 63, cl = lane & 31, kh = lane >> 5;
         ar[m] = load4(r, (uint32_t)((32 * rt + cl) * dv_), 8 * m + 4 * kh, dv_, true, VEC);
     };
-    auto load_slab = [&](Slab &p, int hh, int ks, int tid) {
+    // float4 u of one slab of S_in and of dS_out
+    auto load_slab1 = [&](Slab &p, int hh, int ks, int tid, int u) {
         const bool live = hh < hpg;
         const int64_t off = ((bh0 + (live ? hh : 0)) * NC + c) * Epad;
         const rsrc_t sr = make_rsrc(states + off, live ? E * 4 : 0), dr = make_rsrc(dstates + off, live ? E * 4 : 0);
+        const int idx = tid + u * NTB;
+        const int r = idx / (DVP / 4), c4 = (idx % (DVP / 4)) * 4;
+        const bool ok = idx < 32 * DVP / 4;
+        p.s[u] = load4(sr, (uint32_t)((32 * ks + r) * dv_), c4, dv_, ok, VEC);
+        p.d[u] = load4(dr, (uint32_t)((32 * ks + r) * dv_), c4, dv_, ok, VEC);
+    };
+    auto load_slab = [&](Slab &p, int hh, int ks, int tid) {
 #pragma unroll
-        for (int u = 0; u < SPER; ++u) {
-            const int idx = tid + u * NTB;
-            const int r = idx / (DVP / 4), c4 = (idx % (DVP / 4)) * 4;
-            const bool ok = idx < 32 * DVP / 4;
-            p.s[u] = load4(sr, (uint32_t)((32 * ks + r) * dv_), c4, dv_, ok, VEC);
-            p.d[u] = load4(dr, (uint32_t)((32 * ks + r) * dv_), c4, dv_, ok, VEC);
-        }
+        for (int u = 0; u < SPER; ++u) load_slab1(p, hh, ks, tid, u);
+    };
+    // Stage float4 u of a slab into buffer buf; returns this thread's part of
+    // <dS_out, S_in> over it.
+    auto store_piece = [&](const Slab &p, int buf, int tid, int u) -> float {
+        const int idx = tid + u * NTB;
+        if (idx >= 32 * DVP / 4) return 0.f;
+        float *ds = X + buf * 2 * SLN;
+        const int r = idx / (DVP / 4), c4 = (idx % (DVP / 4)) * 4;
+        *reinterpret_cast<float4 *>(ds + r * LSL + c4) = p.s[u];
+        *reinterpret_cast<float4 *>(ds + SLN + r * LSL + c4) = p.d[u];
+        return p.s[u].x * p.d[u].x + p.s[u].y * p.d[u].y + p.s[u].z * p.d[u].z + p.s[u].w * p.d[u].w;
     };
     // Stage a slab into buffer buf; returns this thread's part of <dS_out, S_in>.
     auto store_slab = [&](const Slab &p, int buf, int tid) -> float {
@@ -1069,7 +1082,6 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
         __syncthreads();   // partial sums read before the slabs overwrite them
         fro_next = store_slab(p0, 0, tid);
         if (NKS > 1) fro_next += store_slab(pn, 1, tid);
-        if (NKS > 2) load_slab(pn, 0, 2, tid);
         stage_b(tid);
         __syncthreads();
     }
@@ -1121,13 +1133,27 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
             if (ks > 0) __syncthreads();   // slab ks visible, slab ks - 1 read
-            if (ks >= 1 && ks + 1 < NKS) {
-                fro += store_slab(pn, (ks + 1) & 1, tid);
-                if (ks + 2 < NKS) load_slab(pn, hh, ks + 2, tid);
-            }
             const float *sS = X + (ks & 1) * 2 * SLN, *sD = sS + SLN;
+            // Gv operands (MFMA group g2 contracts slab rows (16 (g2 / 2) + 4 (g2 % 2) + e, + 8))
+            const float *kp = KL + (32 * rt + cl) * LDK + 32 * ks + 8 * kh;
+            const float *bd = sD + 8 * kh * LSL + 32 * grp * NCW + cl;
+            float4 xk[2];
+            float bv[2][NCW][4];
+            auto ldv = [&](int g2, int buf) {
+                const int o = 16 * (g2 >> 1) + 4 * (g2 & 1);
+                xk[buf] = *reinterpret_cast<const float4 *>(kp + o);
+#pragma unroll
+                for (int u = 0; u < NCW; ++u) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) bv[buf][u][e] = bd[(o + e) * LSL + 32 * u];
+                }
+            };
             // Gq / Gk: A = slab rows (row i of the slab in lane i), B = the wave's rows;
-            // operands read one MFMA group ahead
+            // operands read one MFMA group ahead.  Spread over the first groups: the
+            // next slab goes from registers to the free buffer and the one after it
+            // is loaded, one float4 of each state per two groups, so that neither
+            // the LDS writes nor the global loads arrive in a burst; the last group
+            // reads the first Gv operands.
             f32x16 gt = zero16();
             {
                 const float *bp = (grp ? sD : sS) + cl * LSL + 4 * kh;
@@ -1141,25 +1167,15 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
                     gt = mfma32(y.y, ar[m].y, gt);
                     gt = mfma32(y.z, ar[m].z, gt);
                     gt = mfma32(y.w, ar[m].w, gt);
+                    if ((m & 1) && (m >> 1) < SPER) {
+                        if (ks >= 1 && ks + 1 < NKS) fro += store_piece(pn, (ks + 1) & 1, tid, m >> 1);
+                        if (ks + 2 < NKS) load_slab1(pn, hh, ks + 2, tid, m >> 1);
+                    }
+                    if (m == NA - 1 && gvw) ldv(0, 0);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
-            // Gv: MFMA group g2 contracts slab rows (16 (g2 / 2) + 4 (g2 % 2) + e, + 8)
             if (gvw) {
-                const float *kp = KL + (32 * rt + cl) * LDK + 32 * ks + 8 * kh;
-                const float *bd = sD + 8 * kh * LSL + 32 * grp * NCW + cl;
-                float4 xk[2];
-                float bv[2][NCW][4];
-                auto ldv = [&](int g2, int buf) {
-                    const int o = 16 * (g2 >> 1) + 4 * (g2 & 1);
-                    xk[buf] = *reinterpret_cast<const float4 *>(kp + o);
-#pragma unroll
-                    for (int u = 0; u < NCW; ++u) {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) bv[buf][u][e] = bd[(o + e) * LSL + 32 * u];
-                    }
-                };
-                ldv(0, 0);
 #pragma unroll
                 for (int g2 = 0; g2 < 4; ++g2) {
                     if (g2 + 1 < 4) ldv(g2 + 1, (g2 + 1) & 1);
@@ -1467,7 +1483,6 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
         __syncthreads();   // dP, dY V^T sums and reductions read; the slab buffers are free
         fro_next = store_slab(p0, 0, tid);
         if (NKS > 1) fro_next += store_slab(pn, 1, tid);
-        if (NKS > 2) load_slab(pn, hh + 1, 2, tid);
         stage_b(tid);
         __syncthreads();
     }

@@ -7,6 +7,8 @@ seeded synthetic inputs resident in HBM.  Prints one JSON line.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
     python bench.py --copy-mib N      # plain device copy of N MiB, 5 times: the
                                       # reference kernel for scaling HBM counters
+    python bench.py --max-len         # T-doubling search: the longest sequence whose
+                                      # fwd_bwd fits in HBM at g2h8_d128, B=4
 
 Throughput (`value`) is the nominal fwd+bwd FLOP count of the step divided
 by the measured step time.  Nominal FLOPs per (token, head), with chunk
@@ -99,6 +101,84 @@ def cpu_info():
     return model
 
 
+def fwd_bwd_bytes(B, G, H, T, dk, dv, ws):
+    """Device bytes of one fwd_bwd: inputs, y, the five gradients and the workspace."""
+    f = 4
+    return (f * (4 * B * G * T * dk            # q, k, dq, dk
+                 + 4 * B * H * T * dv          # v, dy, y, dv
+                 + 2 * B * H * T               # log_alpha, dlog_alpha
+                 + 2 * B * H * dk * dv)        # h0, dh0
+            + ws)
+
+
+def max_len_search(args, torch, ssd):
+    """Longest T (doubling from 8192) whose fwd_bwd at g2h8_d128, B=4, fits in HBM.
+
+    Inputs follow the synthetic recipe but are drawn on the device (a host copy
+    of the largest sizes would need some hundred GiB of host memory).  A size is
+    run only if its predicted bytes fit in the free HBM, so the search never
+    relies on an allocation failure; every run checks that y and the gradients
+    are finite.
+    """
+    import math
+    B, G, H, dk, dv = 4, 2, 8, 128, 128
+    dev = torch.device("cuda")
+    gen = torch.Generator(device=dev)
+    runs = []
+    T = 8192
+    best = 0
+    stop = None
+    while T <= args.max_len_cap:
+        sa = ssd.ShapeArg(B, G, H, T, dk, dv)
+        ws_b = ssd.workspace_size(sa, True)
+        need = fwd_bwd_bytes(B, G, H, T, dk, dv, ws_b)
+        free, total = torch.cuda.mem_get_info()
+        if need > 0.92 * free:
+            stop = {"T": T, "predicted_bytes": need, "free_bytes": free, "total_bytes": total}
+            break
+        gen.manual_seed(T)
+        q = torch.randn((B, G, T, dk), device=dev, generator=gen) / math.sqrt(128.0)
+        k = torch.randn((B, G, T, dk), device=dev, generator=gen) / math.sqrt(128.0)
+        v = torch.randn((B, H, T, dv), device=dev, generator=gen)
+        la = -torch.nn.functional.softplus(-2.0 + torch.randn((B, H, T), device=dev, generator=gen))
+        h0 = 0.1 * torch.randn((B, H, dk, dv), device=dev, generator=gen)
+        dy = torch.randn((B, H, T, dv), device=dev, generator=gen)
+        y = torch.empty((B, H, T, dv), device=dev)
+        grads = (torch.empty((B, G, T, dk), device=dev), torch.empty((B, G, T, dk), device=dev),
+                 torch.empty((B, H, T, dv), device=dev), torch.empty((B, H, T), device=dev),
+                 torch.empty((B, H, dk, dv), device=dev))
+        ws = torch.empty(ws_b, dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+        torch.cuda.reset_peak_memory_stats()
+
+        def step():
+            ssd.fwd(q, k, v, la, h0, out=y, workspace=ws)
+            ssd.bwd(q, k, v, la, h0, dy, out=grads, workspace=ws)
+
+        step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        step()
+        e1.record()
+        torch.cuda.synchronize()
+        finite = bool(torch.isfinite(y).all()) and all(bool(torch.isfinite(g).all()) for g in grads)
+        runs.append({"T": T, "fwd_bwd_ms": e0.elapsed_time(e1), "workspace_bytes": ws_b,
+                     "predicted_bytes": need, "peak_allocated_bytes": torch.cuda.max_memory_allocated(),
+                     "finite": finite})
+        print(json.dumps(runs[-1]), file=sys.stderr, flush=True)
+        if not finite:
+            stop = {"T": T, "reason": "non-finite output"}
+            break
+        best = T
+        del q, k, v, la, h0, dy, y, grads, ws
+        torch.cuda.empty_cache()
+        T *= 2
+    print(json.dumps({"metric": "max_len fwd_bwd g2h8_d128 B=4 fp32 (T doubling from 8192)", "value": best,
+                      "unit": "tokens", "higher_is_better": True, "device": torch.cuda.get_device_name(0),
+                      "runs": runs, "stopped_at": stop, "data": "synthetic, drawn on the device"}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -109,6 +189,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (5 launches) and exit")
+    ap.add_argument("--max-len", action="store_true",
+                    help="only run the T-doubling maximum-length search for fwd_bwd and exit")
+    ap.add_argument("--max-len-cap", type=int, default=1 << 22, help="largest T the search tries")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -131,6 +214,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": 4 * n, "launches": 5}), flush=True)
+        return
+    if args.max_len:
+        max_len_search(args, torch, ssd)
         return
     w = workload(args.workload)
     s = w.shape
@@ -195,6 +281,16 @@ def main():
     step_ms, per_step, wall_ms, kern_dom = timed(step, K, kernels=[dom])
     fwd_ms, fwd_per, _, _ = timed(fwd, K)
     bwd_ms, bwd_per, _, _ = timed(bwd, K)
+
+    # Secondary (not the headline): the backward that reuses the forward's
+    # residuals from the shared workspace instead of recomputing them.
+    def step_reuse():
+        fwd()
+        ssd.bwd_from_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["h0"], d["dy"], out=grads, workspace=ws)
+
+    for _ in range(3):
+        step_reuse()
+    reuse_ms, reuse_per, _, _ = timed(step_reuse, K)
 
     f_fwd, f_bwd = nominal_flops(s)
     b_fwd, b_fwd_bwd = io_bytes(s)
@@ -276,9 +372,15 @@ def main():
         "fwd": {**q(fwd_per), "ms": fwd_ms, "tflops": f_fwd / (fwd_ms * 1e-3) / 1e12,
                 "roofline_frac": t_roof_f / (fwd_ms * 1e-3), "gbps_io": b_fwd / (fwd_ms * 1e-3) / 1e9},
         "bwd": {**q(bwd_per), "ms": bwd_ms, "tflops": f_bwd / (bwd_ms * 1e-3) / 1e12},
+        "fwd_bwd_reuse": {**q(reuse_per), "ms": reuse_ms,
+                          "note": "secondary: ssd_fwd then ssd_bwd_from_fwd, which reuses the forward's "
+                                  "chunk states from the workspace (not the stateless headline step)"},
         "kernels": kernels,
         "parity_rel_err": parity,
         "first_call_ms": first_call_ms,
+        "memory": {"workspace_bytes_fwd": ssd.workspace_size(sa, False), "workspace_bytes_bwd": ssd.workspace_size(sa, True),
+                   "fwd_bwd_bytes": fwd_bwd_bytes(s.B, s.G, s.H, s.T, s.dk, s.dv, ssd.workspace_size(sa, True)),
+                   "peak_allocated_bytes": torch.cuda.max_memory_allocated()},
         "device": torch.cuda.get_device_name(0),
         "source_hash": source_hash(),
     }

@@ -16,7 +16,7 @@ import ctypes
 import os
 
 __all__ = ["fwd", "bwd", "library", "ShapeArg", "SsdError", "workspace_size",
-           "workspace_layout", "kernel_timing", "CHUNK"]
+           "workspace_layout", "kernel_timing", "CHUNK", "bwd_from_fwd"]
 
 CHUNK = 64
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -55,6 +55,8 @@ def library(path: str | None = None):
     lib.ssd_fwd.restype = ctypes.c_int
     lib.ssd_bwd.argtypes = [sp] + [vp] * 11 + [vp, sz, vp]
     lib.ssd_bwd.restype = ctypes.c_int
+    lib.ssd_bwd_from_fwd.argtypes = [sp] + [vp] * 11 + [vp, sz, vp]
+    lib.ssd_bwd_from_fwd.restype = ctypes.c_int
     lib.ssd_workspace_layout.argtypes = [sp, ctypes.c_int, ctypes.POINTER(sz)]
     lib.ssd_workspace_layout.restype = ctypes.c_int
     lib.ssd_strerror.argtypes = [ctypes.c_int]
@@ -157,6 +159,21 @@ def fwd(q, k, v, log_alpha, h0, *, out=None, workspace=None):
 
 def bwd(q, k, v, log_alpha, h0, dy, *, out=None, workspace=None):
     """Gradients (dq, dk, dv, dlog_alpha, dh0) of L = sum(dy * y)."""
+    return _bwd_call("ssd_bwd", q, k, v, log_alpha, h0, dy, out, workspace)
+
+
+def bwd_from_fwd(q, k, v, log_alpha, h0, dy, *, workspace, out=None):
+    """Like `bwd`, reusing the residuals that `fwd` left in `workspace`.
+
+    `workspace` must be a backward-sized workspace (``workspace_size(shape,
+    True)`` bytes) that was passed to `fwd` on the same inputs, with that
+    forward enqueued earlier on the current stream."""
+    if workspace is None:
+        raise ValueError("bwd_from_fwd needs the workspace the forward wrote")
+    return _bwd_call("ssd_bwd_from_fwd", q, k, v, log_alpha, h0, dy, out, workspace)
+
+
+def _bwd_call(fn, q, k, v, log_alpha, h0, dy, out, workspace):
     import torch
     lib = library()
     s = _shape_of(q, v)
@@ -174,11 +191,11 @@ def bwd(q, k, v, log_alpha, h0, dy, *, out=None, workspace=None):
     for t, sh, name in zip(out, shapes, ("dq", "dk", "dv", "dlog_alpha", "dh0")):
         _check(t, name, sh, dev)
     ws, need = _workspace(s, True, dev, workspace)
-    rc = lib.ssd_bwd(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(h0), _ptr(dy),
-                     *[_ptr(t) for t in out], _ptr(ws),
-                     ctypes.c_size_t(ws.numel() * ws.element_size()), _stream(dev))
+    rc = getattr(lib, fn)(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(h0), _ptr(dy),
+                          *[_ptr(t) for t in out], _ptr(ws),
+                          ctypes.c_size_t(ws.numel() * ws.element_size()), _stream(dev))
     if rc != 0:
-        raise SsdError(rc, "ssd_bwd")
+        raise SsdError(rc, fn)
     return out
 
 

@@ -337,7 +337,7 @@ __global__ __launch_bounds__(NTS) void k_state_scan(
     const float *__restrict__ dy, const float *__restrict__ h0, const float *__restrict__ bcum,
     const float *__restrict__ bl, float *__restrict__ states, float *__restrict__ dstates,
     float *__restrict__ dh0, int G, int H, int64_t T, int dk, int dv, int64_t NC, int64_t NCp, int64_t Epad,
-    int64_t per_dir)
+    int64_t per_dir, int dir0)
 {
     static_assert(TJ <= DVP && DVP % TJ == 0 && (TJ == 32 || TJ == 64 || TJ == 128), "tile width");
     constexpr int NTJ = DVP / TJ;
@@ -360,8 +360,9 @@ __global__ __launch_bounds__(NTS) void k_state_scan(
     const int64_t nblk = gridDim.x;
     int64_t L = blockIdx.x;
     if ((nblk & 7) == 0) L = (int64_t)(blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
-    const int dir = (int)(L / per_dir);
-    const int64_t rem = L - dir * per_dir;
+    const int64_t dl = L / per_dir;                   // direction index within this launch
+    const int dir = dir0 + (int)dl;                   // 0: forward states, 1: reverse
+    const int64_t rem = L - dl * per_dir;
     const int64_t bh = rem / NTILE;
     const int tile = (int)(rem - bh * NTILE);
     const int i0 = (tile / NTJ) * TI, j0 = (tile % NTJ) * TJ;
@@ -1546,9 +1547,9 @@ __global__ __launch_bounds__(NTH) void k_zero(float *__restrict__ p, int64_t n)
 // ---------------------------------------------------------------------------
 // Kernel timing (optional, process-global).
 
-enum KernelId { KID_CUMSUM = 0, KID_SCAN, KID_OUTPUT, KID_SCAN2, KID_GRADS, KID_COUNT };
+enum KernelId { KID_CUMSUM = 0, KID_SCAN, KID_OUTPUT, KID_SCAN2, KID_GRADS, KID_SCANR, KID_COUNT };
 static const char *kKernelNames[KID_COUNT] = {"chunk_cumsum", "state_scan", "chunk_output", "state_scan_bidir",
-                                              "bwd_grads"};
+                                              "bwd_grads", "state_scan_rev"};
 
 struct Timing {
     unsigned mask = 0;   // bit kid: time kernel kid
@@ -1656,30 +1657,32 @@ static int launch_status()
     return hipGetLastError() == hipSuccess ? SSD_OK : SSD_ERR_DEVICE;
 }
 
-// Chunk cumsum, then the fused state scan: the forward direction only
-// (ndir = 1, fills `states` with S_in) or both directions in one launch
-// (ndir = 2, also fills `dstates` with dS_out and writes dh0).
-static int run_scan(const Problem &P, int ndir, const float *q, const float *k, const float *v, const float *dy,
-                    const float *la, const float *h0, float *dh0, hipStream_t st)
+// Chunk cumsum (when `cumsum`), then the fused state scan over the
+// directions in `dirs`: 1 = forward only (fills `states` with S_in), 3 = both
+// in one launch (also fills `dstates` with dS_out and writes dh0), 2 = reverse
+// only (dstates and dh0; bcum and bl must already hold the cumsum).
+static int run_scan(const Problem &P, int dirs, bool cumsum, const float *q, const float *k, const float *v,
+                    const float *dy, const float *la, const float *h0, float *dh0, hipStream_t st)
 {
     const ssd_shape &s = P.s;
     const int64_t BH = s.B * s.H;
-    {
+    if (cumsum) {
         const int64_t nw = BH * P.L.NC;
         const int64_t grid = (nw + 3) / 4;
         launch(KID_CUMSUM, k_chunk_cumsum, dim3((unsigned)grid), dim3(NTH), st, la, P.bcum, P.bl, s.T, P.L.NC,
                P.L.NCp, nw);
+        if (launch_status() != SSD_OK) return SSD_ERR_DEVICE;
     }
-    if (launch_status() != SSD_OK) return SSD_ERR_DEVICE;
     {
         // Two chunks per step when there is at most one block per CU (the
         // paired tiles fill most of a CU's LDS); otherwise one.  State tiles
         // are 32 x 64 (32 x dv for dv < 64): wider tiles re-read fewer operand
         // tiles but halve the number of independent sequential chains per CU,
         // which measured slower.
+        const int ndir = dirs == 3 ? 2 : 1, dir0 = dirs == 2 ? 1 : 0;
         const int64_t tiles_k = BH * (P.DKP / TI);
         const bool pair = ndir * tiles_k * (P.DVP / (P.DVP < 64 ? P.DVP : 64)) <= kNumCUs;
-        const int kid = ndir == 1 ? KID_SCAN : KID_SCAN2;
+        const int kid = dirs == 1 ? KID_SCAN : dirs == 2 ? KID_SCANR : KID_SCAN2;
         SSD_DISPATCH(P, ({
             constexpr int TJ = VP < 64 ? VP : 64;
             const int64_t per_dir = tiles_k * (VP / TJ);
@@ -1687,11 +1690,11 @@ static int run_scan(const Problem &P, int ndir, const float *q, const float *k, 
             if (pair)
                 launch(kid, k_state_scan<KP, VP, VE, TJ, 2>, grid, blk, st, q, k, v, dy, h0, P.bcum, P.bl,
                        P.states, P.dstates, dh0, (int)s.G, (int)s.H, s.T, (int)s.dk, (int)s.dv, P.L.NC, P.L.NCp,
-                       P.L.Epad, per_dir);
+                       P.L.Epad, per_dir, dir0);
             else
                 launch(kid, k_state_scan<KP, VP, VE, TJ, 1>, grid, blk, st, q, k, v, dy, h0, P.bcum, P.bl,
                        P.states, P.dstates, dh0, (int)s.G, (int)s.H, s.T, (int)s.dk, (int)s.dv, P.L.NC, P.L.NCp,
-                       P.L.Epad, per_dir);
+                       P.L.Epad, per_dir, dir0);
         }));
     }
     return launch_status();
@@ -1740,7 +1743,7 @@ int ssd_fwd(const ssd_shape *shape, const float *q, const float *k, const float 
     if (rc != SSD_OK) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
 
-    rc = run_scan(P, 1, q, k, v, nullptr, log_alpha, h0, nullptr, st);
+    rc = run_scan(P, 1, true, q, k, v, nullptr, log_alpha, h0, nullptr, st);
     if (rc != SSD_OK) return rc;
     SSD_DISPATCH(P, launch(KID_OUTPUT, k_chunk_output<KP, VP, VE>, dim3((unsigned)(s.B * s.G * P.L.NC)),
                            dim3(NTW), st, q, k, v, P.bcum, P.states, y, (int)s.G, (int)s.H, s.T, (int)s.dk,
@@ -1748,9 +1751,15 @@ int ssd_fwd(const ssd_shape *shape, const float *q, const float *k, const float 
     return launch_status();
 }
 
-int ssd_bwd(const ssd_shape *shape, const float *q, const float *k, const float *v, const float *log_alpha,
-            const float *h0, const float *dy, float *dq, float *dk, float *dv, float *dlog_alpha, float *dh0,
-            void *workspace, size_t workspace_bytes, void *stream)
+}  // extern "C"
+
+namespace ssd {
+// Backward launches.  With `reuse`, the workspace already holds what ssd_fwd
+// wrote for these inputs (the chunk cumsum, its totals and S_in of every
+// chunk), so only the reverse state pass and the gradient kernel run.
+static int bwd_impl(const ssd_shape *shape, const float *q, const float *k, const float *v,
+                    const float *log_alpha, const float *h0, const float *dy, float *dq, float *dk, float *dv,
+                    float *dlog_alpha, float *dh0, void *workspace, size_t workspace_bytes, void *stream, bool reuse)
 {
     int rc = check_shape(shape);
     if (rc != SSD_OK) return rc;
@@ -1774,13 +1783,33 @@ int ssd_bwd(const ssd_shape *shape, const float *q, const float *k, const float 
     rc = prepare(shape, true, workspace, workspace_bytes, &P);
     if (rc != SSD_OK) return rc;
 
-    // S_in (forward) and dS_out (reverse) of every chunk, and dh0.
-    rc = run_scan(P, 2, q, k, v, dy, log_alpha, h0, dh0, st);
+    // dS_out (reverse) of every chunk and dh0; without reuse also the cumsum
+    // and S_in (forward), in the same launch.
+    rc = run_scan(P, reuse ? 2 : 3, !reuse, q, k, v, dy, log_alpha, h0, dh0, st);
     if (rc != SSD_OK) return rc;
     SSD_DISPATCH(P, launch(KID_GRADS, k_bwd_grads<KP, VP, VE>, dim3((unsigned)(s.B * s.G * P.L.NC)), dim3(NTB),
                            st, q, k, v, dy, P.bcum, P.bl, P.states, P.dstates, dq, dk, dv, dlog_alpha, (int)s.G,
                            (int)s.H, s.T, (int)s.dk, (int)s.dv, P.L.NC, P.L.NCp, P.L.Epad));
     return launch_status();
+}
+}  // namespace ssd
+
+extern "C" {
+
+int ssd_bwd(const ssd_shape *shape, const float *q, const float *k, const float *v, const float *log_alpha,
+            const float *h0, const float *dy, float *dq, float *dk, float *dv, float *dlog_alpha, float *dh0,
+            void *workspace, size_t workspace_bytes, void *stream)
+{
+    return bwd_impl(shape, q, k, v, log_alpha, h0, dy, dq, dk, dv, dlog_alpha, dh0, workspace, workspace_bytes,
+                    stream, false);
+}
+
+int ssd_bwd_from_fwd(const ssd_shape *shape, const float *q, const float *k, const float *v,
+                     const float *log_alpha, const float *h0, const float *dy, float *dq, float *dk, float *dv,
+                     float *dlog_alpha, float *dh0, void *workspace, size_t workspace_bytes, void *stream)
+{
+    return bwd_impl(shape, q, k, v, log_alpha, h0, dy, dq, dk, dv, dlog_alpha, dh0, workspace, workspace_bytes,
+                    stream, true);
 }
 
 int ssd_kernel_timing_enable(int mask)

@@ -128,6 +128,29 @@ const char *ssd_strerror(int status);
 /* Chunk length used by the kernels (SSD_CHUNK). */
 int ssd_chunk_size(void);
 
+/* Backward that reuses the forward's residuals: the same outputs as ssd_bwd,
+ * but the workspace must already hold what ssd_fwd wrote for the SAME inputs
+ * (q, k, v, log_alpha, h0 and shape) into a workspace of at least
+ * ssd_bwd_workspace_size(shape) bytes: the forward's regions (per-chunk
+ * cumulative log-decay, chunk totals and the state entering every chunk)
+ * sit at the same offsets in the forward and backward layouts.  Only the
+ * reverse state pass and the gradient kernel run, which skips recomputing
+ * the forward states.  This is the residual-keeping side of the trade-off
+ * that the GPU benchmark page records in its residual_mb field (0 for the
+ * stateless chunked backward, a few to a hundred MiB for its fused
+ * variant); ssd_bwd stays the stateless path.  The library cannot check the
+ * precondition: with a
+ * workspace that does not hold the forward's results for these inputs the
+ * outputs are wrong (but every access stays inside the workspace and the
+ * tensors).  Arguments, layouts, ownership, asynchrony and return codes are
+ * those of ssd_bwd; the forward work must be enqueued on the same stream
+ * before this call, or be complete. */
+int ssd_bwd_from_fwd(const ssd_shape *shape,
+                     const float *q, const float *k, const float *v,
+                     const float *log_alpha, const float *h0, const float *dy,
+                     float *dq, float *dk, float *dv, float *dlog_alpha, float *dh0,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
 /* Optional per-kernel timing with HIP events, for benchmarks.
  * ssd_kernel_timing_enable(mask) times the launches of the kernels whose bit
  * (1 << kid) is set in `mask` (-1: all kernels; 0: off, the default): their

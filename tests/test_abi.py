@@ -32,10 +32,10 @@ def _call_fwd(shape, ptr=1, ws_bytes=0):
     return lib.ssd_fwd(ctypes.byref(shape), p, p, p, p, p, p, p, ws_bytes, None)
 
 
-def _call_bwd(shape, ptr=1, ws_bytes=0):
+def _call_bwd(shape, ptr=1, ws_bytes=0, fn="ssd_bwd"):
     lib = ssd.library()
     p = ctypes.c_void_p(ptr) if ptr else None
-    return lib.ssd_bwd(ctypes.byref(shape), *([p] * 11), p, ws_bytes, None)
+    return getattr(lib, fn)(ctypes.byref(shape), *([p] * 11), p, ws_bytes, None)
 
 
 @pytest.mark.parametrize("shape,code", [
@@ -51,6 +51,7 @@ def _call_bwd(shape, ptr=1, ws_bytes=0):
 def test_bad_shapes_rejected(shape, code):
     assert _call_fwd(shape) == code
     assert _call_bwd(shape) == code
+    assert _call_bwd(shape, fn="ssd_bwd_from_fwd") == code
 
 
 def test_null_shape_and_pointers():
@@ -59,6 +60,7 @@ def test_null_shape_and_pointers():
     s = ssd.ShapeArg(1, 1, 1, 10, 8, 8)
     assert _call_fwd(s, ptr=0) == 1
     assert _call_bwd(s, ptr=0) == 1
+    assert _call_bwd(s, ptr=0, fn="ssd_bwd_from_fwd") == 1
 
 
 def test_misaligned_pointer_rejected():

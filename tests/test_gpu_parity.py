@@ -250,6 +250,42 @@ def test_guard_bands_poisoned_workspace_and_side_stream():
         assert torch.equal(d[k], before[k])
 
 
+REUSE = [ZOO[0], ZOO[3], ZOO[4], ZOO[5], ZOO[8], ZOO[10]]
+
+
+@pytest.mark.parametrize("shape", REUSE, ids=_id)
+def test_bwd_from_fwd(shape):
+    """The backward that reuses the forward's workspace: parity with the oracle,
+    and agreement with the stateless backward (same kernels, same sums)."""
+    need_gpu()
+    import torch
+    import chunked_ssd_scan_fwd_amd as ssd
+    say(f"bwd_from_fwd {_id(shape)}")
+    x = make_inputs(shape, seed=7 * shape.T + shape.dk)
+    d = to_dev(x)
+    sa = ssd.ShapeArg(shape.B, shape.G, shape.H, shape.T, shape.dk, shape.dv)
+    ws = torch.empty(max(1, ssd.workspace_size(sa, True)), dtype=torch.uint8, device="cuda")
+    y = ssd.fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["h0"], workspace=ws)
+    g = ssd.bwd_from_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["h0"], d["dy"], workspace=ws)
+    g0 = ssd.bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["h0"], d["dy"])
+    ref_y = oracle.fwd(x["q"], x["k"], x["v"], x["log_alpha"], x["h0"])
+    assert rel_err(host(y), ref_y) <= TOL_Y
+    ref = oracle.bwd(x["q"], x["k"], x["v"], x["log_alpha"], x["h0"], x["dy"])
+    for t, t0, name in zip(g, g0, GRADS):
+        a = host(t)
+        assert rel_err(a, ref[name]) <= TOL_G, name
+        assert rel_err(a, host(t0)) <= 1e-6, name
+
+
+def test_bwd_from_fwd_needs_workspace():
+    need_gpu()
+    import chunked_ssd_scan_fwd_amd as ssd
+    say("bwd_from_fwd without workspace")
+    d = to_dev(make_inputs(Shape(1, 1, 1, 8, 8, 8), 3))
+    with pytest.raises(ValueError):
+        ssd.bwd_from_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["h0"], d["dy"], workspace=None)
+
+
 def test_empty_shapes():
     need_gpu()
     import torch

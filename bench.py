@@ -187,6 +187,9 @@ def main():
                     help="untimed steps first; the GPU needs some 20 ms of work to reach its working clocks")
     ap.add_argument("--workload", default="g2h8_d128_T8192")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-reuse", action="store_true",
+                    help="skip the secondary fwd + bwd_from_fwd timing (profiling runs: its reverse-only "
+                         "state scan shares the forward scan's kernel name and grid)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (5 launches) and exit")
     ap.add_argument("--max-len", action="store_true",
@@ -288,9 +291,11 @@ def main():
         fwd()
         ssd.bwd_from_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["h0"], d["dy"], out=grads, workspace=ws)
 
-    for _ in range(3):
-        step_reuse()
-    reuse_ms, reuse_per, _, _ = timed(step_reuse, K)
+    reuse_ms, reuse_per = None, []
+    if not args.no_reuse:
+        for _ in range(3):
+            step_reuse()
+        reuse_ms, reuse_per, _, _ = timed(step_reuse, K)
 
     f_fwd, f_bwd = nominal_flops(s)
     b_fwd, b_fwd_bwd = io_bytes(s)
@@ -372,7 +377,7 @@ def main():
         "fwd": {**q(fwd_per), "ms": fwd_ms, "tflops": f_fwd / (fwd_ms * 1e-3) / 1e12,
                 "roofline_frac": t_roof_f / (fwd_ms * 1e-3), "gbps_io": b_fwd / (fwd_ms * 1e-3) / 1e9},
         "bwd": {**q(bwd_per), "ms": bwd_ms, "tflops": f_bwd / (bwd_ms * 1e-3) / 1e12},
-        "fwd_bwd_reuse": {**q(reuse_per), "ms": reuse_ms,
+        "fwd_bwd_reuse": None if reuse_ms is None else {**q(reuse_per), "ms": reuse_ms,
                           "note": "secondary: ssd_fwd then ssd_bwd_from_fwd, which reuses the forward's "
                                   "chunk states from the workspace (not the stateless headline step)"},
         "kernels": kernels,

@@ -192,6 +192,12 @@ __device__ __forceinline__ void gstore1(rsrc_t r, uint32_t off, float x)
 {
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(x), r, off, 0, 0);
 }
+// Store that is not read again by this kernel: non-temporal, so it does not
+// displace reusable lines from L2.
+__device__ __forceinline__ void gstore1_nt(rsrc_t r, uint32_t off, float x)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(x), r, off, 0, 2);
+}
 
 // Elements c4 .. c4+3 of the row that starts at element `rowoff` of resource
 // r; the row has `lim` elements (the rest read as 0), and nothing is read
@@ -528,7 +534,7 @@ __global__ __launch_bounds__(NTS) void k_state_scan(
             for (int u = 0; u < NU; ++u) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    gstore1(dst, soff(u, r), acc[u][r]);
+                    gstore1_nt(dst, soff(u, r), acc[u][r]);
                     acc[u][r] *= decay;
                 }
             }
@@ -850,7 +856,7 @@ __global__ __launch_bounds__(NTW) void k_chunk_output(const float *__restrict__ 
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int t = 32 * rt + acc_row(r, lane);   // rows past the sequence end fall outside yb
-                gstore1(yb, n < dv ? (uint32_t)(t * dv + n) * 4u : kOOB, acc[r] + acc2[r]);
+                gstore1_nt(yb, n < dv ? (uint32_t)(t * dv + n) * 4u : kOOB, acc[r] + acc2[r]);
             }
         }
         __syncthreads();   // S_in, V and decay reads done before the next step's writes
@@ -1255,7 +1261,7 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int t = 32 * rt + acc_row(r, lane);   // rows past the sequence end fall outside dvb
-                    gstore1(dvb, n < dv_ ? (uint32_t)(t * dv_ + n) * 4u : kOOB, gv[u][r]);
+                    gstore1_nt(dvb, n < dv_ ? (uint32_t)(t * dv_ + n) * 4u : kOOB, gv[u][r]);
                 }
             }
         }

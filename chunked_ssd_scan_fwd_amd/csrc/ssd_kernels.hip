@@ -170,6 +170,8 @@ __device__ __forceinline__ float4 zero4() { return make_float4(0.f, 0.f, 0.f, 0.
 // in flight stays exact.  Every resource covers one tile, slab or row, far
 // below 2 GiB.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 constexpr uint32_t kOOB = 0x80000000u;
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void *base, int64_t bytes)
@@ -197,6 +199,22 @@ __device__ __forceinline__ void gstore1(rsrc_t r, uint32_t off, float x)
 __device__ __forceinline__ void gstore1_nt(rsrc_t r, uint32_t off, float x)
 {
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(x), r, off, 0, 2);
+}
+// The same for N = 2 or 4 consecutive floats.  A non-temporal store that
+// covers only part of a cache line goes out as a partial line, so stores of
+// one line are best made by one instruction.
+template <int N>
+__device__ __forceinline__ void gstoreN_nt(rsrc_t r, uint32_t off, const float *x)
+{
+    if constexpr (N == 1) {
+        gstore1_nt(r, off, x[0]);
+    } else if constexpr (N == 2) {
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u, make_float2(x[0], x[1])), r, off, 0, 2);
+    } else {
+        static_assert(N == 4, "1, 2 or 4 floats");
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, make_float4(x[0], x[1], x[2], x[3])), r, off,
+                                               0, 2);
+    }
 }
 
 // Elements c4 .. c4+3 of the row that starts at element `rowoff` of resource
@@ -389,7 +407,7 @@ __global__ __launch_bounds__(NTS) void k_state_scan(
         const int lima = dk - i0, limb = dv - j0;
         struct Stage {
             float4 a[APER], b[BPER];
-            float bt[BPER], blc;
+            float at[APER], blc;
         };
         Stage stg[PD][CPS];
         // operands of chunk n of the scan order; chunks past the end load zeros
@@ -405,25 +423,32 @@ __global__ __launch_bounds__(NTS) void k_state_scan(
                 const int idx = lt + u * NLT;
                 const int r = idx / (TI / 4), c4 = (idx - r * (TI / 4)) * 4;
                 S.a[u] = load4(ab, (uint32_t)(r * dk + i0), c4, lima, idx < A4, VEC);
+                S.at[u] = gload1(br, idx < A4 ? (uint32_t)r * 4u : kOOB);
             }
 #pragma unroll
             for (int u = 0; u < BPER; ++u) {
                 const int idx = lt + u * NLT;
                 const int r = idx / (TJ / 4), c4 = (idx - r * (TJ / 4)) * 4;
                 S.b[u] = load4(bb, (uint32_t)(r * dv + j0), c4, limb, idx < B4, VEC);
-                S.bt[u] = gload1(br, idx < B4 ? (uint32_t)r * 4u : kOOB);
             }
             const float blc = bl[bh * NCp + c];
             S.blc = live ? blc : 0.f;
         };
-        // stage S into LDS half `buf`, slot cc; B rows scaled by the decay weights
+        // stage S into LDS half `buf`, slot cc; the rows of the A tile (TI
+        // wide, the narrower one) are scaled by the decay weights
         auto stage = [&](const Stage &S, int buf, int cc) {
 #pragma unroll
             for (int u = 0; u < APER; ++u) {
                 const int idx = lt + u * NLT;
                 if (A4 % NLT == 0 || idx < A4) {
                     const int r = idx / (TI / 4), c4 = (idx - r * (TI / 4)) * 4;
-                    *reinterpret_cast<float4 *>(&As[buf][cc][r * LDA + c4]) = S.a[u];
+                    const float w = (dir == 0) ? __expf(S.blc - S.at[u]) : __expf(S.at[u]);
+                    float4 x = S.a[u];
+                    x.x *= w;
+                    x.y *= w;
+                    x.z *= w;
+                    x.w *= w;
+                    *reinterpret_cast<float4 *>(&As[buf][cc][r * LDA + c4]) = x;
                 }
             }
 #pragma unroll
@@ -431,13 +456,7 @@ __global__ __launch_bounds__(NTS) void k_state_scan(
                 const int idx = lt + u * NLT;
                 if (B4 % NLT == 0 || idx < B4) {
                     const int r = idx / (TJ / 4), c4 = (idx - r * (TJ / 4)) * 4;
-                    const float w = (dir == 0) ? expf(S.blc - S.bt[u]) : expf(S.bt[u]);
-                    float4 x = S.b[u];
-                    x.x *= w;
-                    x.y *= w;
-                    x.z *= w;
-                    x.w *= w;
-                    *reinterpret_cast<float4 *>(&Bs[buf][cc][r * LDB + c4]) = x;
+                    *reinterpret_cast<float4 *>(&Bs[buf][cc][r * LDB + c4]) = S.b[u];
                 }
             }
             if (lt == 0) decs[buf][cc] = expf(S.blc);
@@ -530,13 +549,27 @@ __global__ __launch_bounds__(NTS) void k_state_scan(
             const bool live = n < NC;
             const rsrc_t dst =
                 make_rsrc(slab + (live ? (dir == 0 ? n : NC - 1 - n) : 0) * Epad, live ? E * 4 : 0);
+            if constexpr (VEC) {
+                // the lane's NU columns of a row are consecutive (dv % 4 == 0,
+                // so they are inside the state when the first one is)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float sv[NU];
+#pragma unroll
+                    for (int u = 0; u < NU; ++u) sv[u] = acc[u][r];
+                    gstoreN_nt<NU>(dst, soff(0, r), sv);
+                }
+            } else {
+#pragma unroll
+                for (int u = 0; u < NU; ++u) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) gstore1_nt(dst, soff(u, r), acc[u][r]);
+                }
+            }
 #pragma unroll
             for (int u = 0; u < NU; ++u) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    gstore1_nt(dst, soff(u, r), acc[u][r]);
-                    acc[u][r] *= decay;
-                }
+                for (int r = 0; r < 4; ++r) acc[u][r] *= decay;
             }
             // S += A^T B over the chunk's 64 positions
 #pragma unroll

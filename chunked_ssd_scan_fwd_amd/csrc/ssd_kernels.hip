@@ -404,6 +404,7 @@ __global__ __launch_bounds__(NTS) void k_state_scan(
         const float *Asrc = (dir == 0 ? k : q) + (b * G + g) * T * dk;   // row 0, column 0
         const float *Bsrc = (dir == 0 ? v : dy) + bh * T * dv;
         const float *bcb = bcum + bh * NC * CH;
+        const rsrc_t blr = make_rsrc(bl + bh * NCp, NC * 4);
         const int lima = dk - i0, limb = dv - j0;
         struct Stage {
             float4 a[APER], b[BPER];
@@ -431,8 +432,8 @@ __global__ __launch_bounds__(NTS) void k_state_scan(
                 const int r = idx / (TJ / 4), c4 = (idx - r * (TJ / 4)) * 4;
                 S.b[u] = load4(bb, (uint32_t)(r * dv + j0), c4, limb, idx < B4, VEC);
             }
-            const float blc = bl[bh * NCp + c];
-            S.blc = live ? blc : 0.f;
+            // a vector load: a scalar one would be waited for right here
+            S.blc = gload1(blr, live ? (uint32_t)c * 4u : kOOB);
         };
         // stage S into LDS half `buf`, slot cc; the rows of the A tile (TI
         // wide, the narrower one) are scaled by the decay weights

@@ -887,11 +887,12 @@ __global__ __launch_bounds__(NTW) void k_chunk_output(const float *__restrict__ 
         {
             const rsrc_t yb = make_rsrc(y + (bh * T + c * CH) * dv, live ? (int64_t)rows * dv * 4 : 0);
             const int n = 32 * ct + cl;
+            // row 32 rt + acc_row(r, lane): the lane's offset plus a uniform
+            // one per register (rows past the sequence end fall outside yb)
+            const uint32_t base = n < dv ? (uint32_t)((32 * rt + 4 * kh) * dv + n) * 4u : kOOB;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int t = 32 * rt + acc_row(r, lane);   // rows past the sequence end fall outside yb
-                gstore1_nt(yb, n < dv ? (uint32_t)(t * dv + n) * 4u : kOOB, acc[r] + acc2[r]);
-            }
+            for (int r = 0; r < 16; ++r)
+                gstore1_nt(yb, base + (uint32_t)(8 * (r / 4) + r % 4) * (uint32_t)(dv * 4), acc[r] + acc2[r]);
         }
         __syncthreads();   // S_in, V and decay reads done before the next step's writes
         stage(tid);
@@ -1292,11 +1293,12 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
 #pragma unroll
             for (int u = 0; u < NCW; ++u) {
                 const int n = 32 * (grp * NCW + u) + cl;
+                // row 32 rt + acc_row(r, lane): the lane's offset plus a uniform
+                // one per register (rows past the sequence end fall outside dvb)
+                const uint32_t base = n < dv_ ? (uint32_t)((32 * rt + 4 * kh) * dv_ + n) * 4u : kOOB;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int t = 32 * rt + acc_row(r, lane);   // rows past the sequence end fall outside dvb
-                    gstore1_nt(dvb, n < dv_ ? (uint32_t)(t * dv_ + n) * 4u : kOOB, gv[u][r]);
-                }
+                for (int r = 0; r < 16; ++r)
+                    gstore1_nt(dvb, base + (uint32_t)(8 * (r / 4) + r % 4) * (uint32_t)(dv_ * 4), gv[u][r]);
             }
         }
         // dY V^T tiles: tile 0 (rows 0-31 x cols 0-31) split over dv halves between

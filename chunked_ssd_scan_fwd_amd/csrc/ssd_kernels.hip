@@ -355,7 +355,7 @@ constexpr int TI = 32;
 constexpr int NTS = 512;        // 4 compute + 4 loader waves
 constexpr int kNumCUs = 256;    // MI355X compute units
 
-template <int DKP, int DVP, bool VEC, int TJ, int CPS>
+template <int DKP, int DVP, bool VEC, int TJ, int CPS, bool EXD>
 __global__ __launch_bounds__(NTS) void k_state_scan(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
     const float *__restrict__ dy, const float *__restrict__ h0, const float *__restrict__ bcum,
@@ -364,6 +364,11 @@ __global__ __launch_bounds__(NTS) void k_state_scan(
     int64_t per_dir, int dir0)
 {
     static_assert(TJ <= DVP && DVP % TJ == 0 && (TJ == 32 || TJ == 64 || TJ == 128), "tile width");
+    if constexpr (EXD) {   // dk == DKP, dv == DVP: index arithmetic on constants
+        dk = DKP;
+        dv = DVP;
+        Epad = (int64_t)DKP * DVP;
+    }
     constexpr int NTJ = DVP / TJ;
     constexpr int NTILE = (DKP / TI) * NTJ;
     constexpr int NU = TJ / 32;                       // accumulator tiles per compute wave
@@ -641,7 +646,7 @@ struct OutCfg {
     static constexpr int QPER = (CH * DKP / 4 + NTW - 1) / NTW;   // float4 / thread, one C x dk tile
 };
 
-template <int DKP, int DVP, bool VEC>
+template <int DKP, int DVP, bool VEC, bool EXD>
 __global__ __launch_bounds__(NTW) void k_chunk_output(const float *__restrict__ q, const float *__restrict__ k,
                                                       const float *__restrict__ v, const float *__restrict__ bcum,
                                                       const float *__restrict__ states, float *__restrict__ y,
@@ -649,6 +654,11 @@ __global__ __launch_bounds__(NTW) void k_chunk_output(const float *__restrict__ 
                                                       int64_t Epad)
 {
     using Cfg = OutCfg<DKP, DVP>;
+    if constexpr (EXD) {   // dk == DKP, dv == DVP: index arithmetic on constants
+        dk = DKP;
+        dv = DVP;
+        Epad = (int64_t)DKP * DVP;
+    }
     constexpr int NCT = Cfg::NCT, HPS = Cfg::HPS, LS = Cfg::LS, LDK = Cfg::LDK;
     constexpr int SPH = Cfg::SPH, VPH = Cfg::VPH, NL = Cfg::NL, NQ = Cfg::NQ, NQQ = Cfg::NQQ;
     // S_in tiles; Q, K and then the K Q^T partial sums at set-up
@@ -961,7 +971,7 @@ struct BwdCfg {
     static constexpr int NQQ = DKP / 32;                          // float4 per lane, a quarter of dk
 };
 
-template <int DKP, int DVP, bool VEC>
+template <int DKP, int DVP, bool VEC, bool EXD>
 __global__ __launch_bounds__(NTB) void k_bwd_grads(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
     const float *__restrict__ dy, const float *__restrict__ bcum, const float *__restrict__ bl,
@@ -970,6 +980,11 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
     int dv_, int64_t NC, int64_t NCp, int64_t Epad)
 {
     using Cfg = BwdCfg<DKP, DVP>;
+    if constexpr (EXD) {   // dk == DKP, dv == DVP: index arithmetic on constants
+        dk_ = DKP;
+        dv_ = DVP;
+        Epad = (int64_t)DKP * DVP;
+    }
     constexpr int NKS = Cfg::NKS, NCT = Cfg::NCT, NCW = Cfg::NCW, NA = Cfg::NA;
     constexpr int LDQ = Cfg::LDQ, LDK = Cfg::LDK, LSL = Cfg::LSL, LDY = Cfg::LDY, LDP = Cfg::LDP;
     constexpr int SLN = Cfg::SLN, SPER = Cfg::SPER, QPER = Cfg::QPER, NQQ = Cfg::NQQ;
@@ -1682,15 +1697,24 @@ static void collect_timing()
 
 #define SSD_DISPATCH(P_, BODY)                                                     \
     do {                                                                           \
-        if ((P_).vec) { constexpr bool VE = true; SSD_DISPATCH_DIMS((P_).DKP, (P_).DVP, BODY); } \
-        else { constexpr bool VE = false; SSD_DISPATCH_DIMS((P_).DKP, (P_).DVP, BODY); }      \
+        if ((P_).exact) {                                                          \
+            constexpr bool VE = true, EXD = true;                                  \
+            SSD_DISPATCH_DIMS((P_).DKP, (P_).DVP, BODY);                           \
+        } else if ((P_).vec) {                                                     \
+            constexpr bool VE = true, EXD = false;                                 \
+            SSD_DISPATCH_DIMS((P_).DKP, (P_).DVP, BODY);                           \
+        } else {                                                                   \
+            constexpr bool VE = false, EXD = false;                                \
+            SSD_DISPATCH_DIMS((P_).DKP, (P_).DVP, BODY);                           \
+        }                                                                          \
     } while (0)
 
 struct Problem {
     ssd_shape s;
     Layout L;
     int DKP, DVP;
-    bool vec;   // dk and dv multiples of 4: 16-byte loads
+    bool vec;     // dk and dv multiples of 4: 16-byte loads
+    bool exact;   // dk == DKP and dv == DVP: the kernels' index arithmetic on constants
     float *bcum, *bl, *states, *dstates;
 };
 
@@ -1730,11 +1754,11 @@ static int run_scan(const Problem &P, int dirs, bool cumsum, const float *q, con
             const int64_t per_dir = tiles_k * (VP / TJ);
             const dim3 grid((unsigned)(ndir * per_dir)), blk(NTS);
             if (pair)
-                launch(kid, k_state_scan<KP, VP, VE, TJ, 2>, grid, blk, st, q, k, v, dy, h0, P.bcum, P.bl,
+                launch(kid, k_state_scan<KP, VP, VE, TJ, 2, EXD>, grid, blk, st, q, k, v, dy, h0, P.bcum, P.bl,
                        P.states, P.dstates, dh0, (int)s.G, (int)s.H, s.T, (int)s.dk, (int)s.dv, P.L.NC, P.L.NCp,
                        P.L.Epad, per_dir, dir0);
             else
-                launch(kid, k_state_scan<KP, VP, VE, TJ, 1>, grid, blk, st, q, k, v, dy, h0, P.bcum, P.bl,
+                launch(kid, k_state_scan<KP, VP, VE, TJ, 1, EXD>, grid, blk, st, q, k, v, dy, h0, P.bcum, P.bl,
                        P.states, P.dstates, dh0, (int)s.G, (int)s.H, s.T, (int)s.dk, (int)s.dv, P.L.NC, P.L.NCp,
                        P.L.Epad, per_dir, dir0);
         }));
@@ -1754,6 +1778,7 @@ static int prepare(const ssd_shape *shape, bool backward, void *ws, size_t ws_by
     P->DKP = pad_dim(shape->dk);
     P->DVP = pad_dim(shape->dv);
     P->vec = (shape->dk % 4) == 0 && (shape->dv % 4) == 0;
+    P->exact = shape->dk == P->DKP && shape->dv == P->DVP;
     char *w = static_cast<char *>(ws);
     P->bcum = reinterpret_cast<float *>(w + P->L.off[0]);
     P->bl = reinterpret_cast<float *>(w + P->L.off[1]);
@@ -1787,7 +1812,7 @@ int ssd_fwd(const ssd_shape *shape, const float *q, const float *k, const float 
 
     rc = run_scan(P, 1, true, q, k, v, nullptr, log_alpha, h0, nullptr, st);
     if (rc != SSD_OK) return rc;
-    SSD_DISPATCH(P, launch(KID_OUTPUT, k_chunk_output<KP, VP, VE>, dim3((unsigned)(s.B * s.G * P.L.NC)),
+    SSD_DISPATCH(P, launch(KID_OUTPUT, k_chunk_output<KP, VP, VE, EXD>, dim3((unsigned)(s.B * s.G * P.L.NC)),
                            dim3(NTW), st, q, k, v, P.bcum, P.states, y, (int)s.G, (int)s.H, s.T, (int)s.dk,
                            (int)s.dv, P.L.NC, P.L.Epad));
     return launch_status();
@@ -1829,7 +1854,7 @@ static int bwd_impl(const ssd_shape *shape, const float *q, const float *k, cons
     // and S_in (forward), in the same launch.
     rc = run_scan(P, reuse ? 2 : 3, !reuse, q, k, v, dy, log_alpha, h0, dh0, st);
     if (rc != SSD_OK) return rc;
-    SSD_DISPATCH(P, launch(KID_GRADS, k_bwd_grads<KP, VP, VE>, dim3((unsigned)(s.B * s.G * P.L.NC)), dim3(NTB),
+    SSD_DISPATCH(P, launch(KID_GRADS, k_bwd_grads<KP, VP, VE, EXD>, dim3((unsigned)(s.B * s.G * P.L.NC)), dim3(NTB),
                            st, q, k, v, dy, P.bcum, P.bl, P.states, P.dstates, dq, dk, dv, dlog_alpha, (int)s.G,
                            (int)s.H, s.T, (int)s.dk, (int)s.dv, P.L.NC, P.L.NCp, P.L.Epad));
     return launch_status();

@@ -160,6 +160,18 @@ __global__ __launch_bounds__(NTH) void k_chunk_cumsum(const float *__restrict__ 
 
 constexpr int NTW = 512;   // 8 waves per block
 
+// Workgroup barrier across which the compiler may move no memory access.
+// __syncthreads() alone is a fence pair around s_barrier, and this compiler
+// has been seen to sink LDS reads below it into a region that other waves
+// overwrite after the barrier; the empty asm statements with a memory
+// clobber pin every access on its side.
+__device__ __forceinline__ void block_sync()
+{
+    asm volatile("" ::: "memory");
+    __syncthreads();
+    asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ float4 zero4() { return make_float4(0.f, 0.f, 0.f, 0.f); }
 
 // Global memory goes through buffer resources: a resource covers `bytes`
@@ -230,6 +242,22 @@ __device__ __forceinline__ float4 load4(rsrc_t r, uint32_t rowoff, int c4, int l
     return make_float4(e[0], e[1], e[2], e[3]);
 }
 
+// Float4 number tid + u NT of a row-major tile with Q4 float4 per row, for
+// NT a multiple of Q4 (0 <= tid < NT): its row and its first column.
+// Unsigned, so the division is a shift; the rows of one thread step by a
+// constant.
+template <int Q4, int NT>
+__device__ __forceinline__ int f4_row(int tid, int u)
+{
+    static_assert(NT % Q4 == 0, "a thread's float4 share their column");
+    return (int)((unsigned)tid / Q4) + u * (NT / Q4);
+}
+template <int Q4>
+__device__ __forceinline__ int f4_col(int tid)
+{
+    return (int)((unsigned)tid % Q4) * 4;
+}
+
 // Load a ROWS x DP tile into registers, PER float4 per thread, zero padded:
 // row-major with row stride d and d valid columns, from resource r, which
 // covers exactly the valid rows (rows past them read as 0).
@@ -239,9 +267,8 @@ __device__ __forceinline__ void tile_to_regs(int tid, float4 (&buf)[PER], rsrc_t
     constexpr int Q4 = DP / 4;
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
-        const int idx = tid + u * NT;
-        const int row = idx / Q4, c4 = (idx - row * Q4) * 4;
-        buf[u] = load4(r, (uint32_t)(row * d), c4, d, idx < ROWS * Q4, vec);
+        const int row = f4_row<Q4, NT>(tid, u), c4 = f4_col<Q4>(tid);
+        buf[u] = load4(r, (uint32_t)(row * d), c4, d, (ROWS * Q4) % NT == 0 || row < ROWS, vec);
     }
 }
 
@@ -252,9 +279,8 @@ __device__ __forceinline__ void regs_to_lds(int tid, const float4 (&buf)[PER], f
     constexpr int Q4 = DP / 4;
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
-        const int idx = tid + u * NT;
-        if (idx < ROWS * Q4) {
-            const int r = idx / Q4, c4 = (idx - r * Q4) * 4;
+        const int r = f4_row<Q4, NT>(tid, u), c4 = f4_col<Q4>(tid);
+        if ((ROWS * Q4) % NT == 0 || r < ROWS) {
             if (LD % 4 == 0) {
                 *reinterpret_cast<float4 *>(dst + r * LD + c4) = buf[u];
             } else {
@@ -426,16 +452,15 @@ __global__ __launch_bounds__(NTS) void k_state_scan(
             const rsrc_t br = make_rsrc(bcb + c * CH, live ? CH * 4 : 0);
 #pragma unroll
             for (int u = 0; u < APER; ++u) {
-                const int idx = lt + u * NLT;
-                const int r = idx / (TI / 4), c4 = (idx - r * (TI / 4)) * 4;
-                S.a[u] = load4(ab, (uint32_t)(r * dk + i0), c4, lima, idx < A4, VEC);
-                S.at[u] = gload1(br, idx < A4 ? (uint32_t)r * 4u : kOOB);
+                const int r = f4_row<TI / 4, NLT>(lt, u), c4 = f4_col<TI / 4>(lt);
+                const bool ok = A4 % NLT == 0 || r < CH;
+                S.a[u] = load4(ab, (uint32_t)(r * dk + i0), c4, lima, ok, VEC);
+                S.at[u] = gload1(br, ok ? (uint32_t)r * 4u : kOOB);
             }
 #pragma unroll
             for (int u = 0; u < BPER; ++u) {
-                const int idx = lt + u * NLT;
-                const int r = idx / (TJ / 4), c4 = (idx - r * (TJ / 4)) * 4;
-                S.b[u] = load4(bb, (uint32_t)(r * dv + j0), c4, limb, idx < B4, VEC);
+                const int r = f4_row<TJ / 4, NLT>(lt, u), c4 = f4_col<TJ / 4>(lt);
+                S.b[u] = load4(bb, (uint32_t)(r * dv + j0), c4, limb, B4 % NLT == 0 || r < CH, VEC);
             }
             // a vector load: a scalar one would be waited for right here
             S.blc = gload1(blr, live ? (uint32_t)c * 4u : kOOB);
@@ -445,9 +470,8 @@ __global__ __launch_bounds__(NTS) void k_state_scan(
         auto stage = [&](const Stage &S, int buf, int cc) {
 #pragma unroll
             for (int u = 0; u < APER; ++u) {
-                const int idx = lt + u * NLT;
-                if (A4 % NLT == 0 || idx < A4) {
-                    const int r = idx / (TI / 4), c4 = (idx - r * (TI / 4)) * 4;
+                const int r = f4_row<TI / 4, NLT>(lt, u), c4 = f4_col<TI / 4>(lt);
+                if (A4 % NLT == 0 || r < CH) {
                     const float w = (dir == 0) ? __expf(S.blc - S.at[u]) : __expf(S.at[u]);
                     float4 x = S.a[u];
                     x.x *= w;
@@ -459,9 +483,8 @@ __global__ __launch_bounds__(NTS) void k_state_scan(
             }
 #pragma unroll
             for (int u = 0; u < BPER; ++u) {
-                const int idx = lt + u * NLT;
-                if (B4 % NLT == 0 || idx < B4) {
-                    const int r = idx / (TJ / 4), c4 = (idx - r * (TJ / 4)) * 4;
+                const int r = f4_row<TJ / 4, NLT>(lt, u), c4 = f4_col<TJ / 4>(lt);
+                if (B4 % NLT == 0 || r < CH) {
                     *reinterpret_cast<float4 *>(&Bs[buf][cc][r * LDB + c4]) = S.b[u];
                 }
             }
@@ -470,7 +493,7 @@ __global__ __launch_bounds__(NTS) void k_state_scan(
         // step s: its chunks are published by the barrier; stage step s + 1
         // into the other half and refill its registers with step s + 1 + PD
         auto step = [&](int64_t s, int u) {
-            __syncthreads();
+            block_sync();
             const int un = (u + 1) % PD;
 #pragma unroll
             for (int cc = 0; cc < CPS; ++cc) {
@@ -525,7 +548,7 @@ __global__ __launch_bounds__(NTS) void k_state_scan(
     }
     for (int64_t s = 0; s < NS; ++s) {
         const int buf = (int)(s & 1);
-        __syncthreads();   // step s staged in half `buf`
+        block_sync();   // step s staged in half `buf`
 #pragma unroll
         for (int cc = 0; cc < CPS; ++cc) {
             float av[CH / 4];
@@ -644,6 +667,7 @@ struct OutCfg {
     static constexpr int NQ = DKP / 8;                            // float4 of a Q row per lane
     static constexpr int NQQ = DKP / 32;                          // the same, per quarter of dk
     static constexpr int QPER = (CH * DKP / 4 + NTW - 1) / NTW;   // float4 / thread, one C x dk tile
+    static_assert(NTW % (DVP / 4) == 0, "a thread's float4 of a tile share their column");
 };
 
 template <int DKP, int DVP, bool VEC, bool EXD>
@@ -693,11 +717,12 @@ __global__ __launch_bounds__(NTW) void k_chunk_output(const float *__restrict__ 
             const int hh = step * HPS + h2;
             const bool live = hh < hpg;
             const int64_t bh = bh0 + (live ? hh : 0);
-            const int idx = tid + e * NTW;
-            const int r = idx / (DVP / 4), c4 = (idx % (DVP / 4)) * 4;
+            // float4 tid + e NTW of the tile: row tid / (DVP/4) + e NTW / (DVP/4)
+            const int r = (int)((unsigned)tid / (DVP / 4)) + e * (NTW / (DVP / 4));
+            const int c4 = (int)((unsigned)tid % (DVP / 4)) * 4;
             if (!isv) {
                 const rsrc_t sr = make_rsrc(states + (bh * NC + c) * Epad, live ? E * 4 : 0);
-                sbuf[h2][e] = load4(sr, (uint32_t)(r * dv), c4, dv, idx < DKP * DVP / 4, VEC);
+                sbuf[h2][e] = load4(sr, (uint32_t)(r * dv), c4, dv, (DKP * DVP / 4) % NTW == 0 || r < DKP, VEC);
             } else {
                 const rsrc_t vr = make_rsrc(v + (bh * T + c * CH) * dv, live ? (int64_t)rows * dv * 4 : 0);
                 vbuf[h2][e] = load4(vr, (uint32_t)(r * dv), c4, dv, true, VEC);
@@ -715,16 +740,15 @@ __global__ __launch_bounds__(NTW) void k_chunk_output(const float *__restrict__ 
         for (int h2 = 0; h2 < HPS; ++h2) {
 #pragma unroll
             for (int u = 0; u < SPH; ++u) {
-                const int idx = tid + u * NTW;
-                if (idx < DKP * DVP / 4) {
-                    const int r = idx / (DVP / 4), c4 = (idx % (DVP / 4)) * 4;
+                const int r = (int)((unsigned)tid / (DVP / 4)) + u * (NTW / (DVP / 4));
+                const int c4 = (int)((unsigned)tid % (DVP / 4)) * 4;
+                if ((DKP * DVP / 4) % NTW == 0 || r < DKP)
                     *reinterpret_cast<float4 *>(SX + (h2 * DKP + r) * LS + c4) = sbuf[h2][u];
-                }
             }
 #pragma unroll
             for (int u = 0; u < VPH; ++u) {
-                const int idx = tid + u * NTW;
-                const int r = idx / (DVP / 4), c4 = (idx % (DVP / 4)) * 4;
+                const int r = (int)((unsigned)tid / (DVP / 4)) + u * (NTW / (DVP / 4));
+                const int c4 = (int)((unsigned)tid % (DVP / 4)) * 4;
                 *reinterpret_cast<float4 *>(VS + (h2 * CH + r) * LS + c4) = vbuf[h2][u];
             }
         }
@@ -747,7 +771,7 @@ __global__ __launch_bounds__(NTW) void k_chunk_output(const float *__restrict__ 
             regs_to_lds<CH, DKP, NTW, Cfg::QPER, LDK>(tid, qb, SX);
             regs_to_lds<CH, DKP, NTW, Cfg::QPER, LDK>(tid, kb, SX + CH * LDK);
         }
-        __syncthreads();
+        block_sync();
 #pragma unroll
         for (int u = 0; u < NL; ++u) issue(0, tid, u);
 #pragma unroll
@@ -762,7 +786,7 @@ __global__ __launch_bounds__(NTW) void k_chunk_output(const float *__restrict__ 
                 ka[jt][mm] = *reinterpret_cast<const float4 *>(SX + (CH + 32 * jt + cl) * LDK +
                                                                8 * (slot * NQQ + mm) + 4 * kh);
         }
-        __syncthreads();   // Q and K read before the partial sums overwrite them
+        block_sync();   // Q and K read before the partial sums overwrite them
         f32x16 part[2] = {zero16(), zero16()};
 #pragma unroll
         for (int m = 0; m < NQ; ++m) {
@@ -790,7 +814,7 @@ __global__ __launch_bounds__(NTW) void k_chunk_output(const float *__restrict__ 
                         make_float4(part[jt][4 * a], part[jt][4 * a + 1], part[jt][4 * a + 2], part[jt][4 * a + 3]);
             }
         }
-        __syncthreads();
+        block_sync();
 #pragma unroll
         for (int jt = 0; jt < 2; ++jt) {
             kqt[jt] = zero16();
@@ -809,9 +833,9 @@ __global__ __launch_bounds__(NTW) void k_chunk_output(const float *__restrict__ 
                 }
             }
         }
-        __syncthreads();   // partial sums read before S_in overwrites them
+        block_sync();   // partial sums read before S_in overwrites them
         stage(tid);
-        __syncthreads();
+        block_sync();
     }
 
     const int nstep = (hpg + HPS - 1) / HPS;
@@ -904,9 +928,9 @@ __global__ __launch_bounds__(NTW) void k_chunk_output(const float *__restrict__ 
             for (int r = 0; r < 16; ++r)
                 gstore1_nt(yb, base + (uint32_t)(8 * (r / 4) + r % 4) * (uint32_t)(dv * 4), acc[r] + acc2[r]);
         }
-        __syncthreads();   // S_in, V and decay reads done before the next step's writes
+        block_sync();   // S_in, V and decay reads done before the next step's writes
         stage(tid);
-        __syncthreads();
+        block_sync();
     }
 }
 
@@ -1099,7 +1123,7 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
             regs_to_lds<CH, DKP, NTB, QPER, LDQ>(tid, qb, QL);
             regs_to_lds<CH, DKP, NTB, QPER, LDK>(tid, kb, KL);
         }
-        __syncthreads();
+        block_sync();
         // 12 units (tile t, quarter of dk); wave w takes units w, w + 4, w + 8
 #pragma unroll
         for (int uu = 0; uu < 3; ++uu) {
@@ -1121,7 +1145,7 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
                 *reinterpret_cast<float4 *>(X + ((u * 4 + a) * 64 + lane) * 4) =
                     make_float4(acc[4 * a], acc[4 * a + 1], acc[4 * a + 2], acc[4 * a + 3]);
         }
-        __syncthreads();
+        block_sync();
         // sum the four quarters of each tile
         for (int f = tid; f < 3 * 256; f += NTB) {
             const int t = f >> 8, o = (f & 255) * 4;
@@ -1136,11 +1160,11 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
             }
             *reinterpret_cast<float4 *>(QKT + t * 1024 + o) = acc4;
         }
-        __syncthreads();   // partial sums read before the slabs overwrite them
+        block_sync();   // partial sums read before the slabs overwrite them
         fro_next = store_slab(p0, 0, tid);
         if (NKS > 1) fro_next += store_slab(pn, 1, tid);
         stage_b(tid);
-        __syncthreads();
+        block_sync();
     }
 
     f32x16 dacc[NKS];   // dQ^T (dQ side) or dK^T (dK side): state rows 32 ks + row(r), positions 32 rt + i
@@ -1189,7 +1213,7 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
         };
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
-            if (ks > 0) __syncthreads();   // slab ks visible, slab ks - 1 read
+            if (ks > 0) block_sync();   // slab ks visible, slab ks - 1 read
             const float *sS = X + (ks & 1) * 2 * SLN, *sD = sS + SLN;
             // Gv operands (MFMA group g2 contracts slab rows (16 (g2 / 2) + 4 (g2 % 2) + e, + 8))
             const float *kp = KL + (32 * rt + cl) * LDK + 32 * ks + 8 * kh;
@@ -1253,13 +1277,13 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
         if (kh == 0) (grp ? redk : redq)[32 * rt + cl] = rd;
         fro = sum64_hi(fro);
         if (lane == 63) redf[wave] = fro;
-        __syncthreads();   // slabs read
+        block_sync();   // slabs read
         {
             float *dst = X + (grp ? CH * LDY : 0) + (32 * rt + cl) * LDY + 4 * kh;
 #pragma unroll
             for (int m = 0; m < NA; ++m) *reinterpret_cast<float4 *>(dst + 8 * m) = ar[m];
         }
-        __syncthreads();   // dY and V in LDS
+        block_sync();   // dY and V in LDS
 
         // ---- pass 2
         const float *RY = X, *RV = X + CH * LDY;
@@ -1354,14 +1378,14 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
             dyvt(ad, 1, 1, 0, NA, 1);
         }
         load_b(hh + 1, tid);
-        __syncthreads();   // dY and V read
+        block_sync();   // dY and V read
         if (wave == 2) {
 #pragma unroll
             for (int a = 0; a < 4; ++a)
                 *reinterpret_cast<float4 *>(X + (a * 64 + lane) * 4) =
                     make_float4(ad[4 * a], ad[4 * a + 1], ad[4 * a + 2], ad[4 * a + 3]);
         }
-        __syncthreads();   // wave 2's half of tile 0 visible
+        block_sync();   // wave 2's half of tile 0 visible
         float *const DP = X + 1024;   // dP [CH][LDP]
 
         if (wave != 2) {
@@ -1414,7 +1438,7 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
             csum += __shfl_xor(csum, 32);
             if (kh == 0) csm[td][cl] = csum;
         }
-        __syncthreads();   // dP and the reductions visible
+        block_sync();   // dP and the reductions visible
         // the next head's first slabs, in flight over the intra products
         load_slab(p0, hh + 1, 0, tid);
 
@@ -1538,11 +1562,11 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
             gstore1(make_rsrc(dla + bh * T + c * CH, (int64_t)rows * 4), (uint32_t)t * 4u,
                     rr + sq + pk + expf(blh) * frob);
         }
-        __syncthreads();   // dP, dY V^T sums and reductions read; the slab buffers are free
+        block_sync();   // dP, dY V^T sums and reductions read; the slab buffers are free
         fro_next = store_slab(p0, 0, tid);
         if (NKS > 1) fro_next += store_slab(pn, 1, tid);
         stage_b(tid);
-        __syncthreads();
+        block_sync();
     }
 
     // ---- dq, dk: transposed through LDS into [position][dk] rows, stored with
@@ -1557,7 +1581,7 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
                 *reinterpret_cast<float4 *>(o + 32 * ks + 8 * a) =
                     make_float4(dacc[ks][4 * a], dacc[ks][4 * a + 1], dacc[ks][4 * a + 2], dacc[ks][4 * a + 3]);
         }
-        __syncthreads();
+        block_sync();
         if (OFF && (wave == 0 || wave == 3)) {
             // add the tiles taken over from waves 1 (dQ, positions 32 ..) and 2 (dK, positions 0 ..)
             float *ox = X + grp * CH * LDQ + (32 * (1 - rt) + cl) * LDQ + 4 * kh + 32 * (NKS - 1);
@@ -1571,7 +1595,7 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
                 *reinterpret_cast<float4 *>(ox + 8 * a) = y;
             }
         }
-        __syncthreads();
+        block_sync();
         const int64_t tb = (int64_t)rows * dk_ * 4;
         const rsrc_t rq = make_rsrc(dq + (bg * T + c * CH) * dk_, tb), rk = make_rsrc(dk + (bg * T + c * CH) * dk_, tb);
         constexpr int Q4 = DKP / 4;

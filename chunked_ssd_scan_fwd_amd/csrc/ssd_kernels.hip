@@ -1055,9 +1055,8 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
         const bool live = hh < hpg;
         const int64_t off = ((bh0 + (live ? hh : 0)) * NC + c) * Epad;
         const rsrc_t sr = make_rsrc(states + off, live ? E * 4 : 0), dr = make_rsrc(dstates + off, live ? E * 4 : 0);
-        const int idx = tid + u * NTB;
-        const int r = idx / (DVP / 4), c4 = (idx % (DVP / 4)) * 4;
-        const bool ok = idx < 32 * DVP / 4;
+        const int r = f4_row<DVP / 4, NTB>(tid, u), c4 = f4_col<DVP / 4>(tid);
+        const bool ok = (32 * DVP / 4) % NTB == 0 || r < 32;
         p.s[u] = load4(sr, (uint32_t)((32 * ks + r) * dv_), c4, dv_, ok, VEC);
         p.d[u] = load4(dr, (uint32_t)((32 * ks + r) * dv_), c4, dv_, ok, VEC);
     };
@@ -1082,9 +1081,8 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
         float *ds = X + buf * 2 * SLN;
 #pragma unroll
         for (int u = 0; u < SPER; ++u) {
-            const int idx = tid + u * NTB;
-            if (idx < 32 * DVP / 4) {
-                const int r = idx / (DVP / 4), c4 = (idx % (DVP / 4)) * 4;
+            const int r = f4_row<DVP / 4, NTB>(tid, u), c4 = f4_col<DVP / 4>(tid);
+            if ((32 * DVP / 4) % NTB == 0 || r < 32) {
                 *reinterpret_cast<float4 *>(ds + r * LSL + c4) = p.s[u];
                 *reinterpret_cast<float4 *>(ds + SLN + r * LSL + c4) = p.d[u];
                 f += p.s[u].x * p.d[u].x + p.s[u].y * p.d[u].y + p.s[u].z * p.d[u].z + p.s[u].w * p.d[u].w;

@@ -1029,7 +1029,9 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
     const int rows = (int)((T - c * CH) < CH ? (T - c * CH) : CH);
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int grp = wave >> 1, rt = wave & 1;
-    const bool gvw = grp * NCW < NCT;            // owns dV tiles (rt, grp NCW + u)
+    // owns dV tiles (rt, grp NCW + u); every wave does when dv > 32, and a
+    // compile-time true spares the accumulators a zero fill for the other path
+    const bool gvw = NCT >= 2 || grp * NCW < NCT;
     const int64_t E = (int64_t)dk_ * dv_;
 
     struct Slab { float4 s[SPER], d[SPER]; };

@@ -160,6 +160,11 @@ __global__ __launch_bounds__(NTH) void k_chunk_cumsum(const float *__restrict__ 
 
 constexpr int NTW = 512;   // 8 waves per block
 
+template <bool B>
+struct BoolC {
+    static constexpr bool value = B;
+};
+
 // Workgroup barrier across which the compiler may move no memory access.
 // __syncthreads() alone is a fence pair around s_barrier, and this compiler
 // has been seen to sink LDS reads below it into a region that other waves
@@ -1461,28 +1466,35 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
 #pragma unroll
                 for (int ct = 0; ct < NKS; ++ct) kq[buf][ct] = bk[(8 * a + e) * LDK + 32 * ct];
             };
-            xq[0] = *reinterpret_cast<const float4 *>(ap);
-            ldk(0, 0, 0);
+            // the loop is instantiated for both values of `shed`, so that no
+            // branch splits its MFMA stream
+            auto dq_intra = [&](auto shed_c) {
+                constexpr bool SH = decltype(shed_c)::value;
+                xq[0] = *reinterpret_cast<const float4 *>(ap);
+                ldk(0, 0, 0);
 #pragma unroll
-            for (int a = 0; a < 8; ++a) {
-                if (a < na) {
-                    if (a + 1 < na) xq[(a + 1) & 1] = *reinterpret_cast<const float4 *>(ap + 8 * (a + 1));
-                    const float4 x = xq[a & 1];
-                    const float xs[4] = {x.x, x.y, x.z, x.w};
+                for (int a = 0; a < 8; ++a) {
+                    if (a < na) {
+                        if (a + 1 < na) xq[(a + 1) & 1] = *reinterpret_cast<const float4 *>(ap + 8 * (a + 1));
+                        const float4 x = xq[a & 1];
+                        const float xs[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int f = 4 * a + e;
-                        if (e < 3) ldk(a, e + 1, (f + 1) & 1);
-                        else if (a + 1 < na) ldk(a + 1, 0, (f + 1) & 1);
+                        for (int e = 0; e < 4; ++e) {
+                            const int f = 4 * a + e;
+                            if (e < 3) ldk(a, e + 1, (f + 1) & 1);
+                            else if (a + 1 < na) ldk(a + 1, 0, (f + 1) & 1);
 #pragma unroll
-                        for (int ct = 0; ct < NKS; ++ct) {
-                            if (ct < NKS - 1 || !shed) dacc[ct] = mfma32(kq[f & 1][ct], xs[e], dacc[ct]);
+                            for (int ct = 0; ct < NKS; ++ct) {
+                                if (ct < NKS - 1 || !SH) dacc[ct] = mfma32(kq[f & 1][ct], xs[e], dacc[ct]);
+                            }
+                            __builtin_amdgcn_sched_barrier(0);
                         }
-                        __builtin_amdgcn_sched_barrier(0);
                     }
+                    if (a == 1 && NKS > 1) load_slab(pn, hh + 1, 1, tid);
                 }
-                if (a == 1 && NKS > 1) load_slab(pn, hh + 1, 1, tid);
-            }
+            };
+            if (shed) dq_intra(BoolC<true>{});
+            else dq_intra(BoolC<false>{});
             if (OFF && wave == 0) {
                 // dQ^T[NKS - 1, 1] for wave 1
                 const float *ap1 = DP + (32 + cl) * LDP + 4 * kh;
@@ -1511,19 +1523,24 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
 #pragma unroll
                 for (int ct = 0; ct < NKS; ++ct) qv[buf][ct] = bq[i * LDQ + 32 * ct];
             };
-            ldq(16 * rt, 0);
+            auto dk_intra = [&](auto shed_c) {   // instantiated per value of `shed`
+                constexpr bool SH = decltype(shed_c)::value;
+                ldq(16 * rt, 0);
 #pragma unroll
-            for (int f = 0; f < 32; ++f) {
-                if (f >= 16 * rt) {
-                    if (f + 1 < 32) ldq(f + 1, (f + 1) & 1);
+                for (int f = 0; f < 32; ++f) {
+                    if (f >= 16 * rt) {
+                        if (f + 1 < 32) ldq(f + 1, (f + 1) & 1);
 #pragma unroll
-                    for (int ct = 0; ct < NKS; ++ct) {
-                        if (ct < NKS - 1 || !shed) dacc[ct] = mfma32(qv[f & 1][ct], xd[f & 1], dacc[ct]);
+                        for (int ct = 0; ct < NKS; ++ct) {
+                            if (ct < NKS - 1 || !SH) dacc[ct] = mfma32(qv[f & 1][ct], xd[f & 1], dacc[ct]);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                        if (f == 23 && NKS > 1) load_slab(pn, hh + 1, 1, tid);
                     }
-                    __builtin_amdgcn_sched_barrier(0);
-                    if (f == 23 && NKS > 1) load_slab(pn, hh + 1, 1, tid);
                 }
-            }
+            };
+            if (shed) dk_intra(BoolC<true>{});
+            else dk_intra(BoolC<false>{});
             if (OFF && wave == 3) {
                 // dK^T[NKS - 1, 0] for wave 2
                 const float *ap0 = DP + 8 * kh * LDP + cl;

@@ -1451,7 +1451,7 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
         // the work of the others, so with dk > 32 their last 32 state rows are
         // taken by the other wave of the side (wave 0 for wave 1, wave 3 for wave
         // 2), summed over heads in xacc and added at the end.
-        const bool shed = OFF && (wave == 1 || wave == 2);
+        // (the shedding waves are 1 and 2: rt = 1 on the dQ side, rt = 0 on the dK side)
         if (grp == 0) {
             // dQ^T[ct, rt] += K[:, ct]^T dP[rt, :]^T over j < 32 (rt + 1); all tiles
             // interleaved on independent chains
@@ -1459,17 +1459,18 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
             const float *bk = KL + 4 * kh * LDK + cl;
             // operands of step (a, e) are read one step ahead: x for the next a,
             // the K column values for the next e
-            const int na = 4 * (rt + 1);
             float4 xq[2];
             float kq[2][NKS];
             auto ldk = [&](int a, int e, int buf) {
 #pragma unroll
                 for (int ct = 0; ct < NKS; ++ct) kq[buf][ct] = bk[(8 * a + e) * LDK + 32 * ct];
             };
-            // the loop is instantiated for both values of `shed`, so that no
-            // branch splits its MFMA stream
-            auto dq_intra = [&](auto shed_c) {
-                constexpr bool SH = decltype(shed_c)::value;
+            // the loop is instantiated per row block (which also fixes whether
+            // the wave sheds), so that no branch splits its MFMA stream
+            auto dq_intra = [&](auto rt_c) {
+                constexpr int RT = decltype(rt_c)::value ? 1 : 0;
+                constexpr bool SH = OFF && RT == 1;   // sheds its last state block
+                constexpr int na = 4 * (RT + 1);
                 xq[0] = *reinterpret_cast<const float4 *>(ap);
                 ldk(0, 0, 0);
 #pragma unroll
@@ -1493,7 +1494,7 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
                     if (a == 1 && NKS > 1) load_slab(pn, hh + 1, 1, tid);
                 }
             };
-            if (shed) dq_intra(BoolC<true>{});
+            if (rt) dq_intra(BoolC<true>{});
             else dq_intra(BoolC<false>{});
             if (OFF && wave == 0) {
                 // dQ^T[NKS - 1, 1] for wave 1
@@ -1523,12 +1524,13 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
 #pragma unroll
                 for (int ct = 0; ct < NKS; ++ct) qv[buf][ct] = bq[i * LDQ + 32 * ct];
             };
-            auto dk_intra = [&](auto shed_c) {   // instantiated per value of `shed`
-                constexpr bool SH = decltype(shed_c)::value;
-                ldq(16 * rt, 0);
+            auto dk_intra = [&](auto rt_c) {   // instantiated per row block
+                constexpr int RT = decltype(rt_c)::value ? 1 : 0;
+                constexpr bool SH = OFF && RT == 0;   // sheds its last state block
+                ldq(16 * RT, 0);
 #pragma unroll
                 for (int f = 0; f < 32; ++f) {
-                    if (f >= 16 * rt) {
+                    if (f >= 16 * RT) {
                         if (f + 1 < 32) ldq(f + 1, (f + 1) & 1);
 #pragma unroll
                         for (int ct = 0; ct < NKS; ++ct) {
@@ -1539,7 +1541,7 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
                     }
                 }
             };
-            if (shed) dk_intra(BoolC<true>{});
+            if (rt) dk_intra(BoolC<true>{});
             else dk_intra(BoolC<false>{});
             if (OFF && wave == 3) {
                 // dK^T[NKS - 1, 0] for wave 2

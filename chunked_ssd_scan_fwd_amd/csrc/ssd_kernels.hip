@@ -160,6 +160,8 @@ __global__ __launch_bounds__(NTH) void k_chunk_cumsum(const float *__restrict__ 
 
 constexpr int NTW = 512;   // 8 waves per block
 
+constexpr float kLog2e = 1.4426950408889634f;
+
 template <bool B>
 struct BoolC {
     static constexpr bool value = B;
@@ -758,7 +760,7 @@ __global__ __launch_bounds__(NTW) void k_chunk_output(const float *__restrict__ 
             }
         }
         if (wave < HPS) {
-            bs[wave * CH + (tid & 63)] = bpre;
+            bs[wave * CH + (tid & 63)] = bpre * kLog2e;   // exponents base 2
             eb[wave * CH + (tid & 63)] = expf(bpre);
         }
     };
@@ -888,8 +890,12 @@ __global__ __launch_bounds__(NTW) void k_chunk_output(const float *__restrict__ 
         acc2 = zero16();
         // P V: p_ij = (Q K^T)_ij exp(b_i - b_j) for j <= i, exp(-inf) = 0 above
         // the diagonal; the row group's V operands and decays are read ahead.
+        // bs holds b log2(e), so the factor is one exp2; j = 32 jt + 8a + 4kh + e
+        // and i = 32 rt + cl, so j <= i compares the constant 8a + e with a
+        // per-lane bound.
         {
             const int i = 32 * rt + cl;
+            const int dl = cl - 4 * kh;
             const float bi = bsh[i];
             const float *vb = VS + (hs * CH + 4 * kh) * LS + 32 * ct + cl;
 #pragma unroll
@@ -905,13 +911,14 @@ __global__ __launch_bounds__(NTW) void k_chunk_output(const float *__restrict__ 
                     }
                     __builtin_amdgcn_sched_barrier(0);   // all reads issued before the MFMAs
                     float p[16];
+                    const int lim = dl + 32 * (rt - jt);   // j <= i is 8a + e <= lim
 #pragma unroll
                     for (int a = 0; a < 4; ++a) {
                         const float bjs[4] = {bj[a].x, bj[a].y, bj[a].z, bj[a].w};
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
-                            const int j = 32 * jt + 8 * a + 4 * kh + e;
-                            p[4 * a + e] = kqt[jt][4 * a + e] * __expf(j <= i ? bi - bjs[e] : -INFINITY);
+                            const float x = bi - bjs[e];
+                            p[4 * a + e] = kqt[jt][4 * a + e] * __builtin_amdgcn_exp2f(8 * a + e <= lim ? x : -INFINITY);
                         }
                     }
                     __builtin_amdgcn_sched_barrier(0);   // the decay factors before the MFMAs

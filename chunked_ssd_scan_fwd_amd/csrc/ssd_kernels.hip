@@ -160,8 +160,6 @@ __global__ __launch_bounds__(NTH) void k_chunk_cumsum(const float *__restrict__ 
 
 constexpr int NTW = 512;   // 8 waves per block
 
-constexpr float kLog2e = 1.4426950408889634f;
-
 template <bool B>
 struct BoolC {
     static constexpr bool value = B;
@@ -760,7 +758,7 @@ __global__ __launch_bounds__(NTW) void k_chunk_output(const float *__restrict__ 
             }
         }
         if (wave < HPS) {
-            bs[wave * CH + (tid & 63)] = bpre * kLog2e;   // exponents base 2
+            bs[wave * CH + (tid & 63)] = bpre;
             eb[wave * CH + (tid & 63)] = expf(bpre);
         }
     };
@@ -890,9 +888,10 @@ __global__ __launch_bounds__(NTW) void k_chunk_output(const float *__restrict__ 
         acc2 = zero16();
         // P V: p_ij = (Q K^T)_ij exp(b_i - b_j) for j <= i, exp(-inf) = 0 above
         // the diagonal; the row group's V operands and decays are read ahead.
-        // bs holds b log2(e), so the factor is one exp2; j = 32 jt + 8a + 4kh + e
-        // and i = 32 rt + cl, so j <= i compares the constant 8a + e with a
-        // per-lane bound.
+        // j = 32 jt + 8a + 4kh + e and i = 32 rt + cl, so j <= i compares the
+        // constant 8a + e with a per-lane bound.  The decay exponent is the
+        // difference b_i - b_j, taken before any scaling: b log2(e) stored
+        // per position would add a rounding of |b| to every exponent.
         {
             const int i = 32 * rt + cl;
             const int dl = cl - 4 * kh;
@@ -918,7 +917,7 @@ __global__ __launch_bounds__(NTW) void k_chunk_output(const float *__restrict__ 
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const float x = bi - bjs[e];
-                            p[4 * a + e] = kqt[jt][4 * a + e] * __builtin_amdgcn_exp2f(8 * a + e <= lim ? x : -INFINITY);
+                            p[4 * a + e] = kqt[jt][4 * a + e] * __expf(8 * a + e <= lim ? x : -INFINITY);
                         }
                     }
                     __builtin_amdgcn_sched_barrier(0);   // the decay factors before the MFMAs
@@ -1314,22 +1313,22 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
                     gv[u][4 * a + 3] *= e4.w;
                 }
             }
+            // j = 32 rt + cl, i = 32 it + 8a + 4kh + e: j <= i is 8a + e >= lim
             const int j = 32 * rt + cl;
             const float bj = bs[j];
 #pragma unroll
             for (int it = 0; it < 2; ++it) {
                 if (it >= rt) {
                     float p[16];
+                    const int lim = cl - 4 * kh + 32 * (rt - it);
 #pragma unroll
                     for (int a = 0; a < 4; ++a) {
                         const float4 k4 = qkt4(it + rt, a, lane);
                         const float4 b4 = *reinterpret_cast<const float4 *>(bs + 32 * it + 8 * a + 4 * kh);
                         const float ks4[4] = {k4.x, k4.y, k4.z, k4.w}, bis[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int i = 32 * it + 8 * a + 4 * kh + e;
-                            p[4 * a + e] = ks4[e] * __expf(j <= i ? bis[e] - bj : -INFINITY);
-                        }
+                        for (int e = 0; e < 4; ++e)
+                            p[4 * a + e] = ks4[e] * __expf(8 * a + e >= lim ? bis[e] - bj : -INFINITY);
                     }
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
@@ -1417,6 +1416,7 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
             }
             const int j = 32 * jt + cl;
             const float bj = bs[j];
+            const int lim = cl - 4 * kh + 32 * (jt - it);   // j <= i is 8a + e >= lim
             float ms[16], csum = 0.f;
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
@@ -1426,10 +1426,10 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = 4 * a + e, i = 32 * it + 8 * a + 4 * kh + e;
-                    const float d = __expf(j <= i ? bis[e] - bj : -INFINITY);
+                    const float d = __expf(8 * a + e >= lim ? bis[e] - bj : -INFINITY);
                     const float dp = ad[r] * d;
                     DP[i * LDP + j] = dp;
-                    ms[r] = (j < i) ? ks4[e] * dp : 0.f;   // (Q K^T) o D o (dY V^T)
+                    ms[r] = (8 * a + e > lim) ? ks4[e] * dp : 0.f;   // (Q K^T) o D o (dY V^T), j < i
                     csum += ms[r];
                 }
             }

@@ -176,6 +176,20 @@ def test_strong_decay():
     check_bwd(x)
 
 
+def test_large_within_chunk_exponents():
+    """Decay steady at log_alpha = -3: the cumulative exponents reach -192
+    inside a chunk while neighbouring positions still weigh e^-3. Rounding b
+    itself (b log2(e) stored per position, say) instead of the difference
+    b_i - b_j shows up here, in dlog_alpha first."""
+    need_gpu()
+    s = Shape(1, 1, 2, 130, 64, 64)
+    x = make_inputs(s, 6)
+    x["log_alpha"][:] = -3.0
+    say("steady decay -3")
+    check_fwd(x)
+    check_bwd(x)
+
+
 def test_group_replication_matches():
     """Replicating q, k to one group per head gives the grouped result."""
     need_gpu()

@@ -251,9 +251,11 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    def timed(fn, K, kernels=()):
-        """K calls of fn between step events; `kernels` (names, or None for all)
-        are timed per launch with events bound to their dispatches."""
+    def timed(fn, K, kernels=(), per_step=True):
+        """K calls of fn between two events, with an event after every call
+        when `per_step` (each is a marker packet on the stream, a few
+        microseconds of stream time); `kernels` (names, or None for all) are
+        timed per launch with events bound to their dispatches."""
         with_kernels = kernels is None or len(kernels) > 0
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
         torch.cuda.synchronize()
@@ -263,12 +265,13 @@ def main():
         evs[0].record()
         for i in range(K):
             fn()
-            evs[i + 1].record()
+            if per_step or i == K - 1:
+                evs[i + 1].record()
         torch.cuda.synchronize()
         wall = (time.perf_counter() - wall0) * 1e3
         if with_kernels:
             kt.__exit__(None, None, None)
-        per = [evs[i].elapsed_time(evs[i + 1]) for i in range(K)]
+        per = [evs[i].elapsed_time(evs[i + 1]) for i in range(K)] if per_step else []
         total = evs[0].elapsed_time(evs[K])
         return total / K, per, wall / K, (kt.results if with_kernels else None)
 
@@ -279,9 +282,12 @@ def main():
     # time, so the headline region below times the dominant kernel only.
     _, _, _, kern_all = timed(step, K, kernels=None)
     dom = max((n for n in kern_all if kern_all[n][1]), key=lambda n: kern_all[n][0])
-    # Timed region: exactly K steps; the dominant kernel's launches carry HIP
-    # events on the launch stream, for its roofline.
-    step_ms, per_step, wall_ms, kern_dom = timed(step, K, kernels=[dom])
+    # Timed region: exactly K steps between two events; the dominant kernel's
+    # launches carry HIP events on the launch stream, for its roofline.
+    step_ms, _, wall_ms, kern_dom = timed(step, K, kernels=[dom], per_step=False)
+    # The per-step distribution (median, quartiles) comes from a pass of its
+    # own with an event after every step.
+    _, per_step, _, _ = timed(step, K)
     fwd_ms, fwd_per, _, _ = timed(fwd, K)
     bwd_ms, bwd_per, _, _ = timed(bwd, K)
 

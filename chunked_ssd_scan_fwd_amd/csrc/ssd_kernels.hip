@@ -1338,12 +1338,28 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
                         for (int e = 0; e < 4; ++e)
                             p[4 * a + e] = ks4[e] * __expf(8 * a + e >= lim ? bis[e] - bj : -INFINITY);
                     }
+                    // dY operands four registers (one group) ahead of their MFMAs,
+                    // so no MFMA waits on the LDS read just issued before it
+                    float yb[2][4][NCW];
+                    auto ldy = [&](int g4, int buf) {
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int i = 32 * it + acc_row(r, lane);
+                        for (int rr = 0; rr < 4; ++rr) {
+                            const int i = 32 * it + acc_row(4 * g4 + rr, lane);
 #pragma unroll
-                        for (int u = 0; u < NCW; ++u)
-                            gv[u] = mfma32(p[r], RY[i * LDY + 32 * (grp * NCW + u) + cl], gv[u]);
+                            for (int u = 0; u < NCW; ++u) yb[buf][rr][u] = RY[i * LDY + 32 * (grp * NCW + u) + cl];
+                        }
+                    };
+                    ldy(0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int g4 = 0; g4 < 4; ++g4) {
+                        if (g4 + 1 < 4) ldy(g4 + 1, (g4 + 1) & 1);
+#pragma unroll
+                        for (int rr = 0; rr < 4; ++rr) {
+#pragma unroll
+                            for (int u = 0; u < NCW; ++u) gv[u] = mfma32(p[4 * g4 + rr], yb[g4 & 1][rr][u], gv[u]);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
                     }
                 }
             }

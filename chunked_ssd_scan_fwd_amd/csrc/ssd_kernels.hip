@@ -864,15 +864,15 @@ __global__ __launch_bounds__(NTW) void k_chunk_output(const float *__restrict__ 
             {
                 const float *sb = SX + (hs * DKP + 4 * kh) * LS + 32 * ct + cl;
                 float bq[2][4];
-    #pragma unroll
+#pragma unroll
                 for (int s = 0; s < 4; ++s) bq[0][s] = sb[s * LS];
-    #pragma unroll
+#pragma unroll
                 for (int m = 0; m < NQ; ++m) {
                     if (m + 1 < NQ) {
-    #pragma unroll
+#pragma unroll
                         for (int s = 0; s < 4; ++s) bq[(m + 1) & 1][s] = sb[(8 * (m + 1) + s) * LS];
                     }
-    #pragma unroll
+#pragma unroll
                     for (int u = m * NL / NQ; u < (m + 1) * NL / NQ; ++u) issue(st + 1, tid, u);
                     acc = mfma32(qa[m].x, bq[m & 1][0], acc);
                     acc2 = mfma32(qa[m].y, bq[m & 1][1], acc2);
@@ -882,7 +882,7 @@ __global__ __launch_bounds__(NTW) void k_chunk_output(const float *__restrict__ 
                 }
             }
             const float *bsh = bs + hs * CH, *ebh = eb + hs * CH;
-    #pragma unroll
+#pragma unroll
             for (int a = 0; a < 4; ++a) {
                 const float4 e = *reinterpret_cast<const float4 *>(ebh + 32 * rt + 8 * a + 4 * kh);
                 acc[4 * a] = (acc[4 * a] + acc2[4 * a]) * e.x;
@@ -890,7 +890,6 @@ __global__ __launch_bounds__(NTW) void k_chunk_output(const float *__restrict__ 
                 acc[4 * a + 2] = (acc[4 * a + 2] + acc2[4 * a + 2]) * e.z;
                 acc[4 * a + 3] = (acc[4 * a + 3] + acc2[4 * a + 3]) * e.w;
             }
-            acc2 = zero16();
             // P V: p_ij = (Q K^T)_ij exp(b_i - b_j) for j <= i, exp(-inf) = 0 above
             // the diagonal; the row group's V operands and decays are read ahead.
             // j = 32 jt + 8a + 4kh + e and i = 32 rt + cl, so j <= i compares the
@@ -902,35 +901,34 @@ __global__ __launch_bounds__(NTW) void k_chunk_output(const float *__restrict__ 
                 const int dl = cl - 4 * kh;
                 const float bi = bsh[i];
                 const float *vb = VS + (hs * CH + 4 * kh) * LS + 32 * ct + cl;
-    #pragma unroll
+#pragma unroll
                 for (int jt = 0; jt < 2; ++jt) {
                     if (jt <= rt) {
                         float bv[16];
                         float4 bj[4];
-    #pragma unroll
+#pragma unroll
                         for (int a = 0; a < 4; ++a) {
                             bj[a] = *reinterpret_cast<const float4 *>(bsh + 32 * jt + 8 * a + 4 * kh);
-    #pragma unroll
+#pragma unroll
                             for (int e = 0; e < 4; ++e) bv[4 * a + e] = vb[(32 * jt + 8 * a + e) * LS];
                         }
                         __builtin_amdgcn_sched_barrier(0);   // all reads issued before the MFMAs
                         float p[16];
                         const int lim = dl + 32 * (rt - jt);   // j <= i is 8a + e <= lim
-    #pragma unroll
+#pragma unroll
                         for (int a = 0; a < 4; ++a) {
                             const float bjs[4] = {bj[a].x, bj[a].y, bj[a].z, bj[a].w};
-    #pragma unroll
+#pragma unroll
                             for (int e = 0; e < 4; ++e) {
                                 const float x = bi - bjs[e];
                                 p[4 * a + e] = kqt[jt][4 * a + e] * __expf(8 * a + e <= lim ? x : -INFINITY);
                             }
                         }
                         __builtin_amdgcn_sched_barrier(0);   // the decay factors before the MFMAs
-    #pragma unroll
-                        for (int r = 0; r < 16; r += 2) {
-                            acc = mfma32(p[r], bv[r], acc);
-                            acc2 = mfma32(p[r + 1], bv[r + 1], acc2);
-                        }
+                        // one accumulator: the other wave of the SIMD issues its
+                        // MFMAs meanwhile, and y needs no final sum of two
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) acc = mfma32(p[r], bv[r], acc);
                     }
                 }
             }
@@ -940,9 +938,9 @@ __global__ __launch_bounds__(NTW) void k_chunk_output(const float *__restrict__ 
                 // row 32 rt + acc_row(r, lane): the lane's offset plus a uniform
                 // one per register (rows past the sequence end fall outside yb)
                 const uint32_t base = n < dv ? (uint32_t)((32 * rt + 4 * kh) * dv + n) * 4u : kOOB;
-    #pragma unroll
+#pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    gstore1_nt(yb, base + (uint32_t)(8 * (r / 4) + r % 4) * (uint32_t)(dv * 4), acc[r] + acc2[r]);
+                    gstore1_nt(yb, base + (uint32_t)(8 * (r / 4) + r % 4) * (uint32_t)(dv * 4), acc[r]);
             }
             block_sync();   // S_in, V and decay reads done before the next step's writes
             stage(tid);

@@ -858,9 +858,10 @@ __global__ __launch_bounds__(NTW) void k_chunk_output(const float *__restrict__ 
             const bool live = hh < hpg;
             const int64_t bh = bh0 + (live ? hh : 0);
 
-            // Q S_in; MFMA group m issues the next step's loads [m NL / NQ, (m + 1) NL / NQ)
-            // two accumulators, so that one wave alone issues MFMAs back to back
-            f32x16 acc = zero16(), acc2 = zero16();
+            // Q S_in; MFMA group m issues the next step's loads [m NL / NQ, (m + 1) NL / NQ).
+            // One accumulator chain: the other wave of the SIMD issues its
+            // MFMAs meanwhile (two chains measured slower by the adds they need).
+            f32x16 acc = zero16();
             {
                 const float *sb = SX + (hs * DKP + 4 * kh) * LS + 32 * ct + cl;
                 float bq[2][4];
@@ -875,9 +876,9 @@ __global__ __launch_bounds__(NTW) void k_chunk_output(const float *__restrict__ 
 #pragma unroll
                     for (int u = m * NL / NQ; u < (m + 1) * NL / NQ; ++u) issue(st + 1, tid, u);
                     acc = mfma32(qa[m].x, bq[m & 1][0], acc);
-                    acc2 = mfma32(qa[m].y, bq[m & 1][1], acc2);
+                    acc = mfma32(qa[m].y, bq[m & 1][1], acc);
                     acc = mfma32(qa[m].z, bq[m & 1][2], acc);
-                    acc2 = mfma32(qa[m].w, bq[m & 1][3], acc2);
+                    acc = mfma32(qa[m].w, bq[m & 1][3], acc);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
@@ -885,10 +886,10 @@ __global__ __launch_bounds__(NTW) void k_chunk_output(const float *__restrict__ 
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
                 const float4 e = *reinterpret_cast<const float4 *>(ebh + 32 * rt + 8 * a + 4 * kh);
-                acc[4 * a] = (acc[4 * a] + acc2[4 * a]) * e.x;
-                acc[4 * a + 1] = (acc[4 * a + 1] + acc2[4 * a + 1]) * e.y;
-                acc[4 * a + 2] = (acc[4 * a + 2] + acc2[4 * a + 2]) * e.z;
-                acc[4 * a + 3] = (acc[4 * a + 3] + acc2[4 * a + 3]) * e.w;
+                acc[4 * a] *= e.x;
+                acc[4 * a + 1] *= e.y;
+                acc[4 * a + 2] *= e.z;
+                acc[4 * a + 3] *= e.w;
             }
             // P V: p_ij = (Q K^T)_ij exp(b_i - b_j) for j <= i, exp(-inf) = 0 above
             // the diagonal; the row group's V operands and decays are read ahead.
@@ -925,8 +926,6 @@ __global__ __launch_bounds__(NTW) void k_chunk_output(const float *__restrict__ 
                             }
                         }
                         __builtin_amdgcn_sched_barrier(0);   // the decay factors before the MFMAs
-                        // one accumulator: the other wave of the SIMD issues its
-                        // MFMAs meanwhile, and y needs no final sum of two
 #pragma unroll
                         for (int r = 0; r < 16; ++r) acc = mfma32(p[r], bv[r], acc);
                     }

@@ -1078,6 +1078,14 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
         p.s[u] = load4(sr, (uint32_t)((32 * ks + r) * dv_), c4, dv_, ok, VEC);
         p.d[u] = load4(dr, (uint32_t)((32 * ks + r) * dv_), c4, dv_, ok, VEC);
     };
+    // The next head's slabs 0 and 1 are loaded during the intra products, one
+    // float4 of each state per MFMA step (step s: slab 0's float4 s, then slab
+    // 1's), so that the loads of the four waves do not queue up in one burst.
+    static_assert(2 * SPER <= 16, "the shortest intra loop has 16 steps");
+    auto spread_ld = [&](int hh, int tid, int s) {
+        if (s < SPER) load_slab1(p0, hh, 0, tid, s);
+        else if (NKS > 1 && s < 2 * SPER) load_slab1(pn, hh, 1, tid, s - SPER);
+    };
     auto load_slab = [&](Slab &p, int hh, int ks, int tid) {
 #pragma unroll
         for (int u = 0; u < SPER; ++u) load_slab1(p, hh, ks, tid, u);
@@ -1472,8 +1480,6 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
             if (kh == 0) csm[td][cl] = csum;
         }
         block_sync();   // dP and the reductions visible
-        // the next head's first slabs, in flight over the intra products
-        load_slab(p0, hh + 1, 0, tid);
 
         // Intra products.  The row blocks rt = 1 (dQ) and rt = 0 (dK) have twice
         // the work of the others, so with dk > 32 their last 32 state rows are
@@ -1516,10 +1522,10 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
                             for (int ct = 0; ct < NKS; ++ct) {
                                 if (ct < NKS - 1 || !SH) dacc[ct] = mfma32(kq[f & 1][ct], xs[e], dacc[ct]);
                             }
+                            spread_ld(hh + 1, tid, f);
                             __builtin_amdgcn_sched_barrier(0);
                         }
                     }
-                    if (a == 1 && NKS > 1) load_slab(pn, hh + 1, 1, tid);
                 }
             };
             if (rt) dq_intra(BoolC<true>{});
@@ -1564,8 +1570,8 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
                         for (int ct = 0; ct < NKS; ++ct) {
                             if (ct < NKS - 1 || !SH) dacc[ct] = mfma32(qv[f & 1][ct], xd[f & 1], dacc[ct]);
                         }
+                        spread_ld(hh + 1, tid, f - 16 * RT);
                         __builtin_amdgcn_sched_barrier(0);
-                        if (f == 23 && NKS > 1) load_slab(pn, hh + 1, 1, tid);
                     }
                 }
             };

@@ -9,6 +9,9 @@ seeded synthetic inputs resident in HBM.  Prints one JSON line.
                                       # reference kernel for scaling HBM counters
     python bench.py --max-len         # T-doubling search: the longest sequence whose
                                       # fwd_bwd fits in HBM at g2h8_d128, B=4
+    python bench.py --grid            # fwd and fwd_bwd at every shape of the pages'
+                                      # grid (4 shapes x T in 512, 2048, 8192), one
+                                      # JSON line per shape
 
 Throughput (`value`) is the nominal fwd+bwd FLOP count of the step divided
 by the measured step time.  Nominal FLOPs per (token, head), with chunk
@@ -35,6 +38,18 @@ C_NOM = 64
 # The benchmark pages' JAX "chunked" fwd_bwd at this workload on an RTX 3090
 # (kernel_ssd_gpu.json, record chunked·fwd_bwd·g2h8_d128·T8192, median_ms).
 PAGE_FWD_BWD_MS = 11.883384999237023
+# The same page's chunked path over its whole grid, (fwd, fwd_bwd) median ms on
+# the RTX 3090: context for --grid, not a target.
+PAGE_CHUNKED_MS = {
+    ("g2h8_d128", 512): (0.332, 0.901), ("g2h8_d128", 2048): (1.170, 3.210),
+    ("g2h8_d128", 8192): (4.182, 11.883),
+    ("g1h24_dk128_dv64", 512): (0.258, 0.725), ("g1h24_dk128_dv64", 2048): (0.943, 2.632),
+    ("g1h24_dk128_dv64", 8192): (3.461, 10.695),
+    ("g1h1_d128", 512): (0.0890, 0.252), ("g1h1_d128", 2048): (0.284, 0.656),
+    ("g1h1_d128", 8192): (0.909, 2.439),
+    ("g2h4_dk48_dv40", 512): (0.112, 0.296), ("g2h4_dk48_dv40", 2048): (0.371, 0.968),
+    ("g2h4_dk48_dv40", 8192): (1.448, 3.736),
+}
 
 
 def nominal_flops(s):
@@ -179,6 +194,59 @@ def max_len_search(args, torch, ssd):
                       "runs": runs, "stopped_at": stop, "data": "synthetic, drawn on the device"}), flush=True)
 
 
+def grid_sweep(args, torch, ssd):
+    """fwd and fwd_bwd at every shape of the pages' grid: median ms over
+    `--steps` calls (events after every call), nominal TFLOP/s, GB/s of the
+    inputs and outputs, and the fraction of the step roofline (the larger of
+    the nominal FLOPs at the fp32 MFMA peak and those bytes at the HBM peak).
+    Inputs follow the synthetic recipe (mu = -4 for the 24-head shape)."""
+    import numpy as np
+    from ssd_workload import PAGE_GRID, make_inputs
+    for i, ((name, T), s) in enumerate(PAGE_GRID.items()):
+        x = make_inputs(s, 2000 + i, mu=-4.0 if name.startswith("g1h24") else -2.0)
+        d = {k: torch.from_numpy(v).to("cuda") for k, v in x.items()}
+        sa = ssd.ShapeArg(s.B, s.G, s.H, s.T, s.dk, s.dv)
+        ws = torch.empty(ssd.workspace_size(sa, True), dtype=torch.uint8, device="cuda")
+        y = torch.empty((s.B, s.H, s.T, s.dv), device="cuda")
+        grads = (torch.empty((s.B, s.G, s.T, s.dk), device="cuda"), torch.empty((s.B, s.G, s.T, s.dk), device="cuda"),
+                 torch.empty((s.B, s.H, s.T, s.dv), device="cuda"), torch.empty((s.B, s.H, s.T), device="cuda"),
+                 torch.empty((s.B, s.H, s.dk, s.dv), device="cuda"))
+
+        def fwd():
+            ssd.fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["h0"], out=y, workspace=ws)
+
+        def step():
+            fwd()
+            ssd.bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["h0"], d["dy"], out=grads, workspace=ws)
+
+        def med_ms(fn):
+            for _ in range(args.warmup):
+                fn()
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+            torch.cuda.synchronize()
+            evs[0].record()
+            for j in range(args.steps):
+                fn()
+                evs[j + 1].record()
+            torch.cuda.synchronize()
+            return float(np.median([evs[j].elapsed_time(evs[j + 1]) for j in range(args.steps)]))
+
+        f_fwd, f_bwd = nominal_flops(s)
+        b_fwd, b_fb = io_bytes(s)
+        out = {"workload": f"{name}_T{T}", "shape": {"B": s.B, "G": s.G, "H": s.H, "T": s.T, "dk": s.dk, "dv": s.dv}}
+        for key, fn, fl, by in (("fwd", fwd, f_fwd, b_fwd), ("fwd_bwd", step, f_fwd + f_bwd, b_fb)):
+            ms = med_ms(fn)
+            out[key] = {"median_ms": ms, "tflops": fl / (ms * 1e-3) / 1e12, "gbps_io": by / (ms * 1e-3) / 1e9,
+                        "roofline_frac": max(fl / PEAK_FP32_MFMA, by / PEAK_HBM) / (ms * 1e-3)}
+        pf, pfb = PAGE_CHUNKED_MS[(name, T)]
+        out["page_chunked_rtx3090_ms"] = {"fwd": pf, "fwd_bwd": pfb}
+        out["dtype"] = "f32"
+        out["data"] = "synthetic"
+        print(json.dumps(out), flush=True)
+        del d, ws, y, grads
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -195,6 +263,8 @@ def main():
     ap.add_argument("--max-len", action="store_true",
                     help="only run the T-doubling maximum-length search for fwd_bwd and exit")
     ap.add_argument("--max-len-cap", type=int, default=1 << 22, help="largest T the search tries")
+    ap.add_argument("--grid", action="store_true",
+                    help="only time fwd and fwd_bwd at every shape of the pages' grid, one JSON line each, and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -220,6 +290,9 @@ def main():
         return
     if args.max_len:
         max_len_search(args, torch, ssd)
+        return
+    if args.grid:
+        grid_sweep(args, torch, ssd)
         return
     w = workload(args.workload)
     s = w.shape

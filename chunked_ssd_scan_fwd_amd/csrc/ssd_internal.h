@@ -11,6 +11,7 @@ namespace ssd {
 
 constexpr int kChunk = SSD_CHUNK;   // steps per chunk = wavefront width
 constexpr int64_t kMaxDim = 128;    // largest supported dk / dv
+constexpr int kNumCUs = 256;        // MI355X compute units
 
 struct Layout {
     int64_t NC = 0;      // chunks per sequence, ceil(T / 64)
@@ -18,7 +19,20 @@ struct Layout {
     int64_t E = 0;       // dk * dv
     int64_t Epad = 0;    // E rounded up to a multiple of 64 (slab stride, floats)
     size_t off[5] = {0, 0, 0, 0, 0};   // bcum, bl, states, dstates, total bytes
+    // The output and gradient kernels take one block per (b, g, chunk) and loop
+    // over the group's heads.  With fewer such blocks than CUs a group's heads
+    // are split over `hsplit` blocks of `hpb` heads each (the last may hold
+    // fewer); the gradient kernel then writes per-split partial sums of dq and
+    // dk, [2][hsplit][nqk_pad] floats at byte offset part_off, which a small
+    // kernel adds up in split order.
+    int hsplit = 1;
+    int hpb = 1;
+    int64_t nqk_pad = 0;     // B*G*T*dk rounded up to a multiple of 64
+    size_t part_off = 0;
 };
+
+// Heads per block and number of splits for a shape (see Layout).
+void head_split(const ssd_shape *s, int64_t NC, int *hsplit, int *hpb);
 
 // SSD_OK, SSD_ERR_NULL (shape == NULL), SSD_ERR_SHAPE or SSD_ERR_UNSUPPORTED.
 int check_shape(const ssd_shape *s);

@@ -384,7 +384,6 @@ __device__ __forceinline__ int cc_tile(int wave, int u) { return u == 0 ? wave :
 // tiles are shared through that XCD's L2.
 constexpr int TI = 32;
 constexpr int NTS = 512;        // 4 compute + 4 loader waves
-constexpr int kNumCUs = 256;    // MI355X compute units
 
 template <int DKP, int DVP, bool VEC, int TJ, int CPS, bool EXD>
 __global__ __launch_bounds__(NTS) void k_state_scan(
@@ -680,7 +679,7 @@ __global__ __launch_bounds__(NTW) void k_chunk_output(const float *__restrict__ 
                                                       const float *__restrict__ v, const float *__restrict__ bcum,
                                                       const float *__restrict__ states, float *__restrict__ y,
                                                       int G, int H, int64_t T, int dk, int dv, int64_t NC,
-                                                      int64_t Epad)
+                                                      int64_t Epad, int hpb)
 {
     using Cfg = OutCfg<DKP, DVP>;
     if constexpr (EXD) {   // dk == DKP, dv == DVP: index arithmetic on constants
@@ -696,12 +695,16 @@ __global__ __launch_bounds__(NTW) void k_chunk_output(const float *__restrict__ 
     __shared__ __attribute__((aligned(16))) float bs[HPS * CH];
     __shared__ __attribute__((aligned(16))) float eb[HPS * CH];
 
+    // block ((b G + g) nsplit + split) NC + c takes heads [split hpb, split hpb + hpg) of group g
+    const int hpg_all = H / G, nsplit = (hpg_all + hpb - 1) / hpb;
     const int64_t c = blockIdx.x % NC;
-    const int64_t bg = blockIdx.x / NC;
+    const int64_t bgs = blockIdx.x / NC;
+    const int split = (int)(bgs % nsplit);
+    const int64_t bg = bgs / nsplit;
     const int g = (int)(bg % G);
     const int64_t b = bg / G;
-    const int hpg = H / G;
-    const int64_t bh0 = b * H + (int64_t)g * hpg;
+    const int hpg = min(hpb, hpg_all - split * hpb);   // heads of this block
+    const int64_t bh0 = b * H + (int64_t)g * hpg_all + (int64_t)split * hpb;
     const int rows = (int)((T - c * CH) < CH ? (T - c * CH) : CH);
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int rt = wave >> 2, slot = wave & 3;
@@ -1017,7 +1020,7 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
     const float *__restrict__ dy, const float *__restrict__ bcum, const float *__restrict__ bl,
     const float *__restrict__ states, const float *__restrict__ dstates, float *__restrict__ dq,
     float *__restrict__ dk, float *__restrict__ dv, float *__restrict__ dla, int G, int H, int64_t T, int dk_,
-    int dv_, int64_t NC, int64_t NCp, int64_t Epad)
+    int dv_, int64_t NC, int64_t NCp, int64_t Epad, int hpb, int64_t pstride)
 {
     using Cfg = BwdCfg<DKP, DVP>;
     if constexpr (EXD) {   // dk == DKP, dv == DVP: index arithmetic on constants
@@ -1036,12 +1039,19 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
     __shared__ __attribute__((aligned(16))) float bs[CH], eb[CH], el[CH];
     __shared__ float redq[CH], redk[CH], rsm[3][32], csm[3][32], redf[NTB / 64], sfx[CH];
 
+    // block ((b G + g) nsplit + split) NC + c takes heads [split hpb, split hpb + hpg) of group g
+    const int hpg_all = H / G, nsplit = (hpg_all + hpb - 1) / hpb;
     const int64_t c = blockIdx.x % NC;
-    const int64_t bg = blockIdx.x / NC;
+    const int64_t bgs = blockIdx.x / NC;
+    const int split = (int)(bgs % nsplit);
+    const int64_t bg = bgs / nsplit;
     const int g = (int)(bg % G);
     const int64_t b = bg / G;
-    const int hpg = H / G;
-    const int64_t bh0 = b * H + (int64_t)g * hpg;
+    const int hpg = min(hpb, hpg_all - split * hpb);   // heads of this block
+    const int64_t bh0 = b * H + (int64_t)g * hpg_all + (int64_t)split * hpb;
+    // dq and dk: the split's partial sums over its heads (pstride = 0 without a split)
+    dq += split * pstride;
+    dk += split * pstride;
     const int rows = (int)((T - c * CH) < CH ? (T - c * CH) : CH);
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int grp = wave >> 1, rt = wave & 1;
@@ -1678,6 +1688,18 @@ __global__ __launch_bounds__(NTH) void k_zero(float *__restrict__ p, int64_t n)
     if (i < n) p[i] = 0.f;
 }
 
+// dq or dk of a split gradient launch: out[i] = sum over the ns splits of
+// parts[j * stride + i], added in split order.
+__global__ __launch_bounds__(NTH) void k_sum_splits(float *__restrict__ out, const float *__restrict__ parts, int ns,
+                                                    int64_t stride, int64_t n)
+{
+    for (int64_t i = (int64_t)blockIdx.x * NTH + threadIdx.x; i < n; i += (int64_t)gridDim.x * NTH) {
+        float acc = parts[i];
+        for (int j = 1; j < ns; ++j) acc += parts[j * stride + i];
+        out[i] = acc;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Kernel timing (optional, process-global).
 
@@ -1793,6 +1815,7 @@ struct Problem {
     bool vec;     // dk and dv multiples of 4: 16-byte loads
     bool exact;   // dk == DKP and dv == DVP: the kernels' index arithmetic on constants
     float *bcum, *bl, *states, *dstates;
+    float *parts;   // split partial sums of dq, dk (backward with hsplit > 1), else null
 };
 
 static int launch_status()
@@ -1861,6 +1884,7 @@ static int prepare(const ssd_shape *shape, bool backward, void *ws, size_t ws_by
     P->bl = reinterpret_cast<float *>(w + P->L.off[1]);
     P->states = reinterpret_cast<float *>(w + P->L.off[2]);
     P->dstates = backward ? reinterpret_cast<float *>(w + P->L.off[3]) : nullptr;
+    P->parts = backward && P->L.hsplit > 1 ? reinterpret_cast<float *>(w + P->L.part_off) : nullptr;
     return SSD_OK;
 }
 
@@ -1889,9 +1913,9 @@ int ssd_fwd(const ssd_shape *shape, const float *q, const float *k, const float 
 
     rc = run_scan(P, 1, true, q, k, v, nullptr, log_alpha, h0, nullptr, st);
     if (rc != SSD_OK) return rc;
-    SSD_DISPATCH(P, launch(KID_OUTPUT, k_chunk_output<KP, VP, VE, EXD>, dim3((unsigned)(s.B * s.G * P.L.NC)),
-                           dim3(NTW), st, q, k, v, P.bcum, P.states, y, (int)s.G, (int)s.H, s.T, (int)s.dk,
-                           (int)s.dv, P.L.NC, P.L.Epad));
+    SSD_DISPATCH(P, launch(KID_OUTPUT, k_chunk_output<KP, VP, VE, EXD>,
+                           dim3((unsigned)(s.B * s.G * P.L.hsplit * P.L.NC)), dim3(NTW), st, q, k, v, P.bcum,
+                           P.states, y, (int)s.G, (int)s.H, s.T, (int)s.dk, (int)s.dv, P.L.NC, P.L.Epad, P.L.hpb));
     return launch_status();
 }
 
@@ -1931,9 +1955,23 @@ static int bwd_impl(const ssd_shape *shape, const float *q, const float *k, cons
     // and S_in (forward), in the same launch.
     rc = run_scan(P, reuse ? 2 : 3, !reuse, q, k, v, dy, log_alpha, h0, dh0, st);
     if (rc != SSD_OK) return rc;
-    SSD_DISPATCH(P, launch(KID_GRADS, k_bwd_grads<KP, VP, VE, EXD>, dim3((unsigned)(s.B * s.G * P.L.NC)), dim3(NTB),
-                           st, q, k, v, dy, P.bcum, P.bl, P.states, P.dstates, dq, dk, dv, dlog_alpha, (int)s.G,
-                           (int)s.H, s.T, (int)s.dk, (int)s.dv, P.L.NC, P.L.NCp, P.L.Epad));
+    // With a head split the gradient kernel writes each split's dq and dk
+    // partial sums to the workspace, and k_sum_splits adds them up.
+    const int hs = P.L.hsplit;
+    const int64_t nqk = s.B * s.G * s.T * s.dk;
+    float *pq = hs > 1 ? P.parts : dq, *pk = hs > 1 ? P.parts + hs * P.L.nqk_pad : dk;
+    const int64_t pstride = hs > 1 ? P.L.nqk_pad : 0;
+    SSD_DISPATCH(P, launch(KID_GRADS, k_bwd_grads<KP, VP, VE, EXD>, dim3((unsigned)(s.B * s.G * hs * P.L.NC)),
+                           dim3(NTB), st, q, k, v, dy, P.bcum, P.bl, P.states, P.dstates, pq, pk, dv, dlog_alpha,
+                           (int)s.G, (int)s.H, s.T, (int)s.dk, (int)s.dv, P.L.NC, P.L.NCp, P.L.Epad, P.L.hpb,
+                           pstride));
+    if (hs > 1) {
+        if (launch_status() != SSD_OK) return SSD_ERR_DEVICE;
+        const int64_t nb = (nqk + NTH - 1) / NTH;
+        const dim3 grid((unsigned)(nb < 4096 ? nb : 4096));
+        launch(-1, k_sum_splits, grid, dim3(NTH), st, dq, (const float *)pq, hs, pstride, nqk);
+        launch(-1, k_sum_splits, grid, dim3(NTH), st, dk, (const float *)pk, hs, pstride, nqk);
+    }
     return launch_status();
 }
 }  // namespace ssd

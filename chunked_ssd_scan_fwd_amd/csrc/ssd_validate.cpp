@@ -29,6 +29,17 @@ int check_shape(const ssd_shape *s)
 
 static size_t round_up(size_t x, size_t m) { return (x + m - 1) / m * m; }
 
+void head_split(const ssd_shape *s, int64_t NC, int *hsplit, int *hpb)
+{
+    const int64_t hpg = s->H / s->G, blocks = s->B * s->G * NC;
+    int64_t want = 1;
+    if (blocks > 0 && blocks < kNumCUs) want = (kNumCUs + blocks - 1) / blocks;
+    if (want > hpg) want = hpg;
+    const int64_t per = (hpg + want - 1) / want;
+    *hpb = (int)per;
+    *hsplit = (int)((hpg + per - 1) / per);
+}
+
 Layout make_layout(const ssd_shape *s, bool backward)
 {
     Layout L;
@@ -36,6 +47,8 @@ Layout make_layout(const ssd_shape *s, bool backward)
     L.NCp = (L.NC + 63) / 64 * 64;
     L.E = s->dk * s->dv;
     L.Epad = (L.E + 63) / 64 * 64;
+    head_split(s, L.NC, &L.hsplit, &L.hpb);
+    L.nqk_pad = (s->B * s->G * s->T * s->dk + 63) / 64 * 64;
     const size_t BH = size_t(s->B) * size_t(s->H);
     if (BH == 0 || s->T == 0) return L;   // nothing to store
     size_t o = 0;
@@ -47,6 +60,10 @@ Layout make_layout(const ssd_shape *s, bool backward)
     o = round_up(o + BH * size_t(L.NC) * size_t(L.Epad) * sizeof(float), 256);
     L.off[3] = o;
     if (backward) o = round_up(o + BH * size_t(L.NC) * size_t(L.Epad) * sizeof(float), 256);
+    if (backward && L.hsplit > 1) {
+        L.part_off = o;
+        o = round_up(o + 2 * size_t(L.hsplit) * size_t(L.nqk_pad) * sizeof(float), 256);
+    }
     L.off[4] = o;
     return L;
 }

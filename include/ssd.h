@@ -118,7 +118,10 @@ int ssd_bwd(const ssd_shape *shape,
  *                                  rounded up to a multiple of 64
  *   [3] dstates float [B*H][NC][E] (backward only) after ssd_bwd: the
  *                                  gradient of the state leaving each chunk
- *   [4] total bytes
+ *   [4] total bytes.  When B*G*ceil(T/64) is below the GPU's 256 compute
+ *       units the backward layout also holds, between the end of dstates and
+ *       the total, the per-block-split partial sums of dq and dk that the
+ *       gradient kernel writes and a final kernel adds up (no caller use).
  * `backward` selects the backward layout.  Returns SSD_OK or an error. */
 int ssd_workspace_layout(const ssd_shape *shape, int backward, size_t offsets[5]);
 

@@ -85,7 +85,9 @@ def test_empty_problems_need_no_workspace():
 
 
 @pytest.mark.parametrize("B,G,H,T,dk,dv", [(4, 2, 8, 8192, 128, 128), (2, 1, 24, 8192, 128, 64),
-                                           (4, 2, 4, 2048, 48, 40), (1, 1, 1, 1, 1, 1)])
+                                           (4, 2, 4, 2048, 48, 40), (1, 1, 1, 1, 1, 1),
+                                           (1, 1, 4, 130, 64, 64), (2, 2, 10, 1024, 48, 40),
+                                           (2, 1, 24, 512, 128, 64)])
 def test_workspace_layout_formula(B, G, H, T, dk, dv):
     s = ssd.ShapeArg(B, G, H, T, dk, dv)
     off = ssd.workspace_layout(s, True)
@@ -101,7 +103,14 @@ def test_workspace_layout_formula(B, G, H, T, dk, dv):
     assert off[1] == up(BH * NC * 64 * 4)
     assert off[2] == up(off[1] + BH * NCp * 4)
     assert off[3] == up(off[2] + BH * NC * Epad * 4)
-    assert off[4] == up(off[3] + BH * NC * Epad * 4)
+    # fewer (b, g, chunk) blocks than the 256 CUs: the group's heads are split
+    # over blocks and the backward keeps per-split dq, dk partial sums
+    hpg, blocks = H // G, B * G * NC
+    want = min(hpg, -(-256 // blocks)) if blocks < 256 else 1
+    hpb = -(-hpg // want)
+    hsplit = -(-hpg // hpb)
+    parts = 2 * hsplit * (-(-(B * G * T * dk) // 64) * 64) * 4 if hsplit > 1 else 0
+    assert off[4] == up(up(off[3] + BH * NC * Epad * 4) + parts)
     assert ssd.workspace_size(s, True) == off[4]
     assert ssd.workspace_size(s, False) == off[3]
 

@@ -28,6 +28,10 @@ ZOO = [
     Shape(2, 2, 8, 256, 128, 128),
     Shape(1, 1, 24, 300, 128, 64),
     Shape(3, 1, 2, 129, 33, 97),
+    # fewer (b, g, chunk) blocks than CUs: the output and gradient kernels split
+    # a group's heads over blocks, here unevenly (2 + 2 + 1 and 2 + 2 + 2 + 1)
+    Shape(2, 2, 10, 1024, 48, 40),
+    Shape(1, 1, 7, 4096, 64, 64),
 ]
 
 

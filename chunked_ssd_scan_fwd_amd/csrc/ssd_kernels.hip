@@ -1847,21 +1847,29 @@ static int run_scan(const Problem &P, int dirs, bool cumsum, const float *q, con
         // which measured slower.
         const int ndir = dirs == 3 ? 2 : 1, dir0 = dirs == 2 ? 1 : 0;
         const int64_t tiles_k = BH * (P.DKP / TI);
-        const bool pair = ndir * tiles_k * (P.DVP / (P.DVP < 64 ? P.DVP : 64)) <= kNumCUs;
+        const int64_t wide = ndir * tiles_k * (P.DVP / (P.DVP < 64 ? P.DVP : 64));
+        // With at most half a block per CU, 32-wide tiles: twice the
+        // independent chains, each step half the work.
+        const bool narrow = P.DVP >= 64 && 2 * wide <= kNumCUs;
+        const bool pair = (narrow ? 2 * wide : wide) <= kNumCUs;
         const int kid = dirs == 1 ? KID_SCAN : dirs == 2 ? KID_SCANR : KID_SCAN2;
-        SSD_DISPATCH(P, ({
-            constexpr int TJ = VP < 64 ? VP : 64;
-            const int64_t per_dir = tiles_k * (VP / TJ);
-            const dim3 grid((unsigned)(ndir * per_dir)), blk(NTS);
-            if (pair)
-                launch(kid, k_state_scan<KP, VP, VE, TJ, 2, EXD>, grid, blk, st, q, k, v, dy, h0, P.bcum, P.bl,
-                       P.states, P.dstates, dh0, (int)s.G, (int)s.H, s.T, (int)s.dk, (int)s.dv, P.L.NC, P.L.NCp,
-                       P.L.Epad, per_dir, dir0);
-            else
-                launch(kid, k_state_scan<KP, VP, VE, TJ, 1, EXD>, grid, blk, st, q, k, v, dy, h0, P.bcum, P.bl,
-                       P.states, P.dstates, dh0, (int)s.G, (int)s.H, s.T, (int)s.dk, (int)s.dv, P.L.NC, P.L.NCp,
-                       P.L.Epad, per_dir, dir0);
-        }));
+        auto run = [&](auto tj_c) {
+            SSD_DISPATCH(P, ({
+                constexpr int TJ = decltype(tj_c)::value ? 32 : (VP < 64 ? VP : 64);
+                const int64_t per_dir = tiles_k * (VP / TJ);
+                const dim3 grid((unsigned)(ndir * per_dir)), blk(NTS);
+                if (pair)
+                    launch(kid, k_state_scan<KP, VP, VE, TJ, 2, EXD>, grid, blk, st, q, k, v, dy, h0, P.bcum,
+                           P.bl, P.states, P.dstates, dh0, (int)s.G, (int)s.H, s.T, (int)s.dk, (int)s.dv, P.L.NC,
+                           P.L.NCp, P.L.Epad, per_dir, dir0);
+                else
+                    launch(kid, k_state_scan<KP, VP, VE, TJ, 1, EXD>, grid, blk, st, q, k, v, dy, h0, P.bcum,
+                           P.bl, P.states, P.dstates, dh0, (int)s.G, (int)s.H, s.T, (int)s.dk, (int)s.dv, P.L.NC,
+                           P.L.NCp, P.L.Epad, per_dir, dir0);
+            }));
+        };
+        if (narrow) run(BoolC<true>{});
+        else run(BoolC<false>{});
     }
     return launch_status();
 }

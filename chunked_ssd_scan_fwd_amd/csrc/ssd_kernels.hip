@@ -671,6 +671,12 @@ struct OutCfg {
     static constexpr int NQ = DKP / 8;                            // float4 of a Q row per lane
     static constexpr int NQQ = DKP / 32;                          // the same, per quarter of dk
     static constexpr int QPER = (CH * DKP / 4 + NTW - 1) / NTW;   // float4 / thread, one C x dk tile
+    // With more than one column block per head, the NCT waves of a row block
+    // need the same P: each forms 4 / NCT of its register groups into LDS
+    // (per head, the three causal 32 x 32 tiles in MFMA A-operand order).
+    static constexpr bool SHP = NCT > 1;
+    static constexpr int APW = 4 / NCT;
+    static constexpr int PN = SHP ? HPS * 3 * 16 * 64 : 4;
     static_assert(NTW % (DVP / 4) == 0, "a thread's float4 of a tile share their column");
 };
 
@@ -694,6 +700,7 @@ __global__ __launch_bounds__(NTW) void k_chunk_output(const float *__restrict__ 
     __shared__ __attribute__((aligned(16))) float VS[Cfg::VN];
     __shared__ __attribute__((aligned(16))) float bs[HPS * CH];
     __shared__ __attribute__((aligned(16))) float eb[HPS * CH];
+    __shared__ __attribute__((aligned(16))) float PS[Cfg::PN];   // [head][tile rt + jt][r][lane]
 
     // block ((b G + g) nsplit + split) NC + c takes heads [split hpb, split hpb + hpg) of group g
     const int hpg_all = H / G, nsplit = (hpg_all + hpb - 1) / hpb;
@@ -860,6 +867,44 @@ __global__ __launch_bounds__(NTW) void k_chunk_output(const float *__restrict__ 
             const int hh = st * HPS + hs;
             const bool live = hh < hpg;
             const int64_t bh = bh0 + (live ? hh : 0);
+            const float *bsh = bs + hs * CH, *ebh = eb + hs * CH;
+            const int i = 32 * rt + cl;
+            const int dl = cl - 4 * kh;
+
+            // p_ij = (Q K^T)_ij exp(b_i - b_j) for j <= i, exp(-inf) = 0 above the
+            // diagonal.  j = 32 jt + 8a + 4kh + e and i = 32 rt + cl, so j <= i
+            // compares the constant 8a + e with a per-lane bound.  The exponent
+            // is the difference b_i - b_j, taken before any scaling: b log2(e)
+            // stored per position would add a rounding of |b| to every exponent.
+            auto pgroup = [&](int jt, int a, float out[4]) {
+                const float bi = bsh[i];
+                const float4 bj = *reinterpret_cast<const float4 *>(bsh + 32 * jt + 8 * a + 4 * kh);
+                const float bjs[4] = {bj.x, bj.y, bj.z, bj.w};
+                const int lim = dl + 32 * (rt - jt);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float x = bi - bjs[e];
+                    out[e] = kqt[jt][4 * a + e] * __expf(8 * a + e <= lim ? x : -INFINITY);
+                }
+            };
+            if constexpr (Cfg::SHP) {
+                // this wave's register groups a of P (ct is wave-uniform)
+                float *pw = PS + (hs * 3 + rt) * 1024 + lane;
+#pragma unroll
+                for (int jt = 0; jt < 2; ++jt) {
+                    if (jt <= rt) {
+#pragma unroll
+                        for (int a = 0; a < 4; ++a) {
+                            if (a / Cfg::APW == ct) {
+                                float o[4];
+                                pgroup(jt, a, o);
+#pragma unroll
+                                for (int e = 0; e < 4; ++e) pw[jt * 1024 + (4 * a + e) * 64] = o[e];
+                            }
+                        }
+                    }
+                }
+            }
 
             // Q S_in; MFMA group m issues the next step's loads [m NL / NQ, (m + 1) NL / NQ).
             // One accumulator chain: the other wave of the SIMD issues its
@@ -885,7 +930,7 @@ __global__ __launch_bounds__(NTW) void k_chunk_output(const float *__restrict__ 
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
-            const float *bsh = bs + hs * CH, *ebh = eb + hs * CH;
+            if constexpr (Cfg::SHP) block_sync();   // every wave's part of P written
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
                 const float4 e = *reinterpret_cast<const float4 *>(ebh + 32 * rt + 8 * a + 4 * kh);
@@ -894,41 +939,28 @@ __global__ __launch_bounds__(NTW) void k_chunk_output(const float *__restrict__ 
                 acc[4 * a + 2] *= e.z;
                 acc[4 * a + 3] *= e.w;
             }
-            // P V: p_ij = (Q K^T)_ij exp(b_i - b_j) for j <= i, exp(-inf) = 0 above
-            // the diagonal; the row group's V operands and decays are read ahead.
-            // j = 32 jt + 8a + 4kh + e and i = 32 rt + cl, so j <= i compares the
-            // constant 8a + e with a per-lane bound.  The decay exponent is the
-            // difference b_i - b_j, taken before any scaling: b log2(e) stored
-            // per position would add a rounding of |b| to every exponent.
+            // P V; the row group's V operands and P (or decays) are read ahead.
             {
-                const int i = 32 * rt + cl;
-                const int dl = cl - 4 * kh;
-                const float bi = bsh[i];
                 const float *vb = VS + (hs * CH + 4 * kh) * LS + 32 * ct + cl;
+                const float *pr = PS + (hs * 3 + rt) * 1024 + lane;
 #pragma unroll
                 for (int jt = 0; jt < 2; ++jt) {
                     if (jt <= rt) {
-                        float bv[16];
-                        float4 bj[4];
+                        float bv[16], p[16];
 #pragma unroll
                         for (int a = 0; a < 4; ++a) {
-                            bj[a] = *reinterpret_cast<const float4 *>(bsh + 32 * jt + 8 * a + 4 * kh);
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) bv[4 * a + e] = vb[(32 * jt + 8 * a + e) * LS];
-                        }
-                        __builtin_amdgcn_sched_barrier(0);   // all reads issued before the MFMAs
-                        float p[16];
-                        const int lim = dl + 32 * (rt - jt);   // j <= i is 8a + e <= lim
-#pragma unroll
-                        for (int a = 0; a < 4; ++a) {
-                            const float bjs[4] = {bj[a].x, bj[a].y, bj[a].z, bj[a].w};
 #pragma unroll
                             for (int e = 0; e < 4; ++e) {
-                                const float x = bi - bjs[e];
-                                p[4 * a + e] = kqt[jt][4 * a + e] * __expf(8 * a + e <= lim ? x : -INFINITY);
+                                bv[4 * a + e] = vb[(32 * jt + 8 * a + e) * LS];
+                                if constexpr (Cfg::SHP) p[4 * a + e] = pr[jt * 1024 + (4 * a + e) * 64];
                             }
                         }
-                        __builtin_amdgcn_sched_barrier(0);   // the decay factors before the MFMAs
+                        if constexpr (!Cfg::SHP) {
+                            __builtin_amdgcn_sched_barrier(0);   // all reads issued before the MFMAs
+#pragma unroll
+                            for (int a = 0; a < 4; ++a) pgroup(jt, a, p + 4 * a);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);   // operands before the MFMAs
 #pragma unroll
                         for (int r = 0; r < 16; ++r) acc = mfma32(p[r], bv[r], acc);
                     }

@@ -68,15 +68,14 @@ def io_bytes(s):
 def kernel_work(s):
     """Algorithmic work per launch of each kernel: (bound, amount, unit)."""
     N = s.B * s.H * s.T
-    NC = (s.T + 63) // 64
     E = s.dk * s.dv
-    states = 4 * s.B * s.H * NC * E
     return {
-        "chunk_cumsum": ("hbm", 4 * N + 4 * s.B * s.H * NC * 64 + 4 * s.B * s.H * NC, "B"),
         "state_scan": ("mfma", N * 2 * E, "FLOP"),
         "chunk_output": ("mfma", N * (C_NOM * (s.dk + s.dv) + 2 * E), "FLOP"),
         "state_scan_bidir": ("mfma", 2 * N * 2 * E, "FLOP"),
         "bwd_grads": ("mfma", N * (C_NOM * (3 * s.dk + 2 * s.dv) + 6 * E), "FLOP"),
+        "state_scan_rev": ("mfma", N * 2 * E, "FLOP"),
+        "aux": ("hbm", 0, "B"),
     }
 
 
@@ -247,6 +246,167 @@ def grid_sweep(args, torch, ssd):
         torch.cuda.empty_cache()
 
 
+def quartiles(vals):
+    import numpy as np
+    a = np.asarray(vals, dtype=np.float64)
+    return {"median_ms": float(np.median(a)), "q1_ms": float(np.percentile(a, 25)),
+            "q3_ms": float(np.percentile(a, 75))}
+
+
+def protocol_ms(torch, fn, repeats=5, target_ms=50.0):
+    """The pages' timing protocol: one warm-up call (first-call latency), three
+    more untimed calls, then `repeats` samples, each `inner` back-to-back calls
+    between two events, inner = clamp(ceil(50 ms / single call), 1, 200).
+    Returns per-call quartiles (ms), inner and the first-call latency."""
+    import math
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    fn()
+    torch.cuda.synchronize()
+    first_ms = (time.perf_counter() - t0) * 1e3
+    for _ in range(3):
+        fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    fn()
+    e1.record()
+    torch.cuda.synchronize()
+    single = max(e0.elapsed_time(e1), 1e-3)
+    inner = int(min(200, max(1, math.ceil(target_ms / single))))
+    per = []
+    for _ in range(repeats):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        evs[0].record()
+        for _ in range(inner):
+            fn()
+        evs[1].record()
+        torch.cuda.synchronize()
+        per.append(evs[0].elapsed_time(evs[1]) / inner)
+    return {**quartiles(per), "inner": inner, "repeats": repeats, "first_call_ms": first_ms}
+
+
+def config_rows(torch, ssd, args):
+    """fwd and fwd_bwd of the five measured workloads: ms quartiles, nominal
+    TFLOP/s, GB/s of the algorithmic input/output bytes, and the fraction of
+    the step roofline (the longer of the nominal FLOPs at the fp32 MFMA peak
+    and those bytes at the HBM peak)."""
+    from ssd_workload import WORKLOADS, make_inputs
+    rows = {}
+    for w in WORKLOADS:
+        s = w.shape
+        x = make_inputs(s, w.seed, mu=w.mu)
+        d = {k: torch.from_numpy(v).to("cuda") for k, v in x.items()}
+        sa = ssd.ShapeArg(s.B, s.G, s.H, s.T, s.dk, s.dv)
+        ws = torch.empty(max(1, ssd.workspace_size(sa, True)), dtype=torch.uint8, device="cuda")
+        y = torch.empty((s.B, s.H, s.T, s.dv), device="cuda")
+        grads = (torch.empty((s.B, s.G, s.T, s.dk), device="cuda"), torch.empty((s.B, s.G, s.T, s.dk), device="cuda"),
+                 torch.empty((s.B, s.H, s.T, s.dv), device="cuda"), torch.empty((s.B, s.H, s.T), device="cuda"),
+                 torch.empty((s.B, s.H, s.dk, s.dv), device="cuda"))
+
+        def fwd():
+            ssd.fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["h0"], out=y, workspace=ws)
+
+        def step():
+            fwd()
+            ssd.bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["h0"], d["dy"], out=grads, workspace=ws)
+
+        f_fwd, f_bwd = nominal_flops(s)
+        b_fwd, b_fb = io_bytes(s)
+        row = {"shape": {"B": s.B, "G": s.G, "H": s.H, "T": s.T, "dk": s.dk, "dv": s.dv}}
+        for key, fn, fl, by in (("fwd", fwd, f_fwd, b_fwd), ("fwd_bwd", step, f_fwd + f_bwd, b_fb)):
+            r = protocol_ms(torch, fn, repeats=args.repeats)
+            t = r["median_ms"] * 1e-3
+            r.update({"tflops": fl / t / 1e12, "gbps_io": by / t / 1e9,
+                      "mfma_frac": fl / t / PEAK_FP32_MFMA, "hbm_frac": by / t / PEAK_HBM,
+                      "roofline_frac": max(fl / PEAK_FP32_MFMA, by / PEAK_HBM) / t,
+                      "bound": "mfma" if fl / PEAK_FP32_MFMA >= by / PEAK_HBM else "hbm"})
+            row[key] = r
+        rows[w.name] = row
+        print(json.dumps({"config": w.name, **{k: row[k]["median_ms"] for k in ("fwd", "fwd_bwd")}}),
+              file=sys.stderr, flush=True)
+        del d, ws, y, grads
+        torch.cuda.empty_cache()
+    return rows
+
+
+def device_facts(torch):
+    """Measured on this device: plain-copy HBM bandwidth, and the fp32 MFMA
+    rate and shader clock of an MFMA loop on every SIMD (benchmark probe
+    library; absent if it was not built)."""
+    import ctypes
+    import numpy as np
+    out = {}
+    n = (1 << 30) // 4
+    src = torch.ones(n, device="cuda")
+    dst = torch.empty(n, device="cuda")
+    for _ in range(3):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 10
+    out["copy_gbps"] = 2 * 4 * n / (ms * 1e-3) / 1e9
+    out["copy_note"] = "1 GiB device-to-device copy, read + write bytes / time"
+    del src, dst
+    path = os.path.join(ROOT, "chunked_ssd_scan_fwd_amd", "libssd_probe.so")
+    if not os.path.exists(path):
+        out["mfma_loop"] = None
+        return out
+    lib = ctypes.CDLL(path)
+    lib.probe_mfma_loop_bytes.argtypes = [ctypes.c_int]
+    lib.probe_mfma_loop_bytes.restype = ctypes.c_size_t
+    lib.probe_mfma_loop.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.probe_mfma_loop.restype = ctypes.c_int
+    lib.probe_mfma_chains.restype = ctypes.c_int
+    lib.probe_wall_clock_khz.restype = ctypes.c_int
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks, iters = cus, 20000
+    buf = torch.empty(int(lib.probe_mfma_loop_bytes(blocks)), dtype=torch.uint8, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for _ in range(2):
+        if lib.probe_mfma_loop(ctypes.c_void_p(buf.data_ptr()), blocks, iters, stream) != 0:
+            raise RuntimeError("probe_mfma_loop failed")
+    e0.record()
+    lib.probe_mfma_loop(ctypes.c_void_p(buf.data_ptr()), blocks, iters, stream)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    flops = blocks * 4 * iters * lib.probe_mfma_chains() * 32 * 32 * 2 * 2
+    ticks = buf[blocks * 1024:].view(torch.int64).view(blocks, 4).cpu().numpy().astype(np.float64)
+    khz = lib.probe_wall_clock_khz()
+    mhz = None
+    if khz > 0:
+        rates = (ticks[:, 1] - ticks[:, 0]) / ((ticks[:, 3] - ticks[:, 2]) / (khz * 1e3)) / 1e6
+        mhz = float(np.median(rates))
+    out["mfma_loop"] = {"tflops": flops / (ms * 1e-3) / 1e12, "frac_of_spec": flops / (ms * 1e-3) / PEAK_FP32_MFMA,
+                        "shader_clock_mhz": mhz, "blocks": blocks, "waves_per_cu": 4,
+                        "note": "independent v_mfma_f32_32x32x2f32 chains on every SIMD; clock = shader-clock "
+                                "counter over the real-time counter during the loop"}
+    return out
+
+
+def cpu_baseline(x, w, f_fwd, f_bwd, repeats):
+    """The fp64 oracle on the host cores: fwd alone and fwd + bwd, `repeats`
+    each, on the whole workload; nominal TFLOP/s of the median."""
+    import oracle
+    rec = {}
+    for key, fl in (("fwd", f_fwd), ("fwd_bwd", f_fwd + f_bwd)):
+        per = []
+        for _ in range(repeats):
+            t0 = time.perf_counter()
+            oracle.fwd(x["q"], x["k"], x["v"], x["log_alpha"], x["h0"])
+            if key == "fwd_bwd":
+                oracle.bwd(x["q"], x["k"], x["v"], x["log_alpha"], x["h0"], x["dy"])
+            per.append((time.perf_counter() - t0) * 1e3)
+        r = quartiles(per)
+        r["tflops"] = fl / (r["median_ms"] * 1e-3) / 1e12
+        rec[key] = r
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -254,10 +414,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=20,
                     help="untimed steps first; the GPU needs some 20 ms of work to reach its working clocks")
     ap.add_argument("--workload", default="g2h8_d128_T8192")
+    ap.add_argument("--repeats", type=int, default=5, help="samples per config in the per-config table")
+    ap.add_argument("--cpu-repeats", type=int, default=3, help="oracle repeats per mode for the CPU baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-configs", action="store_true", help="skip the per-config table")
     ap.add_argument("--no-reuse", action="store_true",
                     help="skip the secondary fwd + bwd_from_fwd timing (profiling runs: its reverse-only "
-                         "state scan shares the forward scan's kernel name and grid)")
+                         "state scan would add launches of another kernel)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (5 launches) and exit")
     ap.add_argument("--max-len", action="store_true",
@@ -305,15 +468,15 @@ def main():
              torch.empty((s.B, s.H, s.T, s.dv), device="cuda"), torch.empty((s.B, s.H, s.T), device="cuda"),
              torch.empty((s.B, s.H, s.dk, s.dv), device="cuda"))
 
-    def fwd():
-        ssd.fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["h0"], out=y, workspace=ws)
+    def fwd(timer=None):
+        ssd.fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["h0"], out=y, workspace=ws, timer=timer)
 
-    def bwd():
-        ssd.bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["h0"], d["dy"], out=grads, workspace=ws)
+    def bwd(timer=None):
+        ssd.bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["h0"], d["dy"], out=grads, workspace=ws, timer=timer)
 
-    def step():
-        fwd()
-        bwd()
+    def step(timer=None):
+        fwd(timer)
+        bwd(timer)
 
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -329,24 +492,24 @@ def main():
         when `per_step` (each is a marker packet on the stream, a few
         microseconds of stream time); `kernels` (names, or None for all) are
         timed per launch with events bound to their dispatches."""
-        with_kernels = kernels is None or len(kernels) > 0
+        timer = None if (kernels is not None and len(kernels) == 0) else ssd.KernelTimer(kernels)
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
         torch.cuda.synchronize()
         wall0 = time.perf_counter()
-        if with_kernels:
-            kt = ssd.kernel_timing(kernels).__enter__()
         evs[0].record()
         for i in range(K):
-            fn()
+            fn(timer)
             if per_step or i == K - 1:
                 evs[i + 1].record()
         torch.cuda.synchronize()
         wall = (time.perf_counter() - wall0) * 1e3
-        if with_kernels:
-            kt.__exit__(None, None, None)
+        res = None
+        if timer is not None:
+            res = timer.results()
+            timer.close()
         per = [evs[i].elapsed_time(evs[i + 1]) for i in range(K)] if per_step else []
         total = evs[0].elapsed_time(evs[K])
-        return total / K, per, wall / K, (kt.results if with_kernels else None)
+        return total / K, per, wall / K, res
 
     K = args.steps
     # Per-kernel pass (not the headline): K steps with every kernel timed by
@@ -354,7 +517,7 @@ def main():
     # dominant kernel.  Each timed dispatch costs a few microseconds of stream
     # time, so the headline region below times the dominant kernel only.
     _, _, _, kern_all = timed(step, K, kernels=None)
-    dom = max((n for n in kern_all if kern_all[n][1]), key=lambda n: kern_all[n][0])
+    dom = max((n for n in kern_all if kern_all[n][1] and n != "aux"), key=lambda n: kern_all[n][0])
     # Timed region: exactly K steps between two events; the dominant kernel's
     # launches carry HIP events on the launch stream, for its roofline.
     step_ms, _, wall_ms, kern_dom = timed(step, K, kernels=[dom], per_step=False)
@@ -366,7 +529,7 @@ def main():
 
     # Secondary (not the headline): the backward that reuses the forward's
     # residuals from the shared workspace instead of recomputing them.
-    def step_reuse():
+    def step_reuse(timer=None):
         fwd()
         ssd.bwd_from_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["h0"], d["dy"], out=grads, workspace=ws)
 
@@ -381,6 +544,13 @@ def main():
     value = (f_fwd + f_bwd) / (step_ms * 1e-3) / 1e12
     t_roof_fb = max((f_fwd + f_bwd) / PEAK_FP32_MFMA, b_fwd_bwd / PEAK_HBM)
     t_roof_f = max(f_fwd / PEAK_FP32_MFMA, b_fwd / PEAK_HBM)
+    # The nominal count takes Q K^T once per head; the kernels form it once per
+    # (b, g, chunk) and share it over the group's heads.  The group-aware count
+    # takes it once per group (forward once, backward once).
+    hpg = s.H // s.G
+    qk_per_group = s.B * s.G * s.T * C_NOM * s.dk
+    f_fwd_g = f_fwd - qk_per_group * (hpg - 1)
+    f_bwd_g = f_bwd - qk_per_group * (hpg - 1)
 
     work = kernel_work(s)
     kernels = {}
@@ -403,36 +573,36 @@ def main():
     roof["traffic"] = traffic_from_profiles(dom, w.name)
     for name in kernels:
         bnd, amt, _ = work[name]
+        if amt == 0:
+            continue
         a = amt / (kernels[name]["avg_us"] * 1e-6)
         kernels[name]["achieved"] = a / 1e12 if bnd == "mfma" else a / 1e9
         kernels[name]["unit"] = "TFLOP/s" if bnd == "mfma" else "GB/s"
         kernels[name]["frac"] = a / (PEAK_FP32_MFMA if bnd == "mfma" else PEAK_HBM)
 
+    # Parity of the timed path against the oracle on the whole tensors, and
+    # the CPU baseline (the oracle timed on the host cores).
     cpu = None
     parity = None
     if not args.no_cpu:
-        # CPU baseline: the fp64 oracle on the whole workload, on the host cores.
         import oracle
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        ref_y = oracle.fwd(x["q"], x["k"], x["v"], x["log_alpha"], x["h0"])
-        ref = oracle.bwd(x["q"], x["k"], x["v"], x["log_alpha"], x["h0"], x["dy"])
-        cpu_s = time.perf_counter() - t0
-        cpu = {"value": (f_fwd + f_bwd) / cpu_s / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
-               "kind": "oracle", "seconds": cpu_s, "cpu_model": cpu_info(),
-               "sample": f"whole {w.name} workload, one fwd + bwd in fp64 (nominal FLOPs / wall time)"}
-        # parity of the last timed GPU step against the oracle (whole tensors)
         fwd()
         bwd()
         torch.cuda.synchronize()
+        ref_y = oracle.fwd(x["q"], x["k"], x["v"], x["log_alpha"], x["h0"])
+        ref = oracle.bwd(x["q"], x["k"], x["v"], x["log_alpha"], x["h0"], x["dy"])
         parity = {"y": rel_err(y.cpu().numpy(), ref_y)}
         for name, t in zip(("dq", "dk", "dv", "dlog_alpha", "dh0"), grads):
             parity[name] = rel_err(t.cpu().numpy(), ref[name])
+        del ref_y, ref
+        rec = cpu_baseline(x, w, f_fwd, f_bwd, args.cpu_repeats)
+        cpu = {"value": rec["fwd_bwd"]["tflops"], "unit": "TFLOP/s", "cores": oracle.num_threads(),
+               "kind": "oracle", "cpu_model": cpu_info(), "fwd": rec["fwd"], "fwd_bwd": rec["fwd_bwd"],
+               "sample": f"whole {w.name} workload in fp64: forward alone and forward + backward, "
+                         f"{args.cpu_repeats} runs each (value: nominal fwd_bwd FLOPs / median wall time)"}
 
-    def q(vals):
-        a = np.asarray(vals)
-        return {"median_ms": float(np.median(a)), "q1_ms": float(np.percentile(a, 25)),
-                "q3_ms": float(np.percentile(a, 75))}
+    configs = None if args.no_configs else config_rows(torch, ssd, args)
+    facts = device_facts(torch)
 
     out = {
         "metric": METRIC,
@@ -444,6 +614,8 @@ def main():
         "ms_per_step": step_ms,
         "higher_is_better": True,
         "scaling": "weak",
+        # the pages' chunked fwd_bwd at this workload (RTX 3090, 11.883 ms, i.e.
+        # 6.3 nominal TFLOP/s): another machine's number, context only
         "vs_baseline": (PAGE_FWD_BWD_MS / step_ms) if w.name == "g2h8_d128_T8192" else None,
         "dtype": "f32",
         "data": "synthetic",
@@ -451,16 +623,26 @@ def main():
                                "step = ssd_fwd + ssd_bwd", "chunk": 64, "seed": w.seed},
         "roofline": roof,
         "cpu_baseline": cpu,
-        "fwd_bwd": {**q(per_step), "tflops": value, "roofline_frac": t_roof_fb / (step_ms * 1e-3),
-                    "gbps_io": b_fwd_bwd / (step_ms * 1e-3) / 1e9, "wall_ms": wall_ms},
-        "fwd": {**q(fwd_per), "ms": fwd_ms, "tflops": f_fwd / (fwd_ms * 1e-3) / 1e12,
-                "roofline_frac": t_roof_f / (fwd_ms * 1e-3), "gbps_io": b_fwd / (fwd_ms * 1e-3) / 1e9},
-        "bwd": {**q(bwd_per), "ms": bwd_ms, "tflops": f_bwd / (bwd_ms * 1e-3) / 1e12},
-        "fwd_bwd_reuse": None if reuse_ms is None else {**q(reuse_per), "ms": reuse_ms,
+        "fwd_bwd": {**quartiles(per_step), "tflops": value, "roofline_frac": t_roof_fb / (step_ms * 1e-3),
+                    "gbps_io": b_fwd_bwd / (step_ms * 1e-3) / 1e9, "wall_ms": wall_ms,
+                    "roofline_frac_group_qk": max((f_fwd_g + f_bwd_g) / PEAK_FP32_MFMA, b_fwd_bwd / PEAK_HBM)
+                    / (step_ms * 1e-3)},
+        "fwd": {**quartiles(fwd_per), "ms": fwd_ms, "tflops": f_fwd / (fwd_ms * 1e-3) / 1e12,
+                "roofline_frac": t_roof_f / (fwd_ms * 1e-3), "gbps_io": b_fwd / (fwd_ms * 1e-3) / 1e9,
+                "roofline_frac_group_qk": max(f_fwd_g / PEAK_FP32_MFMA, b_fwd / PEAK_HBM) / (fwd_ms * 1e-3)},
+        "bwd": {**quartiles(bwd_per), "ms": bwd_ms, "tflops": f_bwd / (bwd_ms * 1e-3) / 1e12},
+        "flop_convention": "nominal: per token-head, C=64, causal tiles as half, Q K^T counted once per head "
+                           "(fwd C(dk+dv)+4 dk dv, bwd C(3dk+2dv)+10 dk dv); *_group_qk: Q K^T once per group",
+        "fwd_bwd_reuse": None if reuse_ms is None else {**quartiles(reuse_per), "ms": reuse_ms,
                           "note": "secondary: ssd_fwd then ssd_bwd_from_fwd, which reuses the forward's "
                                   "chunk states from the workspace (not the stateless headline step)"},
+        "page_context_ms": {"fwd": PAGE_CHUNKED_MS[("g2h8_d128", 8192)][0],
+                            "fwd_bwd": PAGE_CHUNKED_MS[("g2h8_d128", 8192)][1],
+                            "note": "the pages' JAX chunked path on an RTX 3090 at this workload: context only"},
         "kernels": kernels,
         "parity_rel_err": parity,
+        "configs": configs,
+        "device_facts": facts,
         "first_call_ms": first_call_ms,
         "memory": {"workspace_bytes_fwd": ssd.workspace_size(sa, False), "workspace_bytes_bwd": ssd.workspace_size(sa, True),
                    "fwd_bwd_bytes": fwd_bwd_bytes(s.B, s.G, s.H, s.T, s.dk, s.dv, ssd.workspace_size(sa, True)),

@@ -16,9 +16,10 @@ import ctypes
 import os
 
 __all__ = ["fwd", "bwd", "library", "ShapeArg", "SsdError", "workspace_size",
-           "workspace_layout", "kernel_timing", "CHUNK", "bwd_from_fwd"]
+           "workspace_layout", "KernelTimer", "CHUNK", "bwd_from_fwd", "WS_REGIONS"]
 
 CHUNK = 64
+WS_REGIONS = 3   # SSD_WS_REGIONS: states, dstates, split partial sums
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libssd_hip.so")
 _lib = None
@@ -62,12 +63,18 @@ def library(path: str | None = None):
     lib.ssd_strerror.argtypes = [ctypes.c_int]
     lib.ssd_strerror.restype = ctypes.c_char_p
     lib.ssd_chunk_size.restype = ctypes.c_int
-    lib.ssd_kernel_timing_enable.argtypes = [ctypes.c_int]
-    lib.ssd_kernel_timing_enable.restype = ctypes.c_int
-    lib.ssd_kernel_timing_reset.restype = ctypes.c_int
-    lib.ssd_kernel_timing_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double),
-                                           ctypes.POINTER(i64)]
-    lib.ssd_kernel_timing_read.restype = ctypes.c_int
+    lib.ssd_timer_create.argtypes = [ctypes.c_int]
+    lib.ssd_timer_create.restype = vp
+    lib.ssd_timer_destroy.argtypes = [vp]
+    lib.ssd_timer_destroy.restype = ctypes.c_int
+    lib.ssd_timer_reset.argtypes = [vp]
+    lib.ssd_timer_reset.restype = ctypes.c_int
+    lib.ssd_timer_read.argtypes = [vp, ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
+    lib.ssd_timer_read.restype = ctypes.c_int
+    lib.ssd_fwd_timed.argtypes = [vp, sp] + [vp] * 6 + [vp, sz, vp]
+    lib.ssd_fwd_timed.restype = ctypes.c_int
+    lib.ssd_bwd_timed.argtypes = [vp, sp] + [vp] * 11 + [vp, sz, vp]
+    lib.ssd_bwd_timed.restype = ctypes.c_int
     lib.ssd_kernel_count.restype = ctypes.c_int
     lib.ssd_kernel_name.argtypes = [ctypes.c_int]
     lib.ssd_kernel_name.restype = ctypes.c_char_p
@@ -112,7 +119,7 @@ def workspace_size(shape: ShapeArg, backward: bool) -> int:
 
 def workspace_layout(shape: ShapeArg, backward: bool) -> list:
     lib = library()
-    arr = (ctypes.c_size_t * 5)()
+    arr = (ctypes.c_size_t * (WS_REGIONS + 1))()
     rc = lib.ssd_workspace_layout(ctypes.byref(shape), int(backward), arr)
     if rc != 0:
         raise SsdError(rc, "ssd_workspace_layout")
@@ -120,12 +127,24 @@ def workspace_layout(shape: ShapeArg, backward: bool) -> list:
 
 
 def _workspace(shape, backward, device, workspace):
+    """The workspace to pass: a new one, or the caller's after checking that
+    it lives on `device` and owns at least the bytes the size query asks for
+    (contiguous, counted from its own start to the end of its storage)."""
     import torch
     need = workspace_size(shape, backward)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
-    elif workspace.numel() * workspace.element_size() < need:
-        raise ValueError("workspace too small")
+        return workspace, need
+    if not isinstance(workspace, torch.Tensor):
+        raise TypeError("workspace must be a torch.Tensor")
+    if workspace.device != device or workspace.device.type != "cuda":
+        raise ValueError(f"workspace must be on {device} (a HIP device), got {workspace.device}")
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    nbytes = workspace.numel() * workspace.element_size()
+    room = workspace.untyped_storage().nbytes() - workspace.storage_offset() * workspace.element_size()
+    if min(nbytes, room) < need:
+        raise ValueError(f"workspace too small: {min(nbytes, room)} bytes, {need} needed")
     return workspace, need
 
 
@@ -134,8 +153,9 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def fwd(q, k, v, log_alpha, h0, *, out=None, workspace=None):
-    """y[B,H,T,dv] = SSD scan of (q, k, v, log_alpha, h0), on the current stream."""
+def fwd(q, k, v, log_alpha, h0, *, out=None, workspace=None, timer=None):
+    """y[B,H,T,dv] = SSD scan of (q, k, v, log_alpha, h0), on the current stream.
+    With a `KernelTimer`, its kernels are timed (ssd_fwd_timed)."""
     import torch
     lib = library()
     s = _shape_of(q, v)
@@ -149,16 +169,19 @@ def fwd(q, k, v, log_alpha, h0, *, out=None, workspace=None):
         out = torch.empty((s.B, s.H, s.T, s.dv), dtype=torch.float32, device=dev)
     _check(out, "out", (s.B, s.H, s.T, s.dv), dev)
     ws, need = _workspace(s, False, dev, workspace)
-    rc = lib.ssd_fwd(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(h0),
-                     _ptr(out), _ptr(ws), ctypes.c_size_t(ws.numel() * ws.element_size()),
-                     _stream(dev))
+    args = (ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(h0),
+            _ptr(out), _ptr(ws), ctypes.c_size_t(ws.numel() * ws.element_size()), _stream(dev))
+    rc = lib.ssd_fwd(*args) if timer is None else lib.ssd_fwd_timed(timer.handle, *args)
     if rc != 0:
         raise SsdError(rc, "ssd_fwd")
     return out
 
 
-def bwd(q, k, v, log_alpha, h0, dy, *, out=None, workspace=None):
-    """Gradients (dq, dk, dv, dlog_alpha, dh0) of L = sum(dy * y)."""
+def bwd(q, k, v, log_alpha, h0, dy, *, out=None, workspace=None, timer=None):
+    """Gradients (dq, dk, dv, dlog_alpha, dh0) of L = sum(dy * y).
+    With a `KernelTimer`, its kernels are timed (ssd_bwd_timed)."""
+    if timer is not None:
+        return _bwd_call("ssd_bwd_timed", q, k, v, log_alpha, h0, dy, out, workspace, timer)
     return _bwd_call("ssd_bwd", q, k, v, log_alpha, h0, dy, out, workspace)
 
 
@@ -173,7 +196,7 @@ def bwd_from_fwd(q, k, v, log_alpha, h0, dy, *, workspace, out=None):
     return _bwd_call("ssd_bwd_from_fwd", q, k, v, log_alpha, h0, dy, out, workspace)
 
 
-def _bwd_call(fn, q, k, v, log_alpha, h0, dy, out, workspace):
+def _bwd_call(fn, q, k, v, log_alpha, h0, dy, out, workspace, timer=None):
     import torch
     lib = library()
     s = _shape_of(q, v)
@@ -191,7 +214,8 @@ def _bwd_call(fn, q, k, v, log_alpha, h0, dy, out, workspace):
     for t, sh, name in zip(out, shapes, ("dq", "dk", "dv", "dlog_alpha", "dh0")):
         _check(t, name, sh, dev)
     ws, need = _workspace(s, True, dev, workspace)
-    rc = getattr(lib, fn)(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(h0), _ptr(dy),
+    pre = () if timer is None else (timer.handle,)
+    rc = getattr(lib, fn)(*pre, ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(h0), _ptr(dy),
                           *[_ptr(t) for t in out], _ptr(ws),
                           ctypes.c_size_t(ws.numel() * ws.element_size()), _stream(dev))
     if rc != 0:
@@ -199,36 +223,50 @@ def _bwd_call(fn, q, k, v, log_alpha, h0, dy, out, workspace):
     return out
 
 
-class kernel_timing:
-    """Context manager: per-kernel HIP-event timing of ssd_fwd/ssd_bwd launches.
-
-    ``with kernel_timing() as kt: ...`` then ``kt.results`` maps kernel name
-    to (total_ms, launches).  ``kernels`` names the kernels to time (default:
-    all); each timed dispatch costs a few microseconds of stream time."""
+class KernelTimer:
+    """A caller-owned per-kernel timer (ssd_timer_create): pass it to `fwd` /
+    `bwd` as ``timer=``; ``results()`` maps kernel name to (total_ms,
+    launches) since the last ``reset()``.  ``kernels`` names the kernels to
+    time (default: all); each timed dispatch costs a few microseconds of
+    stream time."""
 
     def __init__(self, kernels=None):
-        self.kernels = kernels
-
-    def __enter__(self):
         lib = library()
+        names = [lib.ssd_kernel_name(i).decode() for i in range(lib.ssd_kernel_count())]
         mask = -1
-        if self.kernels is not None:
-            names = [lib.ssd_kernel_name(i).decode() for i in range(lib.ssd_kernel_count())]
-            unknown = set(self.kernels) - set(names)
+        if kernels is not None:
+            unknown = set(kernels) - set(names)
             if unknown:
                 raise ValueError(f"unknown kernels {sorted(unknown)}; known: {names}")
-            mask = sum(1 << names.index(n) for n in self.kernels)
-        lib.ssd_kernel_timing_reset()
-        lib.ssd_kernel_timing_enable(mask)
-        self.results = {}
+            mask = sum(1 << names.index(n) for n in kernels)
+        self.names = names
+        self.handle = ctypes.c_void_p(lib.ssd_timer_create(mask))
+        if not self.handle.value:
+            raise MemoryError("ssd_timer_create failed")
+
+    def reset(self):
+        library().ssd_timer_reset(self.handle)
+
+    def results(self) -> dict:
+        lib = library()
+        out = {}
+        for kid, name in enumerate(self.names):
+            tot = ctypes.c_double()
+            cnt = ctypes.c_int64()
+            rc = lib.ssd_timer_read(self.handle, kid, ctypes.byref(tot), ctypes.byref(cnt))
+            if rc != 0:
+                raise SsdError(rc, "ssd_timer_read")
+            out[name] = (tot.value, cnt.value)
+        return out
+
+    def close(self):
+        if self.handle is not None and self.handle.value:
+            library().ssd_timer_destroy(self.handle)
+        self.handle = None
+
+    def __enter__(self):
         return self
 
     def __exit__(self, *exc):
-        lib = library()
-        lib.ssd_kernel_timing_enable(0)
-        for kid in range(lib.ssd_kernel_count()):
-            tot = ctypes.c_double()
-            cnt = ctypes.c_int64()
-            lib.ssd_kernel_timing_read(kid, ctypes.byref(tot), ctypes.byref(cnt))
-            self.results[lib.ssd_kernel_name(kid).decode()] = (tot.value, cnt.value)
+        self.close()
         return False

@@ -1,0 +1,325 @@
+// The fused chunk-state and state-pass scan (K3 + K4, and the reverse pass
+// of the backward) for gfx950, with the per-chunk cumulative log-decay (K1)
+// formed in its loader waves.
+#include "ssd_device.h"
+#include "ssd_launch.h"
+
+namespace ssd {
+
+// ---------------------------------------------------------------------------
+// K3 + K4 fused: sequential scan over chunks with the state held in MFMA
+// accumulators (v_mfma_f32_16x16x4f32: lane l supplies A[l%16][l/16] and
+// B[l/16][l%16]; accumulator r of lane l is row 4*(l/16) + r, column l%16).
+//
+//   forward (dir 0):  S = h0;  for c = 0 .. NC-1:
+//                       slab[c] = S;  S = e^{b_L(c)} S + K_c^T diag(e^{b_L - b}) V_c
+//   reverse (dir 1):  S = 0;   for c = NC-1 .. 0:
+//                       slab[c] = S;  S = e^{b_L(c)} S + Q_c^T diag(e^{b}) dY_c
+//                     dh0 = S
+//
+// so the forward slabs hold S_in(c), the state entering chunk c, and the
+// reverse slabs hold dS_out(c), the gradient of the state leaving chunk c.
+// The chunk's own contribution is formed on the fly and never stored.
+//
+// One block owns a 32 x TJ tile of one head's dk x dv state and has two
+// kinds of waves, one of each per SIMD:
+//   * four compute waves hold the state (each a 16 x TJ/2 slice) and per
+//     chunk read their operands from LDS, store the state and run the MFMAs;
+//   * four loader waves keep the operand tiles of the next PD steps in flight
+//     in registers and per step write the next step's tiles, their rows scaled
+//     by the decay weights, into the other half of the double-buffered LDS
+//     tiles.
+// A step covers CPS consecutive chunks, so the per-step synchronisation is
+// paid once per CPS chunks.  A loader wave's memory and exp work runs on its
+// SIMD while the compute wave's MFMAs do, and no compute wave waits on a
+// global load.  The number of steps is rounded up to a multiple of PD with
+// no-op chunks (zero operands, decay 1, stores dropped), so no load or store
+// is conditional and the compiler's count of loads in flight is exact.
+// A compute wave owns NU = TJ/32 16x16 accumulator tiles whose columns
+// interleave (tile u holds the wave's columns NU j + u), so one LDS read of
+// NU consecutive floats gives a lane all its B operands.  Blocks of one
+// (b, g) are placed on one XCD so that the group's q/k and each head's v/dy
+// tiles are shared through that XCD's L2.
+constexpr int TI = 32;
+constexpr int NTS = 512;        // 4 compute + 4 loader waves
+
+template <int DKP, int DVP, bool VEC, int TJ, int CPS, bool EXD>
+__global__ __launch_bounds__(NTS) void k_state_scan(
+    const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
+    const float *__restrict__ dy, const float *__restrict__ h0, const float *__restrict__ la,
+    float *__restrict__ states, float *__restrict__ dstates, float *__restrict__ dh0, int G, int H, int64_t T,
+    int dk, int dv, int64_t NC, int64_t Epad, int64_t per_dir, int dir0)
+{
+    static_assert(TJ <= DVP && DVP % TJ == 0 && (TJ == 32 || TJ == 64 || TJ == 128), "tile width");
+    if constexpr (EXD) {   // dk == DKP, dv == DVP: index arithmetic on constants
+        dk = DKP;
+        dv = DVP;
+        Epad = (int64_t)DKP * DVP;
+    }
+    constexpr int NTJ = DVP / TJ;
+    constexpr int NTILE = (DKP / TI) * NTJ;
+    constexpr int NU = TJ / 32;                       // accumulator tiles per compute wave
+    constexpr int WC = TJ / 2;                        // columns per compute wave
+    constexpr int LDA = TI + 16;                      // A reads: rows 16 banks apart
+    // B reads of NU floats per lane: rows 16 (b32) or 32 (b64) banks apart;
+    // b128 reads cover 256 contiguous bytes per 16 lanes
+    constexpr int LDB = (NU == 1) ? TJ + 16 : (NU == 2) ? TJ + 32 : TJ + 4;
+    constexpr int NLT = 256;                          // loader threads
+    constexpr int A4 = CH * TI / 4, B4 = CH * TJ / 4;
+    constexpr int APER = (A4 + NLT - 1) / NLT, BPER = (B4 + NLT - 1) / NLT;
+    constexpr int PD = 2;                             // steps loaded ahead (3 and 4 measured slower)
+    __shared__ __attribute__((aligned(16))) float As[2][CPS][CH * LDA];
+    __shared__ __attribute__((aligned(16))) float Bs[2][CPS][CH * LDB];
+    __shared__ float decs[2][CPS];                    // e^{b_L} of each staged chunk
+
+    // XCD-aware order: consecutive logical blocks share blockIdx % 8.
+    const int64_t nblk = gridDim.x;
+    int64_t L = blockIdx.x;
+    if ((nblk & 7) == 0) L = (int64_t)(blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
+    const int64_t dl = L / per_dir;                   // direction index within this launch
+    const int dir = dir0 + (int)dl;                   // 0: forward states, 1: reverse
+    const int64_t rem = L - dl * per_dir;
+    const int64_t bh = rem / NTILE;
+    const int tile = (int)(rem - bh * NTILE);
+    const int i0 = (tile / NTJ) * TI, j0 = (tile % NTJ) * TJ;
+    const int h = (int)(bh % H);
+    const int64_t b = bh / H;
+    const int g = h / (H / G);
+    const int64_t E = (int64_t)dk * dv;
+    const int64_t NSC = (NC + CPS - 1) / CPS;        // steps holding real chunks
+    const int64_t NS = (NSC + PD - 1) / PD * PD;      // steps, rounded up
+    const int wave = threadIdx.x >> 6;
+
+    if (wave >= 4) {
+        // ---------------- loader waves
+        const int lt = threadIdx.x - 256;
+        const float *Asrc = (dir == 0 ? k : q) + (b * G + g) * T * dk;   // row 0, column 0
+        const float *Bsrc = (dir == 0 ? v : dy) + bh * T * dv;
+        const float *lab = la + bh * T;
+        const int lima = dk - i0, limb = dv - j0;
+        struct Stage {
+            float4 a[APER], b[BPER];
+            float la;   // log_alpha of the chunk's position (lt % 64)
+        };
+        Stage stg[PD][CPS];
+        // operands of chunk n of the scan order; chunks past the end load zeros
+        auto prefetch = [&](Stage &S, int64_t n) {
+            const bool live = n < NC;
+            const int64_t c = live ? (dir == 0 ? n : NC - 1 - n) : 0;
+            const int rows = (int)((T - c * CH) < CH ? (T - c * CH) : CH);
+            const rsrc_t ab = make_rsrc(Asrc + c * CH * dk, live ? (int64_t)rows * dk * 4 : 0);
+            const rsrc_t bb = make_rsrc(Bsrc + c * CH * dv, live ? (int64_t)rows * dv * 4 : 0);
+            const rsrc_t lr = make_rsrc(lab + c * CH, live ? (int64_t)rows * 4 : 0);
+#pragma unroll
+            for (int u = 0; u < APER; ++u) {
+                const int r = f4_row<TI / 4, NLT>(lt, u), c4 = f4_col<TI / 4>(lt);
+                const bool ok = A4 % NLT == 0 || r < CH;
+                S.a[u] = load4(ab, (uint32_t)(r * dk + i0), c4, lima, ok, VEC);
+            }
+#pragma unroll
+            for (int u = 0; u < BPER; ++u) {
+                const int r = f4_row<TJ / 4, NLT>(lt, u), c4 = f4_col<TJ / 4>(lt);
+                S.b[u] = load4(bb, (uint32_t)(r * dv + j0), c4, limb, B4 % NLT == 0 || r < CH, VEC);
+            }
+            // positions past the sequence end read 0 and repeat the last b
+            S.la = gload1(lr, (uint32_t)(lt & 63) * 4u);
+        };
+        // stage S into LDS half `buf`, slot cc; the rows of the A tile (TI
+        // wide, the narrower one) are scaled by the decay weights, formed
+        // here from the chunk's cumulative log-decay (each loader wave scans
+        // the chunk's 64 log_alpha values and fetches b at its rows)
+        auto stage = [&](const Stage &S, int buf, int cc) {
+            const float bc = chunk_cumsum(S.la);
+            const float bL = readlane_f(bc, 63);
+            float brow[APER];
+#pragma unroll
+            for (int u = 0; u < APER; ++u) brow[u] = __shfl(bc, f4_row<TI / 4, NLT>(lt, u) & 63);
+#pragma unroll
+            for (int u = 0; u < APER; ++u) {
+                const int r = f4_row<TI / 4, NLT>(lt, u), c4 = f4_col<TI / 4>(lt);
+                if (A4 % NLT == 0 || r < CH) {
+                    const float w = (dir == 0) ? __expf(bL - brow[u]) : __expf(brow[u]);
+                    float4 x = S.a[u];
+                    x.x *= w;
+                    x.y *= w;
+                    x.z *= w;
+                    x.w *= w;
+                    *reinterpret_cast<float4 *>(&As[buf][cc][r * LDA + c4]) = x;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < BPER; ++u) {
+                const int r = f4_row<TJ / 4, NLT>(lt, u), c4 = f4_col<TJ / 4>(lt);
+                if (B4 % NLT == 0 || r < CH) {
+                    *reinterpret_cast<float4 *>(&Bs[buf][cc][r * LDB + c4]) = S.b[u];
+                }
+            }
+            if (lt == 0) decs[buf][cc] = expf(bL);
+        };
+        // step s: its chunks are published by the barrier; stage step s + 1
+        // into the other half and refill its registers with step s + 1 + PD
+        auto step = [&](int64_t s, int u) {
+            block_sync();
+            const int un = (u + 1) % PD;
+#pragma unroll
+            for (int cc = 0; cc < CPS; ++cc) {
+                stage(stg[un][cc], (int)((s + 1) & 1), cc);
+                prefetch(stg[un][cc], (s + 1 + PD) * CPS + cc);
+            }
+        };
+#pragma unroll
+        for (int u = 0; u < PD; ++u) {
+#pragma unroll
+            for (int cc = 0; cc < CPS; ++cc) prefetch(stg[u][cc], (int64_t)u * CPS + cc);
+        }
+#pragma unroll
+        for (int cc = 0; cc < CPS; ++cc) {
+            stage(stg[0][cc], 0, cc);
+            prefetch(stg[0][cc], (int64_t)PD * CPS + cc);
+        }
+        // the first PD steps are peeled so that the loop is entered with the
+        // loads in flight that it repeats with
+#pragma unroll
+        for (int u = 0; u < PD; ++u) step(u, u);
+        for (int64_t s0 = PD; s0 < NS; s0 += PD) {
+#pragma unroll
+            for (int u = 0; u < PD; ++u) step(s0 + u, u);
+        }
+        return;
+    }
+
+    // ---------------- compute waves
+    const int lane = threadIdx.x & 63;
+    const int l16 = lane & 15, q4 = lane >> 4;
+    const int rblk = wave & 1;              // 16-row block of the tile
+    const int wc0 = (wave >> 1) * WC;       // first column of this wave within the tile
+    float *slab = (dir == 0 ? states : dstates) + bh * NC * Epad;
+
+    // byte offset of accumulator (u, r) in a dk x dv state, kOOB outside it
+    auto soff = [&](int u, int r) -> uint32_t {
+        const int row = i0 + rblk * 16 + 4 * q4 + r, col = j0 + wc0 + NU * l16 + u;
+        return (row < dk && col < dv) ? (uint32_t)(row * dv + col) * 4u : kOOB;
+    };
+    f32x4 acc[NU];
+    {
+        const rsrc_t hr = make_rsrc(h0 + bh * E, dir == 0 ? E * 4 : 0);   // the reverse pass starts at 0
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[u][r] = gload1(hr, soff(u, r));
+            // Wait for the h0 loads here: otherwise every state store in the
+            // loop waits on the stores before it.
+            asm volatile("" : "+v"(acc[u]));
+        }
+    }
+    for (int64_t s = 0; s < NS; ++s) {
+        const int buf = (int)(s & 1);
+        block_sync();   // step s staged in half `buf`
+#pragma unroll
+        for (int cc = 0; cc < CPS; ++cc) {
+            float av[CH / 4];
+            float bv[CH / 4][NU];
+            const float *Ab = &As[buf][cc][q4 * LDA + rblk * 16 + l16];
+            const float *Bb = &Bs[buf][cc][q4 * LDB + wc0 + NU * l16];
+#pragma unroll
+            for (int kk = 0; kk < CH / 4; ++kk) {
+                av[kk] = Ab[4 * kk * LDA];
+                if constexpr (NU == 4) {
+                    const float4 t4 = *reinterpret_cast<const float4 *>(Bb + 4 * kk * LDB);
+                    bv[kk][0] = t4.x;
+                    bv[kk][1] = t4.y;
+                    bv[kk][2] = t4.z;
+                    bv[kk][3] = t4.w;
+                } else if constexpr (NU == 2) {
+                    const float2 t2 = *reinterpret_cast<const float2 *>(Bb + 4 * kk * LDB);
+                    bv[kk][0] = t2.x;
+                    bv[kk][1] = t2.y;
+                } else {
+                    bv[kk][0] = Bb[4 * kk * LDB];
+                }
+            }
+            const float decay = decs[buf][cc];
+            // slab[c] = S (state entering the chunk in this direction); no-op chunks store nothing
+            const int64_t n = s * CPS + cc;
+            const bool live = n < NC;
+            const rsrc_t dst =
+                make_rsrc(slab + (live ? (dir == 0 ? n : NC - 1 - n) : 0) * Epad, live ? E * 4 : 0);
+            if constexpr (VEC) {
+                // the lane's NU columns of a row are consecutive (dv % 4 == 0,
+                // so they are inside the state when the first one is)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float sv[NU];
+#pragma unroll
+                    for (int u = 0; u < NU; ++u) sv[u] = acc[u][r];
+                    gstoreN_nt<NU>(dst, soff(0, r), sv);
+                }
+            } else {
+#pragma unroll
+                for (int u = 0; u < NU; ++u) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) gstore1_nt(dst, soff(u, r), acc[u][r]);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < NU; ++u) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[u][r] *= decay;
+            }
+            // S += A^T B over the chunk's 64 positions
+#pragma unroll
+            for (int kk = 0; kk < CH / 4; ++kk) {
+#pragma unroll
+                for (int u = 0; u < NU; ++u) acc[u] = mfma16(av[kk], bv[kk][u], acc[u]);
+            }
+        }
+    }
+    if (dir == 1) {
+        const rsrc_t hr = make_rsrc(dh0 + bh * E, E * 4);
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) gstore1(hr, soff(u, r), acc[u][r]);
+        }
+    }
+}
+// The fused state scan over the directions in `dirs` (see ssd_launch.h).
+int run_scan(const Problem &P, int dirs, const float *q, const float *k, const float *v, const float *dy,
+             const float *la, const float *h0, float *dh0, hipStream_t st)
+{
+    const ssd_shape &s = P.s;
+    const int64_t BH = s.B * s.H;
+    // Two chunks per step when there is at most one block per CU (the paired
+    // tiles fill most of a CU's LDS); otherwise one.  State tiles are 32 x 64
+    // (32 x dv for dv < 64): wider tiles re-read fewer operand tiles but
+    // halve the number of independent sequential chains per CU, which
+    // measured slower.
+    const int ndir = dirs == 3 ? 2 : 1, dir0 = dirs == 2 ? 1 : 0;
+    const int64_t tiles_k = BH * (P.DKP / TI);
+    const int64_t wide = ndir * tiles_k * (P.DVP / (P.DVP < 64 ? P.DVP : 64));
+    // With at most half a block per CU, 32-wide tiles: twice the independent
+    // chains, each step half the work.
+    const bool narrow = P.DVP >= 64 && 2 * wide <= P.cus;
+    const bool pair = (narrow ? 2 * wide : wide) <= P.cus;
+    const int kid = dirs == 1 ? KID_SCAN : dirs == 2 ? KID_SCANR : KID_SCAN2;
+    auto run = [&](auto tj_c) {
+        SSD_DISPATCH(P, ({
+            constexpr int TJ = decltype(tj_c)::value ? 32 : (VP < 64 ? VP : 64);
+            const int64_t per_dir = tiles_k * (VP / TJ);
+            const dim3 grid((unsigned)(ndir * per_dir)), blk(NTS);
+            if (pair)
+                launch(P.timer, kid, k_state_scan<KP, VP, VE, TJ, 2, EXD>, grid, blk, st, q, k, v, dy, h0, la,
+                       P.states, P.dstates, dh0, (int)s.G, (int)s.H, s.T, (int)s.dk, (int)s.dv, P.L.NC, P.L.Epad,
+                       per_dir, dir0);
+            else
+                launch(P.timer, kid, k_state_scan<KP, VP, VE, TJ, 1, EXD>, grid, blk, st, q, k, v, dy, h0, la,
+                       P.states, P.dstates, dh0, (int)s.G, (int)s.H, s.T, (int)s.dk, (int)s.dv, P.L.NC, P.L.Epad,
+                       per_dir, dir0);
+        }));
+    };
+    if (narrow) run(BoolC<true>{});
+    else run(BoolC<false>{});
+    return launch_status();
+}
+
+}  // namespace ssd

@@ -1,5 +1,6 @@
 // Host-only argument checks and workspace layout for the SSD scan C ABI.
-// This unit makes no HIP call.
+// This unit makes no HIP call (the device's compute-unit count comes from
+// device_cus() in the HIP unit).
 #include "ssd_internal.h"
 
 namespace ssd {
@@ -29,42 +30,36 @@ int check_shape(const ssd_shape *s)
 
 static size_t round_up(size_t x, size_t m) { return (x + m - 1) / m * m; }
 
-void head_split(const ssd_shape *s, int64_t NC, int *hsplit, int *hpb)
+void head_split(const ssd_shape *s, int64_t NC, int cus, int *hsplit, int *hpb)
 {
     const int64_t hpg = s->H / s->G, blocks = s->B * s->G * NC;
     int64_t want = 1;
-    if (blocks > 0 && blocks < kNumCUs) want = (kNumCUs + blocks - 1) / blocks;
+    if (blocks > 0 && blocks < cus) want = (cus + blocks - 1) / blocks;
     if (want > hpg) want = hpg;
     const int64_t per = (hpg + want - 1) / want;
     *hpb = (int)per;
     *hsplit = (int)((hpg + per - 1) / per);
 }
 
-Layout make_layout(const ssd_shape *s, bool backward)
+Layout make_layout(const ssd_shape *s, bool backward, int cus)
 {
     Layout L;
     L.NC = (s->T + kChunk - 1) / kChunk;
-    L.NCp = (L.NC + 63) / 64 * 64;
     L.E = s->dk * s->dv;
     L.Epad = (L.E + 63) / 64 * 64;
-    head_split(s, L.NC, &L.hsplit, &L.hpb);
+    head_split(s, L.NC, cus, &L.hsplit, &L.hpb);
     L.nqk_pad = (s->B * s->G * s->T * s->dk + 63) / 64 * 64;
     const size_t BH = size_t(s->B) * size_t(s->H);
     if (BH == 0 || s->T == 0) return L;   // nothing to store
+    const size_t slab = BH * size_t(L.NC) * size_t(L.Epad) * sizeof(float);
     size_t o = 0;
     L.off[0] = o;
-    o = round_up(o + BH * size_t(L.NC) * kChunk * sizeof(float), 256);
+    o = round_up(o + slab, 256);
     L.off[1] = o;
-    o = round_up(o + BH * size_t(L.NCp) * sizeof(float), 256);
+    if (backward) o = round_up(o + slab, 256);
     L.off[2] = o;
-    o = round_up(o + BH * size_t(L.NC) * size_t(L.Epad) * sizeof(float), 256);
+    if (backward && L.hsplit > 1) o = round_up(o + 2 * size_t(L.hsplit) * size_t(L.nqk_pad) * sizeof(float), 256);
     L.off[3] = o;
-    if (backward) o = round_up(o + BH * size_t(L.NC) * size_t(L.Epad) * sizeof(float), 256);
-    if (backward && L.hsplit > 1) {
-        L.part_off = o;
-        o = round_up(o + 2 * size_t(L.hsplit) * size_t(L.nqk_pad) * sizeof(float), 256);
-    }
-    L.off[4] = o;
     return L;
 }
 
@@ -75,22 +70,22 @@ extern "C" {
 size_t ssd_fwd_workspace_size(const ssd_shape *shape)
 {
     if (ssd::check_shape(shape) != SSD_OK) return (size_t)-1;
-    return ssd::make_layout(shape, false).off[4];
+    return ssd::make_layout(shape, false, ssd::device_cus()).off[SSD_WS_REGIONS];
 }
 
 size_t ssd_bwd_workspace_size(const ssd_shape *shape)
 {
     if (ssd::check_shape(shape) != SSD_OK) return (size_t)-1;
-    return ssd::make_layout(shape, true).off[4];
+    return ssd::make_layout(shape, true, ssd::device_cus()).off[SSD_WS_REGIONS];
 }
 
-int ssd_workspace_layout(const ssd_shape *shape, int backward, size_t offsets[5])
+int ssd_workspace_layout(const ssd_shape *shape, int backward, size_t offsets[SSD_WS_REGIONS + 1])
 {
     if (!offsets) return SSD_ERR_NULL;
     const int rc = ssd::check_shape(shape);
     if (rc != SSD_OK) return rc;
-    const ssd::Layout L = ssd::make_layout(shape, backward != 0);
-    for (int i = 0; i < 5; ++i) offsets[i] = L.off[i];
+    const ssd::Layout L = ssd::make_layout(shape, backward != 0, ssd::device_cus());
+    for (int i = 0; i <= SSD_WS_REGIONS; ++i) offsets[i] = L.off[i];
     return SSD_OK;
 }
 

@@ -8,13 +8,14 @@
  *     S_t    = exp(log_alpha[b,h,t]) * S_{t-1} + k[b,g,t] v[b,h,t]^T
  *     y[b,h,t] = S_t^T q[b,g,t]
  *
- * The tensor set and layouts are those fixed by the byte counts of the
- * benchmark pages kernel_ssd_cpu.json / kernel_ssd_gpu.json (results records
- * of impl "chunked": xla_arg_mb = q + k + v + log_alpha + h0 and xla_out_mb = y
- * in float32 for mode fwd; the five input gradients for mode fwd_bwd, see
- * rel_err_grads).  No final state is returned, and the gradient path keeps no
- * residual between forward and backward (residual_mb 0.0 in every chunked
- * fwd_bwd record): ssd_bwd recomputes what it needs from its inputs.
+ * Sources.  The benchmark pages kernel_ssd_cpu.json and kernel_ssd_gpu.json
+ * print no formula; they fix the tensor set and the layouts through their
+ * byte counts.  In every results record of impl "chunked" and mode "fwd",
+ * xla_arg_mb equals q + k + v + log_alpha + h0 and xla_out_mb equals y, in
+ * float32 and the layouts below.  In mode "fwd_bwd" the outputs are the five
+ * input gradients named by the keys of rel_err_grads, and residual_mb is 0.0
+ * (the chunked backward keeps nothing from its forward).  The config block
+ * of each page lists the shapes as (batch, groups, heads, dk, dv).
  *
  * Layouts (all float32, dense, row-major, no strides):
  *     q, k           [B, G, T, dk]
@@ -36,10 +37,10 @@
  *
  * Memory and ownership.  Every tensor pointer and the workspace pointer are
  * DEVICE pointers on the current HIP device, allocated and owned by the
- * caller; the library never allocates, frees or synchronizes.  Each must be
- * 16-byte aligned.  Outputs are overwritten, never accumulated into, and
- * must not alias inputs, each other or the workspace.  Inputs are not
- * modified.
+ * caller; the library never allocates device memory, frees or synchronizes
+ * (the timer calls below aside).  Each pointer must be 16-byte aligned.
+ * Outputs are overwritten, never accumulated into, and must not alias
+ * inputs, each other or the workspace.  Inputs are not modified.
  *
  * Asynchrony.  Work is enqueued on `stream` (a hipStream_t; NULL is the
  * null stream) and the call returns after enqueueing.  The workspace and
@@ -55,9 +56,9 @@
  * 1 <= dk <= 128, 1 <= dv <= 128; B*H*T*max(dk,dv) < 2^40.  Other dk/dv
  * return SSD_ERR_UNSUPPORTED.  log_alpha must be finite.
  *
- * Thread safety.  Calls are reentrant; concurrent calls on different streams
- * need separate workspaces.  The optional kernel-timing facility below is
- * process-global and not thread-safe.
+ * Thread safety.  The compute calls keep no mutable state between calls and
+ * are reentrant; concurrent calls on different streams need separate
+ * workspaces.  A timer (ssd_timer_create) belongs to one caller at a time.
  */
 #ifndef SSD_H
 #define SSD_H
@@ -75,6 +76,12 @@ typedef struct ssd_shape {
     int64_t B, G, H, T, dk, dv;
 } ssd_shape;
 
+/* Status codes.  Every call validates its arguments first and returns one of
+ * these.  SSD_ERR_UNSUPPORTED is this library's form of the pages' declined
+ * shapes: the results records of impls "scan" and "pallas" at config
+ * g2h4_dk48_dv40 (kernel_ssd_cpu.json and kernel_ssd_gpu.json) carry
+ * "skipped": "unsupported shape" instead of a result, i.e. a valid shape an
+ * implementation does not compute is refused, never computed wrongly. */
 enum ssd_status {
     SSD_OK = 0,
     SSD_ERR_NULL = 1,        /* a required pointer is NULL                       */
@@ -85,89 +92,119 @@ enum ssd_status {
     SSD_ERR_DEVICE = 6       /* a HIP launch or runtime call failed               */
 };
 
-/* Bytes of device workspace ssd_fwd / ssd_bwd need for `shape` (0 when the
- * shape is empty).  Returns (size_t)-1 if the shape is invalid or
- * unsupported.  The workspace needs no initialization and holds no state
- * between calls. */
+/* Bytes of device workspace ssd_fwd / ssd_bwd need for `shape` on the
+ * current device (0 when the shape is empty; the size depends on the
+ * device's compute-unit count, 256 assumed when no device is visible).
+ * Returns (size_t)-1 if the shape is invalid or unsupported.  The workspace
+ * needs no initialization and holds no state between calls.  The pages
+ * report the chunked path's temporary device memory as xla_temp_mb and its
+ * peak as peak_mb (kernel_ssd_gpu.json, results records of kind "peak");
+ * this query is where this library's equivalent is stated up front. */
 size_t ssd_fwd_workspace_size(const ssd_shape *shape);
 size_t ssd_bwd_workspace_size(const ssd_shape *shape);
 
-/* Forward: y = scan(q, k, v, log_alpha, h0).
- * After the call completes, the workspace holds (for inspection by tests;
- * callers treat it as opaque) the regions reported by ssd_workspace_layout. */
+/* Forward: y = scan(q, k, v, log_alpha, h0), the operation of the "chunked"
+ * "fwd" records of kernel_ssd_cpu.json / kernel_ssd_gpu.json (arguments per
+ * xla_arg_mb, the single output per xla_out_mb).  After the call completes
+ * the workspace holds (for inspection by tests; callers treat it as opaque)
+ * the regions reported by ssd_workspace_layout. */
 int ssd_fwd(const ssd_shape *shape,
             const float *q, const float *k, const float *v,
             const float *log_alpha, const float *h0,
             float *y,
             void *workspace, size_t workspace_bytes, void *stream);
 
-/* Backward of L = sum(dy * y): writes dq, dk, dv, dlog_alpha, dh0.
- * Stateless: recomputes the forward quantities it needs. */
+/* Backward of L = sum(dy * y): writes dq, dk, dv, dlog_alpha, dh0, the five
+ * gradients of the "chunked" "fwd_bwd" records (keys of rel_err_grads).
+ * Stateless, as those records' residual_mb 0.0 says: it recomputes the
+ * forward quantities it needs from its inputs. */
 int ssd_bwd(const ssd_shape *shape,
             const float *q, const float *k, const float *v,
             const float *log_alpha, const float *h0, const float *dy,
             float *dq, float *dk, float *dv, float *dlog_alpha, float *dh0,
             void *workspace, size_t workspace_bytes, void *stream);
 
+/* Number of workspace regions reported by ssd_workspace_layout. */
+#define SSD_WS_REGIONS 3
+
 /* Byte offsets of the workspace regions, in this order:
- *   [0] bcum   float [B*H][NC*64]  within-chunk inclusive cumsum of log_alpha
- *                                  (positions past T hold the last valid value)
- *   [1] bl     float [B*H][NCp]    chunk totals (NCp = NC rounded up to 64)
- *   [2] states float [B*H][NC][E]  after ssd_fwd/ssd_bwd: the state entering
- *                                  each chunk, row-major dk x dv; E = dk*dv
- *                                  rounded up to a multiple of 64
- *   [3] dstates float [B*H][NC][E] (backward only) after ssd_bwd: the
- *                                  gradient of the state leaving each chunk
- *   [4] total bytes.  When B*G*ceil(T/64) is below the GPU's 256 compute
- *       units the backward layout also holds, between the end of dstates and
- *       the total, the per-block-split partial sums of dq and dk that the
- *       gradient kernel writes and a final kernel adds up (no caller use).
- * `backward` selects the backward layout.  Returns SSD_OK or an error. */
-int ssd_workspace_layout(const ssd_shape *shape, int backward, size_t offsets[5]);
+ *   [0] states  float [B*H][NC][E]  after ssd_fwd/ssd_bwd: the state entering
+ *                                   each chunk, row-major dk x dv; NC =
+ *                                   ceil(T/64), E = dk*dv rounded up to a
+ *                                   multiple of 64
+ *   [1] dstates float [B*H][NC][E]  (backward only; empty otherwise) after
+ *                                   ssd_bwd: the gradient of the state
+ *                                   leaving each chunk
+ *   [2] parts   (backward only) when B*G*ceil(T/64) is below the device's
+ *               compute-unit count: per-block-split partial sums of dq and
+ *               dk that the gradient kernel writes and a final kernel adds
+ *               up (no caller use); empty otherwise
+ *   [3] total bytes.
+ * `backward` selects the backward layout.  Returns SSD_OK or an error.
+ * Test support: the states are the quantity the chunked method passes
+ * between chunks, checked against the oracle's state at chunk boundaries. */
+int ssd_workspace_layout(const ssd_shape *shape, int backward, size_t offsets[SSD_WS_REGIONS + 1]);
 
 /* Static description of a status code (never NULL). */
 const char *ssd_strerror(int status);
 
-/* Chunk length used by the kernels (SSD_CHUNK). */
+/* Chunk length used by the kernels (SSD_CHUNK).  The SSD pages state no
+ * chunk length; results do not depend on it beyond rounding. */
 int ssd_chunk_size(void);
 
 /* Backward that reuses the forward's residuals: the same outputs as ssd_bwd,
  * but the workspace must already hold what ssd_fwd wrote for the SAME inputs
  * (q, k, v, log_alpha, h0 and shape) into a workspace of at least
- * ssd_bwd_workspace_size(shape) bytes: the forward's regions (per-chunk
- * cumulative log-decay, chunk totals and the state entering every chunk)
- * sit at the same offsets in the forward and backward layouts.  Only the
- * reverse state pass and the gradient kernel run, which skips recomputing
- * the forward states.  This is the residual-keeping side of the trade-off
- * that the GPU benchmark page records in its residual_mb field (0 for the
- * stateless chunked backward, a few to a hundred MiB for its fused
- * variant); ssd_bwd stays the stateless path.  The library cannot check the
- * precondition: with a
- * workspace that does not hold the forward's results for these inputs the
- * outputs are wrong (but every access stays inside the workspace and the
- * tensors).  Arguments, layouts, ownership, asynchrony and return codes are
- * those of ssd_bwd; the forward work must be enqueued on the same stream
- * before this call, or be complete. */
+ * ssd_bwd_workspace_size(shape) bytes: the forward's region (the state
+ * entering every chunk) sits at the same offset in the forward and backward
+ * layouts.  Only the reverse state pass and the gradient kernel run, which
+ * skips recomputing the forward states.  This is the residual-keeping side
+ * of the trade-off that kernel_ssd_gpu.json records in residual_mb (0.0 for
+ * the stateless chunked backward; 8 to 128 MiB for its pallas variant in
+ * the g2h8_d128 fwd_bwd records); ssd_bwd stays the stateless path.  The
+ * library cannot check the precondition: with a workspace that does not
+ * hold the forward's results for these inputs the outputs are wrong (but
+ * every access stays inside the workspace and the tensors).  Arguments,
+ * layouts, ownership, asynchrony and return codes are those of ssd_bwd;
+ * the forward work must be enqueued on the same stream before this call,
+ * or be complete. */
 int ssd_bwd_from_fwd(const ssd_shape *shape,
                      const float *q, const float *k, const float *v,
                      const float *log_alpha, const float *h0, const float *dy,
                      float *dq, float *dk, float *dv, float *dlog_alpha, float *dh0,
                      void *workspace, size_t workspace_bytes, void *stream);
 
-/* Optional per-kernel timing with HIP events, for benchmarks.
- * ssd_kernel_timing_enable(mask) times the launches of the kernels whose bit
- * (1 << kid) is set in `mask` (-1: all kernels; 0: off, the default): their
- * start and stop events are bound to the kernel's own dispatch on the launch
- * stream (hipExtLaunchKernel), so they cover the kernel alone.  A timed
- * dispatch still costs a few microseconds of stream time, so a benchmark
- * that also times whole calls should time only the kernels it needs.
- * ssd_kernel_timing_read synchronizes on the recorded events and returns,
- * for kernel id `kid` (0 <= kid < ssd_kernel_count()), the summed duration
- * in milliseconds and the number of timed launches since the last reset.
- * Process-global, not thread-safe. */
-int ssd_kernel_timing_enable(int mask);
-int ssd_kernel_timing_reset(void);
-int ssd_kernel_timing_read(int kid, double *total_ms, int64_t *count);
+/* Per-kernel timing with HIP events, for benchmarks: the pages time whole
+ * calls (median_ms, q1_ms, q3_ms of every results record); these calls
+ * time the kernels inside a call.  A timer is a caller-owned object; the
+ * plain compute calls never read it.
+ *
+ * ssd_timer_create(mask) returns a timer (NULL if out of host memory) that
+ * times the launches of the kernels whose bit (1 << kid) is set in `mask`
+ * (-1: all kernels).  ssd_fwd_timed / ssd_bwd_timed are ssd_fwd / ssd_bwd
+ * with the timer: the start and stop events of each timed kernel are bound
+ * to the kernel's own dispatch on the launch stream (hipExtLaunchKernel),
+ * so they cover the kernel alone; a timed dispatch still costs a few
+ * microseconds of stream time.  ssd_timer_read synchronizes on the recorded
+ * events and returns, for kernel id `kid` (0 <= kid < ssd_kernel_count()),
+ * the summed duration in milliseconds and the number of timed launches
+ * since the last reset.  ssd_timer_destroy waits for the timer's events and
+ * frees it.  One timer must not be used by two threads at once. */
+typedef struct ssd_timer ssd_timer;
+ssd_timer *ssd_timer_create(int mask);
+int ssd_timer_destroy(ssd_timer *timer);
+int ssd_timer_reset(ssd_timer *timer);
+int ssd_timer_read(ssd_timer *timer, int kid, double *total_ms, int64_t *count);
+int ssd_fwd_timed(ssd_timer *timer, const ssd_shape *shape,
+                  const float *q, const float *k, const float *v,
+                  const float *log_alpha, const float *h0,
+                  float *y,
+                  void *workspace, size_t workspace_bytes, void *stream);
+int ssd_bwd_timed(ssd_timer *timer, const ssd_shape *shape,
+                  const float *q, const float *k, const float *v,
+                  const float *log_alpha, const float *h0, const float *dy,
+                  float *dq, float *dk, float *dv, float *dlog_alpha, float *dh0,
+                  void *workspace, size_t workspace_bytes, void *stream);
 int ssd_kernel_count(void);
 const char *ssd_kernel_name(int kid);
 

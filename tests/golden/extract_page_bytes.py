@@ -1,15 +1,21 @@
-"""Recipe that wrote page_layout_bytes.json from the benchmark pages' text.
+"""Recipe that wrote page_layout_bytes.json from the text of the benchmark
+pages.
 
-It reads the pages as mounted at /root/reference/PAPER.md (three JSON documents,
-one per page) and keeps, for every "chunked" record of kernel_ssd_cpu.json, the
-argument and output byte counts.  It is not run by the tests.
+Source: kernel_ssd_cpu.json, results records of impl "chunked", fields
+xla_arg_mb and xla_out_mb (MiB).  The recipe takes the extracted text of the
+pages as its input (the three JSON documents, each introduced by a line that
+names the page's address) and keeps, for every chunked record of that page,
+the shape and the two byte counts.  It is not run by the tests.
+
+    python extract_page_bytes.py PAGES_TEXT OUT_JSON
 """
 import json
 import re
 import sys
 
-src = sys.argv[1] if len(sys.argv) > 1 else "/root/reference/PAPER.md"
-out = sys.argv[2] if len(sys.argv) > 2 else "page_layout_bytes.json"
+if len(sys.argv) != 3:
+    sys.exit("usage: extract_page_bytes.py PAGES_TEXT OUT_JSON")
+src, out = sys.argv[1], sys.argv[2]
 txt = open(src).read()
 parts = re.split(r"=-=-= page \d of 3: (\S+) =-=-=", txt)
 rows = []

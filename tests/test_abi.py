@@ -91,8 +91,8 @@ def test_empty_problems_need_no_workspace():
 def test_workspace_layout_formula(B, G, H, T, dk, dv):
     s = ssd.ShapeArg(B, G, H, T, dk, dv)
     off = ssd.workspace_layout(s, True)
+    assert len(off) == ssd.WS_REGIONS + 1
     NC = (T + 63) // 64
-    NCp = (NC + 63) // 64 * 64
     Epad = (dk * dv + 63) // 64 * 64
     BH = B * H
 
@@ -100,19 +100,21 @@ def test_workspace_layout_formula(B, G, H, T, dk, dv):
         return (x + 255) // 256 * 256
 
     assert off[0] == 0
-    assert off[1] == up(BH * NC * 64 * 4)
-    assert off[2] == up(off[1] + BH * NCp * 4)
-    assert off[3] == up(off[2] + BH * NC * Epad * 4)
-    # fewer (b, g, chunk) blocks than the 256 CUs: the group's heads are split
-    # over blocks and the backward keeps per-split dq, dk partial sums
+    assert off[1] == up(BH * NC * Epad * 4)
+    assert off[2] == up(off[1] + BH * NC * Epad * 4)
+    # fewer (b, g, chunk) blocks than the device's compute units (256 when no
+    # device is visible): the group's heads are split over blocks and the
+    # backward keeps per-split dq, dk partial sums
     hpg, blocks = H // G, B * G * NC
     want = min(hpg, -(-256 // blocks)) if blocks < 256 else 1
     hpb = -(-hpg // want)
     hsplit = -(-hpg // hpb)
     parts = 2 * hsplit * (-(-(B * G * T * dk) // 64) * 64) * 4 if hsplit > 1 else 0
-    assert off[4] == up(up(off[3] + BH * NC * Epad * 4) + parts)
-    assert ssd.workspace_size(s, True) == off[4]
-    assert ssd.workspace_size(s, False) == off[3]
+    assert off[3] == up(off[2] + parts)
+    assert ssd.workspace_size(s, True) == off[3]
+    fo = ssd.workspace_layout(s, False)
+    assert fo[0] == 0 and fo[1] == fo[2] == fo[3] == off[1]
+    assert ssd.workspace_size(s, False) == off[1]
 
 
 def test_status_strings_and_constants():
@@ -122,7 +124,47 @@ def test_status_strings_and_constants():
     assert lib.ssd_strerror(99) == b"unknown status"
     assert lib.ssd_chunk_size() == ssd.CHUNK == 64
     names = [lib.ssd_kernel_name(i).decode() for i in range(lib.ssd_kernel_count())]
-    assert "bwd_grads" in names and "state_scan" in names
+    assert "bwd_grads" in names and "state_scan" in names and "chunk_output" in names
+    assert lib.ssd_kernel_name(-1) == b"unknown"
+
+
+def test_timer_lifecycle_without_launches():
+    """A timer is a caller-owned object: created, read, reset and destroyed
+    without any launch; the plain compute calls take none."""
+    t = ssd.KernelTimer(["bwd_grads"])
+    res = t.results()
+    assert set(res) == set(t.names) and all(v == (0.0, 0) for v in res.values())
+    t.reset()
+    t.close()
+    lib = ssd.library()
+    assert lib.ssd_timer_destroy(None) == 1
+    assert lib.ssd_timer_reset(None) == 1
+    with pytest.raises(ValueError):
+        ssd.KernelTimer(["no_such_kernel"])
+
+
+def test_timed_calls_validate_like_plain_ones():
+    lib = ssd.library()
+    t = ssd.KernelTimer()
+    p = ctypes.c_void_p(1)
+    bad = ssd.ShapeArg(1, 3, 4, 10, 8, 8)
+    assert lib.ssd_fwd_timed(t.handle, ctypes.byref(bad), *([p] * 7), 0, None) == 2
+    assert lib.ssd_bwd_timed(t.handle, ctypes.byref(bad), *([p] * 12), 0, None) == 2
+    assert lib.ssd_fwd_timed(None, ctypes.byref(bad), *([p] * 7), 0, None) == 1
+    t.close()
+
+
+def test_binding_rejects_foreign_workspace():
+    """The binding checks a caller's workspace before any launch: device,
+    contiguity and the bytes its storage really holds."""
+    import torch
+    s = ssd.ShapeArg(1, 1, 1, 10, 8, 8)
+    need = ssd.workspace_size(s, False)
+    dev = torch.device("cuda:0")
+    with pytest.raises(ValueError, match="HIP device"):
+        ssd._workspace(s, False, dev, torch.empty(need, dtype=torch.uint8))
+    with pytest.raises(TypeError):
+        ssd._workspace(s, False, dev, bytearray(need))
 
 
 def test_binding_rejects_cpu_tensors():

@@ -89,22 +89,21 @@ def test_chunk_states_match_oracle():
     NC = (shape.T + 63) // 64
     E = shape.dk * shape.dv
     Epad = (E + 63) // 64 * 64
-    st = host(ws[off[2]:off[2] + shape.B * shape.H * NC * Epad * 4].view(torch.float32))
+    st = host(ws[off[0]:off[0] + shape.B * shape.H * NC * Epad * 4].view(torch.float32))
     st = st.reshape(shape.B, shape.H, NC, Epad)[..., :E].reshape(shape.B, shape.H, NC, shape.dk, shape.dv)
     _, ref = oracle.fwd(x["q"], x["k"], x["v"], x["log_alpha"], x["h0"], chunk=64)
     assert rel_err(st, ref) <= TOL_Y
-    # within-chunk cumulative log-decay and chunk totals
-    bc = host(ws[off[0]:off[0] + shape.B * shape.H * NC * 64 * 4].view(torch.float32))
-    bc = bc.reshape(shape.B, shape.H, NC * 64)
-    la = np.zeros((shape.B, shape.H, NC * 64))
-    la[..., :shape.T] = x["log_alpha"]
-    ref_b = np.cumsum(la.reshape(shape.B, shape.H, NC, 64), axis=-1).reshape(shape.B, shape.H, -1)
-    assert rel_err(bc, ref_b) <= 1e-6
+    # per chunk as well: a state that decays to nothing would hide in the
+    # whole-tensor maximum (the within-chunk cumulative log-decay that weighs
+    # every contribution is checked through these)
+    for c in range(NC):
+        assert rel_err(st[:, :, c], ref[:, :, c]) <= 1e-4, c
 
 
-@pytest.mark.parametrize("idx", [0, 1, 2])
+@pytest.mark.parametrize("idx", [0, 1, 2, 3, 4])
 def test_workload_full_size(idx):
-    """Full-size parity on the three smaller workloads (whole tensors)."""
+    """Full-size parity on all five workloads, whole tensors (the pages'
+    rel_err is a whole-tensor metric)."""
     need_gpu()
     w = WORKLOADS[idx]
     say(f"workload {w.name}")
@@ -113,30 +112,18 @@ def test_workload_full_size(idx):
     check_bwd(x)
 
 
-@pytest.mark.parametrize("name,b,g", [("g1h24_dk128_dv64_T8192", 1, 0), ("g2h8_d128_T8192", 3, 1),
-                                      ("g2h8_d128_T8192", 0, 0)])
-def test_workload_large_sampled(name, b, g):
-    """Large workloads: the HIP path runs the whole problem; the oracle
-    recomputes one (batch, group) slice, which depends on nothing else."""
+@pytest.mark.parametrize("T", [65536, 131072])
+def test_long_sequence_unit(T):
+    """One independent unit at the headline's head and state sizes (B=1, G=1,
+    H=4, dk=dv=128), far beyond the workloads' T: the GPU page's chunked path
+    reaches T = 65536 at most (kernel_ssd_gpu.json, max_len record).  The
+    whole tensors of y and of all five gradients against the oracle."""
     need_gpu()
-    w = workload(name)
-    s = w.shape
-    hpg = s.hpg
-    say(f"workload {name} slice b={b} g={g}")
-    x = make_inputs(s, w.seed, mu=w.mu)
-    d = to_dev(x)
-    y = host(hip_fwd(d))
-    gr = {k: host(v) for k, v in hip_bwd(d).items()}
-    hs = slice(g * hpg, (g + 1) * hpg)
-    xs = {"q": x["q"][b:b + 1, g:g + 1], "k": x["k"][b:b + 1, g:g + 1], "v": x["v"][b:b + 1, hs],
-          "log_alpha": x["log_alpha"][b:b + 1, hs], "h0": x["h0"][b:b + 1, hs], "dy": x["dy"][b:b + 1, hs]}
-    ref_y = oracle.fwd(xs["q"], xs["k"], xs["v"], xs["log_alpha"], xs["h0"])
-    assert rel_err(y[b:b + 1, hs], ref_y) <= TOL_Y
-    ref = oracle.bwd(xs["q"], xs["k"], xs["v"], xs["log_alpha"], xs["h0"], xs["dy"])
-    got = {"dq": gr["dq"][b:b + 1, g:g + 1], "dk": gr["dk"][b:b + 1, g:g + 1], "dv": gr["dv"][b:b + 1, hs],
-           "dlog_alpha": gr["dlog_alpha"][b:b + 1, hs], "dh0": gr["dh0"][b:b + 1, hs]}
-    errs = {k: rel_err(got[k], ref[k]) for k in GRADS}
-    assert all(e <= TOL_G for e in errs.values()), errs
+    s = Shape(1, 1, 4, T, 128, 128)
+    say(f"long sequence T={T}")
+    x = make_inputs(s, seed=4000 + T // 65536)
+    check_fwd(x)
+    check_bwd(x)
 
 
 def test_headline_identities_full_size():
@@ -315,3 +302,49 @@ def test_empty_shapes():
     dq, dk, dv, dla, dh0 = ssd.bwd(x["q"], x["k"], x["v"], x["log_alpha"], x["h0"], x["dy"])
     torch.cuda.synchronize()
     assert torch.count_nonzero(dh0).item() == 0
+
+
+def test_timed_calls_match_plain_ones():
+    """ssd_fwd_timed / ssd_bwd_timed give bitwise the plain calls' outputs and
+    record one launch per timed kernel and call."""
+    need_gpu()
+    import torch
+    import chunked_ssd_scan_fwd_amd as ssd
+    s = Shape(2, 2, 4, 300, 64, 64)
+    x = make_inputs(s, 21)
+    d = to_dev(x)
+    say("timed calls")
+    y0 = host(hip_fwd(d))
+    g0 = {k: host(v) for k, v in hip_bwd(d).items()}
+    with ssd.KernelTimer() as t:
+        y1 = ssd.fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["h0"], timer=t)
+        g1 = ssd.bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["h0"], d["dy"], timer=t)
+        torch.cuda.synchronize()
+        res = t.results()
+    np.testing.assert_array_equal(host(y1), y0)
+    for name, a in zip(GRADS, g1):
+        np.testing.assert_array_equal(host(a), g0[name])
+    for kname in ("state_scan", "chunk_output", "state_scan_bidir", "bwd_grads"):
+        assert res[kname][1] == 1 and res[kname][0] > 0, (kname, res[kname])
+
+
+def test_binding_rejects_short_or_strided_workspace():
+    """A workspace view whose storage holds fewer bytes than needed, or a
+    strided one, is refused before anything is launched."""
+    need_gpu()
+    import torch
+    import chunked_ssd_scan_fwd_amd as ssd
+    s = Shape(1, 1, 2, 100, 32, 32)
+    d = to_dev(make_inputs(s, 22))
+    sa = ssd.ShapeArg(s.B, s.G, s.H, s.T, s.dk, s.dv)
+    need = ssd.workspace_size(sa, False)
+    say("workspace checks")
+    base = torch.empty(need, dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError):   # starts 16 bytes in: 16 bytes short
+        ssd.fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["h0"], workspace=base[16:])
+    wide = torch.empty(2 * need, dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError):   # every other byte: not contiguous
+        ssd.fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["h0"], workspace=wide[::2])
+    x = make_inputs(s, 22)
+    y = ssd.fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["h0"], workspace=base)
+    assert rel_err(host(y), oracle.fwd(x["q"], x["k"], x["v"], x["log_alpha"], x["h0"])) <= TOL_Y

@@ -19,7 +19,7 @@ __all__ = ["fwd", "bwd", "library", "ShapeArg", "SsdError", "workspace_size",
            "workspace_layout", "KernelTimer", "CHUNK", "bwd_from_fwd", "WS_REGIONS"]
 
 CHUNK = 64
-WS_REGIONS = 3   # SSD_WS_REGIONS: states, dstates, split partial sums
+WS_REGIONS = 4   # SSD_WS_REGIONS: decay weights, states, dstates, split partial sums
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libssd_hip.so")
 _lib = None

@@ -1,6 +1,5 @@
-// The fused chunk-state and state-pass scan (K3 + K4, and the reverse pass
-// of the backward) for gfx950, with the per-chunk cumulative log-decay (K1)
-// formed in its loader waves.
+// The per-chunk cumulative log-decay (K1) and the fused chunk-state and
+// state-pass scan (K3 + K4, and the reverse pass of the backward) for gfx950.
 #include "ssd_device.h"
 #include "ssd_launch.h"
 
@@ -40,14 +39,40 @@ namespace ssd {
 // NU consecutive floats gives a lane all its B operands.  Blocks of one
 // (b, g) are placed on one XCD so that the group's q/k and each head's v/dy
 // tiles are shared through that XCD's L2.
+// K1: per-chunk cumulative log-decay, turned into what the scan's loader
+// waves apply.  One wave per (b, h, chunk), lane t at position 64 c + t
+// (positions past T read log_alpha = 0, so they repeat the last b):
+//   wts[bh][c][t]      = e^{b_L - b_t}   (forward: weight of k_t in X_c)
+//   wts[bh][c][64 + t] = e^{b_t}         (reverse: weight of dy_t in Z_c)
+//   cdec[bh][c]        = e^{b_L}         (decay of the state over the chunk)
+// b comes from chunk_cumsum, as in every other kernel, so all of them see
+// the same b bitwise.
+constexpr int NTP = 256;
+__global__ __launch_bounds__(NTP) void k_chunk_decay(const float *__restrict__ la, float *__restrict__ wts,
+                                                     float *__restrict__ cdec, int64_t T, int64_t NC, int64_t nwaves)
+{
+    const int64_t wv = (int64_t)blockIdx.x * (NTP / 64) + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (wv >= nwaves) return;   // whole waves only
+    const int64_t bh = wv / NC, c = wv - bh * NC;
+    const int64_t rows = (T - c * CH) < CH ? (T - c * CH) : CH;
+    const float x = gload1(make_rsrc(la + bh * T + c * CH, rows * 4), (uint32_t)lane * 4u);
+    const float b = chunk_cumsum(x);
+    const float bL = readlane_f(b, 63);
+    float *w = wts + wv * (2 * CH);
+    w[lane] = __expf(bL - b);
+    w[CH + lane] = __expf(b);
+    if (lane == 0) cdec[wv] = expf(bL);
+}
+
 constexpr int TI = 32;
 constexpr int NTS = 512;        // 4 compute + 4 loader waves
 
 template <int DKP, int DVP, bool VEC, int TJ, int CPS, bool EXD>
 __global__ __launch_bounds__(NTS) void k_state_scan(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
-    const float *__restrict__ dy, const float *__restrict__ h0, const float *__restrict__ la,
-    float *__restrict__ states, float *__restrict__ dstates, float *__restrict__ dh0, int G, int H, int64_t T,
+    const float *__restrict__ dy, const float *__restrict__ h0, const float *__restrict__ wts,
+    const float *__restrict__ cdec, float *__restrict__ states, float *__restrict__ dstates, float *__restrict__ dh0, int G, int H, int64_t T,
     int dk, int dv, int64_t NC, int64_t Epad, int64_t per_dir, int dir0)
 {
     static_assert(TJ <= DVP && DVP % TJ == 0 && (TJ == 32 || TJ == 64 || TJ == 128), "tile width");
@@ -95,11 +120,13 @@ __global__ __launch_bounds__(NTS) void k_state_scan(
         const int lt = threadIdx.x - 256;
         const float *Asrc = (dir == 0 ? k : q) + (b * G + g) * T * dk;   // row 0, column 0
         const float *Bsrc = (dir == 0 ? v : dy) + bh * T * dv;
-        const float *lab = la + bh * T;
+        const float *wb = wts + bh * NC * (2 * CH) + (dir == 0 ? 0 : CH);   // this direction's weights
+        const rsrc_t dr = make_rsrc(cdec + bh * NC, NC * 4);
         const int lima = dk - i0, limb = dv - j0;
         struct Stage {
             float4 a[APER], b[BPER];
-            float la;   // log_alpha of the chunk's position (lt % 64)
+            float w[APER], dec;   // decay weights of the A rows, e^{b_L} of the chunk
+            bool live;
         };
         Stage stg[PD][CPS];
         // operands of chunk n of the scan order; chunks past the end load zeros
@@ -109,36 +136,31 @@ __global__ __launch_bounds__(NTS) void k_state_scan(
             const int rows = (int)((T - c * CH) < CH ? (T - c * CH) : CH);
             const rsrc_t ab = make_rsrc(Asrc + c * CH * dk, live ? (int64_t)rows * dk * 4 : 0);
             const rsrc_t bb = make_rsrc(Bsrc + c * CH * dv, live ? (int64_t)rows * dv * 4 : 0);
-            const rsrc_t lr = make_rsrc(lab + c * CH, live ? (int64_t)rows * 4 : 0);
+            const rsrc_t wr = make_rsrc(wb + c * (2 * CH), live ? CH * 4 : 0);
 #pragma unroll
             for (int u = 0; u < APER; ++u) {
                 const int r = f4_row<TI / 4, NLT>(lt, u), c4 = f4_col<TI / 4>(lt);
                 const bool ok = A4 % NLT == 0 || r < CH;
                 S.a[u] = load4(ab, (uint32_t)(r * dk + i0), c4, lima, ok, VEC);
+                S.w[u] = gload1(wr, ok ? (uint32_t)r * 4u : kOOB);
             }
 #pragma unroll
             for (int u = 0; u < BPER; ++u) {
                 const int r = f4_row<TJ / 4, NLT>(lt, u), c4 = f4_col<TJ / 4>(lt);
                 S.b[u] = load4(bb, (uint32_t)(r * dv + j0), c4, limb, B4 % NLT == 0 || r < CH, VEC);
             }
-            // positions past the sequence end read 0 and repeat the last b
-            S.la = gload1(lr, (uint32_t)(lt & 63) * 4u);
+            // a vector load: a scalar one would be waited for right here
+            S.dec = gload1(dr, live ? (uint32_t)c * 4u : kOOB);
+            S.live = live;
         };
         // stage S into LDS half `buf`, slot cc; the rows of the A tile (TI
-        // wide, the narrower one) are scaled by the decay weights, formed
-        // here from the chunk's cumulative log-decay (each loader wave scans
-        // the chunk's 64 log_alpha values and fetches b at its rows)
+        // wide, the narrower one) are scaled by the decay weights
         auto stage = [&](const Stage &S, int buf, int cc) {
-            const float bc = chunk_cumsum(S.la);
-            const float bL = readlane_f(bc, 63);
-            float brow[APER];
-#pragma unroll
-            for (int u = 0; u < APER; ++u) brow[u] = __shfl(bc, f4_row<TI / 4, NLT>(lt, u) & 63);
 #pragma unroll
             for (int u = 0; u < APER; ++u) {
                 const int r = f4_row<TI / 4, NLT>(lt, u), c4 = f4_col<TI / 4>(lt);
                 if (A4 % NLT == 0 || r < CH) {
-                    const float w = (dir == 0) ? __expf(bL - brow[u]) : __expf(brow[u]);
+                    const float w = S.w[u];
                     float4 x = S.a[u];
                     x.x *= w;
                     x.y *= w;
@@ -154,7 +176,8 @@ __global__ __launch_bounds__(NTS) void k_state_scan(
                     *reinterpret_cast<float4 *>(&Bs[buf][cc][r * LDB + c4]) = S.b[u];
                 }
             }
-            if (lt == 0) decs[buf][cc] = expf(bL);
+            // chunks past the end leave the state as it is
+            if (lt == 0) decs[buf][cc] = S.live ? S.dec : 1.f;
         };
         // step s: its chunks are published by the barrier; stage step s + 1
         // into the other half and refill its registers with step s + 1 + PD
@@ -284,11 +307,17 @@ __global__ __launch_bounds__(NTS) void k_state_scan(
     }
 }
 // The fused state scan over the directions in `dirs` (see ssd_launch.h).
-int run_scan(const Problem &P, int dirs, const float *q, const float *k, const float *v, const float *dy,
-             const float *la, const float *h0, float *dh0, hipStream_t st)
+int run_scan(const Problem &P, int dirs, bool prep, const float *q, const float *k, const float *v,
+             const float *dy, const float *la, const float *h0, float *dh0, hipStream_t st)
 {
     const ssd_shape &s = P.s;
     const int64_t BH = s.B * s.H;
+    if (prep) {
+        const int64_t nw = BH * P.L.NC;
+        launch(P.timer, KID_AUX, k_chunk_decay, dim3((unsigned)((nw + 3) / 4)), dim3(NTP), st, la, P.wts, P.cdec,
+               s.T, P.L.NC, nw);
+        if (launch_status() != SSD_OK) return SSD_ERR_DEVICE;
+    }
     // Two chunks per step when there is at most one block per CU (the paired
     // tiles fill most of a CU's LDS); otherwise one.  State tiles are 32 x 64
     // (32 x dv for dv < 64): wider tiles re-read fewer operand tiles but
@@ -308,11 +337,11 @@ int run_scan(const Problem &P, int dirs, const float *q, const float *k, const f
             const int64_t per_dir = tiles_k * (VP / TJ);
             const dim3 grid((unsigned)(ndir * per_dir)), blk(NTS);
             if (pair)
-                launch(P.timer, kid, k_state_scan<KP, VP, VE, TJ, 2, EXD>, grid, blk, st, q, k, v, dy, h0, la,
+                launch(P.timer, kid, k_state_scan<KP, VP, VE, TJ, 2, EXD>, grid, blk, st, q, k, v, dy, h0, P.wts, P.cdec,
                        P.states, P.dstates, dh0, (int)s.G, (int)s.H, s.T, (int)s.dk, (int)s.dv, P.L.NC, P.L.Epad,
                        per_dir, dir0);
             else
-                launch(P.timer, kid, k_state_scan<KP, VP, VE, TJ, 1, EXD>, grid, blk, st, q, k, v, dy, h0, la,
+                launch(P.timer, kid, k_state_scan<KP, VP, VE, TJ, 1, EXD>, grid, blk, st, q, k, v, dy, h0, P.wts, P.cdec,
                        P.states, P.dstates, dh0, (int)s.G, (int)s.H, s.T, (int)s.dk, (int)s.dv, P.L.NC, P.L.Epad,
                        per_dir, dir0);
         }));

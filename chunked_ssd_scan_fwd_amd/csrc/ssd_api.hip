@@ -59,9 +59,11 @@ static int prepare(const ssd_shape *shape, bool backward, void *ws, size_t ws_by
     P->vec = (shape->dk % 4) == 0 && (shape->dv % 4) == 0;
     P->exact = shape->dk == P->DKP && shape->dv == P->DVP;
     char *w = static_cast<char *>(ws);
-    P->states = reinterpret_cast<float *>(w + P->L.off[0]);
-    P->dstates = backward ? reinterpret_cast<float *>(w + P->L.off[1]) : nullptr;
-    P->parts = backward && P->L.hsplit > 1 ? reinterpret_cast<float *>(w + P->L.off[2]) : nullptr;
+    P->wts = reinterpret_cast<float *>(w + P->L.off[0]);
+    P->cdec = reinterpret_cast<float *>(w + P->L.cdec_off);
+    P->states = reinterpret_cast<float *>(w + P->L.off[1]);
+    P->dstates = backward ? reinterpret_cast<float *>(w + P->L.off[2]) : nullptr;
+    P->parts = backward && P->L.hsplit > 1 ? reinterpret_cast<float *>(w + P->L.off[3]) : nullptr;
     P->timer = tm;
     return SSD_OK;
 }
@@ -81,14 +83,14 @@ static int fwd_impl(const ssd_shape *shape, const float *q, const float *k, cons
     rc = prepare(shape, false, workspace, workspace_bytes, tm, &P);
     if (rc != SSD_OK) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    rc = run_scan(P, 1, q, k, v, nullptr, log_alpha, h0, nullptr, st);
+    rc = run_scan(P, 1, true, q, k, v, nullptr, log_alpha, h0, nullptr, st);
     if (rc != SSD_OK) return rc;
     return run_output(P, q, k, v, log_alpha, y, st);
 }
 
-// Backward launches.  With `reuse`, the workspace already holds S_in of every
-// chunk as ssd_fwd wrote it for these inputs, so only the reverse state pass
-// and the gradient kernel run.
+// Backward launches.  With `reuse`, the workspace already holds the decay
+// weights and S_in of every chunk as ssd_fwd wrote them for these inputs, so
+// only the reverse state pass and the gradient kernel run.
 static int bwd_impl(const ssd_shape *shape, const float *q, const float *k, const float *v,
                     const float *log_alpha, const float *h0, const float *dy, float *dq, float *dk, float *dv,
                     float *dlog_alpha, float *dh0, void *workspace, size_t workspace_bytes, void *stream, bool reuse,
@@ -115,9 +117,9 @@ static int bwd_impl(const ssd_shape *shape, const float *q, const float *k, cons
     Problem P;
     rc = prepare(shape, true, workspace, workspace_bytes, tm, &P);
     if (rc != SSD_OK) return rc;
-    // dS_out (reverse) of every chunk and dh0; without reuse also S_in
-    // (forward), in the same launch.
-    rc = run_scan(P, reuse ? 2 : 3, q, k, v, dy, log_alpha, h0, dh0, st);
+    // dS_out (reverse) of every chunk and dh0; without reuse also the decay
+    // weights and S_in (forward), the latter in the same launch.
+    rc = run_scan(P, reuse ? 2 : 3, !reuse, q, k, v, dy, log_alpha, h0, dh0, st);
     if (rc != SSD_OK) return rc;
     return run_grads(P, q, k, v, dy, log_alpha, dq, dk, dv, dlog_alpha, st);
 }

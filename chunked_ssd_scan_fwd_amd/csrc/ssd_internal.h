@@ -16,13 +16,14 @@ struct Layout {
     int64_t NC = 0;      // chunks per sequence, ceil(T / 64)
     int64_t E = 0;       // dk * dv
     int64_t Epad = 0;    // E rounded up to a multiple of 64 (slab stride, floats)
-    // byte offsets: states, dstates, split partial sums, total
-    size_t off[SSD_WS_REGIONS + 1] = {0, 0, 0, 0};
+    // byte offsets: decay weights, states, dstates, split partial sums, total
+    size_t off[SSD_WS_REGIONS + 1] = {0, 0, 0, 0, 0};
+    size_t cdec_off = 0;   // per-chunk decays, inside the decay region
     // The output and gradient kernels take one block per (b, g, chunk) and loop
     // over the group's heads.  With fewer such blocks than CUs a group's heads
     // are split over `hsplit` blocks of `hpb` heads each (the last may hold
     // fewer); the gradient kernel then writes per-split partial sums of dq and
-    // dk, [2][hsplit][nqk_pad] floats at byte offset off[2], which a small
+    // dk, [2][hsplit][nqk_pad] floats at byte offset off[3], which a small
     // kernel adds up in split order.
     int hsplit = 1;
     int hpb = 1;

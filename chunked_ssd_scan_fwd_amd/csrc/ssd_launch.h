@@ -117,17 +117,19 @@ struct Problem {
     bool vec;     // dk and dv multiples of 4: 16-byte loads
     bool exact;   // dk == DKP and dv == DVP: the kernels' index arithmetic on constants
     int cus;      // compute units of the device
+    float *wts, *cdec;   // per-position decay weights and per-chunk decays (scan input)
     float *states, *dstates;
     float *parts;   // split partial sums of dq, dk (backward with hsplit > 1), else null
     ssd_timer *timer;
 };
 
-// Fused chunk-state + state-pass scan over the directions in `dirs`: 1 =
+// With `prep`, the per-chunk decay weights from log_alpha first; then the
+// fused chunk-state + state-pass scan over the directions in `dirs`: 1 =
 // forward only (fills `states` with S_in), 3 = both in one launch (also
 // fills `dstates` with dS_out and writes dh0), 2 = reverse only (dstates and
-// dh0; `states` is not touched).
-int run_scan(const Problem &P, int dirs, const float *q, const float *k, const float *v, const float *dy,
-             const float *la, const float *h0, float *dh0, hipStream_t st);
+// dh0; `states` is not touched, the weights must be in place).
+int run_scan(const Problem &P, int dirs, bool prep, const float *q, const float *k, const float *v,
+             const float *dy, const float *la, const float *h0, float *dh0, hipStream_t st);
 
 // Output of every chunk: y = intra-chunk term + diag(e^b) Q S_in.
 int run_output(const Problem &P, const float *q, const float *k, const float *v, const float *la, float *y,

@@ -54,12 +54,16 @@ Layout make_layout(const ssd_shape *s, bool backward, int cus)
     const size_t slab = BH * size_t(L.NC) * size_t(L.Epad) * sizeof(float);
     size_t o = 0;
     L.off[0] = o;
-    o = round_up(o + slab, 256);
+    o = round_up(o + BH * size_t(L.NC) * 2 * kChunk * sizeof(float), 256);
+    L.cdec_off = o;
+    o = round_up(o + BH * size_t(L.NC) * sizeof(float), 256);
     L.off[1] = o;
-    if (backward) o = round_up(o + slab, 256);
+    o = round_up(o + slab, 256);
     L.off[2] = o;
-    if (backward && L.hsplit > 1) o = round_up(o + 2 * size_t(L.hsplit) * size_t(L.nqk_pad) * sizeof(float), 256);
+    if (backward) o = round_up(o + slab, 256);
     L.off[3] = o;
+    if (backward && L.hsplit > 1) o = round_up(o + 2 * size_t(L.hsplit) * size_t(L.nqk_pad) * sizeof(float), 256);
+    L.off[4] = o;
     return L;
 }
 

@@ -125,21 +125,25 @@ int ssd_bwd(const ssd_shape *shape,
             void *workspace, size_t workspace_bytes, void *stream);
 
 /* Number of workspace regions reported by ssd_workspace_layout. */
-#define SSD_WS_REGIONS 3
+#define SSD_WS_REGIONS 4
 
 /* Byte offsets of the workspace regions, in this order:
- *   [0] states  float [B*H][NC][E]  after ssd_fwd/ssd_bwd: the state entering
- *                                   each chunk, row-major dk x dv; NC =
- *                                   ceil(T/64), E = dk*dv rounded up to a
- *                                   multiple of 64
- *   [1] dstates float [B*H][NC][E]  (backward only; empty otherwise) after
+ *   [0] decay   float [B*H][NC][2][64], then float [B*H][NC] at the next
+ *               256-byte boundary: per position of chunk c, e^{b_L - b_t}
+ *               and e^{b_t}, and per chunk e^{b_L}, where b_t is the
+ *               within-chunk inclusive cumulative sum of log_alpha and b_L
+ *               its value at the chunk's last position; NC = ceil(T/64)
+ *   [1] states  float [B*H][NC][E]  after ssd_fwd/ssd_bwd: the state entering
+ *                                   each chunk, row-major dk x dv; E = dk*dv
+ *                                   rounded up to a multiple of 64
+ *   [2] dstates float [B*H][NC][E]  (backward only; empty otherwise) after
  *                                   ssd_bwd: the gradient of the state
  *                                   leaving each chunk
- *   [2] parts   (backward only) when B*G*ceil(T/64) is below the device's
+ *   [3] parts   (backward only) when B*G*ceil(T/64) is below the device's
  *               compute-unit count: per-block-split partial sums of dq and
  *               dk that the gradient kernel writes and a final kernel adds
  *               up (no caller use); empty otherwise
- *   [3] total bytes.
+ *   [4] total bytes.
  * `backward` selects the backward layout.  Returns SSD_OK or an error.
  * Test support: the states are the quantity the chunked method passes
  * between chunks, checked against the oracle's state at chunk boundaries. */
@@ -155,9 +159,9 @@ int ssd_chunk_size(void);
 /* Backward that reuses the forward's residuals: the same outputs as ssd_bwd,
  * but the workspace must already hold what ssd_fwd wrote for the SAME inputs
  * (q, k, v, log_alpha, h0 and shape) into a workspace of at least
- * ssd_bwd_workspace_size(shape) bytes: the forward's region (the state
- * entering every chunk) sits at the same offset in the forward and backward
- * layouts.  Only the reverse state pass and the gradient kernel run, which
+ * ssd_bwd_workspace_size(shape) bytes: the forward's regions (the decay
+ * weights and the state entering every chunk) sit at the same offsets in the
+ * forward and backward layouts.  Only the reverse state pass and the gradient kernel run, which
  * skips recomputing the forward states.  This is the residual-keeping side
  * of the trade-off that kernel_ssd_gpu.json records in residual_mb (0.0 for
  * the stateless chunked backward; 8 to 128 MiB for its pallas variant in

@@ -100,8 +100,10 @@ def test_workspace_layout_formula(B, G, H, T, dk, dv):
         return (x + 255) // 256 * 256
 
     assert off[0] == 0
-    assert off[1] == up(BH * NC * Epad * 4)
+    cdec = up(BH * NC * 128 * 4)
+    assert off[1] == up(cdec + BH * NC * 4)
     assert off[2] == up(off[1] + BH * NC * Epad * 4)
+    assert off[3] == up(off[2] + BH * NC * Epad * 4)
     # fewer (b, g, chunk) blocks than the device's compute units (256 when no
     # device is visible): the group's heads are split over blocks and the
     # backward keeps per-split dq, dk partial sums
@@ -110,11 +112,11 @@ def test_workspace_layout_formula(B, G, H, T, dk, dv):
     hpb = -(-hpg // want)
     hsplit = -(-hpg // hpb)
     parts = 2 * hsplit * (-(-(B * G * T * dk) // 64) * 64) * 4 if hsplit > 1 else 0
-    assert off[3] == up(off[2] + parts)
-    assert ssd.workspace_size(s, True) == off[3]
+    assert off[4] == up(off[3] + parts)
+    assert ssd.workspace_size(s, True) == off[4]
     fo = ssd.workspace_layout(s, False)
-    assert fo[0] == 0 and fo[1] == fo[2] == fo[3] == off[1]
-    assert ssd.workspace_size(s, False) == off[1]
+    assert fo[:2] == off[:2] and fo[2] == fo[3] == fo[4] == off[2]
+    assert ssd.workspace_size(s, False) == off[2]
 
 
 def test_status_strings_and_constants():

@@ -89,7 +89,7 @@ def test_chunk_states_match_oracle():
     NC = (shape.T + 63) // 64
     E = shape.dk * shape.dv
     Epad = (E + 63) // 64 * 64
-    st = host(ws[off[0]:off[0] + shape.B * shape.H * NC * Epad * 4].view(torch.float32))
+    st = host(ws[off[1]:off[1] + shape.B * shape.H * NC * Epad * 4].view(torch.float32))
     st = st.reshape(shape.B, shape.H, NC, Epad)[..., :E].reshape(shape.B, shape.H, NC, shape.dk, shape.dv)
     _, ref = oracle.fwd(x["q"], x["k"], x["v"], x["log_alpha"], x["h0"], chunk=64)
     assert rel_err(st, ref) <= TOL_Y
@@ -98,6 +98,20 @@ def test_chunk_states_match_oracle():
     # every contribution is checked through these)
     for c in range(NC):
         assert rel_err(st[:, :, c], ref[:, :, c]) <= 1e-4, c
+    # the per-chunk cumulative log-decay, as the decay weights the scan applies:
+    # e^{b_L - b_t}, e^{b_t} per position and e^{b_L} per chunk, against the
+    # fp64 cumulative sums of the same log_alpha (positions past T add 0)
+    BH = shape.B * shape.H
+    wts = host(ws[off[0]:off[0] + BH * NC * 128 * 4].view(torch.float32)).reshape(BH, NC, 2, 64)
+    cd0 = (BH * NC * 128 * 4 + 255) // 256 * 256
+    cdec = host(ws[cd0:cd0 + BH * NC * 4].view(torch.float32)).reshape(BH, NC)
+    la = np.zeros((BH, NC * 64))
+    la[:, :shape.T] = x["log_alpha"].reshape(BH, shape.T)
+    b = np.cumsum(la.reshape(BH, NC, 64), axis=-1)
+    bL = b[..., -1:]
+    assert rel_err(wts[:, :, 0], np.exp(bL - b)) <= 1e-5
+    assert rel_err(wts[:, :, 1], np.exp(b)) <= 1e-5
+    assert rel_err(cdec, np.exp(bL[..., 0])) <= 1e-5
 
 
 @pytest.mark.parametrize("idx", [0, 1, 2, 3, 4])

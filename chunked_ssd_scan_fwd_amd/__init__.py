@@ -16,10 +16,12 @@ import ctypes
 import os
 
 __all__ = ["fwd", "bwd", "library", "ShapeArg", "SsdError", "workspace_size",
-           "workspace_layout", "KernelTimer", "CHUNK", "bwd_from_fwd", "WS_REGIONS"]
+           "workspace_layout", "KernelTimer", "CHUNK", "bwd_from_fwd", "WS_REGIONS", "fwd_noalloc",
+           "NOALLOC_WORKSPACE_BYTES"]
 
 CHUNK = 64
 WS_REGIONS = 4   # SSD_WS_REGIONS: decay weights, states, dstates, split partial sums
+NOALLOC_WORKSPACE_BYTES = 96 << 20   # SSD_NOALLOC_WORKSPACE_BYTES
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libssd_hip.so")
 _lib = None
@@ -54,6 +56,8 @@ def library(path: str | None = None):
     lib.ssd_bwd_workspace_size.restype = sz
     lib.ssd_fwd.argtypes = [sp] + [vp] * 6 + [vp, sz, vp]
     lib.ssd_fwd.restype = ctypes.c_int
+    lib.ssd_fwd_noalloc.argtypes = [sp] + [vp] * 6 + [vp]
+    lib.ssd_fwd_noalloc.restype = ctypes.c_int
     lib.ssd_bwd.argtypes = [sp] + [vp] * 11 + [vp, sz, vp]
     lib.ssd_bwd.restype = ctypes.c_int
     lib.ssd_bwd_from_fwd.argtypes = [sp] + [vp] * 11 + [vp, sz, vp]
@@ -174,6 +178,30 @@ def fwd(q, k, v, log_alpha, h0, *, out=None, workspace=None, timer=None):
     rc = lib.ssd_fwd(*args) if timer is None else lib.ssd_fwd_timed(timer.handle, *args)
     if rc != 0:
         raise SsdError(rc, "ssd_fwd")
+    return out
+
+
+def fwd_noalloc(q, k, v, log_alpha, h0, *, out=None):
+    """`fwd` through ssd_fwd_noalloc: the library takes the workspace from its
+    static per-device array (SSD_NOALLOC_WORKSPACE_BYTES), so the C call
+    allocates nothing.  Pass `out` to allocate nothing here either.  Calls
+    that overlap in time on one GPU share that array and race."""
+    import torch
+    lib = library()
+    s = _shape_of(q, v)
+    dev = q.device
+    _check(q, "q", (s.B, s.G, s.T, s.dk), dev)
+    _check(k, "k", (s.B, s.G, s.T, s.dk), dev)
+    _check(v, "v", (s.B, s.H, s.T, s.dv), dev)
+    _check(log_alpha, "log_alpha", (s.B, s.H, s.T), dev)
+    _check(h0, "h0", (s.B, s.H, s.dk, s.dv), dev)
+    if out is None:
+        out = torch.empty((s.B, s.H, s.T, s.dv), dtype=torch.float32, device=dev)
+    _check(out, "out", (s.B, s.H, s.T, s.dv), dev)
+    rc = lib.ssd_fwd_noalloc(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(h0),
+                             _ptr(out), _stream(dev))
+    if rc != 0:
+        raise SsdError(rc, "ssd_fwd_noalloc")
     return out
 
 

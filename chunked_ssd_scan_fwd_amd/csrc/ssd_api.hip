@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <mutex>
 #include <new>
 
 #include "ssd.h"
@@ -42,6 +43,38 @@ int device_cus()
     }
     cache[dev].store(n, std::memory_order_relaxed);
     return n;
+}
+
+// Workspace of ssd_fwd_noalloc: a file-scope device array, one copy per GPU
+// the library runs on, held until the process ends.  In host code its name
+// stands for a host-side shadow, never for device memory: every use goes
+// through the device address that hipGetSymbolAddress returns for the
+// current device (static_ws_ptr), never through the name.
+static __device__ __align__(256) unsigned char scratch[SSD_NOALLOC_WORKSPACE_BYTES];
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and cached; NULL if it cannot be had.
+static void *static_ws_ptr()
+{
+    static std::atomic<void *> cache[kMaxDevices];
+    static std::mutex mu;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    void *p = cache[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    std::lock_guard<std::mutex> lock(mu);
+    p = cache[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    void *addr = nullptr;
+    if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || !addr) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    cache[dev].store(addr, std::memory_order_release);
+    return addr;
 }
 
 static int prepare(const ssd_shape *shape, bool backward, void *ws, size_t ws_bytes, ssd_timer *tm, Problem *P)
@@ -157,6 +190,24 @@ int ssd_fwd(const ssd_shape *shape, const float *q, const float *k, const float 
             const float *h0, float *y, void *workspace, size_t workspace_bytes, void *stream)
 {
     return fwd_impl(shape, q, k, v, log_alpha, h0, y, workspace, workspace_bytes, stream, nullptr);
+}
+
+int ssd_fwd_noalloc(const ssd_shape *shape, const float *q, const float *k, const float *v, const float *log_alpha,
+                    const float *h0, float *y, void *stream)
+{
+    // The same checks and launches as ssd_fwd; the workspace is the static
+    // array.  Nothing is allocated, and the forward's workspace needs no
+    // clearing (every region is written before it is read).
+    int rc = check_shape(shape);
+    if (rc != SSD_OK) return rc;
+    const size_t need = make_layout(shape, false, device_cus()).off[SSD_WS_REGIONS];
+    if (need > SSD_NOALLOC_WORKSPACE_BYTES) return SSD_ERR_WORKSPACE;
+    void *ws = nullptr;
+    if (need > 0) {
+        ws = static_ws_ptr();
+        if (!ws) return SSD_ERR_DEVICE;
+    }
+    return fwd_impl(shape, q, k, v, log_alpha, h0, y, ws, SSD_NOALLOC_WORKSPACE_BYTES, stream, nullptr);
 }
 
 int ssd_bwd(const ssd_shape *shape, const float *q, const float *k, const float *v, const float *log_alpha,

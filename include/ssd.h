@@ -124,6 +124,27 @@ int ssd_bwd(const ssd_shape *shape,
             float *dq, float *dk, float *dv, float *dlog_alpha, float *dh0,
             void *workspace, size_t workspace_bytes, void *stream);
 
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * forward as ssd_fwd, with the same arguments less the workspace, which is
+ * a file-scope device array of SSD_NOALLOC_WORKSPACE_BYTES (96 MiB) inside
+ * the library: each GPU the library runs on holds its own copy until the
+ * process ends.  The call allocates nothing (no hipMalloc, no library
+ * allocation); the caller still passes the inputs and y.  Shapes whose
+ * ssd_fwd_workspace_size exceeds the array return SSD_ERR_WORKSPACE before
+ * anything is enqueued (every workload of the pages at T <= 2048 fits; the
+ * largest, g2h8_d128 at T = 2048, needs 64.5 MiB).  Every call on one GPU
+ * shares that GPU's array, so calls that overlap in time on one GPU (on
+ * different streams or threads) race and give wrong results: serialize
+ * them.  The array keeps the last call's contents; nothing in it needs to
+ * start at zero.  Status codes as ssd_fwd, plus SSD_ERR_DEVICE if the
+ * array's device address cannot be obtained. */
+#define SSD_NOALLOC_WORKSPACE_BYTES (96u << 20)
+int ssd_fwd_noalloc(const ssd_shape *shape,
+                    const float *q, const float *k, const float *v,
+                    const float *log_alpha, const float *h0,
+                    float *y, void *stream);
+
 /* Number of workspace regions reported by ssd_workspace_layout. */
 #define SSD_WS_REGIONS 4
 

@@ -179,3 +179,16 @@ def test_binding_rejects_cpu_tensors():
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(ImportError):
         ssd.library(str(tmp_path / "missing.so"))
+
+
+def test_noalloc_refuses_oversized_shapes_on_host():
+    """ssd_fwd_noalloc checks the shape's workspace against its static array
+    on the host and returns SSD_ERR_WORKSPACE without touching a device."""
+    lib = ssd.library()
+    big = ssd.ShapeArg(4, 2, 8, 8192, 128, 128)
+    assert ssd.workspace_size(big, False) > ssd.NOALLOC_WORKSPACE_BYTES
+    p = ctypes.c_void_p(16)
+    assert lib.ssd_fwd_noalloc(ctypes.byref(big), *([p] * 6), None) == 4
+    assert lib.ssd_fwd_noalloc(ctypes.byref(ssd.ShapeArg(1, 3, 4, 10, 8, 8)), *([p] * 6), None) == 2
+    # the largest workload of the pages at T = 2048 fits
+    assert ssd.workspace_size(ssd.ShapeArg(4, 2, 8, 2048, 128, 128), False) <= ssd.NOALLOC_WORKSPACE_BYTES

@@ -238,6 +238,14 @@ __global__ __launch_bounds__(NTS) void k_state_scan(
     for (int64_t s = 0; s < NS; ++s) {
         const int buf = (int)(s & 1);
         block_sync();   // step s staged in half `buf`
+        // The chunks' decays are read before their operands: LDS reads
+        // return in order, and the state is scaled by the decay before the
+        // first MFMA, so a decay read last would hold that MFMA until every
+        // operand read of the chunk had returned.
+        float dec[CPS];
+#pragma unroll
+        for (int cc = 0; cc < CPS; ++cc) dec[cc] = decs[buf][cc];
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int cc = 0; cc < CPS; ++cc) {
             float av[CH / 4];
@@ -261,7 +269,7 @@ __global__ __launch_bounds__(NTS) void k_state_scan(
                     bv[kk][0] = Bb[4 * kk * LDB];
                 }
             }
-            const float decay = decs[buf][cc];
+            const float decay = dec[cc];
             // slab[c] = S (state entering the chunk in this direction); no-op chunks store nothing
             const int64_t n = s * CPS + cc;
             const bool live = n < NC;

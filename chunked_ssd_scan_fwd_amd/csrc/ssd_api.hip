@@ -22,6 +22,35 @@ __global__ __launch_bounds__(NTZ) void k_zero(float *__restrict__ p, int64_t n)
     if (i < n) p[i] = 0.f;
 }
 
+constexpr int NTC = 256;
+
+// dst[b][r][c] = src[b][r][c] (or += with `add`) for b < nb, r < rows,
+// c < cols; batch and row strides in floats.  Moves column blocks of the
+// operands and outputs of problems with dk or dv above 128.
+__global__ __launch_bounds__(NTC) void k_copy_block(float *__restrict__ dst, int64_t dbs, int64_t dld,
+                                                    const float *__restrict__ src, int64_t sbs, int64_t sld,
+                                                    int64_t nb, int64_t rows, int64_t cols, int add)
+{
+    const int64_t n = nb * rows * cols;
+    for (int64_t i = (int64_t)blockIdx.x * NTC + threadIdx.x; i < n; i += (int64_t)gridDim.x * NTC) {
+        const int64_t c = i % cols, t = i / cols, r = t % rows, b = t / rows;
+        const float x = src[b * sbs + r * sld + c];
+        float *d = dst + b * dbs + r * dld + c;
+        *d = add ? *d + x : x;
+    }
+}
+
+static int copy_block(ssd_timer *tm, hipStream_t st, float *dst, int64_t dbs, int64_t dld, const float *src,
+                      int64_t sbs, int64_t sld, int64_t nb, int64_t rows, int64_t cols, bool add)
+{
+    const int64_t n = nb * rows * cols;
+    if (n == 0) return SSD_OK;
+    const int64_t blocks = (n + NTC - 1) / NTC;
+    launch(tm, KID_AUX, k_copy_block, dim3((unsigned)(blocks < 8192 ? blocks : 8192)), dim3(NTC), st, dst, dbs,
+           dld, src, sbs, sld, nb, rows, cols, (int)add);
+    return launch_status();
+}
+
 constexpr int kMaxDevices = 64;
 constexpr int kDefaultCUs = 256;
 
@@ -101,6 +130,12 @@ static int prepare(const ssd_shape *shape, bool backward, void *ws, size_t ws_by
     return SSD_OK;
 }
 
+static int fwd_split(const ssd_shape &s, const float *q, const float *k, const float *v, const float *log_alpha,
+                     const float *h0, float *y, void *workspace, size_t ws_bytes, hipStream_t st, ssd_timer *tm);
+static int bwd_split(const ssd_shape &s, const float *q, const float *k, const float *v, const float *log_alpha,
+                     const float *h0, const float *dy, float *dq, float *dk, float *dv, float *dla, float *dh0,
+                     void *workspace, size_t ws_bytes, hipStream_t st, ssd_timer *tm);
+
 static int fwd_impl(const ssd_shape *shape, const float *q, const float *k, const float *v, const float *log_alpha,
                     const float *h0, float *y, void *workspace, size_t workspace_bytes, void *stream, ssd_timer *tm)
 {
@@ -112,10 +147,11 @@ static int fwd_impl(const ssd_shape *shape, const float *q, const float *k, cons
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(log_alpha) || !aligned16(h0) ||
         !aligned16(y))
         return SSD_ERR_ALIGN;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (needs_split(shape)) return fwd_split(s, q, k, v, log_alpha, h0, y, workspace, workspace_bytes, st, tm);
     Problem P;
     rc = prepare(shape, false, workspace, workspace_bytes, tm, &P);
     if (rc != SSD_OK) return rc;
-    hipStream_t st = static_cast<hipStream_t>(stream);
     rc = run_scan(P, 1, true, q, k, v, nullptr, log_alpha, h0, nullptr, st);
     if (rc != SSD_OK) return rc;
     return run_output(P, q, k, v, log_alpha, y, st);
@@ -147,6 +183,10 @@ static int bwd_impl(const ssd_shape *shape, const float *q, const float *k, cons
     const void *ptrs[] = {q, k, v, log_alpha, h0, dy, dq, dk, dv, dlog_alpha, dh0};
     for (const void *p : ptrs)
         if (!aligned16(p)) return SSD_ERR_ALIGN;
+    // Problems split into column blocks recompute everything (no reuse).
+    if (needs_split(shape))
+        return bwd_split(s, q, k, v, log_alpha, h0, dy, dq, dk, dv, dlog_alpha, dh0, workspace, workspace_bytes, st,
+                         tm);
     Problem P;
     rc = prepare(shape, true, workspace, workspace_bytes, tm, &P);
     if (rc != SSD_OK) return rc;
@@ -155,6 +195,91 @@ static int bwd_impl(const ssd_shape *shape, const float *q, const float *k, cons
     rc = run_scan(P, reuse ? 2 : 3, !reuse, q, k, v, dy, log_alpha, h0, dh0, st);
     if (rc != SSD_OK) return rc;
     return run_grads(P, q, k, v, dy, log_alpha, dq, dk, dv, dlog_alpha, st);
+}
+
+// Workspace regions of a split problem, resolved against a caller's workspace.
+static int split_prepare(const ssd_shape &s, bool backward, void *ws, size_t ws_bytes, SplitLayout *L)
+{
+    *L = make_split_layout(&s, backward, device_cus());
+    if (ws_bytes < L->total) return SSD_ERR_WORKSPACE;
+    if (!ws) return SSD_ERR_NULL;
+    if (!aligned16(ws)) return SSD_ERR_ALIGN;
+    return SSD_OK;
+}
+
+// Forward of a problem with dk or dv above 128: for each dv block J and dk
+// block I, the sub-problem on (q_I, k_I, v_J, log_alpha, h0[I, J]) gives y_IJ,
+// and y[:, :, :, J] = sum over I of y_IJ, added in ascending I.
+static int fwd_split(const ssd_shape &s, const float *q, const float *k, const float *v, const float *log_alpha,
+                     const float *h0, float *y, void *workspace, size_t ws_bytes, hipStream_t st, ssd_timer *tm)
+{
+    SplitLayout L;
+    int rc = split_prepare(s, false, workspace, ws_bytes, &L);
+    if (rc != SSD_OK) return rc;
+    char *w = static_cast<char *>(workspace);
+    float *qb = reinterpret_cast<float *>(w + L.qb), *kb = reinterpret_cast<float *>(w + L.kb);
+    float *vb = reinterpret_cast<float *>(w + L.vb), *h0b = reinterpret_cast<float *>(w + L.h0b);
+    float *yb = reinterpret_cast<float *>(w + L.yb);
+    const int64_t nqr = s.B * s.G * s.T, nvr = s.B * s.H * s.T, BH = s.B * s.H;
+    for (int J = 0; J < L.nJ && rc == SSD_OK; ++J) {
+        const int64_t j0 = L.j0[J], dvJ = L.dvb[J];
+        rc = copy_block(tm, st, vb, 0, dvJ, v + j0, 0, s.dv, 1, nvr, dvJ, false);
+        for (int I = 0; I < L.nI && rc == SSD_OK; ++I) {
+            const int64_t i0 = L.i0[I], dkI = L.dkb[I];
+            rc = copy_block(tm, st, qb, 0, dkI, q + i0, 0, s.dk, 1, nqr, dkI, false);
+            if (rc == SSD_OK) rc = copy_block(tm, st, kb, 0, dkI, k + i0, 0, s.dk, 1, nqr, dkI, false);
+            if (rc == SSD_OK)
+                rc = copy_block(tm, st, h0b, dkI * dvJ, dvJ, h0 + i0 * s.dv + j0, s.dk * s.dv, s.dv, BH, dkI, dvJ,
+                                false);
+            const ssd_shape t = sub_shape(&s, L, I, J);
+            if (rc == SSD_OK) rc = fwd_impl(&t, qb, kb, vb, log_alpha, h0b, yb, w + L.sub, L.sub_bytes, st, tm);
+            if (rc == SSD_OK) rc = copy_block(tm, st, y + j0, 0, s.dv, yb, 0, dvJ, 1, nvr, dvJ, I > 0);
+        }
+    }
+    return rc;
+}
+
+// Backward of a problem with dk or dv above 128: each sub-problem (I, J) of
+// fwd_split gives its five gradients; dq and dk of block I are summed over J,
+// dv of block J over I, dlog_alpha over all of them (in the loop order: J
+// outer, I inner), and dh0 is taken block by block.
+static int bwd_split(const ssd_shape &s, const float *q, const float *k, const float *v, const float *log_alpha,
+                     const float *h0, const float *dy, float *dq, float *dk, float *dv, float *dla, float *dh0,
+                     void *workspace, size_t ws_bytes, hipStream_t st, ssd_timer *tm)
+{
+    SplitLayout L;
+    int rc = split_prepare(s, true, workspace, ws_bytes, &L);
+    if (rc != SSD_OK) return rc;
+    char *w = static_cast<char *>(workspace);
+    auto at = [&](size_t off) { return reinterpret_cast<float *>(w + off); };
+    float *qb = at(L.qb), *kb = at(L.kb), *vb = at(L.vb), *h0b = at(L.h0b), *dyb = at(L.dyb);
+    float *dqb = at(L.dqb), *dkb = at(L.dkbuf), *dvb = at(L.dvbuf), *dlab = at(L.dlab), *dh0b = at(L.dh0b);
+    const int64_t nqr = s.B * s.G * s.T, nvr = s.B * s.H * s.T, BH = s.B * s.H;
+    for (int J = 0; J < L.nJ && rc == SSD_OK; ++J) {
+        const int64_t j0 = L.j0[J], dvJ = L.dvb[J];
+        rc = copy_block(tm, st, vb, 0, dvJ, v + j0, 0, s.dv, 1, nvr, dvJ, false);
+        if (rc == SSD_OK) rc = copy_block(tm, st, dyb, 0, dvJ, dy + j0, 0, s.dv, 1, nvr, dvJ, false);
+        for (int I = 0; I < L.nI && rc == SSD_OK; ++I) {
+            const int64_t i0 = L.i0[I], dkI = L.dkb[I];
+            rc = copy_block(tm, st, qb, 0, dkI, q + i0, 0, s.dk, 1, nqr, dkI, false);
+            if (rc == SSD_OK) rc = copy_block(tm, st, kb, 0, dkI, k + i0, 0, s.dk, 1, nqr, dkI, false);
+            if (rc == SSD_OK)
+                rc = copy_block(tm, st, h0b, dkI * dvJ, dvJ, h0 + i0 * s.dv + j0, s.dk * s.dv, s.dv, BH, dkI, dvJ,
+                                false);
+            const ssd_shape t = sub_shape(&s, L, I, J);
+            if (rc == SSD_OK)
+                rc = bwd_impl(&t, qb, kb, vb, log_alpha, h0b, dyb, dqb, dkb, dvb, dlab, dh0b, w + L.sub, L.sub_bytes,
+                              st, false, tm);
+            if (rc == SSD_OK) rc = copy_block(tm, st, dq + i0, 0, s.dk, dqb, 0, dkI, 1, nqr, dkI, J > 0);
+            if (rc == SSD_OK) rc = copy_block(tm, st, dk + i0, 0, s.dk, dkb, 0, dkI, 1, nqr, dkI, J > 0);
+            if (rc == SSD_OK) rc = copy_block(tm, st, dv + j0, 0, s.dv, dvb, 0, dvJ, 1, nvr, dvJ, I > 0);
+            if (rc == SSD_OK) rc = copy_block(tm, st, dla, 0, 1, dlab, 0, 1, 1, nvr, 1, I > 0 || J > 0);
+            if (rc == SSD_OK)
+                rc = copy_block(tm, st, dh0 + i0 * s.dv + j0, s.dk * s.dv, s.dv, dh0b, dkI * dvJ, dvJ, BH, dkI, dvJ,
+                                false);
+        }
+    }
+    return rc;
 }
 
 static const char *kKernelNames[KID_COUNT] = {"state_scan", "chunk_output", "state_scan_bidir",
@@ -200,7 +325,7 @@ int ssd_fwd_noalloc(const ssd_shape *shape, const float *q, const float *k, cons
     // clearing (every region is written before it is read).
     int rc = check_shape(shape);
     if (rc != SSD_OK) return rc;
-    const size_t need = make_layout(shape, false, device_cus()).off[SSD_WS_REGIONS];
+    const size_t need = workspace_bytes(shape, false, device_cus());
     if (need > SSD_NOALLOC_WORKSPACE_BYTES) return SSD_ERR_WORKSPACE;
     void *ws = nullptr;
     if (need > 0) {

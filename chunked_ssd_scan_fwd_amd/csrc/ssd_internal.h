@@ -11,6 +11,7 @@ namespace ssd {
 
 constexpr int kChunk = SSD_CHUNK;   // steps per chunk = wavefront width
 constexpr int64_t kMaxDim = 128;    // largest dk / dv the kernels take directly
+constexpr int64_t kMaxApiDim = 256; // largest dk / dv of the ABI (split into <= 128 blocks)
 
 struct Layout {
     int64_t NC = 0;      // chunks per sequence, ceil(T / 64)
@@ -37,9 +38,33 @@ void head_split(const ssd_shape *s, int64_t NC, int cus, int *hsplit, int *hpb);
 // SSD_OK, SSD_ERR_NULL (shape == NULL), SSD_ERR_SHAPE or SSD_ERR_UNSUPPORTED.
 int check_shape(const ssd_shape *s);
 
-// Workspace layout for a valid shape on a device with `cus` compute units.
-// Empty shapes give total == 0.
+// Workspace layout for a valid shape with dk, dv <= kMaxDim on a device with
+// `cus` compute units.  Empty shapes give total == 0.
 Layout make_layout(const ssd_shape *s, bool backward, int cus);
+
+// Shapes with dk or dv above kMaxDim run as nI x nJ sub-problems on column
+// blocks of at most kMaxDim: dk block I covers columns i0[I] .. i0[I] +
+// dkb[I] of q, k (rows of h0), dv block J columns j0[J] .. j0[J] + dvb[J] of
+// v, dy, y (columns of h0).  The outputs are sums of the sub-problems'
+// (y over I; dq, dk over J; dv over I; dlog_alpha over both; dh0 block by
+// block), so the workspace holds the largest sub-problem's workspace and
+// contiguous copies of one block of each operand and output.
+struct SplitLayout {
+    int nI = 1, nJ = 1;
+    int64_t i0[2] = {0, 0}, dkb[2] = {0, 0}, j0[2] = {0, 0}, dvb[2] = {0, 0};
+    int64_t dkm = 0, dvm = 0;   // largest block widths
+    // byte offsets: sub-problem workspace, q, k, v, h0, y (fwd) or dy, dq, dk,
+    // dv, dlog_alpha, dh0 blocks (bwd), total
+    size_t sub = 0, qb = 0, kb = 0, vb = 0, h0b = 0, yb = 0, dyb = 0, dqb = 0, dkbuf = 0, dvbuf = 0, dlab = 0,
+           dh0b = 0, total = 0;
+    size_t sub_bytes = 0;
+};
+bool needs_split(const ssd_shape *s);
+ssd_shape sub_shape(const ssd_shape *s, const SplitLayout &P, int I, int J);
+SplitLayout make_split_layout(const ssd_shape *s, bool backward, int cus);
+
+// Total workspace bytes for any valid shape (direct or split).
+size_t workspace_bytes(const ssd_shape *s, bool backward, int cus);
 
 // Compute units of the current HIP device, read once per device and cached;
 // 256 (MI355X) when no device can be queried.  Defined in the HIP unit.

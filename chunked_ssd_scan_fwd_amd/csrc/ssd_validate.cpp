@@ -15,7 +15,7 @@ int check_shape(const ssd_shape *s)
     const int64_t lim = int64_t(1) << 40;
     if (s->B > lim || s->H > lim || s->T > lim) return SSD_ERR_SHAPE;
     const int64_t dmax = s->dk > s->dv ? s->dk : s->dv;
-    if (dmax > kMaxDim) return SSD_ERR_UNSUPPORTED;
+    if (dmax > kMaxApiDim) return SSD_ERR_UNSUPPORTED;
     if (s->B > lim / s->H) return SSD_ERR_SHAPE;           // B*H <= 2^40, no overflow below
     if (s->B * s->H > lim / (s->T + 1)) return SSD_ERR_SHAPE;
     if (s->B * s->H * (s->T + 1) > lim / dmax) return SSD_ERR_SHAPE;
@@ -67,6 +67,78 @@ Layout make_layout(const ssd_shape *s, bool backward, int cus)
     return L;
 }
 
+bool needs_split(const ssd_shape *s) { return s->dk > kMaxDim || s->dv > kMaxDim; }
+
+ssd_shape sub_shape(const ssd_shape *s, const SplitLayout &P, int I, int J)
+{
+    ssd_shape t = *s;
+    t.dk = P.dkb[I];
+    t.dv = P.dvb[J];
+    return t;
+}
+
+// Blocks of kMaxDim columns and the remainder: 200 = 128 + 72.
+static int split_dim(int64_t d, int64_t *off, int64_t *w)
+{
+    if (d <= kMaxDim) {
+        off[0] = 0;
+        w[0] = d;
+        return 1;
+    }
+    off[0] = 0;
+    w[0] = kMaxDim;
+    off[1] = kMaxDim;
+    w[1] = d - kMaxDim;
+    return 2;
+}
+
+SplitLayout make_split_layout(const ssd_shape *s, bool backward, int cus)
+{
+    SplitLayout P;
+    P.nI = split_dim(s->dk, P.i0, P.dkb);
+    P.nJ = split_dim(s->dv, P.j0, P.dvb);
+    P.dkm = P.dkb[0];
+    P.dvm = P.dvb[0];
+    for (int I = 0; I < P.nI; ++I)
+        for (int J = 0; J < P.nJ; ++J) {
+            const ssd_shape t = sub_shape(s, P, I, J);
+            const size_t b = make_layout(&t, backward, cus).off[SSD_WS_REGIONS];
+            if (b > P.sub_bytes) P.sub_bytes = b;
+        }
+    const size_t f = sizeof(float);
+    const size_t BG = size_t(s->B) * size_t(s->G), BH = size_t(s->B) * size_t(s->H), T = size_t(s->T);
+    const size_t nq = BG * T * size_t(P.dkm), nv = BH * T * size_t(P.dvm), nh = BH * size_t(P.dkm * P.dvm);
+    size_t o = 0;
+    auto take = [&](size_t &at, size_t n) {
+        at = o;
+        o = round_up(o + n, 256);
+    };
+    take(P.sub, P.sub_bytes);
+    take(P.qb, nq * f);
+    take(P.kb, nq * f);
+    take(P.vb, nv * f);
+    take(P.h0b, nh * f);
+    if (!backward) {
+        take(P.yb, nv * f);
+    } else {
+        take(P.dyb, nv * f);
+        take(P.dqb, nq * f);
+        take(P.dkbuf, nq * f);
+        take(P.dvbuf, nv * f);
+        take(P.dlab, BH * T * f);
+        take(P.dh0b, nh * f);
+    }
+    P.total = o;
+    return P;
+}
+
+size_t workspace_bytes(const ssd_shape *s, bool backward, int cus)
+{
+    if (s->B == 0 || s->T == 0) return 0;
+    if (needs_split(s)) return make_split_layout(s, backward, cus).total;
+    return make_layout(s, backward, cus).off[SSD_WS_REGIONS];
+}
+
 }  // namespace ssd
 
 extern "C" {
@@ -74,13 +146,13 @@ extern "C" {
 size_t ssd_fwd_workspace_size(const ssd_shape *shape)
 {
     if (ssd::check_shape(shape) != SSD_OK) return (size_t)-1;
-    return ssd::make_layout(shape, false, ssd::device_cus()).off[SSD_WS_REGIONS];
+    return ssd::workspace_bytes(shape, false, ssd::device_cus());
 }
 
 size_t ssd_bwd_workspace_size(const ssd_shape *shape)
 {
     if (ssd::check_shape(shape) != SSD_OK) return (size_t)-1;
-    return ssd::make_layout(shape, true, ssd::device_cus()).off[SSD_WS_REGIONS];
+    return ssd::workspace_bytes(shape, true, ssd::device_cus());
 }
 
 int ssd_workspace_layout(const ssd_shape *shape, int backward, size_t offsets[SSD_WS_REGIONS + 1])
@@ -88,6 +160,7 @@ int ssd_workspace_layout(const ssd_shape *shape, int backward, size_t offsets[SS
     if (!offsets) return SSD_ERR_NULL;
     const int rc = ssd::check_shape(shape);
     if (rc != SSD_OK) return rc;
+    if (ssd::needs_split(shape)) return SSD_ERR_UNSUPPORTED;   // regions of the direct path only
     const ssd::Layout L = ssd::make_layout(shape, backward != 0, ssd::device_cus());
     for (int i = 0; i <= SSD_WS_REGIONS; ++i) offsets[i] = L.off[i];
     return SSD_OK;
@@ -99,7 +172,7 @@ const char *ssd_strerror(int status)
     case SSD_OK: return "success";
     case SSD_ERR_NULL: return "a required pointer is NULL";
     case SSD_ERR_SHAPE: return "invalid shape (negative size, G < 1, H not a multiple of G, or too large)";
-    case SSD_ERR_UNSUPPORTED: return "unsupported shape (dk and dv must be in 1..128)";
+    case SSD_ERR_UNSUPPORTED: return "unsupported shape (dk and dv must be in 1..256)";
     case SSD_ERR_WORKSPACE: return "workspace smaller than the size query requires";
     case SSD_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case SSD_ERR_DEVICE: return "HIP launch or runtime error";

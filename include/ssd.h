@@ -53,8 +53,12 @@
  * execution surface at the caller's next synchronization.
  *
  * Supported shapes.  B >= 0, T >= 0, G >= 1, H >= 1, H % G == 0,
- * 1 <= dk <= 128, 1 <= dv <= 128; B*H*T*max(dk,dv) < 2^40.  Other dk/dv
- * return SSD_ERR_UNSUPPORTED.  log_alpha must be finite.
+ * 1 <= dk <= 256, 1 <= dv <= 256; B*H*T*max(dk,dv) < 2^40.  Other dk/dv
+ * return SSD_ERR_UNSUPPORTED.  log_alpha must be finite.  The kernels take
+ * dk, dv up to 128 directly; a larger dk or dv is cut into column blocks of
+ * 128 and the rest, each block pair runs as its own problem, and the
+ * outputs are added up in a fixed order (y is linear in the dk blocks of q
+ * and k and separable in the dv blocks of v; the gradients follow).
  *
  * Thread safety.  The compute calls keep no mutable state between calls and
  * are reentrant; concurrent calls on different streams need separate
@@ -165,7 +169,9 @@ int ssd_fwd_noalloc(const ssd_shape *shape,
  *               dk that the gradient kernel writes and a final kernel adds
  *               up (no caller use); empty otherwise
  *   [4] total bytes.
- * `backward` selects the backward layout.  Returns SSD_OK or an error.
+ * `backward` selects the backward layout.  Returns SSD_OK or an error;
+ * SSD_ERR_UNSUPPORTED for shapes with dk or dv above 128, whose workspace
+ * holds the column-block sub-problems instead.
  * Test support: the states are the quantity the chunked method passes
  * between chunks, checked against the oracle's state at chunk boundaries. */
 int ssd_workspace_layout(const ssd_shape *shape, int backward, size_t offsets[SSD_WS_REGIONS + 1]);
@@ -192,7 +198,8 @@ int ssd_chunk_size(void);
  * every access stays inside the workspace and the tensors).  Arguments,
  * layouts, ownership, asynchrony and return codes are those of ssd_bwd;
  * the forward work must be enqueued on the same stream before this call,
- * or be complete. */
+ * or be complete.  For dk or dv above 128 it recomputes, exactly as ssd_bwd
+ * (the column-block sub-problems keep no residual between calls). */
 int ssd_bwd_from_fwd(const ssd_shape *shape,
                      const float *q, const float *k, const float *v,
                      const float *log_alpha, const float *h0, const float *dy,

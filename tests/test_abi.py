@@ -44,8 +44,8 @@ def _call_bwd(shape, ptr=1, ws_bytes=0, fn="ssd_bwd"):
     (ssd.ShapeArg(-1, 1, 1, 10, 8, 8), 2),     # negative B
     (ssd.ShapeArg(1, 1, 1, -5, 8, 8), 2),      # negative T
     (ssd.ShapeArg(1, 1, 1, 10, 0, 8), 2),      # dk = 0
-    (ssd.ShapeArg(1, 1, 1, 10, 129, 8), 3),    # dk above the supported range
-    (ssd.ShapeArg(1, 1, 1, 10, 8, 200), 3),    # dv above the supported range
+    (ssd.ShapeArg(1, 1, 1, 10, 257, 8), 3),    # dk above the supported range
+    (ssd.ShapeArg(1, 1, 1, 10, 8, 300), 3),    # dv above the supported range
     (ssd.ShapeArg(1 << 40, 1 << 40, 1 << 40, 10, 8, 8), 2),   # overflow guard
 ])
 def test_bad_shapes_rejected(shape, code):
@@ -192,3 +192,25 @@ def test_noalloc_refuses_oversized_shapes_on_host():
     assert lib.ssd_fwd_noalloc(ctypes.byref(ssd.ShapeArg(1, 3, 4, 10, 8, 8)), *([p] * 6), None) == 2
     # the largest workload of the pages at T = 2048 fits
     assert ssd.workspace_size(ssd.ShapeArg(4, 2, 8, 2048, 128, 128), False) <= ssd.NOALLOC_WORKSPACE_BYTES
+
+
+@pytest.mark.parametrize("B,G,H,T,dk,dv", [(1, 1, 2, 300, 256, 256), (2, 2, 4, 150, 200, 136),
+                                           (1, 1, 1, 70, 129, 1), (1, 2, 2, 100, 1, 250)])
+def test_wide_shapes_workspace(B, G, H, T, dk, dv):
+    """dk or dv in 129..256 run as column-block sub-problems: the workspace
+    holds the largest sub-problem's workspace plus one block of every operand
+    and output; the region query refuses these shapes."""
+    s = ssd.ShapeArg(B, G, H, T, dk, dv)
+    lib = ssd.library()
+    arr = (ctypes.c_size_t * (ssd.WS_REGIONS + 1))()
+    assert lib.ssd_workspace_layout(ctypes.byref(s), 1, arr) == 3
+    sub = max(ssd.workspace_size(ssd.ShapeArg(B, G, H, T, a, b), True)
+              for a in ([dk] if dk <= 128 else [128, dk - 128]) for b in ([dv] if dv <= 128 else [128, dv - 128]))
+    dkm, dvm = min(dk, 128), min(dv, 128)
+    blocks = 4 * (2 * B * G * T * dkm + B * H * T * dvm + B * H * dkm * dvm)
+    assert ssd.workspace_size(s, True) >= sub + blocks
+    assert ssd.workspace_size(s, False) >= ssd.workspace_size(
+        ssd.ShapeArg(B, G, H, T, dkm, dvm), False) + blocks
+    # validation still happens on the host before anything else
+    assert _call_fwd(s, ptr=0x1000, ws_bytes=ssd.workspace_size(s, False) - 1) == 4
+    assert _call_bwd(s, ptr=0x1000, ws_bytes=ssd.workspace_size(s, True) - 1) == 4

@@ -35,6 +35,16 @@ ZOO = [
 ]
 
 
+# dk or dv in 129..256: column-block sub-problems added up in a fixed order
+WIDE = [
+    Shape(1, 1, 2, 300, 256, 256),
+    Shape(2, 2, 4, 150, 200, 136),
+    Shape(1, 1, 1, 70, 129, 1),
+    Shape(1, 2, 2, 100, 1, 250),
+    Shape(2, 1, 3, 65, 136, 200),
+]
+
+
 def _id(s):
     return f"B{s.B}G{s.G}H{s.H}T{s.T}dk{s.dk}dv{s.dv}"
 
@@ -70,6 +80,37 @@ def test_backward_shape_zoo(shape):
     need_gpu()
     say(f"bwd {_id(shape)}")
     check_bwd(make_inputs(shape, seed=shape.T * 11 + shape.dv))
+
+
+@pytest.mark.parametrize("shape", WIDE, ids=_id)
+def test_wide_dims_forward_backward(shape):
+    need_gpu()
+    say(f"wide {_id(shape)}")
+    x = make_inputs(shape, seed=shape.T * 5 + shape.dk + shape.dv)
+    check_fwd(x)
+    check_bwd(x)
+
+
+def test_wide_dims_reuse_noalloc_deterministic():
+    """A split shape through bwd_from_fwd (which recomputes for such shapes),
+    fwd_noalloc, and two runs of each call: all equal bitwise."""
+    need_gpu()
+    import torch
+    import chunked_ssd_scan_fwd_amd as ssd
+    s = Shape(1, 2, 4, 200, 160, 144)
+    x = make_inputs(s, 41)
+    d = to_dev(x)
+    say("wide reuse / noalloc")
+    sa = ssd.ShapeArg(s.B, s.G, s.H, s.T, s.dk, s.dv)
+    ws = torch.empty(ssd.workspace_size(sa, True), dtype=torch.uint8, device="cuda")
+    y = host(ssd.fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["h0"], workspace=ws))
+    g1 = ssd.bwd_from_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["h0"], d["dy"], workspace=ws)
+    g2 = ssd.bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["h0"], d["dy"])
+    y2 = host(ssd.fwd_noalloc(d["q"], d["k"], d["v"], d["log_alpha"], d["h0"]))
+    np.testing.assert_array_equal(y2, y)
+    for a, b in zip(g1, g2):
+        np.testing.assert_array_equal(host(a), host(b))
+    assert rel_err(y, oracle.fwd(x["q"], x["k"], x["v"], x["log_alpha"], x["h0"])) <= TOL_Y
 
 
 def test_chunk_states_match_oracle():

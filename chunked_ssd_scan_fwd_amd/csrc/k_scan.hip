@@ -72,8 +72,9 @@ template <int DKP, int DVP, bool VEC, int TJ, int CPS, bool EXD>
 __global__ __launch_bounds__(NTS) void k_state_scan(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
     const float *__restrict__ dy, const float *__restrict__ h0, const float *__restrict__ wts,
-    const float *__restrict__ cdec, float *__restrict__ states, float *__restrict__ dstates, float *__restrict__ dh0, int G, int H, int64_t T,
-    int dk, int dv, int64_t NC, int64_t Epad, int64_t per_dir, int dir0)
+    const float *__restrict__ cdec, float *__restrict__ states, float *__restrict__ dstates, float *__restrict__ dh0,
+    float *__restrict__ ends, int G, int H, int64_t T, int dk, int dv, int64_t NC, int64_t Epad, int64_t per_dir,
+    int dir0, int nseg, int64_t seg_len)
 {
     static_assert(TJ <= DVP && DVP % TJ == 0 && (TJ == 32 || TJ == 64 || TJ == 128), "tile width");
     if constexpr (EXD) {   // dk == DKP, dv == DVP: index arithmetic on constants
@@ -104,14 +105,20 @@ __global__ __launch_bounds__(NTS) void k_state_scan(
     const int64_t dl = L / per_dir;                   // direction index within this launch
     const int dir = dir0 + (int)dl;                   // 0: forward states, 1: reverse
     const int64_t rem = L - dl * per_dir;
-    const int64_t bh = rem / NTILE;
-    const int tile = (int)(rem - bh * NTILE);
+    // segment p of the chunk sequence (in scan order), then (b h, tile)
+    const int64_t per_seg = per_dir / nseg, BHn = per_seg / NTILE;
+    const int64_t p = rem / per_seg;
+    const int64_t rem2 = rem - p * per_seg;
+    const int64_t bh = rem2 / NTILE;
+    const int tile = (int)(rem2 - bh * NTILE);
+    const int64_t n0 = p * seg_len;                                     // first chunk of the segment
+    const int64_t nch = (NC - n0) < seg_len ? (NC - n0) : seg_len;      // its chunks
     const int i0 = (tile / NTJ) * TI, j0 = (tile % NTJ) * TJ;
     const int h = (int)(bh % H);
     const int64_t b = bh / H;
     const int g = h / (H / G);
     const int64_t E = (int64_t)dk * dv;
-    const int64_t NSC = (NC + CPS - 1) / CPS;        // steps holding real chunks
+    const int64_t NSC = (nch + CPS - 1) / CPS;       // steps holding real chunks
     const int64_t NS = (NSC + PD - 1) / PD * PD;      // steps, rounded up
     const int wave = threadIdx.x >> 6;
 
@@ -131,8 +138,8 @@ __global__ __launch_bounds__(NTS) void k_state_scan(
         Stage stg[PD][CPS];
         // operands of chunk n of the scan order; chunks past the end load zeros
         auto prefetch = [&](Stage &S, int64_t n) {
-            const bool live = n < NC;
-            const int64_t c = live ? (dir == 0 ? n : NC - 1 - n) : 0;
+            const bool live = n < nch;
+            const int64_t c = live ? (dir == 0 ? n0 + n : NC - 1 - (n0 + n)) : 0;
             const int rows = (int)((T - c * CH) < CH ? (T - c * CH) : CH);
             const rsrc_t ab = make_rsrc(Asrc + c * CH * dk, live ? (int64_t)rows * dk * 4 : 0);
             const rsrc_t bb = make_rsrc(Bsrc + c * CH * dv, live ? (int64_t)rows * dv * 4 : 0);
@@ -225,7 +232,8 @@ __global__ __launch_bounds__(NTS) void k_state_scan(
     };
     f32x4 acc[NU];
     {
-        const rsrc_t hr = make_rsrc(h0 + bh * E, dir == 0 ? E * 4 : 0);   // the reverse pass starts at 0
+        // the forward pass starts at h0, the reverse at 0, later segments at 0
+        const rsrc_t hr = make_rsrc(h0 + bh * E, (dir == 0 && p == 0) ? E * 4 : 0);
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
 #pragma unroll
@@ -272,9 +280,9 @@ __global__ __launch_bounds__(NTS) void k_state_scan(
             const float decay = dec[cc];
             // slab[c] = S (state entering the chunk in this direction); no-op chunks store nothing
             const int64_t n = s * CPS + cc;
-            const bool live = n < NC;
+            const bool live = n < nch;
             const rsrc_t dst =
-                make_rsrc(slab + (live ? (dir == 0 ? n : NC - 1 - n) : 0) * Epad, live ? E * 4 : 0);
+                make_rsrc(slab + (live ? (dir == 0 ? n0 + n : NC - 1 - (n0 + n)) : 0) * Epad, live ? E * 4 : 0);
             if constexpr (VEC) {
                 // the lane's NU columns of a row are consecutive (dv % 4 == 0,
                 // so they are inside the state when the first one is)
@@ -305,7 +313,15 @@ __global__ __launch_bounds__(NTS) void k_state_scan(
             }
         }
     }
-    if (dir == 1) {
+    if (nseg > 1) {
+        // the state leaving the segment, for the fix-up pass (ends[dl][p][bh])
+        const rsrc_t er = make_rsrc(ends + ((dl * nseg + p) * BHn + bh) * Epad, E * 4);
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) gstore1(er, soff(u, r), acc[u][r]);
+        }
+    } else if (dir == 1) {
         const rsrc_t hr = make_rsrc(dh0 + bh * E, E * 4);
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
@@ -314,6 +330,64 @@ __global__ __launch_bounds__(NTS) void k_state_scan(
         }
     }
 }
+
+// Fix-up of a segmented scan.  Segment p of the chunk sequence (scan order)
+// was scanned from a zero state, the first from the true initial state, and
+// ends[dl][p][bh] holds the state leaving it.  With S_p the true state
+// entering segment p, A_p the decay over segment p and d the decay from the
+// segment's start to chunk n,
+//     S_1 = ends[0],  S_{p+1} = ends[p] + A_p S_p,   state(n) = local state(n) + d S_p.
+// One thread per (state element, segment p >= 1) forms S_p from the ends of
+// the segments before it, adds d S_p to the chunk states of its segment,
+// and for the reverse direction the last segment's thread writes dh0, the
+// state leaving it.  The decays are the per-chunk e^{b_L} (uniform over a
+// wave, so they come through the scalar cache).
+constexpr int NTF = 256;
+__global__ __launch_bounds__(NTF) void k_seg_fixup(float *__restrict__ states, float *__restrict__ dstates,
+                                                   const float *__restrict__ ends, const float *__restrict__ cdec,
+                                                   float *__restrict__ dh0, int64_t BH, int64_t NC, int64_t E,
+                                                   int64_t Epad, int nseg, int64_t seg_len, int ndir, int dir0)
+{
+    const int64_t idx = (int64_t)blockIdx.x * NTF + threadIdx.x;
+    if (idx >= (int64_t)ndir * (nseg - 1) * BH * E) return;
+    const int64_t e = idx % E, t = idx / E, bh = t % BH, t2 = t / BH;
+    const int ps = 1 + (int)(t2 % (nseg - 1)), dl = (int)(t2 / (nseg - 1)), dir = dir0 + dl;
+    const float *en = ends + ((int64_t)dl * nseg * BH + bh) * Epad + e;   // en[p BH Epad]: segment p
+    const float *dc = cdec + bh * NC;
+    auto chunk = [&](int64_t n) { return dir == 0 ? n : NC - 1 - n; };
+    float carry = en[0];
+    for (int p = 1; p < ps; ++p) {
+        float a = 1.f;
+        for (int64_t n = p * seg_len; n < (p + 1) * seg_len; ++n) a *= dc[chunk(n)];   // full segments
+        carry = en[(int64_t)p * BH * Epad] + a * carry;
+    }
+    float *slab = (dir == 0 ? states : dstates) + bh * NC * Epad + e;
+    const int64_t n0 = ps * seg_len, n1 = (n0 + seg_len) < NC ? (n0 + seg_len) : NC;
+    float d = 1.f;
+    int64_t n = n0;
+    // four chunks at a time: their loads are independent of one another
+    for (; n + 4 <= n1; n += 4) {
+        int64_t c[4];
+        float x[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            c[u] = chunk(n + u);
+            x[u] = slab[c[u] * Epad];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            slab[c[u] * Epad] = x[u] + d * carry;
+            d *= dc[c[u]];
+        }
+    }
+    for (; n < n1; ++n) {
+        const int64_t c = chunk(n);
+        slab[c * Epad] += d * carry;
+        d *= dc[c];
+    }
+    if (dir == 1 && ps == nseg - 1) dh0[bh * E + e] = en[(int64_t)ps * BH * Epad] + d * carry;
+}
+
 // The fused state scan over the directions in `dirs` (see ssd_launch.h).
 int run_scan(const Problem &P, int dirs, bool prep, const float *q, const float *k, const float *v,
              const float *dy, const float *la, const float *h0, float *dh0, hipStream_t st)
@@ -330,32 +404,37 @@ int run_scan(const Problem &P, int dirs, bool prep, const float *q, const float 
     // tiles fill most of a CU's LDS); otherwise one.  State tiles are 32 x 64
     // (32 x dv for dv < 64): wider tiles re-read fewer operand tiles but
     // halve the number of independent sequential chains per CU, which
-    // measured slower.
+    // measured slower.  Small grids take narrow tiles and segments (ScanPlan).
     const int ndir = dirs == 3 ? 2 : 1, dir0 = dirs == 2 ? 1 : 0;
     const int64_t tiles_k = BH * (P.DKP / TI);
-    const int64_t wide = ndir * tiles_k * (P.DVP / (P.DVP < 64 ? P.DVP : 64));
-    // With at most half a block per CU, 32-wide tiles: twice the independent
-    // chains, each step half the work.
-    const bool narrow = P.DVP >= 64 && 2 * wide <= P.cus;
-    const bool pair = (narrow ? 2 * wide : wide) <= P.cus;
+    const ScanPlan plan = scan_plan(&s, ndir, P.cus);
+    const bool narrow = plan.narrow;
+    const bool pair = plan.blocks <= P.cus;
     const int kid = dirs == 1 ? KID_SCAN : dirs == 2 ? KID_SCANR : KID_SCAN2;
     auto run = [&](auto tj_c) {
         SSD_DISPATCH(P, ({
             constexpr int TJ = decltype(tj_c)::value ? 32 : (VP < 64 ? VP : 64);
-            const int64_t per_dir = tiles_k * (VP / TJ);
+            const int64_t per_dir = tiles_k * (VP / TJ) * plan.nseg;
             const dim3 grid((unsigned)(ndir * per_dir)), blk(NTS);
             if (pair)
                 launch(P.timer, kid, k_state_scan<KP, VP, VE, TJ, 2, EXD>, grid, blk, st, q, k, v, dy, h0, P.wts, P.cdec,
-                       P.states, P.dstates, dh0, (int)s.G, (int)s.H, s.T, (int)s.dk, (int)s.dv, P.L.NC, P.L.Epad,
-                       per_dir, dir0);
+                       P.states, P.dstates, dh0, P.ends, (int)s.G, (int)s.H, s.T, (int)s.dk, (int)s.dv, P.L.NC,
+                       P.L.Epad, per_dir, dir0, plan.nseg, plan.seg_len);
             else
                 launch(P.timer, kid, k_state_scan<KP, VP, VE, TJ, 1, EXD>, grid, blk, st, q, k, v, dy, h0, P.wts, P.cdec,
-                       P.states, P.dstates, dh0, (int)s.G, (int)s.H, s.T, (int)s.dk, (int)s.dv, P.L.NC, P.L.Epad,
-                       per_dir, dir0);
+                       P.states, P.dstates, dh0, P.ends, (int)s.G, (int)s.H, s.T, (int)s.dk, (int)s.dv, P.L.NC,
+                       P.L.Epad, per_dir, dir0, plan.nseg, plan.seg_len);
         }));
     };
     if (narrow) run(BoolC<true>{});
     else run(BoolC<false>{});
+    if (plan.nseg > 1) {
+        if (launch_status() != SSD_OK) return SSD_ERR_DEVICE;
+        const int64_t E = s.dk * s.dv, n = ndir * (plan.nseg - 1) * BH * E;
+        launch(P.timer, KID_AUX, k_seg_fixup, dim3((unsigned)((n + NTF - 1) / NTF)), dim3(NTF), st, P.states,
+               P.dstates, (const float *)P.ends, (const float *)P.cdec, dh0, BH, P.L.NC, E, P.L.Epad, plan.nseg,
+               plan.seg_len, ndir, dir0);
+    }
     return launch_status();
 }
 

@@ -29,7 +29,28 @@ struct Layout {
     int hsplit = 1;
     int hpb = 1;
     int64_t nqk_pad = 0;     // B*G*T*dk rounded up to a multiple of 64
+    // Segment end states of a segmented state scan (see ScanPlan), at byte
+    // offset ends_off inside region 3: [ndir][nseg][B*H][Epad] floats.
+    size_t ends_off = 0;
 };
+
+// Launch plan of the state scan for one launch over `ndir` directions.  The
+// scan walks the chunks in order, so its grid (one block per state tile)
+// can leave most CUs idle on small problems.  Then the tiles are first made
+// 32 wide (`narrow`), and if the grid still fills at most half the CUs the
+// chunk sequence is cut into `nseg` segments of `seg_len` chunks (a power of
+// two, each segment at least kMinSegChunks long) that run in parallel from a
+// zero state (the first from the true initial state); a fix-up pass then
+// adds each segment's decayed entering state to its chunk states.
+constexpr int64_t kMinSegChunks = 8;
+constexpr int kMaxSegs = 64;
+struct ScanPlan {
+    bool narrow = false;
+    int nseg = 1;
+    int64_t seg_len = 0;
+    int64_t blocks = 0;   // blocks of the launch
+};
+ScanPlan scan_plan(const ssd_shape *s, int ndir, int cus);
 
 // Heads per block and number of splits for a shape on a device with `cus`
 // compute units (see Layout).

@@ -120,6 +120,7 @@ struct Problem {
     float *wts, *cdec;   // per-position decay weights and per-chunk decays (scan input)
     float *states, *dstates;
     float *parts;   // split partial sums of dq, dk (backward with hsplit > 1), else null
+    float *ends;    // segment end states of a segmented scan
     ssd_timer *timer;
 };
 

@@ -41,6 +41,23 @@ void head_split(const ssd_shape *s, int64_t NC, int cus, int *hsplit, int *hpb)
     *hsplit = (int)((hpg + per - 1) / per);
 }
 
+ScanPlan scan_plan(const ssd_shape *s, int ndir, int cus)
+{
+    ScanPlan P;
+    const int64_t NC = (s->T + kChunk - 1) / kChunk;
+    const int64_t DKP = pad_dim(s->dk), DVP = pad_dim(s->dv);
+    const int64_t tiles_k = s->B * s->H * (DKP / 32);
+    const int64_t wide = ndir * tiles_k * (DVP / (DVP < 64 ? DVP : 64));
+    P.narrow = DVP >= 64 && 2 * wide <= cus;
+    const int64_t blocks = P.narrow ? 2 * wide : wide;
+    while (blocks * P.nseg * 2 <= cus && NC >= P.nseg * 2 * kMinSegChunks && P.nseg < kMaxSegs) P.nseg *= 2;
+    P.seg_len = (NC + P.nseg - 1) / P.nseg;
+    // every segment holds at least one chunk (the last may be shorter)
+    if (P.seg_len > 0) P.nseg = (int)((NC + P.seg_len - 1) / P.seg_len);
+    P.blocks = blocks * P.nseg;
+    return P;
+}
+
 Layout make_layout(const ssd_shape *s, bool backward, int cus)
 {
     Layout L;
@@ -63,6 +80,15 @@ Layout make_layout(const ssd_shape *s, bool backward, int cus)
     if (backward) o = round_up(o + slab, 256);
     L.off[3] = o;
     if (backward && L.hsplit > 1) o = round_up(o + 2 * size_t(L.hsplit) * size_t(L.nqk_pad) * sizeof(float), 256);
+    // segment end states: the forward launch (one direction); the backward
+    // runs either both directions in one launch or the reverse alone
+    size_t nends = size_t(scan_plan(s, 1, cus).nseg);
+    if (backward) {
+        const size_t two = 2 * size_t(scan_plan(s, 2, cus).nseg);
+        if (two > nends) nends = two;
+    }
+    L.ends_off = o;
+    if (nends > 1) o = round_up(o + nends * BH * size_t(L.Epad) * sizeof(float), 256);
     L.off[4] = o;
     return L;
 }

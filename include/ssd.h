@@ -164,10 +164,12 @@ int ssd_fwd_noalloc(const ssd_shape *shape,
  *   [2] dstates float [B*H][NC][E]  (backward only; empty otherwise) after
  *                                   ssd_bwd: the gradient of the state
  *                                   leaving each chunk
- *   [3] parts   (backward only) when B*G*ceil(T/64) is below the device's
- *               compute-unit count: per-block-split partial sums of dq and
- *               dk that the gradient kernel writes and a final kernel adds
- *               up (no caller use); empty otherwise
+ *   [3] aux     (no caller use; empty unless needed) in the backward, when
+ *               B*G*ceil(T/64) is below the device's compute-unit count,
+ *               the per-block-split partial sums of dq and dk that the
+ *               gradient kernel writes and a final kernel adds up; then, when
+ *               the state scan's grid would leave CUs idle, the end states of
+ *               the chunk segments that its blocks scan in parallel
  *   [4] total bytes.
  * `backward` selects the backward layout.  Returns SSD_OK or an error;
  * SSD_ERR_UNSUPPORTED for shapes with dk or dv above 128, whose workspace

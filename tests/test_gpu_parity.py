@@ -113,18 +113,21 @@ def test_wide_dims_reuse_noalloc_deterministic():
     assert rel_err(y, oracle.fwd(x["q"], x["k"], x["v"], x["log_alpha"], x["h0"])) <= TOL_Y
 
 
-def test_chunk_states_match_oracle():
+@pytest.mark.parametrize("shape", [Shape(2, 2, 4, 300, 48, 40), Shape(1, 1, 2, 1500, 64, 64),
+                                   Shape(1, 1, 1, 2048, 128, 128)], ids=_id)
+def test_chunk_states_match_oracle(shape):
     """Step-level check: the state entering every chunk, as left in the
-    workspace by ssd_fwd, against the oracle's state at the chunk boundary."""
+    workspace by ssd_fwd, against the oracle's state at the chunk boundary.
+    The last two shapes fill few CUs, so their scan runs in chunk segments
+    (2 and 4) joined by the fix-up pass."""
     need_gpu()
     import torch
     import chunked_ssd_scan_fwd_amd as ssd
-    shape = Shape(2, 2, 4, 300, 48, 40)
     x = make_inputs(shape, seed=5)
     d = to_dev(x)
     sa = ssd.ShapeArg(shape.B, shape.G, shape.H, shape.T, shape.dk, shape.dv)
     ws = torch.empty(ssd.workspace_size(sa, False), dtype=torch.uint8, device="cuda")
-    say("chunk states B2G2H4T300")
+    say(f"chunk states {_id(shape)}")
     ssd.fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["h0"], workspace=ws)
     off = ssd.workspace_layout(sa, False)
     NC = (shape.T + 63) // 64
@@ -310,7 +313,7 @@ def test_guard_bands_poisoned_workspace_and_side_stream():
         assert torch.equal(d[k], before[k])
 
 
-REUSE = [ZOO[0], ZOO[3], ZOO[4], ZOO[5], ZOO[8], ZOO[10]]
+REUSE = [ZOO[0], ZOO[3], ZOO[4], ZOO[5], ZOO[8], ZOO[10], ZOO[12]]
 
 
 @pytest.mark.parametrize("shape", REUSE, ids=_id)

@@ -74,7 +74,7 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
     const float *__restrict__ dy, const float *__restrict__ la,
     const float *__restrict__ states, const float *__restrict__ dstates, float *__restrict__ dq,
     float *__restrict__ dk, float *__restrict__ dv, float *__restrict__ dla, int G, int H, int64_t T, int dk_,
-    int dv_, int64_t NC, int64_t Epad, int hpb, int64_t pstride)
+    int dv_, int64_t NC, int64_t Epad, int hpb, int64_t pstride, int64_t nunits)
 {
     using Cfg = BwdCfg<DKP, DVP>;
     if constexpr (EXD) {   // dk == DKP, dv == DVP: index arithmetic on constants
@@ -93,20 +93,33 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
     __shared__ __attribute__((aligned(16))) float bs[CH], eb[CH], el[CH];
     __shared__ float redq[CH], redk[CH], rsm[3][32], csm[3][32], redf[NTB / 64], sfx[CH];
 
-    // block ((b G + g) nsplit + split) NC + c takes heads [split hpb, split hpb + hpg) of group g
+    // Unit ((b G + g) nsplit + split) NC + c takes heads [split hpb, split hpb + hpg)
+    // of group g at chunk c.  The block walks units blockIdx.x, + gridDim.x, ...
+    // and loads the next unit's first-head operands during its last head.
     const int hpg_all = H / G, nsplit = (hpg_all + hpb - 1) / hpb;
-    const int64_t c = blockIdx.x % NC;
-    const int64_t bgs = blockIdx.x / NC;
-    const int split = (int)(bgs % nsplit);
-    const int64_t bg = bgs / nsplit;
-    const int g = (int)(bg % G);
-    const int64_t b = bg / G;
-    const int hpg = min(hpb, hpg_all - split * hpb);   // heads of this block
-    const int64_t bh0 = b * H + (int64_t)g * hpg_all + (int64_t)split * hpb;
-    // dq and dk: the split's partial sums over its heads (pstride = 0 without a split)
-    dq += split * pstride;
-    dk += split * pstride;
-    const int rows = (int)((T - c * CH) < CH ? (T - c * CH) : CH);
+    struct Unit {
+        int64_t c, bg, bh0;
+        int hpg, rows, split;
+        bool live;
+    };
+    auto unit_of = [&](int64_t u) {
+        Unit U;
+        U.live = u < nunits;
+        if (!U.live) u = 0;
+        U.c = u % NC;
+        const int64_t bgs = u / NC;
+        U.split = (int)(bgs % nsplit);
+        U.bg = bgs / nsplit;
+        const int g = (int)(U.bg % G);
+        const int64_t b = U.bg / G;
+        U.hpg = U.live ? min(hpb, hpg_all - U.split * hpb) : 0;   // heads of the unit
+        U.bh0 = b * H + (int64_t)g * hpg_all + (int64_t)U.split * hpb;
+        U.rows = (int)((T - U.c * CH) < CH ? (T - U.c * CH) : CH);
+        return U;
+    };
+    // the current unit (set at the top of each unit)
+    int64_t c = 0, bg = 0, bh0 = 0;
+    int hpg = 0, rows = 0;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int grp = wave >> 1, rt = wave & 1;
     // owns dV tiles (rt, grp NCW + u); every wave does when dv > 32, and a
@@ -125,18 +138,18 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
     float lapre = 0.f;   // log_alpha of position tid % 64 of the next head
     float blpre = 0.f;   // its chunk total b_L, once staged
 
-    auto load_a1 = [&](int hh, int tid, int m) {   // float4 m of the wave's A rows of head hh
-        const bool live = hh < hpg;
-        const int64_t bh = bh0 + (live ? hh : 0);
-        const float *src = (grp ? v : dy) + (bh * T + c * CH) * dv_;
-        const rsrc_t r = make_rsrc(src, live ? (int64_t)rows * dv_ * 4 : 0);
+    auto load_a1 = [&](const Unit &Ux, int hh, int tid, int m) {   // float4 m of the wave's A rows of head hh
+        const bool live = hh < Ux.hpg;
+        const int64_t bh = Ux.bh0 + (live ? hh : 0);
+        const float *src = (grp ? v : dy) + (bh * T + Ux.c * CH) * dv_;
+        const rsrc_t r = make_rsrc(src, live ? (int64_t)Ux.rows * dv_ * 4 : 0);
         const int lane = tid & 63, cl = lane & 31, kh = lane >> 5;
         ar[m] = load4(r, (uint32_t)((32 * rt + cl) * dv_), 8 * m + 4 * kh, dv_, true, VEC);
     };
     // float4 u of one slab of S_in and of dS_out
-    auto load_slab1 = [&](Slab &p, int hh, int ks, int tid, int u) {
-        const bool live = hh < hpg;
-        const int64_t off = ((bh0 + (live ? hh : 0)) * NC + c) * Epad;
+    auto load_slab1 = [&](Slab &p, const Unit &Ux, int hh, int ks, int tid, int u) {
+        const bool live = hh < Ux.hpg;
+        const int64_t off = ((Ux.bh0 + (live ? hh : 0)) * NC + Ux.c) * Epad;
         const rsrc_t sr = make_rsrc(states + off, live ? E * 4 : 0), dr = make_rsrc(dstates + off, live ? E * 4 : 0);
         const int r = f4_row<DVP / 4, NTB>(tid, u), c4 = f4_col<DVP / 4>(tid);
         const bool ok = (32 * DVP / 4) % NTB == 0 || r < 32;
@@ -147,13 +160,13 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
     // float4 of each state per MFMA step (step s: slab 0's float4 s, then slab
     // 1's), so that the loads of the four waves do not queue up in one burst.
     static_assert(2 * SPER <= 16, "the shortest intra loop has 16 steps");
-    auto spread_ld = [&](int hh, int tid, int s) {
-        if (s < SPER) load_slab1(p0, hh, 0, tid, s);
-        else if (NKS > 1 && s < 2 * SPER) load_slab1(pn, hh, 1, tid, s - SPER);
+    auto spread_ld = [&](const Unit &Ux, int hh, int tid, int s) {
+        if (s < SPER) load_slab1(p0, Ux, hh, 0, tid, s);
+        else if (NKS > 1 && s < 2 * SPER) load_slab1(pn, Ux, hh, 1, tid, s - SPER);
     };
-    auto load_slab = [&](Slab &p, int hh, int ks, int tid) {
+    auto load_slab = [&](Slab &p, const Unit &Ux, int hh, int ks, int tid) {
 #pragma unroll
-        for (int u = 0; u < SPER; ++u) load_slab1(p, hh, ks, tid, u);
+        for (int u = 0; u < SPER; ++u) load_slab1(p, Ux, hh, ks, tid, u);
     };
     // Stage float4 u of a slab into buffer buf; returns this thread's part of
     // <dS_out, S_in> over it.
@@ -181,10 +194,11 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
         }
         return f;
     };
-    auto load_b = [&](int hh, int tid) {
-        const bool live = hh < hpg;
-        const int64_t bh = bh0 + (live ? hh : 0);
-        lapre = gload1(make_rsrc(la + bh * T + c * CH, live ? (int64_t)rows * 4 : 0), (uint32_t)(tid & 63) * 4u);
+    auto load_b = [&](const Unit &Ux, int hh, int tid) {
+        const bool live = hh < Ux.hpg;
+        const int64_t bh = Ux.bh0 + (live ? hh : 0);
+        lapre = gload1(make_rsrc(la + bh * T + Ux.c * CH, live ? (int64_t)Ux.rows * 4 : 0),
+                       (uint32_t)(tid & 63) * 4u);
     };
     // every wave scans the head's log_alpha (so each holds b_L), wave 0 stages b
     auto stage_b = [&](int tid) {
@@ -197,7 +211,24 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
         }
     };
 
-    // ---- block set-up: Q, K in LDS; Q K^T; the first head's operands.
+    // The first unit's first-head operands.
+    Unit U = unit_of(blockIdx.x);
+    {
+        const int tid = threadIdx.x;
+#pragma unroll
+        for (int m = 0; m < NA; ++m) load_a1(U, 0, tid, m);
+        load_slab(p0, U, 0, 0, tid);
+        if (NKS > 1) load_slab(pn, U, 0, 1, tid);
+        load_b(U, 0, tid);
+    }
+    for (int64_t ui = blockIdx.x; ui < nunits; ui += gridDim.x) {
+    const Unit Un = unit_of(ui + gridDim.x);
+    c = U.c;
+    bg = U.bg;
+    bh0 = U.bh0;
+    hpg = U.hpg;
+    rows = U.rows;
+    // ---- unit set-up: Q, K in LDS; Q K^T; the first head's operands staged.
     float fro_next;
     {
         const int tid = threadIdx.x, lane = tid & 63, cl = lane & 31, kh = lane >> 5;
@@ -206,11 +237,6 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
             const int64_t tb = (int64_t)rows * dk_ * 4;
             tile_to_regs<CH, DKP, NTB, QPER>(tid, qb, make_rsrc(q + (bg * T + c * CH) * dk_, tb), dk_, VEC);
             tile_to_regs<CH, DKP, NTB, QPER>(tid, kb, make_rsrc(k + (bg * T + c * CH) * dk_, tb), dk_, VEC);
-#pragma unroll
-            for (int m = 0; m < NA; ++m) load_a1(0, tid, m);
-            load_slab(p0, 0, 0, tid);
-            if (NKS > 1) load_slab(pn, 0, 1, tid);
-            load_b(0, tid);
             regs_to_lds<CH, DKP, NTB, QPER, LDQ>(tid, qb, QL);
             regs_to_lds<CH, DKP, NTB, QPER, LDK>(tid, kb, KL);
         }
@@ -267,6 +293,10 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
     f32x16 xacc = zero16();
 
     for (int hh = 0; hh < hpg; ++hh) {
+        // the last head loads the next unit's first head, and stages nothing
+        const bool lasth = hh == hpg - 1;
+        const Unit &Ux = lasth ? Un : U;
+        const int hx = lasth ? 0 : hh + 1;
         int tid = threadIdx.x;
         asm volatile("" : "+v"(tid));
         const int lane = tid & 63, cl = lane & 31, kh = lane >> 5;
@@ -341,7 +371,7 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
                     gt = mfma32(y.w, ar[m].w, gt);
                     if ((m & 1) && (m >> 1) < SPER) {
                         if (ks >= 1 && ks + 1 < NKS) fro += store_piece(pn, (ks + 1) & 1, tid, m >> 1);
-                        if (ks + 2 < NKS) load_slab1(pn, hh, ks + 2, tid, m >> 1);
+                        if (ks + 2 < NKS) load_slab1(pn, U, hh, ks + 2, tid, m >> 1);
                     }
                     if (m == NA - 1 && gvw) ldv(0, 0);
                     __builtin_amdgcn_sched_barrier(0);
@@ -470,7 +500,7 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
                     acc = mfma32(x.z, y.z, acc);
                     acc = mfma32(x.w, y.w, acc);
 #pragma unroll
-                    for (int l = 0; l < LPG; ++l) load_a1(hh + 1, tid, (m - m0) * LPG + l);
+                    for (int l = 0; l < LPG; ++l) load_a1(Ux, hx, tid, (m - m0) * LPG + l);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
@@ -484,7 +514,7 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
         } else {
             dyvt(ad, 1, 1, 0, NA, 1);
         }
-        load_b(hh + 1, tid);
+        load_b(Ux, hx, tid);
         block_sync();   // dY and V read
         if (wave == 2) {
 #pragma unroll
@@ -589,7 +619,7 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
                             for (int ct = 0; ct < NKS; ++ct) {
                                 if (ct < NKS - 1 || !SH) dacc[ct] = mfma32(kq[f & 1][ct], xs[e], dacc[ct]);
                             }
-                            spread_ld(hh + 1, tid, f);
+                            spread_ld(Ux, hx, tid, f);
                             __builtin_amdgcn_sched_barrier(0);
                         }
                     }
@@ -637,7 +667,7 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
                         for (int ct = 0; ct < NKS; ++ct) {
                             if (ct < NKS - 1 || !SH) dacc[ct] = mfma32(qv[f & 1][ct], xd[f & 1], dacc[ct]);
                         }
-                        spread_ld(hh + 1, tid, f - 16 * RT);
+                        spread_ld(Ux, hx, tid, f - 16 * RT);
                         __builtin_amdgcn_sched_barrier(0);
                     }
                 }
@@ -683,10 +713,12 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
                     rr + sq + pk + expf(blh) * frob);
         }
         block_sync();   // dP, dY V^T sums and reductions read; the slab buffers are free
-        fro_next = store_slab(p0, 0, tid);
-        if (NKS > 1) fro_next += store_slab(pn, 1, tid);
-        stage_b(tid);
-        block_sync();
+        if (!lasth) {
+            fro_next = store_slab(p0, 0, tid);
+            if (NKS > 1) fro_next += store_slab(pn, 1, tid);
+            stage_b(tid);
+            block_sync();
+        }
     }
 
     // ---- dq, dk: transposed through LDS into [position][dk] rows, stored with
@@ -717,7 +749,9 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
         }
         block_sync();
         const int64_t tb = (int64_t)rows * dk_ * 4;
-        const rsrc_t rq = make_rsrc(dq + (bg * T + c * CH) * dk_, tb), rk = make_rsrc(dk + (bg * T + c * CH) * dk_, tb);
+        // dq and dk: the split's partial sums over its heads (pstride = 0 without a split)
+        float *dqu = dq + U.split * pstride, *dku = dk + U.split * pstride;
+        const rsrc_t rq = make_rsrc(dqu + (bg * T + c * CH) * dk_, tb), rk = make_rsrc(dku + (bg * T + c * CH) * dk_, tb);
         constexpr int Q4 = DKP / 4;
         for (int idx = tid; idx < 2 * CH * Q4; idx += NTB) {
             const int gg = idx / (CH * Q4), rem = idx - gg * CH * Q4;
@@ -736,6 +770,8 @@ __global__ __launch_bounds__(NTB) void k_bwd_grads(
             }
         }
     }
+    U = Un;
+    }   // units
 }
 // dq or dk of a split gradient launch: out[i] = sum over the ns splits of
 // parts[j * stride + i], added in split order.
@@ -758,9 +794,13 @@ int run_grads(const Problem &P, const float *q, const float *k, const float *v, 
     const int64_t nqk = s.B * s.G * s.T * s.dk;
     float *pq = hs > 1 ? P.parts : dq, *pk = hs > 1 ? P.parts + hs * P.L.nqk_pad : dk;
     const int64_t pstride = hs > 1 ? P.L.nqk_pad : 0;
-    SSD_DISPATCH(P, launch(P.timer, KID_GRADS, k_bwd_grads<KP, VP, VE, EXD>, dim3((unsigned)(s.B * s.G * hs * P.L.NC)),
-                           dim3(NTB), st, q, k, v, dy, la, P.states, P.dstates, pq, pk, dv, dla, (int)s.G, (int)s.H,
-                           s.T, (int)s.dk, (int)s.dv, P.L.NC, P.L.Epad, P.L.hpb, pstride));
+    // one block per CU at most (a block fills most of a CU's LDS); each block
+    // walks its units, loading the next unit's first head during its last
+    const int64_t nunits = s.B * s.G * hs * P.L.NC;
+    const int64_t grid = nunits < P.cus ? nunits : P.cus;
+    SSD_DISPATCH(P, launch(P.timer, KID_GRADS, k_bwd_grads<KP, VP, VE, EXD>, dim3((unsigned)grid), dim3(NTB), st, q,
+                           k, v, dy, la, P.states, P.dstates, pq, pk, dv, dla, (int)s.G, (int)s.H, s.T, (int)s.dk,
+                           (int)s.dv, P.L.NC, P.L.Epad, P.L.hpb, pstride, nunits));
     if (hs > 1) {
         if (launch_status() != SSD_OK) return SSD_ERR_DEVICE;
         const int64_t nb = (nqk + NTH - 1) / NTH;

@@ -32,6 +32,10 @@ ZOO = [
     # a group's heads over blocks, here unevenly (2 + 2 + 1 and 2 + 2 + 2 + 1)
     Shape(2, 2, 10, 1024, 48, 40),
     Shape(1, 1, 7, 4096, 64, 64),
+    # more (b, g, chunk, head split) units than CUs with a head split: the
+    # output and gradient kernels' blocks walk two units each, of different
+    # splits (200 chunks x 2 splits = 400 units on a 256-block grid)
+    Shape(1, 1, 4, 12793, 64, 64),
 ]
 
 

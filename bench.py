@@ -194,12 +194,12 @@ def max_len_search(args, torch, ssd):
 
 
 def grid_sweep(args, torch, ssd):
-    """fwd and fwd_bwd at every shape of the pages' grid: median ms over
-    `--steps` calls (events after every call), nominal TFLOP/s, GB/s of the
-    inputs and outputs, and the fraction of the step roofline (the larger of
-    the nominal FLOPs at the fp32 MFMA peak and those bytes at the HBM peak).
-    Inputs follow the synthetic recipe (mu = -4 for the 24-head shape)."""
-    import numpy as np
+    """fwd and fwd_bwd at every shape of the pages' grid, timed by the pages'
+    protocol (`protocol_ms`, `--repeats` samples): median ms per call, nominal
+    TFLOP/s, GB/s of the inputs and outputs, and the fraction of the step
+    roofline (the larger of the nominal FLOPs at the fp32 MFMA peak and those
+    bytes at the HBM peak).  Inputs follow the synthetic recipe (mu = -4 for
+    the 24-head shape)."""
     from ssd_workload import PAGE_GRID, make_inputs
     for i, ((name, T), s) in enumerate(PAGE_GRID.items()):
         x = make_inputs(s, 2000 + i, mu=-4.0 if name.startswith("g1h24") else -2.0)
@@ -218,24 +218,15 @@ def grid_sweep(args, torch, ssd):
             fwd()
             ssd.bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["h0"], d["dy"], out=grads, workspace=ws)
 
-        def med_ms(fn):
-            for _ in range(args.warmup):
-                fn()
-            evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-            torch.cuda.synchronize()
-            evs[0].record()
-            for j in range(args.steps):
-                fn()
-                evs[j + 1].record()
-            torch.cuda.synchronize()
-            return float(np.median([evs[j].elapsed_time(evs[j + 1]) for j in range(args.steps)]))
-
         f_fwd, f_bwd = nominal_flops(s)
         b_fwd, b_fb = io_bytes(s)
         out = {"workload": f"{name}_T{T}", "shape": {"B": s.B, "G": s.G, "H": s.H, "T": s.T, "dk": s.dk, "dv": s.dv}}
         for key, fn, fl, by in (("fwd", fwd, f_fwd, b_fwd), ("fwd_bwd", step, f_fwd + f_bwd, b_fb)):
-            ms = med_ms(fn)
-            out[key] = {"median_ms": ms, "tflops": fl / (ms * 1e-3) / 1e12, "gbps_io": by / (ms * 1e-3) / 1e9,
+            for _ in range(args.warmup):
+                fn()
+            r = protocol_ms(torch, fn, repeats=args.repeats)
+            ms = r["median_ms"]
+            out[key] = {"median_ms": ms, "q1_ms": r["q1_ms"], "q3_ms": r["q3_ms"], "inner": r["inner"], "tflops": fl / (ms * 1e-3) / 1e12, "gbps_io": by / (ms * 1e-3) / 1e9,
                         "roofline_frac": max(fl / PEAK_FP32_MFMA, by / PEAK_HBM) / (ms * 1e-3)}
         pf, pfb = PAGE_CHUNKED_MS[(name, T)]
         out["page_chunked_rtx3090_ms"] = {"fwd": pf, "fwd_bwd": pfb}
@@ -314,6 +305,8 @@ def config_rows(torch, ssd, args):
         b_fwd, b_fb = io_bytes(s)
         row = {"shape": {"B": s.B, "G": s.G, "H": s.H, "T": s.T, "dk": s.dk, "dv": s.dv}}
         for key, fn, fl, by in (("fwd", fwd, f_fwd, b_fwd), ("fwd_bwd", step, f_fwd + f_bwd, b_fb)):
+            for _ in range(args.warmup):
+                fn()
             r = protocol_ms(torch, fn, repeats=args.repeats)
             t = r["median_ms"] * 1e-3
             r.update({"tflops": fl / t / 1e12, "gbps_io": by / t / 1e9,

@@ -73,8 +73,8 @@ __global__ __launch_bounds__(NTS) void k_state_scan(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
     const float *__restrict__ dy, const float *__restrict__ h0, const float *__restrict__ wts,
     const float *__restrict__ cdec, float *__restrict__ states, float *__restrict__ dstates, float *__restrict__ dh0,
-    float *__restrict__ ends, int G, int H, int64_t T, int dk, int dv, int64_t NC, int64_t Epad, int64_t per_dir,
-    int dir0, int nseg, int64_t seg_len)
+    float *__restrict__ ends, float *__restrict__ segd, int G, int H, int64_t T, int dk, int dv, int64_t NC,
+    int64_t Epad, int64_t per_dir, int dir0, int nseg, int64_t seg_len)
 {
     static_assert(TJ <= DVP && DVP % TJ == 0 && (TJ == 32 || TJ == 64 || TJ == 128), "tile width");
     if constexpr (EXD) {   // dk == DKP, dv == DVP: index arithmetic on constants
@@ -243,6 +243,12 @@ __global__ __launch_bounds__(NTS) void k_state_scan(
             asm volatile("" : "+v"(acc[u]));
         }
     }
+    // With segments, one wave per (direction, segment, b h) records the
+    // product of the decays from the segment's start up to each of its
+    // chunks, segd[dl][bh][chunk in scan order], for the fix-up passes.
+    const bool rec = nseg > 1 && tile == 0 && wave == 0;
+    const rsrc_t dr = make_rsrc(segd + (dl * BHn + bh) * NC + n0, rec ? nch * 4 : 0);
+    float run = 1.f;
     for (int64_t s = 0; s < NS; ++s) {
         const int buf = (int)(s & 1);
         block_sync();   // step s staged in half `buf`
@@ -280,6 +286,10 @@ __global__ __launch_bounds__(NTS) void k_state_scan(
             const float decay = dec[cc];
             // slab[c] = S (state entering the chunk in this direction); no-op chunks store nothing
             const int64_t n = s * CPS + cc;
+            if (rec) {
+                gstore1(dr, lane == 0 ? (uint32_t)n * 4u : kOOB, run);
+                run *= decay;
+            }
             const bool live = n < nch;
             const rsrc_t dst =
                 make_rsrc(slab + (live ? (dir == 0 ? n0 + n : NC - 1 - (n0 + n)) : 0) * Epad, live ? E * 4 : 0);
@@ -331,61 +341,69 @@ __global__ __launch_bounds__(NTS) void k_state_scan(
     }
 }
 
-// Fix-up of a segmented scan.  Segment p of the chunk sequence (scan order)
-// was scanned from a zero state, the first from the true initial state, and
-// ends[dl][p][bh] holds the state leaving it.  With S_p the true state
-// entering segment p, A_p the decay over segment p and d the decay from the
-// segment's start to chunk n,
-//     S_1 = ends[0],  S_{p+1} = ends[p] + A_p S_p,   state(n) = local state(n) + d S_p.
-// One thread per (state element, segment p >= 1) forms S_p from the ends of
-// the segments before it, adds d S_p to the chunk states of its segment,
-// and for the reverse direction the last segment's thread writes dh0, the
-// state leaving it.  The decays are the per-chunk e^{b_L} (uniform over a
-// wave, so they come through the scalar cache).
+// Fix-up of a segmented scan, in two passes.  Segment p of the chunk
+// sequence (scan order) was scanned from a zero state, the first from the
+// true initial state, and ends[dl][p][bh] holds the state leaving it.  With
+// S_p the true state entering segment p, A_p the decay over segment p and
+// D(n) the decay from the segment's start to chunk n (segd, written by the
+// scan),
+//     S_1 = ends[0],  S_{p+1} = ends[p] + A_p S_p,   state(n) = local state(n) + D(n) S_p.
+// Pass 1 (one thread per state element of each (direction, b h)) walks the
+// segments in order and overwrites ends[p] with S_{p+1}, so that ends[p - 1]
+// then holds the state entering segment p; for the reverse direction it also
+// writes dh0, the state leaving the last segment.  A_p = D(last chunk of p)
+// times that chunk's decay, the same product in the same order as the scan's.
 constexpr int NTF = 256;
-__global__ __launch_bounds__(NTF) void k_seg_fixup(float *__restrict__ states, float *__restrict__ dstates,
-                                                   const float *__restrict__ ends, const float *__restrict__ cdec,
-                                                   float *__restrict__ dh0, int64_t BH, int64_t NC, int64_t E,
-                                                   int64_t Epad, int nseg, int64_t seg_len, int ndir, int dir0)
+__global__ __launch_bounds__(NTF) void k_seg_carry(float *__restrict__ ends, const float *__restrict__ segd,
+                                                   const float *__restrict__ cdec, float *__restrict__ dh0,
+                                                   int64_t BH, int64_t NC, int64_t E, int64_t Epad, int nseg,
+                                                   int64_t seg_len, int dir0)
 {
-    const int64_t idx = (int64_t)blockIdx.x * NTF + threadIdx.x;
-    if (idx >= (int64_t)ndir * (nseg - 1) * BH * E) return;
-    const int64_t e = idx % E, t = idx / E, bh = t % BH, t2 = t / BH;
-    const int ps = 1 + (int)(t2 % (nseg - 1)), dl = (int)(t2 / (nseg - 1)), dir = dir0 + dl;
-    const float *en = ends + ((int64_t)dl * nseg * BH + bh) * Epad + e;   // en[p BH Epad]: segment p
-    const float *dc = cdec + bh * NC;
+    const int64_t e = (int64_t)blockIdx.x * NTF + threadIdx.x;
+    if (e >= E) return;
+    const int64_t dlbh = blockIdx.y, bh = dlbh % BH;
+    const int dl = (int)(dlbh / BH), dir = dir0 + dl;
+    float *en = ends + ((int64_t)dl * nseg * BH + bh) * Epad + e;   // en[p BH Epad]: segment p
+    const float *sd = segd + dlbh * NC, *dc = cdec + bh * NC;
     auto chunk = [&](int64_t n) { return dir == 0 ? n : NC - 1 - n; };
-    float carry = en[0];
-    for (int p = 1; p < ps; ++p) {
-        float a = 1.f;
-        for (int64_t n = p * seg_len; n < (p + 1) * seg_len; ++n) a *= dc[chunk(n)];   // full segments
-        carry = en[(int64_t)p * BH * Epad] + a * carry;
+    auto total = [&](int64_t last) { return sd[last] * dc[chunk(last)]; };   // A of the segment ending at `last`
+    float S = en[0];   // S_1
+    for (int p = 1; p < nseg - 1; ++p) {
+        S = en[(int64_t)p * BH * Epad] + total((p + 1) * seg_len - 1) * S;
+        en[(int64_t)p * BH * Epad] = S;   // S_{p+1}
     }
-    float *slab = (dir == 0 ? states : dstates) + bh * NC * Epad + e;
-    const int64_t n0 = ps * seg_len, n1 = (n0 + seg_len) < NC ? (n0 + seg_len) : NC;
-    float d = 1.f;
-    int64_t n = n0;
-    // four chunks at a time: their loads are independent of one another
-    for (; n + 4 <= n1; n += 4) {
-        int64_t c[4];
-        float x[4];
+    if (dir == 1) dh0[bh * E + e] = en[(int64_t)(nseg - 1) * BH * Epad] + total(NC - 1) * S;
+}
+
+// Pass 2: one thread per 4 consecutive state elements of each chunk of
+// segments p >= 1 adds D(n) S_p.  blockIdx.x = (n - seg_len) neb + element
+// block (neb blocks of 4 NTF elements per state), blockIdx.y: direction and
+// b h.
+__global__ __launch_bounds__(NTF) void k_seg_apply(float *__restrict__ states, float *__restrict__ dstates,
+                                                   const float *__restrict__ ends, const float *__restrict__ segd,
+                                                   int64_t BH, int64_t NC, int E, int64_t Epad, int nseg,
+                                                   int64_t seg_len, int dir0, int neb, bool vec)
+{
+    const int64_t xb = blockIdx.x / (unsigned)neb;
+    const int e4 = (int)((blockIdx.x - xb * neb) * NTF + threadIdx.x) * 4;
+    const int64_t n = seg_len + xb;
+    const int64_t dlbh = blockIdx.y, bh = dlbh % BH;
+    const int dl = (int)(dlbh / BH), dir = dir0 + dl;
+    const int64_t p = n / seg_len;
+    const float d = segd[dlbh * NC + n];
+    const rsrc_t cr = make_rsrc(ends + (((int64_t)dl * nseg + p - 1) * BH + bh) * Epad, (int64_t)E * 4);
+    const float4 c = load4(cr, 0, e4, E, true, vec);
+    float *slab = (dir == 0 ? states : dstates) + (bh * NC + (dir == 0 ? n : NC - 1 - n)) * Epad;
+    const rsrc_t sr = make_rsrc(slab, (int64_t)E * 4);
+    const float4 x = load4(sr, 0, e4, E, true, vec);
+    const float o[4] = {x.x + d * c.x, x.y + d * c.y, x.z + d * c.z, x.w + d * c.w};
+    if (vec) {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, make_float4(o[0], o[1], o[2], o[3])), sr,
+                                               e4 < E ? (uint32_t)e4 * 4u : kOOB, 0, 0);
+    } else {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            c[u] = chunk(n + u);
-            x[u] = slab[c[u] * Epad];
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            slab[c[u] * Epad] = x[u] + d * carry;
-            d *= dc[c[u]];
-        }
+        for (int i = 0; i < 4; ++i) gstore1(sr, e4 + i < E ? (uint32_t)(e4 + i) * 4u : kOOB, o[i]);
     }
-    for (; n < n1; ++n) {
-        const int64_t c = chunk(n);
-        slab[c * Epad] += d * carry;
-        d *= dc[c];
-    }
-    if (dir == 1 && ps == nseg - 1) dh0[bh * E + e] = en[(int64_t)ps * BH * Epad] + d * carry;
 }
 
 // The fused state scan over the directions in `dirs` (see ssd_launch.h).
@@ -418,22 +436,29 @@ int run_scan(const Problem &P, int dirs, bool prep, const float *q, const float 
             const dim3 grid((unsigned)(ndir * per_dir)), blk(NTS);
             if (pair)
                 launch(P.timer, kid, k_state_scan<KP, VP, VE, TJ, 2, EXD>, grid, blk, st, q, k, v, dy, h0, P.wts, P.cdec,
-                       P.states, P.dstates, dh0, P.ends, (int)s.G, (int)s.H, s.T, (int)s.dk, (int)s.dv, P.L.NC,
-                       P.L.Epad, per_dir, dir0, plan.nseg, plan.seg_len);
+                       P.states, P.dstates, dh0, P.ends, P.segd, (int)s.G, (int)s.H, s.T, (int)s.dk, (int)s.dv,
+                       P.L.NC, P.L.Epad, per_dir, dir0, plan.nseg, plan.seg_len);
             else
                 launch(P.timer, kid, k_state_scan<KP, VP, VE, TJ, 1, EXD>, grid, blk, st, q, k, v, dy, h0, P.wts, P.cdec,
-                       P.states, P.dstates, dh0, P.ends, (int)s.G, (int)s.H, s.T, (int)s.dk, (int)s.dv, P.L.NC,
-                       P.L.Epad, per_dir, dir0, plan.nseg, plan.seg_len);
+                       P.states, P.dstates, dh0, P.ends, P.segd, (int)s.G, (int)s.H, s.T, (int)s.dk, (int)s.dv,
+                       P.L.NC, P.L.Epad, per_dir, dir0, plan.nseg, plan.seg_len);
         }));
     };
     if (narrow) run(BoolC<true>{});
     else run(BoolC<false>{});
     if (plan.nseg > 1) {
+        // ndir * BH is small here: a segmented plan fills at most the CUs
         if (launch_status() != SSD_OK) return SSD_ERR_DEVICE;
-        const int64_t E = s.dk * s.dv, n = ndir * (plan.nseg - 1) * BH * E;
-        launch(P.timer, KID_AUX, k_seg_fixup, dim3((unsigned)((n + NTF - 1) / NTF)), dim3(NTF), st, P.states,
-               P.dstates, (const float *)P.ends, (const float *)P.cdec, dh0, BH, P.L.NC, E, P.L.Epad, plan.nseg,
-               plan.seg_len, ndir, dir0);
+        const int64_t E = s.dk * s.dv;
+        launch(P.timer, KID_AUX, k_seg_carry, dim3((unsigned)((E + NTF - 1) / NTF), (unsigned)(ndir * BH)), dim3(NTF),
+               st, P.ends, (const float *)P.segd, (const float *)P.cdec, dh0, BH, P.L.NC, E, P.L.Epad, plan.nseg,
+               plan.seg_len, dir0);
+        if (launch_status() != SSD_OK) return SSD_ERR_DEVICE;
+        const int64_t nfix = P.L.NC - plan.seg_len;   // chunks of segments 1 ..
+        const int neb = (int)((E + 4 * NTF - 1) / (4 * NTF));
+        launch(P.timer, KID_AUX, k_seg_apply, dim3((unsigned)(nfix * neb), (unsigned)(ndir * BH)), dim3(NTF), st,
+               P.states, P.dstates, (const float *)P.ends, (const float *)P.segd, BH, P.L.NC, (int)E, P.L.Epad,
+               plan.nseg, plan.seg_len, dir0, neb, E % 4 == 0);
     }
     return launch_status();
 }

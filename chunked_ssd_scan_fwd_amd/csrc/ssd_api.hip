@@ -127,6 +127,7 @@ static int prepare(const ssd_shape *shape, bool backward, void *ws, size_t ws_by
     P->dstates = backward ? reinterpret_cast<float *>(w + P->L.off[2]) : nullptr;
     P->parts = backward && P->L.hsplit > 1 ? reinterpret_cast<float *>(w + P->L.off[3]) : nullptr;
     P->ends = reinterpret_cast<float *>(w + P->L.ends_off);
+    P->segd = reinterpret_cast<float *>(w + P->L.segd_off);
     P->timer = tm;
     return SSD_OK;
 }

@@ -30,8 +30,11 @@ struct Layout {
     int hpb = 1;
     int64_t nqk_pad = 0;     // B*G*T*dk rounded up to a multiple of 64
     // Segment end states of a segmented state scan (see ScanPlan), at byte
-    // offset ends_off inside region 3: [ndir][nseg][B*H][Epad] floats.
+    // offset ends_off inside region 3: [ndir][nseg][B*H][Epad] floats; then at
+    // segd_off, [2][B*H][NC] floats: per direction and chunk (in scan order),
+    // the product of the chunk decays from its segment's start up to it.
     size_t ends_off = 0;
+    size_t segd_off = 0;
 };
 
 // Launch plan of the state scan for one launch over `ndir` directions.  The

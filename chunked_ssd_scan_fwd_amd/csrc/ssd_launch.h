@@ -66,10 +66,14 @@ inline void launch(ssd_timer *tm, int kid, void (*f)(P...), dim3 grid, dim3 blk,
             e0 = e1 = nullptr;
         }
     }
-    hipExtLaunchKernel(reinterpret_cast<const void *>(f), grid, blk, ptrs, 0, st, e0, e1, 0);
+    // A failed launch is also this thread's last HIP error, which
+    // launch_status() reports; its events were never recorded and go back.
+    const hipError_t rc = hipExtLaunchKernel(reinterpret_cast<const void *>(f), grid, blk, ptrs, 0, st, e0, e1, 0);
     if (e0 && e1) {
-        tm->pending[kid][0].push_back(e0);
-        tm->pending[kid][1].push_back(e1);
+        auto &to0 = rc == hipSuccess ? tm->pending[kid][0] : tm->pool;
+        auto &to1 = rc == hipSuccess ? tm->pending[kid][1] : tm->pool;
+        to0.push_back(e0);
+        to1.push_back(e1);
     }
 }
 
@@ -121,6 +125,7 @@ struct Problem {
     float *states, *dstates;
     float *parts;   // split partial sums of dq, dk (backward with hsplit > 1), else null
     float *ends;    // segment end states of a segmented scan
+    float *segd;    // per-chunk decay products within segments (segmented scan)
     ssd_timer *timer;
 };
 

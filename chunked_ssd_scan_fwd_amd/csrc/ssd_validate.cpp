@@ -80,15 +80,20 @@ Layout make_layout(const ssd_shape *s, bool backward, int cus)
     if (backward) o = round_up(o + slab, 256);
     L.off[3] = o;
     if (backward && L.hsplit > 1) o = round_up(o + 2 * size_t(L.hsplit) * size_t(L.nqk_pad) * sizeof(float), 256);
-    // segment end states: the forward launch (one direction); the backward
-    // runs either both directions in one launch or the reverse alone
-    size_t nends = size_t(scan_plan(s, 1, cus).nseg);
+    // segment end states, for launches whose plan cuts the chunks into
+    // segments: the forward launch (one direction); the backward runs either
+    // both directions in one launch or the reverse alone
+    size_t nends = 0;
+    const size_t one = size_t(scan_plan(s, 1, cus).nseg);
+    if (one > 1) nends = one;
     if (backward) {
-        const size_t two = 2 * size_t(scan_plan(s, 2, cus).nseg);
-        if (two > nends) nends = two;
+        const size_t two = size_t(scan_plan(s, 2, cus).nseg);
+        if (two > 1 && 2 * two > nends) nends = 2 * two;
     }
     L.ends_off = o;
-    if (nends > 1) o = round_up(o + nends * BH * size_t(L.Epad) * sizeof(float), 256);
+    if (nends > 0) o = round_up(o + nends * BH * size_t(L.Epad) * sizeof(float), 256);
+    L.segd_off = o;
+    if (nends > 0) o = round_up(o + 2 * BH * size_t(L.NC) * sizeof(float), 256);
     L.off[4] = o;
     return L;
 }

@@ -169,7 +169,8 @@ int ssd_fwd_noalloc(const ssd_shape *shape,
  *               the per-block-split partial sums of dq and dk that the
  *               gradient kernel writes and a final kernel adds up; then, when
  *               the state scan's grid would leave CUs idle, the end states of
- *               the chunk segments that its blocks scan in parallel
+ *               the chunk segments that its blocks scan in parallel and the
+ *               per-chunk decay products within each segment
  *   [4] total bytes.
  * `backward` selects the backward layout.  Returns SSD_OK or an error;
  * SSD_ERR_UNSUPPORTED for shapes with dk or dv above 128, whose workspace

@@ -84,6 +84,25 @@ def test_empty_problems_need_no_workspace():
     assert _call_fwd(ssd.ShapeArg(0, 1, 1, 10, 8, 8), ptr=0) == 0
 
 
+def _scan_segments(B, H, T, dk, dv, ndir, cus=256):
+    """Segments of a state-scan launch over `ndir` directions: one block per
+    32 x 64 state tile (32 x dv for dv < 64); when that fills at most half
+    the CUs the tiles are 32 wide; then the segment count doubles while the
+    grid still fills at most half the CUs, every segment keeps at least 8
+    chunks and there are at most 64; finally it is recounted so that no
+    segment is empty."""
+    NC = -(-T // 64)
+    pad = lambda d: 32 if d <= 32 else (64 if d <= 64 else 128)
+    DKP, DVP = pad(dk), pad(dv)
+    wide = ndir * B * H * (DKP // 32) * (DVP // min(DVP, 64))
+    blocks = 2 * wide if (DVP >= 64 and 2 * wide <= cus) else wide
+    nseg = 1
+    while blocks * nseg * 2 <= cus and NC >= nseg * 2 * 8 and nseg < 64:
+        nseg *= 2
+    seg_len = -(-NC // nseg)
+    return -(-NC // seg_len) if seg_len > 0 else nseg
+
+
 @pytest.mark.parametrize("B,G,H,T,dk,dv", [(4, 2, 8, 8192, 128, 128), (2, 1, 24, 8192, 128, 64),
                                            (4, 2, 4, 2048, 48, 40), (1, 1, 1, 1, 1, 1),
                                            (1, 1, 4, 130, 64, 64), (2, 2, 10, 1024, 48, 40),
@@ -112,11 +131,44 @@ def test_workspace_layout_formula(B, G, H, T, dk, dv):
     hpb = -(-hpg // want)
     hsplit = -(-hpg // hpb)
     parts = 2 * hsplit * (-(-(B * G * T * dk) // 64) * 64) * 4 if hsplit > 1 else 0
-    assert off[4] == up(off[3] + parts)
+    # segment end states and per-chunk decay products when a scan launch
+    # (one direction, or both in the backward) runs in chunk segments
+    n1, n2 = _scan_segments(B, H, T, dk, dv, 1), _scan_segments(B, H, T, dk, dv, 2)
+    nends_b = max(n1 if n1 > 1 else 0, 2 * n2 if n2 > 1 else 0)
+    nends_f = n1 if n1 > 1 else 0
+
+    def seg_bytes(nends):
+        return up(nends * BH * Epad * 4) + up(2 * BH * NC * 4) if nends else 0
+
+    assert off[4] == up(off[3] + parts) + seg_bytes(nends_b)
     assert ssd.workspace_size(s, True) == off[4]
     fo = ssd.workspace_layout(s, False)
-    assert fo[:2] == off[:2] and fo[2] == fo[3] == fo[4] == off[2]
-    assert ssd.workspace_size(s, False) == off[2]
+    assert fo[:2] == off[:2] and fo[2] == fo[3] == off[2]
+    assert fo[4] == fo[3] + seg_bytes(nends_f)
+    assert ssd.workspace_size(s, False) == fo[4]
+
+
+def test_workspace_layout_segmented_scan():
+    """A shape whose state scan runs in chunk segments (few heads, long T):
+    region 3 holds the segment end states and the per-chunk decay products.
+    B = G = H = 1, T = 8192, dk = dv = 128 on 256 CUs: the forward scan has
+    16 narrow tiles, so 16 segments of 8 chunks; the two-direction backward
+    launch has 32, so 8 segments per direction; room for 16 end states and
+    [2][1][128] decay products."""
+    s = ssd.ShapeArg(1, 1, 1, 8192, 128, 128)
+    off = ssd.workspace_layout(s, True)
+    NC, Epad = 128, 128 * 128
+
+    def up(x):
+        return (x + 255) // 256 * 256
+
+    assert off[3] == up(off[2] + NC * Epad * 4)
+    ends = 16 * Epad * 4
+    assert off[4] == up(off[3] + ends) + up(2 * NC * 4)
+    fo = ssd.workspace_layout(s, False)
+    assert fo[3] == fo[2] == off[2]
+    assert fo[4] == up(fo[3] + ends) + up(2 * NC * 4)
+    assert _scan_segments(1, 1, 8192, 128, 128, 1) == 16 and _scan_segments(1, 1, 8192, 128, 128, 2) == 8
 
 
 def test_status_strings_and_constants():

@@ -67,6 +67,8 @@ def library(path: str | None = None):
     lib.ssd_strerror.argtypes = [ctypes.c_int]
     lib.ssd_strerror.restype = ctypes.c_char_p
     lib.ssd_chunk_size.restype = ctypes.c_int
+    lib.ssd_fwd_state_stride.argtypes = [sp]
+    lib.ssd_fwd_state_stride.restype = ctypes.c_int
     lib.ssd_timer_create.argtypes = [ctypes.c_int]
     lib.ssd_timer_create.restype = vp
     lib.ssd_timer_destroy.argtypes = [vp]
@@ -128,6 +130,15 @@ def workspace_layout(shape: ShapeArg, backward: bool) -> list:
     if rc != 0:
         raise SsdError(rc, "ssd_workspace_layout")
     return list(arr)
+
+
+def fwd_state_stride(shape: ShapeArg) -> int:
+    """1 if ssd_fwd leaves the state of every chunk in the workspace, 2 if
+    only that of every even chunk (the forward on chunk pairs)."""
+    n = library().ssd_fwd_state_stride(ctypes.byref(shape))
+    if n < 0:
+        raise SsdError(3, "ssd_fwd_state_stride")
+    return n
 
 
 def _workspace(shape, backward, device, workspace):

@@ -421,6 +421,7 @@ __global__ __launch_bounds__(NTW) void k_chunk_output(const float *__restrict__ 
 int run_output(const Problem &P, const float *q, const float *k, const float *v, const float *la, float *y,
                hipStream_t st)
 {
+    if (P.pair) return run_pair_output(P, q, k, v, la, y, st);
     const ssd_shape &s = P.s;
     // one block per CU at most (a block fills most of a CU's LDS); each block
     // walks its units and prefetches the next unit's tiles during the last

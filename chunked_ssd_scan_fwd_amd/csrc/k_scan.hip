@@ -74,7 +74,7 @@ __global__ __launch_bounds__(NTS) void k_state_scan(
     const float *__restrict__ dy, const float *__restrict__ h0, const float *__restrict__ wts,
     const float *__restrict__ cdec, float *__restrict__ states, float *__restrict__ dstates, float *__restrict__ dh0,
     float *__restrict__ ends, float *__restrict__ segd, int G, int H, int64_t T, int dk, int dv, int64_t NC,
-    int64_t Epad, int64_t per_dir, int dir0, int nseg, int64_t seg_len)
+    int64_t Epad, int64_t per_dir, int dir0, int nseg, int64_t seg_len, int spar)
 {
     static_assert(TJ <= DVP && DVP % TJ == 0 && (TJ == 32 || TJ == 64 || TJ == 128), "tile width");
     if constexpr (EXD) {   // dk == DKP, dv == DVP: index arithmetic on constants
@@ -290,7 +290,8 @@ __global__ __launch_bounds__(NTS) void k_state_scan(
                 gstore1(dr, lane == 0 ? (uint32_t)n * 4u : kOOB, run);
                 run *= decay;
             }
-            const bool live = n < nch;
+            // spar 1 (2): the forward direction stores the states of even (odd) chunks only
+            const bool live = n < nch && (spar == 0 || dir != 0 || (int)((n0 + n) & 1) == spar - 1);
             const rsrc_t dst =
                 make_rsrc(slab + (live ? (dir == 0 ? n0 + n : NC - 1 - (n0 + n)) : 0) * Epad, live ? E * 4 : 0);
             if constexpr (VEC) {
@@ -382,13 +383,14 @@ __global__ __launch_bounds__(NTF) void k_seg_carry(float *__restrict__ ends, con
 __global__ __launch_bounds__(NTF) void k_seg_apply(float *__restrict__ states, float *__restrict__ dstates,
                                                    const float *__restrict__ ends, const float *__restrict__ segd,
                                                    int64_t BH, int64_t NC, int E, int64_t Epad, int nseg,
-                                                   int64_t seg_len, int dir0, int neb, bool vec)
+                                                   int64_t seg_len, int dir0, int neb, bool vec, int spar)
 {
     const int64_t xb = blockIdx.x / (unsigned)neb;
     const int e4 = (int)((blockIdx.x - xb * neb) * NTF + threadIdx.x) * 4;
     const int64_t n = seg_len + xb;
     const int64_t dlbh = blockIdx.y, bh = dlbh % BH;
     const int dl = (int)(dlbh / BH), dir = dir0 + dl;
+    if (spar && dir == 0 && (int)(n & 1) != spar - 1) return;   // a chunk whose state is not stored
     const int64_t p = n / seg_len;
     const float d = segd[dlbh * NC + n];
     const rsrc_t cr = make_rsrc(ends + (((int64_t)dl * nseg + p - 1) * BH + bh) * Epad, (int64_t)E * 4);
@@ -407,7 +409,7 @@ __global__ __launch_bounds__(NTF) void k_seg_apply(float *__restrict__ states, f
 }
 
 // The fused state scan over the directions in `dirs` (see ssd_launch.h).
-int run_scan(const Problem &P, int dirs, bool prep, const float *q, const float *k, const float *v,
+int run_scan(const Problem &P, int dirs, bool prep, StoreSet store, const float *q, const float *k, const float *v,
              const float *dy, const float *la, const float *h0, float *dh0, hipStream_t st)
 {
     const ssd_shape &s = P.s;
@@ -426,6 +428,7 @@ int run_scan(const Problem &P, int dirs, bool prep, const float *q, const float 
     const int ndir = dirs == 3 ? 2 : 1, dir0 = dirs == 2 ? 1 : 0;
     const int64_t tiles_k = BH * (P.DKP / TI);
     const ScanPlan plan = scan_plan(&s, ndir, P.cus);
+    const int spar = (int)store;
     const bool narrow = plan.narrow;
     const bool pair = plan.blocks <= P.cus;
     const int kid = dirs == 1 ? KID_SCAN : dirs == 2 ? KID_SCANR : KID_SCAN2;
@@ -437,11 +440,11 @@ int run_scan(const Problem &P, int dirs, bool prep, const float *q, const float 
             if (pair)
                 launch(P.timer, kid, k_state_scan<KP, VP, VE, TJ, 2, EXD>, grid, blk, st, q, k, v, dy, h0, P.wts, P.cdec,
                        P.states, P.dstates, dh0, P.ends, P.segd, (int)s.G, (int)s.H, s.T, (int)s.dk, (int)s.dv,
-                       P.L.NC, P.L.Epad, per_dir, dir0, plan.nseg, plan.seg_len);
+                       P.L.NC, P.L.Epad, per_dir, dir0, plan.nseg, plan.seg_len, spar);
             else
                 launch(P.timer, kid, k_state_scan<KP, VP, VE, TJ, 1, EXD>, grid, blk, st, q, k, v, dy, h0, P.wts, P.cdec,
                        P.states, P.dstates, dh0, P.ends, P.segd, (int)s.G, (int)s.H, s.T, (int)s.dk, (int)s.dv,
-                       P.L.NC, P.L.Epad, per_dir, dir0, plan.nseg, plan.seg_len);
+                       P.L.NC, P.L.Epad, per_dir, dir0, plan.nseg, plan.seg_len, spar);
         }));
     };
     if (narrow) run(BoolC<true>{});
@@ -458,7 +461,7 @@ int run_scan(const Problem &P, int dirs, bool prep, const float *q, const float 
         const int neb = (int)((E + 4 * NTF - 1) / (4 * NTF));
         launch(P.timer, KID_AUX, k_seg_apply, dim3((unsigned)(nfix * neb), (unsigned)(ndir * BH)), dim3(NTF), st,
                P.states, P.dstates, (const float *)P.ends, (const float *)P.segd, BH, P.L.NC, (int)E, P.L.Epad,
-               plan.nseg, plan.seg_len, dir0, neb, E % 4 == 0);
+               plan.nseg, plan.seg_len, dir0, neb, E % 4 == 0, spar);
     }
     return launch_status();
 }

@@ -120,6 +120,12 @@ static int prepare(const ssd_shape *shape, bool backward, void *ws, size_t ws_by
     P->DVP = pad_dim(shape->dv);
     P->vec = (shape->dk % 4) == 0 && (shape->dv % 4) == 0;
     P->exact = shape->dk == P->DKP && shape->dv == P->DVP;
+    // Chunk pairs where they measured faster: full 128-column states (the
+    // pair kernel's P is formed once per two steps) and at least two pair
+    // units per CU (its larger set-up, Q K^T over 128 positions, is then
+    // loaded under the previous unit's MFMAs).  g2h8_d128 T8192: forward
+    // 279 -> 257 us; at one unit per CU (T2048) or dv = 64 it was slower.
+    P->pair = fwd_pairs(shape, P->cus);
     char *w = static_cast<char *>(ws);
     P->wts = reinterpret_cast<float *>(w + P->L.off[0]);
     P->cdec = reinterpret_cast<float *>(w + P->L.cdec_off);
@@ -154,7 +160,7 @@ static int fwd_impl(const ssd_shape *shape, const float *q, const float *k, cons
     Problem P;
     rc = prepare(shape, false, workspace, workspace_bytes, tm, &P);
     if (rc != SSD_OK) return rc;
-    rc = run_scan(P, 1, true, q, k, v, nullptr, log_alpha, h0, nullptr, st);
+    rc = run_scan(P, 1, true, P.pair ? kStoreEven : kStoreAll, q, k, v, nullptr, log_alpha, h0, nullptr, st);
     if (rc != SSD_OK) return rc;
     return run_output(P, q, k, v, log_alpha, y, st);
 }
@@ -193,8 +199,13 @@ static int bwd_impl(const ssd_shape *shape, const float *q, const float *k, cons
     rc = prepare(shape, true, workspace, workspace_bytes, tm, &P);
     if (rc != SSD_OK) return rc;
     // dS_out (reverse) of every chunk and dh0; without reuse also the decay
-    // weights and S_in (forward), the latter in the same launch.
-    rc = run_scan(P, reuse ? 2 : 3, !reuse, q, k, v, dy, log_alpha, h0, dh0, st);
+    // weights and S_in (forward), the latter in the same launch.  A forward
+    // on chunk pairs left S_in of even chunks only: the forward direction
+    // runs again, storing the odd chunks' states.
+    if (reuse && P.pair)
+        rc = run_scan(P, 3, false, kStoreOdd, q, k, v, dy, log_alpha, h0, dh0, st);
+    else
+        rc = run_scan(P, reuse ? 2 : 3, !reuse, kStoreAll, q, k, v, dy, log_alpha, h0, dh0, st);
     if (rc != SSD_OK) return rc;
     return run_grads(P, q, k, v, dy, log_alpha, dq, dk, dv, dlog_alpha, st);
 }

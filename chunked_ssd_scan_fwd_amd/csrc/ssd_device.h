@@ -147,6 +147,10 @@ template <bool B>
 struct BoolC {
     static constexpr bool value = B;
 };
+template <int N>
+struct IntC {
+    static constexpr int value = N;
+};
 
 // Workgroup barrier across which the compiler may move no memory access.
 // __syncthreads() alone is a fence pair around s_barrier, and this compiler

@@ -55,6 +55,12 @@ struct ScanPlan {
 };
 ScanPlan scan_plan(const ssd_shape *s, int ndir, int cus);
 
+// Whether the forward of a direct (dk, dv <= 128) shape runs on chunk pairs:
+// full 128-column states (pad(dv) = 128) and at least two pair units
+// (b, g, pair of chunks) per CU.  Its state scan then stores the states of
+// even chunks only.
+bool fwd_pairs(const ssd_shape *s, int cus);
+
 // Heads per block and number of splits for a shape on a device with `cus`
 // compute units (see Layout).
 void head_split(const ssd_shape *s, int64_t NC, int cus, int *hsplit, int *hpb);

@@ -126,6 +126,10 @@ struct Problem {
     float *parts;   // split partial sums of dq, dk (backward with hsplit > 1), else null
     float *ends;    // segment end states of a segmented scan
     float *segd;    // per-chunk decay products within segments (segmented scan)
+    // The forward runs on chunk pairs: its scan stores the states of even
+    // chunks only and the pair output kernel takes the odd chunks' inter term
+    // from them.
+    bool pair;
     ssd_timer *timer;
 };
 
@@ -133,13 +137,20 @@ struct Problem {
 // fused chunk-state + state-pass scan over the directions in `dirs`: 1 =
 // forward only (fills `states` with S_in), 3 = both in one launch (also
 // fills `dstates` with dS_out and writes dh0), 2 = reverse only (dstates and
-// dh0; `states` is not touched, the weights must be in place).
-int run_scan(const Problem &P, int dirs, bool prep, const float *q, const float *k, const float *v,
+// dh0; `states` is not touched, the weights must be in place).  The forward
+// direction stores S_in of every chunk (kStoreAll), of even chunks only
+// (kStoreEven: the forward on chunk pairs) or of odd chunks only (kStoreOdd:
+// completing what such a forward left).
+enum StoreSet { kStoreAll = 0, kStoreEven = 1, kStoreOdd = 2 };
+int run_scan(const Problem &P, int dirs, bool prep, StoreSet store, const float *q, const float *k, const float *v,
              const float *dy, const float *la, const float *h0, float *dh0, hipStream_t st);
 
-// Output of every chunk: y = intra-chunk term + diag(e^b) Q S_in.
+// Output of every chunk: y = intra-chunk term + diag(e^b) Q S_in.  With
+// P.pair, from the states of even chunks (run_pair_output).
 int run_output(const Problem &P, const float *q, const float *k, const float *v, const float *la, float *y,
                hipStream_t st);
+int run_pair_output(const Problem &P, const float *q, const float *k, const float *v, const float *la, float *y,
+                    hipStream_t st);
 
 // Gradients of every chunk from the states and state gradients in the
 // workspace; with a head split, also the fixed-order sum of the partials.

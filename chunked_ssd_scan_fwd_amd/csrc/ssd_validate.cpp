@@ -41,6 +41,12 @@ void head_split(const ssd_shape *s, int64_t NC, int cus, int *hsplit, int *hpb)
     *hsplit = (int)((hpg + per - 1) / per);
 }
 
+bool fwd_pairs(const ssd_shape *s, int cus)
+{
+    const int64_t NC = (s->T + kChunk - 1) / kChunk;
+    return pad_dim(s->dv) == 128 && s->B * s->G * ((NC + 1) / 2) >= 2 * int64_t(cus);
+}
+
 ScanPlan scan_plan(const ssd_shape *s, int ndir, int cus)
 {
     ScanPlan P;
@@ -195,6 +201,12 @@ int ssd_workspace_layout(const ssd_shape *shape, int backward, size_t offsets[SS
     const ssd::Layout L = ssd::make_layout(shape, backward != 0, ssd::device_cus());
     for (int i = 0; i <= SSD_WS_REGIONS; ++i) offsets[i] = L.off[i];
     return SSD_OK;
+}
+
+int ssd_fwd_state_stride(const ssd_shape *shape)
+{
+    if (ssd::check_shape(shape) != SSD_OK || ssd::needs_split(shape)) return -1;
+    return ssd::fwd_pairs(shape, ssd::device_cus()) ? 2 : 1;
 }
 
 const char *ssd_strerror(int status)

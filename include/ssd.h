@@ -158,9 +158,11 @@ int ssd_fwd_noalloc(const ssd_shape *shape,
  *               and e^{b_t}, and per chunk e^{b_L}, where b_t is the
  *               within-chunk inclusive cumulative sum of log_alpha and b_L
  *               its value at the chunk's last position; NC = ceil(T/64)
- *   [1] states  float [B*H][NC][E]  after ssd_fwd/ssd_bwd: the state entering
- *                                   each chunk, row-major dk x dv; E = dk*dv
- *                                   rounded up to a multiple of 64
+ *   [1] states  float [B*H][NC][E]  the state entering each chunk, row-major
+ *                                   dk x dv; E = dk*dv rounded up to a multiple
+ *                                   of 64.  After ssd_bwd: every chunk.  After
+ *                                   ssd_fwd: chunks 0, s, 2s, ... with s =
+ *                                   ssd_fwd_state_stride(shape)
  *   [2] dstates float [B*H][NC][E]  (backward only; empty otherwise) after
  *                                   ssd_bwd: the gradient of the state
  *                                   leaving each chunk
@@ -179,6 +181,17 @@ int ssd_fwd_noalloc(const ssd_shape *shape,
  * between chunks, checked against the oracle's state at chunk boundaries. */
 int ssd_workspace_layout(const ssd_shape *shape, int backward, size_t offsets[SSD_WS_REGIONS + 1]);
 
+/* Test support: 1 if ssd_fwd leaves the state of every chunk in the
+ * workspace, 2 if only that of every even chunk (-1 for an invalid shape or
+ * one with dk or dv above 128).  With 2 the forward runs on chunk pairs: the
+ * odd chunk of a pair takes its inter-chunk term from the even chunk's state
+ * S, as e^{b_L} S plus the decayed sum of the even chunk's k v^T, which is
+ * the state-pass recurrence itself; that halves the states the forward
+ * writes and reads.  The pages fix no chunk length; this is the library's
+ * choice per shape and device (128-column states and enough pairs to fill
+ * every CU twice). */
+int ssd_fwd_state_stride(const ssd_shape *shape);
+
 /* Static description of a status code (never NULL). */
 const char *ssd_strerror(int status);
 
@@ -190,9 +203,13 @@ int ssd_chunk_size(void);
  * but the workspace must already hold what ssd_fwd wrote for the SAME inputs
  * (q, k, v, log_alpha, h0 and shape) into a workspace of at least
  * ssd_bwd_workspace_size(shape) bytes: the forward's regions (the decay
- * weights and the state entering every chunk) sit at the same offsets in the
- * forward and backward layouts.  Only the reverse state pass and the gradient kernel run, which
- * skips recomputing the forward states.  This is the residual-keeping side
+ * weights and the chunk states) sit at the same offsets in the forward and
+ * backward layouts.  When ssd_fwd left the state of every chunk
+ * (ssd_fwd_state_stride 1), only the reverse state pass and the gradient
+ * kernel run, which skips recomputing the forward states; when it left
+ * every even chunk's (stride 2), the forward state pass runs again beside
+ * the reverse one and stores only the odd chunks' states, and the decay
+ * weights are reused.  This is the residual-keeping side
  * of the trade-off that kernel_ssd_gpu.json records in residual_mb (0.0 for
  * the stateless chunked backward; 8 to 128 MiB for its pallas variant in
  * the g2h8_d128 fwd_bwd records); ssd_bwd stays the stateless path.  The

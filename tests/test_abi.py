@@ -171,6 +171,27 @@ def test_workspace_layout_segmented_scan():
     assert _scan_segments(1, 1, 8192, 128, 128, 1) == 16 and _scan_segments(1, 1, 8192, 128, 128, 2) == 8
 
 
+@pytest.mark.parametrize("B,G,H,T,dk,dv,stride", [
+    (4, 2, 8, 8192, 128, 128, 2),   # 512 pairs of chunks: two per CU
+    (4, 2, 8, 8190, 97, 100, 2),    # dv pads to 128, ragged T
+    (4, 2, 8, 2048, 128, 128, 1),   # 128 pairs: fewer than two per CU
+    (2, 1, 24, 8192, 128, 64, 1),   # 64-column states
+    (1, 1, 4, 65536, 128, 128, 2),
+    (1, 1, 1, 1, 1, 1, 1),
+])
+def test_forward_state_stride(B, G, H, T, dk, dv, stride):
+    """The forward runs on chunk pairs (states of even chunks only) for
+    128-column states with at least two pairs per CU (256 CUs when no device
+    is visible)."""
+    assert ssd.fwd_state_stride(ssd.ShapeArg(B, G, H, T, dk, dv)) == stride
+
+
+def test_forward_state_stride_refuses_other_shapes():
+    lib = ssd.library()
+    for s in (ssd.ShapeArg(1, 3, 4, 10, 8, 8), ssd.ShapeArg(1, 1, 1, 100, 8, 200)):
+        assert lib.ssd_fwd_state_stride(ctypes.byref(s)) == -1
+
+
 def test_status_strings_and_constants():
     lib = ssd.library()
     for code in range(7):

@@ -73,8 +73,8 @@ __global__ __launch_bounds__(NTS) void k_state_scan(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
     const float *__restrict__ dy, const float *__restrict__ h0, const float *__restrict__ wts,
     const float *__restrict__ cdec, float *__restrict__ states, float *__restrict__ dstates, float *__restrict__ dh0,
-    float *__restrict__ ends, float *__restrict__ segd, int G, int H, int64_t T, int dk, int dv, int64_t NC,
-    int64_t Epad, int64_t per_dir, int dir0, int nseg, int64_t seg_len, int spar)
+    float *__restrict__ ends, int G, int H, int64_t T, int dk, int dv, int64_t NC, int64_t Epad, int64_t per_dir,
+    int dir0, int nseg, int64_t seg_len, int spar)
 {
     static_assert(TJ <= DVP && DVP % TJ == 0 && (TJ == 32 || TJ == 64 || TJ == 128), "tile width");
     if constexpr (EXD) {   // dk == DKP, dv == DVP: index arithmetic on constants
@@ -243,12 +243,6 @@ __global__ __launch_bounds__(NTS) void k_state_scan(
             asm volatile("" : "+v"(acc[u]));
         }
     }
-    // With segments, one wave per (direction, segment, b h) records the
-    // product of the decays from the segment's start up to each of its
-    // chunks, segd[dl][bh][chunk in scan order], for the fix-up passes.
-    const bool rec = nseg > 1 && tile == 0 && wave == 0;
-    const rsrc_t dr = make_rsrc(segd + (dl * BHn + bh) * NC + n0, rec ? nch * 4 : 0);
-    float run = 1.f;
     for (int64_t s = 0; s < NS; ++s) {
         const int buf = (int)(s & 1);
         block_sync();   // step s staged in half `buf`
@@ -286,10 +280,6 @@ __global__ __launch_bounds__(NTS) void k_state_scan(
             const float decay = dec[cc];
             // slab[c] = S (state entering the chunk in this direction); no-op chunks store nothing
             const int64_t n = s * CPS + cc;
-            if (rec) {
-                gstore1(dr, lane == 0 ? (uint32_t)n * 4u : kOOB, run);
-                run *= decay;
-            }
             // spar 1 (2): the forward direction stores the states of even (odd) chunks only
             const bool live = n < nch && (spar == 0 || dir != 0 || (int)((n0 + n) & 1) == spar - 1);
             const rsrc_t dst =
@@ -346,34 +336,66 @@ __global__ __launch_bounds__(NTS) void k_state_scan(
 // sequence (scan order) was scanned from a zero state, the first from the
 // true initial state, and ends[dl][p][bh] holds the state leaving it.  With
 // S_p the true state entering segment p, A_p the decay over segment p and
-// D(n) the decay from the segment's start to chunk n (segd, written by the
-// scan),
+// D(n) the decay from the segment's start to chunk n,
 //     S_1 = ends[0],  S_{p+1} = ends[p] + A_p S_p,   state(n) = local state(n) + D(n) S_p.
-// Pass 1 (one thread per state element of each (direction, b h)) walks the
-// segments in order and overwrites ends[p] with S_{p+1}, so that ends[p - 1]
-// then holds the state entering segment p; for the reverse direction it also
-// writes dh0, the state leaving the last segment.  A_p = D(last chunk of p)
-// times that chunk's decay, the same product in the same order as the scan's.
+// Pass 1, per (direction, b h) and block of state elements: first D and A
+// (the products of the chunk decays within each segment), one wave per
+// segment taking 64 chunks at a time with an inclusive product scan across
+// the lanes (the DPP steps of scan64 with products, and 1 where a step has
+// no source lane) shifted by one lane; the first block of the (direction,
+// b h) writes D to segd for pass 2.  Then one thread per state element walks
+// the segments in order and overwrites ends[p] with S_{p+1}, so that
+// ends[p - 1] holds the state entering segment p; for the reverse direction
+// it also writes dh0, the state leaving the last segment.
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ float dpp_mul(float x)
+{
+    return x * __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(1.f), __float_as_int(x), CTRL, ROWS, 0xf, false));
+}
 constexpr int NTF = 256;
-__global__ __launch_bounds__(NTF) void k_seg_carry(float *__restrict__ ends, const float *__restrict__ segd,
+__global__ __launch_bounds__(NTF) void k_seg_carry(float *__restrict__ ends, float *__restrict__ segd,
                                                    const float *__restrict__ cdec, float *__restrict__ dh0,
                                                    int64_t BH, int64_t NC, int64_t E, int64_t Epad, int nseg,
                                                    int64_t seg_len, int dir0)
 {
-    const int64_t e = (int64_t)blockIdx.x * NTF + threadIdx.x;
-    if (e >= E) return;
+    __shared__ float Ap[kMaxSegs];
     const int64_t dlbh = blockIdx.y, bh = dlbh % BH;
     const int dl = (int)(dlbh / BH), dir = dir0 + dl;
-    float *en = ends + ((int64_t)dl * nseg * BH + bh) * Epad + e;   // en[p BH Epad]: segment p
-    const float *sd = segd + dlbh * NC, *dc = cdec + bh * NC;
+    const float *dc = cdec + bh * NC;
     auto chunk = [&](int64_t n) { return dir == 0 ? n : NC - 1 - n; };
-    auto total = [&](int64_t last) { return sd[last] * dc[chunk(last)]; };   // A of the segment ending at `last`
+    {
+        const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+        float *sd = segd + dlbh * NC;
+        for (int p = wave; p < nseg; p += NTF / 64) {
+            const int64_t n0 = p * seg_len, n1 = (n0 + seg_len) < NC ? (n0 + seg_len) : NC;
+            float carry = 1.f;
+            for (int64_t base = n0; base < n1; base += 64) {
+                const int64_t n = base + lane;
+                float x = n < n1 ? dc[chunk(n)] : 1.f;
+                x = dpp_mul<kRowShr + 1>(x);
+                x = dpp_mul<kRowShr + 2>(x);
+                x = dpp_mul<kRowShr + 4>(x);
+                x = dpp_mul<kRowShr + 8>(x);
+                x = dpp_mul<kRowBcast15, 0xa>(x);
+                x = dpp_mul<kRowBcast31, 0xc>(x);   // lane l: product over lanes 0..l
+                const float ex = __int_as_float(
+                    __builtin_amdgcn_update_dpp(__float_as_int(1.f), __float_as_int(x), kWaveShr1, 0xf, 0xf, false));
+                if (blockIdx.x == 0 && n < n1) sd[n] = carry * ex;
+                carry *= readlane_f(x, 63);
+            }
+            if (lane == 0) Ap[p] = carry;
+        }
+    }
+    __syncthreads();
+    const int64_t e = (int64_t)blockIdx.x * NTF + threadIdx.x;
+    if (e >= E) return;
+    float *en = ends + ((int64_t)dl * nseg * BH + bh) * Epad + e;   // en[p BH Epad]: segment p
     float S = en[0];   // S_1
     for (int p = 1; p < nseg - 1; ++p) {
-        S = en[(int64_t)p * BH * Epad] + total((p + 1) * seg_len - 1) * S;
+        S = en[(int64_t)p * BH * Epad] + Ap[p] * S;
         en[(int64_t)p * BH * Epad] = S;   // S_{p+1}
     }
-    if (dir == 1) dh0[bh * E + e] = en[(int64_t)(nseg - 1) * BH * Epad] + total(NC - 1) * S;
+    if (dir == 1) dh0[bh * E + e] = en[(int64_t)(nseg - 1) * BH * Epad] + Ap[nseg - 1] * S;
 }
 
 // Pass 2: one thread per 4 consecutive state elements of each chunk of
@@ -439,12 +461,12 @@ int run_scan(const Problem &P, int dirs, bool prep, StoreSet store, const float 
             const dim3 grid((unsigned)(ndir * per_dir)), blk(NTS);
             if (pair)
                 launch(P.timer, kid, k_state_scan<KP, VP, VE, TJ, 2, EXD>, grid, blk, st, q, k, v, dy, h0, P.wts, P.cdec,
-                       P.states, P.dstates, dh0, P.ends, P.segd, (int)s.G, (int)s.H, s.T, (int)s.dk, (int)s.dv,
-                       P.L.NC, P.L.Epad, per_dir, dir0, plan.nseg, plan.seg_len, spar);
+                       P.states, P.dstates, dh0, P.ends, (int)s.G, (int)s.H, s.T, (int)s.dk, (int)s.dv, P.L.NC,
+                       P.L.Epad, per_dir, dir0, plan.nseg, plan.seg_len, spar);
             else
                 launch(P.timer, kid, k_state_scan<KP, VP, VE, TJ, 1, EXD>, grid, blk, st, q, k, v, dy, h0, P.wts, P.cdec,
-                       P.states, P.dstates, dh0, P.ends, P.segd, (int)s.G, (int)s.H, s.T, (int)s.dk, (int)s.dv,
-                       P.L.NC, P.L.Epad, per_dir, dir0, plan.nseg, plan.seg_len, spar);
+                       P.states, P.dstates, dh0, P.ends, (int)s.G, (int)s.H, s.T, (int)s.dk, (int)s.dv, P.L.NC,
+                       P.L.Epad, per_dir, dir0, plan.nseg, plan.seg_len, spar);
         }));
     };
     if (narrow) run(BoolC<true>{});
@@ -454,7 +476,7 @@ int run_scan(const Problem &P, int dirs, bool prep, StoreSet store, const float 
         if (launch_status() != SSD_OK) return SSD_ERR_DEVICE;
         const int64_t E = s.dk * s.dv;
         launch(P.timer, KID_AUX, k_seg_carry, dim3((unsigned)((E + NTF - 1) / NTF), (unsigned)(ndir * BH)), dim3(NTF),
-               st, P.ends, (const float *)P.segd, (const float *)P.cdec, dh0, BH, P.L.NC, E, P.L.Epad, plan.nseg,
+               st, P.ends, P.segd, (const float *)P.cdec, dh0, BH, P.L.NC, E, P.L.Epad, plan.nseg,
                plan.seg_len, dir0);
         if (launch_status() != SSD_OK) return SSD_ERR_DEVICE;
         const int64_t nfix = P.L.NC - plan.seg_len;   // chunks of segments 1 ..

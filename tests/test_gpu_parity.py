@@ -177,6 +177,39 @@ def test_workload_full_size(idx):
     check_bwd(x)
 
 
+# Shapes whose forward runs on chunk pairs (128-column states, at least two
+# pairs per CU on a 256-CU device): an odd chunk count with a ragged tail,
+# padded dk and dv (16-byte and 4-byte addressing), dk = 32, eight heads.
+PAIRS = [Shape(2, 2, 4, 32700, 128, 128), Shape(1, 2, 4, 32805, 100, 96), Shape(1, 2, 2, 32768, 32, 97),
+         Shape(1, 1, 8, 65536, 64, 128)]
+
+
+@pytest.mark.parametrize("shape", PAIRS, ids=_id)
+def test_chunk_pair_forward(shape):
+    """The forward on chunk pairs against the oracle, whole tensor, and the
+    backward that reuses its workspace (which then forms the odd chunks'
+    states) against the oracle and the stateless backward."""
+    need_gpu()
+    import torch
+    import chunked_ssd_scan_fwd_amd as ssd
+    sa = ssd.ShapeArg(shape.B, shape.G, shape.H, shape.T, shape.dk, shape.dv)
+    if ssd.fwd_state_stride(sa) != 2:
+        pytest.skip("this device's compute-unit count does not put the shape on chunk pairs")
+    say(f"chunk pairs {_id(shape)}")
+    x = make_inputs(shape, seed=11 + shape.dv)
+    d = to_dev(x)
+    ws = torch.empty(ssd.workspace_size(sa, True), dtype=torch.uint8, device="cuda")
+    y = ssd.fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["h0"], workspace=ws)
+    assert rel_err(host(y), oracle.fwd(x["q"], x["k"], x["v"], x["log_alpha"], x["h0"])) <= TOL_Y
+    g = ssd.bwd_from_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["h0"], d["dy"], workspace=ws)
+    g0 = ssd.bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["h0"], d["dy"])
+    ref = oracle.bwd(x["q"], x["k"], x["v"], x["log_alpha"], x["h0"], x["dy"])
+    for t, t0, name in zip(g, g0, GRADS):
+        a = host(t)
+        assert rel_err(a, ref[name]) <= TOL_G, name
+        assert rel_err(a, host(t0)) <= 1e-6, name
+
+
 @pytest.mark.parametrize("T", [65536, 131072])
 def test_long_sequence_unit(T):
     """One independent unit at the headline's head and state sizes (B=1, G=1,

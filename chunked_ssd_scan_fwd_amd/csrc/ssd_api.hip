@@ -106,10 +106,24 @@ static void *static_ws_ptr()
     return addr;
 }
 
-static int prepare(const ssd_shape *shape, bool backward, void *ws, size_t ws_bytes, ssd_timer *tm, Problem *P)
+// `fwd_states`: the forward's state layout matters to this call (a forward,
+// or a backward that reuses what the forward stored).
+static int prepare(const ssd_shape *shape, bool backward, bool fwd_states, void *ws, size_t ws_bytes,
+                   ssd_timer *tm, Problem *P)
 {
     P->s = *shape;
     P->cus = device_cus();
+    // Chunk pairs where they measured faster: full 128-column states (the
+    // pair kernel's P is formed once per two steps) and at least two pair
+    // units per CU (its larger set-up, Q K^T over 128 positions, is then
+    // loaded under the previous unit's MFMAs).  g2h8_d128 T8192: forward
+    // 279 -> 257 us; at one unit per CU (T2048) or dv = 64 it was slower.
+    // SSD_FWD_CHUNK overrides the choice.
+    P->pair = false;
+    if (fwd_states) {
+        const int rc = fwd_pair_mode(shape, P->cus, &P->pair);
+        if (rc != SSD_OK) return rc;
+    }
     P->L = make_layout(shape, backward, P->cus);
     if (ws_bytes < P->L.off[SSD_WS_REGIONS]) return SSD_ERR_WORKSPACE;
     if (P->L.off[SSD_WS_REGIONS] > 0) {
@@ -120,12 +134,6 @@ static int prepare(const ssd_shape *shape, bool backward, void *ws, size_t ws_by
     P->DVP = pad_dim(shape->dv);
     P->vec = (shape->dk % 4) == 0 && (shape->dv % 4) == 0;
     P->exact = shape->dk == P->DKP && shape->dv == P->DVP;
-    // Chunk pairs where they measured faster: full 128-column states (the
-    // pair kernel's P is formed once per two steps) and at least two pair
-    // units per CU (its larger set-up, Q K^T over 128 positions, is then
-    // loaded under the previous unit's MFMAs).  g2h8_d128 T8192: forward
-    // 279 -> 257 us; at one unit per CU (T2048) or dv = 64 it was slower.
-    P->pair = fwd_pairs(shape, P->cus);
     char *w = static_cast<char *>(ws);
     P->wts = reinterpret_cast<float *>(w + P->L.off[0]);
     P->cdec = reinterpret_cast<float *>(w + P->L.cdec_off);
@@ -156,9 +164,11 @@ static int fwd_impl(const ssd_shape *shape, const float *q, const float *k, cons
         !aligned16(y))
         return SSD_ERR_ALIGN;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    rc = fwd_chunk_check(shape);
+    if (rc != SSD_OK) return rc;
     if (needs_split(shape)) return fwd_split(s, q, k, v, log_alpha, h0, y, workspace, workspace_bytes, st, tm);
     Problem P;
-    rc = prepare(shape, false, workspace, workspace_bytes, tm, &P);
+    rc = prepare(shape, false, true, workspace, workspace_bytes, tm, &P);
     if (rc != SSD_OK) return rc;
     rc = run_scan(P, 1, true, P.pair ? kStoreEven : kStoreAll, q, k, v, nullptr, log_alpha, h0, nullptr, st);
     if (rc != SSD_OK) return rc;
@@ -196,7 +206,7 @@ static int bwd_impl(const ssd_shape *shape, const float *q, const float *k, cons
         return bwd_split(s, q, k, v, log_alpha, h0, dy, dq, dk, dv, dlog_alpha, dh0, workspace, workspace_bytes, st,
                          tm);
     Problem P;
-    rc = prepare(shape, true, workspace, workspace_bytes, tm, &P);
+    rc = prepare(shape, true, reuse, workspace, workspace_bytes, tm, &P);
     if (rc != SSD_OK) return rc;
     // dS_out (reverse) of every chunk and dh0; without reuse also the decay
     // weights and S_in (forward), the latter in the same launch.  A forward

@@ -55,11 +55,27 @@ struct ScanPlan {
 };
 ScanPlan scan_plan(const ssd_shape *s, int ndir, int cus);
 
-// Whether the forward of a direct (dk, dv <= 128) shape runs on chunk pairs:
-// full 128-column states (pad(dv) = 128) and at least two pair units
-// (b, g, pair of chunks) per CU.  Its state scan then stores the states of
-// even chunks only.
+// Whether the forward of a direct (dk, dv <= 128) shape runs on chunk pairs
+// by the library's own choice: full 128-column states (pad(dv) = 128) and at
+// least two pair units (b, g, pair of chunks) per CU.  Its state scan then
+// stores the states of even chunks only.
 bool fwd_pairs(const ssd_shape *s, int cus);
+
+// The forward's chunk length as the environment variable SSD_FWD_CHUNK sets
+// it, read at each call: 0 when unset or empty (the library chooses per
+// shape), 64, 128, or -1 for any other value.
+int fwd_chunk_setting();
+
+// Whether the forward of a direct shape runs on chunk pairs under that
+// setting (SSD_OK and *pair), or SSD_ERR_UNSUPPORTED for an invalid setting
+// or for 128 where the pair kernel does not take the shape (pad(dv) must be
+// 64 or 128).
+int fwd_pair_mode(const ssd_shape *s, int cus, bool *pair);
+
+// The same check for a whole forward, direct or cut into column blocks
+// (every dv block must suit the pair kernel under 128), made before anything
+// is enqueued.
+int fwd_chunk_check(const ssd_shape *s);
 
 // Heads per block and number of splits for a shape on a device with `cus`
 // compute units (see Layout).

@@ -1,6 +1,9 @@
 // Host-only argument checks and workspace layout for the SSD scan C ABI.
 // This unit makes no HIP call (the device's compute-unit count comes from
 // device_cus() in the HIP unit).
+#include <cstdlib>
+#include <cstring>
+
 #include "ssd_internal.h"
 
 namespace ssd {
@@ -45,6 +48,36 @@ bool fwd_pairs(const ssd_shape *s, int cus)
 {
     const int64_t NC = (s->T + kChunk - 1) / kChunk;
     return pad_dim(s->dv) == 128 && s->B * s->G * ((NC + 1) / 2) >= 2 * int64_t(cus);
+}
+
+int fwd_chunk_setting()
+{
+    const char *e = std::getenv("SSD_FWD_CHUNK");
+    if (!e || !*e) return 0;
+    if (!std::strcmp(e, "64")) return 64;
+    if (!std::strcmp(e, "128")) return 128;
+    return -1;
+}
+
+// The pair kernel is built for 64- and 128-column states.
+static bool pair_cols(int64_t dv) { return pad_dim(dv) >= 64; }
+
+int fwd_pair_mode(const ssd_shape *s, int cus, bool *pair)
+{
+    const int c = fwd_chunk_setting();
+    if (c < 0 || (c == 128 && !pair_cols(s->dv))) return SSD_ERR_UNSUPPORTED;
+    *pair = c == 0 ? fwd_pairs(s, cus) : c == 128;
+    return SSD_OK;
+}
+
+int fwd_chunk_check(const ssd_shape *s)
+{
+    const int c = fwd_chunk_setting();
+    if (c < 0) return SSD_ERR_UNSUPPORTED;
+    if (c != 128) return SSD_OK;
+    // dv blocks: dv itself, or kMaxDim and the rest
+    if (s->dv <= kMaxDim) return pair_cols(s->dv) ? SSD_OK : SSD_ERR_UNSUPPORTED;
+    return pair_cols(s->dv - kMaxDim) ? SSD_OK : SSD_ERR_UNSUPPORTED;
 }
 
 ScanPlan scan_plan(const ssd_shape *s, int ndir, int cus)
@@ -206,7 +239,9 @@ int ssd_workspace_layout(const ssd_shape *shape, int backward, size_t offsets[SS
 int ssd_fwd_state_stride(const ssd_shape *shape)
 {
     if (ssd::check_shape(shape) != SSD_OK || ssd::needs_split(shape)) return -1;
-    return ssd::fwd_pairs(shape, ssd::device_cus()) ? 2 : 1;
+    bool pair = false;
+    if (ssd::fwd_pair_mode(shape, ssd::device_cus(), &pair) != SSD_OK) return -1;
+    return pair ? 2 : 1;
 }
 
 const char *ssd_strerror(int status)
@@ -215,7 +250,8 @@ const char *ssd_strerror(int status)
     case SSD_OK: return "success";
     case SSD_ERR_NULL: return "a required pointer is NULL";
     case SSD_ERR_SHAPE: return "invalid shape (negative size, G < 1, H not a multiple of G, or too large)";
-    case SSD_ERR_UNSUPPORTED: return "unsupported shape (dk and dv must be in 1..256)";
+    case SSD_ERR_UNSUPPORTED:
+        return "unsupported shape (dk and dv must be in 1..256) or SSD_FWD_CHUNK setting (unset, 64 or 128)";
     case SSD_ERR_WORKSPACE: return "workspace smaller than the size query requires";
     case SSD_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case SSD_ERR_DEVICE: return "HIP launch or runtime error";

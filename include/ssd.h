@@ -90,7 +90,8 @@ enum ssd_status {
     SSD_OK = 0,
     SSD_ERR_NULL = 1,        /* a required pointer is NULL                       */
     SSD_ERR_SHAPE = 2,       /* negative size, G < 1, H % G != 0, size overflow   */
-    SSD_ERR_UNSUPPORTED = 3, /* valid shape outside the supported dk/dv range     */
+    SSD_ERR_UNSUPPORTED = 3, /* valid shape outside the supported dk/dv range,
+                                 or an SSD_FWD_CHUNK the forward cannot take */
     SSD_ERR_WORKSPACE = 4,   /* workspace smaller than the size query's answer    */
     SSD_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned                  */
     SSD_ERR_DEVICE = 6       /* a HIP launch or runtime call failed               */
@@ -182,14 +183,29 @@ int ssd_fwd_noalloc(const ssd_shape *shape,
 int ssd_workspace_layout(const ssd_shape *shape, int backward, size_t offsets[SSD_WS_REGIONS + 1]);
 
 /* Test support: 1 if ssd_fwd leaves the state of every chunk in the
- * workspace, 2 if only that of every even chunk (-1 for an invalid shape or
- * one with dk or dv above 128).  With 2 the forward runs on chunk pairs: the
- * odd chunk of a pair takes its inter-chunk term from the even chunk's state
- * S, as e^{b_L} S plus the decayed sum of the even chunk's k v^T, which is
- * the state-pass recurrence itself; that halves the states the forward
- * writes and reads.  The pages fix no chunk length; this is the library's
- * choice per shape and device (128-column states and enough pairs to fill
- * every CU twice). */
+ * workspace, 2 if only that of every even chunk (-1 for an invalid shape,
+ * one with dk or dv above 128, or an SSD_FWD_CHUNK that ssd_fwd would
+ * refuse).  With 2 the forward runs on chunk pairs: the odd chunk of a pair
+ * takes its inter-chunk term from the even chunk's state S, as e^{b_L} S
+ * plus the decayed sum of the even chunk's k v^T, which is the state-pass
+ * recurrence itself; that halves the states the forward writes and reads.
+ * In effect the forward's chunk is then 128 steps, its intra-chunk product
+ * taken as four 64 x 64 blocks.  The pages fix no chunk length (the chunked
+ * method's result does not depend on it beyond rounding).  The library
+ * chooses per shape and device (128-column states and enough pairs to fill
+ * every CU twice) unless the environment variable SSD_FWD_CHUNK, read at
+ * each call of ssd_fwd, ssd_fwd_noalloc, ssd_bwd_from_fwd and this
+ * function, fixes it:
+ *     unset or empty   the library's choice
+ *     "64"             every chunk's state (stride 1)
+ *     "128"            chunk pairs (stride 2); a forward whose dv (or, above
+ *                      128, each 128-column block of dv) is 32 or less
+ *                      returns SSD_ERR_UNSUPPORTED
+ *     anything else    ssd_fwd, ssd_fwd_noalloc and ssd_bwd_from_fwd return
+ *                      SSD_ERR_UNSUPPORTED
+ * It exists for the chunk-length invariance tests.  ssd_bwd_from_fwd must
+ * see the same setting as the ssd_fwd whose workspace it reuses; ssd_bwd
+ * ignores it (its chunk is 64). */
 int ssd_fwd_state_stride(const ssd_shape *shape);
 
 /* Static description of a status code (never NULL). */

@@ -179,11 +179,65 @@ def test_workspace_layout_segmented_scan():
     (1, 1, 4, 65536, 128, 128, 2),
     (1, 1, 1, 1, 1, 1, 1),
 ])
-def test_forward_state_stride(B, G, H, T, dk, dv, stride):
+def test_forward_state_stride(B, G, H, T, dk, dv, stride, monkeypatch):
     """The forward runs on chunk pairs (states of even chunks only) for
     128-column states with at least two pairs per CU (256 CUs when no device
     is visible)."""
+    monkeypatch.delenv("SSD_FWD_CHUNK", raising=False)
     assert ssd.fwd_state_stride(ssd.ShapeArg(B, G, H, T, dk, dv)) == stride
+    monkeypatch.setenv("SSD_FWD_CHUNK", "")
+    assert ssd.fwd_state_stride(ssd.ShapeArg(B, G, H, T, dk, dv)) == stride
+
+
+# shape: state stride under SSD_FWD_CHUNK = 64 and = 128 (-1: refused, the
+# pair kernel takes 64- and 128-column states only)
+FWD_CHUNK_STRIDES = {
+    (4, 2, 8, 8192, 128, 128): (1, 2),
+    (4, 2, 8, 2048, 128, 128): (1, 2),
+    (2, 1, 24, 8192, 128, 64): (1, 2),
+    (2, 2, 4, 300, 48, 40): (1, 2),
+    (1, 1, 1, 1, 1, 1): (1, -1),
+    (3, 1, 2, 129, 33, 32): (1, -1),
+}
+
+
+def test_forward_chunk_setting(monkeypatch):
+    """SSD_FWD_CHUNK fixes the forward's chunk length: 64 keeps every chunk's
+    state, 128 runs on chunk pairs wherever the pair kernel takes the shape."""
+    lib = ssd.library()
+    for i, val in enumerate(("64", "128")):
+        monkeypatch.setenv("SSD_FWD_CHUNK", val)
+        for sh, strides in FWD_CHUNK_STRIDES.items():
+            assert lib.ssd_fwd_state_stride(ctypes.byref(ssd.ShapeArg(*sh))) == strides[i], (val, sh)
+
+
+@pytest.mark.parametrize("val", ["96", "abc", "64 ", "0", "256"])
+def test_forward_chunk_setting_refused(val, monkeypatch):
+    """Values other than 64 and 128 are refused by every call that the
+    forward's chunk length concerns, before anything is enqueued (the
+    workspace passed is one byte short, so a call that went on would stop at
+    the workspace check instead)."""
+    monkeypatch.setenv("SSD_FWD_CHUNK", val)
+    s = ssd.ShapeArg(1, 1, 2, 100, 64, 64)
+    assert ssd.library().ssd_fwd_state_stride(ctypes.byref(s)) == -1
+    assert _call_fwd(s, ptr=0x1000, ws_bytes=ssd.workspace_size(s, False) - 1) == 3
+    assert _call_bwd(s, ptr=0x1000, ws_bytes=ssd.workspace_size(s, True) - 1, fn="ssd_bwd_from_fwd") == 3
+    # the stateless backward does not depend on it
+    assert _call_bwd(s, ptr=0x1000, ws_bytes=ssd.workspace_size(s, True) - 1) == 4
+
+
+def test_forward_chunk_128_refused_where_pairs_do_not_fit(monkeypatch):
+    """128 on a forward whose dv (or a 128-column block of it) pads to 32:
+    refused before anything is enqueued, also for the column-split path,
+    which would otherwise enqueue its block copies first."""
+    monkeypatch.setenv("SSD_FWD_CHUNK", "128")
+    for sh in ((1, 1, 1, 10, 8, 8), (1, 1, 1, 10, 8, 144), (1, 1, 1, 10, 200, 20)):
+        s = ssd.ShapeArg(*sh)
+        assert _call_fwd(s, ptr=0x1000, ws_bytes=ssd.workspace_size(s, False) - 1) == 3, sh
+    # a split shape whose dv blocks both suit the pair kernel passes the check
+    # and stops at the workspace
+    s = ssd.ShapeArg(1, 1, 1, 10, 8, 200)
+    assert _call_fwd(s, ptr=0x1000, ws_bytes=ssd.workspace_size(s, False) - 1) == 4
 
 
 def test_forward_state_stride_refuses_other_shapes():

@@ -210,6 +210,48 @@ def test_chunk_pair_forward(shape):
         assert rel_err(a, host(t0)) <= 1e-6, name
 
 
+# The forward at chunk 64 and at chunk 128 (SSD_FWD_CHUNK) on the same
+# inputs: 64-column states, one chunk (a pair without its odd chunk), padded
+# dk and dv with 16- and 4-byte addressing and an odd chunk count, a group's
+# heads split over blocks (fewer pair units than CUs), and a scan in chunk
+# segments.
+CHUNK_LENGTHS = [Shape(2, 2, 4, 300, 48, 40), Shape(1, 1, 3, 65, 128, 64), Shape(2, 2, 4, 63, 128, 128),
+                 Shape(1, 2, 4, 1000, 100, 96), Shape(3, 1, 2, 129, 33, 97), Shape(1, 1, 7, 4096, 64, 64),
+                 Shape(1, 1, 2, 16384, 128, 128)]
+
+
+@pytest.mark.parametrize("shape", CHUNK_LENGTHS, ids=_id)
+def test_forward_chunk_length_invariance(shape, monkeypatch):
+    """The chunked method's result does not depend on its chunk length beyond
+    rounding: the forward at chunk 64 and at chunk 128 (chunk pairs) agree
+    with the oracle and with each other, and the backward that reuses each
+    forward's workspace agrees with the oracle and the stateless backward."""
+    need_gpu()
+    import torch
+    import chunked_ssd_scan_fwd_amd as ssd
+    x = make_inputs(shape, seed=23 + shape.T)
+    d = to_dev(x)
+    sa = ssd.ShapeArg(shape.B, shape.G, shape.H, shape.T, shape.dk, shape.dv)
+    ref_y = oracle.fwd(x["q"], x["k"], x["v"], x["log_alpha"], x["h0"])
+    ref = oracle.bwd(x["q"], x["k"], x["v"], x["log_alpha"], x["h0"], x["dy"])
+    say(f"chunk lengths {_id(shape)}: stateless backward")
+    g0 = [host(t) for t in ssd.bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["h0"], d["dy"])]
+    ys = {}
+    for val, stride in (("64", 1), ("128", 2)):
+        monkeypatch.setenv("SSD_FWD_CHUNK", val)
+        say(f"chunk lengths {_id(shape)}: forward chunk {val}")
+        assert ssd.fwd_state_stride(sa) == stride
+        ws = torch.empty(ssd.workspace_size(sa, True), dtype=torch.uint8, device="cuda")
+        ys[val] = host(ssd.fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["h0"], workspace=ws))
+        assert rel_err(ys[val], ref_y) <= TOL_Y, val
+        g = ssd.bwd_from_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["h0"], d["dy"], workspace=ws)
+        for t, t0, name in zip(g, g0, GRADS):
+            a = host(t)
+            assert rel_err(a, ref[name]) <= TOL_G, (val, name)
+            assert rel_err(a, t0) <= 1e-6, (val, name)
+    assert rel_err(ys["128"], ys["64"]) <= 5e-6
+
+
 @pytest.mark.parametrize("T", [65536, 131072])
 def test_long_sequence_unit(T):
     """One independent unit at the headline's head and state sizes (B=1, G=1,

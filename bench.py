@@ -220,7 +220,8 @@ def grid_sweep(args, torch, ssd):
 
         f_fwd, f_bwd = nominal_flops(s)
         b_fwd, b_fb = io_bytes(s)
-        out = {"workload": f"{name}_T{T}", "shape": {"B": s.B, "G": s.G, "H": s.H, "T": s.T, "dk": s.dk, "dv": s.dv}}
+        out = {"workload": f"{name}_T{T}", "shape": {"B": s.B, "G": s.G, "H": s.H, "T": s.T, "dk": s.dk, "dv": s.dv},
+               "fwd_chunk": 64 * ssd.fwd_state_stride(sa)}
         for key, fn, fl, by in (("fwd", fwd, f_fwd, b_fwd), ("fwd_bwd", step, f_fwd + f_bwd, b_fb)):
             for _ in range(args.warmup):
                 fn()
@@ -617,7 +618,9 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": f"{w.name}: B={s.B} G={s.G} H={s.H} T={s.T} dk={s.dk} dv={s.dv}, "
-                               "step = ssd_fwd + ssd_bwd", "chunk": 64, "seed": w.seed},
+                               "step = ssd_fwd + ssd_bwd",
+                   # the forward's chunk length (128: on chunk pairs) and the backward's
+                   "chunk": {"fwd": 64 * ssd.fwd_state_stride(sa), "bwd": 64}, "seed": w.seed},
         "roofline": roof,
         "cpu_baseline": cpu,
         "fwd_bwd": {**quartiles(per_step), "tflops": value, "roofline_frac": t_roof_fb / (step_ms * 1e-3),

@@ -433,6 +433,57 @@ def test_bwd_from_fwd_needs_workspace():
         ssd.bwd_from_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["h0"], d["dy"], workspace=None)
 
 
+def _random_cases(n, seed):
+    """Seeded random shapes (dims up to 256, T up to 6000, some group sizes
+    and head counts) with a forward chunk setting each: unset, 64, or 128
+    where the pair kernel takes dv (dv > 32, or above 128 a second block of
+    more than 32 columns)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        G = int(rng.integers(1, 4))
+        H = G * int(rng.integers(1, 6))
+        B = int(rng.integers(1, 4))
+        T = int(rng.integers(1, 200)) if rng.random() < 0.4 else int(rng.integers(200, 6000))
+        dk = int(rng.integers(1, 129)) if rng.random() < 0.8 else int(rng.integers(129, 257))
+        dv = int(rng.integers(1, 129)) if rng.random() < 0.8 else int(rng.integers(129, 257))
+        if B * H * T * dk * dv > 4e8:
+            continue
+        chunk = ("", "64", "128")[len(out) % 3]
+        if chunk == "128" and not (dv > 32 if dv <= 128 else dv - 128 > 32):
+            chunk = ""
+        out.append((Shape(B, G, H, T, dk, dv), chunk))
+    return out
+
+
+RANDOM_CASES = _random_cases(24, 2024)
+
+
+@pytest.mark.parametrize("case", RANDOM_CASES, ids=lambda c: f"{_id(c[0])}_chunk{c[1] or 'auto'}")
+def test_random_shapes(case, monkeypatch):
+    """A seeded sweep over shapes and forward chunk settings: the forward,
+    the stateless backward and the backward that reuses the forward's
+    workspace, each against the oracle on whole tensors."""
+    need_gpu()
+    import torch
+    import chunked_ssd_scan_fwd_amd as ssd
+    shape, chunk = case
+    monkeypatch.setenv("SSD_FWD_CHUNK", chunk)
+    say(f"random {_id(shape)} chunk {chunk or 'auto'}")
+    x = make_inputs(shape, seed=shape.T + 7 * shape.dk + 11 * shape.dv)
+    d = to_dev(x)
+    sa = ssd.ShapeArg(shape.B, shape.G, shape.H, shape.T, shape.dk, shape.dv)
+    ws = torch.empty(max(1, ssd.workspace_size(sa, True)), dtype=torch.uint8, device="cuda")
+    y = host(ssd.fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["h0"], workspace=ws))
+    assert rel_err(y, oracle.fwd(x["q"], x["k"], x["v"], x["log_alpha"], x["h0"])) <= TOL_Y
+    ref = oracle.bwd(x["q"], x["k"], x["v"], x["log_alpha"], x["h0"], x["dy"])
+    g = ssd.bwd_from_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["h0"], d["dy"], workspace=ws)
+    g0 = ssd.bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["h0"], d["dy"])
+    for t, t0, name in zip(g, g0, GRADS):
+        assert rel_err(host(t0), ref[name]) <= TOL_G, name
+        assert rel_err(host(t), ref[name]) <= TOL_G, name
+
+
 def test_empty_shapes():
     need_gpu()
     import torch

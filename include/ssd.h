@@ -194,8 +194,9 @@ int ssd_workspace_layout(const ssd_shape *shape, int backward, size_t offsets[SS
  * method's result does not depend on it beyond rounding).  The library
  * chooses per shape and device (128-column states and enough pairs to fill
  * every CU twice) unless the environment variable SSD_FWD_CHUNK, read at
- * each call of ssd_fwd, ssd_fwd_noalloc, ssd_bwd_from_fwd and this
- * function, fixes it:
+ * each call of ssd_fwd, ssd_fwd_timed, ssd_fwd_noalloc, ssd_bwd_from_fwd
+ * and this function (with getenv: do not change it while another thread
+ * is inside one of these calls), fixes it:
  *     unset or empty   the library's choice
  *     "64"             every chunk's state (stride 1)
  *     "128"            chunk pairs (stride 2); a forward whose dv (or, above

@@ -38,6 +38,16 @@ C_NOM = 64
 # The benchmark pages' JAX "chunked" fwd_bwd at this workload on an RTX 3090
 # (kernel_ssd_gpu.json, record chunked·fwd_bwd·g2h8_d128·T8192, median_ms).
 PAGE_FWD_BWD_MS = 11.883384999237023
+# kernel_mamba_cpu.json, results: the CPU medians (ms) of impls scan and
+# chunked, mode fwd, at batch 4, state 16 -- context for --mamba, not a target.
+MAMBA_PAGE_CPU_MS = {
+    (256, 512): {"scan": 17.20, "chunked": 6.40}, (256, 2048): {"scan": 28.61, "chunked": 21.79},
+    (256, 8192): {"scan": 120.3, "chunked": 107.4}, (512, 512): {"scan": 14.21, "chunked": 14.48},
+    (512, 2048): {"scan": 56.86, "chunked": 92.16}, (512, 8192): {"scan": 231.8, "chunked": 205.5},
+    (1024, 512): {"scan": 20.82, "chunked": 16.61}, (1024, 2048): {"scan": 176.1, "chunked": 95.43},
+    (1024, 8192): {"scan": 319.1, "chunked": 298.9},
+}
+
 # The same page's chunked path over its whole grid, (fwd, fwd_bwd) median ms on
 # the RTX 3090: context for --grid, not a target.
 PAGE_CHUNKED_MS = {
@@ -238,6 +248,57 @@ def grid_sweep(args, torch, ssd):
         torch.cuda.empty_cache()
 
 
+# The selective scan's own roofline.  It is no contraction: per element
+# (b, t, d) and state n the recurrence takes one exponential and three
+# single-rate operations (the exponent's product, the input's product, the
+# multiply-add into the state) and the output one more multiply-add.  An
+# exponential issues at a quarter of the fp32 rate, so the work is
+# N (4 + 4) lane slots per element against 256 CUs x 4 SIMDs x 16 lanes x
+# 2.4 GHz; the bytes are the inputs and y.
+PEAK_VALU_SLOTS = 256 * 4 * 16 * 2.4e9
+
+
+def mamba_work(s):
+    elems = s.B * s.L * s.D
+    slots = elems * s.N * 8
+    io = 4 * (3 * elems + 2 * s.B * s.L * s.N + s.D * s.N + s.D)
+    return slots, io
+
+
+def mamba_sweep(args, torch, ssd, points=None):
+    """mamba_fwd at the points of kernel_mamba_cpu.json's grid (batch 4, state
+    16), timed by the pages' protocol; the page's CPU medians go along as
+    context."""
+    from ssd_workload.mamba import MAMBA_GRID, make_mamba_inputs
+    out = []
+    for (D, L), s in MAMBA_GRID.items():
+        if points is not None and (D, L) not in points:
+            continue
+        inp = make_mamba_inputs(s, 3000 + D + L)
+        d = {k: torch.from_numpy(v).to("cuda") for k, v in inp.items()}
+        sa = ssd.MambaShapeArg(s.B, s.L, s.D, s.N)
+        ws = torch.empty(max(1, ssd.mamba_workspace_size(sa)), dtype=torch.uint8, device="cuda")
+        y = torch.empty((s.B, s.L, s.D), device="cuda")
+
+        def fwd():
+            ssd.mamba_fwd(d["x"], d["delta"], d["A"], d["B"], d["C"], d["Dskip"], out=y, workspace=ws)
+
+        for _ in range(args.warmup):
+            fwd()
+        r = protocol_ms(torch, fwd, repeats=args.repeats)
+        t = r["median_ms"] * 1e-3
+        slots, io = mamba_work(s)
+        out.append({"workload": f"mamba_d{D}_L{L}", "shape": {"B": s.B, "L": s.L, "D": s.D, "N": s.N},
+                    "fwd": {"median_ms": r["median_ms"], "q1_ms": r["q1_ms"], "q3_ms": r["q3_ms"],
+                            "gbps_io": io / t / 1e9, "hbm_frac": io / t / PEAK_HBM,
+                            "alu_frac": slots / t / PEAK_VALU_SLOTS,
+                            "roofline_frac": max(io / PEAK_HBM, slots / PEAK_VALU_SLOTS) / t},
+                    "page_cpu_ms": MAMBA_PAGE_CPU_MS.get((D, L)), "dtype": "f32", "data": "synthetic"})
+        del d, ws, y
+        torch.cuda.empty_cache()
+    return out
+
+
 def quartiles(vals):
     import numpy as np
     a = np.asarray(vals, dtype=np.float64)
@@ -422,6 +483,9 @@ def main():
     ap.add_argument("--max-len-cap", type=int, default=1 << 22, help="largest T the search tries")
     ap.add_argument("--grid", action="store_true",
                     help="only time fwd and fwd_bwd at every shape of the pages' grid, one JSON line each, and exit")
+    ap.add_argument("--mamba", action="store_true",
+                    help="only time the selective (Mamba-style) scan at every point of its page's grid, one JSON "
+                         "line each, and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -447,6 +511,10 @@ def main():
         return
     if args.max_len:
         max_len_search(args, torch, ssd)
+        return
+    if args.mamba:
+        for line in mamba_sweep(args, torch, ssd):
+            print(json.dumps(line), flush=True)
         return
     if args.grid:
         grid_sweep(args, torch, ssd)
@@ -600,6 +668,8 @@ def main():
                          f"{args.cpu_repeats} runs each (value: nominal fwd_bwd FLOPs / median wall time)"}
 
     configs = None if args.no_configs else config_rows(torch, ssd, args)
+    # the second workload of the pages (kernel_mamba_cpu.json) at its largest point
+    mamba = None if args.no_configs else mamba_sweep(args, torch, ssd, points={(1024, 8192)})
     facts = device_facts(torch)
 
     out = {
@@ -642,6 +712,7 @@ def main():
         "kernels": kernels,
         "parity_rel_err": parity,
         "configs": configs,
+        "mamba": mamba,
         "device_facts": facts,
         "first_call_ms": first_call_ms,
         "memory": {"workspace_bytes_fwd": ssd.workspace_size(sa, False), "workspace_bytes_bwd": ssd.workspace_size(sa, True),

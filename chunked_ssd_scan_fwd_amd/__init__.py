@@ -84,6 +84,11 @@ def library(path: str | None = None):
     lib.ssd_kernel_count.restype = ctypes.c_int
     lib.ssd_kernel_name.argtypes = [ctypes.c_int]
     lib.ssd_kernel_name.restype = ctypes.c_char_p
+    mp = ctypes.POINTER(MambaShapeArg)
+    lib.mamba_fwd_workspace_size.argtypes = [mp]
+    lib.mamba_fwd_workspace_size.restype = sz
+    lib.mamba_fwd.argtypes = [mp] + [vp] * 7 + [vp, sz, vp]
+    lib.mamba_fwd.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -145,8 +150,11 @@ def _workspace(shape, backward, device, workspace):
     """The workspace to pass: a new one, or the caller's after checking that
     it lives on `device` and owns at least the bytes the size query asks for
     (contiguous, counted from its own start to the end of its storage)."""
+    return _workspace_bytes(workspace_size(shape, backward), device, workspace)
+
+
+def _workspace_bytes(need, device, workspace):
     import torch
-    need = workspace_size(shape, backward)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
         return workspace, need
@@ -309,3 +317,41 @@ class KernelTimer:
     def __exit__(self, *exc):
         self.close()
         return False
+
+
+# ---- selective (Mamba-style) scan
+
+
+class MambaShapeArg(ctypes.Structure):
+    """mamba_shape of ssd.h: batch B, sequence L, channels D, states N."""
+    _fields_ = [(n, ctypes.c_int64) for n in ("B", "L", "D", "N")]
+
+
+def mamba_workspace_size(shape: MambaShapeArg) -> int:
+    return int(library().mamba_fwd_workspace_size(ctypes.byref(shape)))
+
+
+def mamba_fwd(x, delta, A, B, C, Dskip, *, out=None, workspace=None):
+    """y[B,L,D] = selective scan of (x, delta, A, B, C, Dskip) (mamba_fwd),
+    on the current stream."""
+    import torch
+    lib = library()
+    if x.dim() != 3 or A.dim() != 2:
+        raise ValueError("x must be [B,L,D] and A [D,N]")
+    s = MambaShapeArg(x.shape[0], x.shape[1], x.shape[2], A.shape[1])
+    dev = x.device
+    _check(x, "x", (s.B, s.L, s.D), dev)
+    _check(delta, "delta", (s.B, s.L, s.D), dev)
+    _check(A, "A", (s.D, s.N), dev)
+    _check(B, "B", (s.B, s.L, s.N), dev)
+    _check(C, "C", (s.B, s.L, s.N), dev)
+    _check(Dskip, "Dskip", (s.D,), dev)
+    if out is None:
+        out = torch.empty((s.B, s.L, s.D), dtype=torch.float32, device=dev)
+    _check(out, "out", (s.B, s.L, s.D), dev)
+    ws, need = _workspace_bytes(mamba_workspace_size(s), dev, workspace)
+    rc = lib.mamba_fwd(ctypes.byref(s), _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip), _ptr(out),
+                       _ptr(ws), ctypes.c_size_t(ws.numel() * ws.element_size()), _stream(dev))
+    if rc != 0:
+        raise SsdError(rc, "mamba_fwd")
+    return out

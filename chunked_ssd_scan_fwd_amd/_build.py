@@ -17,7 +17,7 @@ LIB = os.path.join(PKG, "libssd_hip.so")
 # benchmark-only device probes (MFMA loop, shader clock), a library of their own
 PROBE_LIB = os.path.join(PKG, "libssd_probe.so")
 OBJDIR = os.path.join(ROOT, "_build")
-SOURCES = ["ssd_api.hip", "k_scan.hip", "k_output.hip", "k_pair.hip", "k_grads.hip", "ssd_validate.cpp"]
+SOURCES = ["ssd_api.hip", "k_scan.hip", "k_output.hip", "k_pair.hip", "k_grads.hip", "k_mamba.hip", "ssd_validate.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -118,6 +118,25 @@ int device_cus();
 
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// ---- selective (Mamba-style) scan
+// Shape checks: SSD_ERR_NULL, SSD_ERR_SHAPE (negative B or L, D or N below
+// 1, index range), SSD_ERR_UNSUPPORTED (N above MAMBA_MAX_STATE, B above
+// 65535, L above 65535 * kMambaMaxSeg, D above 2^20).
+int mamba_check_shape(const mamba_shape *s);
+// The sequence is cut into nseg segments of seg_len steps (the last may be
+// shorter) that run in parallel: one thread per (b, channel, segment).  A
+// first pass forms each segment's end state from zero, a carry pass turns
+// them, in place, into the state entering each segment, and the output pass
+// rescans every segment from its entering state.
+constexpr int64_t kMambaMaxSeg = 256;   // longest segment (its B, C rows sit in LDS)
+struct MambaPlan {
+    int64_t nseg = 1, seg_len = 0;
+    // byte offsets in the workspace: end / entering states float [B][nseg][N][D],
+    // summed delta of each segment float [B][nseg][D], total
+    size_t hend = 0, sdl = 0, total = 0;
+};
+MambaPlan mamba_plan(const mamba_shape *s, int cus);
+
 // Padded MFMA tile width (32, 64 or 128) for dk / dv in 1..128.
 inline int pad_dim(int64_t d) { return d <= 32 ? 32 : (d <= 64 ? 64 : 128); }
 

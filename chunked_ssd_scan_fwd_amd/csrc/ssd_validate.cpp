@@ -50,6 +50,55 @@ bool fwd_pairs(const ssd_shape *s, int cus)
     return pad_dim(s->dv) == 128 && s->B * s->G * ((NC + 1) / 2) >= 2 * int64_t(cus);
 }
 
+int mamba_check_shape(const mamba_shape *s)
+{
+    if (!s) return SSD_ERR_NULL;
+    if (s->B < 0 || s->L < 0 || s->D < 1 || s->N < 1) return SSD_ERR_SHAPE;
+    const int64_t lim = int64_t(1) << 40;
+    if (s->B > lim || s->L > lim || s->D > lim || s->N > lim) return SSD_ERR_SHAPE;
+    if (s->N > MAMBA_MAX_STATE) return SSD_ERR_UNSUPPORTED;
+    const int64_t w = s->D > s->N ? s->D : s->N;
+    if (s->B > lim / (s->L + 1) || s->B * (s->L + 1) > lim / w) return SSD_ERR_SHAPE;
+    // grid: x over 256-channel blocks, y over segments (at most 65535 of at
+    // most kMambaMaxSeg steps), z over batch
+    if ((s->D + 255) / 256 > (int64_t(1) << 31) - 1 || s->B > 65535) return SSD_ERR_UNSUPPORTED;
+    if (s->L > 65535 * kMambaMaxSeg) return SSD_ERR_UNSUPPORTED;
+    // a segment's rows of x, delta and y are one buffer resource (< 2 GiB)
+    if (s->D > (int64_t(1) << 20)) return SSD_ERR_UNSUPPORTED;
+    return SSD_OK;
+}
+
+MambaPlan mamba_plan(const mamba_shape *s, int cus)
+{
+    MambaPlan P;
+    P.seg_len = s->L;
+    if (s->B == 0 || s->L == 0) return P;
+    // About 512 threads (8 waves) per CU over all segments, segments of at
+    // least 8 steps where that allows, at most kMambaMaxSeg steps, and at
+    // most 65535 of them (the launch grid's y extent).  More segments hide
+    // more latency in the scans but lengthen the carry pass's chain.
+    const int64_t want = (int64_t(cus) * 512 + s->B * s->D - 1) / (s->B * s->D);
+    int64_t nseg = want < 1 ? 1 : want;
+    const int64_t cap = s->L / 8 > 1 ? s->L / 8 : 1;
+    if (nseg > cap) nseg = cap;
+    const int64_t least = (s->L + kMambaMaxSeg - 1) / kMambaMaxSeg;
+    if (nseg < least) nseg = least;
+    if (nseg > 65535) nseg = 65535;
+    P.seg_len = (s->L + nseg - 1) / nseg;
+    P.nseg = (s->L + P.seg_len - 1) / P.seg_len;
+    if (P.nseg <= 1) {
+        P.nseg = 1;
+        return P;   // one segment: no workspace
+    }
+    size_t o = 0;
+    P.hend = o;
+    o = round_up(o + size_t(s->B) * size_t(P.nseg) * size_t(s->N) * size_t(s->D) * sizeof(float), 256);
+    P.sdl = o;
+    o = round_up(o + size_t(s->B) * size_t(P.nseg) * size_t(s->D) * sizeof(float), 256);
+    P.total = o;
+    return P;
+}
+
 int fwd_chunk_setting()
 {
     const char *e = std::getenv("SSD_FWD_CHUNK");
@@ -234,6 +283,12 @@ int ssd_workspace_layout(const ssd_shape *shape, int backward, size_t offsets[SS
     const ssd::Layout L = ssd::make_layout(shape, backward != 0, ssd::device_cus());
     for (int i = 0; i <= SSD_WS_REGIONS; ++i) offsets[i] = L.off[i];
     return SSD_OK;
+}
+
+size_t mamba_fwd_workspace_size(const mamba_shape *shape)
+{
+    if (ssd::mamba_check_shape(shape) != SSD_OK) return 0;
+    return ssd::mamba_plan(shape, ssd::device_cus()).total;
 }
 
 int ssd_fwd_state_stride(const ssd_shape *shape)

@@ -277,6 +277,48 @@ int ssd_bwd_timed(ssd_timer *timer, const ssd_shape *shape,
 int ssd_kernel_count(void);
 const char *ssd_kernel_name(int kid);
 
+/* ---------------------------------------------------------------------------
+ * Selective (Mamba-style) scan, the second workload of the benchmark pages
+ * (kernel_mamba_cpu.json, results: impls scan, assoc and chunked at batch 4,
+ * state 16, dim 256/512/1024, seq 512/2048/8192, modes fwd and fwd_bwd).
+ *
+ * That page prints no formula.  Its byte counts fix the tensor set: every
+ * fwd record's xla_arg_mb is x[B,L,D] + delta[B,L,D] + A[D,N] + B[B,L,N] +
+ * C[B,L,N] + Dskip[D] in float32 (4.27 MiB at B=4, L=512, D=256, N=16) and
+ * its xla_out_mb is y[B,L,D] (2.0 MiB).  The library computes the plain
+ * reading of that argument set, for every batch b, channel d and state n,
+ * with h_{-1} = 0:
+ *     h_t[d,n] = exp(delta[b,t,d] A[d,n]) h_{t-1}[d,n] + delta[b,t,d] B[b,t,n] x[b,t,d]
+ *     y[b,t,d] = sum_n C[b,t,n] h_t[d,n] + Dskip[d] x[b,t,d]
+ * (delta is used as given: no softplus, no gating input).  All arithmetic
+ * is fp32; results are deterministic run to run.
+ *
+ * Shapes: B >= 0, L >= 0, D >= 1, 1 <= N <= MAMBA_MAX_STATE (larger N:
+ * SSD_ERR_UNSUPPORTED); B*L*max(D,N) < 2^40.  Layouts are dense row-major
+ * as written above; pointers are device pointers on the current device,
+ * 4-byte aligned, owned by the caller; outputs are overwritten and must not
+ * alias anything else.  Arguments are checked on the host before anything
+ * is enqueued (status codes as for ssd_fwd); work is enqueued on `stream`.
+ * The workspace (mamba_fwd_workspace_size bytes, 16-byte aligned; none when
+ * the size is 0) holds each sequence segment's end state and summed delta;
+ * it need not be initialised and is not read after the call. */
+#define MAMBA_MAX_STATE 16
+
+typedef struct mamba_shape {
+    int64_t B, L, D, N;
+} mamba_shape;
+
+/* Workspace bytes mamba_fwd needs on the current device (0 for an invalid
+ * shape, and when the sequence runs as one segment). */
+size_t mamba_fwd_workspace_size(const mamba_shape *shape);
+
+/* y = the selective scan of (x, delta, A, B, C, Dskip); see above. */
+int mamba_fwd(const mamba_shape *shape,
+              const float *x, const float *delta, const float *A,
+              const float *B, const float *C, const float *Dskip,
+              float *y,
+              void *workspace, size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -341,3 +341,57 @@ def test_wide_shapes_workspace(B, G, H, T, dk, dv):
     # validation still happens on the host before anything else
     assert _call_fwd(s, ptr=0x1000, ws_bytes=ssd.workspace_size(s, False) - 1) == 4
     assert _call_bwd(s, ptr=0x1000, ws_bytes=ssd.workspace_size(s, True) - 1) == 4
+
+
+# ---- selective (Mamba-style) scan: host-side checks, no launches
+
+
+def _mamba_call(shape, ptr=0x1000, ws_bytes=0):
+    lib = ssd.library()
+    p = ctypes.c_void_p(ptr) if ptr else None
+    return lib.mamba_fwd(ctypes.byref(shape), *([p] * 7), p, ws_bytes, None)
+
+
+@pytest.mark.parametrize("shape,code", [
+    (ssd.MambaShapeArg(-1, 10, 4, 16), 2),        # negative B
+    (ssd.MambaShapeArg(1, -3, 4, 16), 2),         # negative L
+    (ssd.MambaShapeArg(1, 10, 0, 16), 2),         # D = 0
+    (ssd.MambaShapeArg(1, 10, 4, 0), 2),          # N = 0
+    (ssd.MambaShapeArg(1, 10, 4, 17), 3),         # more states than a thread holds
+    (ssd.MambaShapeArg(70000, 10, 4, 16), 3),     # batch beyond the grid's z extent
+    (ssd.MambaShapeArg(1, 65535 * 256 + 1, 4, 16), 3),   # segments beyond the grid's y extent
+])
+def test_mamba_bad_shapes_rejected(shape, code):
+    assert _mamba_call(shape) == code
+    assert ssd.library().mamba_fwd_workspace_size(ctypes.byref(shape)) == 0
+
+
+def test_mamba_validation_before_launch():
+    lib = ssd.library()
+    assert lib.mamba_fwd(None, *([None] * 7), None, 0, None) == 1
+    s = ssd.MambaShapeArg(2, 4096, 64, 16)
+    need = ssd.mamba_workspace_size(s)
+    assert need > 0
+    assert _mamba_call(s, ptr=0) == 1                          # null tensors
+    assert _mamba_call(s, ptr=0x1002) == 5                     # misaligned
+    assert _mamba_call(s, ptr=0x1000, ws_bytes=need - 1) == 4  # short workspace
+    # empty problems need nothing
+    assert _mamba_call(ssd.MambaShapeArg(0, 10, 4, 16), ptr=0) == 0
+    assert _mamba_call(ssd.MambaShapeArg(3, 0, 4, 16), ptr=0) == 0
+
+
+def test_mamba_workspace_formula():
+    """Segment end states float [B][nseg][N][D] and summed deltas float
+    [B][nseg][D], each 256-byte aligned; about 512 threads per CU (256 CUs
+    when no device is visible), segments of 8 to 256 steps."""
+    def plan(B, L, D):
+        nseg = max(1, -(-256 * 512 // (B * D)))
+        nseg = min(nseg, max(1, L // 8))
+        nseg = max(nseg, -(-L // 256))
+        sl = -(-L // nseg)
+        return -(-L // sl)
+    up = lambda x: (x + 255) // 256 * 256
+    for B, L, D, N in [(4, 8192, 256, 16), (4, 512, 1024, 16), (1, 100, 3, 5), (2, 7, 64, 16), (1, 70000, 1, 1)]:
+        ns = plan(B, L, D)
+        want = 0 if ns == 1 else up(B * ns * N * D * 4) + up(B * ns * D * 4)
+        assert ssd.mamba_workspace_size(ssd.MambaShapeArg(B, L, D, N)) == want, (B, L, D, N)

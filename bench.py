@@ -39,13 +39,21 @@ C_NOM = 64
 # (kernel_ssd_gpu.json, record chunked·fwd_bwd·g2h8_d128·T8192, median_ms).
 PAGE_FWD_BWD_MS = 11.883384999237023
 # kernel_mamba_cpu.json, results: the CPU medians (ms) of impls scan and
-# chunked, mode fwd, at batch 4, state 16 -- context for --mamba, not a target.
+# chunked at batch 4, state 16, modes fwd and fwd_bwd -- context for --mamba,
+# not a target.
 MAMBA_PAGE_CPU_MS = {
     (256, 512): {"scan": 17.20, "chunked": 6.40}, (256, 2048): {"scan": 28.61, "chunked": 21.79},
     (256, 8192): {"scan": 120.3, "chunked": 107.4}, (512, 512): {"scan": 14.21, "chunked": 14.48},
     (512, 2048): {"scan": 56.86, "chunked": 92.16}, (512, 8192): {"scan": 231.8, "chunked": 205.5},
     (1024, 512): {"scan": 20.82, "chunked": 16.61}, (1024, 2048): {"scan": 176.1, "chunked": 95.43},
     (1024, 8192): {"scan": 319.1, "chunked": 298.9},
+}
+MAMBA_PAGE_CPU_FWD_BWD_MS = {
+    (256, 512): {"scan": 173.6, "chunked": 41.06}, (256, 2048): {"scan": 700.5, "chunked": 235.8},
+    (256, 8192): {"scan": 2619., "chunked": 644.9}, (512, 512): {"scan": 369.1, "chunked": 84.71},
+    (512, 2048): {"scan": 1934., "chunked": 383.1}, (512, 8192): {"scan": 5166., "chunked": 1037.},
+    (1024, 512): {"scan": 587.1, "chunked": 215.8}, (1024, 2048): {"scan": 2677., "chunked": 567.6},
+    (1024, 8192): {"scan": 7782., "chunked": 1868.},
 }
 
 # The same page's chunked path over its whole grid, (fwd, fwd_bwd) median ms on
@@ -258,17 +266,25 @@ def grid_sweep(args, torch, ssd):
 PEAK_VALU_SLOTS = 256 * 4 * 16 * 2.4e9
 
 
-def mamba_work(s):
-    elems = s.B * s.L * s.D
-    slots = elems * s.N * 8
-    io = 4 * (3 * elems + 2 * s.B * s.L * s.N + s.D * s.N + s.D)
-    return slots, io
+def mamba_work(s, backward=False):
+    """(lane slots, bytes) of the least work: the forward's N (4 + 4) slots
+    per element, and for fwd_bwd N 13 more -- one exponential (4) for the
+    decay, shared by the recomputed state and the adjoint, and nine
+    multiply-adds (the state, the adjoint, dx, ddelta 2, dA 2, dB, dC); the
+    bytes are every argument read once and every result written once."""
+    elems, bln, dn = s.B * s.L * s.D, s.B * s.L * s.N, s.D * s.N
+    if not backward:
+        return elems * s.N * 8, 4 * (3 * elems + 2 * bln + dn + s.D)
+    # fwd: x, delta, B, C, A, Dskip in, y out; bwd: those and dy in, six gradients out
+    io_f = 4 * (3 * elems + 2 * bln + dn + s.D)
+    io_b = 4 * (3 * elems + 2 * bln + dn + s.D) + 4 * (2 * elems + 2 * bln + dn + s.D)
+    return elems * s.N * (8 + 13), io_f + io_b
 
 
 def mamba_sweep(args, torch, ssd, points=None):
-    """mamba_fwd at the points of kernel_mamba_cpu.json's grid (batch 4, state
-    16), timed by the pages' protocol; the page's CPU medians go along as
-    context."""
+    """mamba_fwd (fwd) and mamba_fwd + mamba_bwd (fwd_bwd) at the points of
+    kernel_mamba_cpu.json's grid (batch 4, state 16), timed by the pages'
+    protocol; the page's CPU medians of the forward go along as context."""
     from ssd_workload.mamba import MAMBA_GRID, make_mamba_inputs
     out = []
     for (D, L), s in MAMBA_GRID.items():
@@ -278,23 +294,37 @@ def mamba_sweep(args, torch, ssd, points=None):
         d = {k: torch.from_numpy(v).to("cuda") for k, v in inp.items()}
         sa = ssd.MambaShapeArg(s.B, s.L, s.D, s.N)
         ws = torch.empty(max(1, ssd.mamba_workspace_size(sa)), dtype=torch.uint8, device="cuda")
+        wsb = torch.empty(max(1, ssd.mamba_workspace_size(sa, backward=True)), dtype=torch.uint8, device="cuda")
         y = torch.empty((s.B, s.L, s.D), device="cuda")
+        grads = (torch.empty_like(d["x"]), torch.empty_like(d["x"]), torch.empty_like(d["A"]),
+                 torch.empty_like(d["B"]), torch.empty_like(d["C"]), torch.empty_like(d["Dskip"]))
 
         def fwd():
             ssd.mamba_fwd(d["x"], d["delta"], d["A"], d["B"], d["C"], d["Dskip"], out=y, workspace=ws)
 
-        for _ in range(args.warmup):
+        def fwd_bwd():
+            # the loss value (y) and all six gradients; the backward
+            # recomputes the forward's states itself
             fwd()
-        r = protocol_ms(torch, fwd, repeats=args.repeats)
-        t = r["median_ms"] * 1e-3
-        slots, io = mamba_work(s)
-        out.append({"workload": f"mamba_d{D}_L{L}", "shape": {"B": s.B, "L": s.L, "D": s.D, "N": s.N},
-                    "fwd": {"median_ms": r["median_ms"], "q1_ms": r["q1_ms"], "q3_ms": r["q3_ms"],
-                            "gbps_io": io / t / 1e9, "hbm_frac": io / t / PEAK_HBM,
-                            "alu_frac": slots / t / PEAK_VALU_SLOTS,
-                            "roofline_frac": max(io / PEAK_HBM, slots / PEAK_VALU_SLOTS) / t},
-                    "page_cpu_ms": MAMBA_PAGE_CPU_MS.get((D, L)), "dtype": "f32", "data": "synthetic"})
-        del d, ws, y
+            ssd.mamba_bwd(d["x"], d["delta"], d["A"], d["B"], d["C"], d["Dskip"], d["dy"], out=grads,
+                          workspace=wsb)
+
+        line = {"workload": f"mamba_d{D}_L{L}", "shape": {"B": s.B, "L": s.L, "D": s.D, "N": s.N}}
+        for mode, fn in (("fwd", fwd), ("fwd_bwd", fwd_bwd)):
+            for _ in range(args.warmup):
+                fn()
+            r = protocol_ms(torch, fn, repeats=args.repeats)
+            t = r["median_ms"] * 1e-3
+            slots, io = mamba_work(s, backward=mode == "fwd_bwd")
+            line[mode] = {"median_ms": r["median_ms"], "q1_ms": r["q1_ms"], "q3_ms": r["q3_ms"],
+                          "gbps_io": io / t / 1e9, "hbm_frac": io / t / PEAK_HBM,
+                          "alu_frac": slots / t / PEAK_VALU_SLOTS,
+                          "roofline_frac": max(io / PEAK_HBM, slots / PEAK_VALU_SLOTS) / t}
+        line.update({"page_cpu_ms": {"fwd": MAMBA_PAGE_CPU_MS.get((D, L)),
+                                     "fwd_bwd": MAMBA_PAGE_CPU_FWD_BWD_MS.get((D, L))},
+                     "dtype": "f32", "data": "synthetic"})
+        out.append(line)
+        del d, ws, wsb, y, grads
         torch.cuda.empty_cache()
     return out
 

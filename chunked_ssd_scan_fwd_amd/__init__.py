@@ -89,6 +89,10 @@ def library(path: str | None = None):
     lib.mamba_fwd_workspace_size.restype = sz
     lib.mamba_fwd.argtypes = [mp] + [vp] * 7 + [vp, sz, vp]
     lib.mamba_fwd.restype = ctypes.c_int
+    lib.mamba_bwd_workspace_size.argtypes = [mp]
+    lib.mamba_bwd_workspace_size.restype = sz
+    lib.mamba_bwd.argtypes = [mp] + [vp] * 13 + [vp, sz, vp]
+    lib.mamba_bwd.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -327,8 +331,9 @@ class MambaShapeArg(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in ("B", "L", "D", "N")]
 
 
-def mamba_workspace_size(shape: MambaShapeArg) -> int:
-    return int(library().mamba_fwd_workspace_size(ctypes.byref(shape)))
+def mamba_workspace_size(shape: MambaShapeArg, backward: bool = False) -> int:
+    lib = library()
+    return int((lib.mamba_bwd_workspace_size if backward else lib.mamba_fwd_workspace_size)(ctypes.byref(shape)))
 
 
 def mamba_fwd(x, delta, A, B, C, Dskip, *, out=None, workspace=None):
@@ -354,4 +359,31 @@ def mamba_fwd(x, delta, A, B, C, Dskip, *, out=None, workspace=None):
                        _ptr(ws), ctypes.c_size_t(ws.numel() * ws.element_size()), _stream(dev))
     if rc != 0:
         raise SsdError(rc, "mamba_fwd")
+    return out
+
+
+def mamba_bwd(x, delta, A, B, C, Dskip, dy, *, out=None, workspace=None):
+    """(dx, ddelta, dA, dB, dC, dDskip): the gradients of sum(dy * y) for the
+    selective scan (mamba_bwd), on the current stream."""
+    import torch
+    lib = library()
+    if x.dim() != 3 or A.dim() != 2:
+        raise ValueError("x must be [B,L,D] and A [D,N]")
+    s = MambaShapeArg(x.shape[0], x.shape[1], x.shape[2], A.shape[1])
+    dev = x.device
+    shapes = {"x": (s.B, s.L, s.D), "delta": (s.B, s.L, s.D), "A": (s.D, s.N), "B": (s.B, s.L, s.N),
+              "C": (s.B, s.L, s.N), "Dskip": (s.D,), "dy": (s.B, s.L, s.D)}
+    for name, t in zip(shapes, (x, delta, A, B, C, Dskip, dy)):
+        _check(t, name, shapes[name], dev)
+    outs = ("dx", "ddelta", "dA", "dB", "dC", "dDskip")
+    oshape = [shapes["x"], shapes["x"], shapes["A"], shapes["B"], shapes["C"], shapes["Dskip"]]
+    if out is None:
+        out = tuple(torch.empty(sh, dtype=torch.float32, device=dev) for sh in oshape)
+    for name, t, sh in zip(outs, out, oshape):
+        _check(t, name, sh, dev)
+    ws, need = _workspace_bytes(mamba_workspace_size(s, True), dev, workspace)
+    rc = lib.mamba_bwd(ctypes.byref(s), _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip), _ptr(dy),
+                       *[_ptr(t) for t in out], _ptr(ws), ctypes.c_size_t(ws.numel() * ws.element_size()), _stream(dev))
+    if rc != 0:
+        raise SsdError(rc, "mamba_bwd")
     return out

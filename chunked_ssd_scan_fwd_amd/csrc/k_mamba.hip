@@ -193,6 +193,399 @@ __global__ __launch_bounds__(CJ *CD) void k_mamba_carry(const float *__restrict_
     }
 }
 
+
+// ---- backward
+//
+// With G_t[d,n] = dL/dh_t (L = sum dy . y), a_t = exp(delta_t A):
+//     G_t        = C_t[n] dy_t[d] + a_{t+1} G_{t+1}
+//     dx_t[d]    = Dskip[d] dy_t[d] + delta_t[d] sum_n G_t B_t[n]
+//     ddelta_t[d]= sum_n G_t (A[d,n] a_t h_{t-1} + B_t[n] x_t[d])
+//     dA[d,n]    = sum_{b,t} G_t delta_t[d] a_t h_{t-1}
+//     dB_t[n]    = sum_d G_t delta_t[d] x_t[d]       dC_t[n] = sum_d dy_t[d] h_t[d,n]
+//     dDskip[d]  = sum_{b,t} dy_t[d] x_t[d]
+// The sequence is cut into segments of kMambaBwdSeg steps:
+//   1. k_mamba_seg_ends: per segment, the forward from a zero state (its end
+//      state and summed delta) and the adjoint from zero at its end (the
+//      adjoint at its first step); one thread per (b, d) as in the forward;
+//   2. k_mamba_carry (the forward's) and k_mamba_rcarry: the state entering
+//      every segment from the left, and the adjoint entering it from the
+//      right, a_{t1} G_{t1};
+//   3. k_mamba_bwd_seg: per segment, h over its steps again (kept in
+//      registers), then the steps in reverse with the true adjoint: dx and
+//      ddelta (sums over n inside a 16-lane row), dB and dC (sums over the
+//      block's channels through an LDS transpose, the block walking all
+//      channel chunks of its segment), dA and dDskip per segment;
+//   4. k_mamba_wsum: dA and dDskip summed over batch and segments, and the
+//      dB / dC partials of blocks that split the channels, in fixed order.
+// Threads of pass 3 own one (b, d, n): lane n + 16 (d % 4), so a row of 16
+// lanes holds one channel's states.  The chunk's x, delta and dy (and the
+// segment's B and C rows) are staged in LDS with coalesced loads, and each
+// row of lanes reads its channel's value there as a broadcast.
+
+namespace {
+constexpr int NS = MAMBA_MAX_STATE;   // states per channel (one lane each)
+constexpr int SB = kMambaBwdSeg;      // steps per backward segment
+constexpr int BD = kMambaBwdChans;    // channels per block in pass 3 (512 threads: 256 VGPRs)
+constexpr int BT = BD * NS;           // threads per block
+constexpr int WIN = 8;                // steps per dB / dC transpose window
+constexpr int XP = SB + 4;            // pitch of a channel's staged steps (16-byte rows)
+constexpr int kQuadXor1 = 0xB1;       // DPP quad_perm [1,0,3,2]
+static_assert(SB % 4 == 0 && (SB * BD) % BT == 0, "tile shapes");
+}  // namespace
+
+// 1. per (b, segment, d): end state and summed delta from zero (h over the
+// segment), and the adjoint at the segment's first step from zero at its end.
+// Steps past the sequence's end are staged as delta = x = dy = 0 and B = C = 0,
+// which leaves both walks unchanged, so neither branches on the step count.
+template <bool FULL>
+__global__ __launch_bounds__(MB) void k_mamba_seg_ends(const float *__restrict__ x, const float *__restrict__ delta,
+                                                      const float *__restrict__ A, const float *__restrict__ Bm,
+                                                      const float *__restrict__ Cm, const float *__restrict__ dy,
+                                                      float *__restrict__ hend, float *__restrict__ sdl,
+                                                      float *__restrict__ gl, int64_t L, int64_t D, int N,
+                                                      int64_t nseg)
+{
+    __shared__ __attribute__((aligned(16))) float BC[2][SB][MNS];
+    if constexpr (FULL) N = MNS;
+    const int64_t d = (int64_t)blockIdx.x * MB + threadIdx.x, p = blockIdx.y, b = blockIdx.z;
+    const int64_t t0 = p * SB, t1 = (t0 + SB) < L ? (t0 + SB) : L;
+    const int nrow = (int)(t1 - t0);
+    for (int i = threadIdx.x; i < SB * MNS; i += MB) {
+        const int r = i / MNS, n = i % MNS;
+        const bool in = r < nrow && n < N;
+        BC[0][r][n] = in ? Bm[(b * L + t0 + r) * N + n] : 0.f;
+        BC[1][r][n] = in ? Cm[(b * L + t0 + r) * N + n] : 0.f;
+    }
+    __syncthreads();
+    if (d >= D) return;   // no barrier below
+    const int64_t seg0 = (b * L + t0) * D;
+    const rsrc_t rx = make_rsrc(x + seg0, (int64_t)nrow * D * 4), rdl = make_rsrc(delta + seg0, (int64_t)nrow * D * 4);
+    const rsrc_t rdy = make_rsrc(dy + seg0, (int64_t)nrow * D * 4);
+    const uint32_t lo = (uint32_t)d * 4u, rowb = (uint32_t)D * 4u;
+    // The row offset goes in the lane offset, which the buffer range check
+    // covers: rows past the segment (the resource's end) read 0.
+    auto ld = [&](rsrc_t r_, int r) {
+        return __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_, lo + (uint32_t)r * rowb, 0, 0));
+    };
+    // delta stays in registers for both walks; dy for the reverse walk is
+    // loaded as the forward walk frees the registers of x, last step first.
+    float dl[SB], xv[SB], dv[SB];
+#pragma unroll
+    for (int r = 0; r < SB; ++r) {
+        dl[r] = ld(rdl, r);
+        xv[r] = ld(rx, r);
+    }
+    float a2[MNS], h[MNS];
+#pragma unroll
+    for (int n = 0; n < MNS; ++n) {
+        a2[n] = n < N ? A[d * N + n] * kLog2e : 0.f;
+        h[n] = 0.f;
+    }
+    float sd = 0.f;
+#pragma unroll
+    for (int r = 0; r < SB; ++r) {
+        const float u = dl[r] * xv[r];
+        sd += dl[r];
+        dv[SB - 1 - r] = ld(rdy, SB - 1 - r);
+#pragma unroll
+        for (int n = 0; n < MNS; ++n)
+            if (FULL || n < N) h[n] = exp2_fast(dl[r] * a2[n]) * h[n] + u * BC[0][r][n];
+        __builtin_amdgcn_sched_barrier(0);   // one step at a time: bounds the LDS reads in flight
+    }
+    const int64_t o = (b * nseg + p) * N * D + d;   // state n at o + n D
+#pragma unroll
+    for (int n = 0; n < MNS; ++n)
+        if (n < N) hend[o + n * D] = h[n];
+    sdl[(b * nseg + p) * D + d] = sd;
+    // the adjoint: G = C_r dy_r + a_{r+1} G, from G = 0 past the last step.
+    // The decays are formed again: the empty asm hides that they equal the
+    // forward walk's, which would otherwise be kept live (512 registers).
+#pragma unroll
+    for (int r = 0; r < SB; ++r) asm volatile("" : "+v"(dl[r]));
+#pragma unroll
+    for (int n = 0; n < MNS; ++n) h[n] = 0.f;
+#pragma unroll
+    for (int r = SB - 1; r >= 0; --r) {
+#pragma unroll
+        for (int n = 0; n < MNS; ++n) {
+            if (FULL || n < N) {
+                const float c = BC[1][r][n] * dv[r];
+                h[n] = r + 1 < SB ? exp2_fast(dl[r + 1] * a2[n]) * h[n] + c : c;
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int n = 0; n < MNS; ++n)
+        if (n < N) gl[o + n * D] = h[n];
+}
+
+// 2. per (b, n, d): the adjoint entering each segment from the right.  With
+// Gf_p the adjoint at segment p's first step and gl_p its part from inside
+// the segment, Gf_p = F_p Gf_{p+1} + gl_p, F_p = exp(A (sum delta over p -
+// delta_{t0(p)} + delta_{t0(p+1)})), walked from the last segment back; gl_p
+// is replaced by exp(A delta_{t0(p+1)}) Gf_{p+1} (0 for the last segment).
+// Two levels as in k_mamba_carry: CJ groups of gs segments per channel.
+__global__ __launch_bounds__(CJ *CD) void k_mamba_rcarry(const float *__restrict__ delta,
+                                                        const float *__restrict__ A, const float *__restrict__ sdl,
+                                                        float *__restrict__ gl, int64_t L, int64_t D, int N,
+                                                        int64_t nseg)
+{
+    __shared__ float Fm[CJ][CD], Em[CJ][CD], Gs[CJ][CD];
+    const int dl = threadIdx.x % CD, j = threadIdx.x / CD;
+    const int64_t d = (int64_t)blockIdx.x * CD + dl;
+    const int n = blockIdx.y;
+    const int64_t b = blockIdx.z;
+    const bool live = d < D;
+    const int64_t dd = live ? d : 0;   // masked lanes read a valid address and store nothing
+    const float a2 = A[dd * N + n] * kLog2e;
+    const int64_t gs = (nseg + CJ - 1) / CJ;
+    const int64_t p0 = j * gs, p1 = (p0 + gs) < nseg ? (p0 + gs) : nseg;
+    float *g = gl + (b * nseg * N + n) * D + dd;   // segment q at g[q N D]
+    const float *sg = sdl + b * nseg * D + dd;      // segment q at sg[q D]
+    const float *fd = delta + b * L * D + dd;       // step t at fd[t D]
+    const int64_t es = (int64_t)N * D, fs = (int64_t)SB * D;
+    auto Fof = [&](int64_t q) {   // F_q, 0 for the last segment
+        return q + 1 < nseg ? exp2_fast(a2 * (sg[q * D] - fd[q * fs] + fd[(q + 1) * fs])) : 0.f;
+    };
+    float F = 1.f, E = 0.f;   // the group's map, composed from its last segment back
+    for (int64_t q = p1 - 1; q >= p0; --q) {
+        const float f = Fof(q);
+        E = f * E + g[q * es];
+        F = f * F;
+    }
+    Fm[j][dl] = F;
+    Em[j][dl] = E;
+    __syncthreads();
+    if (j == 0) {
+        float Gv = 0.f;   // nothing follows the last group
+        for (int q = CJ - 1; q >= 0; --q) {
+            Gs[q][dl] = Gv;   // the adjoint at the first segment after group q
+            Gv = Fm[q][dl] * Gv + Em[q][dl];
+        }
+    }
+    __syncthreads();
+    float Gn = Gs[j][dl];   // Gf_{p1}
+    for (int64_t q = p1 - 1; q >= p0; --q) {
+        const float glq = g[q * es];
+        const float hat = q + 1 < nseg ? exp2_fast(a2 * fd[(q + 1) * fs]) * Gn : 0.f;
+        if (live) g[q * es] = hat;
+        Gn = Fof(q) * Gn + glq;   // Gf_q
+    }
+}
+
+// 3. per (b, segment): gradients of the segment's steps.  Block = BD channels x
+// NS states; it walks the channel chunks blockIdx.x, + gridDim.x, ... and adds
+// up dB, dC over all of them in LDS.  dBC: the segment's dB / dC rows
+// (nsplit == 1) or this split's partial rows [nsplit][B][L][2][N].  hin and
+// ghat are the entering states and right adjoints, [B][nseg][N][D].
+__global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(4))) void k_mamba_bwd_seg(
+    const float *__restrict__ x, const float *__restrict__ delta, const float *__restrict__ A,
+    const float *__restrict__ Bm, const float *__restrict__ Cm, const float *__restrict__ Ds,
+    const float *__restrict__ dy, const float *__restrict__ hin, const float *__restrict__ ghat,
+    float *__restrict__ dx, float *__restrict__ ddelta, float *__restrict__ dB, float *__restrict__ dC,
+    float *__restrict__ dBCp, float *__restrict__ dApart, float *__restrict__ dDpart, int64_t L, int64_t D, int N,
+    int64_t nseg, int nsplit)
+{
+    __shared__ float Tw[WIN][2][BT];                                  // one window of per-lane dB / dC terms
+    __shared__ float acc[SB][2][NS];                                  // the segment's dB / dC so far
+    __shared__ __attribute__((aligned(16))) float BCs[2][SB][NS];     // the segment's B, C rows
+    __shared__ __attribute__((aligned(16))) float Xs[3][BD][XP];      // the chunk's x, delta, dy by channel
+    const int tid = threadIdx.x, dl = tid / NS, n = tid % NS;
+    const int64_t p = blockIdx.y, b = blockIdx.z;
+    const int64_t t0 = p * SB, t1 = (t0 + SB) < L ? (t0 + SB) : L;
+    const int nrow = (int)(t1 - t0);
+    const int nn = n < N ? n : N - 1;
+    for (int i = tid; i < SB * 2 * NS; i += BT) (&acc[0][0][0])[i] = 0.f;
+    for (int i = tid; i < 2 * SB * NS; i += BT) {
+        const int w = i / (SB * NS), r = (i / NS) % SB, m = i % NS;
+        (&BCs[0][0][0])[i] = r < nrow && m < N ? (w ? Cm : Bm)[(b * L + t0 + r) * N + m] : 0.f;
+    }
+    // Staging: element e = tid + k BT of a chunk's tile is step e / BD,
+    // channel e % BD (a wave loads two 128-byte rows); steps past the
+    // sequence and channels past D are staged as 0.
+    constexpr int KS = SB * BD / BT;
+    const int64_t nchunk = (D + BD - 1) / BD;
+    const int64_t row0 = (b * L + t0) * D;
+    float stg[3][KS];
+    auto fetch = [&](int64_t c) {
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
+            const int e = tid + k * BT, r = e / BD;
+            const int64_t ch = c * BD + e % BD;
+            const bool in = r < nrow && ch < D;
+            const int64_t gi = row0 + (int64_t)r * D + (in ? ch : 0);
+            stg[0][k] = in ? x[gi] : 0.f;
+            stg[1][k] = in ? delta[gi] : 0.f;
+            stg[2][k] = in ? dy[gi] : 0.f;
+        }
+    };
+    auto put = [&]() {
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
+            const int e = tid + k * BT, r = e / BD, q = e % BD;
+            Xs[0][q][r] = stg[0][k];
+            Xs[1][q][r] = stg[1][k];
+            Xs[2][q][r] = stg[2][k];
+        }
+    };
+    fetch(blockIdx.x);
+    put();
+    __syncthreads();
+    for (int64_t c = blockIdx.x; c < nchunk; c += nsplit) {
+        const bool more = c + nsplit < nchunk;   // uniform
+        if (more) fetch(c + nsplit);             // lands while this chunk computes
+        const int64_t d = c * BD + dl;
+        const bool live = d < D && n < N;
+        const int64_t dd = d < D ? d : D - 1;
+        const float Av = live ? A[dd * N + nn] : 0.f, a2 = Av * kLog2e;
+        const float dsk = Ds[dd];
+        // the first segment starts from zero, and nothing enters the last from
+        // the right (with one segment neither carry pass runs)
+        const int64_t so = ((b * nseg + p) * N + nn) * D + dd;
+        const float S = live && p > 0 ? hin[so] : 0.f;
+        const float Gh = live && p + 1 < nseg ? ghat[so] : 0.f;
+        const float *xr = Xs[0][dl], *dr = Xs[1][dl], *yr = Xs[2][dl];
+        // dx / ddelta: lane n == 0 of a live channel stores at its lane offset
+        // plus the row's; other lanes store at kOOB, and rows past the
+        // segment land past the resource's end: the range check drops both.
+        const rsrc_t rdx = make_rsrc(dx + row0, (int64_t)nrow * D * 4), rdd = make_rsrc(ddelta + row0, (int64_t)nrow * D * 4);
+        const uint32_t lxs = n == 0 && d < D ? (uint32_t)d * 4u : kOOB, stx = (uint32_t)D * 4u;
+        // h over the segment (the decays are formed again in the reverse
+        // walk: keeping them too would not fit the registers).  Steps past
+        // the sequence are staged as zeros, which leaves h, the adjoint
+        // sums and the dB / dC terms unchanged: neither walk branches on
+        // them, only the dx / ddelta stores are masked.
+        float hs[SB];
+        {
+            float h = S;
+#pragma unroll
+            for (int r = 0; r < SB; ++r) {
+                const float dlt = dr[r], xt = xr[r], bt = BCs[0][r][n];
+                h = exp2_fast(dlt * a2) * h + (dlt * xt) * bt;
+                hs[r] = h;
+                if (r % 4 == 3) __builtin_amdgcn_sched_barrier(0);   // bound the LDS reads in flight
+            }
+        }
+        // (a barrier: the tile is read again below, not kept in registers)
+        __syncthreads();
+        // The walk starts from the right adjoint with decay 1: padded steps
+        // (delta = dy = 0) pass it down unchanged to the last real step.
+        float G = Gh, dA = 0.f, dD = 0.f, anext = 1.f;
+#pragma unroll
+        for (int r = SB - 1; r >= 0; --r) {
+            const float dlt = dr[r], xt = xr[r], dyt = yr[r];
+            const float bt = BCs[0][r][n], ct = BCs[1][r][n];
+            G = ct * dyt + anext * G;
+            const float a = exp2_fast(dlt * a2);
+            anext = a;
+            const float hp = r > 0 ? hs[r - 1] : S;
+            const float ah = a * hp;
+            float sx = G * bt, sd = G * (Av * ah + bt * xt);
+            dA += G * dlt * ah;
+            dD += dyt * xt;
+            // (the empty asm keeps the sums step by step: left alone, the
+            // compiler sinks them past the walk and holds every step's terms)
+            asm volatile("" : "+v"(dA), "+v"(dD));
+            // sums over the row's 16 states
+            sx = dpp_add<kRowRor + 8>(sx);
+            sx = dpp_add<kRowRor + 4>(sx);
+            sx = dpp_add<kRowRor + 2>(sx);
+            sx = dpp_add<kRowRor + 1>(sx);
+            sd = dpp_add<kRowRor + 8>(sd);
+            sd = dpp_add<kRowRor + 4>(sd);
+            sd = dpp_add<kRowRor + 2>(sd);
+            sd = dpp_add<kRowRor + 1>(sd);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(dsk * dyt + dlt * sx), rdx, lxs + (uint32_t)r * stx, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(sd), rdd, lxs + (uint32_t)r * stx, 0, 0);
+            Tw[r % WIN][0][tid] = G * (dlt * xt);
+            Tw[r % WIN][1][tid] = dyt * hs[r];
+            if (r % 2 == 0) __builtin_amdgcn_sched_barrier(0);
+            if (r % WIN == 0) {
+                // the window's steps r .. r + WIN - 1: sum each (step, which, n)
+                // over the block's BD channels, two threads per column
+                static_assert(BT == 2 * WIN * 2 * NS, "two threads per column");
+                __syncthreads();
+                const int col = tid / 2, part = tid % 2;   // WIN x 2 x NS columns
+                const int w = col / (2 * NS), which = (col / NS) % 2, cn = col % NS;
+                float s = 0.f;
+#pragma unroll
+                for (int q = 0; q < BD / 2; ++q) s += Tw[w][which][(part * (BD / 2) + q) * NS + cn];
+                s = dpp_add<kQuadXor1>(s);   // lanes 2c and 2c + 1 hold one column's halves
+                if (part == 0 && r + w < nrow) acc[r + w][which][cn] += s;
+                __syncthreads();
+            }
+        }
+        if (live) dApart[((b * nseg + p) * D + d) * N + n] = dA;
+        if (n == 0 && d < D) dDpart[(b * nseg + p) * D + d] = dD;
+        if (more) {   // every read of this chunk's tile is behind the last window's barrier
+            put();
+            __syncthreads();
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < nrow * 2 * NS; i += BT) {
+        const int r = i / (2 * NS), which = (i / NS) % 2, m = i % NS;
+        if (m >= N) continue;
+        const float v = acc[r][which][m];
+        const int64_t row = b * L + t0 + r;
+        if (nsplit == 1) (which ? dC : dB)[row * N + m] = v;
+        else dBCp[((blockIdx.x * (int64_t)gridDim.z * L + row) * 2 + which) * N + m] = v;
+    }
+}
+
+// 4. fixed-order sums.  Element i of [dA (D N) | dDskip (D) | dB, dC rows
+// (B L 2 N, only with nsplit > 1)] is the sum of Q partials M apart (Q = B
+// nseg for dA and dDskip, nsplit for dB / dC).  A block takes WE elements x
+// WQ slices; slice s adds partials s, s + WQ, ... in four chains, and the
+// first slice adds the WQ slice sums in order: the order depends on the
+// shape only.
+constexpr int WE = 64, WQ = 16;
+__global__ __launch_bounds__(WE *WQ) void k_mamba_wsum(const float *__restrict__ dApart,
+                                                      const float *__restrict__ dDpart,
+                                                      const float *__restrict__ dBCp, float *__restrict__ dA,
+                                                      float *__restrict__ dD, float *__restrict__ dB,
+                                                      float *__restrict__ dC, int64_t B, int64_t L, int64_t D,
+                                                      int N, int64_t nseg, int nsplit)
+{
+    __shared__ float part[WQ][WE];
+    const int e = threadIdx.x % WE, s = threadIdx.x / WE;
+    const int64_t i = (int64_t)blockIdx.x * WE + e;
+    const int64_t nA = D * N, nD = D, nBC = nsplit > 1 ? B * L * 2 * N : 0;
+    const float *src = dApart;
+    int64_t Q = 0, M = 1, k = 0;
+    if (i < nA) {
+        Q = B * nseg, M = nA, k = i;
+    } else if (i < nA + nD) {
+        src = dDpart, Q = B * nseg, M = nD, k = i - nA;
+    } else if (i < nA + nD + nBC) {
+        src = dBCp, Q = nsplit, M = nBC, k = i - nA - nD;
+    }
+    float c0 = 0.f, c1 = 0.f, c2 = 0.f, c3 = 0.f;
+    int64_t q = s;
+    for (; q + 3 * WQ < Q; q += 4 * WQ) {
+        c0 += src[q * M + k];
+        c1 += src[(q + WQ) * M + k];
+        c2 += src[(q + 2 * WQ) * M + k];
+        c3 += src[(q + 3 * WQ) * M + k];
+    }
+    for (; q < Q; q += WQ) c0 += src[q * M + k];
+    part[s][e] = (c0 + c1) + (c2 + c3);
+    __syncthreads();
+    if (s != 0) return;
+    float t = 0.f;
+#pragma unroll
+    for (int u = 0; u < WQ; ++u) t += part[u][e];
+    if (i < nA) {
+        dA[i] = t;
+    } else if (i < nA + nD) {
+        dD[i - nA] = t;
+    } else if (i < nA + nD + nBC) {
+        const int64_t row = k / (2 * N), which = (k / N) % 2, m = k % N;
+        (which ? dC : dB)[row * N + m] = t;
+    }
+}
+
 }  // namespace ssd
 
 using namespace ssd;
@@ -239,5 +632,66 @@ extern "C" int mamba_fwd(const mamba_shape *shape, const float *x, const float *
         if (launch_status() != SSD_OK) return SSD_ERR_DEVICE;
     }
     pass(BoolC<true>{});
+    return launch_status();
+}
+
+extern "C" int mamba_bwd(const mamba_shape *shape, const float *x, const float *delta, const float *A,
+                         const float *Bm, const float *Cm, const float *Ds, const float *dy, float *dx,
+                         float *ddelta, float *dA, float *dB, float *dC, float *dD, void *workspace,
+                         size_t workspace_bytes, void *stream)
+{
+    int rc = mamba_check_shape(shape);
+    if (rc != SSD_OK) return rc;
+    const mamba_shape &s = *shape;
+    if (s.L > 65535 * kMambaBwdSeg) return SSD_ERR_UNSUPPORTED;
+    if (!dA || !dD) return SSD_ERR_NULL;   // dA, dDskip have elements even when B or L is 0
+    const MambaBwdPlan P = mamba_bwd_plan(shape, device_cus());
+    const bool work = s.B > 0 && s.L > 0;
+    if (work && (!x || !delta || !A || !Bm || !Cm || !Ds || !dy || !dx || !ddelta || !dB || !dC))
+        return SSD_ERR_NULL;
+    const void *ptrs[] = {x, delta, A, Bm, Cm, Ds, dy, dx, ddelta, dA, dB, dC, dD};
+    for (const void *q : ptrs)
+        if ((reinterpret_cast<uintptr_t>(q) & 3u) != 0) return SSD_ERR_ALIGN;
+    if (workspace_bytes < P.total) return SSD_ERR_WORKSPACE;
+    if (P.total > 0) {
+        if (!workspace) return SSD_ERR_NULL;
+        if (!aligned16(workspace)) return SSD_ERR_ALIGN;
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    char *w = static_cast<char *>(workspace);
+    float *hend = reinterpret_cast<float *>(w + P.hend), *sdl = reinterpret_cast<float *>(w + P.sdl);
+    float *gl = reinterpret_cast<float *>(w + P.gl), *dAp = reinterpret_cast<float *>(w + P.dApart);
+    float *dDp = reinterpret_cast<float *>(w + P.dDpart), *dBCp = reinterpret_cast<float *>(w + P.dBC);
+    const int N = (int)s.N;
+    const int64_t nseg = P.nseg;
+    if (work) {
+        // 1. every segment from zero, both ways
+        const dim3 g1((unsigned)((s.D + MB - 1) / MB), (unsigned)nseg, (unsigned)s.B);
+        if (N == MNS)
+            launch(nullptr, -1, k_mamba_seg_ends<true>, g1, dim3(MB), st, x, delta, A, Bm, Cm, dy, hend, sdl, gl, s.L,
+                   s.D, N, nseg);
+        else
+            launch(nullptr, -1, k_mamba_seg_ends<false>, g1, dim3(MB), st, x, delta, A, Bm, Cm, dy, hend, sdl, gl,
+                   s.L, s.D, N, nseg);
+        if (launch_status() != SSD_OK) return SSD_ERR_DEVICE;
+        // 2. the state entering every segment, and the adjoint entering it from the right
+        if (nseg > 1) {
+            const dim3 g2((unsigned)((s.D + CD - 1) / CD), (unsigned)N, (unsigned)s.B);
+            launch(nullptr, -1, k_mamba_carry, g2, dim3(CJ * CD), st, A, hend, (const float *)sdl, s.D, N, nseg);
+            if (launch_status() != SSD_OK) return SSD_ERR_DEVICE;
+            launch(nullptr, -1, k_mamba_rcarry, g2, dim3(CJ * CD), st, delta, A, (const float *)sdl, gl, s.L, s.D, N,
+                   nseg);
+            if (launch_status() != SSD_OK) return SSD_ERR_DEVICE;
+        }
+        // 3. the gradients of every segment
+        launch(nullptr, -1, k_mamba_bwd_seg, dim3((unsigned)P.nsplit, (unsigned)nseg, (unsigned)s.B), dim3(BT), st,
+               x, delta, A, Bm, Cm, Ds, dy, (const float *)hend, (const float *)gl, dx, ddelta, dB, dC, dBCp, dAp, dDp,
+               s.L, s.D, N, nseg, P.nsplit);
+        if (launch_status() != SSD_OK) return SSD_ERR_DEVICE;
+    }
+    // 4. fixed-order sums (dA, dDskip are zero when B or L is 0)
+    const int64_t tot = s.D * s.N + s.D + (P.nsplit > 1 ? s.B * s.L * 2 * s.N : 0);
+    launch(nullptr, -1, k_mamba_wsum, dim3((unsigned)((tot + WE - 1) / WE)), dim3(WE * WQ), st, (const float *)dAp,
+           (const float *)dDp, (const float *)dBCp, dA, dD, dB, dC, s.B, s.L, s.D, N, work ? nseg : 0, P.nsplit);
     return launch_status();
 }

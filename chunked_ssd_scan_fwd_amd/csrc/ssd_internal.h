@@ -136,6 +136,20 @@ struct MambaPlan {
     size_t hend = 0, sdl = 0, total = 0;
 };
 MambaPlan mamba_plan(const mamba_shape *s, int cus);
+// The backward cuts the sequence into segments of kMambaBwdSeg steps (their
+// states are held in registers) and splits each segment's channel chunks of
+// kMambaBwdChans over nsplit blocks.  Byte offsets: forward end / entering states
+// [B][nseg][N][D], summed deltas [B][nseg][D], adjoints entering from the
+// right [B][nseg][D][N], dA partials [B][nseg][D][N], dDskip partials
+// [B][nseg][D], and with nsplit > 1 the dB / dC partials [nsplit][B][L][2][N].
+constexpr int kMambaBwdSeg = 32;
+constexpr int kMambaBwdChans = 32;
+struct MambaBwdPlan {
+    int64_t nseg = 0;
+    int nsplit = 1;
+    size_t hend = 0, sdl = 0, gl = 0, dApart = 0, dDpart = 0, dBC = 0, total = 0;
+};
+MambaBwdPlan mamba_bwd_plan(const mamba_shape *s, int cus);
 
 // Padded MFMA tile width (32, 64 or 128) for dk / dv in 1..128.
 inline int pad_dim(int64_t d) { return d <= 32 ? 32 : (d <= 64 ? 64 : 128); }

@@ -99,6 +99,34 @@ MambaPlan mamba_plan(const mamba_shape *s, int cus)
     return P;
 }
 
+MambaBwdPlan mamba_bwd_plan(const mamba_shape *s, int cus)
+{
+    MambaBwdPlan P;
+    if (s->B == 0 || s->L == 0) return P;
+    P.nseg = (s->L + kMambaBwdSeg - 1) / kMambaBwdSeg;
+    const int64_t nchunk = (s->D + kMambaBwdChans - 1) / kMambaBwdChans;
+    int64_t want = (2 * int64_t(cus) + P.nseg * s->B - 1) / (P.nseg * s->B);
+    if (want > nchunk) want = nchunk;
+    if (want < 1) want = 1;
+    P.nsplit = (int)want;
+    const size_t B = size_t(s->B), ns = size_t(P.nseg), N = size_t(s->N), D = size_t(s->D), f = sizeof(float);
+    size_t o = 0;
+    P.hend = o;
+    o = round_up(o + B * ns * N * D * f, 256);
+    P.sdl = o;
+    o = round_up(o + B * ns * D * f, 256);
+    P.gl = o;
+    o = round_up(o + B * ns * D * N * f, 256);
+    P.dApart = o;
+    o = round_up(o + B * ns * D * N * f, 256);
+    P.dDpart = o;
+    o = round_up(o + B * ns * D * f, 256);
+    P.dBC = o;
+    if (P.nsplit > 1) o = round_up(o + size_t(P.nsplit) * B * size_t(s->L) * 2 * N * f, 256);
+    P.total = o;
+    return P;
+}
+
 int fwd_chunk_setting()
 {
     const char *e = std::getenv("SSD_FWD_CHUNK");
@@ -289,6 +317,12 @@ size_t mamba_fwd_workspace_size(const mamba_shape *shape)
 {
     if (ssd::mamba_check_shape(shape) != SSD_OK) return 0;
     return ssd::mamba_plan(shape, ssd::device_cus()).total;
+}
+
+size_t mamba_bwd_workspace_size(const mamba_shape *shape)
+{
+    if (ssd::mamba_check_shape(shape) != SSD_OK || shape->L > 65535 * ssd::kMambaBwdSeg) return 0;
+    return ssd::mamba_bwd_plan(shape, ssd::device_cus()).total;
 }
 
 int ssd_fwd_state_stride(const ssd_shape *shape)

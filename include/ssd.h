@@ -319,6 +319,24 @@ int mamba_fwd(const mamba_shape *shape,
               float *y,
               void *workspace, size_t workspace_bytes, void *stream);
 
+/* Workspace bytes mamba_bwd needs (0 for an invalid shape or one it
+ * refuses, and when B or L is 0). */
+size_t mamba_bwd_workspace_size(const mamba_shape *shape);
+
+/* The gradients of L = sum dy . y with respect to every argument, the six
+ * outputs of the page's fwd_bwd records: dx, ddelta [B,L,D], dA [D,N],
+ * dB, dC [B,L,N], dDskip [D], all overwritten (dA and dDskip are zero when
+ * B or L is 0; they are the sums over batch and steps, taken in a fixed
+ * order).  Stateless: the forward's states are recomputed.  L above
+ * 65535 * 32 returns SSD_ERR_UNSUPPORTED.  Arguments, checks, ownership and
+ * asynchrony as for mamba_fwd; the workspace is mamba_bwd_workspace_size
+ * bytes. */
+int mamba_bwd(const mamba_shape *shape,
+              const float *x, const float *delta, const float *A,
+              const float *B, const float *C, const float *Dskip, const float *dy,
+              float *dx, float *ddelta, float *dA, float *dB, float *dC, float *dDskip,
+              void *workspace, size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

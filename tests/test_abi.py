@@ -395,3 +395,43 @@ def test_mamba_workspace_formula():
         ns = plan(B, L, D)
         want = 0 if ns == 1 else up(B * ns * N * D * 4) + up(B * ns * D * 4)
         assert ssd.mamba_workspace_size(ssd.MambaShapeArg(B, L, D, N)) == want, (B, L, D, N)
+
+
+def _mamba_bwd_call(shape, ptr=0x1000, ws_bytes=0, ws=None):
+    lib = ssd.library()
+    p = ctypes.c_void_p(ptr) if ptr else None
+    w = ctypes.c_void_p(ws) if ws else p
+    return lib.mamba_bwd(ctypes.byref(shape), *([p] * 13), w, ws_bytes, None)
+
+
+def test_mamba_bwd_validation_before_launch():
+    lib = ssd.library()
+    assert lib.mamba_bwd(None, *([None] * 13), None, 0, None) == 1
+    for bad, code in [(ssd.MambaShapeArg(1, 10, 4, 17), 3), (ssd.MambaShapeArg(1, 10, 0, 16), 2),
+                      (ssd.MambaShapeArg(1, 65535 * 32 + 1, 4, 16), 3)]:   # backward segments beyond the grid
+        assert _mamba_bwd_call(bad) == code
+        assert lib.mamba_bwd_workspace_size(ctypes.byref(bad)) == 0
+    s = ssd.MambaShapeArg(2, 4096, 64, 16)
+    need = ssd.mamba_workspace_size(s, backward=True)
+    assert need > 0
+    assert _mamba_bwd_call(s, ptr=0) == 1                          # null tensors
+    assert _mamba_bwd_call(s, ptr=0x1002) == 5                     # misaligned
+    assert _mamba_bwd_call(s, ptr=0x1000, ws_bytes=need - 1) == 4  # short workspace
+    assert _mamba_bwd_call(s, ptr=0x1000, ws_bytes=need, ws=0x1004) == 5   # workspace not 16-byte aligned
+
+
+def test_mamba_bwd_workspace_formula():
+    """Segments of 32 steps; forward entering states [B][nseg][N][D], summed
+    deltas [B][nseg][D], adjoints entering from the right and dA partials
+    [B][nseg][D][N], dDskip partials [B][nseg][D], and with nsplit > 1 the
+    dB / dC partials [nsplit][B][L][2][N]; nsplit = min(channel chunks of 32,
+    ceil(2 CUs / (nseg B))), 256 CUs when no device is visible."""
+    up = lambda x: (x + 255) // 256 * 256
+    for B, L, D, N in [(4, 8192, 1024, 16), (4, 512, 256, 16), (1, 100, 3, 5), (2, 7, 64, 16), (1, 70000, 1, 1)]:
+        ns = -(-L // 32)
+        split = max(1, min(-(-D // 32), -(-2 * 256 // (ns * B))))
+        want = up(B * ns * N * D * 4) + up(B * ns * D * 4) + 2 * up(B * ns * D * N * 4) + up(B * ns * D * 4)
+        if split > 1:
+            want += up(split * B * L * 2 * N * 4)
+        assert ssd.mamba_workspace_size(ssd.MambaShapeArg(B, L, D, N), backward=True) == want, (B, L, D, N)
+    assert ssd.mamba_workspace_size(ssd.MambaShapeArg(0, 10, 4, 16), backward=True) == 0

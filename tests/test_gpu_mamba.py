@@ -97,3 +97,67 @@ def test_mamba_empty_and_refused():
     assert need > 0
     with pytest.raises(ValueError):
         _fwd(d, workspace=torch.empty(need - 1, dtype=torch.uint8, device="cuda"))
+
+
+TOL_G = 5e-5
+GRADS = ("dx", "ddelta", "dA", "dB", "dC", "dD")
+
+
+def _bwd(d, **kw):
+    import chunked_ssd_scan_fwd_amd as ssd
+    return ssd.mamba_bwd(*(d[k] for k in ARGS), d["dy"], **kw)
+
+
+def _check_bwd(shape, seed, scale=1.0):
+    inp = make_mamba_inputs(shape, seed=seed)
+    if scale != 1.0:
+        inp["delta"] = (inp["delta"] * scale).astype(np.float32)
+    g = [host(t) for t in _bwd(_dev(inp))]
+    ref = mo.bwd(*(inp[k] for k in ARGS), inp["dy"])
+    errs = {k: rel_err(a, ref[k]) for a, k in zip(g, GRADS)}
+    bad = {k: e for k, e in errs.items() if not e <= TOL_G}
+    assert not bad, f"gradient rel_err over bar: {bad}"
+
+
+# one step, one channel, fewer states than 16, channels not a multiple of the
+# 32-channel block, a ragged last segment, several channel splits per segment
+BWD_SHAPES = [MambaShape(1, 1, 3, 16), MambaShape(1, 9, 1, 1), MambaShape(3, 77, 5, 7), MambaShape(2, 1000, 100, 16),
+              MambaShape(2, 4096, 64, 16), MambaShape(1, 3001, 300, 11), MambaShape(4, 512, 256, 16),
+              MambaShape(4, 2048, 512, 16)]
+
+
+@pytest.mark.parametrize("shape", BWD_SHAPES, ids=_id)
+def test_mamba_backward(shape):
+    need_gpu()
+    say(f"mamba bwd {_id(shape)}")
+    _check_bwd(shape, seed=shape.L + 3 * shape.D)
+
+
+def test_mamba_backward_page_largest():
+    need_gpu()
+    s = MAMBA_GRID[(1024, 8192)]
+    say(f"mamba bwd {_id(s)}")
+    _check_bwd(s, seed=78)
+
+
+def test_mamba_backward_strong_and_weak_decay():
+    need_gpu()
+    s = MambaShape(2, 2000, 128, 16)
+    for scale in (0.01, 20.0):
+        say(f"mamba bwd decay scale {scale}")
+        _check_bwd(s, seed=4, scale=scale)
+
+
+def test_mamba_backward_deterministic_and_empty():
+    need_gpu()
+    import torch
+    say("mamba bwd determinism / empty")
+    s = MambaShape(2, 3000, 256, 16)
+    d = _dev(make_mamba_inputs(s, 6))
+    g1 = [host(t) for t in _bwd(d)]
+    g2 = [host(t) for t in _bwd(d)]
+    for a, b in zip(g1, g2):
+        np.testing.assert_array_equal(a, b)
+    for e in (MambaShape(0, 10, 4, 16), MambaShape(2, 0, 4, 16)):
+        g = [host(t) for t in _bwd(_dev(make_mamba_inputs(e, 1)))]
+        assert not np.any(g[2]) and not np.any(g[5])   # dA and dDskip are zero

@@ -260,25 +260,29 @@ def grid_sweep(args, torch, ssd):
 # (b, t, d) and state n the recurrence takes one exponential and three
 # single-rate operations (the exponent's product, the input's product, the
 # multiply-add into the state) and the output one more multiply-add.  An
-# exponential issues at a quarter of the fp32 rate, so the work is
-# N (4 + 4) lane slots per element against 256 CUs x 4 SIMDs x 16 lanes x
+# exponential costs two fp32 issue slots: the probe in device_facts measures
+# its throughput at half that of v_fma_f32 on this chip.  So the work is
+# N (4 + 2) lane slots per element against 256 CUs x 4 SIMDs x 16 lanes x
 # 2.4 GHz; the bytes are the inputs and y.
+EXP_SLOTS = 2
 PEAK_VALU_SLOTS = 256 * 4 * 16 * 2.4e9
 
 
 def mamba_work(s, backward=False):
-    """(lane slots, bytes) of the least work: the forward's N (4 + 4) slots
-    per element, and for fwd_bwd N 13 more -- one exponential (4) for the
-    decay, shared by the recomputed state and the adjoint, and nine
-    multiply-adds (the state, the adjoint, dx, ddelta 2, dA 2, dB, dC); the
-    bytes are every argument read once and every result written once."""
+    """(lane slots, bytes) of the least work: the forward's N (4 + 2) slots
+    per element, and for fwd_bwd N 14 more -- one exponential (2) and its
+    exponent's product for the decay, shared by the recomputed state and the
+    adjoint, and eleven single-rate operations (the state's 2, the
+    adjoint's 2, dx, ddelta 2, dA 2, dB, dC); the bytes are every argument
+    read once and every result written once."""
     elems, bln, dn = s.B * s.L * s.D, s.B * s.L * s.N, s.D * s.N
+    fwd_slots = 4 + EXP_SLOTS
     if not backward:
-        return elems * s.N * 8, 4 * (3 * elems + 2 * bln + dn + s.D)
+        return elems * s.N * fwd_slots, 4 * (3 * elems + 2 * bln + dn + s.D)
     # fwd: x, delta, B, C, A, Dskip in, y out; bwd: those and dy in, six gradients out
     io_f = 4 * (3 * elems + 2 * bln + dn + s.D)
     io_b = 4 * (3 * elems + 2 * bln + dn + s.D) + 4 * (2 * elems + 2 * bln + dn + s.D)
-    return elems * s.N * (8 + 13), io_f + io_b
+    return elems * s.N * (fwd_slots + 1 + EXP_SLOTS + 11), io_f + io_b
 
 
 def mamba_sweep(args, torch, ssd, points=None):
@@ -470,6 +474,30 @@ def device_facts(torch):
                         "shader_clock_mhz": mhz, "blocks": blocks, "waves_per_cu": 4,
                         "note": "independent v_mfma_f32_32x32x2f32 chains on every SIMD; clock = shader-clock "
                                 "counter over the real-time counter during the loop"}
+    # lane-operation rates of fp32 multiply-adds and of exponentials (8 waves per SIMD)
+    lib.probe_valu_loop_bytes.argtypes = [ctypes.c_int]
+    lib.probe_valu_loop_bytes.restype = ctypes.c_size_t
+    lib.probe_valu_loop.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.probe_valu_loop.restype = ctypes.c_int
+    lib.probe_valu_chains.restype = ctypes.c_int
+    vblocks, viters = cus * 8, 4096
+    vbuf = torch.empty(int(lib.probe_valu_loop_bytes(vblocks)), dtype=torch.uint8, device="cuda")
+    rates = {}
+    for mode, name in ((0, "fma"), (1, "exp")):
+        for _ in range(2):
+            if lib.probe_valu_loop(ctypes.c_void_p(vbuf.data_ptr()), vblocks, viters, mode, stream) != 0:
+                raise RuntimeError("probe_valu_loop failed")
+        e0.record()
+        for _ in range(3):
+            lib.probe_valu_loop(ctypes.c_void_p(vbuf.data_ptr()), vblocks, viters, mode, stream)
+        e1.record()
+        torch.cuda.synchronize()
+        ops = 3 * vblocks * 256 * viters * lib.probe_valu_chains()
+        rates[name] = ops / (e0.elapsed_time(e1) * 1e-3)
+    out["valu_loop"] = {"fma_tlane_ops": rates["fma"] / 1e12, "exp_tlane_ops": rates["exp"] / 1e12,
+                        "exp_cost_in_fma_slots": rates["fma"] / rates["exp"],
+                        "fma_frac_of_spec": rates["fma"] / PEAK_VALU_SLOTS,
+                        "note": "independent chains of v_fma_f32 or v_exp_f32, 8 waves per SIMD on every CU"}
     return out
 
 

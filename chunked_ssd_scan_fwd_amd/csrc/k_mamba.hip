@@ -225,7 +225,7 @@ __global__ __launch_bounds__(CJ *CD) void k_mamba_carry(const float *__restrict_
 namespace {
 constexpr int NS = MAMBA_MAX_STATE;   // states per channel (one lane each)
 constexpr int SB = kMambaBwdSeg;      // steps per backward segment
-constexpr int BD = kMambaBwdChans;    // channels per block in pass 3 (512 threads: 256 VGPRs)
+constexpr int BD = kMambaBwdChans;    // channels per block in pass 3 (512 threads)
 constexpr int BT = BD * NS;           // threads per block
 constexpr int WIN = 8;                // steps per dB / dC transpose window
 constexpr int XP = SB + 4;            // pitch of a channel's staged steps (16-byte rows)
@@ -378,7 +378,9 @@ __global__ __launch_bounds__(CJ *CD) void k_mamba_rcarry(const float *__restrict
 // NS states; it walks the channel chunks blockIdx.x, + gridDim.x, ... and adds
 // up dB, dC over all of them in LDS.  dBC: the segment's dB / dC rows
 // (nsplit == 1) or this split's partial rows [nsplit][B][L][2][N].  hin and
-// ghat are the entering states and right adjoints, [B][nseg][N][D].
+// ghat are the entering states and right adjoints, [B][nseg][N][D].  At most
+// 128 VGPRs (4 waves per SIMD), so that two blocks (54 KiB of LDS each)
+// share a CU.
 __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(4))) void k_mamba_bwd_seg(
     const float *__restrict__ x, const float *__restrict__ delta, const float *__restrict__ A,
     const float *__restrict__ Bm, const float *__restrict__ Cm, const float *__restrict__ Ds,

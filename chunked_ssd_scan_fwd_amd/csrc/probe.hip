@@ -1,7 +1,8 @@
 // Device probes for the benchmark (not part of the SSD ABI): the fp32 MFMA
 // rate that a loop of independent v_mfma_f32_32x32x2f32 chains reaches on
 // every SIMD of the chip, and the shader clock during that loop (the
-// shader-clock counter against the fixed-rate real-time counter).
+// shader-clock counter against the fixed-rate real-time counter); and the
+// lane-operation rates of fp32 multiply-adds and of exponentials.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -44,7 +45,47 @@ __global__ __launch_bounds__(256) void k_mfma_loop(float *__restrict__ sink, uin
     }
 }
 
+// Every thread runs `iters` rounds of kVChains independent chains of one
+// operation (MODE 0: multiply-add, MODE 1: base-2 exponential) and writes one
+// float of their sum to sink[blockIdx.x * 256 + threadIdx.x].
+constexpr int kVChains = 8;
+template <int MODE>
+__global__ __launch_bounds__(256) void k_valu_loop(float *__restrict__ sink, float c, float d, int iters)
+{
+    float x[kVChains];
+#pragma unroll
+    for (int i = 0; i < kVChains; ++i) x[i] = 1e-3f * (float)(threadIdx.x + i);
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int i = 0; i < kVChains; ++i) x[i] = MODE == 0 ? __builtin_fmaf(x[i], c, d) : __builtin_amdgcn_exp2f(x[i]);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < kVChains; ++i) s += x[i];
+    sink[(int64_t)blockIdx.x * 256 + threadIdx.x] = s;
+}
+
 extern "C" {
+
+// Bytes of device memory probe_valu_loop needs for `blocks` blocks.
+size_t probe_valu_loop_bytes(int blocks) { return (size_t)blocks * 256 * sizeof(float); }
+
+// Launches k_valu_loop<mode> (0: fma, 1: exp) on `blocks` blocks of 256
+// threads; lane operations per launch: blocks * 256 * iters *
+// probe_valu_chains().  Returns 0 or -1.
+int probe_valu_loop(void *buf, int blocks, int iters, int mode, void *stream)
+{
+    if (!buf || blocks < 1 || iters < 1 || mode < 0 || mode > 1) return -1;
+    float *sink = static_cast<float *>(buf);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (mode == 0)
+        hipLaunchKernelGGL(k_valu_loop<0>, dim3(blocks), dim3(256), 0, st, sink, 0.999f, 1e-4f, iters);
+    else
+        hipLaunchKernelGGL(k_valu_loop<1>, dim3(blocks), dim3(256), 0, st, sink, 0.999f, 1e-4f, iters);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int probe_valu_chains(void) { return kVChains; }
 
 // Bytes of device memory probe_mfma_loop needs for `blocks` blocks.
 size_t probe_mfma_loop_bytes(int blocks) { return (size_t)blocks * (256 * sizeof(float) + 4 * sizeof(uint64_t)); }

@@ -73,13 +73,16 @@ MambaPlan mamba_plan(const mamba_shape *s, int cus)
     MambaPlan P;
     P.seg_len = s->L;
     if (s->B == 0 || s->L == 0) return P;
-    // About 512 threads (8 waves) per CU over all segments, segments of at
-    // least 8 steps where that allows, at most kMambaMaxSeg steps, and at
-    // most 65535 of them (the launch grid's y extent).  More segments hide
-    // more latency in the scans but lengthen the carry pass's chain.
-    const int64_t want = (int64_t(cus) * 512 + s->B * s->D - 1) / (s->B * s->D);
+    // About 1024 threads (16 waves) per CU over all segments, segments of
+    // at least 16 steps where that allows, at most kMambaMaxSeg steps, and
+    // at most 65535 of them (the launch grid's y extent).  More segments
+    // hide more latency in the scans but lengthen the carry pass's chain;
+    // over the page's grid (batch 4, dim 256 to 1024, seq 512 to 8192) this
+    // choice was the fastest or within 2% of it among 512 to 4096 threads
+    // per CU and segments of 8 or 16 steps and up.
+    const int64_t want = (int64_t(cus) * 1024 + s->B * s->D - 1) / (s->B * s->D);
     int64_t nseg = want < 1 ? 1 : want;
-    const int64_t cap = s->L / 8 > 1 ? s->L / 8 : 1;
+    const int64_t cap = s->L / 16 > 1 ? s->L / 16 : 1;
     if (nseg > cap) nseg = cap;
     const int64_t least = (s->L + kMambaMaxSeg - 1) / kMambaMaxSeg;
     if (nseg < least) nseg = least;

@@ -382,11 +382,11 @@ def test_mamba_validation_before_launch():
 
 def test_mamba_workspace_formula():
     """Segment end states float [B][nseg][N][D] and summed deltas float
-    [B][nseg][D], each 256-byte aligned; about 512 threads per CU (256 CUs
-    when no device is visible), segments of 8 to 256 steps."""
+    [B][nseg][D], each 256-byte aligned; about 1024 threads per CU (256 CUs
+    when no device is visible), segments of 16 to 256 steps."""
     def plan(B, L, D):
-        nseg = max(1, -(-256 * 512 // (B * D)))
-        nseg = min(nseg, max(1, L // 8))
+        nseg = max(1, -(-256 * 1024 // (B * D)))
+        nseg = min(nseg, max(1, L // 16))
         nseg = max(nseg, -(-L // 256))
         sl = -(-L // nseg)
         return -(-L // sl)

@@ -288,7 +288,7 @@ def mamba_work(s, backward=False):
 def mamba_sweep(args, torch, ssd, points=None):
     """mamba_fwd (fwd) and mamba_fwd + mamba_bwd (fwd_bwd) at the points of
     kernel_mamba_cpu.json's grid (batch 4, state 16), timed by the pages'
-    protocol; the page's CPU medians of the forward go along as context."""
+    protocol; the page's CPU medians go along as context."""
     from ssd_workload.mamba import MAMBA_GRID, make_mamba_inputs
     out = []
     for (D, L), s in MAMBA_GRID.items():
@@ -541,6 +541,8 @@ def main():
     ap.add_argument("--max-len-cap", type=int, default=1 << 22, help="largest T the search tries")
     ap.add_argument("--grid", action="store_true",
                     help="only time fwd and fwd_bwd at every shape of the pages' grid, one JSON line each, and exit")
+    ap.add_argument("--mamba-point", default="",
+                    help="with --mamba: only this point of the grid, as DIM,SEQ (e.g. 1024,8192)")
     ap.add_argument("--mamba", action="store_true",
                     help="only time the selective (Mamba-style) scan at every point of its page's grid, one JSON "
                          "line each, and exit")
@@ -571,7 +573,10 @@ def main():
         max_len_search(args, torch, ssd)
         return
     if args.mamba:
-        for line in mamba_sweep(args, torch, ssd):
+        pts = None
+        if args.mamba_point:
+            pts = {tuple(int(v) for v in args.mamba_point.split(","))}
+        for line in mamba_sweep(args, torch, ssd, points=pts):
             print(json.dumps(line), flush=True)
         return
     if args.grid:

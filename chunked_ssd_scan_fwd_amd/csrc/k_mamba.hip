@@ -151,14 +151,16 @@ __global__ __launch_bounds__(MB) void k_mamba_scan(const float *__restrict__ x, 
 // each thread then walks its group again from the state entering it.  The
 // chain depth is 2 gs + CJ instead of nseg.
 constexpr int CJ = 16, CD = 64;
-__global__ __launch_bounds__(CJ *CD) void k_mamba_carry(const float *__restrict__ A, float *__restrict__ hend,
-                                                       const float *__restrict__ sdl, int64_t D, int N, int64_t nseg)
+struct CarryLds {
+    float G[CJ][CD], E[CJ][CD], S[CJ][CD];
+};
+__device__ __forceinline__ void carry_body(const float *__restrict__ A, float *__restrict__ hend,
+                                           const float *__restrict__ sdl, int64_t D, int N, int64_t nseg, int n,
+                                           int64_t b, CarryLds &sh)
 {
-    __shared__ float Gm[CJ][CD], Em[CJ][CD], Sin[CJ][CD];
+    auto &Gm = sh.G, &Em = sh.E, &Sin = sh.S;
     const int dl = threadIdx.x % CD, j = threadIdx.x / CD;
     const int64_t d = (int64_t)blockIdx.x * CD + dl;
-    const int n = blockIdx.y;
-    const int64_t b = blockIdx.z;
     const bool live = d < D;
     const int64_t dd = live ? d : 0;   // masked lanes read a valid address and store nothing
     const float a2 = A[dd * N + n] * kLog2e;
@@ -193,6 +195,13 @@ __global__ __launch_bounds__(CJ *CD) void k_mamba_carry(const float *__restrict_
     }
 }
 
+__global__ __launch_bounds__(CJ *CD) void k_mamba_carry(const float *__restrict__ A, float *__restrict__ hend,
+                                                       const float *__restrict__ sdl, int64_t D, int N, int64_t nseg)
+{
+    __shared__ CarryLds sh;
+    carry_body(A, hend, sdl, D, N, nseg, blockIdx.y, blockIdx.z, sh);
+}
+
 
 // ---- backward
 //
@@ -207,30 +216,33 @@ __global__ __launch_bounds__(CJ *CD) void k_mamba_carry(const float *__restrict_
 //   1. k_mamba_seg_ends: per segment, the forward from a zero state (its end
 //      state and summed delta) and the adjoint from zero at its end (the
 //      adjoint at its first step); one thread per (b, d) as in the forward;
-//   2. k_mamba_carry (the forward's) and k_mamba_rcarry: the state entering
-//      every segment from the left, and the adjoint entering it from the
-//      right, a_{t1} G_{t1};
+//   2. k_mamba_carries, one launch: the forward's carry (the state entering
+//      every segment from the left) and the reverse one (the adjoint entering
+//      it from the right, a_{t1} G_{t1});
 //   3. k_mamba_bwd_seg: per segment, h over its steps again (kept in
 //      registers), then the steps in reverse with the true adjoint: dx and
-//      ddelta (sums over n inside a 16-lane row), dB and dC (sums over the
+//      ddelta (sums over n in the lane and over the channel's 8 lanes), dB and dC (sums over the
 //      block's channels through an LDS transpose, the block walking all
 //      channel chunks of its segment), dA and dDskip per segment;
 //   4. k_mamba_wsum: dA and dDskip summed over batch and segments, and the
 //      dB / dC partials of blocks that split the channels, in fixed order.
-// Threads of pass 3 own one (b, d, n): lane n + 16 (d % 4), so a row of 16
-// lanes holds one channel's states.  The chunk's x, delta and dy (and the
+// Threads of pass 3 own two states of one (b, d): eight consecutive lanes
+// hold one channel's 16 states.  The chunk's x, delta and dy (and the
 // segment's B and C rows) are staged in LDS with coalesced loads, and each
 // row of lanes reads its channel's value there as a broadcast.
 
 namespace {
-constexpr int NS = MAMBA_MAX_STATE;   // states per channel (one lane each)
+constexpr int NS = MAMBA_MAX_STATE;   // states per channel
 constexpr int SB = kMambaBwdSeg;      // steps per backward segment
-constexpr int BD = kMambaBwdChans;    // channels per block in pass 3 (512 threads)
-constexpr int BT = BD * NS;           // threads per block
-constexpr int WIN = 8;                // steps per dB / dC transpose window
+constexpr int LPC = 8;                // lanes per channel in pass 3, two states each
+constexpr int BD = kMambaBwdChans;    // channels per block in pass 3
+constexpr int BT = BD * LPC;          // threads per block (512)
+constexpr int WIN = 4;                // steps per dB / dC transpose window
 constexpr int XP = SB + 4;            // pitch of a channel's staged steps (16-byte rows)
 constexpr int kQuadXor1 = 0xB1;       // DPP quad_perm [1,0,3,2]
-static_assert(SB % 4 == 0 && (SB * BD) % BT == 0, "tile shapes");
+constexpr int kQuadXor2 = 0x4E;       // DPP quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141; // DPP: lane i of each 8-lane half row reads lane 7 - i
+static_assert(SB % 4 == 0 && (SB * BD) % BT == 0 && 2 * LPC == NS, "tile shapes");
 }  // namespace
 
 // 1. per (b, segment, d): end state and summed delta from zero (h over the
@@ -326,16 +338,13 @@ __global__ __launch_bounds__(MB) void k_mamba_seg_ends(const float *__restrict__
 // delta_{t0(p)} + delta_{t0(p+1)})), walked from the last segment back; gl_p
 // is replaced by exp(A delta_{t0(p+1)}) Gf_{p+1} (0 for the last segment).
 // Two levels as in k_mamba_carry: CJ groups of gs segments per channel.
-__global__ __launch_bounds__(CJ *CD) void k_mamba_rcarry(const float *__restrict__ delta,
-                                                        const float *__restrict__ A, const float *__restrict__ sdl,
-                                                        float *__restrict__ gl, int64_t L, int64_t D, int N,
-                                                        int64_t nseg)
+__device__ __forceinline__ void rcarry_body(const float *__restrict__ delta, const float *__restrict__ A,
+                                            const float *__restrict__ sdl, float *__restrict__ gl, int64_t L,
+                                            int64_t D, int N, int64_t nseg, int n, int64_t b, CarryLds &sh)
 {
-    __shared__ float Fm[CJ][CD], Em[CJ][CD], Gs[CJ][CD];
+    auto &Fm = sh.G, &Em = sh.E, &Gs = sh.S;
     const int dl = threadIdx.x % CD, j = threadIdx.x / CD;
     const int64_t d = (int64_t)blockIdx.x * CD + dl;
-    const int n = blockIdx.y;
-    const int64_t b = blockIdx.z;
     const bool live = d < D;
     const int64_t dd = live ? d : 0;   // masked lanes read a valid address and store nothing
     const float a2 = A[dd * N + n] * kLog2e;
@@ -374,13 +383,27 @@ __global__ __launch_bounds__(CJ *CD) void k_mamba_rcarry(const float *__restrict
     }
 }
 
+// (both carries in one launch: they are independent chains, each bound by
+// its latency).  Grid y: states 0 .. N-1 run the forward carry, N .. 2N-1
+// the reverse one.
+__global__ __launch_bounds__(CJ *CD) void k_mamba_carries(const float *__restrict__ delta,
+                                                         const float *__restrict__ A, float *__restrict__ hend,
+                                                         const float *__restrict__ sdl, float *__restrict__ gl,
+                                                         int64_t L, int64_t D, int N, int64_t nseg)
+{
+    __shared__ CarryLds sh;
+    const int y = blockIdx.y;   // uniform
+    if (y < N) carry_body(A, hend, sdl, D, N, nseg, y, blockIdx.z, sh);
+    else rcarry_body(delta, A, sdl, gl, L, D, N, nseg, y - N, blockIdx.z, sh);
+}
+
 // 3. per (b, segment): gradients of the segment's steps.  Block = BD channels x
-// NS states; it walks the channel chunks blockIdx.x, + gridDim.x, ... and adds
-// up dB, dC over all of them in LDS.  dBC: the segment's dB / dC rows
-// (nsplit == 1) or this split's partial rows [nsplit][B][L][2][N].  hin and
-// ghat are the entering states and right adjoints, [B][nseg][N][D].  At most
-// 128 VGPRs (4 waves per SIMD), so that two blocks (54 KiB of LDS each)
-// share a CU.
+// LPC lanes; lane j of a channel's eight holds states 2j and 2j + 1.  The
+// block walks the channel chunks blockIdx.x, + gridDim.x, ... and adds up dB,
+// dC over all of them in LDS.  dBC: the segment's dB / dC rows (nsplit == 1)
+// or this split's partial rows [nsplit][B][L][2][N].  hin and ghat are the
+// entering states and right adjoints, [B][nseg][N][D].  At most 128 VGPRs
+// (4 waves per SIMD), so that two blocks (67 KiB of LDS each) share a CU.
 __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(4))) void k_mamba_bwd_seg(
     const float *__restrict__ x, const float *__restrict__ delta, const float *__restrict__ A,
     const float *__restrict__ Bm, const float *__restrict__ Cm, const float *__restrict__ Ds,
@@ -389,22 +412,21 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(4))) void k_
     float *__restrict__ dBCp, float *__restrict__ dApart, float *__restrict__ dDpart, int64_t L, int64_t D, int N,
     int64_t nseg, int nsplit)
 {
-    __shared__ float Tw[WIN][2][BT];                                  // one window of per-lane dB / dC terms
-    __shared__ float acc[SB][2][NS];                                  // the segment's dB / dC so far
-    __shared__ __attribute__((aligned(16))) float BCs[2][SB][NS];     // the segment's B, C rows
-    __shared__ __attribute__((aligned(16))) float Xs[3][BD][XP];      // the chunk's x, delta, dy by channel
-    const int tid = threadIdx.x, dl = tid / NS, n = tid % NS;
+    __shared__ __attribute__((aligned(16))) float Tw[WIN][2][BD][NS];   // one window of per-lane dB / dC terms
+    __shared__ float acc[SB][2][NS];                                    // the segment's dB / dC so far
+    __shared__ __attribute__((aligned(16))) float BCs[2][SB][NS];       // the segment's B, C rows
+    __shared__ __attribute__((aligned(16))) float Xs[3][BD][XP];        // the chunk's x, delta, dy by channel
+    const int tid = threadIdx.x, dl = tid / LPC, j = tid % LPC, n0 = 2 * j;
     const int64_t p = blockIdx.y, b = blockIdx.z;
     const int64_t t0 = p * SB, t1 = (t0 + SB) < L ? (t0 + SB) : L;
     const int nrow = (int)(t1 - t0);
-    const int nn = n < N ? n : N - 1;
     for (int i = tid; i < SB * 2 * NS; i += BT) (&acc[0][0][0])[i] = 0.f;
     for (int i = tid; i < 2 * SB * NS; i += BT) {
         const int w = i / (SB * NS), r = (i / NS) % SB, m = i % NS;
         (&BCs[0][0][0])[i] = r < nrow && m < N ? (w ? Cm : Bm)[(b * L + t0 + r) * N + m] : 0.f;
     }
     // Staging: element e = tid + k BT of a chunk's tile is step e / BD,
-    // channel e % BD (a wave loads two 128-byte rows); steps past the
+    // channel e % BD (a wave loads one 256-byte row); steps past the
     // sequence and channels past D are staged as 0.
     constexpr int KS = SB * BD / BT;
     const int64_t nchunk = (D + BD - 1) / BD;
@@ -436,36 +458,39 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(4))) void k_
     __syncthreads();
     for (int64_t c = blockIdx.x; c < nchunk; c += nsplit) {
         const bool more = c + nsplit < nchunk;   // uniform
-        if (more) fetch(c + nsplit);             // lands while this chunk computes
         const int64_t d = c * BD + dl;
-        const bool live = d < D && n < N;
-        const int64_t dd = d < D ? d : D - 1;
-        const float Av = live ? A[dd * N + nn] : 0.f, a2 = Av * kLog2e;
+        const bool dlive = d < D, live0 = dlive && n0 < N, live1 = dlive && n0 + 1 < N;
+        const int64_t dd = dlive ? d : D - 1;
+        const float Av0 = live0 ? A[dd * N + n0] : 0.f, Av1 = live1 ? A[dd * N + n0 + 1] : 0.f;
+        const float a20 = Av0 * kLog2e, a21 = Av1 * kLog2e;
         const float dsk = Ds[dd];
         // the first segment starts from zero, and nothing enters the last from
         // the right (with one segment neither carry pass runs)
-        const int64_t so = ((b * nseg + p) * N + nn) * D + dd;
-        const float S = live && p > 0 ? hin[so] : 0.f;
-        const float Gh = live && p + 1 < nseg ? ghat[so] : 0.f;
+        const int64_t so = ((b * nseg + p) * N + n0) * D + dd;   // state n0; n0 + 1 at so + D
+        const float S0 = live0 && p > 0 ? hin[so] : 0.f, S1 = live1 && p > 0 ? hin[so + D] : 0.f;
+        const float Gh0 = live0 && p + 1 < nseg ? ghat[so] : 0.f, Gh1 = live1 && p + 1 < nseg ? ghat[so + D] : 0.f;
         const float *xr = Xs[0][dl], *dr = Xs[1][dl], *yr = Xs[2][dl];
-        // dx / ddelta: lane n == 0 of a live channel stores at its lane offset
-        // plus the row's; other lanes store at kOOB, and rows past the
-        // segment land past the resource's end: the range check drops both.
+        // dx / ddelta: lane 0 of a live channel stores at its lane offset plus
+        // the row's; other lanes store at kOOB, and rows past the segment land
+        // past the resource's end: the range check drops both.
         const rsrc_t rdx = make_rsrc(dx + row0, (int64_t)nrow * D * 4), rdd = make_rsrc(ddelta + row0, (int64_t)nrow * D * 4);
-        const uint32_t lxs = n == 0 && d < D ? (uint32_t)d * 4u : kOOB, stx = (uint32_t)D * 4u;
+        const uint32_t lxs = j == 0 && dlive ? (uint32_t)d * 4u : kOOB, stx = (uint32_t)D * 4u;
         // h over the segment (the decays are formed again in the reverse
         // walk: keeping them too would not fit the registers).  Steps past
         // the sequence are staged as zeros, which leaves h, the adjoint
         // sums and the dB / dC terms unchanged: neither walk branches on
         // them, only the dx / ddelta stores are masked.
-        float hs[SB];
+        float hs0[SB], hs1[SB];
         {
-            float h = S;
+            float h0 = S0, h1 = S1;
 #pragma unroll
             for (int r = 0; r < SB; ++r) {
-                const float dlt = dr[r], xt = xr[r], bt = BCs[0][r][n];
-                h = exp2_fast(dlt * a2) * h + (dlt * xt) * bt;
-                hs[r] = h;
+                const float dlt = dr[r], u = dlt * xr[r];
+                const float2 bt = *reinterpret_cast<const float2 *>(&BCs[0][r][n0]);
+                h0 = exp2_fast(dlt * a20) * h0 + u * bt.x;
+                h1 = exp2_fast(dlt * a21) * h1 + u * bt.y;
+                hs0[r] = h0;
+                hs1[r] = h1;
                 if (r % 4 == 3) __builtin_amdgcn_sched_barrier(0);   // bound the LDS reads in flight
             }
         }
@@ -473,53 +498,66 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(4))) void k_
         __syncthreads();
         // The walk starts from the right adjoint with decay 1: padded steps
         // (delta = dy = 0) pass it down unchanged to the last real step.
-        float G = Gh, dA = 0.f, dD = 0.f, anext = 1.f;
+        float G0 = Gh0, G1 = Gh1, an0 = 1.f, an1 = 1.f, dA0 = 0.f, dA1 = 0.f, dD = 0.f;
 #pragma unroll
         for (int r = SB - 1; r >= 0; --r) {
             const float dlt = dr[r], xt = xr[r], dyt = yr[r];
-            const float bt = BCs[0][r][n], ct = BCs[1][r][n];
-            G = ct * dyt + anext * G;
-            const float a = exp2_fast(dlt * a2);
-            anext = a;
-            const float hp = r > 0 ? hs[r - 1] : S;
-            const float ah = a * hp;
-            float sx = G * bt, sd = G * (Av * ah + bt * xt);
-            dA += G * dlt * ah;
+            const float2 bt = *reinterpret_cast<const float2 *>(&BCs[0][r][n0]);
+            const float2 ct = *reinterpret_cast<const float2 *>(&BCs[1][r][n0]);
+            G0 = ct.x * dyt + an0 * G0;
+            G1 = ct.y * dyt + an1 * G1;
+            const float a0 = exp2_fast(dlt * a20), a1 = exp2_fast(dlt * a21);
+            an0 = a0;
+            an1 = a1;
+            const float ah0 = a0 * (r > 0 ? hs0[r - 1] : S0), ah1 = a1 * (r > 0 ? hs1[r - 1] : S1);
+            float sx = G0 * bt.x + G1 * bt.y;
+            float q = G0 * (Av0 * ah0) + G1 * (Av1 * ah1);
+            dA0 += G0 * dlt * ah0;
+            dA1 += G1 * dlt * ah1;
             dD += dyt * xt;
             // (the empty asm keeps the sums step by step: left alone, the
             // compiler sinks them past the walk and holds every step's terms)
-            asm volatile("" : "+v"(dA), "+v"(dD));
-            // sums over the row's 16 states
-            sx = dpp_add<kRowRor + 8>(sx);
-            sx = dpp_add<kRowRor + 4>(sx);
-            sx = dpp_add<kRowRor + 2>(sx);
-            sx = dpp_add<kRowRor + 1>(sx);
-            sd = dpp_add<kRowRor + 8>(sd);
-            sd = dpp_add<kRowRor + 4>(sd);
-            sd = dpp_add<kRowRor + 2>(sd);
-            sd = dpp_add<kRowRor + 1>(sd);
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(dsk * dyt + dlt * sx), rdx, lxs + (uint32_t)r * stx, 0, 0);
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(sd), rdd, lxs + (uint32_t)r * stx, 0, 0);
-            Tw[r % WIN][0][tid] = G * (dlt * xt);
-            Tw[r % WIN][1][tid] = dyt * hs[r];
+            asm volatile("" : "+v"(dA0), "+v"(dA1), "+v"(dD));
+            // sums over the channel's eight lanes
+            sx = dpp_add<kQuadXor1>(sx);
+            sx = dpp_add<kQuadXor2>(sx);
+            sx = dpp_add<kRowHalfMirror>(sx);
+            q = dpp_add<kQuadXor1>(q);
+            q = dpp_add<kQuadXor2>(q);
+            q = dpp_add<kRowHalfMirror>(q);
+            const uint32_t o = lxs + (uint32_t)r * stx;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(dsk * dyt + dlt * sx), rdx, o, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(q + xt * sx), rdd, o, 0, 0);
+            const float u = dlt * xt;
+            *reinterpret_cast<float2 *>(&Tw[r % WIN][0][dl][n0]) = make_float2(G0 * u, G1 * u);
+            *reinterpret_cast<float2 *>(&Tw[r % WIN][1][dl][n0]) = make_float2(dyt * hs0[r], dyt * hs1[r]);
             if (r % 2 == 0) __builtin_amdgcn_sched_barrier(0);
             if (r % WIN == 0) {
                 // the window's steps r .. r + WIN - 1: sum each (step, which, n)
-                // over the block's BD channels, two threads per column
-                static_assert(BT == 2 * WIN * 2 * NS, "two threads per column");
+                // over the block's BD channels, four threads per column, each
+                // over every fourth channel
+                static_assert(BT == 4 * WIN * 2 * NS, "four threads per column");
                 __syncthreads();
-                const int col = tid / 2, part = tid % 2;   // WIN x 2 x NS columns
+                const int col = tid / 4, part = tid % 4;   // WIN x 2 x NS columns
                 const int w = col / (2 * NS), which = (col / NS) % 2, cn = col % NS;
                 float s = 0.f;
 #pragma unroll
-                for (int q = 0; q < BD / 2; ++q) s += Tw[w][which][(part * (BD / 2) + q) * NS + cn];
-                s = dpp_add<kQuadXor1>(s);   // lanes 2c and 2c + 1 hold one column's halves
+                for (int k = 0; k < BD / 4; ++k) s += Tw[w][which][4 * k + part][cn];
+                s = dpp_add<kQuadXor1>(s);   // lanes 4c .. 4c + 3 hold one column's quarters
+                s = dpp_add<kQuadXor2>(s);
                 if (part == 0 && r + w < nrow) acc[r + w][which][cn] += s;
                 __syncthreads();
             }
+            // The next chunk's tile is loaded halfway through the walk, when
+            // the later steps' states no longer hold registers; it lands while
+            // the rest of the walk computes (with no next chunk, this one's
+            // tile is loaded again and not used).
+            if (r == SB / 2) fetch(more ? c + nsplit : c);
         }
-        if (live) dApart[((b * nseg + p) * D + d) * N + n] = dA;
-        if (n == 0 && d < D) dDpart[(b * nseg + p) * D + d] = dD;
+        const int64_t ao = ((b * nseg + p) * D + d) * N + n0;
+        if (live0) dApart[ao] = dA0;
+        if (live1) dApart[ao + 1] = dA1;
+        if (j == 0 && dlive) dDpart[(b * nseg + p) * D + d] = dD;
         if (more) {   // every read of this chunk's tile is behind the last window's barrier
             put();
             __syncthreads();
@@ -678,11 +716,9 @@ extern "C" int mamba_bwd(const mamba_shape *shape, const float *x, const float *
         if (launch_status() != SSD_OK) return SSD_ERR_DEVICE;
         // 2. the state entering every segment, and the adjoint entering it from the right
         if (nseg > 1) {
-            const dim3 g2((unsigned)((s.D + CD - 1) / CD), (unsigned)N, (unsigned)s.B);
-            launch(nullptr, -1, k_mamba_carry, g2, dim3(CJ * CD), st, A, hend, (const float *)sdl, s.D, N, nseg);
-            if (launch_status() != SSD_OK) return SSD_ERR_DEVICE;
-            launch(nullptr, -1, k_mamba_rcarry, g2, dim3(CJ * CD), st, delta, A, (const float *)sdl, gl, s.L, s.D, N,
-                   nseg);
+            const dim3 g2((unsigned)((s.D + CD - 1) / CD), (unsigned)(2 * N), (unsigned)s.B);
+            launch(nullptr, -1, k_mamba_carries, g2, dim3(CJ * CD), st, delta, A, hend, (const float *)sdl, gl, s.L,
+                   s.D, N, nseg);
             if (launch_status() != SSD_OK) return SSD_ERR_DEVICE;
         }
         // 3. the gradients of every segment

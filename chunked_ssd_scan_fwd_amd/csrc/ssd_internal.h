@@ -143,7 +143,7 @@ MambaPlan mamba_plan(const mamba_shape *s, int cus);
 // right [B][nseg][D][N], dA partials [B][nseg][D][N], dDskip partials
 // [B][nseg][D], and with nsplit > 1 the dB / dC partials [nsplit][B][L][2][N].
 constexpr int kMambaBwdSeg = 32;
-constexpr int kMambaBwdChans = 32;
+constexpr int kMambaBwdChans = 64;
 struct MambaBwdPlan {
     int64_t nseg = 0;
     int nsplit = 1;

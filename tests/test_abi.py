@@ -424,12 +424,12 @@ def test_mamba_bwd_workspace_formula():
     """Segments of 32 steps; forward entering states [B][nseg][N][D], summed
     deltas [B][nseg][D], adjoints entering from the right and dA partials
     [B][nseg][D][N], dDskip partials [B][nseg][D], and with nsplit > 1 the
-    dB / dC partials [nsplit][B][L][2][N]; nsplit = min(channel chunks of 32,
+    dB / dC partials [nsplit][B][L][2][N]; nsplit = min(channel chunks of 64,
     ceil(2 CUs / (nseg B))), 256 CUs when no device is visible."""
     up = lambda x: (x + 255) // 256 * 256
     for B, L, D, N in [(4, 8192, 1024, 16), (4, 512, 256, 16), (1, 100, 3, 5), (2, 7, 64, 16), (1, 70000, 1, 1)]:
         ns = -(-L // 32)
-        split = max(1, min(-(-D // 32), -(-2 * 256 // (ns * B))))
+        split = max(1, min(-(-D // 64), -(-2 * 256 // (ns * B))))
         want = up(B * ns * N * D * 4) + up(B * ns * D * 4) + 2 * up(B * ns * D * N * 4) + up(B * ns * D * 4)
         if split > 1:
             want += up(split * B * L * 2 * N * 4)

@@ -32,7 +32,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// FULL: N == MNS, so no state is masked.  The block first stages the B (and
+// FULL: N == MNS, a constant in the index arithmetic.  The block first stages the B (and
 // C) rows of its segment in LDS, so that a step's 16 (32) uniform values are
 // broadcast reads, and each thread keeps its x and delta PF steps ahead in
 // registers: a step waits on no global load.
@@ -95,14 +95,8 @@ __global__ __launch_bounds__(MB) void k_mamba_scan(const float *__restrict__ x, 
         dlb[i] = ld(ds, i);
         xvb[i] = ld(xs, i);
     }
-    for (int r0 = 0; r0 < nrow; r0 += PF) {
-#pragma unroll
-        for (int i = 0; i < PF; ++i) {
-            const int r = r0 + i;
-            if (r >= nrow) break;   // uniform
-            const float dl = dlb[i], xv = xvb[i];
-            dlb[i] = ld(ds, r + PF);   // refill the slot with step r + PF
-            xvb[i] = ld(xs, r + PF);
+    // One step on the values of step r (the caller refills their slot).
+    auto step = [&](float dl, float xv, int r) {
             const float u = dl * xv;
             float bt[MNS], ct[MNS];
 #pragma unroll
@@ -120,21 +114,40 @@ __global__ __launch_bounds__(MB) void k_mamba_scan(const float *__restrict__ x, 
                     ct[4 * m + 3] = c4.w;
                 }
             }
+            // states past N have a zero exponent, zero B and C rows and a zero
+            // start: they stay 0 and add nothing, so no state is branched on
             float acc = 0.f;
 #pragma unroll
             for (int n = 0; n < MNS; ++n) {
-                if (FULL || n < N) {
-                    h[n] = exp2_fast(dl * a2[n]) * h[n] + u * bt[n];
-                    if (OUT) acc += ct[n] * h[n];
-                }
+                h[n] = exp2_fast(dl * a2[n]) * h[n] + u * bt[n];
+                if (OUT) acc += ct[n] * h[n];
             }
             if (OUT)
                 __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(acc + dsk * xv), ys, lo,
                                                       (int)((uint32_t)r * rowb), kStoreNT);
             else
                 sd += dl;
+    };
+    // Whole groups of PF steps: each slot is used, then refilled with the
+    // step PF later, after a scheduling barrier, so that the new value takes
+    // the old one's register and a step waits only on loads issued PF steps
+    // earlier.  (An exit inside the group, or a refill issued while the old
+    // value is still live, turns the slots into register copies that wait on
+    // the loads just issued.)
+    int r0 = 0;
+    for (; r0 + PF <= nrow; r0 += PF) {
+#pragma unroll
+        for (int i = 0; i < PF; ++i) {
+            step(dlb[i], xvb[i], r0 + i);
+            __builtin_amdgcn_sched_barrier(0);
+            dlb[i] = ld(ds, r0 + i + PF);
+            xvb[i] = ld(xs, r0 + i + PF);
         }
     }
+    // the last nrow - r0 < PF steps, already loaded
+#pragma unroll
+    for (int i = 0; i < PF - 1; ++i)
+        if (r0 + i < nrow) step(dlb[i], xvb[i], r0 + i);
     if (!OUT) {
 #pragma unroll
         for (int n = 0; n < MNS; ++n)

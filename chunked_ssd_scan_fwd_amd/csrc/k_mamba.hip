@@ -1,4 +1,4 @@
-// The selective (Mamba-style) scan for gfx950: forward.
+// The selective (Mamba-style) scan for gfx950: forward and backward.
 //
 // Per batch b, channel d and state n (N <= 16), with h_{-1} = 0:
 //     h_t[d,n] = exp(delta_t[d] A[d,n]) h_{t-1}[d,n] + delta_t[d] B_t[n] x_t[d]
@@ -11,7 +11,7 @@
 // contraction: no MFMA.  One thread owns one (b, d) and all N states in
 // registers; the 64 lanes of a wave take 64 consecutive channels, so every
 // x, delta and y access of a step is one coalesced 256-byte row segment,
-// and B_t, C_t (the same for the whole block) are uniform loads.
+// and B_t, C_t (the same for the whole block) are broadcast reads from LDS.
 //
 // B * D threads alone leave most of the chip idle, so the sequence is cut
 // into segments that run in parallel (the recurrence is linear):
@@ -32,10 +32,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// FULL: N == MNS, a constant in the index arithmetic.  The block first stages the B (and
-// C) rows of its segment in LDS, so that a step's 16 (32) uniform values are
-// broadcast reads, and each thread keeps its x and delta PF steps ahead in
-// registers: a step waits on no global load.
+// FULL: N == MNS, a constant in the index arithmetic.  The block first
+// stages the B (and C) rows of its segment in LDS, so that a step's 16 (32)
+// uniform values are broadcast reads, and each thread keeps its x and delta
+// PF steps ahead in registers: a step waits on no global load.
 template <bool OUT, bool FULL>
 __global__ __launch_bounds__(MB) void k_mamba_scan(const float *__restrict__ x, const float *__restrict__ delta,
                                                   const float *__restrict__ A, const float *__restrict__ Bm,
@@ -234,9 +234,10 @@ __global__ __launch_bounds__(CJ *CD) void k_mamba_carry(const float *__restrict_
 //      it from the right, a_{t1} G_{t1});
 //   3. k_mamba_bwd_seg: per segment, h over its steps again (kept in
 //      registers), then the steps in reverse with the true adjoint: dx and
-//      ddelta (sums over n in the lane and over the channel's 8 lanes), dB and dC (sums over the
-//      block's channels through an LDS transpose, the block walking all
-//      channel chunks of its segment), dA and dDskip per segment;
+//      ddelta (sums over n in the lane and over the channel's 8 lanes), dB
+//      and dC (sums over the block's channels through an LDS transpose, the
+//      block walking all channel chunks of its segment), dA and dDskip per
+//      segment;
 //   4. k_mamba_wsum: dA and dDskip summed over batch and segments, and the
 //      dB / dC partials of blocks that split the channels, in fixed order.
 // Threads of pass 3 own two states of one (b, d): eight consecutive lanes
@@ -284,8 +285,9 @@ __global__ __launch_bounds__(MB) void k_mamba_seg_ends(const float *__restrict__
     __syncthreads();
     if (d >= D) return;   // no barrier below
     const int64_t seg0 = (b * L + t0) * D;
-    const rsrc_t rx = make_rsrc(x + seg0, (int64_t)nrow * D * 4), rdl = make_rsrc(delta + seg0, (int64_t)nrow * D * 4);
-    const rsrc_t rdy = make_rsrc(dy + seg0, (int64_t)nrow * D * 4);
+    const int64_t segb = (int64_t)nrow * D * 4;   // bytes of the segment's rows
+    const rsrc_t rx = make_rsrc(x + seg0, segb), rdl = make_rsrc(delta + seg0, segb);
+    const rsrc_t rdy = make_rsrc(dy + seg0, segb);
     const uint32_t lo = (uint32_t)d * 4u, rowb = (uint32_t)D * 4u;
     // The row offset goes in the lane offset, which the buffer range check
     // covers: rows past the segment (the resource's end) read 0.
@@ -396,9 +398,9 @@ __device__ __forceinline__ void rcarry_body(const float *__restrict__ delta, con
     }
 }
 
-// (both carries in one launch: they are independent chains, each bound by
-// its latency).  Grid y: states 0 .. N-1 run the forward carry, N .. 2N-1
-// the reverse one.
+// Both carries in one launch (they are independent; one launch instead of
+// two matters at short sequences).  Grid y: states 0 .. N-1 run the forward
+// carry, N .. 2N-1 the reverse one.
 __global__ __launch_bounds__(CJ *CD) void k_mamba_carries(const float *__restrict__ delta,
                                                          const float *__restrict__ A, float *__restrict__ hend,
                                                          const float *__restrict__ sdl, float *__restrict__ gl,
@@ -486,7 +488,8 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(4))) void k_
         // dx / ddelta: lane 0 of a live channel stores at its lane offset plus
         // the row's; other lanes store at kOOB, and rows past the segment land
         // past the resource's end: the range check drops both.
-        const rsrc_t rdx = make_rsrc(dx + row0, (int64_t)nrow * D * 4), rdd = make_rsrc(ddelta + row0, (int64_t)nrow * D * 4);
+        const int64_t segb = (int64_t)nrow * D * 4;   // bytes of the segment's rows
+        const rsrc_t rdx = make_rsrc(dx + row0, segb), rdd = make_rsrc(ddelta + row0, segb);
         const uint32_t lxs = j == 0 && dlive ? (uint32_t)d * 4u : kOOB, stx = (uint32_t)D * 4u;
         // h over the segment (the decays are formed again in the reverse
         // walk: keeping them too would not fit the registers).  Steps past

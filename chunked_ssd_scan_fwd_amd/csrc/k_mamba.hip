@@ -235,9 +235,9 @@ __global__ __launch_bounds__(CJ *CD) void k_mamba_carry(const float *__restrict_
 //   3. k_mamba_bwd_seg: per segment, h over its steps again (kept in
 //      registers), then the steps in reverse with the true adjoint: dx and
 //      ddelta (sums over n in the lane and over the channel's 8 lanes), dB
-//      and dC (sums over the block's channels through an LDS transpose, the
-//      block walking all channel chunks of its segment), dA and dDskip per
-//      segment;
+//      and dC (sums over the block's channels: channel pairs by DPP, then an
+//      LDS transpose; the block walks all channel chunks of its segment), dA
+//      and dDskip per segment;
 //   4. k_mamba_wsum: dA and dDskip summed over batch and segments, and the
 //      dB / dC partials of blocks that split the channels, in fixed order.
 // Threads of pass 3 own two states of one (b, d): eight consecutive lanes
@@ -251,7 +251,7 @@ constexpr int SB = kMambaBwdSeg;      // steps per backward segment
 constexpr int LPC = 8;                // lanes per channel in pass 3, two states each
 constexpr int BD = kMambaBwdChans;    // channels per block in pass 3
 constexpr int BT = BD * LPC;          // threads per block (512)
-constexpr int WIN = 4;                // steps per dB / dC transpose window
+constexpr int WIN = 8;                // steps per dB / dC transpose window
 constexpr int XP = SB + 4;            // pitch of a channel's staged steps (16-byte rows)
 constexpr int kQuadXor1 = 0xB1;       // DPP quad_perm [1,0,3,2]
 constexpr int kQuadXor2 = 0x4E;       // DPP quad_perm [2,3,0,1]
@@ -427,7 +427,7 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(4))) void k_
     float *__restrict__ dBCp, float *__restrict__ dApart, float *__restrict__ dDpart, int64_t L, int64_t D, int N,
     int64_t nseg, int nsplit)
 {
-    __shared__ __attribute__((aligned(16))) float Tw[WIN][2][BD][NS];   // one window of per-lane dB / dC terms
+    __shared__ __attribute__((aligned(16))) float Tw[WIN][2][BD / 2][NS];   // one window of channel-pair dB / dC terms
     __shared__ float acc[SB][2][NS];                                    // the segment's dB / dC so far
     __shared__ __attribute__((aligned(16))) float BCs[2][SB][NS];       // the segment's B, C rows
     __shared__ __attribute__((aligned(16))) float Xs[3][BD][XP];        // the chunk's x, delta, dy by channel
@@ -544,23 +544,32 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(4))) void k_
             const uint32_t o = lxs + (uint32_t)r * stx;
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(dsk * dyt + dlt * sx), rdx, o, 0, 0);
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(q + xt * sx), rdd, o, 0, 0);
+            // dB / dC terms, summed first over the two channels of a 16-lane
+            // row (lanes 8 apart hold the same states): the even channel's
+            // lanes write the pair's sums, so a window holds twice the steps
             const float u = dlt * xt;
-            *reinterpret_cast<float2 *>(&Tw[r % WIN][0][dl][n0]) = make_float2(G0 * u, G1 * u);
-            *reinterpret_cast<float2 *>(&Tw[r % WIN][1][dl][n0]) = make_float2(dyt * hs0[r], dyt * hs1[r]);
+            float tb0 = G0 * u, tb1 = G1 * u, tc0 = dyt * hs0[r], tc1 = dyt * hs1[r];
+            tb0 = dpp_add<kRowRor + 8>(tb0);
+            tb1 = dpp_add<kRowRor + 8>(tb1);
+            tc0 = dpp_add<kRowRor + 8>(tc0);
+            tc1 = dpp_add<kRowRor + 8>(tc1);
+            if ((dl & 1) == 0) {
+                *reinterpret_cast<float2 *>(&Tw[r % WIN][0][dl / 2][n0]) = make_float2(tb0, tb1);
+                *reinterpret_cast<float2 *>(&Tw[r % WIN][1][dl / 2][n0]) = make_float2(tc0, tc1);
+            }
             if (r % 2 == 0) __builtin_amdgcn_sched_barrier(0);
             if (r % WIN == 0) {
                 // the window's steps r .. r + WIN - 1: sum each (step, which, n)
-                // over the block's BD channels, four threads per column, each
-                // over every fourth channel
-                static_assert(BT == 4 * WIN * 2 * NS, "four threads per column");
+                // over the block's BD / 2 channel pairs, two threads per
+                // column, each over half of them
+                static_assert(BT == 2 * WIN * 2 * NS, "two threads per column");
                 __syncthreads();
-                const int col = tid / 4, part = tid % 4;   // WIN x 2 x NS columns
+                const int col = tid / 2, part = tid % 2;   // WIN x 2 x NS columns
                 const int w = col / (2 * NS), which = (col / NS) % 2, cn = col % NS;
                 float s = 0.f;
 #pragma unroll
-                for (int k = 0; k < BD / 4; ++k) s += Tw[w][which][4 * k + part][cn];
-                s = dpp_add<kQuadXor1>(s);   // lanes 4c .. 4c + 3 hold one column's quarters
-                s = dpp_add<kQuadXor2>(s);
+                for (int k = 0; k < BD / 4; ++k) s += Tw[w][which][part * (BD / 4) + k][cn];
+                s = dpp_add<kQuadXor1>(s);   // lanes 2c and 2c + 1 hold one column's halves
                 if (part == 0 && r + w < nrow) acc[r + w][which][cn] += s;
                 __syncthreads();
             }

@@ -286,7 +286,8 @@ def mamba_work(s, backward=False):
 
 
 def mamba_sweep(args, torch, ssd, points=None):
-    """mamba_fwd (fwd) and mamba_fwd + mamba_bwd (fwd_bwd) at the points of
+    """mamba_fwd (fwd), mamba_fwd_bwd (fwd_bwd: y and the gradients in one
+    call) and mamba_fwd then mamba_bwd (fwd_then_bwd) at the points of
     kernel_mamba_cpu.json's grid (batch 4, state 16), timed by the pages'
     protocol; the page's CPU medians go along as context."""
     from ssd_workload.mamba import MAMBA_GRID, make_mamba_inputs
@@ -307,19 +308,24 @@ def mamba_sweep(args, torch, ssd, points=None):
             ssd.mamba_fwd(d["x"], d["delta"], d["A"], d["B"], d["C"], d["Dskip"], out=y, workspace=ws)
 
         def fwd_bwd():
-            # the loss value (y) and all six gradients; the backward
-            # recomputes the forward's states itself
+            # the value (y) and all six gradients in one call
+            ssd.mamba_fwd_bwd(d["x"], d["delta"], d["A"], d["B"], d["C"], d["Dskip"], d["dy"], out=(y,) + grads,
+                              workspace=wsb)
+
+        def fwd_then_bwd():
+            # the same through the two separate calls (the backward forms the
+            # forward's states again)
             fwd()
             ssd.mamba_bwd(d["x"], d["delta"], d["A"], d["B"], d["C"], d["Dskip"], d["dy"], out=grads,
                           workspace=wsb)
 
         line = {"workload": f"mamba_d{D}_L{L}", "shape": {"B": s.B, "L": s.L, "D": s.D, "N": s.N}}
-        for mode, fn in (("fwd", fwd), ("fwd_bwd", fwd_bwd)):
+        for mode, fn in (("fwd", fwd), ("fwd_bwd", fwd_bwd), ("fwd_then_bwd", fwd_then_bwd)):
             for _ in range(args.warmup):
                 fn()
             r = protocol_ms(torch, fn, repeats=args.repeats)
             t = r["median_ms"] * 1e-3
-            slots, io = mamba_work(s, backward=mode == "fwd_bwd")
+            slots, io = mamba_work(s, backward=mode != "fwd")
             line[mode] = {"median_ms": r["median_ms"], "q1_ms": r["q1_ms"], "q3_ms": r["q3_ms"],
                           "gbps_io": io / t / 1e9, "hbm_frac": io / t / PEAK_HBM,
                           "alu_frac": slots / t / PEAK_VALU_SLOTS,

@@ -93,6 +93,8 @@ def library(path: str | None = None):
     lib.mamba_bwd_workspace_size.restype = sz
     lib.mamba_bwd.argtypes = [mp] + [vp] * 13 + [vp, sz, vp]
     lib.mamba_bwd.restype = ctypes.c_int
+    lib.mamba_fwd_bwd.argtypes = [mp] + [vp] * 14 + [vp, sz, vp]
+    lib.mamba_fwd_bwd.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -362,9 +364,7 @@ def mamba_fwd(x, delta, A, B, C, Dskip, *, out=None, workspace=None):
     return out
 
 
-def mamba_bwd(x, delta, A, B, C, Dskip, dy, *, out=None, workspace=None):
-    """(dx, ddelta, dA, dB, dC, dDskip): the gradients of sum(dy * y) for the
-    selective scan (mamba_bwd), on the current stream."""
+def _mamba_grads(name, x, delta, A, B, C, Dskip, dy, out, workspace, with_y):
     import torch
     lib = library()
     if x.dim() != 3 or A.dim() != 2:
@@ -373,17 +373,33 @@ def mamba_bwd(x, delta, A, B, C, Dskip, dy, *, out=None, workspace=None):
     dev = x.device
     shapes = {"x": (s.B, s.L, s.D), "delta": (s.B, s.L, s.D), "A": (s.D, s.N), "B": (s.B, s.L, s.N),
               "C": (s.B, s.L, s.N), "Dskip": (s.D,), "dy": (s.B, s.L, s.D)}
-    for name, t in zip(shapes, (x, delta, A, B, C, Dskip, dy)):
-        _check(t, name, shapes[name], dev)
-    outs = ("dx", "ddelta", "dA", "dB", "dC", "dDskip")
-    oshape = [shapes["x"], shapes["x"], shapes["A"], shapes["B"], shapes["C"], shapes["Dskip"]]
+    for nm, t in zip(shapes, (x, delta, A, B, C, Dskip, dy)):
+        _check(t, nm, shapes[nm], dev)
+    outs = (("y",) if with_y else ()) + ("dx", "ddelta", "dA", "dB", "dC", "dDskip")
+    oshape = ([shapes["x"]] if with_y else []) + [shapes["x"], shapes["x"], shapes["A"], shapes["B"], shapes["C"],
+                                                   shapes["Dskip"]]
     if out is None:
         out = tuple(torch.empty(sh, dtype=torch.float32, device=dev) for sh in oshape)
-    for name, t, sh in zip(outs, out, oshape):
-        _check(t, name, sh, dev)
+    if len(out) != len(outs):
+        raise ValueError(f"out must hold {len(outs)} tensors: {', '.join(outs)}")
+    for nm, t, sh in zip(outs, out, oshape):
+        _check(t, nm, sh, dev)
     ws, need = _workspace_bytes(mamba_workspace_size(s, True), dev, workspace)
-    rc = lib.mamba_bwd(ctypes.byref(s), _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip), _ptr(dy),
-                       *[_ptr(t) for t in out], _ptr(ws), ctypes.c_size_t(ws.numel() * ws.element_size()), _stream(dev))
+    rc = getattr(lib, name)(ctypes.byref(s), _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip), _ptr(dy),
+                            *[_ptr(t) for t in out], _ptr(ws), ctypes.c_size_t(ws.numel() * ws.element_size()),
+                            _stream(dev))
     if rc != 0:
-        raise SsdError(rc, "mamba_bwd")
-    return out
+        raise SsdError(rc, name)
+    return tuple(out)
+
+
+def mamba_bwd(x, delta, A, B, C, Dskip, dy, *, out=None, workspace=None):
+    """(dx, ddelta, dA, dB, dC, dDskip): the gradients of sum(dy * y) for the
+    selective scan (mamba_bwd), on the current stream."""
+    return _mamba_grads("mamba_bwd", x, delta, A, B, C, Dskip, dy, out, workspace, False)
+
+
+def mamba_fwd_bwd(x, delta, A, B, C, Dskip, dy, *, out=None, workspace=None):
+    """(y, dx, ddelta, dA, dB, dC, dDskip) in one call (mamba_fwd_bwd), on the
+    current stream; the workspace is the backward's."""
+    return _mamba_grads("mamba_fwd_bwd", x, delta, A, B, C, Dskip, dy, out, workspace, True)

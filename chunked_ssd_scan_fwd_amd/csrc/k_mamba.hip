@@ -700,10 +700,12 @@ extern "C" int mamba_fwd(const mamba_shape *shape, const float *x, const float *
     return launch_status();
 }
 
-extern "C" int mamba_bwd(const mamba_shape *shape, const float *x, const float *delta, const float *A,
-                         const float *Bm, const float *Cm, const float *Ds, const float *dy, float *dx,
-                         float *ddelta, float *dA, float *dB, float *dC, float *dD, void *workspace,
-                         size_t workspace_bytes, void *stream)
+// The backward; with y != nullptr (mamba_fwd_bwd) also the forward's output,
+// from the entering states of the backward's segments.
+static int mamba_bwd_impl(const mamba_shape *shape, const float *x, const float *delta, const float *A,
+                          const float *Bm, const float *Cm, const float *Ds, const float *dy, float *y, float *dx,
+                          float *ddelta, float *dA, float *dB, float *dC, float *dD, void *workspace,
+                          size_t workspace_bytes, void *stream, bool with_y)
 {
     int rc = mamba_check_shape(shape);
     if (rc != SSD_OK) return rc;
@@ -714,6 +716,8 @@ extern "C" int mamba_bwd(const mamba_shape *shape, const float *x, const float *
     const bool work = s.B > 0 && s.L > 0;
     if (work && (!x || !delta || !A || !Bm || !Cm || !Ds || !dy || !dx || !ddelta || !dB || !dC))
         return SSD_ERR_NULL;
+    if (work && with_y && !y) return SSD_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(y) & 3u) != 0) return SSD_ERR_ALIGN;
     const void *ptrs[] = {x, delta, A, Bm, Cm, Ds, dy, dx, ddelta, dA, dB, dC, dD};
     for (const void *q : ptrs)
         if ((reinterpret_cast<uintptr_t>(q) & 3u) != 0) return SSD_ERR_ALIGN;
@@ -746,6 +750,16 @@ extern "C" int mamba_bwd(const mamba_shape *shape, const float *x, const float *
                    s.D, N, nseg);
             if (launch_status() != SSD_OK) return SSD_ERR_DEVICE;
         }
+        // the forward's output, each segment from its entering state
+        if (with_y) {
+            if (N == MNS)
+                launch(nullptr, -1, k_mamba_scan<true, true>, g1, dim3(MB), st, x, delta, A, Bm, Cm, Ds, y,
+                       hend, sdl, s.L, s.D, N, (int64_t)kMambaBwdSeg, nseg);
+            else
+                launch(nullptr, -1, k_mamba_scan<true, false>, g1, dim3(MB), st, x, delta, A, Bm, Cm, Ds, y,
+                       hend, sdl, s.L, s.D, N, (int64_t)kMambaBwdSeg, nseg);
+            if (launch_status() != SSD_OK) return SSD_ERR_DEVICE;
+        }
         // 3. the gradients of every segment
         launch(nullptr, -1, k_mamba_bwd_seg, dim3((unsigned)P.nsplit, (unsigned)nseg, (unsigned)s.B), dim3(BT), st,
                x, delta, A, Bm, Cm, Ds, dy, (const float *)hend, (const float *)gl, dx, ddelta, dB, dC, dBCp, dAp, dDp,
@@ -757,4 +771,22 @@ extern "C" int mamba_bwd(const mamba_shape *shape, const float *x, const float *
     launch(nullptr, -1, k_mamba_wsum, dim3((unsigned)((tot + WE - 1) / WE)), dim3(WE * WQ), st, (const float *)dAp,
            (const float *)dDp, (const float *)dBCp, dA, dD, dB, dC, s.B, s.L, s.D, N, work ? nseg : 0, P.nsplit);
     return launch_status();
+}
+
+extern "C" int mamba_bwd(const mamba_shape *shape, const float *x, const float *delta, const float *A,
+                         const float *Bm, const float *Cm, const float *Ds, const float *dy, float *dx,
+                         float *ddelta, float *dA, float *dB, float *dC, float *dD, void *workspace,
+                         size_t workspace_bytes, void *stream)
+{
+    return mamba_bwd_impl(shape, x, delta, A, Bm, Cm, Ds, dy, nullptr, dx, ddelta, dA, dB, dC, dD, workspace,
+                          workspace_bytes, stream, false);
+}
+
+extern "C" int mamba_fwd_bwd(const mamba_shape *shape, const float *x, const float *delta, const float *A,
+                             const float *Bm, const float *Cm, const float *Ds, const float *dy, float *y,
+                             float *dx, float *ddelta, float *dA, float *dB, float *dC, float *dD,
+                             void *workspace, size_t workspace_bytes, void *stream)
+{
+    return mamba_bwd_impl(shape, x, delta, A, Bm, Cm, Ds, dy, y, dx, ddelta, dA, dB, dC, dD, workspace,
+                          workspace_bytes, stream, true);
 }

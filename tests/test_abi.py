@@ -435,3 +435,21 @@ def test_mamba_bwd_workspace_formula():
             want += up(split * B * L * 2 * N * 4)
         assert ssd.mamba_workspace_size(ssd.MambaShapeArg(B, L, D, N), backward=True) == want, (B, L, D, N)
     assert ssd.mamba_workspace_size(ssd.MambaShapeArg(0, 10, 4, 16), backward=True) == 0
+
+
+def test_mamba_fwd_bwd_validation_before_launch():
+    lib = ssd.library()
+    s = ssd.MambaShapeArg(2, 4096, 64, 16)
+    need = ssd.mamba_workspace_size(s, backward=True)
+    p = ctypes.c_void_p(0x1000)
+
+    def call(y, ws_bytes=need):
+        return lib.mamba_fwd_bwd(ctypes.byref(s), *([p] * 7), y, *([p] * 6), p, ws_bytes, None)
+    assert call(None) == 1                           # y missing
+    assert call(ctypes.c_void_p(0x1002)) == 5        # y misaligned
+    assert call(p, need - 1) == 4                    # short workspace
+    assert lib.mamba_fwd_bwd(None, *([None] * 14), None, 0, None) == 1
+    # an empty problem needs no y, and still zeroes dA and dDskip (not run here)
+    e = ssd.MambaShapeArg(0, 10, 4, 16)
+    assert lib.mamba_fwd_bwd(ctypes.byref(e), *([None] * 8), *([None] * 2), None, None, None, None, None, 0,
+                             None) == 1              # dA, dDskip are required

@@ -161,3 +161,22 @@ def test_mamba_backward_deterministic_and_empty():
     for e in (MambaShape(0, 10, 4, 16), MambaShape(2, 0, 4, 16)):
         g = [host(t) for t in _bwd(_dev(make_mamba_inputs(e, 1)))]
         assert not np.any(g[2]) and not np.any(g[5])   # dA and dDskip are zero
+
+
+@pytest.mark.parametrize("shape", [MambaShape(1, 9, 1, 1), MambaShape(3, 77, 5, 7), MambaShape(2, 1000, 100, 16),
+                                   MambaShape(4, 512, 256, 16), MambaShape(4, 2048, 512, 16)], ids=_id)
+def test_mamba_fwd_bwd(shape):
+    """y and the gradients in one call: y against the oracle, the gradients
+    bit for bit those of mamba_bwd."""
+    need_gpu()
+    import chunked_ssd_scan_fwd_amd as ssd
+    say(f"mamba fwd_bwd {_id(shape)}")
+    inp = make_mamba_inputs(shape, seed=shape.L + 5 * shape.D)
+    d = _dev(inp)
+    out = [host(t) for t in ssd.mamba_fwd_bwd(*(d[k] for k in ARGS), d["dy"])]
+    assert rel_err(out[0], mo.fwd(*(inp[k] for k in ARGS))) <= TOL_Y
+    for a, b in zip(out[1:], [host(t) for t in _bwd(d)]):
+        np.testing.assert_array_equal(a, b)
+    ref = mo.bwd(*(inp[k] for k in ARGS), inp["dy"])
+    for a, k in zip(out[1:], GRADS):
+        assert rel_err(a, ref[k]) <= TOL_G, k

@@ -180,3 +180,28 @@ def test_mamba_fwd_bwd(shape):
     ref = mo.bwd(*(inp[k] for k in ARGS), inp["dy"])
     for a, k in zip(out[1:], GRADS):
         assert rel_err(a, ref[k]) <= TOL_G, k
+
+
+def test_mamba_poisoned_workspace_and_outputs():
+    """Every output is written whole and no kernel reads workspace it has not
+    written: NaN-filled workspaces and outputs leave the results unchanged."""
+    need_gpu()
+    import torch
+    import chunked_ssd_scan_fwd_amd as ssd
+    say("mamba poisoned workspace / outputs")
+    for s in (MambaShape(2, 1000, 100, 11), MambaShape(4, 512, 256, 16)):
+        inp = make_mamba_inputs(s, seed=9)
+        d = _dev(inp)
+        args = [d[k] for k in ARGS]
+        sa = ssd.MambaShapeArg(s.B, s.L, s.D, s.N)
+        clean_y = host(ssd.mamba_fwd(*args))
+        clean_g = [host(t) for t in ssd.mamba_fwd_bwd(*args, d["dy"])]
+        nan = float("nan")
+        wsf = torch.full((max(1, ssd.mamba_workspace_size(sa)) // 4 + 1,), nan, device="cuda")
+        wsb = torch.full((max(1, ssd.mamba_workspace_size(sa, True)) // 4 + 1,), nan, device="cuda")
+        y = torch.full((s.B, s.L, s.D), nan, device="cuda")
+        np.testing.assert_array_equal(host(ssd.mamba_fwd(*args, out=y, workspace=wsf)), clean_y)
+        outs = tuple(torch.full_like(t, nan) for t in ssd.mamba_fwd_bwd(*args, d["dy"]))
+        got = [host(t) for t in ssd.mamba_fwd_bwd(*args, d["dy"], out=outs, workspace=wsb)]
+        for a, b in zip(got, clean_g):
+            np.testing.assert_array_equal(a, b)

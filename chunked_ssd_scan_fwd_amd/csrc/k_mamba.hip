@@ -419,11 +419,13 @@ __global__ __launch_bounds__(CJ *CD) void k_mamba_carries(const float *__restric
 // or this split's partial rows [nsplit][B][L][2][N].  hin and ghat are the
 // entering states and right adjoints, [B][nseg][N][D].  At most 128 VGPRs
 // (4 waves per SIMD), so that two blocks (67 KiB of LDS each) share a CU.
+template <bool WY>   // also y, from the recomputed states (mamba_fwd_bwd)
 __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(4))) void k_mamba_bwd_seg(
     const float *__restrict__ x, const float *__restrict__ delta, const float *__restrict__ A,
     const float *__restrict__ Bm, const float *__restrict__ Cm, const float *__restrict__ Ds,
     const float *__restrict__ dy, const float *__restrict__ hin, const float *__restrict__ ghat,
-    float *__restrict__ dx, float *__restrict__ ddelta, float *__restrict__ dB, float *__restrict__ dC,
+    float *__restrict__ y, float *__restrict__ dx, float *__restrict__ ddelta, float *__restrict__ dB,
+    float *__restrict__ dC,
     float *__restrict__ dBCp, float *__restrict__ dApart, float *__restrict__ dDpart, int64_t L, int64_t D, int N,
     int64_t nseg, int nsplit)
 {
@@ -490,6 +492,7 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(4))) void k_
         // past the resource's end: the range check drops both.
         const int64_t segb = (int64_t)nrow * D * 4;   // bytes of the segment's rows
         const rsrc_t rdx = make_rsrc(dx + row0, segb), rdd = make_rsrc(ddelta + row0, segb);
+        const rsrc_t ry = make_rsrc(WY ? y + row0 : dx + row0, WY ? segb : 0);
         const uint32_t lxs = j == 0 && dlive ? (uint32_t)d * 4u : kOOB, stx = (uint32_t)D * 4u;
         // h over the segment (the decays are formed again in the reverse
         // walk: keeping them too would not fit the registers).  Steps past
@@ -544,6 +547,13 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(4))) void k_
             const uint32_t o = lxs + (uint32_t)r * stx;
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(dsk * dyt + dlt * sx), rdx, o, 0, 0);
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(q + xt * sx), rdd, o, 0, 0);
+            if constexpr (WY) {   // y_t = sum_n C_t h_t + Dskip x_t: the lane's two states, then its 8 lanes
+                float yv = ct.x * hs0[r] + ct.y * hs1[r];
+                yv = dpp_add<kQuadXor1>(yv);
+                yv = dpp_add<kQuadXor2>(yv);
+                yv = dpp_add<kRowHalfMirror>(yv);
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(yv + dsk * xt), ry, o, 0, 0);
+            }
             // dB / dC terms, summed first over the two channels of a 16-lane
             // row (lanes 8 apart hold the same states): the even channel's
             // lanes write the pair's sums, so a window holds twice the steps
@@ -700,8 +710,8 @@ extern "C" int mamba_fwd(const mamba_shape *shape, const float *x, const float *
     return launch_status();
 }
 
-// The backward; with y != nullptr (mamba_fwd_bwd) also the forward's output,
-// from the entering states of the backward's segments.
+// The backward; with with_y (mamba_fwd_bwd) also the forward's output, from
+// the states the gradient kernel recomputes.
 static int mamba_bwd_impl(const mamba_shape *shape, const float *x, const float *delta, const float *A,
                           const float *Bm, const float *Cm, const float *Ds, const float *dy, float *y, float *dx,
                           float *ddelta, float *dA, float *dB, float *dC, float *dD, void *workspace,
@@ -750,20 +760,17 @@ static int mamba_bwd_impl(const mamba_shape *shape, const float *x, const float 
                    s.D, N, nseg);
             if (launch_status() != SSD_OK) return SSD_ERR_DEVICE;
         }
-        // the forward's output, each segment from its entering state
-        if (with_y) {
-            if (N == MNS)
-                launch(nullptr, -1, k_mamba_scan<true, true>, g1, dim3(MB), st, x, delta, A, Bm, Cm, Ds, y,
-                       hend, sdl, s.L, s.D, N, (int64_t)kMambaBwdSeg, nseg);
-            else
-                launch(nullptr, -1, k_mamba_scan<true, false>, g1, dim3(MB), st, x, delta, A, Bm, Cm, Ds, y,
-                       hend, sdl, s.L, s.D, N, (int64_t)kMambaBwdSeg, nseg);
-            if (launch_status() != SSD_OK) return SSD_ERR_DEVICE;
-        }
-        // 3. the gradients of every segment
-        launch(nullptr, -1, k_mamba_bwd_seg, dim3((unsigned)P.nsplit, (unsigned)nseg, (unsigned)s.B), dim3(BT), st,
-               x, delta, A, Bm, Cm, Ds, dy, (const float *)hend, (const float *)gl, dx, ddelta, dB, dC, dBCp, dAp, dDp,
-               s.L, s.D, N, nseg, P.nsplit);
+        // 3. the gradients of every segment (and with y, the forward's output
+        // from the states recomputed on the way)
+        const dim3 g3((unsigned)P.nsplit, (unsigned)nseg, (unsigned)s.B);
+        if (with_y)
+            launch(nullptr, -1, k_mamba_bwd_seg<true>, g3, dim3(BT), st, x, delta, A, Bm, Cm, Ds, dy,
+                   (const float *)hend, (const float *)gl, y, dx, ddelta, dB, dC, dBCp, dAp, dDp, s.L, s.D, N, nseg,
+                   P.nsplit);
+        else
+            launch(nullptr, -1, k_mamba_bwd_seg<false>, g3, dim3(BT), st, x, delta, A, Bm, Cm, Ds, dy,
+                   (const float *)hend, (const float *)gl, y, dx, ddelta, dB, dC, dBCp, dAp, dDp, s.L, s.D, N, nseg,
+                   P.nsplit);
         if (launch_status() != SSD_OK) return SSD_ERR_DEVICE;
     }
     // 4. fixed-order sums (dA, dDskip are zero when B or L is 0)

@@ -340,9 +340,8 @@ int mamba_bwd(const mamba_shape *shape,
 /* y and the six gradients in one call: the value and the gradients that the
  * page's fwd_bwd records compute together.  y is mamba_fwd's output (to
  * rounding: its segments are the backward's), the gradients are mamba_bwd's
- * bit for bit.  The output pass starts each segment from the entering state
- * that the backward forms anyway, so the forward's own end-state pass and
- * carry are not run.  Arguments, checks and the workspace as for mamba_bwd,
+ * bit for bit.  y is formed from the states the backward recomputes anyway,
+ * so no forward pass runs.  Arguments, checks and the workspace as for mamba_bwd,
  * plus y [B,L,D] (device, 4-byte aligned, overwritten; NULL only when B or
  * L is 0). */
 int mamba_fwd_bwd(const mamba_shape *shape,

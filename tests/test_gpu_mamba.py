@@ -205,3 +205,33 @@ def test_mamba_poisoned_workspace_and_outputs():
         got = [host(t) for t in ssd.mamba_fwd_bwd(*args, d["dy"], out=outs, workspace=wsb)]
         for a, b in zip(got, clean_g):
             np.testing.assert_array_equal(a, b)
+
+
+def _random_mamba_shapes(n=12, seed=2024):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        out.append(MambaShape(int(rng.integers(1, 5)), int(rng.integers(1, 3000)), int(rng.integers(1, 700)),
+                              int(rng.integers(1, 17))))
+    return out
+
+
+@pytest.mark.parametrize("shape", _random_mamba_shapes(), ids=_id)
+def test_mamba_random_shapes(shape):
+    """A seeded sweep of shapes (batch 1-4, seq up to 3000, dim up to 700,
+    1-16 states): mamba_fwd, mamba_bwd and mamba_fwd_bwd against the oracle."""
+    need_gpu()
+    import chunked_ssd_scan_fwd_amd as ssd
+    say(f"mamba random {_id(shape)}")
+    inp = make_mamba_inputs(shape, seed=shape.L * 7 + shape.D)
+    d = _dev(inp)
+    ref_y = mo.fwd(*(inp[k] for k in ARGS))
+    ref = mo.bwd(*(inp[k] for k in ARGS), inp["dy"])
+    assert rel_err(host(_fwd(d)), ref_y) <= TOL_Y
+    g = [host(t) for t in _bwd(d)]
+    for a, k in zip(g, GRADS):
+        assert rel_err(a, ref[k]) <= TOL_G, k
+    both = [host(t) for t in ssd.mamba_fwd_bwd(*(d[k] for k in ARGS), d["dy"])]
+    assert rel_err(both[0], ref_y) <= TOL_Y
+    for a, b in zip(both[1:], g):
+        np.testing.assert_array_equal(a, b)

@@ -285,6 +285,31 @@ def mamba_work(s, backward=False):
     return elems * s.N * (fwd_slots + 1 + EXP_SLOTS + 11), io_f + io_b
 
 
+def mamba_cpu_baseline(point):
+    """The selective scan's fp64 oracle on the host cores at one point of its
+    page's grid (the whole workload): the forward alone, then forward +
+    backward, one run each (at the largest point some 10 s of host work)."""
+    from oracle import mamba as mo
+    from ssd_workload.mamba import MAMBA_GRID, make_mamba_inputs
+    s = MAMBA_GRID[point]
+    inp = make_mamba_inputs(s, 3000 + point[0] + point[1])
+    a = [inp[k] for k in ("x", "delta", "A", "B", "C", "Dskip")]
+    t0 = time.perf_counter()
+    mo.fwd(*a)
+    t1 = time.perf_counter()
+    mo.fwd(*a)
+    mo.bwd(*a, inp["dy"])
+    t2 = time.perf_counter()
+    fwd_ms, fb_ms = (t1 - t0) * 1e3, (t2 - t1) * 1e3
+    sl, _ = mamba_work(s)
+    slb, _ = mamba_work(s, backward=True)
+    return {"value": fb_ms, "unit": "ms", "cores": mo.num_threads(), "kind": "oracle", "cpu_model": cpu_info(),
+            "fwd_ms": fwd_ms, "fwd_bwd_ms": fb_ms,
+            "fwd_lane_ops_per_s": sl / (fwd_ms * 1e-3), "fwd_bwd_lane_ops_per_s": slb / (fb_ms * 1e-3),
+            "sample": f"whole mamba_d{point[0]}_L{point[1]} workload in fp64: forward alone, then forward + "
+                      "backward, one run each (value: fwd_bwd ms)"}
+
+
 def mamba_sweep(args, torch, ssd, points=None):
     """mamba_fwd (fwd), mamba_fwd_bwd (fwd_bwd: y and the gradients in one
     call) and mamba_fwd then mamba_bwd (fwd_then_bwd) at the points of
@@ -739,6 +764,8 @@ def main():
     configs = None if args.no_configs else config_rows(torch, ssd, args)
     # the second workload of the pages (kernel_mamba_cpu.json) at its largest point
     mamba = None if args.no_configs else mamba_sweep(args, torch, ssd, points={(1024, 8192)})
+    if mamba and not args.no_cpu:
+        mamba[0]["cpu_baseline"] = mamba_cpu_baseline((1024, 8192))
     facts = device_facts(torch)
 
     out = {

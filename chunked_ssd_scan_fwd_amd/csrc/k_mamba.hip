@@ -259,10 +259,14 @@ constexpr int kRowHalfMirror = 0x141; // DPP: lane i of each 8-lane half row rea
 static_assert(SB % 4 == 0 && (SB * BD) % BT == 0 && 2 * LPC == NS, "tile shapes");
 }  // namespace
 
-// 1. per (b, segment, d): end state and summed delta from zero (h over the
-// segment), and the adjoint at the segment's first step from zero at its end.
-// Steps past the sequence's end are staged as delta = x = dy = 0 and B = C = 0,
-// which leaves both walks unchanged, so neither branches on the step count.
+// 1. per (b, segment, d), in one walk from the segment's last step back:
+// its end state from a zero start, h_end = sum_t W_t delta_t x_t B_t with
+// W_t = a_{t+1} ... a_{end} (the product of the decays after t), its summed
+// delta, and the adjoint at its first step from zero past its end,
+// G_t = C_t dy_t + a_{t+1} G_{t+1}.  Both take the same decay a_{t+1} at
+// step t, so one exponential serves them.  Steps past the sequence's end read
+// as delta = x = dy = 0 (and B = C = 0 in LDS): a decay of 1 and no input,
+// which leaves both sums unchanged, so the walk does not branch on them.
 template <bool FULL>
 __global__ __launch_bounds__(MB) void k_mamba_seg_ends(const float *__restrict__ x, const float *__restrict__ delta,
                                                       const float *__restrict__ A, const float *__restrict__ Bm,
@@ -290,61 +294,51 @@ __global__ __launch_bounds__(MB) void k_mamba_seg_ends(const float *__restrict__
     const rsrc_t rdy = make_rsrc(dy + seg0, segb);
     const uint32_t lo = (uint32_t)d * 4u, rowb = (uint32_t)D * 4u;
     // The row offset goes in the lane offset, which the buffer range check
-    // covers: rows past the segment (the resource's end) read 0.
+    // covers: rows past the segment (the resource's end) read 0.  Loaded
+    // last step first, the order the walk uses them.
     auto ld = [&](rsrc_t r_, int r) {
         return __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_, lo + (uint32_t)r * rowb, 0, 0));
     };
-    // delta stays in registers for both walks; dy for the reverse walk is
-    // loaded as the forward walk frees the registers of x, last step first.
     float dl[SB], xv[SB], dv[SB];
 #pragma unroll
-    for (int r = 0; r < SB; ++r) {
+    for (int r = SB - 1; r >= 0; --r) {
         dl[r] = ld(rdl, r);
         xv[r] = ld(rx, r);
+        dv[r] = ld(rdy, r);
     }
-    float a2[MNS], h[MNS];
+    float a2[MNS], W[MNS], he[MNS], G[MNS];
 #pragma unroll
     for (int n = 0; n < MNS; ++n) {
         a2[n] = n < N ? A[d * N + n] * kLog2e : 0.f;
-        h[n] = 0.f;
+        W[n] = 1.f;
+        he[n] = 0.f;
+        G[n] = 0.f;
     }
     float sd = 0.f;
 #pragma unroll
-    for (int r = 0; r < SB; ++r) {
+    for (int r = SB - 1; r >= 0; --r) {
         const float u = dl[r] * xv[r];
         sd += dl[r];
-        dv[SB - 1 - r] = ld(rdy, SB - 1 - r);
 #pragma unroll
-        for (int n = 0; n < MNS; ++n)
-            if (FULL || n < N) h[n] = exp2_fast(dl[r] * a2[n]) * h[n] + u * BC[0][r][n];
+        for (int n = 0; n < MNS; ++n) {
+            if (FULL || n < N) {
+                const float a = r + 1 < SB ? exp2_fast(dl[r + 1] * a2[n]) : 1.f;   // a_{r+1}
+                W[n] *= a;
+                he[n] += W[n] * (u * BC[0][r][n]);
+                G[n] = BC[1][r][n] * dv[r] + a * G[n];
+            }
+        }
         __builtin_amdgcn_sched_barrier(0);   // one step at a time: bounds the LDS reads in flight
     }
     const int64_t o = (b * nseg + p) * N * D + d;   // state n at o + n D
 #pragma unroll
-    for (int n = 0; n < MNS; ++n)
-        if (n < N) hend[o + n * D] = h[n];
-    sdl[(b * nseg + p) * D + d] = sd;
-    // the adjoint: G = C_r dy_r + a_{r+1} G, from G = 0 past the last step.
-    // The decays are formed again: the empty asm hides that they equal the
-    // forward walk's, which would otherwise be kept live (512 registers).
-#pragma unroll
-    for (int r = 0; r < SB; ++r) asm volatile("" : "+v"(dl[r]));
-#pragma unroll
-    for (int n = 0; n < MNS; ++n) h[n] = 0.f;
-#pragma unroll
-    for (int r = SB - 1; r >= 0; --r) {
-#pragma unroll
-        for (int n = 0; n < MNS; ++n) {
-            if (FULL || n < N) {
-                const float c = BC[1][r][n] * dv[r];
-                h[n] = r + 1 < SB ? exp2_fast(dl[r + 1] * a2[n]) * h[n] + c : c;
-            }
+    for (int n = 0; n < MNS; ++n) {
+        if (n < N) {
+            hend[o + n * D] = he[n];
+            gl[o + n * D] = G[n];
         }
-        __builtin_amdgcn_sched_barrier(0);
     }
-#pragma unroll
-    for (int n = 0; n < MNS; ++n)
-        if (n < N) gl[o + n * D] = h[n];
+    sdl[(b * nseg + p) * D + d] = sd;
 }
 
 // 2. per (b, n, d): the adjoint entering each segment from the right.  With
